@@ -1,0 +1,431 @@
+"""Pins for the fp64 oracle, independent of the oracle's own code.
+
+Each test ties the oracle to something other than itself: exhaustive comparison
+with numpy/torch number formats, torch's scaled_dot_product_attention in
+float64 (a library special case, including its GQA head mapping), closed forms
+(constant V, zero query, single token), one-hot scores, invariances the pages
+state (splitting is exact; paging and page order do not change the result),
+worked examples printed on the pages (tests/golden), and rotary identities.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from synth import BF16, F16, append_case, cascade_case, contiguous_case, paged_case
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _built(oracle_lib):
+    return oracle_lib
+
+
+def okv(case):
+    return oracle.KV(case.k, case.v, oracle.dtype_code(case.k), case.Hq, case.B, case.page_size,
+                     case.page_table, case.prefix_pages, case.prefix_len)
+
+
+def golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- number formats
+
+def test_f16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle.to_f64(bits, oracle.F16)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zero is kept
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle.to_f64(bits, oracle.BF16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def _halfway_points(vals):
+    v = np.unique(vals[np.isfinite(vals)])
+    return (v[:-1] + v[1:]) / 2.0
+
+
+def test_f16_encode_matches_numpy_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 5, 20000),
+        _halfway_points(np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)),
+        np.array([65504.0, 65519.99, 65520.0, 7e4, 2.0 ** -24, 2.0 ** -25, 2.0 ** -25 * 1.0001,
+                  2.0 ** -14, 0.0, 1 + 2 ** -11 + 2 ** -40]),
+    ])
+    x = np.concatenate([x, -x])
+    ours = oracle.from_f64(x, oracle.F16)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_encode_bruteforce_nearest_even():
+    # all finite non-negative bf16 values, in increasing order of their bit patterns
+    pos_bits = np.arange(0, 0x7F80, dtype=np.uint16)
+    pos_vals = oracle.to_f64(pos_bits, oracle.BF16)
+    assert np.all(np.diff(pos_vals) > 0)
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        np.abs(rng.standard_normal(20000)) * 10.0 ** rng.integers(-40, 38, 20000),
+        (pos_vals[:-1] + pos_vals[1:])[::97] / 2.0,  # exact ties
+        np.array([1.0, 3.0, 2.0 ** -133, 2.0 ** -134, 1e-45]),
+    ])
+    x = x[x <= pos_vals[-1]]
+    ours = oracle.from_f64(x, oracle.BF16)
+    # brute force: nearest of the two neighbours, ties to the even bit pattern
+    hi = np.searchsorted(pos_vals, x, side="left")
+    lo = np.maximum(hi - 1, 0)
+    hi = np.minimum(hi, len(pos_vals) - 1)
+    dlo, dhi = x - pos_vals[lo], pos_vals[hi] - x
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(pos_bits[lo] % 2 == 0, lo, hi)))
+    assert np.array_equal(ours, pos_bits[pick])
+    assert np.array_equal(oracle.from_f64(-x, oracle.BF16), pos_bits[pick] | 0x8000)
+
+
+# ---------------------------------------------------------------- attention definition
+
+def _tiny_cases():
+    out = []
+    rng = np.random.default_rng(2)
+    for i in range(12):
+        Hkv = int(rng.integers(1, 3))
+        G = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([4, 8]))
+        B = int(rng.integers(1, 3))
+        cap = 7
+        lens = rng.integers(1, cap + 1, B)
+        dtype = F16 if i % 2 == 0 else BF16
+        out.append(contiguous_case(100 + i, B, Hkv * G, Hkv, D, lens, cap, dtype, pad="nan"))
+    return out
+
+
+@pytest.mark.parametrize("case", _tiny_cases(), ids=lambda c: f"B{c.B}H{c.Hq}/{c.Hkv}D{c.D}")
+def test_decode_matches_torch_sdpa_fp64(case):
+    scale = 1.0 / math.sqrt(case.D) * (1.0 if case.D == 8 else 0.7)
+    out, lse = oracle.decode(okv(case), case.q, case.seq_lens, scale)
+    for b in range(case.B):
+        L = int(case.seq_lens[b])
+        q = case.q[b].to(torch.float64)[None, :, None, :]                # [1, Hq, 1, D]
+        k = case.k[b, :L].to(torch.float64).permute(1, 0, 2)[None]      # [1, Hkv, L, D]
+        v = case.v[b, :L].to(torch.float64).permute(1, 0, 2)[None]
+        ref = F.scaled_dot_product_attention(q, k.contiguous(), v.contiguous(), scale=scale,
+                                             enable_gqa=True)[0, :, 0, :]
+        np.testing.assert_allclose(out[b], ref.numpy(), rtol=0, atol=1e-12)
+        # LSE through the same library routine: add a zero key (score 0) whose
+        # value is 0 while every real key has value 1; the output is Z / (1 + Z).
+        ones = torch.ones(1, case.Hkv, L + 1, 1, dtype=torch.float64)
+        ones[:, :, L] = 0.0
+        ksink = torch.cat([k, torch.zeros(1, case.Hkv, 1, case.D, dtype=torch.float64)], dim=2)
+        r = F.scaled_dot_product_attention(q, ksink.contiguous(), ones, scale=scale,
+                                           enable_gqa=True)[0, :, 0, 0].numpy()
+        np.testing.assert_allclose(lse[b], np.log(r / (1.0 - r)), rtol=0, atol=1e-10)
+
+
+def test_constant_v_gives_constant_output():
+    case = contiguous_case(7, 2, 8, 2, 32, [1, 100], 100, BF16, pad="nan")
+    c = torch.randn(2, 1, 2, 32).to(BF16)
+    case.v[:] = c
+    out, _ = oracle.decode(okv(case), case.q, case.seq_lens, 0.3)
+    for b in range(2):
+        for h in range(8):
+            np.testing.assert_allclose(out[b, h], c[b, 0, h // 4].to(torch.float64).numpy(),
+                                       rtol=1e-13, atol=1e-13)
+
+
+def test_zero_query_gives_mean_and_log_length():
+    case = contiguous_case(8, 2, 4, 4, 16, [5, 33], 40, F16, pad="nan")
+    case.q.zero_()
+    out, lse = oracle.decode(okv(case), case.q, case.seq_lens, 0.25)
+    for b in range(2):
+        L = int(case.seq_lens[b])
+        mean = case.v[b, :L].to(torch.float64).mean(0).numpy()  # [Hkv, D]
+        np.testing.assert_allclose(out[b], mean, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[b], math.log(L), rtol=0, atol=1e-13)
+
+
+def test_single_token_returns_its_value_row():
+    case = contiguous_case(9, 3, 4, 2, 64, [1, 1, 1], 4, F16, pad="nan")
+    out, lse = oracle.decode(okv(case), case.q, case.seq_lens, 0.125)
+    for b in range(3):
+        for h in range(4):
+            g = h // 2
+            assert np.array_equal(out[b, h], case.v[b, 0, g].to(torch.float64).numpy())
+            s = 0.125 * np.dot(case.q[b, h].to(torch.float64).numpy(),
+                               case.k[b, 0, g].to(torch.float64).numpy())
+            assert abs(lse[b, h] - s) <= 1e-13 * max(1.0, abs(s))
+
+
+def test_one_hot_scores_pick_one_row():
+    D, L = 128, 300
+    case = contiguous_case(10, 1, 4, 1, D, [L], L, F16, pad="zero")
+    case.q.zero_()
+    case.q[0, :, 0] = 40.0
+    case.k[0, :, 0, 0] = 0.0
+    jstar = 217
+    case.k[0, jstar, 0, 0] = 40.0
+    scale = 1.0 / math.sqrt(D)
+    out, lse = oracle.decode(okv(case), case.q, case.seq_lens, scale)
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], case.v[0, jstar, 0].to(torch.float64).numpy(),
+                                   rtol=0, atol=1e-12)
+        assert abs(lse[0, h] - 1600.0 * scale) < 1e-9
+
+
+# ---------------------------------------------------------------- paging
+
+def _scatter_to_pages(case, ps, seed, extra_pages=3):
+    """Copy a contiguous case into a NaN-poisoned paged pool under a random page order."""
+    g = torch.Generator().manual_seed(seed)
+    B, cap, Hkv, D = case.k.shape
+    npages = [math.ceil(int(L) / ps) for L in case.seq_lens]
+    pool = sum(npages) + extra_pages
+    perm = torch.randperm(pool, generator=g)
+    kp = torch.full((pool, ps, Hkv, D), float("nan"), dtype=case.k.dtype)
+    vp = kp.clone()
+    table = torch.full((B, max(npages)), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        for i in range(npages[b]):
+            p = int(perm[off + i])
+            table[b, i] = p
+            n = min(ps, L - i * ps)
+            kp[p, :n] = case.k[b, i * ps:i * ps + n]
+            vp[p, :n] = case.v[b, i * ps:i * ps + n]
+        off += npages[b]
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("ps", [16, 32, 64])
+def test_paged_equals_contiguous(ps):
+    case = contiguous_case(11, 3, 8, 4, 32, [1, 77, 200], 200, BF16, pad="nan")
+    ref = oracle.decode(okv(case), case.q, case.seq_lens, 0.2)
+    kp, vp, table = _scatter_to_pages(case, ps, seed=ps)
+    pk = oracle.KV(kp, vp, oracle.BF16, 8, 3, ps, table)
+    got = oracle.decode(pk, case.q, case.seq_lens, 0.2)
+    assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
+
+
+def test_page_table_example_from_the_pages():
+    rows = [[int(x) for x in r] for r in golden_rows("page_table_example.txt")]
+    table = torch.tensor(rows, dtype=torch.int32)
+    ps, D, Hkv = 16, 16, 2
+    lens = torch.tensor([40, 20], dtype=torch.int32)  # 3 pages and 2 pages
+    g = torch.Generator().manual_seed(12)
+    pool_k = torch.randn(8, ps, Hkv, D, generator=g).to(F16)
+    pool_v = torch.randn(8, ps, Hkv, D, generator=g).to(F16)
+    pool_k[5:] = float("nan")  # pages no request uses
+    pool_v[5:] = float("nan")
+    pool_k[2, 8:] = float("nan")  # past sequence 0's length inside its last page
+    pool_v[4, 4:] = float("nan")
+    q = torch.randn(2, 4, D, generator=g).to(F16)
+    got_out, got_lse = oracle.decode(oracle.KV(pool_k, pool_v, oracle.F16, 4, 2, ps, table), q,
+                                     lens, 0.25)
+    assert np.isfinite(got_out).all() and np.isfinite(got_lse).all()
+    # the same logical sequences laid out contiguously, by hand from the table rows
+    kc = torch.zeros(2, 48, Hkv, D, dtype=F16)
+    vc = torch.zeros(2, 48, Hkv, D, dtype=F16)
+    kc[0, :40] = torch.cat([pool_k[0], pool_k[1], pool_k[2, :8]])
+    vc[0, :40] = torch.cat([pool_v[0], pool_v[1], pool_v[2, :8]])
+    kc[1, :20] = torch.cat([pool_k[3], pool_k[4, :4]])
+    vc[1, :20] = torch.cat([pool_v[3], pool_v[4, :4]])
+    ref_out, ref_lse = oracle.decode(oracle.KV(kc, vc, oracle.F16, 4, 2), q, lens, 0.25)
+    assert np.array_equal(got_out, ref_out) and np.array_equal(got_lse, ref_lse)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    case = contiguous_case(13, 2, 8, 2, 16, [9, 30], 30, F16, pad="nan")
+    gqa = oracle.decode(okv(case), case.q, case.seq_lens, 0.3)
+    rep = oracle.KV(case.k.repeat_interleave(4, dim=2), case.v.repeat_interleave(4, dim=2),
+                    oracle.F16, 8, 2)
+    mha = oracle.decode(rep, case.q, case.seq_lens, 0.3)
+    assert np.array_equal(gqa[0], mha[0]) and np.array_equal(gqa[1], mha[1])
+
+
+# ---------------------------------------------------------------- split / merge exactness
+
+def _random_bounds(rng, lens, S, cap):
+    out = np.zeros((len(lens), S + 1), dtype=np.int32)
+    for b in range(len(lens)):
+        cuts = np.sort(rng.integers(0, cap + 1, S - 1))
+        out[b, 1:S] = cuts
+        out[b, S] = cap
+    return out
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 16])
+def test_merging_partials_at_any_split_points_is_exact(S):
+    rng = np.random.default_rng(S)
+    case = contiguous_case(14 + S, 2, 8, 2, 32, [1, 150], 150, BF16, pad="nan")
+    kv = okv(case)
+    ref_out, ref_lse = oracle.decode(kv, case.q, case.seq_lens, 0.2)
+    bounds = _random_bounds(rng, case.seq_lens.numpy(), S, 150)
+    if S >= 5:  # force an empty split and a one-token split
+        bounds[1, 1] = bounds[1, 2] = 10
+        bounds[1, 3] = 11
+    po, pm, pd = oracle.partials(kv, case.q, case.seq_lens, 0.2, bounds)
+    out, lse = oracle.merge(po, pm, pd)
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-13, atol=1e-13)
+    # the merge order does not matter (max and sum are associative)
+    perm = rng.permutation(S)
+    out2, lse2 = oracle.merge(po[:, :, perm], pm[:, :, perm], pd[:, :, perm])
+    np.testing.assert_allclose(out2, ref_out, rtol=0, atol=1e-12)
+    # normalised states (o, lse) with d = 1 merge to the same result
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o_n = np.where(pd[..., None] > 0, po / pd[..., None], 0.0)
+        l_n = np.where(pd > 0, pm + np.log(pd), -np.inf)
+    out3, lse3 = oracle.merge(o_n, l_n, np.where(pd > 0, 1.0, 0.0))
+    np.testing.assert_allclose(out3, ref_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse3, ref_lse, rtol=1e-13, atol=1e-13)
+
+
+def test_empty_inputs():
+    case = contiguous_case(20, 2, 4, 4, 16, [0, 3], 8, F16, pad="nan")
+    out, lse = oracle.decode(okv(case), case.q, case.seq_lens, 0.25)
+    assert np.array_equal(out[0], np.zeros((4, 16))) and np.all(lse[0] == -np.inf)
+    assert np.isfinite(out[1]).all()
+    po = np.zeros((1, 2, 3, 16))
+    pm = np.full((1, 2, 3), -np.inf)
+    pd = np.zeros((1, 2, 3))
+    mo, ml = oracle.merge(po, pm, pd)
+    assert np.array_equal(mo, np.zeros((1, 2, 16))) and np.all(ml == -np.inf)
+
+
+# ---------------------------------------------------------------- cascade
+
+def test_cascade_equals_attention_over_prefix_then_suffix():
+    case = cascade_case(21, 3, 8, 2, 32, prefix_len=64, ps=16, suffix_lens=[0, 5, 40], dtype=BF16,
+                        pad="nan", extra_pages=2)
+    got = oracle.decode(okv(case), case.q, case.seq_lens, 0.2)
+    # a plain paged table listing the prefix pages, then each request's own pages
+    n_pre = case.prefix_pages.numel()
+    table = torch.full((3, n_pre + case.page_table.shape[1]), -1, dtype=torch.int32)
+    for b in range(3):
+        table[b, :n_pre] = case.prefix_pages
+        table[b, n_pre:] = case.page_table[b]
+    plain = oracle.KV(case.k, case.v, oracle.BF16, 8, 3, 16, table)
+    ref = oracle.decode(plain, case.q, case.seq_lens + 64, 0.2)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_cascade_with_ragged_prefix_matches_gathered_rows():
+    case = cascade_case(22, 2, 4, 2, 16, prefix_len=37, ps=16, suffix_lens=[3, 19], dtype=F16,
+                        pad="nan")
+    got = oracle.decode(okv(case), case.q, case.seq_lens, 0.3)
+    # gather the logical rows by hand: prefix tokens, then the request's suffix tokens
+    kc = torch.zeros(2, 37 + 19, 2, 16, dtype=F16)
+    vc = torch.zeros_like(kc)
+    for b in range(2):
+        rows_k, rows_v = [], []
+        for j in range(37):
+            p = int(case.prefix_pages[j // 16])
+            rows_k.append(case.k[p, j % 16])
+            rows_v.append(case.v[p, j % 16])
+        for j in range(int(case.seq_lens[b])):
+            p = int(case.page_table[b, j // 16])
+            rows_k.append(case.k[p, j % 16])
+            rows_v.append(case.v[p, j % 16])
+        n = len(rows_k)
+        kc[b, :n] = torch.stack(rows_k)
+        vc[b, :n] = torch.stack(rows_v)
+    ref = oracle.decode(oracle.KV(kc, vc, oracle.F16, 4, 2), case.q, case.seq_lens + 37, 0.3)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+# ---------------------------------------------------------------- rotary and append
+
+def test_rope_identities():
+    rng = np.random.default_rng(5)
+    D, rd = 128, 128
+    x = rng.standard_normal(D)
+    assert np.array_equal(oracle.rope_neox(x, 0, rd), x)
+    y = oracle.rope_neox(x, 1234, rd)
+    h = rd // 2
+    np.testing.assert_allclose(np.hypot(y[:h], y[h:]), np.hypot(x[:h], x[h:]), rtol=1e-13)
+    # <rope(q, m), rope(k, n)> depends only on m - n
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    a = np.dot(oracle.rope_neox(q, 700, rd), oracle.rope_neox(k, 300, rd))
+    b = np.dot(oracle.rope_neox(q, 1400, rd), oracle.rope_neox(k, 1000, rd))
+    assert abs(a - b) < 1e-10
+    # complex-number form: z_i = x_i + i x_{i+rd/2} times exp(i * pos * base^(-2i/rd))
+    pos = 77
+    z = (x[:h] + 1j * x[h:]) * np.exp(1j * pos * 10000.0 ** (-2.0 * np.arange(h) / rd))
+    y = oracle.rope_neox(x, pos, rd)
+    np.testing.assert_allclose(y[:h], z.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y[h:], z.imag, rtol=0, atol=1e-12)
+
+
+def test_rope_partial_dim_and_neox_pairing():
+    D, rd = 128, 64
+    x = np.zeros(D)
+    x[0] = 1.0  # pairs with x[32] in NeoX, with x[1] in the interleaved form
+    y = oracle.rope_neox(x, 1, rd)
+    assert y[1] == 0.0 and y[32] != 0.0
+    assert abs(y[0] - math.cos(1.0)) < 1e-15 and abs(y[32] - math.sin(1.0)) < 1e-15
+    x = np.random.default_rng(6).standard_normal(D)
+    y = oracle.rope_neox(x, 999, rd)
+    assert np.array_equal(y[rd:], x[rd:])
+
+
+@pytest.mark.parametrize("rd", [128, 64, 0])
+def test_append_writes_one_row_per_head_and_rotates(rd):
+    case = append_case(23, 3, 8, 2, 128, 64, F16, rotary_dim=rd, pad="zero")
+    kv = okv(case)
+    kc, vc, q_rot, after = oracle.append(kv, case.k_new, case.v_new, case.q, case.seq_lens, rd)
+    k0 = oracle._bits(case.k)
+    v0 = oracle._bits(case.v)
+    kn = oracle._bits(case.k_new)
+    vn = oracle._bits(case.v_new)
+    for b in range(3):
+        c = int(case.seq_lens[b])
+        for g in range(2):
+            assert np.array_equal(vc[b, c, g], vn[b, g])
+            if rd:
+                want = oracle.from_f64(oracle.rope_neox(oracle.to_f64(kn[b, g], 0), c, rd), 0)
+            else:
+                want = kn[b, g]
+            assert np.array_equal(kc[b, c, g], want)
+        keep = np.ones(64, dtype=bool)
+        keep[c] = False
+        assert np.array_equal(kc[b, keep], k0[b, keep]) and np.array_equal(vc[b, keep], v0[b, keep])
+        for h in range(8):
+            qd = oracle.to_f64(oracle._bits(case.q)[b, h], 0)
+            np.testing.assert_array_equal(q_rot[b, h], oracle.rope_neox(qd, c, rd) if rd else qd)
+    # cache_seqlens is an input only
+    assert case.seq_lens.dtype == torch.int32
+
+
+# ---------------------------------------------------------------- worked examples on the pages
+
+def test_golden_split_picture_and_slices():
+    (row,) = golden_rows("split_picture_1024.txt")
+    n, S, bounds = int(row[0]), int(row[1]), [int(x) for x in row[2:]]
+    assert bounds == [n * i // S for i in range(S + 1)]
+    (row,) = golden_rows("lpnh_128k_slices.txt")
+    n, S, slice_len, B, H, tasks = map(int, row)
+    assert n // S == slice_len and B * H * S == tasks

@@ -1,0 +1,52 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle.c (a dropped term, a wrong
+sign or index, a swapped operand, a wrong rounding), builds it with gcc on the
+CPU into a temporary library, and runs the pin suite against it in a child
+process: the suite must fail for every mutant.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "dropped_scale": ("return scale * s;", "return s;"),
+    "gqa_index_modulo": ("g = h / G, D = kv->D;", "g = h % kv->Hkv, D = kv->D;"),
+    "page_slot_swapped": ("slot = jj % kv->page_size;", "slot = (jj + 1) % kv->page_size;"),
+    "merge_alpha_sign": ("0.0 : exp(mi - m);", "0.0 : exp(m - mi);"),
+    "lse_drops_max": ("lse[bh] = m + log(dsum);\n        }\n        free(sbuf);",
+                      "lse[bh] = log(dsum);\n        }\n        free(sbuf);"),
+    "rope_sign": ("x[i] = a * c - b * s;", "x[i] = a * c + b * s;"),
+    "rope_frequency": ("pow(base, -2.0 * (double)i", "pow(base, -1.0 * (double)i"),
+    "rope_pairing": ("double a = x[i], b = x[i + half];", "double a = x[i], b = x[i ^ 1];"),
+    "f16_bias": ("ldexp((double)(m + 1024), e - 25)", "ldexp((double)(m + 1024), e - 24)"),
+    "f16_truncates": ("double v = rint(a / ulp) * ulp; /* rint", "double v = floor(a / ulp) * ulp; /* rint"),
+    "v_reads_k": ("o_tilde[d] += p * elem(kv, kv->v, off + d);", "o_tilde[d] += p * elem(kv, kv->k, off + d);"),
+    "last_token_dropped": ("for (int j = lo; j < hi; ++j) {\n        sbuf",
+                           "for (int j = lo; j < hi - 1; ++j) {\n        sbuf"),
+    "prefix_pages_ignored": ("} else if (kv->prefix_pages && j < kv->prefix_len) {",
+                             "} else if (kv->prefix_pages && j < 0) {"),
+    "append_v_not_written": ("for (int d = 0; d < D; ++d) v_cache[off + d] = vn[d];", ""),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", str(mut), "-o",
+                    str(lib), "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
