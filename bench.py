@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X: µs/step and achieved KV-read GB/s.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload c2] [--mode fused|two]
+
+A step is one full decode call over one batch of synthetic input (map + merge,
+or the single fused kernel; with append or cascade workloads those parts
+too). Inputs are resident in HBM before timing starts. To keep the 256 MB
+last-level cache (MALL) from serving repeated reads, steps rotate through
+enough copies of the KV cache to cover >= 1 GiB; the single-copy ("warm")
+figure is reported separately.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode attention µs/step + achieved KV-read GB/s (% of 8 TB/s HBM peak)"
+WORKLOAD_TEXT = {
+    "c1": "unpaged MHA decode: B=1, Hq=Hkv=32, D=128, 4096 contiguous fp16 tokens, 16 splits",
+    "c2": "long-context GQA decode: B=1, Hq=32, Hkv=8, D=128, 131072 contiguous bf16 tokens",
+    "c3": "paged batched decode: B=32, Hq=32, Hkv=8, D=128, page 16, lengths U[512,8192], bf16",
+    "c4": "decode with KV append + NeoX rotary: B=4, Hq=32, Hkv=8, D=128, max_seqlen 2048, fp16",
+    "c5": "cascade: 64 requests, Hq=32, Hkv=8, D=128, shared 16384-token prefix + U[256,2048] suffix, "
+          "page 64, bf16",
+}
+KERNEL_SOURCES = ["split_kv.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_fdec_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Runner:
+    """Device copies of one workload plus a step function (rotates KV copies)."""
+
+    def __init__(self, F, case, mode: str, splits: int, min_footprint: int, dev):
+        import torch
+
+        self.F, self.case, self.mode = F, case, mode
+        self.dev = dev
+        self.q = case.q.to(dev)
+        self.lens = case.seq_lens.to(dev)
+        self.table = None if case.page_table is None else case.page_table.to(dev)
+        kv_footprint = 2 * case.k.numel() * case.k.element_size()
+        self.copies = max(1, min(64, math.ceil(min_footprint / kv_footprint)))
+        self.k = [case.k.to(dev) for _ in range(self.copies)]
+        self.v = [case.v.to(dev) for _ in range(self.copies)]
+        self.append = None
+        if case.k_new is not None:
+            self.k_new, self.v_new = case.k_new.to(dev), case.v_new.to(dev)
+            self.cos = None if case.rope_cos is None else case.rope_cos.to(dev)
+            self.sin = None if case.rope_sin is None else case.rope_sin.to(dev)
+            self.append = F.make_append(self.k_new, self.v_new, self.cos, self.sin, case.rotary_dim)
+        B, Hq, D = case.q.shape
+        if splits <= 0:
+            splits = case.num_splits
+        if splits <= 0:
+            lens_host = (case.seq_lens + (1 if case.k_new is not None else 0)).tolist()
+            splits = F.plan(B, Hq, case.Hkv, lens_host, case.capacity, case.page_size)
+        self.S = splits
+        self.out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        self.ws = F.Workspace(F.workspace_size(B, Hq, case.Hkv, D, splits), dev)
+        self.i = 0
+
+    def step(self, copy: int | None = None) -> None:
+        c = self.i % self.copies if copy is None else copy
+        self.i += 1
+        self.F.decode(self.q, self.k[c], self.v[c], self.lens, page_table=self.table, num_splits=self.S,
+                      append=self.append, fused=(self.mode == "fused"), out=self.out, lse=self.lse,
+                      workspace=self.ws)
+
+
+def time_region(runner: Runner, steps: int, warmup: int, copy=None):
+    """Whole-region time of `steps` back-to-back steps (events on the launch stream)."""
+    import torch
+
+    for _ in range(warmup):
+        runner.step(copy)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        runner.step(copy)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms
+
+
+def time_per_launch(runner: Runner, steps: int, copy=None):
+    """Per-step durations from an event pair around each step (launch-gap free)."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        runner.step(copy)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)  # ms
+
+
+def pct(xs, p):
+    return xs[min(len(xs) - 1, int(round(p / 100.0 * (len(xs) - 1))))]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, if current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None  # the kernel changed since the counters were taken
+    return t.get("traffic_bytes")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle on the same workload, timed on this host's cores."""
+    import oracle
+
+    oracle.build(force=False)
+    kv = oracle.KV(case.k, case.v, oracle.dtype_code(case.k), case.Hq, case.B, case.page_size, case.page_table,
+                   case.prefix_pages, case.prefix_len)
+    q = oracle.to_f64(case.q, oracle.dtype_code(case.k))
+    scale = 1.0 / math.sqrt(case.D)
+    threads = oracle.max_threads()
+    reps, t0 = 0, oracle.now()
+    while True:
+        oracle.decode(kv, q, case.seq_lens, scale, threads)
+        reps += 1
+        if oracle.now() - t0 >= budget_s or reps >= 1000:
+            break
+    dt = oracle.now() - t0
+    return {"value": round(case.kv_bytes() * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full workload ({case.name}), decoded {reps} time(s) by the fp64 oracle in "
+                      f"{dt:.1f} s with {threads} OpenMP threads; rate = KV bytes per pass x passes / time"}
+
+
+def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: int, dev):
+    import synth
+
+    t0 = time.time()
+    case = synth.workload(name)
+    runner = Runner(F, case, mode, splits, 1 << 30, dev)
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s, copies={runner.copies}, S={runner.S}")
+    ms = time_region(runner, steps, warmup)
+    per = time_per_launch(runner, steps)
+    warm = time_region(runner, steps, 2, copy=0)
+    nbytes = case.kv_bytes()
+    res = {"us_per_step": round(ms * 1e3, 2), "kv_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "pct_of_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+           "step_us_p10_p50_p90": [round(pct(per, p) * 1e3, 2) for p in (10, 50, 90)],
+           "warm_us_per_step": round(warm * 1e3, 2), "num_splits": runner.S, "mode": mode,
+           "kv_copies_rotated": runner.copies}
+    log(f"[bench] {name}: {res['us_per_step']} us/step, {res['GBps']} GB/s ({res['pct_of_peak']}% of peak)")
+    return case, runner, res, per
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--mode", default="fused", choices=["fused", "two"])
+    ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
+    ap.add_argument("--also", default="c1,c3,c4", help="other workloads timed for context ('' = none)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path has no multi-GPU mode in this build", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_attention_fdec_amd as F
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    F.load_library()
+    dev = torch.device("cuda:0")
+
+    case, runner, res, per = measure_workload(F, args.workload, args.mode, args.splits, args.steps,
+                                              args.warmup, dev)
+    # the dominant kernel: with the fused mode the step is one kernel launch
+    kernel_ms = sum(per) / len(per)
+    achieved = case.kv_bytes() / (kernel_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload) if args.mode == "fused" else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "map_kernel (split-KV map + last-block merge)" if args.mode == "fused"
+                else "map_kernel + merge_kernel",
+                "avg_launch_us": round(kernel_ms * 1e3, 2), "algorithmic_bytes_per_launch": case.kv_bytes(),
+                "kernel_hash": kernel_hash()}
+
+    # attainable streaming read at the same footprint (calibration probe)
+    import torch as _t
+
+    buf = runner.k[0].view(_t.uint8).reshape(-1)
+    F.probe_read(buf)
+    _t.cuda.synchronize()
+    e0, e1 = _t.cuda.Event(enable_timing=True), _t.cuda.Event(enable_timing=True)
+    probe = []
+    for c in range(runner.copies):
+        for kv in (runner.k[c], runner.v[c]):
+            b = kv.view(_t.uint8).reshape(-1)
+            e0.record()
+            F.probe_read(b)
+            e1.record()
+            _t.cuda.synchronize()
+            probe.append(b.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    res["probe_read_GBps"] = round(sorted(probe)[len(probe) // 2], 1)
+    res["pct_of_probe"] = round(100 * res["GBps"] / res["probe_read_GBps"], 1)
+    del runner
+
+    others = {}
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        try:
+            _, r2, res2, _ = measure_workload(F, name, args.mode, 0, args.steps, args.warmup, dev)
+            others[name] = res2
+            del r2
+        except F.FdecError as e:  # a workload whose path is not built yet
+            others[name] = {"error": str(e)}
+            log(f"[bench] {name}: {e}")
+        _t.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": res["GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["us_per_step"] / 1e3, 5),
+        "us_per_step": res["us_per_step"],
+        "pct_of_peak": res["pct_of_peak"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",  # arithmetic type: fp32 math on fp16/bf16 KV (kv_dtype in config)
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload],
+                   "kv_dtype": "bf16" if case.dtype == _t.bfloat16 else "fp16", **res},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "other_workloads": others,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

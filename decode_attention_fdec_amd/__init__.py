@@ -1,0 +1,298 @@
+"""Python binding for libfdec (split-KV decode attention on MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfdec.so``. torch supplies device memory and the current
+stream. The names follow the C ABI in ``include/fdec.h``:
+
+    plan, plan_rules, split_chunk, workspace_size, Workspace,
+    decode, decode_partials, merge_states, cascade_decode, cascade_workspace_size
+
+If ``libfdec.so`` has not been built, importing works but every call raises
+``FdecError``; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfdec.so")
+
+FDEC_OK, FDEC_ERR_INVALID_ARG, FDEC_ERR_UNSUPPORTED, FDEC_ERR_WORKSPACE, FDEC_ERR_HIP = range(5)
+FDEC_F16, FDEC_BF16 = 0, 1
+MAX_SPLITS = 256
+
+
+class FdecError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class FdecKV(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("dtype", ctypes.c_int), ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int),
+        ("page_size", ctypes.c_int), ("capacity", ctypes.c_int),
+        ("s_outer", ctypes.c_int64), ("s_token", ctypes.c_int64), ("s_head", ctypes.c_int64),
+        ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int),
+    ]
+
+
+class FdecAppend(ctypes.Structure):
+    _fields_ = [
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p),
+        ("rotary_dim", ctypes.c_int), ("rope_max_pos", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libfdec.so (after torch, so it binds to torch's HIP runtime)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FdecError(FDEC_ERR_HIP, f"{p} is not built; run __graft_entry__.build() "
+                        "or python -m decode_attention_fdec_amd.build")
+    lib = ctypes.CDLL(p)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fdec_status_string.restype = ctypes.c_char_p
+    lib.fdec_status_string.argtypes = [I]
+    lib.fdec_last_error.restype = ctypes.c_char_p
+    lib.fdec_last_error.argtypes = []
+    lib.fdec_plan.argtypes = [I, I, I, P, I, I, I, ctypes.POINTER(I)]
+    lib.fdec_plan_rules.argtypes = [I, I, I, I, ctypes.POINTER(I)]
+    lib.fdec_split_chunk.restype = ctypes.c_int64
+    lib.fdec_split_chunk.argtypes = [I, I]
+    lib.fdec_workspace_size.restype = Z
+    lib.fdec_workspace_size.argtypes = [I, I, I, I, I]
+    lib.fdec_workspace_init.argtypes = [P, Z, P]
+    lib.fdec_decode.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F, ctypes.POINTER(FdecAppend), I,
+                                P, P, P, Z, P]
+    lib.fdec_decode_partials.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F,
+                                         ctypes.POINTER(FdecAppend), P, P, P, P]
+    lib.fdec_merge_states.argtypes = [P, P, P, I, I, I, I, P, P, P]
+    lib.fdec_cascade_decode.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, P, I, I, F, P, P, P, Z, P]
+    lib.fdec_probe_read.argtypes = [P, Z, P, P]
+    lib.fdec_probe_copy.argtypes = [P, P, Z, P]
+    lib.fdec_cascade_workspace_size.restype = Z
+    lib.fdec_cascade_workspace_size.argtypes = [I, I, I, I, I, I]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != FDEC_OK:
+        lib = load_library()
+        raise FdecError(rc, f"{lib.fdec_status_string(rc).decode()}: {lib.fdec_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float16:
+        return FDEC_F16
+    if dt == torch.bfloat16:
+        return FDEC_BF16
+    raise FdecError(FDEC_ERR_UNSUPPORTED, f"dtype {dt} not built (float16, bfloat16)")
+
+
+def make_kv(k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor] = None) -> FdecKV:
+    """Describe a cache: contiguous [B, cap, Hkv, D] or paged [P, page_size, Hkv, D] (+ page_table)."""
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype or k.dim() != 4:
+        raise FdecError(FDEC_ERR_INVALID_ARG, "k and v must be 4-D with equal shapes, strides and dtypes")
+    if k.stride(3) != 1:
+        raise FdecError(FDEC_ERR_INVALID_ARG, "the head_dim axis of k/v must be contiguous")
+    kv = FdecKV()
+    kv.k, kv.v = k.data_ptr(), v.data_ptr()
+    kv.dtype = _dtype_code(k.dtype)
+    kv.num_kv_heads, kv.head_dim = k.shape[2], k.shape[3]
+    kv.s_outer, kv.s_token, kv.s_head = k.stride(0), k.stride(1), k.stride(2)
+    if page_table is None:
+        kv.page_size, kv.capacity = 0, k.shape[1]
+        kv.page_table, kv.max_pages_per_seq = None, 0
+    else:
+        if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.dim() != 2:
+            raise FdecError(FDEC_ERR_INVALID_ARG, "page_table must be a contiguous 2-D int32 tensor")
+        kv.page_size = k.shape[1]
+        kv.max_pages_per_seq = page_table.shape[1]
+        kv.capacity = kv.page_size * kv.max_pages_per_seq
+        kv.page_table = page_table.data_ptr()
+    return kv
+
+
+def make_append(k_new: torch.Tensor, v_new: torch.Tensor, rope_cos: Optional[torch.Tensor] = None,
+                rope_sin: Optional[torch.Tensor] = None, rotary_dim: int = 0) -> FdecAppend:
+    a = FdecAppend()
+    a.k_new, a.v_new = k_new.data_ptr(), v_new.data_ptr()
+    a.rotary_dim = rotary_dim
+    if rotary_dim > 0:
+        a.rope_cos, a.rope_sin = rope_cos.data_ptr(), rope_sin.data_ptr()
+        a.rope_max_pos = rope_cos.shape[0]
+    return a
+
+
+def plan(B: int, Hq: int, Hkv: int, seq_lens_host: Optional[Sequence[int]], capacity: int,
+         page_size: int = 0, cu_count: int = 256) -> int:
+    lib = load_library()
+    out = ctypes.c_int(0)
+    arr = None
+    if seq_lens_host is not None:
+        vals = [int(x) for x in seq_lens_host]
+        arr = (ctypes.c_int32 * len(vals))(*vals)
+    _check(lib.fdec_plan(B, Hq, Hkv, ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
+                         capacity, page_size, cu_count, ctypes.byref(out)))
+    return out.value
+
+
+def plan_rules(B: int, Hkv: int, sm_count: int, max_splits: int = 128) -> int:
+    out = ctypes.c_int(0)
+    _check(load_library().fdec_plan_rules(B, Hkv, sm_count, max_splits, ctypes.byref(out)))
+    return out.value
+
+
+def split_chunk(capacity: int, num_splits: int) -> int:
+    return int(load_library().fdec_split_chunk(capacity, num_splits))
+
+
+def workspace_size(B: int, Hq: int, Hkv: int, head_dim: int, num_splits: int) -> int:
+    return int(load_library().fdec_workspace_size(B, Hq, Hkv, head_dim, num_splits))
+
+
+def cascade_workspace_size(B: int, Hq: int, Hkv: int, head_dim: int, splits_prefix: int,
+                           splits_suffix: int) -> int:
+    return int(load_library().fdec_cascade_workspace_size(B, Hq, Hkv, head_dim, splits_prefix, splits_suffix))
+
+
+class Workspace:
+    """A device workspace (uint8 tensor) prepared with fdec_workspace_init."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _check(load_library().fdec_workspace_init(self.buf.data_ptr(), self.buf.numel(),
+                                                  _stream(self.buf.device)))
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+           page_table: Optional[torch.Tensor] = None, num_splits: int = 0, softmax_scale: float = 0.0,
+           append: Optional[FdecAppend] = None, fused: bool = False, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
+           return_lse: bool = True):
+    """fdec_decode: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32 or None)."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    kv = make_kv(k, v, page_table)
+    if q.dtype != k.dtype or not q.is_contiguous():
+        raise FdecError(FDEC_ERR_INVALID_ARG, "q must be contiguous with the cache dtype")
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    S = num_splits if num_splits > 0 else plan(B, Hq, kv.num_kv_heads, None, kv.capacity, kv.page_size)
+    if workspace is None:
+        workspace = Workspace(workspace_size(B, Hq, kv.num_kv_heads, D, S), q.device)
+    _check(lib.fdec_decode(q.data_ptr(), B, Hq, ctypes.byref(kv), seq_lens.data_ptr(), S,
+                           float(softmax_scale), ctypes.byref(append) if append is not None else None,
+                           int(bool(fused)), out.data_ptr(), _ptr(lse), workspace.buf.data_ptr(),
+                           workspace.nbytes, _stream(q.device)))
+    return out, lse
+
+
+def decode_partials(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                    num_splits: int, page_table: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                    append: Optional[FdecAppend] = None, part_o: Optional[torch.Tensor] = None,
+                    part_m: Optional[torch.Tensor] = None, part_d: Optional[torch.Tensor] = None):
+    """fdec_decode_partials: returns (part_o [B,Hq,S,D], part_m [B,Hq,S], part_d [B,Hq,S]) fp32."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    kv = make_kv(k, v, page_table)
+    S = num_splits
+    if part_o is None:
+        part_o = torch.empty(B, Hq, S, D, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+        part_d = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+    _check(lib.fdec_decode_partials(q.data_ptr(), B, Hq, ctypes.byref(kv), seq_lens.data_ptr(), S,
+                                    float(softmax_scale),
+                                    ctypes.byref(append) if append is not None else None,
+                                    part_o.data_ptr(), part_m.data_ptr(), part_d.data_ptr(),
+                                    _stream(q.device)))
+    return part_o, part_m, part_d
+
+
+def merge_states(part_o: torch.Tensor, part_m: torch.Tensor, part_d: torch.Tensor,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """fdec_merge_states: (out [B,Hq,D], lse [B,Hq]) from states [B,Hq,S,D] / [B,Hq,S]."""
+    lib = load_library()
+    B, Hq, S, D = part_o.shape
+    for t in (part_o, part_m, part_d):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise FdecError(FDEC_ERR_INVALID_ARG, "states must be contiguous float32")
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=part_o.device)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=part_o.device)
+    _check(lib.fdec_merge_states(part_o.data_ptr(), part_m.data_ptr(), part_d.data_ptr(), B, Hq, S, D,
+                                 out.data_ptr(), _ptr(lse), _stream(part_o.device)))
+    return out, lse
+
+
+PROBE_BLOCKS = 2048
+
+
+def probe_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fdec_probe_read: stream every byte of `src` (a calibration probe)."""
+    if sink is None:
+        sink = torch.empty(PROBE_BLOCKS, dtype=torch.int32, device=src.device)
+    _check(load_library().fdec_probe_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                                          _stream(src.device)))
+    return sink
+
+
+def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """fdec_probe_copy: plain copy of src's bytes into dst (a calibration probe)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise FdecError(FDEC_ERR_INVALID_ARG, "dst smaller than src")
+    _check(load_library().fdec_probe_copy(dst.data_ptr(), src.data_ptr(), n, _stream(src.device)))
+
+
+def cascade_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table: torch.Tensor,
+                   prefix_pages: torch.Tensor, prefix_len: int, suffix_lens: torch.Tensor,
+                   splits_prefix: int, splits_suffix: int, softmax_scale: float = 0.0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   workspace: Optional[Workspace] = None):
+    """fdec_cascade_decode: shared prefix + per-request suffix, merged exactly."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    kv = make_kv(k, v, page_table)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = Workspace(cascade_workspace_size(B, Hq, kv.num_kv_heads, D, max(splits_prefix, 1),
+                                                     max(splits_suffix, 1)), q.device)
+    _check(lib.fdec_cascade_decode(q.data_ptr(), B, Hq, ctypes.byref(kv), prefix_pages.data_ptr(), prefix_len,
+                                   suffix_lens.data_ptr(), splits_prefix, splits_suffix, float(softmax_scale),
+                                   out.data_ptr(), _ptr(lse), workspace.buf.data_ptr(), workspace.nbytes,
+                                   _stream(q.device)))
+    return out, lse

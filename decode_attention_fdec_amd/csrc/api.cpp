@@ -1,0 +1,295 @@
+// libfdec C ABI: host-side validation, workspace layout and kernel dispatch.
+// Every check runs before any launch; a failing call launches nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fdec.h"
+#include "fdec_host.h"
+#include "fdec_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct WsLayout {
+    size_t cnt, pm, pd, po, total;
+};
+
+WsLayout ws_layout(int B, int Hq, int Hkv, int D, int S) {
+    WsLayout w;
+    const size_t states = (size_t)B * Hq * S;
+    w.cnt = 0;
+    w.pm = align_up(w.cnt + (size_t)B * Hkv * sizeof(int32_t));
+    w.pd = align_up(w.pm + states * sizeof(float));
+    w.po = align_up(w.pd + states * sizeof(float));
+    w.total = align_up(w.po + states * D * sizeof(float));
+    return w;
+}
+
+int check_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return FDEC_OK;
+    return fdec_fail(FDEC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int page_shift_of(int ps) {
+    if (ps <= 0 || (ps & (ps - 1))) return -1;
+    int s = 0;
+    while ((1 << s) < ps) ++s;
+    return s;
+}
+
+// Checks shared by fdec_decode, fdec_decode_partials and fdec_cascade_decode.
+int validate_common(const char *fn, const void *q, int B, int Hq, const fdec_kv *kv,
+                    const int32_t *seq_lens, float softmax_scale) {
+    if (!kv) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: kv is NULL", fn);
+    if (B < 0) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (Hq < 1 || kv->num_kv_heads < 1)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: Hq = %d and Hkv = %d must be >= 1", fn, Hq, kv->num_kv_heads);
+    if (Hq % kv->num_kv_heads != 0)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: Hq = %d is not a multiple of Hkv = %d", fn, Hq,
+                         kv->num_kv_heads);
+    const int G = Hq / kv->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: GQA group size %d not built (1, 2, 4, 8)", fn, G);
+    if (kv->head_dim != 128 && kv->head_dim != 64)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: head_dim %d not built (128, 64)", fn, kv->head_dim);
+    if (kv->dtype != FDEC_F16 && kv->dtype != FDEC_BF16)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: dtype %d not built (fp16 = 0, bf16 = 1)", fn, kv->dtype);
+    if (kv->page_size < 0 || kv->page_size % 16 != 0)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: page_size %d must be 0 or a multiple of 16", fn,
+                         kv->page_size);
+    if (B == 0) return FDEC_OK;
+    if (!q || !kv->k || !kv->v || !seq_lens)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: q, kv->k, kv->v and seq_lens must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: q, k and v must be 16-byte aligned", fn);
+    if (kv->s_outer < 0 || kv->s_token < 0 || kv->s_head < 0 || kv->s_outer % 8 || kv->s_token % 8 ||
+        kv->s_head % 8)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: strides must be non-negative multiples of 8 elements", fn);
+    if ((int64_t)kv->s_token * 2 * 15 > INT32_MAX)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: token stride too large", fn);
+    if (kv->page_size == 0) {
+        if (kv->capacity < 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: contiguous cache needs capacity >= 1", fn);
+    } else {
+        if (!kv->page_table || kv->max_pages_per_seq < 1)
+            return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: paged cache needs page_table and max_pages_per_seq >= 1", fn);
+        const int64_t cap = (int64_t)kv->max_pages_per_seq * kv->page_size;
+        if (cap > INT32_MAX) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: capacity overflows int32", fn);
+        if (kv->capacity != 0 && kv->capacity != cap)
+            return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: capacity %d != max_pages_per_seq * page_size = %lld", fn,
+                             kv->capacity, (long long)cap);
+    }
+    if (!std::isfinite(softmax_scale))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: softmax_scale is not finite", fn);
+    return FDEC_OK;
+}
+
+int capacity_of(const fdec_kv *kv) {
+    return kv->page_size == 0 ? kv->capacity : kv->max_pages_per_seq * kv->page_size;
+}
+
+int validate_append(const char *fn, const fdec_append *a, const fdec_kv *kv) {
+    if (!a) return FDEC_OK;
+    if (!a->k_new || !a->v_new)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: append needs k_new and v_new", fn);
+    if (a->rotary_dim < 0 || a->rotary_dim % 2 || a->rotary_dim > kv->head_dim)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: rotary_dim %d must be even and in [0, head_dim]", fn,
+                         a->rotary_dim);
+    if (a->rotary_dim > 0 && (!a->rope_cos || !a->rope_sin || a->rope_max_pos < 1))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: rotary needs rope_cos, rope_sin and rope_max_pos >= 1", fn);
+    return FDEC_OK;
+}
+
+fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens, int S,
+                           float scale, const fdec_append *append) {
+    fdec::MapParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k = static_cast<const char *>(kv->k);
+    p.v = static_cast<const char *>(kv->v);
+    p.s_outer = kv->s_outer;
+    p.s_token = kv->s_token;
+    p.s_head = kv->s_head;
+    p.page_table = kv->page_size ? kv->page_table : nullptr;
+    p.max_pages = kv->max_pages_per_seq;
+    p.page_size = kv->page_size;
+    p.page_shift = page_shift_of(kv->page_size);
+    p.seq_lens = seq_lens;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = kv->num_kv_heads;
+    p.chunk = (int)fdec_split_chunk(capacity_of(kv), S);
+    if (scale == 0.0f) scale = 1.0f / std::sqrt((float)kv->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.dtype = kv->dtype;
+    p.head_dim = kv->head_dim;
+    p.mode = fdec::kPlain;
+    if (append) {
+        p.k_new = append->k_new;
+        p.v_new = append->v_new;
+        p.rotary_dim = append->rotary_dim;
+        p.rope_cos = append->rope_cos;
+        p.rope_sin = append->rope_sin;
+        p.mode = append->rotary_dim > 0 ? fdec::kAppendRope : fdec::kAppend;
+    }
+    return p;
+}
+
+int resolve_splits(const char *fn, int num_splits, int B, int Hq, const fdec_kv *kv, int *S) {
+    if (num_splits < 0 || num_splits > FDEC_MAX_SPLITS)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: num_splits %d outside [0, %d]", fn, num_splits, FDEC_MAX_SPLITS);
+    if (num_splits > 0) {
+        *S = num_splits;
+        return FDEC_OK;
+    }
+    int rc = fdec_plan(B, Hq, kv->num_kv_heads, nullptr, capacity_of(kv), kv->page_size, 256, S);
+    return rc;
+}
+
+}  // namespace
+
+void fdec_clear_error() { g_err[0] = '\0'; }
+
+int fdec_fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+extern "C" const char *fdec_status_string(int status) {
+    switch (status) {
+        case FDEC_OK: return "ok";
+        case FDEC_ERR_INVALID_ARG: return "invalid argument";
+        case FDEC_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FDEC_ERR_WORKSPACE: return "workspace missing or too small";
+        case FDEC_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char *fdec_last_error(void) { return g_err; }
+
+extern "C" size_t fdec_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_splits) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || head_dim < 1 || num_splits < 1) return 0;
+    return ws_layout(B, Hq, Hkv, head_dim, num_splits).total;
+}
+
+extern "C" int fdec_workspace_init(void *workspace, size_t bytes, void *stream) {
+    fdec_clear_error();
+    if (!workspace) return fdec_fail(FDEC_ERR_WORKSPACE, "fdec_workspace_init: workspace is NULL");
+    if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_workspace_init: workspace not 16-byte aligned");
+    // The counters sit at the start; zero the whole counter region any call could use.
+    size_t words = bytes / 4;
+    return check_hip(fdec::launch_zero_words(workspace, words, static_cast<hipStream_t>(stream)),
+                     "fdec_workspace_init");
+}
+
+extern "C" int fdec_decode(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                           int num_splits, float softmax_scale, const fdec_append *append, int fused,
+                           float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    fdec_clear_error();
+    const char *fn = "fdec_decode";
+    int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
+    if (rc) return rc;
+    if ((rc = validate_append(fn, append, kv))) return rc;
+    if (fused != 0 && fused != 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: fused must be 0 or 1", fn);
+    int S = 0;
+    if ((rc = resolve_splits(fn, num_splits, B, Hq, kv, &S))) return rc;
+    if (B == 0) return FDEC_OK;
+    if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
+    const WsLayout w = ws_layout(B, Hq, kv->num_kv_heads, kv->head_dim, S);
+    if (!workspace || workspace_bytes < w.total)
+        return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d splits, got %zu", fn,
+                         w.total, S, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+
+    char *ws = static_cast<char *>(workspace);
+    fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, append);
+    p.pm = reinterpret_cast<float *>(ws + w.pm);
+    p.pd = reinterpret_cast<float *>(ws + w.pd);
+    p.po = reinterpret_cast<float *>(ws + w.po);
+    p.s_total = S;
+    p.s_offset = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fused) {
+        p.counters = reinterpret_cast<int *>(ws + w.cnt);
+        p.out = out;
+        p.lse = lse;
+        return check_hip(fdec::launch_map(p, S, st), "fdec_decode: map+merge launch");
+    }
+    if ((rc = check_hip(fdec::launch_map(p, S, st), "fdec_decode: map launch"))) return rc;
+    return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st),
+                     "fdec_decode: merge launch");
+}
+
+extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                                    int num_splits, float softmax_scale, const fdec_append *append,
+                                    float *part_o, float *part_m, float *part_d, void *stream) {
+    fdec_clear_error();
+    const char *fn = "fdec_decode_partials";
+    int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
+    if (rc) return rc;
+    if ((rc = validate_append(fn, append, kv))) return rc;
+    if (num_splits < 1 || num_splits > FDEC_MAX_SPLITS)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: num_splits %d outside [1, %d]", fn, num_splits, FDEC_MAX_SPLITS);
+    if (B == 0) return FDEC_OK;
+    if (!part_o || !part_m || !part_d)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o, part_m and part_d must be non-NULL", fn);
+    if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_m) & 3u) || (reinterpret_cast<uintptr_t>(part_d) & 3u))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o must be 16-byte aligned", fn);
+    fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, num_splits, softmax_scale, append);
+    p.po = part_o;
+    p.pm = part_m;
+    p.pd = part_d;
+    p.s_total = num_splits;
+    p.s_offset = 0;
+    return check_hip(fdec::launch_map(p, num_splits, static_cast<hipStream_t>(stream)), "fdec_decode_partials");
+}
+
+extern "C" int fdec_merge_states(const float *part_o, const float *part_m, const float *part_d, int B, int Hq,
+                                 int S, int head_dim, float *out, float *lse, void *stream) {
+    fdec_clear_error();
+    const char *fn = "fdec_merge_states";
+    if (B < 0 || Hq < 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: need B >= 0 and Hq >= 1", fn);
+    if (S < 1 || S > FDEC_MAX_SPLITS)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: S = %d outside [1, %d]", fn, S, FDEC_MAX_SPLITS);
+    if (head_dim != 128 && head_dim != 64)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: head_dim %d not built (128, 64)", fn, head_dim);
+    if (B == 0) return FDEC_OK;
+    if (!part_o || !part_m || !part_d || !out)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o, part_m, part_d and out must be non-NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(part_o) & 7u) || (reinterpret_cast<uintptr_t>(out) & 7u))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o and out must be 8-byte aligned", fn);
+    return check_hip(fdec::launch_merge(part_o, part_m, part_d, B, Hq, S, head_dim, out, lse,
+                                        static_cast<hipStream_t>(stream)),
+                     fn);
+}
+
+extern "C" size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_dim, int splits_prefix,
+                                              int splits_suffix) {
+    if (splits_prefix < 1 || splits_suffix < 1) return 0;
+    return fdec_workspace_size(B, Hq, Hkv, head_dim, splits_prefix + splits_suffix);
+}
+
+extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *prefix_pages,
+                                   int prefix_len, const int32_t *suffix_lens, int splits_prefix,
+                                   int splits_suffix, float softmax_scale, float *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    fdec_clear_error();
+    (void)q; (void)B; (void)Hq; (void)kv; (void)prefix_pages; (void)prefix_len; (void)suffix_lens;
+    (void)splits_prefix; (void)splits_suffix; (void)softmax_scale; (void)out; (void)lse; (void)workspace;
+    (void)workspace_bytes; (void)stream;
+    return fdec_fail(FDEC_ERR_UNSUPPORTED, "fdec_cascade_decode: not built yet");
+}

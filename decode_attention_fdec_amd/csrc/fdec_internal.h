@@ -1,0 +1,58 @@
+// Launch parameters shared between the host API (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fdec {
+
+constexpr int kMapWaves = 4;                  // waves per split-KV block
+constexpr int kMapThreads = 64 * kMapWaves;   // 256 threads
+constexpr int kMergeWaves = 4;                // (b, h) pairs per merge block
+
+// What happens around the attention itself.
+enum MapMode : int {
+    kPlain = 0,       // attend to seq_lens[b] tokens
+    kAppend = 1,      // write k_new / v_new at row seq_lens[b], attend to seq_lens[b] + 1
+    kAppendRope = 2,  // as kAppend, with NeoX rotary of q and k_new
+};
+
+struct MapParams {
+    const void *q;              // [B, Hq, D]
+    const char *k, *v;          // cache base pointers (bytes)
+    int64_t s_outer, s_token, s_head;  // element strides
+    const int32_t *page_table;  // [B, max_pages] or nullptr (contiguous)
+    int max_pages;
+    int page_size;
+    int page_shift;             // log2(page_size) when a power of two, else -1
+    const int32_t *seq_lens;    // [B]
+    int B, Hq, Hkv;
+    int chunk;                  // tokens per split (multiple of 16)
+    float scale_log2;           // softmax scale * log2(e)
+    // partial states [B, Hq, s_total, D] / [B, Hq, s_total]; this launch fills
+    // split slots [s_offset, s_offset + gridDim.x)
+    float *po, *pm, *pd;
+    int s_total, s_offset;
+    // single-kernel merge: counters [B * Hkv] (nullptr = no merge in this kernel)
+    int *counters;
+    float *out, *lse;
+    // append
+    const void *k_new, *v_new;  // [B, Hkv, D]
+    const float *rope_cos, *rope_sin;  // [max_pos, rotary_dim / 2]
+    int rotary_dim;
+    int mode;                   // MapMode
+    int dtype;                  // 0 fp16, 1 bf16
+    int head_dim;
+};
+
+// Grid: (num_splits, Hkv, B).
+hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t stream);
+
+// One wave per (b, h): merges S states into out / lse.
+hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S,
+                        int head_dim, float *out, float *lse, hipStream_t stream);
+
+// Zero n 32-bit words with a kernel (no memset node, so graph capture stays safe).
+hipError_t launch_zero_words(void *ptr, size_t n_words, hipStream_t stream);
+
+}  // namespace fdec

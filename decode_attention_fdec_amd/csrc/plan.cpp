@@ -1,0 +1,163 @@
+// Split planners for libfdec. Host-only C++: no HIP calls, so it runs (and is
+// tested) on machines without a GPU.
+//
+// fdec_plan is the MI355X planner: a cost model over the batch's lengths, the
+// KV-head count and the compute-unit count, in the spirit of the runtime split
+// cost model of the lpnh.cn FlashDecoding explainer (§3, dynamic split: short
+// sequences split little, long ones a lot). fdec_plan_rules restates the
+// four-rule heuristic of the flash-attn "Inference Cookbook / 推理优化" page
+// (§6.3, with §8.2's block count) for comparison with that page's examples.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <queue>
+#include <vector>
+
+#include "../../include/fdec.h"
+#include "fdec_host.h"
+
+namespace {
+
+// Model constants for one MI355X (gfx950): 256 CUs, 8 TB/s HBM3E.
+struct CostModel {
+    double bw_total = 5.6e12;     // attainable streaming read, bytes/s
+    double bw_block = 14.0e9;     // one resident map block's sustained read, bytes/s
+    int blocks_per_cu = 2;        // resident map blocks per CU
+    double t_block = 1.5e-6;      // fixed cost of one non-empty block (ramp-up + epilogue), s
+    double t_empty = 0.05e-6;     // an empty block's slot time, s
+    double t_merge_launch = 2.0e-6;
+    double bytes_per_token = 2.0 * 128 * 2;  // K + V row of one KV head (D = 128, 2-byte)
+};
+
+double estimate(const CostModel &cm, int B, int Hq, int Hkv, const std::vector<int> &lens, int cap,
+                int S, int cu_count) {
+    const int64_t chunk = fdec_split_chunk(cap, S);
+    const int slots = cu_count * cm.blocks_per_cu;
+    // Blocks in grid dispatch order: split fastest, then KV head, then request.
+    int64_t nonempty = 0;
+    double total_bytes = 0.0;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = (lens[b] + chunk - 1) / chunk;
+        nonempty += n * Hkv;
+        total_bytes += (double)lens[b] * Hkv * cm.bytes_per_token;
+    }
+    if (nonempty == 0) return cm.t_merge_launch;
+    const double active = (double)std::min<int64_t>(nonempty, slots);
+    const double bw_eff = std::min(cm.bw_block, cm.bw_total / active);
+    // List scheduling onto `slots` identical slots, in dispatch order.
+    std::priority_queue<double, std::vector<double>, std::greater<double>> q;
+    for (int i = 0; i < slots; ++i) q.push(0.0);
+    double makespan = 0.0;
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < Hkv; ++g) {
+            for (int s = 0; s < S; ++s) {
+                int64_t lo = s * chunk, hi = std::min<int64_t>((int64_t)lens[b], lo + chunk);
+                double dur = hi > lo ? cm.t_block + (double)(hi - lo) * cm.bytes_per_token / bw_eff
+                                     : cm.t_empty;
+                double t = q.top();
+                q.pop();
+                t += dur;
+                makespan = std::max(makespan, t);
+                q.push(t);
+            }
+        }
+    }
+    makespan = std::max(makespan, total_bytes / cm.bw_total);
+    // Merge: partial states written and read once more (fp32, D + 2 values).
+    double merge = 0.0;
+    if (S > 1) {
+        double bytes = 2.0 * (double)B * Hq * S * (128 + 2) * 4.0;
+        merge = cm.t_merge_launch + bytes / cm.bw_total;
+    }
+    return makespan + merge;
+}
+
+}  // namespace
+
+extern "C" int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, int capacity,
+                         int page_size, int cu_count, int *num_splits_out) {
+    fdec_clear_error();
+    if (!num_splits_out) return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: num_splits_out is NULL");
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: need B >= 0, Hq >= 1, Hkv >= 1, Hq %% Hkv == 0");
+    if (capacity < 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: capacity must be >= 1");
+    if (page_size < 0 || page_size % 16 != 0)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: page_size must be 0 or a multiple of 16");
+    if (cu_count <= 0) cu_count = 256;
+    std::vector<int> lens(B > 0 ? B : 0, capacity);
+    if (seq_lens_host) {
+        for (int b = 0; b < B; ++b) {
+            if (seq_lens_host[b] < 0 || seq_lens_host[b] > capacity)
+                return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: seq_lens_host[%d] = %d outside [0, capacity]",
+                                 b, seq_lens_host[b]);
+            lens[b] = seq_lens_host[b];
+        }
+    }
+    if (B == 0) {
+        *num_splits_out = 1;
+        return FDEC_OK;
+    }
+    CostModel cm;
+    // Candidate split counts: every distinct chunk size, up to 64 blocks per slot.
+    const int max_s = (int)std::min<int64_t>(FDEC_MAX_SPLITS, (capacity + FDEC_CHUNK_ALIGN - 1) / FDEC_CHUNK_ALIGN);
+    const int64_t block_cap = (int64_t)64 * cu_count * cm.blocks_per_cu;
+    double best = 1e30;
+    std::vector<std::pair<int, double>> est;
+    int64_t last_chunk = -1;
+    for (int S = 1; S <= max_s; ++S) {
+        int64_t chunk = fdec_split_chunk(capacity, S);
+        if (chunk == last_chunk) continue;
+        last_chunk = chunk;
+        if ((int64_t)B * Hkv * S > block_cap && S > 1) break;
+        double t = estimate(cm, B, Hq, Hkv, lens, capacity, S, cu_count);
+        est.push_back({S, t});
+        best = std::min(best, t);
+    }
+    // The smallest split count whose estimate is within 2% of the best: fewer
+    // splits means fewer partial states to write and merge.
+    int pick = 1;
+    for (auto &e : est) {
+        if (e.second <= best * 1.02) {
+            pick = e.first;
+            break;
+        }
+    }
+    *num_splits_out = pick;
+    return FDEC_OK;
+}
+
+extern "C" int fdec_plan_rules(int B, int Hkv, int sm_count, int max_splits, int *num_splits_out) {
+    fdec_clear_error();
+    if (!num_splits_out) return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan_rules: num_splits_out is NULL");
+    if (B < 1 || Hkv < 1 || sm_count < 1 || max_splits < 1)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan_rules: arguments must be >= 1");
+    const int64_t blocks = (int64_t)B * Hkv;
+    // Rule 1: the blocks already cover 80% of the SMs.
+    if ((double)blocks >= 0.8 * sm_count) {
+        *num_splits_out = 1;
+        return FDEC_OK;
+    }
+    // Rule 3: SM efficiency of every split count; rule 4: the smallest within 85% of the best.
+    std::vector<double> eff(max_splits + 1, 0.0);
+    double best = 0.0;
+    for (int s = 1; s <= max_splits; ++s) {
+        int64_t n = blocks * s;
+        int64_t waves = (n + sm_count - 1) / sm_count;
+        eff[s] = (double)n / (double)(waves * sm_count);
+        best = std::max(best, eff[s]);
+    }
+    for (int s = 1; s <= max_splits; ++s) {
+        if (eff[s] >= 0.85 * best) {
+            *num_splits_out = s;
+            return FDEC_OK;
+        }
+    }
+    *num_splits_out = 1;
+    return FDEC_OK;
+}
+
+extern "C" int64_t fdec_split_chunk(int capacity, int num_splits) {
+    if (capacity < 1 || num_splits < 1) return 0;
+    int64_t per = ((int64_t)capacity + num_splits - 1) / num_splits;
+    return (per + FDEC_CHUNK_ALIGN - 1) / FDEC_CHUNK_ALIGN * FDEC_CHUNK_ALIGN;
+}

@@ -1,0 +1,228 @@
+/*
+ * libfdec: split-KV (FlashDecoding) decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * One query token per request attends to a long, optionally paged KV cache.
+ * The KV sequence of every (request, KV head) is cut into splits; each split
+ * produces a partial state (O~, m, d) (unnormalised output, local max, local
+ * sum of exponentials), and an exact log-sum-exp merge combines the states into
+ * the output and its LSE.
+ *
+ * Pages this interface follows (extracted web text on FlashDecoding):
+ *   [tbr8]     "FlashDecoding 与 FlashInfer 深度解析" (tbr8.org): §2.1 the three-step
+ *              split / partial / merge method; §3.2 paged KV with plan/run.
+ *   [lpnh]     lpnh.cn/news/1601758 FlashDecoding explainer: §2 stage 1 (map: per
+ *              split (O~_i, m_i, d_i)) and stage 2 (reduce: alpha merge); §3 the
+ *              runtime split cost model, the unified map+reduce kernel, GQA reuse.
+ *   [cookbook] "Inference Cookbook / 推理优化" (inference.lei6393.com):
+ *              §3.2-3.3 cache_seqlens and KV append (lengths are not advanced by the
+ *              library), §3.4 fused NeoX rotary, §3.5 softmax LSE of shape
+ *              (batch, heads), §4.2 page table with -1 padding, §6.2 num_splits
+ *              (0 = automatic), §6.3 the split heuristic, §8.2 block arithmetic.
+ *   [vllm-arch] "FlashAttention 與 FlashInfer:兩大 GPU 注意力後端" (vLLM notes): page
+ *              sizes must be multiples of 16; cascade attention computes a shared
+ *              prefix once and merges it with per-request suffix attention.
+ *
+ * Conventions for every call:
+ *   - Device pointers are caller-owned (for example torch tensors). The library
+ *     never allocates device memory, never synchronises, and launches only on
+ *     the caller's stream (`stream` is a hipStream_t; NULL = the null stream).
+ *   - Argument validation is host-only and happens before any launch: a failing
+ *     call returns a status, launches nothing and records a message readable
+ *     with fdec_last_error() on the calling thread.
+ *   - Device data is trusted: page ids, lengths and positions out of range are
+ *     undefined behaviour (the kernels never read page-table entries past
+ *     ceil(L_b / page_size), so -1 padding is safe).
+ *   - Lengths are never modified. With an append, the new token goes to row
+ *     seq_lens[b] and attention covers seq_lens[b] + 1 tokens; the caller bumps
+ *     the lengths afterwards ([cookbook] §3.2).
+ *   - Scores are s_j = scale * q . k_j; lse = ln sum_j exp(s_j) (natural log);
+ *     out = sum_j exp(s_j - lse) v_j. A request with no tokens gives out = 0,
+ *     lse = -inf.
+ *   - Query head h reads KV head h / (Hq / Hkv) (consecutive GQA groups).
+ *   - Calls that share a workspace must not overlap in time (same stream, or
+ *     ordered by events).
+ */
+#ifndef FDEC_H
+#define FDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FDEC_OK = 0,
+    FDEC_ERR_INVALID_ARG = 1, /* malformed arguments (NULL, negative, misaligned, page size) */
+    FDEC_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, dtype, GQA group size */
+    FDEC_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than fdec_workspace_size() */
+    FDEC_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} fdec_status;
+
+typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1 } fdec_dtype;
+
+/* Largest num_splits accepted by any call. */
+#define FDEC_MAX_SPLITS 256
+/* Split chunks are whole multiples of this many tokens. */
+#define FDEC_CHUNK_ALIGN 16
+
+/*
+ * One KV cache; K and V share geometry and element type. Rows are head_dim
+ * contiguous elements (D stride 1). Layout (NHD, [cookbook] §3.1, §4.2):
+ *   page_size == 0: contiguous, element (b, t, g, d) at b*s_outer + t*s_token + g*s_head + d,
+ *                   t < capacity (the per-request row count, max_seqlen);
+ *   page_size  > 0: a page pool, element (p, slot, g, d) at
+ *                   p*s_outer + slot*s_token + g*s_head + d; logical token j of
+ *                   request b is in page page_table[b*max_pages_per_seq + j/page_size],
+ *                   slot j % page_size. page_size must be a multiple of 16
+ *                   ([vllm-arch] block size rule). capacity must be 0 or
+ *                   max_pages_per_seq * page_size.
+ * k and v must be 16-byte aligned and every stride a multiple of 8 elements.
+ * They are written only by an append (one row per request and KV head).
+ */
+typedef struct fdec_kv {
+    void *k;
+    void *v;
+    int dtype;        /* fdec_dtype: fp16 or bf16 (q has the same dtype) */
+    int num_kv_heads; /* Hkv */
+    int head_dim;     /* D: 128 (64 is also built) */
+    int page_size;    /* 0 = contiguous */
+    int capacity;     /* contiguous: rows per request; paged: 0 or max_pages_per_seq*page_size */
+    int64_t s_outer, s_token, s_head; /* element strides */
+    const int32_t *page_table;        /* device [B, max_pages_per_seq] int32, -1 = unused */
+    int max_pages_per_seq;
+} fdec_kv;
+
+/*
+ * Optional KV append with fused GPT-NeoX rotary ([cookbook] §3.3-3.4). For each
+ * request b with c = seq_lens[b]: k row c of every KV head <- rope(k_new[b,g], c)
+ * rounded once (nearest-even) to the cache dtype; v row c <- v_new[b,g] bit copy;
+ * the query is rotated by the same position in fp32 before attention. Only q and
+ * k are rotated, never v. rotary_dim == 0 appends without rotation. Pairs are
+ * (i, i + rotary_dim/2) for i < rotary_dim/2; dims >= rotary_dim are untouched.
+ */
+typedef struct fdec_append {
+    const void *k_new;    /* device [B, Hkv, D], cache dtype, contiguous */
+    const void *v_new;    /* device [B, Hkv, D] */
+    const float *rope_cos; /* device [rope_max_pos, rotary_dim/2] fp32, or NULL if rotary_dim == 0 */
+    const float *rope_sin;
+    int rotary_dim;       /* 0 or even, <= head_dim */
+    int rope_max_pos;     /* rows of the tables; seq_lens[b] < rope_max_pos (device data, trusted) */
+} fdec_append;
+
+/* Short text for a status code. Never NULL. */
+const char *fdec_status_string(int status);
+
+/* Detail message of the most recent failing call on this thread ("" if none). */
+const char *fdec_last_error(void);
+
+/*
+ * Split planner, MI355X cost model ([lpnh] §3 dynamic split: a runtime cost
+ * model over batch, heads, lengths and compute-unit count). Host only, no HIP
+ * calls. seq_lens_host: [B] attended lengths on the host, or NULL to assume
+ * every request uses the full capacity. cu_count: compute units to fill (256
+ * on MI355X; <= 0 means 256). Writes num_splits in [1, FDEC_MAX_SPLITS].
+ */
+int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, int capacity, int page_size,
+              int cu_count, int *num_splits_out);
+
+/*
+ * The four-rule split heuristic as the flash-attn cookbook states it
+ * ([cookbook] §6.3 with §8.2's block count B*Hkv*num_splits): no split when the
+ * blocks already cover 80% of the SMs; otherwise the SM efficiency
+ * n/(ceil(n/SMs)*SMs) of n = B*Hkv*s blocks is computed for s = 1..max_splits
+ * and the smallest s within 85% of the best is chosen. Kept for comparison
+ * with the page's examples; fdec_plan is the MI355X planner. Host only.
+ */
+int fdec_plan_rules(int B, int Hkv, int sm_count, int max_splits, int *num_splits_out);
+
+/*
+ * Tokens per split for a call with this capacity and num_splits:
+ * chunk = 16 * ceil(ceil(capacity / num_splits) / 16). Split s of request b
+ * covers tokens [s*chunk, min((s+1)*chunk, L_b)) and is empty past L_b
+ * ([cookbook] §6.1: equal contiguous KV ranges). Returns 0 on bad arguments.
+ */
+int64_t fdec_split_chunk(int capacity, int num_splits);
+
+/* Bytes of workspace fdec_decode needs for these sizes (num_splits >= 1). */
+size_t fdec_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_splits);
+
+/*
+ * Prepare a fresh workspace: zeroes the arrival counters the single-kernel
+ * (fused) path uses, with a kernel on `stream`. Needed once per workspace
+ * allocation; every completed fdec_decode call leaves the counters at zero.
+ */
+int fdec_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Decode attention for B requests ([tbr8] §2.1; [lpnh] §2).
+ *   q          device [B, Hq, D], kv->dtype, contiguous, 16-byte aligned.
+ *   seq_lens   device [B] int32: attended lengths, or (with append) cache_seqlens
+ *              before the append. Never modified.
+ *   num_splits >= 1 splits per (request, KV head); 0 = planned from capacity alone
+ *              with fdec_plan (no device read), as num_splits=0 in [cookbook] §6.2.
+ *   softmax_scale 0 => 1/sqrt(D).
+ *   append     NULL or an fdec_append (the caches in *kv are then written).
+ *   fused      0 = map kernel + merge kernel; 1 = one kernel whose last-arriving
+ *              block per (request, KV head) merges ([lpnh] §3 unified kernel).
+ *              Both give bitwise identical results.
+ *   out        device [B, Hq, D] fp32.  lse: device [B, Hq] fp32, or NULL.
+ *   workspace  device, >= fdec_workspace_size(B, Hq, Hkv, D, splits used) bytes,
+ *              initialised once with fdec_workspace_init when fused = 1.
+ */
+int fdec_decode(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                int num_splits, float softmax_scale, const fdec_append *append, int fused,
+                float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The map stage alone ([lpnh] §2 stage 1): writes every split's partial state
+ * for each (b, h) and split s < num_splits (num_splits >= 1 here):
+ *   part_o [B, Hq, num_splits, D] fp32  O~ = sum_j exp(s_j - m) v_j over the split,
+ *   part_m [B, Hq, num_splits]    fp32  m  = max_j s_j (natural-log units),
+ *   part_d [B, Hq, num_splits]    fp32  d  = sum_j exp(s_j - m);
+ * an empty split is (0, -inf, 0). Splits follow fdec_split_chunk. Feeding the
+ * states to fdec_merge_states gives fdec_decode's result; a caller may also
+ * merge states from several devices (decode context parallelism).
+ */
+int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                         int num_splits, float softmax_scale, const fdec_append *append,
+                         float *part_o, float *part_m, float *part_d, void *stream);
+
+/*
+ * The reduce stage ([lpnh] §2 stage 2; [tbr8] §2.1 step 3): for each (b, h),
+ * m = max_i m_i, alpha_i = exp(m_i - m) (0 for an empty state), d = sum alpha_i d_i,
+ * out = sum alpha_i O~_i / d, lse = m + ln d; all states empty gives out = 0,
+ * lse = -inf. Inputs as written by fdec_decode_partials ([B, Hq, S, D], [B, Hq, S],
+ * [B, Hq, S], fp32, contiguous); states need not use a true local max: any
+ * reference m_i with O~_i, d_i scaled to it merges identically. lse may be NULL.
+ * 1 <= S <= FDEC_MAX_SPLITS.
+ */
+int fdec_merge_states(const float *part_o, const float *part_m, const float *part_d, int B, int Hq,
+                      int S, int head_dim, float *out, float *lse, void *stream);
+
+/*
+ * Cascade decode with a shared prefix ([vllm-arch] cascade attention): all B
+ * requests share the first prefix_len tokens, stored once in the pages
+ * prefix_pages[0 .. ceil(prefix_len/page_size)); request b then has
+ * suffix_lens[b] tokens of its own in kv->page_table row b. The prefix is read
+ * once for all requests (matrix-core kernel over the B*G query rows of each KV
+ * head), the suffixes by the split-KV kernel, and one merge combines both:
+ * the result equals fdec_decode over the concatenated [prefix; suffix]
+ * sequence. kv must be paged. splits_prefix / splits_suffix >= 1 (0 = planned).
+ * Workspace: fdec_cascade_workspace_size().
+ */
+int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv,
+                        const int32_t *prefix_pages, int prefix_len, const int32_t *suffix_lens,
+                        int splits_prefix, int splits_suffix, float softmax_scale, float *out,
+                        float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for fdec_cascade_decode with these split counts (both >= 1). */
+size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_dim, int splits_prefix,
+                                   int splits_suffix);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDEC_H */

@@ -18,3 +18,16 @@ def oracle_lib():
 
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(scope="session")
+def fdec():
+    """The HIP library's Python binding, built in-tree first if nothing is built."""
+    import decode_attention_fdec_amd as f
+
+    if not os.path.exists(f.LIB_PATH):
+        from decode_attention_fdec_amd import build
+
+        build.build()
+    f.load_library()
+    return f

@@ -1,0 +1,171 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before any launch (no GPU needed: every call here fails
+validation, so nothing reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_fdec_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(fdec_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["fdec_plan", "fdec_decode", "fdec_merge_states", "fdec_decode_partials",
+                     "fdec_cascade_decode", "fdec_workspace_size", "fdec_workspace_init",
+                     "fdec_status_string", "fdec_last_error", "fdec_plan_rules", "fdec_split_chunk"]:
+        assert required in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_declared_symbol(fdec, name):
+    lib = ctypes.CDLL(F.LIB_PATH)
+    assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_status_strings(fdec):
+    lib = F.load_library()
+    for s in range(5):
+        assert lib.fdec_status_string(s)
+    assert lib.fdec_status_string(99) == b"unknown status"
+
+
+# Fake, 256-byte aligned "device" addresses: validation must reject the call
+# before anything dereferences them.
+FAKE = 0x10000
+
+
+def kv_struct(**over):
+    kv = F.FdecKV()
+    kv.k, kv.v = FAKE, FAKE + 0x1000
+    kv.dtype, kv.num_kv_heads, kv.head_dim = F.FDEC_BF16, 8, 128
+    kv.page_size, kv.capacity = 0, 4096
+    kv.s_outer, kv.s_token, kv.s_head = 4096 * 8 * 128, 8 * 128, 128
+    kv.page_table, kv.max_pages_per_seq = None, 0
+    for k, v in over.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def call_decode(kv, B=1, Hq=32, num_splits=4, ws_bytes=1 << 30, append=None, fused=0, q=FAKE,
+                seq=FAKE, out=FAKE, scale=0.0, ws=FAKE):
+    lib = F.load_library()
+    return lib.fdec_decode(q, B, Hq, ctypes.byref(kv), seq, num_splits, scale,
+                           ctypes.byref(append) if append else None, fused, out, None, ws, ws_bytes,
+                           None)
+
+
+def last_error():
+    return F.load_library().fdec_last_error().decode()
+
+
+@pytest.mark.parametrize("ps", [8, 24, 1, -16])
+def test_page_size_must_be_multiple_of_16(fdec, ps):
+    kv = kv_struct(page_size=ps, page_table=FAKE, max_pages_per_seq=64, capacity=0)
+    assert call_decode(kv) == F.FDEC_ERR_INVALID_ARG
+    assert "page_size" in last_error()
+
+
+def test_head_ratio_must_divide(fdec):
+    assert call_decode(kv_struct(num_kv_heads=5), Hq=32) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_unsupported_shapes_are_reported_as_unsupported(fdec):
+    assert call_decode(kv_struct(head_dim=96)) == F.FDEC_ERR_UNSUPPORTED
+    assert call_decode(kv_struct(head_dim=256)) == F.FDEC_ERR_UNSUPPORTED
+    assert call_decode(kv_struct(dtype=7)) == F.FDEC_ERR_UNSUPPORTED
+    assert call_decode(kv_struct(num_kv_heads=2), Hq=32) == F.FDEC_ERR_UNSUPPORTED  # G = 16
+
+
+def test_null_and_misaligned_pointers(fdec):
+    assert call_decode(kv_struct(), q=None) == F.FDEC_ERR_INVALID_ARG
+    assert call_decode(kv_struct(), seq=None) == F.FDEC_ERR_INVALID_ARG
+    assert call_decode(kv_struct(), out=None) == F.FDEC_ERR_INVALID_ARG
+    assert call_decode(kv_struct(k=FAKE + 2)) == F.FDEC_ERR_INVALID_ARG
+    assert call_decode(kv_struct(s_token=8 * 128 + 4)) == F.FDEC_ERR_INVALID_ARG
+    assert call_decode(kv_struct(), q=FAKE + 8) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_bad_split_counts(fdec):
+    assert call_decode(kv_struct(), num_splits=-1) == F.FDEC_ERR_INVALID_ARG
+    assert call_decode(kv_struct(), num_splits=F.MAX_SPLITS + 1) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_is_reported_not_allocated(fdec):
+    need = F.workspace_size(1, 32, 8, 128, 4)
+    assert need > 0
+    assert call_decode(kv_struct(), ws_bytes=need - 1) == F.FDEC_ERR_WORKSPACE
+    assert str(need) in last_error()
+    assert call_decode(kv_struct(), ws=None) == F.FDEC_ERR_WORKSPACE
+
+
+def test_paged_cache_checks(fdec):
+    kv = kv_struct(page_size=16, page_table=None, max_pages_per_seq=64, capacity=0)
+    assert call_decode(kv) == F.FDEC_ERR_INVALID_ARG
+    kv = kv_struct(page_size=16, page_table=FAKE, max_pages_per_seq=64, capacity=1000)
+    assert call_decode(kv) == F.FDEC_ERR_INVALID_ARG  # capacity != pages * page_size
+
+
+def test_append_checks(fdec):
+    a = F.FdecAppend()
+    a.k_new, a.v_new, a.rotary_dim = FAKE, FAKE, 3
+    assert call_decode(kv_struct(), append=a) == F.FDEC_ERR_INVALID_ARG
+    a.rotary_dim = 64  # rotary without tables
+    assert call_decode(kv_struct(), append=a) == F.FDEC_ERR_INVALID_ARG
+    a.rotary_dim, a.k_new = 0, None
+    assert call_decode(kv_struct(), append=a) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_bad_fused_flag_and_scale(fdec):
+    assert call_decode(kv_struct(), fused=2) == F.FDEC_ERR_INVALID_ARG
+    assert call_decode(kv_struct(), scale=float("nan")) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_merge_states_validation(fdec):
+    lib = F.load_library()
+    assert lib.fdec_merge_states(FAKE, FAKE, FAKE, 1, 32, 0, 128, FAKE, None, None) == F.FDEC_ERR_INVALID_ARG
+    assert lib.fdec_merge_states(FAKE, FAKE, FAKE, 1, 32, 300, 128, FAKE, None, None) == F.FDEC_ERR_INVALID_ARG
+    assert lib.fdec_merge_states(FAKE, FAKE, FAKE, 1, 32, 4, 80, FAKE, None, None) == F.FDEC_ERR_UNSUPPORTED
+    assert lib.fdec_merge_states(None, FAKE, FAKE, 1, 32, 4, 128, FAKE, None, None) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_partials_validation(fdec):
+    lib = F.load_library()
+    kv = kv_struct()
+    assert lib.fdec_decode_partials(FAKE, 1, 32, ctypes.byref(kv), FAKE, 0, 0.0, None, FAKE, FAKE, FAKE,
+                                    None) == F.FDEC_ERR_INVALID_ARG
+    assert lib.fdec_decode_partials(FAKE, 1, 32, ctypes.byref(kv), FAKE, 4, 0.0, None, None, FAKE, FAKE,
+                                    None) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(fdec):
+    # B = 0 returns OK without touching any pointer
+    assert call_decode(kv_struct(), B=0, q=None, seq=None, out=None, ws=None) == F.FDEC_OK
+
+
+def test_workspace_size_grows_with_splits(fdec):
+    a = F.workspace_size(32, 32, 8, 128, 8)
+    b = F.workspace_size(32, 32, 8, 128, 16)
+    assert b > a >= 32 * 32 * 8 * (128 + 2) * 4
+    assert F.workspace_size(1, 32, 8, 128, 0) == 0
+
+
+def test_split_chunk_rule(fdec):
+    assert F.split_chunk(1024, 4) == 256
+    assert F.split_chunk(131072, 16) == 8192
+    assert F.split_chunk(100, 3) == 48  # ceil(100/3) = 34 -> 48
+    assert F.split_chunk(5, 1) == 16
+    assert F.split_chunk(0, 4) == 0
