@@ -121,19 +121,35 @@ __device__ __forceinline__ void merge_states_wave(const float *po, const float *
         dsum += a[k] * dv[k];
     }
     dsum = wave_sum(dsum);
+    // Rows are fetched 16 at a time (all loads of a batch in flight before the
+    // first use); alpha_s is broadcast from lane s % 64 of register a[s / 64].
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int n = min(64, S - 64 * k);
-        for (int j = 0; j < n; ++j) {
-            const float alpha = readlane(a[k], j);
-            const float *row = po + (int64_t)(64 * k + j) * D + lane * NV;
-            if constexpr (NV == 2) {
-                const float2 x = *reinterpret_cast<const float2 *>(row);
-                o[0] += alpha * x.x;
-                o[1] += alpha * x.y;
-            } else {
+        for (int j0 = 0; j0 < n; j0 += 16) {
+            float x[16][NV];
 #pragma unroll
-                for (int e = 0; e < NV; ++e) o[e] += alpha * row[e];
+            for (int u = 0; u < 16; ++u) {
+                const float *row = po + (int64_t)(64 * k + j0 + u) * D + lane * NV;
+                if (j0 + u < n) {
+                    if constexpr (NV == 2) {
+                        const float2 t = *reinterpret_cast<const float2 *>(row);
+                        x[u][0] = t.x;
+                        x[u][1] = t.y;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < NV; ++e) x[u][e] = row[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) x[u][e] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float alpha = (j0 + u < n) ? readlane(a[k], min(j0 + u, 63)) : 0.0f;
+#pragma unroll
+                for (int e = 0; e < NV; ++e) o[e] += alpha * x[u][e];
             }
         }
     }

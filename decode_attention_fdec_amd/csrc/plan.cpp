@@ -18,58 +18,61 @@
 
 namespace {
 
-// Model constants for one MI355X (gfx950): 256 CUs, 8 TB/s HBM3E.
+// Model constants for one MI355X (gfx950: 256 CUs, 8 TB/s HBM3E), fitted to
+// measurements of this library's map kernel (two-kernel path).
 struct CostModel {
-    double bw_total = 5.6e12;     // attainable streaming read, bytes/s
-    double bw_block = 14.0e9;     // one resident map block's sustained read, bytes/s
+    double bw_total = 5.4e12;     // sustained aggregate KV read rate, bytes/s
+    double bw_block = 35.0e9;     // one map block's ceiling, bytes/s
     int blocks_per_cu = 2;        // resident map blocks per CU
-    double t_block = 1.5e-6;      // fixed cost of one non-empty block (ramp-up + epilogue), s
-    double t_empty = 0.05e-6;     // an empty block's slot time, s
-    double t_merge_launch = 2.0e-6;
+    double t_block = 3.0e-6;      // fixed cost of a non-empty block (q load, epilogue), s
+    double t_empty = 0.1e-6;      // an empty block, s
+    double t_merge = 3.0e-6;      // merge kernel launch and latency, s
     double bytes_per_token = 2.0 * 128 * 2;  // K + V row of one KV head (D = 128, 2-byte)
 };
+
+// Fluid model of one launch: blocks enter free slots in dispatch order (split
+// fastest, then KV head, then request); the active blocks share the aggregate
+// bandwidth equally, each capped at bw_block. A block's fixed cost is charged
+// as bytes at its capped rate. Every active block advances at the same rate, so
+// completions happen in order of (progress at entry + bytes): a min-heap of
+// those thresholds gives the schedule in O(n log n).
+double makespan(const CostModel &cm, const std::vector<double> &bytes, int slots) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> heap;
+    size_t next = 0;
+    double progress = 0.0, t = 0.0;
+    while (next < bytes.size() && (int)heap.size() < slots) heap.push(progress + bytes[next++]);
+    while (!heap.empty()) {
+        const double n = (double)heap.size();
+        const double rate = std::min(cm.bw_block, cm.bw_total / n);
+        const double target = heap.top();
+        heap.pop();
+        t += (target - progress) / rate;
+        progress = target;
+        if (next < bytes.size()) heap.push(progress + bytes[next++]);
+    }
+    return t;
+}
 
 double estimate(const CostModel &cm, int B, int Hq, int Hkv, const std::vector<int> &lens, int cap,
                 int S, int cu_count) {
     const int64_t chunk = fdec_split_chunk(cap, S);
-    const int slots = cu_count * cm.blocks_per_cu;
-    // Blocks in grid dispatch order: split fastest, then KV head, then request.
-    int64_t nonempty = 0;
-    double total_bytes = 0.0;
-    for (int b = 0; b < B; ++b) {
-        int64_t n = (lens[b] + chunk - 1) / chunk;
-        nonempty += n * Hkv;
-        total_bytes += (double)lens[b] * Hkv * cm.bytes_per_token;
-    }
-    if (nonempty == 0) return cm.t_merge_launch;
-    const double active = (double)std::min<int64_t>(nonempty, slots);
-    const double bw_eff = std::min(cm.bw_block, cm.bw_total / active);
-    // List scheduling onto `slots` identical slots, in dispatch order.
-    std::priority_queue<double, std::vector<double>, std::greater<double>> q;
-    for (int i = 0; i < slots; ++i) q.push(0.0);
-    double makespan = 0.0;
+    std::vector<double> bytes;
+    bytes.reserve((size_t)B * Hkv * S);
     for (int b = 0; b < B; ++b) {
         for (int g = 0; g < Hkv; ++g) {
             for (int s = 0; s < S; ++s) {
                 int64_t lo = s * chunk, hi = std::min<int64_t>((int64_t)lens[b], lo + chunk);
-                double dur = hi > lo ? cm.t_block + (double)(hi - lo) * cm.bytes_per_token / bw_eff
-                                     : cm.t_empty;
-                double t = q.top();
-                q.pop();
-                t += dur;
-                makespan = std::max(makespan, t);
-                q.push(t);
+                if (hi > lo)
+                    bytes.push_back((double)(hi - lo) * cm.bytes_per_token + cm.t_block * cm.bw_block);
+                else
+                    bytes.push_back(cm.t_empty * cm.bw_block);
             }
         }
     }
-    makespan = std::max(makespan, total_bytes / cm.bw_total);
+    double t = makespan(cm, bytes, cu_count * cm.blocks_per_cu);
     // Merge: partial states written and read once more (fp32, D + 2 values).
-    double merge = 0.0;
-    if (S > 1) {
-        double bytes = 2.0 * (double)B * Hq * S * (128 + 2) * 4.0;
-        merge = cm.t_merge_launch + bytes / cm.bw_total;
-    }
-    return makespan + merge;
+    if (S > 1) t += cm.t_merge + 2.0 * (double)B * Hq * S * (128 + 2) * 4.0 / cm.bw_total;
+    return t;
 }
 
 }  // namespace

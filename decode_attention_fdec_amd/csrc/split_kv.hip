@@ -25,19 +25,35 @@
 
 namespace fdec {
 
+// Register tiles in flight per wave and the waves per SIMD the kernel is
+// compiled for, by GQA group size (D = 128): more tiles hide more latency,
+// fewer registers allow more resident waves.
+#ifndef FDEC_NBUF_G4
+#define FDEC_NBUF_G4 2
+#endif
+#ifndef FDEC_OCC_G4
+#define FDEC_OCC_G4 2
+#endif
+template <int G, int D> struct MapConfig {
+    static constexpr int nbuf = (G >= 8 && D >= 128) ? 2 : (G == 4 && D >= 128) ? FDEC_NBUF_G4 : 3;
+    static constexpr int occ = (G >= 8 && D >= 128) ? 1 : (G == 4 && D >= 128) ? FDEC_OCC_G4 : 2;
+};
+
 template <int DT, int D, int G, bool PAGED, int MODE>
-__global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map_kernel(const MapParams p) {
+__global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kernel(const MapParams p) {
     constexpr int NCH = D / 64;           // 16-byte pieces per lane per row
     constexpr int NE = NCH * 8;           // elements per lane per row
     constexpr int NQ = NCH * 4;           // packed dwords per lane per row
     constexpr int NR = (G >= 8) ? 1 : 2;  // 8-row groups per tile
     constexpr int TT = 8 * NR;            // tokens per tile
     constexpr bool QF32 = (MODE == kAppendRope);
+    constexpr int NBUF = MapConfig<G, D>::nbuf;
     using E = Elem<DT>;
 
     __shared__ float sm_acc[kMapWaves][G][D];
     __shared__ float sm_m[kMapWaves][G];
     __shared__ float sm_l[kMapWaves][G];
+    __shared__ float sm_t[kMapWaves][G];
     __shared__ float sm_vec[(MODE == kAppendRope) ? (G + 1) * D : 1];
     __shared__ int sm_flag;
 
@@ -142,10 +158,19 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
     }
 
     // ---------------------------------------------------------------- stream the split
-    float m[G], l[G], acc[G][NE];
+    // Online softmax with a lazily moved reference: scores are in the log2
+    // domain; m is the reference every exponential is taken against and only
+    // moves (rescaling l and acc) when a score exceeds it by more than kTau, so
+    // p <= 2^kTau. tmax tracks the true maximum for the state written out.
+    // Rows of a lane group that have seen no token keep m = kFloor (finite), so
+    // masked scores (-inf) give p = 0 without a NaN.
+    constexpr float kTau = 8.0f;
+    constexpr float kFloor = -1.0e30f;
+    float m[G], tmax[G], l[G], acc[G][NE];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        m[h] = kNegInf;
+        m[h] = kFloor;
+        tmax[h] = kNegInf;
         l[h] = 0.0f;
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[h][e] = 0.0f;
@@ -153,6 +178,9 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
 
     const int ntok = t_end - t_begin;
     const int ntiles = ntok > 0 ? (ntok + TT - 1) / TT : 0;
+    // tiles wv, wv + 4, wv + 8, ... of this split belong to wave wv (wave-uniform values)
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int n_my = ntiles > wvu ? (ntiles - wvu + kMapWaves - 1) / kMapWaves : 0;
     const char *kbase = p.k;
     const char *vbase = p.v;
     const uint32_t tok_bytes = (uint32_t)(p.s_token * 2);
@@ -161,18 +189,29 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
         uint4 k[NR][NCH];
         uint4 v[NR][NCH];
     };
+    auto tile_t0 = [&](int i) { return t_begin + (wvu + i * kMapWaves) * TT; };
 
-    // Issue the loads of the tile starting at token t0 (rows past t_end clamp to
-    // the last valid row; their scores are masked later).
+    // Per-lane byte offsets of this lane's rows within a tile: loop-invariant,
+    // except in the split's last tile, whose rows past t_end clamp to its last
+    // valid row (their scores are masked later).
+    const int last_t0 = t_begin + (ntiles - 1) * TT;
+    const int nvalid_last = t_end - last_t0;
+    uint32_t off_full[NR], off_last[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        off_full[j] = (uint32_t)(8 * j + ra) * tok_bytes + (uint32_t)cb * 16u;
+        off_last[j] = (uint32_t)min(8 * j + ra, nvalid_last - 1) * tok_bytes + (uint32_t)cb * 16u;
+    }
+
+    // Issue the loads of the tile starting at token t0.
     auto issue = [&](Tile &T, int t0) {
-        const int nvalid = t_end - t0;
         const int64_t base = row_offset(t0);
         const char *kb = kbase + base * 2;
         const char *vb = vbase + base * 2;
+        const bool last = (t0 == last_t0);
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            const int r = min(8 * j + ra, nvalid - 1);
-            const uint32_t off = (uint32_t)r * tok_bytes + (uint32_t)cb * 16u;
+            const uint32_t off = last ? off_last[j] : off_full[j];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 T.k[j][c] = *reinterpret_cast<const uint4 *>(kb + off + c * 128);
@@ -200,8 +239,35 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
 #pragma unroll
                     for (int i = 0; i < NQ; ++i) s = E::dot2(qp[h][i], kw[i], s);
                 }
-                s = sum8(s) * p.scale_log2;
-                sc[j][h] = (8 * j + ra < nvalid) ? s : kNegInf;
+                sc[j][h] = sum8(s) * p.scale_log2;
+            }
+        }
+        if (nvalid < TT) {  // only a split's last tile is partial (wave-uniform branch)
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    if (8 * j + ra >= nvalid) sc[j][h] = kNegInf;
+        }
+        float mx[G];
+        bool move = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            mx[h] = sc[0][h];
+#pragma unroll
+            for (int j = 1; j < NR; ++j) mx[h] = fmaxf(mx[h], sc[j][h]);
+            tmax[h] = fmaxf(tmax[h], mx[h]);
+            move |= mx[h] > m[h] + kTau;
+        }
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {  // rare after the first tiles
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float mn = fmaxf(m[h], mx[h]);
+                const float alpha = fexp2(m[h] - mn);
+                m[h] = mn;
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) acc[h][e] *= alpha;
             }
         }
         float vf[NR][NE];
@@ -216,23 +282,15 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float mx = sc[0][h];
-#pragma unroll
-            for (int j = 1; j < NR; ++j) mx = fmaxf(mx, sc[j][h]);
-            const float mn = fmaxf(m[h], mx);
-            const float mu = (mn == kNegInf) ? 0.0f : mn;
-            const float alpha = fexp2(m[h] - mu);
-            float pj[NR], ps = 0.0f;
+            float pj[NR];
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
-                pj[j] = fexp2(sc[j][h] - mu);
-                ps += pj[j];
+                pj[j] = fexp2(sc[j][h] - m[h]);
+                l[h] += pj[j];
             }
-            l[h] = l[h] * alpha + ps;
-            m[h] = mn;
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
-                float a = acc[h][e] * alpha;
+                float a = acc[h][e];
 #pragma unroll
                 for (int j = 0; j < NR; ++j) a = fmaf(pj[j], vf[j][e], a);
                 acc[h][e] = a;
@@ -240,24 +298,26 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
         }
     };
 
-    if (ntiles > 0) {
-        // tiles wv, wv + 4, wv + 8, ... of this split belong to this wave
-        int k = wv;
-        if (k < ntiles) {
-            Tile A, Bt;
-            issue(A, t_begin + k * TT);
-            while (true) {
-                const int k1 = k + kMapWaves;
-                if (k1 < ntiles) issue(Bt, t_begin + k1 * TT);
-                compute(A, t_begin + k * TT);
-                if (k1 >= ntiles) break;
-                const int k2 = k1 + kMapWaves;
-                if (k2 < ntiles) issue(A, t_begin + k2 * TT);
-                compute(Bt, t_begin + k1 * TT);
-                if (k2 >= ntiles) break;
-                k = k2;
+    if (n_my > 0) {
+        // NBUF register tiles rotate: while one is computed, the next NBUF - 1
+        // are in flight (under load the memory latency is about two tiles'
+        // compute time). Loads are unconditional -- indices past the end
+        // re-issue the last tile -- so every wait count in the loop is static.
+        Tile T[NBUF];
+        const int last = n_my - 1;
+#pragma unroll
+        for (int u = 0; u < NBUF - 1; ++u) issue(T[u], tile_t0(min(u, last)));
+        int i = 0;
+        for (; i + NBUF <= n_my; i += NBUF) {
+#pragma unroll
+            for (int u = 0; u < NBUF; ++u) {
+                issue(T[(u + NBUF - 1) % NBUF], tile_t0(min(i + u + NBUF - 1, last)));
+                compute(T[u], tile_t0(i + u));
             }
         }
+#pragma unroll
+        for (int u = 0; u < NBUF - 1; ++u)
+            if (i + u < n_my) compute(T[u], tile_t0(i + u));
     }
 
     // ---------------------------------------------------------------- merge lane rows, then waves
@@ -267,9 +327,9 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
         for (int h = 0; h < G; ++h) {
             const float mo = shfl_xor(m[h], step);
             const float lo = shfl_xor(l[h], step);
+            tmax[h] = fmaxf(tmax[h], shfl_xor(tmax[h], step));
             const float mn = fmaxf(m[h], mo);
-            const float mu = (mn == kNegInf) ? 0.0f : mn;
-            const float as = fexp2(m[h] - mu), ao = fexp2(mo - mu);
+            const float as = fexp2(m[h] - mn), ao = fexp2(mo - mn);
             l[h] = l[h] * as + lo * ao;
             m[h] = mn;
 #pragma unroll
@@ -289,29 +349,33 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
             if (cb == 0) {
                 sm_m[wv][h] = m[h];
                 sm_l[wv][h] = l[h];
+                sm_t[wv][h] = tmax[h];
             }
         }
     }
     __syncthreads();
 
+    // Block state per head, re-expressed against the true maximum T of the split:
+    // O~ = sum_w 2^(m_w - T) acc_w, d = sum_w 2^(m_w - T) l_w (each factor <= 2^kTau).
     const int64_t slot = p.s_offset + split;
     for (int i = tid; i < G * D; i += kMapThreads) {
         const int h = i / D, d = i - h * D;
-        float M = sm_m[0][h];
+        float T = sm_t[0][h];
 #pragma unroll
-        for (int w = 1; w < kMapWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-        const float mu = (M == kNegInf) ? 0.0f : M;
+        for (int w = 1; w < kMapWaves; ++w) T = fmaxf(T, sm_t[w][h]);
         float o = 0.0f, lsum = 0.0f;
+        if (T != kNegInf) {
 #pragma unroll
-        for (int w = 0; w < kMapWaves; ++w) {
-            const float a = fexp2(sm_m[w][h] - mu);
-            o += a * sm_acc[w][h][d];
-            lsum += a * sm_l[w][h];
+            for (int w = 0; w < kMapWaves; ++w) {
+                const float a = fexp2(sm_m[w][h] - T);
+                o += a * sm_acc[w][h][d];
+                lsum += a * sm_l[w][h];
+            }
         }
         const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
         p.po[(bh * p.s_total + slot) * D + d] = o;
         if (d == 0) {
-            p.pm[bh * p.s_total + slot] = (M == kNegInf) ? kNegInf : M * kLn2;
+            p.pm[bh * p.s_total + slot] = (T == kNegInf) ? kNegInf : T * kLn2;
             p.pd[bh * p.s_total + slot] = lsum;
         }
     }
@@ -319,10 +383,10 @@ __global__ __launch_bounds__(kMapThreads, (G >= 8 && D >= 128) ? 1 : 2) void map
     if (p.counters == nullptr) return;
 
     // ---------------------------------------------------------------- single-kernel merge
-    // Publish this block's states device-wide, count arrivals per (request, KV head);
-    // the last block to arrive merges all splits (in split order) and resets the counter.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
+    // Publish this block's states device-wide and count arrivals per
+    // (request, KV head); the last block to arrive merges all splits (in split
+    // order, with the merge kernel's code) and resets the counter.
+    __syncthreads();  // every wave's state stores are complete
     if (tid == 0) {
         int *cnt = p.counters + (int64_t)b * p.Hkv + g;
         const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
