@@ -144,6 +144,42 @@ def time_map_kernel(F, runner: Runner, steps: int):
     return sorted(a.elapsed_time(b) for a, b in ev)
 
 
+CALIB_BYTES = 256 << 20
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str) -> dict:
+    """HBM traffic of the map kernel from rocprofv3 counter csv files.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counter reads for the calibration probes: a plain read (FETCH) and a plain
+    copy (WRITE) of CALIB_BYTES each.
+    """
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        vals = [v for k, vs in d.items() if key in k for v in vs]
+        return sorted(vals)[len(vals) // 2] if vals else None
+
+    fetch_scale = CALIB_BYTES / 1024.0 / pick(f, "read_kernel")
+    write_scale = CALIB_BYTES / 1024.0 / pick(w, "copy_kernel")
+    fk, wk = pick(f, "map_kernel"), pick(w, "map_kernel")
+    return {"fetch_kib": fk, "write_kib": wk, "fetch_scale": round(fetch_scale, 4),
+            "write_scale": round(write_scale, 4),
+            "traffic_bytes": int(round((fk * fetch_scale + wk * write_scale) * 1024)),
+            "read_bytes": int(round(fk * fetch_scale * 1024)), "write_bytes": int(round(wk * write_scale * 1024)),
+            "kernel_hash": kernel_hash()}
+
+
 def pct(xs, p):
     return xs[min(len(xs) - 1, int(round(p / 100.0 * (len(xs) - 1))))]
 
@@ -214,7 +250,14 @@ def main() -> int:
     ap.add_argument("--also", default="c1,c3,c4", help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain read and a plain copy of 256 MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE csv files and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -263,6 +306,13 @@ def main() -> int:
             _t.cuda.synchronize()
             probe.append(b.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     res["probe_read_GBps"] = round(sorted(probe)[len(probe) // 2], 1)
+    if args.calibrate:
+        src = _t.empty(CALIB_BYTES, dtype=_t.uint8, device=dev)
+        dst = _t.empty(CALIB_BYTES, dtype=_t.uint8, device=dev)
+        F.probe_read(src)
+        F.probe_copy(dst, src)
+        _t.cuda.synchronize()
+        del src, dst
     res["pct_of_probe"] = round(100 * res["GBps"] / res["probe_read_GBps"], 1)
     del runner
 
