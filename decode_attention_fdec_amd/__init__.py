@@ -83,6 +83,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_cascade_decode.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, P, I, I, F, P, P, P, Z, P]
     lib.fdec_probe_read.argtypes = [P, Z, P, P]
     lib.fdec_probe_copy.argtypes = [P, P, Z, P]
+    lib.fdec_cascade_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.fdec_cascade_workspace_size.restype = Z
     lib.fdec_cascade_workspace_size.argtypes = [I, I, I, I, I, I]
     if path is None:
@@ -275,9 +276,18 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     _check(load_library().fdec_probe_copy(dst.data_ptr(), src.data_ptr(), n, _stream(src.device)))
 
 
+def cascade_plan(B: int, Hq: int, Hkv: int, prefix_len: int, capacity: int, page_size: int,
+                 cu_count: int = 256):
+    """fdec_cascade_plan: (splits_prefix, splits_suffix)."""
+    sp, ss = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load_library().fdec_cascade_plan(B, Hq, Hkv, prefix_len, capacity, page_size, cu_count,
+                                            ctypes.byref(sp), ctypes.byref(ss)))
+    return sp.value, ss.value
+
+
 def cascade_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table: torch.Tensor,
                    prefix_pages: torch.Tensor, prefix_len: int, suffix_lens: torch.Tensor,
-                   splits_prefix: int, splits_suffix: int, softmax_scale: float = 0.0,
+                   splits_prefix: int = 0, splits_suffix: int = 0, softmax_scale: float = 0.0,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    workspace: Optional[Workspace] = None):
     """fdec_cascade_decode: shared prefix + per-request suffix, merged exactly."""
@@ -288,10 +298,14 @@ def cascade_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    if splits_prefix <= 0 or splits_suffix <= 0:
+        sp, ss = cascade_plan(B, Hq, kv.num_kv_heads, prefix_len, kv.capacity, kv.page_size)
+        splits_prefix = splits_prefix if splits_prefix > 0 else sp
+        splits_suffix = splits_suffix if splits_suffix > 0 else ss
     if workspace is None:
-        workspace = Workspace(cascade_workspace_size(B, Hq, kv.num_kv_heads, D, max(splits_prefix, 1),
-                                                     max(splits_suffix, 1)), q.device)
-    _check(lib.fdec_cascade_decode(q.data_ptr(), B, Hq, ctypes.byref(kv), prefix_pages.data_ptr(), prefix_len,
+        workspace = Workspace(cascade_workspace_size(B, Hq, kv.num_kv_heads, D, splits_prefix, splits_suffix),
+                              q.device)
+    _check(lib.fdec_cascade_decode(q.data_ptr(), B, Hq, ctypes.byref(kv), _ptr(prefix_pages), prefix_len,
                                    suffix_lens.data_ptr(), splits_prefix, splits_suffix, float(softmax_scale),
                                    out.data_ptr(), _ptr(lse), workspace.buf.data_ptr(), workspace.nbytes,
                                    _stream(q.device)))

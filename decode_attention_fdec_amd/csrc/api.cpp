@@ -1,5 +1,6 @@
 // libfdec C ABI: host-side validation, workspace layout and kernel dispatch.
 // Every check runs before any launch; a failing call launches nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -90,6 +91,12 @@ int validate_common(const char *fn, const void *q, int B, int Hq, const fdec_kv 
     if (!std::isfinite(softmax_scale))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: softmax_scale is not finite", fn);
     return FDEC_OK;
+}
+
+// Prefix tokens per cascade split: a whole number of 64-token tiles.
+int64_t cascade_chunk(int prefix_len, int splits) {
+    int64_t per = ((int64_t)std::max(prefix_len, 1) + splits - 1) / splits;
+    return (per + 63) / 64 * 64;
 }
 
 int capacity_of(const fdec_kv *kv) {
@@ -283,13 +290,116 @@ extern "C" size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_d
     return fdec_workspace_size(B, Hq, Hkv, head_dim, splits_prefix + splits_suffix);
 }
 
+extern "C" int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size,
+                                 int cu_count, int *splits_prefix_out, int *splits_suffix_out) {
+    fdec_clear_error();
+    const char *fn = "fdec_cascade_plan";
+    if (!splits_prefix_out || !splits_suffix_out)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: output pointers must be non-NULL", fn);
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || prefix_len < 0 || capacity < 1 || page_size < 16 ||
+        page_size % 16)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: bad sizes", fn);
+    if (cu_count <= 0) cu_count = 256;
+    const int rows = B * (Hq / Hkv);
+    const int row_chunks = rows > 0 ? (rows + 255) / 256 : 1;
+    int sp = (cu_count + Hkv * row_chunks - 1) / (Hkv * row_chunks);
+    sp = std::min(sp, std::max(1, prefix_len / 256));
+    sp = std::max(1, std::min(sp, FDEC_MAX_SPLITS / 2));
+    // each prefix block stages at most kPrefixPagesPerBlock - 2 page ids
+    while (sp < FDEC_MAX_SPLITS / 2) {
+        const int64_t chunk = cascade_chunk(prefix_len, sp);
+        if (chunk / page_size + 2 <= fdec::kPrefixPagesPerBlock) break;
+        ++sp;
+    }
+    int ss = 1;
+    int rc = fdec_plan(B, Hq, Hkv, nullptr, capacity, page_size, cu_count, &ss);
+    if (rc) return rc;
+    ss = std::min(ss, FDEC_MAX_SPLITS - sp);
+    *splits_prefix_out = sp;
+    *splits_suffix_out = ss;
+    return FDEC_OK;
+}
+
 extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *prefix_pages,
                                    int prefix_len, const int32_t *suffix_lens, int splits_prefix,
                                    int splits_suffix, float softmax_scale, float *out, float *lse,
                                    void *workspace, size_t workspace_bytes, void *stream) {
     fdec_clear_error();
-    (void)q; (void)B; (void)Hq; (void)kv; (void)prefix_pages; (void)prefix_len; (void)suffix_lens;
-    (void)splits_prefix; (void)splits_suffix; (void)softmax_scale; (void)out; (void)lse; (void)workspace;
-    (void)workspace_bytes; (void)stream;
-    return fdec_fail(FDEC_ERR_UNSUPPORTED, "fdec_cascade_decode: not built yet");
+    const char *fn = "fdec_cascade_decode";
+    int rc = validate_common(fn, q, B, Hq, kv, suffix_lens, softmax_scale);
+    if (rc) return rc;
+    if (kv->page_size == 0) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: the cascade path needs a paged cache", fn);
+    if (kv->head_dim != 128)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: head_dim %d not built for the cascade path (128)", fn,
+                         kv->head_dim);
+    if (prefix_len < 0) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: prefix_len < 0", fn);
+    if (prefix_len > 0 && !prefix_pages)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: prefix_pages is NULL with prefix_len > 0", fn);
+    if (splits_prefix < 0 || splits_suffix < 0 || splits_prefix + splits_suffix > FDEC_MAX_SPLITS)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: split counts must be >= 0 with a sum <= %d", fn, FDEC_MAX_SPLITS);
+    const int cap = capacity_of(kv);
+    int sp = splits_prefix, ss = splits_suffix;
+    if (sp == 0 || ss == 0) {
+        int psp = 1, pss = 1;
+        if ((rc = fdec_cascade_plan(B, Hq, kv->num_kv_heads, prefix_len, cap, kv->page_size, 256, &psp, &pss)))
+            return rc;
+        if (sp == 0) sp = psp;
+        if (ss == 0) ss = pss;
+        if (sp + ss > FDEC_MAX_SPLITS) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: too many splits", fn);
+    }
+    const int64_t chunk_p = cascade_chunk(prefix_len, sp);
+    if (chunk_p / kv->page_size + 2 > fdec::kPrefixPagesPerBlock)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: %lld prefix tokens per split span too many pages; use more splits",
+                         fn, (long long)chunk_p);
+    if (B == 0) return FDEC_OK;
+    if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
+    const int S = sp + ss;
+    const WsLayout w = ws_layout(B, Hq, kv->num_kv_heads, kv->head_dim, S);
+    if (!workspace || workspace_bytes < w.total)
+        return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d + %d splits, got %zu", fn,
+                         w.total, sp, ss, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+    char *ws = static_cast<char *>(workspace);
+    float *pm = reinterpret_cast<float *>(ws + w.pm);
+    float *pd = reinterpret_cast<float *>(ws + w.pd);
+    float *po = reinterpret_cast<float *>(ws + w.po);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    float scale = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)kv->head_dim) : softmax_scale;
+    fdec::CascadeParams cp;
+    std::memset(&cp, 0, sizeof(cp));
+    cp.q = q;
+    cp.k = kv->k;
+    cp.v = kv->v;
+    cp.s_outer = kv->s_outer;
+    cp.s_token = kv->s_token;
+    cp.s_head = kv->s_head;
+    cp.prefix_pages = prefix_pages;
+    cp.prefix_len = prefix_len;
+    cp.page_size = kv->page_size;
+    cp.page_shift = page_shift_of(kv->page_size);
+    cp.B = B;
+    cp.Hq = Hq;
+    cp.Hkv = kv->num_kv_heads;
+    cp.chunk = (int)chunk_p;
+    cp.scale_log2 = scale * 1.4426950408889634f;
+    cp.po = po;
+    cp.pm = pm;
+    cp.pd = pd;
+    cp.s_total = S;
+    cp.s_offset = 0;
+    cp.dtype = kv->dtype;
+    if ((rc = check_hip(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch"))) return rc;
+
+    fdec::MapParams p = map_params(q, B, Hq, kv, suffix_lens, ss, softmax_scale, nullptr);
+    p.po = po;
+    p.pm = pm;
+    p.pd = pd;
+    p.s_total = S;
+    p.s_offset = sp;
+    if ((rc = check_hip(fdec::launch_map(p, ss, st), "fdec_cascade_decode: suffix launch"))) return rc;
+    return check_hip(fdec::launch_merge(po, pm, pd, B, Hq, S, kv->head_dim, out, lse, st),
+                     "fdec_cascade_decode: merge launch");
 }

@@ -1,0 +1,319 @@
+// Cascade shared-prefix kernel (matrix cores) for gfx950.
+//
+// Cascade attention (vLLM notes "FlashAttention 與 FlashInfer", design motivation:
+// a prefix shared by the requests of a batch is computed once) splits each
+// request's keys into the shared prefix and its own suffix. The suffix goes
+// through the split-KV map kernel; this kernel produces the prefix's partial
+// states (O~, m, d) for every query row at once -- the FlashDecoding map stage
+// (lpnh.cn explainer §2 stage 1) over the prefix -- and the merge kernel then
+// combines prefix and suffix states exactly (lpnh §2 stage 2).
+//
+// With B requests and G query heads per KV head, the prefix sees R = B*G query
+// rows per KV head (256 in the 64-request, 4:1 GQA workload): a real dense
+// contraction, so it runs on MFMA (v_mfma_f32_16x16x32_{bf16,f16}). Grid
+// (prefix split, KV head, 256-row chunk); 4 waves, each owning 64 query rows
+// (four 16-row blocks). Per 64-key tile:
+//   - the block stages K row-major and V transposed ([d][key], key pairs packed)
+//     in LDS, double-buffered, the next tile's global loads in flight meanwhile;
+//   - S^T = K Q^T: A = K (16 keys x 32 d from LDS), B = Q^T (query rows held in
+//     registers), so each lane's result column is one query row and its four
+//     values are four keys of that row;
+//   - online softmax per row in the log2 domain (lazily moved reference as in the
+//     map kernel); P enters the matrix core rounded to the input type, while the
+//     denominator sums the fp32 weights;
+//   - O += P V: A = P straight from the S^T registers (the key order inside the
+//     K dimension is permuted identically for A and B), B = V^T from LDS.
+// Layout of v_mfma_f32_16x16x32 (lane l, kq = l / 16): A holds row l % 16,
+// k = 8 kq .. 8 kq + 7; B holds column l % 16, k = 8 kq .. 8 kq + 7; D holds rows
+// 4 kq .. 4 kq + 3 of column l % 16.
+#include "device_common.h"
+#include "fdec_internal.h"
+
+namespace fdec {
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Mfma;
+template <> struct Mfma<0> {
+    static __device__ __forceinline__ f32x4_v run(uint4 a, uint4 b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a), __builtin_bit_cast(f16x8_v, b),
+                                                      c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<1> {
+    static __device__ __forceinline__ f32x4_v run(uint4 a, uint4 b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                       __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+    }
+};
+
+constexpr int kPfxKeys = 64;            // keys per tile
+constexpr int kPfxRowsPerWave = 64;     // query rows per wave
+constexpr int kPfxRows = 4 * kPfxRowsPerWave;
+constexpr int kKStride = 128 + 8;       // K tile row stride in elements (padding vs bank conflicts)
+constexpr int kVStride = kPfxKeys + 4;  // V^T tile row stride in elements
+
+template <int DT>
+__global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadeParams p) {
+    constexpr int D = 128;
+    using E = Elem<DT>;
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kPfxKeys * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * kVStride];
+    __shared__ int spages[kPrefixPagesPerBlock];
+    __shared__ float srow[4][3][kPfxRowsPerWave];
+
+    const int split = blockIdx.x, g = blockIdx.y, rc = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kq = lane >> 4, li = lane & 15;
+    const int G = p.Hq / p.Hkv;
+    const int R = p.B * G;
+
+    const int t_begin = split * p.chunk;
+    const int t_end = min(t_begin + p.chunk, p.prefix_len);
+    const int ntiles = t_end > t_begin ? (t_end - t_begin + kPfxKeys - 1) / kPfxKeys : 0;
+
+    // page ids of this split's keys
+    const int pg0 = t_begin / p.page_size;
+    const int npg = ntiles > 0 ? (t_end - 1) / p.page_size - pg0 + 1 : 0;
+    for (int i = tid; i < npg; i += 256) spages[i] = p.prefix_pages[pg0 + i];
+
+    // query rows of this wave: row = rc*256 + 64w + 16rb + li; B operand per (rb, ks)
+    uint4 qb[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int row = rc * kPfxRows + w * kPfxRowsPerWave + rb * 16 + li;
+        const bool ok = row < R;
+        const int b = ok ? row / G : 0, hh = ok ? row - (row / G) * G : 0;
+        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hq + g * G + hh) * D;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qb[rb][ks] = ok ? *reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * kq) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    // Staging: thread t covers rows 2*(t/16) + {0, 1} (+32) of a tile, d piece 8*(t%16).
+    const int srow0 = 2 * (tid >> 4), dpiece = 8 * (tid & 15);
+    uint4 rk[4], rv[4];  // rows srow0, srow0+1, srow0+32, srow0+33
+    auto load_tile = [&](int tile) {
+        const int t0 = t_begin + tile * kPfxKeys;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = srow0 + (i & 1) + 32 * (i >> 1);
+            const int t = t0 + r;
+            if (t < t_end) {
+                const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
+                const int pl = pidx - pg0, slot = t - pidx * p.page_size;
+                const int64_t off = (int64_t)spages[pl] * p.s_outer + (int64_t)slot * p.s_token +
+                                    (int64_t)g * p.s_head + dpiece;
+                rk[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.k) + off);
+                rv[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.v) + off);
+            } else {
+                rk[i] = make_uint4(0, 0, 0, 0);
+                rv[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = srow0 + (i & 1) + 32 * (i >> 1);
+            *reinterpret_cast<uint4 *>(&sk[buf][r * kKStride + dpiece]) = rk[i];
+        }
+        // V^T: dword (key r, key r + 1) for each d of the piece
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 a = rv[2 * h], c = rv[2 * h + 1];
+            const int r = srow0 + 32 * h;
+            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = __builtin_amdgcn_perm(cv[j], av[j], 0x05040100u);  // (a.lo, c.lo)
+                const uint32_t hi = __builtin_amdgcn_perm(cv[j], av[j], 0x07060302u);  // (a.hi, c.hi)
+                *reinterpret_cast<uint32_t *>(&sv[buf][(dpiece + 2 * j) * kVStride + r]) = lo;
+                *reinterpret_cast<uint32_t *>(&sv[buf][(dpiece + 2 * j + 1) * kVStride + r]) = hi;
+            }
+        }
+    };
+
+    constexpr float kTau = 8.0f;
+    constexpr float kFloor = -1.0e30f;
+    float m[4], tmax[4], l[4];
+    f32x4_v o[4][8];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        m[rb] = kFloor;
+        tmax[rb] = kNegInf;
+        l[rb] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[rb][db] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+    }
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int buf = tile & 1;
+        if (tile + 1 < ntiles) load_tile(tile + 1);  // in flight during this tile's math
+        const int t0 = t_begin + tile * kPfxKeys;
+        const uint16_t *K = sk[buf];
+        const uint16_t *V = sv[buf];
+
+        // ---- S^T = K Q^T: s[kb][rb] holds keys 16kb + 4kq + r of row 16rb + li
+        f32x4_v s[4][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) s[kb][rb] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(&K[(16 * kb + li) * kKStride + 32 * ks + 8 * kq]);
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) s[kb][rb] = Mfma<DT>::run(a, qb[rb][ks], s[kb][rb]);
+            }
+        }
+
+        // ---- online softmax per query row
+        const int nvalid = t_end - t0;
+        bool move = false;
+        float mx[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            float x = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = s[kb][rb][r] * p.scale_log2;
+                    if (16 * kb + 4 * kq + r >= nvalid) v = kNegInf;
+                    s[kb][rb][r] = v;
+                    x = fmaxf(x, v);
+                }
+            x = fmaxf(x, shfl_xor(x, 16));
+            x = fmaxf(x, shfl_xor(x, 32));
+            mx[rb] = x;
+            tmax[rb] = fmaxf(tmax[rb], x);
+            move |= x > m[rb] + kTau;
+        }
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            // move the reference; O rows live in lanes by (kq, r), so the
+            // per-row factors go through LDS
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const float mn = fmaxf(m[rb], mx[rb]);
+                const float alpha = fexp2(m[rb] - mn);
+                m[rb] = mn;
+                l[rb] *= alpha;
+                if (kq == 0) srow[w][0][16 * rb + li] = alpha;
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float alpha = srow[w][0][16 * rb + 4 * kq + r];
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) o[rb][db][r] *= alpha;
+                }
+            __builtin_amdgcn_wave_barrier();
+        }
+        // P rounded to the input type, packed as the A operand of P V (the sum of
+        // weights stays in fp32): K-slot 8kq + e is key
+        // 32kk + 4kq + e (e < 4) or 32kk + 16 + 4kq + (e - 4) (e >= 4)
+        uint4 pa[4][2];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            float ps = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int hbk = 0; hbk < 2; ++hbk) {
+                    const int kb = 2 * kk + hbk;
+                    uint16_t e4[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float pv = fexp2(s[kb][rb][r] - m[rb]);
+                        ps += pv;  // the denominator keeps fp32 weights
+                        e4[r] = E::from_float(pv);
+                    }
+                    wv[2 * hbk] = (uint32_t)e4[0] | ((uint32_t)e4[1] << 16);
+                    wv[2 * hbk + 1] = (uint32_t)e4[2] | ((uint32_t)e4[3] << 16);
+                }
+                pa[rb][kk] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+            l[rb] += ps;
+        }
+
+        // ---- O += P V
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const uint16_t *vrow = &V[(16 * db + li) * kVStride + 32 * kk + 4 * kq];
+                const uint2 v0 = *reinterpret_cast<const uint2 *>(vrow);
+                const uint2 v1 = *reinterpret_cast<const uint2 *>(vrow + 16);
+                const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
+            }
+        }
+
+        if (tile + 1 < ntiles) {
+            // the other buffer was last read before the previous barrier
+            store_tile(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- states against the true maximum: O~ = O 2^(m - T), d = l 2^(m - T)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        float lt = l[rb];
+        lt += shfl_xor(lt, 16);
+        lt += shfl_xor(lt, 32);
+        const float T = tmax[rb];
+        const float f = (T == kNegInf) ? 0.0f : fexp2(m[rb] - T);
+        if (kq == 0) {
+            srow[w][0][16 * rb + li] = f;
+            srow[w][1][16 * rb + li] = lt * f;
+            srow[w][2][16 * rb + li] = (T == kNegInf) ? kNegInf : T * kLn2;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int64_t slot = p.s_offset + split;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rl = 16 * rb + 4 * kq + r;
+            const int row = rc * kPfxRows + w * kPfxRowsPerWave + rl;
+            if (row >= R) continue;
+            const int b = row / G, hh = row - b * G;
+            const int64_t bh = (int64_t)b * p.Hq + g * G + hh;
+            const float f = srow[w][0][rl];
+            float *dst = p.po + (bh * p.s_total + slot) * D;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) dst[16 * db + li] = o[rb][db][r] * f;
+            if (li == 0) {
+                p.pd[bh * p.s_total + slot] = srow[w][1][rl];
+                p.pm[bh * p.s_total + slot] = srow[w][2][rl];
+            }
+        }
+    }
+}
+
+hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t st) {
+    const int R = p.B * (p.Hq / p.Hkv);
+    dim3 grid(splits, p.Hkv, (R + kPfxRows - 1) / kPfxRows);
+    if (p.dtype == 0)
+        hipLaunchKernelGGL(cascade_prefix_kernel<0>, grid, dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL(cascade_prefix_kernel<1>, grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace fdec

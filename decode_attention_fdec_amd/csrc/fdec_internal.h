@@ -48,6 +48,25 @@ struct MapParams {
 // Grid: (num_splits, Hkv, B).
 hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t stream);
 
+// Cascade prefix: partial states of every query row over the shared prefix.
+constexpr int kPrefixPagesPerBlock = 1024;  // prefix page ids one prefix block stages in LDS
+struct CascadeParams {
+    const void *q;                  // [B, Hq, D]
+    const void *k, *v;              // page pool
+    int64_t s_outer, s_token, s_head;
+    const int32_t *prefix_pages;    // pages of the shared prefix
+    int prefix_len;
+    int page_size, page_shift;
+    int B, Hq, Hkv;
+    int chunk;                      // prefix tokens per split (multiple of 64)
+    float scale_log2;
+    float *po, *pm, *pd;            // states, slots [s_offset, s_offset + splits)
+    int s_total, s_offset;
+    int dtype;
+};
+// Grid: (splits, Hkv, ceil(B * Hq / Hkv / 256)).
+hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t stream);
+
 // One wave per (b, h): merges S states into out / lse.
 hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S,
                         int head_dim, float *out, float *lse, hipStream_t stream);

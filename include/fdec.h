@@ -209,13 +209,25 @@ int fdec_merge_states(const float *part_o, const float *part_m, const float *par
  * once for all requests (matrix-core kernel over the B*G query rows of each KV
  * head), the suffixes by the split-KV kernel, and one merge combines both:
  * the result equals fdec_decode over the concatenated [prefix; suffix]
- * sequence. kv must be paged. splits_prefix / splits_suffix >= 1 (0 = planned).
- * Workspace: fdec_cascade_workspace_size().
+ * sequence. kv must be paged, head_dim 128. splits_prefix / splits_suffix >= 1
+ * (0 = fdec_cascade_plan's choice); the prefix is cut into chunks of
+ * 64 * ceil(ceil(prefix_len / splits_prefix) / 64) tokens, each of at most 1022
+ * pages. Workspace: fdec_cascade_workspace_size().
  */
 int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv,
                         const int32_t *prefix_pages, int prefix_len, const int32_t *suffix_lens,
                         int splits_prefix, int splits_suffix, float softmax_scale, float *out,
                         float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Split counts for fdec_cascade_decode (host only). The prefix is cut so the
+ * matrix-core kernel has about one block per compute unit with at least 256
+ * prefix tokens each; the suffix split count comes from fdec_plan over the
+ * suffix page table's capacity. prefix_len >= 0; capacity = max_pages_per_seq *
+ * page_size of the suffix table.
+ */
+int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size, int cu_count,
+                      int *splits_prefix_out, int *splits_suffix_out);
 
 /* Workspace bytes for fdec_cascade_decode with these split counts (both >= 1). */
 size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_dim, int splits_prefix,

@@ -169,3 +169,28 @@ def test_split_chunk_rule(fdec):
     assert F.split_chunk(100, 3) == 48  # ceil(100/3) = 34 -> 48
     assert F.split_chunk(5, 1) == 16
     assert F.split_chunk(0, 4) == 0
+
+
+def test_cascade_validation(fdec):
+    lib = F.load_library()
+    kv = kv_struct()  # contiguous: the cascade needs pages
+    args = lambda kv, plen, pages: (FAKE, 2, 32, ctypes.byref(kv), pages, plen, FAKE, 2, 2, 0.0, FAKE, None,
+                                    FAKE, 1 << 30, None)
+    assert lib.fdec_cascade_decode(*args(kv, 64, FAKE)) == F.FDEC_ERR_INVALID_ARG
+    kvp = kv_struct(page_size=64, page_table=FAKE, max_pages_per_seq=32, capacity=0)
+    assert lib.fdec_cascade_decode(*args(kvp, 64, None)) == F.FDEC_ERR_INVALID_ARG  # no prefix pages
+    assert lib.fdec_cascade_decode(*args(kvp, -1, FAKE)) == F.FDEC_ERR_INVALID_ARG
+    kv64 = kv_struct(page_size=64, page_table=FAKE, max_pages_per_seq=32, capacity=0, head_dim=64)
+    assert lib.fdec_cascade_decode(*args(kv64, 64, FAKE)) == F.FDEC_ERR_UNSUPPORTED
+    small = F.cascade_workspace_size(2, 32, 8, 128, 2, 2) - 1
+    assert lib.fdec_cascade_decode(FAKE, 2, 32, ctypes.byref(kvp), FAKE, 64, FAKE, 2, 2, 0.0, FAKE, None, FAKE,
+                                   small, None) == F.FDEC_ERR_WORKSPACE
+
+
+def test_cascade_plan(fdec):
+    sp, ss = F.cascade_plan(64, 32, 8, 16384, 2048, 64)
+    assert 8 * sp >= 256 and 1 <= ss and sp + ss <= F.MAX_SPLITS
+    sp, ss = F.cascade_plan(2, 8, 2, 100, 256, 16)
+    assert sp == 1  # fewer than 256 prefix tokens: one split
+    sp, ss = F.cascade_plan(1, 8, 8, 0, 64, 16)
+    assert sp >= 1 and ss >= 1
