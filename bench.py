@@ -72,6 +72,16 @@ class Runner:
             self.sin = None if case.rope_sin is None else case.rope_sin.to(dev)
             self.append = F.make_append(self.k_new, self.v_new, self.cos, self.sin, case.rotary_dim)
         B, Hq, D = case.q.shape
+        self.cascade = case.prefix_pages is not None
+        if self.cascade:
+            self.prefix_pages = case.prefix_pages.to(dev)
+            sp, ss = F.cascade_plan(B, Hq, case.Hkv, case.prefix_len, case.capacity, case.page_size)
+            self.S = (sp, ss)
+            self.out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+            self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+            self.ws = F.Workspace(F.cascade_workspace_size(B, Hq, case.Hkv, D, sp, ss), dev)
+            self.i = 0
+            return
         if splits <= 0:
             splits = case.num_splits
         if splits <= 0:
@@ -86,6 +96,11 @@ class Runner:
     def step(self, copy: int | None = None) -> None:
         c = self.i % self.copies if copy is None else copy
         self.i += 1
+        if self.cascade:
+            self.F.cascade_decode(self.q, self.k[c], self.v[c], self.table, self.prefix_pages,
+                                  self.case.prefix_len, self.lens, self.S[0], self.S[1], out=self.out,
+                                  lse=self.lse, workspace=self.ws)
+            return
         self.F.decode(self.q, self.k[c], self.v[c], self.lens, page_table=self.table, num_splits=self.S,
                       append=self.append, fused=(self.mode == "fused"), out=self.out, lse=self.lse,
                       workspace=self.ws)
@@ -244,10 +259,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--mode", default="two", choices=["fused", "two"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4", help="other workloads timed for context ('' = none)")
+    ap.add_argument("--also", default="c1,c3,c4,c5", help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
