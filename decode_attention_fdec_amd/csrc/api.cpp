@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/fdec.h"
@@ -93,6 +94,18 @@ int validate_common(const char *fn, const void *q, int B, int Hq, const fdec_kv 
     return FDEC_OK;
 }
 
+// KV heads (one wave each) per split-KV block: the largest divisor of Hkv up to
+// 8 waves (4 when G = 8 at D = 128, whose waves need the whole register file).
+#ifndef FDEC_HPB_CAP
+#define FDEC_HPB_CAP 8
+#endif
+int heads_per_block(int hkv, int G, int D) {
+    const int cap = std::min((G >= 8 && D >= 128) ? fdec::kMapMaxWavesBig : fdec::kMapMaxWaves, FDEC_HPB_CAP);
+    for (int w = cap; w > 1; --w)
+        if (hkv % w == 0) return w;
+    return 1;
+}
+
 // Prefix tokens per cascade split: a whole number of 64-token tiles.
 int64_t cascade_chunk(int prefix_len, int splits) {
     int64_t per = ((int64_t)std::max(prefix_len, 1) + splits - 1) / splits;
@@ -133,6 +146,7 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     p.B = B;
     p.Hq = Hq;
     p.Hkv = kv->num_kv_heads;
+    p.heads_per_block = heads_per_block(kv->num_kv_heads, Hq / kv->num_kv_heads, kv->head_dim);
     p.chunk = (int)fdec_split_chunk(capacity_of(kv), S);
     if (scale == 0.0f) scale = 1.0f / std::sqrt((float)kv->head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
@@ -146,6 +160,17 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
         p.rope_cos = append->rope_cos;
         p.rope_sin = append->rope_sin;
         p.mode = append->rotary_dim > 0 ? fdec::kAppendRope : fdec::kAppend;
+    }
+    // GQA groups of 4 at D = 128 run on matrix cores unless FDEC_MAP_PATH=vector.
+    const char *path = std::getenv("FDEC_MAP_PATH");
+    if (fdec::map_mfma_eligible(p) && !(path && std::strcmp(path, "vector") == 0)) {
+        p.mfma = 1;
+        p.heads_per_block = 1;
+        for (int w = fdec::kMapMfmaWaves; w > 1; --w)
+            if (p.Hkv % w == 0) {
+                p.heads_per_block = w;
+                break;
+            }
     }
     return p;
 }

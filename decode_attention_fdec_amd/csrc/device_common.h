@@ -83,6 +83,14 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// max of two floats that are already canonical (results of arithmetic): one
+// v_max_f32, without the quieting that fmaxf adds for signalling NaNs.
+__device__ __forceinline__ float fmax_nc(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 __device__ __forceinline__ float readlane(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
@@ -91,11 +99,35 @@ __device__ __forceinline__ float readlane(float x, int lane) {
 // m = max_i m_i, alpha_i = exp(m_i - m) (0 for an empty state), d = sum alpha_i d_i,
 // out = sum alpha_i O~_i / d, lse = m + ln d. States are in natural-log units.
 // The same code serves the merge kernel and the single-kernel path, so both give
-// bitwise identical results. All loads are lane-varying vector loads.
+// bitwise identical results. All loads are lane-varying vector loads; the first
+// 32 state rows are requested together with m and d, so up to 32 splits merge in
+// one memory round trip. Rows are accumulated in split order.
 template <int D>
 __device__ __forceinline__ void merge_states_wave(const float *po, const float *pm, const float *pd,
                                                   int S, float *out, float *lse, int lane) {
     constexpr int NV = D / 64;  // output elements per lane
+    constexpr int NB = 32;      // rows per batch
+    auto load_row = [&](int s, float *x) {
+        const float *row = po + (int64_t)s * D + lane * NV;
+        if constexpr (NV == 2) {
+            const float2 t = *reinterpret_cast<const float2 *>(row);
+            x[0] = t.x;
+            x[1] = t.y;
+        } else {
+#pragma unroll
+            for (int e = 0; e < NV; ++e) x[e] = row[e];
+        }
+    };
+    float x[NB][NV];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        if (u < S) {
+            load_row(u, x[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < NV; ++e) x[u][e] = 0.0f;
+        }
+    }
     float mv[4], dv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -121,32 +153,28 @@ __device__ __forceinline__ void merge_states_wave(const float *po, const float *
         dsum += a[k] * dv[k];
     }
     dsum = wave_sum(dsum);
-    // Rows are fetched 16 at a time (all loads of a batch in flight before the
-    // first use); alpha_s is broadcast from lane s % 64 of register a[s / 64].
+    // alpha_s is broadcast from lane s % 64 of register a[s / 64]
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const float alpha = u < S ? readlane(a[0], u) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) o[e] += alpha * x[u][e];
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int n = min(64, S - 64 * k);
-        for (int j0 = 0; j0 < n; j0 += 16) {
-            float x[16][NV];
+        for (int j0 = (k == 0 ? NB : 0); j0 < n; j0 += NB) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const float *row = po + (int64_t)(64 * k + j0 + u) * D + lane * NV;
+            for (int u = 0; u < NB; ++u) {
                 if (j0 + u < n) {
-                    if constexpr (NV == 2) {
-                        const float2 t = *reinterpret_cast<const float2 *>(row);
-                        x[u][0] = t.x;
-                        x[u][1] = t.y;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < NV; ++e) x[u][e] = row[e];
-                    }
+                    load_row(64 * k + j0 + u, x[u]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < NV; ++e) x[u][e] = 0.0f;
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < NB; ++u) {
                 const float alpha = (j0 + u < n) ? readlane(a[k], min(j0 + u, 63)) : 0.0f;
 #pragma unroll
                 for (int e = 0; e < NV; ++e) o[e] += alpha * x[u][e];

@@ -6,9 +6,10 @@
 
 namespace fdec {
 
-constexpr int kMapWaves = 4;                  // waves per split-KV block
-constexpr int kMapThreads = 64 * kMapWaves;   // 256 threads
+constexpr int kMapMaxWaves = 8;     // split-KV block: one wave per KV head, up to 8
+constexpr int kMapMaxWavesBig = 4;  // ... up to 4 when G * D needs more than 256 registers per lane
 constexpr int kMergeWaves = 4;                // (b, h) pairs per merge block
+constexpr int kMapMfmaWaves = 4;    // matrix-core map block (G = 4, D = 128): up to 4 KV heads
 
 // What happens around the attention itself.
 enum MapMode : int {
@@ -27,13 +28,14 @@ struct MapParams {
     int page_shift;             // log2(page_size) when a power of two, else -1
     const int32_t *seq_lens;    // [B]
     int B, Hq, Hkv;
+    int heads_per_block;        // KV heads (= waves) per block: the largest divisor of Hkv <= 8 (4 for G = 8, D = 128)
     int chunk;                  // tokens per split (multiple of 16)
     float scale_log2;           // softmax scale * log2(e)
     // partial states [B, Hq, s_total, D] / [B, Hq, s_total]; this launch fills
     // split slots [s_offset, s_offset + gridDim.x)
     float *po, *pm, *pd;
     int s_total, s_offset;
-    // single-kernel merge: counters [B * Hkv] (nullptr = no merge in this kernel)
+    // single-kernel merge: counters [B * Hkv / heads_per_block] (nullptr = no merge in this kernel)
     int *counters;
     float *out, *lse;
     // append
@@ -43,10 +45,20 @@ struct MapParams {
     int mode;                   // MapMode
     int dtype;                  // 0 fp16, 1 bf16
     int head_dim;
+    int mfma;                   // 1: matrix-core kernel (map_mfma_eligible)
 };
 
-// Grid: (num_splits, Hkv, B).
+// Whether the matrix-core map kernel can take these parameters (mfma aside).
+inline bool map_mfma_eligible(const MapParams &p) {
+    return p.Hq == 4 * p.Hkv && p.head_dim == 128 && p.mode == kPlain &&
+           (p.page_table == nullptr || p.page_size % 16 == 0) && p.s_token > 0 &&
+           p.s_token < (int64_t(1) << 26);  // 16 rows of a tile as 32-bit byte offsets
+}
+
+// Grid: (num_splits, B, Hkv / heads_per_block), 64 * heads_per_block threads.
+// Runs the matrix-core kernel when p.mfma is set (heads_per_block <= 4).
 hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t stream);
+hipError_t launch_map_mfma_g4(const MapParams &p, int num_splits, hipStream_t stream);
 
 // Cascade prefix: partial states of every query row over the shared prefix.
 constexpr int kPrefixPagesPerBlock = 1024;  // prefix page ids one prefix block stages in LDS

@@ -5,21 +5,22 @@
 // is cut into equal chunks; each chunk yields the local max m_i, the local sum of
 // exponentials d_i and the unnormalised output O~_i. With a single-kernel merge
 // (lpnh §3, unified kernel with atomics) the last block to finish a
-// (request, KV head) merges its splits. Optional KV append with NeoX rotary
+// (request, head group) merges its splits. Optional KV append with NeoX rotary
 // follows the flash-attn "Inference Cookbook / 推理优化" page §3.3-3.4.
 //
-// Layout on the chip. Grid (split, kv_head, request), 4 waves per block. One
-// block serves all G = Hq/Hkv query heads of its KV head (GQA reuse, lpnh §3), so
-// every K/V byte is read from HBM once. A wave streams 16-token tiles (tiles of a
-// block are dealt round-robin to its waves, so the four waves read neighbouring
-// rows): each tile is two groups of 8 rows, one row per 8 lanes. Lane
-// (row a = lane / 8, chunk c = lane % 8) loads the 16-byte pieces [8c, 8c+8) and
-// [64+8c, 64+8c+8) of its row (D = 128), so every load instruction covers eight
-// full 128-byte lines. q.k uses v_dot2 on packed fp16/bf16 (products exact in
-// fp32) and an 8-lane DPP sum; softmax runs in the log2 domain in fp32; the
-// next tile's loads are in flight while the current one is computed. Each lane
-// row keeps its own (m, d, acc); the eight row states of a wave and then the
-// four waves are merged once at the end.
+// Layout on the chip. Grid (split, request, head group); a block has one wave
+// per KV head of its group (up to 8), so together its waves read whole token
+// rows of the NHD cache -- the DRAM-friendly order -- while each wave serves
+// the G = Hq/Hkv query heads of its KV head (GQA reuse, lpnh §3): every K/V byte
+// is read from HBM once. A wave streams the split's 16-token tiles on its own;
+// a tile is two groups of 8 rows, one row per 8 lanes. Lane (row a = lane / 8,
+// chunk c = lane % 8) loads the 16-byte pieces [8c, 8c+8) and [64+8c, 64+8c+8)
+// of its row (D = 128), so every load instruction covers eight full 128-byte
+// lines. q.k uses v_dot2 on packed fp16/bf16 (products exact in fp32) and an
+// 8-lane DPP sum; softmax runs in the log2 domain in fp32; the next tiles' loads
+// are in flight while the current one is computed. Each lane row keeps its own
+// (m, d, acc); the eight row states are merged with shuffles and the wave writes
+// its heads' states itself.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -35,12 +36,15 @@ namespace fdec {
 #define FDEC_OCC_G4 2
 #endif
 template <int G, int D> struct MapConfig {
-    static constexpr int nbuf = (G >= 8 && D >= 128) ? 2 : (G == 4 && D >= 128) ? FDEC_NBUF_G4 : 3;
-    static constexpr int occ = (G >= 8 && D >= 128) ? 1 : (G == 4 && D >= 128) ? FDEC_OCC_G4 : 2;
+    static constexpr bool big = (G >= 8 && D >= 128);  // needs more than 256 registers per lane
+    static constexpr int nbuf = big ? 2 : (G == 4 && D >= 128) ? FDEC_NBUF_G4 : 3;
+    static constexpr int occ = big ? 1 : (G == 4 && D >= 128) ? FDEC_OCC_G4 : 2;
+    static constexpr int max_waves = big ? kMapMaxWavesBig : kMapMaxWaves;
 };
 
 template <int DT, int D, int G, bool PAGED, int MODE>
-__global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kernel(const MapParams p) {
+__global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>::occ)) void map_kernel(
+    const MapParams p) {
     constexpr int NCH = D / 64;           // 16-byte pieces per lane per row
     constexpr int NE = NCH * 8;           // elements per lane per row
     constexpr int NQ = NCH * 4;           // packed dwords per lane per row
@@ -50,15 +54,13 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
     constexpr int NBUF = MapConfig<G, D>::nbuf;
     using E = Elem<DT>;
 
-    __shared__ float sm_acc[kMapWaves][G][D];
-    __shared__ float sm_m[kMapWaves][G];
-    __shared__ float sm_l[kMapWaves][G];
-    __shared__ float sm_t[kMapWaves][G];
-    __shared__ float sm_vec[(MODE == kAppendRope) ? (G + 1) * D : 1];
+    __shared__ float sm_vec[(MODE == kAppendRope) ? MapConfig<G, D>::max_waves * (G + 1) * D : 1];
     __shared__ int sm_flag;
 
-    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.z * p.heads_per_block + wv;
     const int ra = lane >> 3, cb = lane & 7;
     const int hq0 = g * G;
 
@@ -82,33 +84,31 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
     // ---------------------------------------------------------------- q (and append)
     uint32_t qp[QF32 ? 1 : G][NQ];
     float qf[QF32 ? G : 1][QF32 ? NE : 1];
+    const bool owner = (MODE != kPlain) && (t_begin <= c_app) && (c_app < t_begin + p.chunk);
     if constexpr (MODE == kAppendRope) {
-        // rotate q (and, in the block owning the new row, k_new) in LDS, fp32
-        float *qs = sm_vec;
-        float *ks = sm_vec + G * D;
-        const bool owner = (t_begin <= c_app) && (c_app < t_begin + p.chunk);
+        // rotate q (and, in the block owning the new row, k_new) in this wave's
+        // part of LDS, fp32
+        float *qs = sm_vec + wv * (G + 1) * D;
+        float *ks = qs + G * D;
         const uint16_t *qsrc = reinterpret_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hq + hq0) * D;
         const uint16_t *ksrc = reinterpret_cast<const uint16_t *>(p.k_new) + ((int64_t)b * p.Hkv + g) * D;
-        for (int i = tid; i < G * D; i += kMapThreads) {
-            uint32_t u = qsrc[i];
-            qs[i] = E::lo(u);
-        }
+        for (int i = lane; i < G * D; i += 64) qs[i] = E::lo((uint32_t)qsrc[i]);
         if (owner)
-            for (int i = tid; i < D; i += kMapThreads) ks[i] = E::lo((uint32_t)ksrc[i]);
-        __syncthreads();
+            for (int i = lane; i < D; i += 64) ks[i] = E::lo((uint32_t)ksrc[i]);
+        __builtin_amdgcn_wave_barrier();
         const int half = p.rotary_dim >> 1;
         const float *cs = p.rope_cos + (int64_t)c_app * half;
         const float *sn = p.rope_sin + (int64_t)c_app * half;
         const int nvec = owner ? G + 1 : G;
-        for (int i = tid; i < nvec * half; i += kMapThreads) {
+        for (int i = lane; i < nvec * half; i += 64) {
             int h = i / half, j = i - h * half;
-            float *x = sm_vec + h * D;
+            float *x = qs + h * D;
             float c = cs[j], s = sn[j];
             float x0 = x[j], x1 = x[j + half];
             x[j] = x0 * c - x1 * s;
             x[j + half] = x0 * s + x1 * c;
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -120,13 +120,12 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
             uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k)) + off;
             uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v)) + off;
             const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)b * p.Hkv + g) * D;
-            for (int i = tid; i < D; i += kMapThreads) {
+            for (int i = lane; i < D; i += 64) {
                 kd[i] = E::from_float(ks[i]);
                 vd[i] = vsrc[i];
             }
-            __threadfence();
+            __threadfence();  // the row is read back by this wave below
         }
-        __syncthreads();
     } else {
         const uint16_t *qsrc = reinterpret_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hq + hq0) * D;
 #pragma unroll
@@ -140,20 +139,18 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
                 qp[h][4 * c + 3] = u.w;
             }
         if constexpr (MODE == kAppend) {
-            const bool owner = (t_begin <= c_app) && (c_app < t_begin + p.chunk);
             if (owner) {
                 const int64_t off = row_offset(c_app);
                 uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k)) + off;
                 uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v)) + off;
                 const uint16_t *ksrc = reinterpret_cast<const uint16_t *>(p.k_new) + ((int64_t)b * p.Hkv + g) * D;
                 const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)b * p.Hkv + g) * D;
-                for (int i = tid; i < D; i += kMapThreads) {
+                for (int i = lane; i < D; i += 64) {
                     kd[i] = ksrc[i];
                     vd[i] = vsrc[i];
                 }
-                __threadfence();
+                __threadfence();  // the row is read back by this wave below
             }
-            __syncthreads();
         }
     }
 
@@ -178,9 +175,6 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
 
     const int ntok = t_end - t_begin;
     const int ntiles = ntok > 0 ? (ntok + TT - 1) / TT : 0;
-    // tiles wv, wv + 4, wv + 8, ... of this split belong to wave wv (wave-uniform values)
-    const int wvu = __builtin_amdgcn_readfirstlane(wv);
-    const int n_my = ntiles > wvu ? (ntiles - wvu + kMapWaves - 1) / kMapWaves : 0;
     const char *kbase = p.k;
     const char *vbase = p.v;
     const uint32_t tok_bytes = (uint32_t)(p.s_token * 2);
@@ -189,7 +183,7 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
         uint4 k[NR][NCH];
         uint4 v[NR][NCH];
     };
-    auto tile_t0 = [&](int i) { return t_begin + (wvu + i * kMapWaves) * TT; };
+    auto tile_t0 = [&](int i) { return t_begin + i * TT; };
 
     // Per-lane byte offsets of this lane's rows within a tile: loop-invariant,
     // except in the split's last tile, whose rows past t_end clamp to its last
@@ -255,14 +249,14 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
         for (int h = 0; h < G; ++h) {
             mx[h] = sc[0][h];
 #pragma unroll
-            for (int j = 1; j < NR; ++j) mx[h] = fmaxf(mx[h], sc[j][h]);
-            tmax[h] = fmaxf(tmax[h], mx[h]);
+            for (int j = 1; j < NR; ++j) mx[h] = fmax_nc(mx[h], sc[j][h]);
+            tmax[h] = fmax_nc(tmax[h], mx[h]);
             move |= mx[h] > m[h] + kTau;
         }
         if (__builtin_amdgcn_ballot_w64(move) != 0) {  // rare after the first tiles
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float mn = fmaxf(m[h], mx[h]);
+                const float mn = fmax_nc(m[h], mx[h]);
                 const float alpha = fexp2(m[h] - mn);
                 m[h] = mn;
                 l[h] *= alpha;
@@ -298,17 +292,16 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
         }
     };
 
-    if (n_my > 0) {
+    if (ntiles > 0) {
         // NBUF register tiles rotate: while one is computed, the next NBUF - 1
-        // are in flight (under load the memory latency is about two tiles'
-        // compute time). Loads are unconditional -- indices past the end
+        // are in flight. Loads are unconditional -- indices past the end
         // re-issue the last tile -- so every wait count in the loop is static.
         Tile T[NBUF];
-        const int last = n_my - 1;
+        const int last = ntiles - 1;
 #pragma unroll
         for (int u = 0; u < NBUF - 1; ++u) issue(T[u], tile_t0(min(u, last)));
         int i = 0;
-        for (; i + NBUF <= n_my; i += NBUF) {
+        for (; i + NBUF <= ntiles; i += NBUF) {
 #pragma unroll
             for (int u = 0; u < NBUF; ++u) {
                 issue(T[(u + NBUF - 1) % NBUF], tile_t0(min(i + u + NBUF - 1, last)));
@@ -317,18 +310,18 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
         }
 #pragma unroll
         for (int u = 0; u < NBUF - 1; ++u)
-            if (i + u < n_my) compute(T[u], tile_t0(i + u));
+            if (i + u < ntiles) compute(T[u], tile_t0(i + u));
     }
 
-    // ---------------------------------------------------------------- merge lane rows, then waves
+    // ---------------------------------------------------------------- merge the lane rows
 #pragma unroll
     for (int step = 8; step <= 32; step <<= 1) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float mo = shfl_xor(m[h], step);
             const float lo = shfl_xor(l[h], step);
-            tmax[h] = fmaxf(tmax[h], shfl_xor(tmax[h], step));
-            const float mn = fmaxf(m[h], mo);
+            tmax[h] = fmax_nc(tmax[h], shfl_xor(tmax[h], step));
+            const float mn = fmax_nc(m[h], mo);
             const float as = fexp2(m[h] - mn), ao = fexp2(mo - mn);
             l[h] = l[h] * as + lo * ao;
             m[h] = mn;
@@ -339,44 +332,30 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
             }
         }
     }
-    if (ra == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sm_acc[wv][h][64 * c + 8 * cb + e] = acc[h][8 * c + e];
-            if (cb == 0) {
-                sm_m[wv][h] = m[h];
-                sm_l[wv][h] = l[h];
-                sm_t[wv][h] = tmax[h];
-            }
-        }
-    }
-    __syncthreads();
 
-    // Block state per head, re-expressed against the true maximum T of the split:
-    // O~ = sum_w 2^(m_w - T) acc_w, d = sum_w 2^(m_w - T) l_w (each factor <= 2^kTau).
+    // The wave's state per head, re-expressed against the true maximum T of the
+    // split: O~ = 2^(m - T) acc, d = 2^(m - T) l (m <= T, so the factor is <= 1).
     const int64_t slot = p.s_offset + split;
-    for (int i = tid; i < G * D; i += kMapThreads) {
-        const int h = i / D, d = i - h * D;
-        float T = sm_t[0][h];
 #pragma unroll
-        for (int w = 1; w < kMapWaves; ++w) T = fmaxf(T, sm_t[w][h]);
-        float o = 0.0f, lsum = 0.0f;
-        if (T != kNegInf) {
+    for (int h = 0; h < G; ++h) {
+        const float T = tmax[h];
+        const float f = (T == kNegInf) ? 0.0f : fexp2(m[h] - T);
+        const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
+        if (ra == 0) {
+            float *dst = p.po + (bh * p.s_total + slot) * D;
 #pragma unroll
-            for (int w = 0; w < kMapWaves; ++w) {
-                const float a = fexp2(sm_m[w][h] - T);
-                o += a * sm_acc[w][h][d];
-                lsum += a * sm_l[w][h];
+            for (int c = 0; c < NCH; ++c) {
+                float4 lo4 = make_float4(acc[h][8 * c] * f, acc[h][8 * c + 1] * f, acc[h][8 * c + 2] * f,
+                                         acc[h][8 * c + 3] * f);
+                float4 hi4 = make_float4(acc[h][8 * c + 4] * f, acc[h][8 * c + 5] * f, acc[h][8 * c + 6] * f,
+                                         acc[h][8 * c + 7] * f);
+                *reinterpret_cast<float4 *>(dst + 64 * c + 8 * cb) = lo4;
+                *reinterpret_cast<float4 *>(dst + 64 * c + 8 * cb + 4) = hi4;
             }
         }
-        const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
-        p.po[(bh * p.s_total + slot) * D + d] = o;
-        if (d == 0) {
+        if (lane == 0) {
             p.pm[bh * p.s_total + slot] = (T == kNegInf) ? kNegInf : T * kLn2;
-            p.pd[bh * p.s_total + slot] = lsum;
+            p.pd[bh * p.s_total + slot] = l[h] * f;
         }
     }
 
@@ -384,11 +363,11 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
 
     // ---------------------------------------------------------------- single-kernel merge
     // Publish this block's states device-wide and count arrivals per
-    // (request, KV head); the last block to arrive merges all splits (in split
+    // (request, head group); the last block to arrive merges all splits (in split
     // order, with the merge kernel's code) and resets the counter.
     __syncthreads();  // every wave's state stores are complete
-    if (tid == 0) {
-        int *cnt = p.counters + (int64_t)b * p.Hkv + g;
+    if (threadIdx.x == 0) {
+        int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
         const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         const int last = (prev == (int)gridDim.x - 1);
         if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -397,7 +376,8 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
     __syncthreads();
     if (!sm_flag) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    for (int h = wv; h < G; h += kMapWaves) {
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {
         const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
         merge_states_wave<D>(p.po + bh * p.s_total * D, p.pm + bh * p.s_total, p.pd + bh * p.s_total,
                              p.s_total, p.out + bh * D, p.lse ? p.lse + bh : nullptr, lane);
@@ -406,8 +386,8 @@ __global__ __launch_bounds__(kMapThreads, (MapConfig<G, D>::occ)) void map_kerne
 
 template <int DT, int D, int G, bool PAGED, int MODE>
 static hipError_t launch_t(const MapParams &p, int S, hipStream_t st) {
-    dim3 grid(S, p.Hkv, p.B);
-    hipLaunchKernelGGL((map_kernel<DT, D, G, PAGED, MODE>), grid, dim3(kMapThreads), 0, st, p);
+    dim3 grid(S, p.B, p.Hkv / p.heads_per_block);
+    hipLaunchKernelGGL((map_kernel<DT, D, G, PAGED, MODE>), grid, dim3(64 * p.heads_per_block), 0, st, p);
     return hipGetLastError();
 }
 
@@ -437,6 +417,10 @@ static hipError_t launch_g(const MapParams &p, int S, hipStream_t st) {
 }
 
 hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t st) {
+    if (p.mfma) {
+        if (!map_mfma_eligible(p) || p.heads_per_block > kMapMfmaWaves) return hipErrorInvalidValue;
+        return launch_map_mfma_g4(p, num_splits, st);
+    }
     if (p.head_dim == 128)
         return p.dtype == 0 ? launch_g<0, 128>(p, num_splits, st) : launch_g<1, 128>(p, num_splits, st);
     if (p.head_dim == 64)

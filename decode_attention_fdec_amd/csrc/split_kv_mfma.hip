@@ -1,0 +1,346 @@
+// Split-KV map kernel on matrix cores for GQA groups of four query heads
+// (gfx950). Same contract as map_kernel in split_kv.hip (the FlashDecoding map
+// stage: per split the local max m_i, the local sum of exponentials d_i and the
+// unnormalised output O~_i -- lpnh.cn explainer §2 stage 1), for G = Hq/Hkv = 4,
+// D = 128, without append.
+//
+// Packing the four query heads of a KV head makes q.K^T a dense contraction for
+// the 16-block v_mfma_f32_4x4x4_16b_{bf16,f16} (M = 4 = G, no padding; lpnh §3
+// "KV-Reused layout" for GQA). Layout facts used (lane L, block b = L / 4,
+// i = L % 4), verified on the GPU:
+//   A: lane holds row i of block b's 4x4 A, four K values;
+//   B: lane holds column i of block b's B, four K values;
+//   D: lane holds column i of block b's result, rows 0..3 in its four registers;
+//   cbsz = 4, abid = q: every block uses block q's A.
+// And of ds_read_b64_tr_b16 (the LDS transpose read): in each group of 16
+// lanes, lane j receives element j % 4 of the 64-bit chunks addressed by lanes
+// j/4, 4 + j/4, 8 + j/4, 12 + j/4.
+//
+// One wave per KV head, up to four per block. Per wave and 32-token tile:
+//   - K and V rows go global -> LDS with global_load_lds_dwordx4 (no registers),
+//     double-buffered per wave, rows XOR-swizzled in 16-byte slots;
+//   - S^T = K Q^T: A = K (lane 4b+i reads token 4b+i's 4 d-values), B = Q^T
+//     (lane 4b+j holds query head j); lane 4b+j receives the scores of tokens
+//     4b..4b+3 for head j -- exactly the A operand of P.V for tokens 4b..4b+3;
+//   - online softmax in the log2 domain with a lazily moved reference per head;
+//   - O += P V: A = P broadcast from block q (tokens 4q..4q+3), B = V^T from the
+//     transpose read of the row-major V tile; lane L accumulates O[head 0..3]
+//     at d = L and 64 + L.
+#include "device_common.h"
+#include "fdec_internal.h"
+
+namespace fdec {
+
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_v __attribute__((ext_vector_type(4)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+
+template <int DT> struct Mfma4;
+template <> struct Mfma4<0> {
+    template <int CBSZ, int ABID>
+    static __device__ __forceinline__ f32x4_v run(uint2 a, uint2 b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4_v, a), __builtin_bit_cast(f16x4_v, b), c,
+                                                  CBSZ, ABID, 0);
+    }
+};
+template <> struct Mfma4<1> {
+    template <int CBSZ, int ABID>
+    static __device__ __forceinline__ f32x4_v run(uint2 a, uint2 b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4_v, a), __builtin_bit_cast(s16x4_v, b),
+                                                      c, CBSZ, ABID, 0);
+    }
+};
+
+// Two 16-bit values packed (lo, hi), rounded to nearest even by the hardware
+// conversion.
+template <int DT> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<0>(float a, float b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+}
+template <> __device__ __forceinline__ uint32_t pack2<1>(float a, float b) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
+}
+
+constexpr int kMT = 32;                 // tokens per tile
+constexpr int kMTileBytes = kMT * 256;  // one tile of K (or V) rows for one KV head
+
+template <int DT, bool PAGED>
+__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(const MapParams p) {
+    constexpr int D = 128, G = 4;
+    using E = Elem<DT>;
+    // [wave][buffer][K, V][tile bytes]
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][2][2][kMTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
+    __shared__ int sm_flag;
+
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.z * p.heads_per_block + wv;
+    const int hq0 = g * G;
+    const int hme = lane & 3;  // this lane's query head in the S^T layout
+
+    const int L = p.seq_lens[b];
+    const int t_begin = split * p.chunk;
+    const int t_end = min(t_begin + p.chunk, L);
+    const int ntok = t_end - t_begin;
+    const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
+
+    // Global -> LDS staging. Instruction i (0..7) of a tile writes rows 4i..4i+3:
+    // lane l fills slot (l & 15) of row r = 4i + l / 16 with 16-byte piece
+    // (l & 15) ^ swz(r) of that row; piece c of row r therefore sits in slot
+    // c ^ swz(r). K rows use swz = r & 15 (an S^T read takes one piece of 16
+    // consecutive rows per quarter wave), V rows swz = 4 (r & 3) (a transpose
+    // read takes 4 pieces of 4 consecutive rows per half wave). Rows past the
+    // end of the split repeat its last row. Paged caches hold whole 16-token
+    // halves of a tile on one page (page_size and chunk are multiples of 16),
+    // so each half needs one page id, read with a scalar load a tile ahead.
+    const int srow = lane >> 4, sslot = lane & 15;
+    typedef const __attribute__((address_space(4))) int32_t *cpage_t;
+    const cpage_t ptab = PAGED ? (cpage_t)(p.page_table + (int64_t)b * p.max_pages) : nullptr;
+    const int64_t stok2 = p.s_token * 2;
+    const int64_t head2 = (int64_t)g * p.s_head * 2;
+    // byte offset of token t (uniform), read a tile ahead for paged caches
+    auto token_offset = [&](int t) -> int64_t {
+        if constexpr (PAGED) {
+            const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : (t / p.page_size);
+            const int64_t page = ptab[pidx];
+            return (page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token) * 2 + head2;
+        } else {
+            return ((int64_t)b * p.s_outer + (int64_t)t * p.s_token) * 2 + head2;
+        }
+    };
+    // first token of each 16-token half of a tile (clamped to the split)
+    auto half_first = [&](int tile, int hf) { return min(t_begin + tile * kMT + 16 * hf, t_end - 1); };
+    auto stage = [&](int tile, int buf, int64_t off0, int64_t off1) {
+        const int t0 = t_begin + tile * kMT;
+        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][buf][0];
+        const uint32_t vl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][buf][1];
+#pragma unroll
+        for (int i = 0; i < kMT / 4; ++i) {
+            const int hf = i >> 2;
+            const int r = 4 * i + srow;
+            // row within the half, clamped; a half that starts past the end
+            // has its first token clamped to the last one, so every row is 0
+            const int rr = max(0, min(t0 + r, t_end - 1) - (t0 + 16 * hf));
+            const uint32_t row = (uint32_t)rr * (uint32_t)stok2;
+            const uint32_t ok = row + 16u * (uint32_t)(sslot ^ (r & 15));
+            const uint32_t ov = row + 16u * (uint32_t)(sslot ^ (4 * (r & 3)));
+            const char *kb = p.k + (hf ? off1 : off0);
+            const char *vb = p.v + (hf ? off1 : off0);
+            asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                         :
+                         : "v"(ok), "s"(kb), "s"(kl + 1024u * i)
+                         : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                         :
+                         : "v"(ov), "s"(vb), "s"(vl + 1024u * i)
+                         : "memory", "m0");
+        }
+    };
+
+    constexpr float kTau = 8.0f;
+    constexpr float kFloor = -1.0e30f;
+    float m_own = kFloor, t_own = kNegInf, l_own = 0.0f;  // per head hme
+    // P enters the P V products as hi + lo, two 16-bit parts whose sum
+    // carries about 16 significant bits, so O is accumulated from P at close
+    // to fp32 accuracy; o[] takes the hi parts, ol[] the lo parts.
+    f32x4_v o[2] = {f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}};
+    f32x4_v ol[2] = {f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}};
+
+    // S^T reads: lane L takes token L & 31 (lanes 32..63 duplicate rows 0..31;
+    // their scores are masked)
+    const int rk = lane & 31;
+    // transpose reads: lane L = 16 gq + 4 k + a takes token 4q + k, d = 64h + 16 gq + 4a
+    const int tk = (lane & 15) >> 2, ta = lane & 3, tg = lane >> 4;
+
+    // Q of the wave's 4 heads (1 KB) goes to LDS with the same DMA path, so
+    // that every vector load the loop waits for is one of these DMA loads and
+    // the counts in the explicit waits below are exact.
+    {
+        const char *qb = reinterpret_cast<const char *>(p.q) + ((int64_t)b * p.Hq + hq0) * D * 2;
+        const uint32_t ql = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)qlds[wv];
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :
+                     : "v"((uint32_t)lane * 16u), "s"(qb), "s"(ql)
+                     : "memory", "m0");
+    }
+    // offsets of the two halves of the next tile to stage
+    int64_t off0 = 0, off1 = 0;
+    if (ntiles > 0) {
+        off0 = token_offset(half_first(0, 0));
+        off1 = token_offset(half_first(0, 1));
+        stage(0, 0, off0, off1);
+        if (ntiles > 1) {
+            off0 = token_offset(half_first(1, 0));
+            off1 = token_offset(half_first(1, 1));
+        }
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // Q has landed
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    // Q^T as the B operand: K-step k (d = 4k .. 4k+3) of head hme, 32 steps
+    uint2 qb[32];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(qlds[wv] + hme * 256 + 16 * c);
+        qb[2 * c] = make_uint2(u.x, u.y);
+        qb[2 * c + 1] = make_uint2(u.z, u.w);
+    }
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int buf = tile & 1;
+        if (tile + 1 < ntiles) {
+            stage(tile + 1, buf ^ 1, off0, off1);
+            if (tile + 2 < ntiles) {
+                off0 = token_offset(half_first(tile + 2, 0));
+                off1 = token_offset(half_first(tile + 2, 1));
+            }
+            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this tile's 16 loads have landed
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const uint8_t *kl = lds[wv][buf][0];
+        const uint8_t *vl = lds[wv][buf][1];
+
+        // ---- S^T = K Q^T over D = 128: 16 pieces of 8 d-values, two K-steps each
+        f32x4_v s = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * (c ^ (rk & 15)));
+            s = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[2 * c], s);
+            s1 = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[2 * c + 1], s1);
+        }
+        s += s1;
+
+        // ---- softmax for head hme, tokens 4(L/4) .. +3 of this tile
+        const int nvalid = t_end - (t_begin + tile * kMT);
+        float sv[4], mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = 4 * (lane >> 2) + r;
+            sv[r] = (tok < nvalid && lane < 32) ? s[r] * p.scale_log2 : kNegInf;
+            mx = fmax_nc(mx, sv[r]);
+        }
+        t_own = fmax_nc(t_own, mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m_own + kTau) != 0) {
+            // move the reference of every head to its running maximum
+            float hm = mx;
+            hm = fmax_nc(hm, shfl_xor(hm, 4));
+            hm = fmax_nc(hm, shfl_xor(hm, 8));
+            hm = fmax_nc(hm, shfl_xor(hm, 16));
+            hm = fmax_nc(hm, shfl_xor(hm, 32));
+            const float mn = fmax_nc(m_own, hm);
+            const float alpha = fexp2(m_own - mn);
+            m_own = mn;
+            l_own *= alpha;
+            f32x4_v al;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = readlane(alpha, i);  // lanes 0..3 carry heads 0..3
+            o[0] *= al;
+            o[1] *= al;
+            ol[0] *= al;
+            ol[1] *= al;
+        }
+        uint32_t ph[2], pl[2];
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+            const float p0 = fexp2(sv[r] - m_own), p1 = fexp2(sv[r + 1] - m_own);
+            l_own += p0 + p1;
+            const uint32_t h = pack2<DT>(p0, p1);
+            ph[r / 2] = h;
+            pl[r / 2] = pack2<DT>(p0 - E::lo(h), p1 - E::hi(h));
+        }
+        const uint2 pa = make_uint2(ph[0], ph[1]), pb = make_uint2(pl[0], pl[1]);
+
+        // ---- O += P V over the tile's 8 groups of 4 tokens
+#define FDEC_PV_STEP(Q)                                                                                       \
+    {                                                                                                         \
+        const int row = 4 * (Q) + tk;                                                                         \
+        _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                       \
+            const int piece = 8 * h + 2 * tg + (ta >> 1);                                                     \
+            lds_s16x4 *src = (lds_s16x4 *)(vl + row * 256 + 16 * (piece ^ (4 * (row & 3))) + 8 * (ta & 1));    \
+            const s16x4_v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);                                  \
+            o[h] = Mfma4<DT>::template run<4, (Q)>(pa, __builtin_bit_cast(uint2, vt), o[h]);                  \
+            ol[h] = Mfma4<DT>::template run<4, (Q)>(pb, __builtin_bit_cast(uint2, vt), ol[h]);                \
+        }                                                                                                     \
+    }
+        FDEC_PV_STEP(0)
+        FDEC_PV_STEP(1)
+        FDEC_PV_STEP(2)
+        FDEC_PV_STEP(3)
+        FDEC_PV_STEP(4)
+        FDEC_PV_STEP(5)
+        FDEC_PV_STEP(6)
+        FDEC_PV_STEP(7)
+#undef FDEC_PV_STEP
+    }
+
+    // ---- the wave's state per head against the true maximum T:
+    // O~ = 2^(m - T) O, d = 2^(m - T) l
+    float lt = l_own, tt = t_own;
+#pragma unroll
+    for (int x = 4; x <= 32; x <<= 1) {
+        lt += shfl_xor(lt, x);
+        tt = fmax_nc(tt, shfl_xor(tt, x));
+    }
+    const float f_own = (tt == kNegInf) ? 0.0f : fexp2(m_own - tt);
+    f32x4_v fs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fs[i] = readlane(f_own, i);
+    const int64_t slot = p.s_offset + split;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t bh = (int64_t)b * p.Hq + hq0 + i;
+        float *dst = p.po + (bh * p.s_total + slot) * D;
+        dst[lane] = (o[0][i] + ol[0][i]) * fs[i];
+        dst[64 + lane] = (o[1][i] + ol[1][i]) * fs[i];
+    }
+    if (lane < 4) {
+        const int64_t bh = (int64_t)b * p.Hq + hq0 + lane;
+        p.pm[bh * p.s_total + slot] = (tt == kNegInf) ? kNegInf : tt * kLn2;
+        p.pd[bh * p.s_total + slot] = lt * f_own;
+    }
+
+    if (p.counters == nullptr) return;
+
+    // ---- single-kernel merge (as in map_kernel)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (prev == (int)gridDim.x - 1);
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_flag = last;
+    }
+    __syncthreads();
+    if (!sm_flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {
+        const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
+        merge_states_wave<D>(p.po + bh * p.s_total * D, p.pm + bh * p.s_total, p.pd + bh * p.s_total,
+                             p.s_total, p.out + bh * D, p.lse ? p.lse + bh : nullptr, lane);
+    }
+}
+
+hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
+    dim3 grid(S, p.B, p.Hkv / p.heads_per_block);
+    dim3 block(64 * p.heads_per_block);
+    if (p.dtype == 0) {
+        if (p.page_table)
+            hipLaunchKernelGGL((map_kernel_mfma_g4<0, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((map_kernel_mfma_g4<0, false>), grid, block, 0, st, p);
+    } else {
+        if (p.page_table)
+            hipLaunchKernelGGL((map_kernel_mfma_g4<1, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((map_kernel_mfma_g4<1, false>), grid, block, 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fdec
