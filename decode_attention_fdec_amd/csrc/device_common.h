@@ -95,100 +95,121 @@ __device__ __forceinline__ float readlane(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-// Merge S <= 256 partial states of one (b, h) with one wave (the reduce stage):
+// Merging S <= 256 partial states of one (b, h) (the reduce stage):
 // m = max_i m_i, alpha_i = exp(m_i - m) (0 for an empty state), d = sum alpha_i d_i,
 // out = sum alpha_i O~_i / d, lse = m + ln d. States are in natural-log units.
-// The same code serves the merge kernel and the single-kernel path, so both give
-// bitwise identical results. All loads are lane-varying vector loads; the first
-// 32 state rows are requested together with m and d, so up to 32 splits merge in
-// one memory round trip. Rows are accumulated in split order.
+//
+// The weighted sum runs over fixed groups of kMergeGroup consecutive states:
+// each group is summed in split order, then the group sums are added in group
+// order. One wave can take every group in turn (merge_states_wave) or one wave
+// per group can take them side by side (merge_kernel_groups); both give the
+// same bits, and so do the merge kernel and the single-kernel path.
+constexpr int kMergeGroup = 32;
+
+// M, dsum and the weights a[k] of states lane + 64 k (every lane of the wave).
 template <int D>
-__device__ __forceinline__ void merge_states_wave(const float *po, const float *pm, const float *pd,
-                                                  int S, float *out, float *lse, int lane) {
-    constexpr int NV = D / 64;  // output elements per lane
-    constexpr int NB = 32;      // rows per batch
-    auto load_row = [&](int s, float *x) {
+__device__ __forceinline__ void merge_weights(const float *pm, const float *pd, int S, int lane, float &M,
+                                              float &dsum, float a[4]) {
+    float mv[4], dv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = lane + 64 * k;
+        mv[k] = i < S ? pm[i] : kNegInf;
+        dv[k] = i < S ? pd[i] : 0.0f;
+    }
+    M = wave_max(fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+    dsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        a[k] = (mv[k] == kNegInf || M == kNegInf) ? 0.0f : fexp2((mv[k] - M) * kLog2e);
+        dsum += a[k] * dv[k];
+    }
+    dsum = wave_sum(dsum);
+}
+
+// The rows of group k (zeros past S): this lane's D / 64 elements of each.
+template <int D>
+__device__ __forceinline__ void merge_load_group(const float *po, int S, int k, int lane,
+                                                 float x[kMergeGroup][D / 64]) {
+    constexpr int NV = D / 64;
+#pragma unroll
+    for (int u = 0; u < kMergeGroup; ++u) {
+        const int s = k * kMergeGroup + u;
         const float *row = po + (int64_t)s * D + lane * NV;
-        if constexpr (NV == 2) {
-            const float2 t = *reinterpret_cast<const float2 *>(row);
-            x[0] = t.x;
-            x[1] = t.y;
-        } else {
+        if (s < S) {
+            if constexpr (NV == 2) {
+                const float2 t = *reinterpret_cast<const float2 *>(row);
+                x[u][0] = t.x;
+                x[u][1] = t.y;
+            } else {
 #pragma unroll
-            for (int e = 0; e < NV; ++e) x[e] = row[e];
-        }
-    };
-    float x[NB][NV];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-        if (u < S) {
-            load_row(u, x[u]);
+                for (int e = 0; e < NV; ++e) x[u][e] = row[e];
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < NV; ++e) x[u][e] = 0.0f;
         }
     }
-    float mv[4], dv[4];
+}
+
+// g = sum over group k's rows, in split order, of alpha_s * row_s.
+template <int D>
+__device__ __forceinline__ void merge_group_sum(const float x[kMergeGroup][D / 64], const float a[4], int S,
+                                                int k, float g[D / 64]) {
+    constexpr int NV = D / 64;
+    const int j = k >> 1;  // state 32 k + u has its weight in lane 32 (k & 1) + u of a[j]
+    const float aj = j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        int i = lane + 64 * k;
-        mv[k] = i < S ? pm[i] : kNegInf;
-        dv[k] = i < S ? pd[i] : 0.0f;
+    for (int e = 0; e < NV; ++e) g[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kMergeGroup; ++u) {
+        const float alpha = (k * kMergeGroup + u < S) ? readlane(aj, 32 * (k & 1) + u) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) g[e] = __builtin_fmaf(alpha, x[u][e], g[e]);
     }
-    float M = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
-    M = wave_max(M);
-    float o[NV];
-#pragma unroll
-    for (int e = 0; e < NV; ++e) o[e] = 0.0f;
+}
+
+template <int D>
+__device__ __forceinline__ void merge_finish(const float acc[D / 64], float M, float dsum, float *out, float *lse,
+                                             int lane) {
+    constexpr int NV = D / 64;
     if (M == kNegInf) {
 #pragma unroll
         for (int e = 0; e < NV; ++e) out[lane * NV + e] = 0.0f;
         if (lse && lane == 0) *lse = kNegInf;
         return;
     }
-    float a[4], dsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        a[k] = mv[k] == kNegInf ? 0.0f : fexp2((mv[k] - M) * kLog2e);
-        dsum += a[k] * dv[k];
-    }
-    dsum = wave_sum(dsum);
-    // alpha_s is broadcast from lane s % 64 of register a[s / 64]
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-        const float alpha = u < S ? readlane(a[0], u) : 0.0f;
-#pragma unroll
-        for (int e = 0; e < NV; ++e) o[e] += alpha * x[u][e];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int n = min(64, S - 64 * k);
-        for (int j0 = (k == 0 ? NB : 0); j0 < n; j0 += NB) {
-#pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                if (j0 + u < n) {
-                    load_row(64 * k + j0 + u, x[u]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < NV; ++e) x[u][e] = 0.0f;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                const float alpha = (j0 + u < n) ? readlane(a[k], min(j0 + u, 63)) : 0.0f;
-#pragma unroll
-                for (int e = 0; e < NV; ++e) o[e] += alpha * x[u][e];
-            }
-        }
-    }
     const float inv = 1.0f / dsum;
     if constexpr (NV == 2) {
-        *reinterpret_cast<float2 *>(out + lane * 2) = make_float2(o[0] * inv, o[1] * inv);
+        *reinterpret_cast<float2 *>(out + lane * 2) = make_float2(acc[0] * inv, acc[1] * inv);
     } else {
 #pragma unroll
-        for (int e = 0; e < NV; ++e) out[lane * NV + e] = o[e] * inv;
+        for (int e = 0; e < NV; ++e) out[lane * NV + e] = acc[e] * inv;
     }
     if (lse && lane == 0) *lse = M + flog2(dsum) * kLn2;
+}
+
+// One wave merges every group in turn; the first group's rows are requested
+// together with m and d, so up to 32 splits merge in one memory round trip.
+template <int D>
+__device__ __forceinline__ void merge_states_wave(const float *po, const float *pm, const float *pd,
+                                                  int S, float *out, float *lse, int lane) {
+    constexpr int NV = D / 64;
+    float x[kMergeGroup][NV];
+    merge_load_group<D>(po, S, 0, lane, x);
+    float M, dsum, a[4];
+    merge_weights<D>(pm, pd, S, lane, M, dsum, a);
+    float acc[NV];
+    merge_group_sum<D>(x, a, S, 0, acc);
+    const int K = (S + kMergeGroup - 1) / kMergeGroup;
+    for (int k = 1; k < K; ++k) {
+        merge_load_group<D>(po, S, k, lane, x);
+        float g[NV];
+        merge_group_sum<D>(x, a, S, k, g);
+#pragma unroll
+        for (int e = 0; e < NV; ++e) acc[e] += g[e];
+    }
+    merge_finish<D>(acc, M, dsum, out, lse, lane);
 }
 
 }  // namespace fdec

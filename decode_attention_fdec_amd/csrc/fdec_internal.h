@@ -9,7 +9,10 @@ namespace fdec {
 constexpr int kMapMaxWaves = 8;     // split-KV block: one wave per KV head, up to 8
 constexpr int kMapMaxWavesBig = 4;  // ... up to 4 when G * D needs more than 256 registers per lane
 constexpr int kMergeWaves = 4;                // (b, h) pairs per merge block
-constexpr int kMapMfmaWaves = 4;    // matrix-core map block (G = 4, D = 128): up to 4 KV heads
+#ifndef FDEC_MFMA_WAVES
+#define FDEC_MFMA_WAVES 4
+#endif
+constexpr int kMapMfmaWaves = FDEC_MFMA_WAVES;  // matrix-core map block (G = 4, D = 128): KV heads
 
 // What happens around the attention itself.
 enum MapMode : int {

@@ -1,7 +1,10 @@
 // Merge kernel: the FlashDecoding reduce stage (lpnh.cn FlashDecoding explainer
 // §2 stage 2; tbr8.org "FlashDecoding 与 FlashInfer 深度解析" §2.1 step 3).
-// One wave per (request, query head) merges its S partial states; the
-// arithmetic is merge_states_wave, shared with the single-kernel path.
+// Up to 32 states: one wave per (request, query head) merges them
+// (merge_states_wave, shared with the single-kernel path). More states: one
+// block per (request, query head), one wave per group of 32 states, each
+// group's rows requested at once; the group sums meet in LDS and are added in
+// group order, which gives the bits of merge_states_wave.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -20,9 +23,53 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float *__
                          lse ? lse + bh : nullptr, lane);
 }
 
+template <int D>
+__global__ __launch_bounds__(64 * (256 / kMergeGroup)) void merge_kernel_groups(
+    const float *__restrict__ po, const float *__restrict__ pm, const float *__restrict__ pd, int S,
+    float *__restrict__ out, float *__restrict__ lse) {
+    constexpr int NV = D / 64;
+    __shared__ float gs[256 / kMergeGroup][D];
+    const int lane = threadIdx.x & 63;
+    const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's group
+    const int64_t bh = blockIdx.x;
+    po += bh * S * D;
+    pm += bh * S;
+    pd += bh * S;
+    float x[kMergeGroup][NV];
+    merge_load_group<D>(po, S, k, lane, x);
+    float M, dsum, a[4];
+    merge_weights<D>(pm, pd, S, lane, M, dsum, a);
+    float g[NV];
+    merge_group_sum<D>(x, a, S, k, g);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) gs[k][lane * NV + e] = g[e];
+    __syncthreads();
+    if (k != 0) return;
+    float acc[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) acc[e] = gs[0][lane * NV + e];
+    const int K = blockDim.x >> 6;
+    for (int j = 1; j < K; ++j) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) acc[e] += gs[j][lane * NV + e];
+    }
+    merge_finish<D>(acc, M, dsum, out + bh * D, lse ? lse + bh : nullptr, lane);
+}
+
 hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S,
                         int head_dim, float *out, float *lse, hipStream_t st) {
     const int BH = B * Hq;
+    if (S > kMergeGroup) {
+        const int K = (S + kMergeGroup - 1) / kMergeGroup;  // <= 8 for S <= 256
+        if (K > 256 / kMergeGroup) return hipErrorInvalidValue;
+        if (head_dim == 128)
+            hipLaunchKernelGGL(merge_kernel_groups<128>, dim3(BH), dim3(64 * K), 0, st, po, pm, pd, S, out, lse);
+        else if (head_dim == 64)
+            hipLaunchKernelGGL(merge_kernel_groups<64>, dim3(BH), dim3(64 * K), 0, st, po, pm, pd, S, out, lse);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     dim3 grid((BH + kMergeWaves - 1) / kMergeWaves);
     if (head_dim == 128)
         hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64 * kMergeWaves), 0, st, po, pm, pd, BH, S, out, lse);

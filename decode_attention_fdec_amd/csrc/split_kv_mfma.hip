@@ -16,12 +16,14 @@
 // lanes, lane j receives element j % 4 of the 64-bit chunks addressed by lanes
 // j/4, 4 + j/4, 8 + j/4, 12 + j/4.
 //
-// One wave per KV head, up to four per block. Per wave and 32-token tile:
-//   - K and V rows go global -> LDS with global_load_lds_dwordx4 (no registers),
-//     double-buffered per wave, rows XOR-swizzled in 16-byte slots;
-//   - S^T = K Q^T: A = K (lane 4b+i reads token 4b+i's 4 d-values), B = Q^T
-//     (lane 4b+j holds query head j); lane 4b+j receives the scores of tokens
-//     4b..4b+3 for head j -- exactly the A operand of P.V for tokens 4b..4b+3;
+// One wave per KV head. Per wave and 16-token tile:
+//   - K and V rows go global -> LDS with global_load_lds_dwordx4 (no registers)
+//     into a ring of kNbuf tiles per wave, rows XOR-swizzled in 16-byte slots;
+//   - S^T = K Q^T with the 16 blocks as 4 token groups x 4 quarters of D:
+//     block b = 4 dq + tg takes tokens 4 tg .. 4 tg + 3 over d in
+//     [32 dq, 32 dq + 32); two lane swaps add the quarters, after which lane
+//     4 tg + j (j = head) holds the scores of tokens 4 tg .. 4 tg + 3 for head
+//     j -- exactly the A operand of P.V for those tokens;
 //   - online softmax in the log2 domain with a lazily moved reference per head;
 //   - O += P V: A = P broadcast from block q (tokens 4q..4q+3), B = V^T from the
 //     transpose read of the row-major V tile; lane L accumulates O[head 0..3]
@@ -64,15 +66,54 @@ template <> __device__ __forceinline__ uint32_t pack2<1>(float a, float b) {
     return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
 }
 
-constexpr int kMT = 32;                 // tokens per tile
-constexpr int kMTileBytes = kMT * 256;  // one tile of K (or V) rows for one KV head
+// x summed over lanes L, L ^ 16, L ^ 32, L ^ 48 (the same order in every lane).
+__device__ __forceinline__ float sum_quarters(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// LDS-DMA load: 64 lanes x 16 bytes from base + voff (per lane) into LDS at
+// lds_addr + 16 * lane. Issued as inline assembly so that the compiler neither
+// waits for it before unrelated LDS reads nor counts it: every wait on these
+// loads is one of the explicit waits below.
+__device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds_addr)
+                 : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+// wait until at most 8 k DMA loads are outstanding (k uniform, clamped to [0, 7])
+__device__ __forceinline__ void wait_vm8(int k) {
+    switch (k) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<8>(); break;
+    case 2: wait_vm<16>(); break;
+    case 3: wait_vm<24>(); break;
+    case 4: wait_vm<32>(); break;
+    case 5: wait_vm<40>(); break;
+    case 6: wait_vm<48>(); break;
+    default: wait_vm<56>(); break;
+    }
+}
+
+constexpr int kMT = 16;                 // tokens per tile
+constexpr int kMTileBytes = kMT * 256;  // one tile of K (or V) rows of one KV head
+#ifndef FDEC_MFMA_NBUF
+#define FDEC_MFMA_NBUF 2
+#endif
+constexpr int kNbuf = FDEC_MFMA_NBUF;   // ring slots per wave: kNbuf - 1 tiles in flight ahead
+static_assert(kNbuf >= 2 && kNbuf <= 8, "ring of 2..8 tiles");
+static_assert(kMapMfmaWaves * kNbuf * 2 * kMTileBytes <= 128 * 1024, "K/V ring fits in LDS");
 
 template <int DT, bool PAGED>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(const MapParams p) {
     constexpr int D = 128, G = 4;
     using E = Elem<DT>;
-    // [wave][buffer][K, V][tile bytes]
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][2][2][kMTileBytes];
+    // [wave][ring slot][K, V][tile bytes]
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
     __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
     __shared__ int sm_flag;
 
@@ -82,6 +123,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     const int g = blockIdx.z * p.heads_per_block + wv;
     const int hq0 = g * G;
     const int hme = lane & 3;  // this lane's query head in the S^T layout
+    const int dq = lane >> 4;  // this lane's quarter of D in the S^T products
 
     const int L = p.seq_lens[b];
     const int t_begin = split * p.chunk;
@@ -89,22 +131,23 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     const int ntok = t_end - t_begin;
     const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
 
-    // Global -> LDS staging. Instruction i (0..7) of a tile writes rows 4i..4i+3:
-    // lane l fills slot (l & 15) of row r = 4i + l / 16 with 16-byte piece
-    // (l & 15) ^ swz(r) of that row; piece c of row r therefore sits in slot
-    // c ^ swz(r). K rows use swz = r & 15 (an S^T read takes one piece of 16
-    // consecutive rows per quarter wave), V rows swz = 4 (r & 3) (a transpose
+    // Global -> LDS staging. Instruction i (0..3) of a tile writes rows
+    // 4i..4i+3: lane l fills slot (l & 15) of row r = 4i + l / 16 with 16-byte
+    // piece (l & 15) ^ swz(r) of that row; piece c of row r therefore sits in
+    // slot c ^ swz(r). K rows use swz = r (an S^T read takes one piece of each
+    // of the 16 rows per quarter wave), V rows swz = 4 (r & 3) (a transpose
     // read takes 4 pieces of 4 consecutive rows per half wave). Rows past the
-    // end of the split repeat its last row. Paged caches hold whole 16-token
-    // halves of a tile on one page (page_size and chunk are multiples of 16),
-    // so each half needs one page id, read with a scalar load a tile ahead.
+    // end of the split repeat its last row. A tile of a paged cache lies on one
+    // page (page_size and chunk are multiples of 16): one page id per tile,
+    // read with a scalar load a tile before it is staged.
     const int srow = lane >> 4, sslot = lane & 15;
     typedef const __attribute__((address_space(4))) int32_t *cpage_t;
     const cpage_t ptab = PAGED ? (cpage_t)(p.page_table + (int64_t)b * p.max_pages) : nullptr;
     const int64_t stok2 = p.s_token * 2;
     const int64_t head2 = (int64_t)g * p.s_head * 2;
-    // byte offset of token t (uniform), read a tile ahead for paged caches
-    auto token_offset = [&](int t) -> int64_t {
+    // byte offset of the first token of a tile (uniform)
+    auto tile_offset = [&](int tile) -> int64_t {
+        const int t = t_begin + tile * kMT;
         if constexpr (PAGED) {
             const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : (t / p.page_size);
             const int64_t page = ptab[pidx];
@@ -113,32 +156,18 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
             return ((int64_t)b * p.s_outer + (int64_t)t * p.s_token) * 2 + head2;
         }
     };
-    // first token of each 16-token half of a tile (clamped to the split)
-    auto half_first = [&](int tile, int hf) { return min(t_begin + tile * kMT + 16 * hf, t_end - 1); };
-    auto stage = [&](int tile, int buf, int64_t off0, int64_t off1) {
+    auto stage = [&](int tile, int64_t off) {
         const int t0 = t_begin + tile * kMT;
-        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][buf][0];
-        const uint32_t vl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][buf][1];
+        const int slot = tile % kNbuf;
+        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][slot][0];
+        const uint32_t vl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][slot][1];
+        const char *kb = p.k + off, *vb = p.v + off;
 #pragma unroll
         for (int i = 0; i < kMT / 4; ++i) {
-            const int hf = i >> 2;
             const int r = 4 * i + srow;
-            // row within the half, clamped; a half that starts past the end
-            // has its first token clamped to the last one, so every row is 0
-            const int rr = max(0, min(t0 + r, t_end - 1) - (t0 + 16 * hf));
-            const uint32_t row = (uint32_t)rr * (uint32_t)stok2;
-            const uint32_t ok = row + 16u * (uint32_t)(sslot ^ (r & 15));
-            const uint32_t ov = row + 16u * (uint32_t)(sslot ^ (4 * (r & 3)));
-            const char *kb = p.k + (hf ? off1 : off0);
-            const char *vb = p.v + (hf ? off1 : off0);
-            asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                         :
-                         : "v"(ok), "s"(kb), "s"(kl + 1024u * i)
-                         : "memory", "m0");
-            asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                         :
-                         : "v"(ov), "s"(vb), "s"(vl + 1024u * i)
-                         : "memory", "m0");
+            const uint32_t row = (uint32_t)(min(t0 + r, t_end - 1) - t0) * (uint32_t)stok2;
+            dma16(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
+            dma16(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
         }
     };
 
@@ -151,77 +180,59 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     f32x4_v o[2] = {f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}};
     f32x4_v ol[2] = {f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}};
 
-    // S^T reads: lane L takes token L & 31 (lanes 32..63 duplicate rows 0..31;
-    // their scores are masked)
-    const int rk = lane & 31;
+    // S^T reads: lane L takes token L & 15, pieces 4 dq .. 4 dq + 3
+    const int rk = lane & 15;
     // transpose reads: lane L = 16 gq + 4 k + a takes token 4q + k, d = 64h + 16 gq + 4a
     const int tk = (lane & 15) >> 2, ta = lane & 3, tg = lane >> 4;
 
     // Q of the wave's 4 heads (1 KB) goes to LDS with the same DMA path, so
-    // that every vector load the loop waits for is one of these DMA loads and
-    // the counts in the explicit waits below are exact.
-    {
-        const char *qb = reinterpret_cast<const char *>(p.q) + ((int64_t)b * p.Hq + hq0) * D * 2;
-        const uint32_t ql = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)qlds[wv];
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                     :
-                     : "v"((uint32_t)lane * 16u), "s"(qb), "s"(ql)
-                     : "memory", "m0");
-    }
-    // offsets of the two halves of the next tile to stage
-    int64_t off0 = 0, off1 = 0;
-    if (ntiles > 0) {
-        off0 = token_offset(half_first(0, 0));
-        off1 = token_offset(half_first(0, 1));
-        stage(0, 0, off0, off1);
-        if (ntiles > 1) {
-            off0 = token_offset(half_first(1, 0));
-            off1 = token_offset(half_first(1, 1));
-        }
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // Q has landed
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    // Q^T as the B operand: K-step k (d = 4k .. 4k+3) of head hme, 32 steps
-    uint2 qb[32];
+    // that every vector load the waits below count is one of these DMA loads.
+    dma16(reinterpret_cast<const char *>(p.q) + ((int64_t)b * p.Hq + hq0) * D * 2, (uint32_t)lane * 16u,
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)qlds[wv]);
+    // prologue: the first kNbuf - 1 tiles
+    const int npro = min(kNbuf - 1, ntiles);
+    for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
+    int64_t noff = (kNbuf - 1 < ntiles) ? tile_offset(kNbuf - 1) : 0;  // next tile to stage
+    wait_vm8(npro);  // Q has landed
+    // Q^T as the B operand: K-step k of quarter dq = d 32 dq + 4k .. +3 of head hme
+    uint2 qb[8];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(qlds[wv] + hme * 256 + 16 * c);
+    for (int c = 0; c < 4; ++c) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(qlds[wv] + hme * 256 + dq * 64 + 16 * c);
         qb[2 * c] = make_uint2(u.x, u.y);
         qb[2 * c + 1] = make_uint2(u.z, u.w);
     }
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        if (tile + 1 < ntiles) {
-            stage(tile + 1, buf ^ 1, off0, off1);
-            if (tile + 2 < ntiles) {
-                off0 = token_offset(half_first(tile + 2, 0));
-                off1 = token_offset(half_first(tile + 2, 1));
-            }
-            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this tile's 16 loads have landed
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        const uint8_t *kl = lds[wv][buf][0];
-        const uint8_t *vl = lds[wv][buf][1];
 
-        // ---- S^T = K Q^T over D = 128: 16 pieces of 8 d-values, two K-steps each
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int ahead = tile + kNbuf - 1;
+        if (ahead < ntiles) {
+            stage(ahead, noff);
+            if (ahead + 1 < ntiles) noff = tile_offset(ahead + 1);
+        }
+        // this tile's loads have landed once only the later tiles' remain
+        wait_vm8(min(kNbuf - 1, ntiles - 1 - tile));
+        const int slot = tile % kNbuf;
+        const uint8_t *kl = lds[wv][slot][0];
+        const uint8_t *vl = lds[wv][slot][1];
+
+        // ---- S^T = K Q^T: this lane's quarter of D, 4 pieces of 8 d-values
         f32x4_v s = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * (c ^ (rk & 15)));
+        for (int c = 0; c < 4; ++c) {
+            const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * ((4 * dq + c) ^ rk));
             s = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[2 * c], s);
             s1 = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[2 * c + 1], s1);
         }
-        s += s1;
 
-        // ---- softmax for head hme, tokens 4(L/4) .. +3 of this tile
+        // ---- softmax for head hme, tokens 4 tg .. 4 tg + 3 of this tile
+        // (lanes 0..15 carry the tile; the others hold copies and stay masked)
         const int nvalid = t_end - (t_begin + tile * kMT);
         float sv[4], mx = kNegInf;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int tok = 4 * (lane >> 2) + r;
-            sv[r] = (tok < nvalid && lane < 32) ? s[r] * p.scale_log2 : kNegInf;
+            const float x = sum_quarters(s[r] + s1[r]);
+            const int tok = 4 * ((lane >> 2) & 3) + r;
+            sv[r] = (tok < nvalid && lane < 16) ? x * p.scale_log2 : kNegInf;
             mx = fmax_nc(mx, sv[r]);
         }
         t_own = fmax_nc(t_own, mx);
@@ -255,7 +266,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
         }
         const uint2 pa = make_uint2(ph[0], ph[1]), pb = make_uint2(pl[0], pl[1]);
 
-        // ---- O += P V over the tile's 8 groups of 4 tokens
+        // ---- O += P V over the tile's 4 groups of 4 tokens
 #define FDEC_PV_STEP(Q)                                                                                       \
     {                                                                                                         \
         const int row = 4 * (Q) + tk;                                                                         \
@@ -271,10 +282,6 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
         FDEC_PV_STEP(1)
         FDEC_PV_STEP(2)
         FDEC_PV_STEP(3)
-        FDEC_PV_STEP(4)
-        FDEC_PV_STEP(5)
-        FDEC_PV_STEP(6)
-        FDEC_PV_STEP(7)
 #undef FDEC_PV_STEP
     }
 
