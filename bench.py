@@ -35,7 +35,7 @@ WORKLOAD_TEXT = {
     "c5": "cascade: 64 requests, Hq=32, Hkv=8, D=128, shared 16384-token prefix + U[256,2048] suffix, "
           "page 64, bf16",
 }
-KERNEL_SOURCES = ["split_kv.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
+KERNEL_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
 
 
 def log(msg: str) -> None:
@@ -82,6 +82,14 @@ class Runner:
             self.ws = F.Workspace(F.cascade_workspace_size(B, Hq, case.Hkv, D, sp, ss), dev)
             self.i = 0
             return
+        if mode == "bal":
+            # balanced split: `splits` is the block count per group of KV heads (0 = default)
+            self.S = max(0, splits)
+            self.out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+            self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+            self.ws = F.Workspace(F.balanced_workspace_size(B, Hq, case.Hkv, D, self.S), dev)
+            self.i = 0
+            return
         if splits <= 0:
             splits = case.num_splits
         if splits <= 0:
@@ -100,6 +108,10 @@ class Runner:
             self.F.cascade_decode(self.q, self.k[c], self.v[c], self.table, self.prefix_pages,
                                   self.case.prefix_len, self.lens, self.S[0], self.S[1], out=self.out,
                                   lse=self.lse, workspace=self.ws)
+            return
+        if self.mode == "bal":
+            self.F.decode_balanced(self.q, self.k[c], self.v[c], self.lens, page_table=self.table,
+                                   num_blocks=self.S, out=self.out, lse=self.lse, workspace=self.ws)
             return
         self.F.decode(self.q, self.k[c], self.v[c], self.lens, page_table=self.table, num_splits=self.S,
                       append=self.append, fused=(self.mode == "fused"), out=self.out, lse=self.lse,
@@ -260,7 +272,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
-    ap.add_argument("--mode", default="two", choices=["fused", "two"])
+    ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
     ap.add_argument("--also", default="c1,c3,c4,c5", help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -300,7 +312,7 @@ def main() -> int:
     traffic = load_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "map_kernel (split-KV map stage, fdec_decode_partials)",
+                "kernel": "map_kernel_mfma_g4 (split-KV map stage on matrix cores, fdec_decode_partials)",
                 "avg_launch_us": round(kernel_ms * 1e3, 2), "algorithmic_bytes_per_launch": case.kv_bytes(),
                 "kernel_hash": kernel_hash()}
 
@@ -331,15 +343,23 @@ def main() -> int:
     res["pct_of_probe"] = round(100 * res["GBps"] / res["probe_read_GBps"], 1)
     del runner
 
+    # the paged batch of mixed lengths runs on the balanced split (equal work per
+    # block whatever the length mix); its uniform-split time is kept beside it
     others = {}
+    runs = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        if name == "c3":
+            runs += [("c3", "c3", "bal"), ("c3_uniform_splits", "c3", args.mode)]
+        else:
+            runs.append((name, name, args.mode))
+    for key, name, mode in runs:
         try:
-            _, r2, res2, _ = measure_workload(F, name, args.mode, 0, args.steps, args.warmup, dev)
-            others[name] = res2
+            _, r2, res2, _ = measure_workload(F, name, mode, 0, args.steps, args.warmup, dev)
+            others[key] = res2
             del r2
         except F.FdecError as e:  # a workload whose path is not built yet
-            others[name] = {"error": str(e)}
-            log(f"[bench] {name}: {e}")
+            others[key] = {"error": str(e)}
+            log(f"[bench] {key}: {e}")
         _t.cuda.empty_cache()
 
     cpu = None

@@ -86,6 +86,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_cascade_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.fdec_cascade_workspace_size.restype = Z
     lib.fdec_cascade_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.fdec_decode_balanced.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F, P, P, P, Z, P]
+    lib.fdec_balanced_workspace_size.restype = Z
+    lib.fdec_balanced_workspace_size.argtypes = [I, I, I, I, I]
     if path is None:
         _lib = lib
     return lib
@@ -215,6 +218,35 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Te
                            float(softmax_scale), ctypes.byref(append) if append is not None else None,
                            int(bool(fused)), out.data_ptr(), _ptr(lse), workspace.buf.data_ptr(),
                            workspace.nbytes, _stream(q.device)))
+    return out, lse
+
+
+def balanced_workspace_size(B: int, Hq: int, Hkv: int, D: int, num_blocks: int = 0) -> int:
+    n = load_library().fdec_balanced_workspace_size(B, Hq, Hkv, D, num_blocks)
+    if n == 0:
+        raise FdecError(FDEC_ERR_INVALID_ARG, "fdec_balanced_workspace_size: bad arguments")
+    return n
+
+
+def decode_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                    page_table: Optional[torch.Tensor] = None, num_blocks: int = 0, softmax_scale: float = 0.0,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[Workspace] = None, return_lse: bool = True):
+    """fdec_decode_balanced: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32 or None)."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    kv = make_kv(k, v, page_table)
+    if q.dtype != k.dtype or not q.is_contiguous():
+        raise FdecError(FDEC_ERR_INVALID_ARG, "q must be contiguous with the cache dtype")
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = Workspace(balanced_workspace_size(B, Hq, kv.num_kv_heads, D, num_blocks), q.device)
+    _check(lib.fdec_decode_balanced(q.data_ptr(), B, Hq, ctypes.byref(kv), seq_lens.data_ptr(), int(num_blocks),
+                                    float(softmax_scale), out.data_ptr(), _ptr(lse), workspace.buf.data_ptr(),
+                                    workspace.nbytes, _stream(q.device)))
     return out, lse
 
 

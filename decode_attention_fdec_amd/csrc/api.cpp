@@ -290,6 +290,79 @@ extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv 
     return check_hip(fdec::launch_map(p, num_splits, static_cast<hipStream_t>(stream)), "fdec_decode_partials");
 }
 
+// Balanced split: blocks per group of KV heads (0 = one per compute unit over all groups).
+int balanced_blocks(int Hkv, int num_blocks) {
+    if (num_blocks > 0) return num_blocks;
+    int hpb = 1;
+    for (int w = fdec::kMapMfmaWaves; w > 1; --w)
+        if (Hkv % w == 0) {
+            hpb = w;
+            break;
+        }
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+        cu = 256;
+    return std::max(1, std::min(FDEC_MAX_SPLITS, cu / (Hkv / hpb)));
+}
+
+struct BalLayout {
+    size_t meta, pm, pd, po, total;
+};
+BalLayout bal_layout(int B, int Hq, int D, int nb) {
+    BalLayout w;
+    const size_t states = (size_t)Hq * (size_t)(nb + B);
+    w.meta = 0;
+    w.pm = align_up(w.meta + (size_t)B * 2 * sizeof(int32_t));
+    w.pd = align_up(w.pm + states * sizeof(float));
+    w.po = align_up(w.pd + states * sizeof(float));
+    w.total = align_up(w.po + states * D * sizeof(float));
+    return w;
+}
+
+extern "C" size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_blocks) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || head_dim < 1 || num_blocks < 0 || num_blocks > FDEC_MAX_SPLITS) return 0;
+    return bal_layout(B, Hq, head_dim, balanced_blocks(Hkv, num_blocks)).total;
+}
+
+extern "C" int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                                    int num_blocks, float softmax_scale, float *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    fdec_clear_error();
+    const char *fn = "fdec_decode_balanced";
+    int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
+    if (rc) return rc;
+    if (num_blocks < 0 || num_blocks > FDEC_MAX_SPLITS)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: num_blocks %d outside [0, %d]", fn, num_blocks, FDEC_MAX_SPLITS);
+    if ((int64_t)B * (((int64_t)capacity_of(kv) + 15) / 16) >= (int64_t(1) << 31))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: B * ceil(capacity / 16) must stay below 2^31", fn);
+    fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, 1, softmax_scale, nullptr);
+    if (!p.mfma)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED,
+                         "%s: needs Hq = 4 Hkv, head_dim 128 and page_size a multiple of 16 (matrix-core kernel)", fn);
+    if (B == 0) return FDEC_OK;
+    if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
+    const int nb = balanced_blocks(kv->num_kv_heads, num_blocks);
+    const BalLayout w = bal_layout(B, Hq, kv->head_dim, nb);
+    if (!workspace || workspace_bytes < w.total)
+        return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d blocks, got %zu", fn, w.total,
+                         nb, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+    char *ws = static_cast<char *>(workspace);
+    p.seg_meta = reinterpret_cast<int *>(ws + w.meta);
+    p.pm = reinterpret_cast<float *>(ws + w.pm);
+    p.pd = reinterpret_cast<float *>(ws + w.pd);
+    p.po = reinterpret_cast<float *>(ws + w.po);
+    p.nslots = nb + B;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = check_hip(fdec::launch_map_mfma_g4_balanced(p, nb, st), "fdec_decode_balanced: map launch"))) return rc;
+    return check_hip(fdec::launch_merge_segments(p.po, p.pm, p.pd, p.seg_meta, B, Hq, p.nslots, nb, kv->head_dim, out,
+                                                 lse, st),
+                     "fdec_decode_balanced: merge launch");
+}
+
 extern "C" int fdec_merge_states(const float *part_o, const float *part_m, const float *part_d, int B, int Hq,
                                  int S, int head_dim, float *out, float *lse, void *stream) {
     fdec_clear_error();

@@ -49,6 +49,9 @@ struct MapParams {
     int dtype;                  // 0 fp16, 1 bf16
     int head_dim;
     int mfma;                   // 1: matrix-core kernel (map_mfma_eligible)
+    // balanced split: states [Hq, nslots] and per-request (first slot, count)
+    int *seg_meta;
+    int nslots;
 };
 
 // Whether the matrix-core map kernel can take these parameters (mfma aside).
@@ -62,6 +65,8 @@ inline bool map_mfma_eligible(const MapParams &p) {
 // Runs the matrix-core kernel when p.mfma is set (heads_per_block <= 4).
 hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t stream);
 hipError_t launch_map_mfma_g4(const MapParams &p, int num_splits, hipStream_t stream);
+// Balanced split over nblocks blocks per group of KV heads (matrix-core kernel).
+hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t stream);
 
 // Cascade prefix: partial states of every query row over the shared prefix.
 constexpr int kPrefixPagesPerBlock = 1024;  // prefix page ids one prefix block stages in LDS
@@ -85,6 +90,11 @@ hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t
 // One wave per (b, h): merges S states into out / lse.
 hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S,
                         int head_dim, float *out, float *lse, hipStream_t stream);
+// Merge of balanced-split states: request b's states are slots
+// [meta[2b], meta[2b] + meta[2b+1]) of [Hq, nslots]; max_count bounds the counts.
+hipError_t launch_merge_segments(const float *po, const float *pm, const float *pd, const int *meta, int B, int Hq,
+                                 int nslots, int max_count, int head_dim, float *out, float *lse,
+                                 hipStream_t stream);
 
 // Zero n 32-bit words with a kernel (no memset node, so graph capture stays safe).
 hipError_t launch_zero_words(void *ptr, size_t n_words, hipStream_t stream);

@@ -19,16 +19,47 @@
 namespace {
 
 // Model constants for one MI355X (gfx950: 256 CUs, 8 TB/s HBM3E), fitted to
-// measurements of this library's map kernel (two-kernel path).
+// measurements of this library's map kernels (two-kernel path). A model block
+// is one launched block: heads_per_block KV heads over one split.
 struct CostModel {
-    double bw_total = 5.4e12;     // sustained aggregate KV read rate, bytes/s
-    double bw_block = 35.0e9;     // one map block's ceiling, bytes/s
-    int blocks_per_cu = 2;        // resident map blocks per CU
-    double t_block = 3.0e-6;      // fixed cost of a non-empty block (q load, epilogue), s
+    double bw_total;              // sustained aggregate KV read rate, bytes/s
+    double bw_block;              // one map block's ceiling, bytes/s
+    int blocks_per_cu;            // map blocks worth running per CU at once
+    int heads_per_block;          // KV heads one block reads
+    double t_block;               // fixed cost of a non-empty block (q load, epilogue), s
     double t_empty = 0.1e-6;      // an empty block, s
     double t_merge = 3.0e-6;      // merge kernel launch and latency, s
     double bytes_per_token = 2.0 * 128 * 2;  // K + V row of one KV head (D = 128, 2-byte)
 };
+
+// G = 4 runs on the matrix-core kernel: blocks of up to 4 KV heads, one block
+// per CU (a second resident block adds no bandwidth), about 42 GB/s per block
+// below saturation and 5.9 TB/s in aggregate (128k-token GQA: 93 us at 256
+// blocks, 107 us at 128). Other shapes run on the vector kernel, modelled per
+// KV head (its blocks stream each head independently).
+CostModel model_for(int Hq, int Hkv) {
+    CostModel cm;
+    if (Hq == 4 * Hkv) {
+        int hpb = 1;
+        for (int w = 4; w > 1; --w)
+            if (Hkv % w == 0) {
+                hpb = w;
+                break;
+            }
+        cm.bw_total = 5.9e12;
+        cm.bw_block = 42.0e9;
+        cm.blocks_per_cu = 1;
+        cm.heads_per_block = hpb;
+        cm.t_block = 2.0e-6;
+    } else {
+        cm.bw_total = 5.4e12;
+        cm.bw_block = 35.0e9;
+        cm.blocks_per_cu = 2;
+        cm.heads_per_block = 1;
+        cm.t_block = 3.0e-6;
+    }
+    return cm;
+}
 
 // Fluid model of one launch: blocks enter free slots in dispatch order (split
 // fastest, then KV head, then request); the active blocks share the aggregate
@@ -56,14 +87,17 @@ double makespan(const CostModel &cm, const std::vector<double> &bytes, int slots
 double estimate(const CostModel &cm, int B, int Hq, int Hkv, const std::vector<int> &lens, int cap,
                 int S, int cu_count) {
     const int64_t chunk = fdec_split_chunk(cap, S);
+    const int groups = Hkv / cm.heads_per_block;
+    const double block_bytes_per_token = cm.bytes_per_token * cm.heads_per_block;
     std::vector<double> bytes;
-    bytes.reserve((size_t)B * Hkv * S);
-    for (int b = 0; b < B; ++b) {
-        for (int g = 0; g < Hkv; ++g) {
+    bytes.reserve((size_t)B * groups * S);
+    // dispatch order of the launch: split fastest, then request, then head group
+    for (int g = 0; g < groups; ++g) {
+        for (int b = 0; b < B; ++b) {
             for (int s = 0; s < S; ++s) {
                 int64_t lo = s * chunk, hi = std::min<int64_t>((int64_t)lens[b], lo + chunk);
                 if (hi > lo)
-                    bytes.push_back((double)(hi - lo) * cm.bytes_per_token + cm.t_block * cm.bw_block);
+                    bytes.push_back((double)(hi - lo) * block_bytes_per_token + cm.t_block * cm.bw_block);
                 else
                     bytes.push_back(cm.t_empty * cm.bw_block);
             }
@@ -100,25 +134,39 @@ extern "C" int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, i
         *num_splits_out = 1;
         return FDEC_OK;
     }
-    CostModel cm;
+    const CostModel cm = model_for(Hq, Hkv);
     // Candidate split counts: every distinct chunk size, up to 64 blocks per slot.
     const int max_s = (int)std::min<int64_t>(FDEC_MAX_SPLITS, (capacity + FDEC_CHUNK_ALIGN - 1) / FDEC_CHUNK_ALIGN);
     const int64_t block_cap = (int64_t)64 * cu_count * cm.blocks_per_cu;
+    // The matrix-core kernel reaches its aggregate rate only with a block on
+    // every CU (measured: 128 or 192 blocks of a 256-CU part stream at ~5.0
+    // TB/s, 256 at 5.9), which the fluid model does not capture: when the
+    // launch is bandwidth-bound (its bytes take over 20 us at the aggregate
+    // rate), candidates start at one block per CU. Short work keeps the model's
+    // choice, which splits little.
+    const int groups = Hkv / cm.heads_per_block;
+    double total_bytes = 0.0;
+    for (int b = 0; b < B; ++b) total_bytes += (double)lens[b] * cm.bytes_per_token * Hkv;
+    const bool bw_bound = total_bytes / cm.bw_total > 20.0e-6;
+    const int s_min = (cm.blocks_per_cu == 1 && bw_bound)
+                          ? (int)std::min<int64_t>(max_s, ((int64_t)cu_count + (int64_t)B * groups - 1) /
+                                                                ((int64_t)B * groups))
+                          : 1;
     double best = 1e30;
     std::vector<std::pair<int, double>> est;
     int64_t last_chunk = -1;
-    for (int S = 1; S <= max_s; ++S) {
+    for (int S = s_min; S <= max_s; ++S) {
         int64_t chunk = fdec_split_chunk(capacity, S);
         if (chunk == last_chunk) continue;
         last_chunk = chunk;
-        if ((int64_t)B * Hkv * S > block_cap && S > 1) break;
+        if ((int64_t)B * groups * S > block_cap && S > s_min) break;
         double t = estimate(cm, B, Hq, Hkv, lens, capacity, S, cu_count);
         est.push_back({S, t});
         best = std::min(best, t);
     }
     // The smallest split count whose estimate is within 2% of the best: fewer
     // splits means fewer partial states to write and merge.
-    int pick = 1;
+    int pick = s_min;
     for (auto &e : est) {
         if (e.second <= best * 1.02) {
             pick = e.first;

@@ -78,9 +78,14 @@ __device__ __forceinline__ float sum_quarters(float x) {
 // lds_addr + 16 * lane. Issued as inline assembly so that the compiler neither
 // waits for it before unrelated LDS reads nor counts it: every wait on these
 // loads is one of the explicit waits below.
+// base and lds_addr are wave-uniform; readfirstlane states that to the compiler.
 __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds_addr)
-                 : "memory", "m0");
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t ua = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+    const uint32_t ul = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(reinterpret_cast<const char *>(ua)),
+                 "s"(ul) : "memory", "m0");
 }
 template <int N> __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
@@ -108,26 +113,19 @@ constexpr int kNbuf = FDEC_MFMA_NBUF;   // ring slots per wave: kNbuf - 1 tiles 
 static_assert(kNbuf >= 2 && kNbuf <= 8, "ring of 2..8 tiles");
 static_assert(kMapMfmaWaves * kNbuf * 2 * kMTileBytes <= 128 * 1024, "K/V ring fits in LDS");
 
+// One wave's pass over tokens [t_begin, t_end) of request b for KV head g
+// (its four query heads): the state (O~, m, d) of each query head goes to
+// po0 / pm0 / pd0 + i * hs (floats; O~ rows of D). ring / qslot are the
+// wave's LDS: kNbuf ring slots of K and V tiles and 1 KB for Q.
 template <int DT, bool PAGED>
-__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(const MapParams p) {
+__device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)[2][kMTileBytes], uint8_t *qslot,
+                                             int b, int g, int lane, int t_begin, int t_end, float *po0, float *pm0,
+                                             float *pd0, int64_t hs) {
     constexpr int D = 128, G = 4;
     using E = Elem<DT>;
-    // [wave][ring slot][K, V][tile bytes]
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
-    __shared__ int sm_flag;
-
-    const int split = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = blockIdx.z * p.heads_per_block + wv;
     const int hq0 = g * G;
     const int hme = lane & 3;  // this lane's query head in the S^T layout
     const int dq = lane >> 4;  // this lane's quarter of D in the S^T products
-
-    const int L = p.seq_lens[b];
-    const int t_begin = split * p.chunk;
-    const int t_end = min(t_begin + p.chunk, L);
     const int ntok = t_end - t_begin;
     const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
 
@@ -159,8 +157,8 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     auto stage = [&](int tile, int64_t off) {
         const int t0 = t_begin + tile * kMT;
         const int slot = tile % kNbuf;
-        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][slot][0];
-        const uint32_t vl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds[wv][slot][1];
+        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring[slot][0];
+        const uint32_t vl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring[slot][1];
         const char *kb = p.k + off, *vb = p.v + off;
 #pragma unroll
         for (int i = 0; i < kMT / 4; ++i) {
@@ -188,7 +186,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     // Q of the wave's 4 heads (1 KB) goes to LDS with the same DMA path, so
     // that every vector load the waits below count is one of these DMA loads.
     dma16(reinterpret_cast<const char *>(p.q) + ((int64_t)b * p.Hq + hq0) * D * 2, (uint32_t)lane * 16u,
-          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)qlds[wv]);
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)qslot);
     // prologue: the first kNbuf - 1 tiles
     const int npro = min(kNbuf - 1, ntiles);
     for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
@@ -198,7 +196,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     uint2 qb[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(qlds[wv] + hme * 256 + dq * 64 + 16 * c);
+        const uint4 u = *reinterpret_cast<const uint4 *>(qslot + hme * 256 + dq * 64 + 16 * c);
         qb[2 * c] = make_uint2(u.x, u.y);
         qb[2 * c + 1] = make_uint2(u.z, u.w);
     }
@@ -212,8 +210,8 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
         // this tile's loads have landed once only the later tiles' remain
         wait_vm8(min(kNbuf - 1, ntiles - 1 - tile));
         const int slot = tile % kNbuf;
-        const uint8_t *kl = lds[wv][slot][0];
-        const uint8_t *vl = lds[wv][slot][1];
+        const uint8_t *kl = ring[slot][0];
+        const uint8_t *vl = ring[slot][1];
 
         // ---- S^T = K Q^T: this lane's quarter of D, 4 pieces of 8 d-values
         f32x4_v s = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -297,19 +295,37 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     f32x4_v fs;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fs[i] = readlane(f_own, i);
-    const int64_t slot = p.s_offset + split;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t bh = (int64_t)b * p.Hq + hq0 + i;
-        float *dst = p.po + (bh * p.s_total + slot) * D;
+        float *dst = po0 + i * hs * D;
         dst[lane] = (o[0][i] + ol[0][i]) * fs[i];
         dst[64 + lane] = (o[1][i] + ol[1][i]) * fs[i];
     }
     if (lane < 4) {
-        const int64_t bh = (int64_t)b * p.Hq + hq0 + lane;
-        p.pm[bh * p.s_total + slot] = (tt == kNegInf) ? kNegInf : tt * kLn2;
-        p.pd[bh * p.s_total + slot] = lt * f_own;
+        pm0[lane * hs] = (tt == kNegInf) ? kNegInf : tt * kLn2;
+        pd0[lane * hs] = lt * f_own;
     }
+}
+
+template <int DT, bool PAGED>
+__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(const MapParams p) {
+    constexpr int D = 128, G = 4;
+    // [wave][ring slot][K, V][tile bytes]
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
+    __shared__ int sm_flag;
+
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.z * p.heads_per_block + wv;
+    const int hq0 = g * G;
+    const int L = p.seq_lens[b];
+    const int t_begin = split * p.chunk;
+    const int t_end = min(t_begin + p.chunk, L);
+    const int64_t st0 = ((int64_t)b * p.Hq + hq0) * p.s_total + p.s_offset + split;
+    mfma_segment<DT, PAGED>(p, lds[wv], qlds[wv], b, g, lane, t_begin, t_end, p.po + st0 * D, p.pm + st0,
+                            p.pd + st0, p.s_total);
 
     if (p.counters == nullptr) return;
 
@@ -331,6 +347,105 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
         merge_states_wave<D>(p.po + bh * p.s_total * D, p.pm + bh * p.s_total, p.pd + bh * p.s_total,
                              p.s_total, p.out + bh * D, p.lse ? p.lse + bh : nullptr, lane);
     }
+}
+
+// Sum and inclusive prefix sum of an int over the wave.
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+    return __builtin_amdgcn_readfirstlane(x);  // the same in every lane
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// Balanced split: the 16-token tiles of all requests, in request order, are
+// cut into gridDim.x equal ranges, one per block (per group of KV heads). A
+// block walks the requests its range touches and writes one state per request
+// piece, in slot (block + request) of [Hq, nslots] (nslots = gridDim.x + B):
+// the pieces of one request take consecutive slots. The block holding a
+// request's first tile records (first slot, piece count) in seg_meta[2b..].
+// With fewer tiles than blocks, only the first (tiles) blocks take work, so
+// every working block has at least one tile and no slot of a request is left
+// unwritten. Every wave of a block scans seq_lens itself (no block barrier).
+template <int DT, bool PAGED>
+__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
+    constexpr int D = 128, G = 4;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.z * p.heads_per_block + wv;
+    const int hq0 = g * G;
+    const int NB = gridDim.x, blk = blockIdx.x;
+
+    int NT = 0;  // tiles of all requests
+    for (int c = 0; c < p.B; c += 64) {
+        const int j = c + lane;
+        NT += wave_sum_int(j < p.B ? (p.seq_lens[j] + kMT - 1) / kMT : 0);
+    }
+    const int NBe = min(NB, NT);  // working blocks
+    // block holding tile x (x < NT), the last working block past the end
+    auto block_of = [&](int x) -> int {
+        return x >= NT ? NBe - 1 : (int)((((int64_t)x + 1) * NBe - 1) / NT);
+    };
+    const bool working = blk < NBe;
+    const int start = working ? (int)((int64_t)blk * NT / NBe) : 0;
+    const int end = working ? (int)((int64_t)(blk + 1) * NT / NBe) : 0;
+    const bool meta_writer = blockIdx.z == 0 && wv == 0;
+
+    int carry = 0;  // tiles of the requests before this group of 64
+    for (int c = 0; c < p.B; c += 64) {
+        const int j = c + lane;
+        const int L = j < p.B ? p.seq_lens[j] : 0;
+        const int T = (L + kMT - 1) / kMT;
+        const int incl = wave_incl_scan(T, lane);
+        const int P = carry + incl - T;  // first tile of request j
+        if (meta_writer && j < p.B) {
+            const int first = NT > 0 ? block_of(P) : 0;
+            if (first == blk) {
+                p.seg_meta[2 * j] = first + j;
+                p.seg_meta[2 * j + 1] = T > 0 ? block_of(P + T - 1) - first + 1 : 0;
+            }
+        }
+        uint64_t mask = __builtin_amdgcn_ballot_w64(working && j < p.B && T > 0 && P < end && P + T > start);
+        while (mask) {
+            const int l = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int bj = c + l;
+            const int Pj = __builtin_amdgcn_readlane(P, l);
+            const int Lj = __builtin_amdgcn_readlane(L, l);
+            const int Tj = __builtin_amdgcn_readlane(T, l);
+            const int ts = max(start, Pj) - Pj, te = min(end, Pj + Tj) - Pj;
+            const int64_t st0 = (int64_t)hq0 * p.nslots + blk + bj;
+            mfma_segment<DT, PAGED>(p, lds[wv], qlds[wv], bj, g, lane, ts * kMT, min(te * kMT, Lj), p.po + st0 * D,
+                                    p.pm + st0, p.pd + st0, p.nslots);
+        }
+        carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+}
+
+hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
+    dim3 grid(nblocks, 1, p.Hkv / p.heads_per_block);
+    dim3 block(64 * p.heads_per_block);
+    if (p.dtype == 0) {
+        if (p.page_table)
+            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<0, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<0, false>), grid, block, 0, st, p);
+    } else {
+        if (p.page_table)
+            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<1, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<1, false>), grid, block, 0, st, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {

@@ -202,6 +202,32 @@ int fdec_merge_states(const float *part_o, const float *part_m, const float *par
                       int S, int head_dim, float *out, float *lse, void *stream);
 
 /*
+ * Decode with a balanced split ([lpnh] §3: the work cut to fill every compute
+ * unit whatever the mix of lengths). Per group of KV heads, the 16-token tiles
+ * of all B requests, taken in request order, are cut into num_blocks equal
+ * contiguous ranges, one block each; a range may cover the end of one request
+ * and the start of the next, and its block writes one partial state per
+ * request piece. A merge then combines each request's pieces; the result is
+ * fdec_decode's up to rounding. The ranges are computed on the device from
+ * seq_lens (no host copy of the lengths), so the call may be captured in a
+ * graph whose lengths change between replays.
+ *   Supported for G = Hq/Hkv = 4, head_dim 128, page_size a multiple of 16 (or
+ *   contiguous), no append: FDEC_ERR_UNSUPPORTED otherwise.
+ *   num_blocks  blocks per group of KV heads, 1..256; 0 = one per compute unit
+ *               of the current device over all groups (measured best on MI355X:
+ *               a second block per unit only adds contention).
+ *   Requires B * ceil(capacity / 16) < 2^31 (FDEC_ERR_INVALID_ARG otherwise).
+ *   out / lse as in fdec_decode. workspace >= fdec_balanced_workspace_size()
+ *   bytes (no initialisation needed).
+ */
+int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                         int num_blocks, float softmax_scale, float *out, float *lse, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for fdec_decode_balanced (num_blocks as there, 0 = default). */
+size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_blocks);
+
+/*
  * Cascade decode with a shared prefix ([vllm-arch] cascade attention): all B
  * requests share the first prefix_len tokens, stored once in the pages
  * prefix_pages[0 .. ceil(prefix_len/page_size)); request b then has

@@ -194,3 +194,36 @@ def test_cascade_plan(fdec):
     assert sp == 1  # fewer than 256 prefix tokens: one split
     sp, ss = F.cascade_plan(1, 8, 8, 0, 64, 16)
     assert sp >= 1 and ss >= 1
+
+
+def call_balanced(kv, B=2, Hq=32, num_blocks=16, ws_bytes=1 << 30, out=FAKE, ws=FAKE):
+    lib = F.load_library()
+    return lib.fdec_decode_balanced(FAKE, B, Hq, ctypes.byref(kv), FAKE, num_blocks, 0.0, out, None, ws,
+                                    ws_bytes, None)
+
+
+def test_balanced_validation(fdec):
+    # only the matrix-core shapes: G = 4, D = 128, pages of 16k tokens
+    assert call_balanced(kv_struct(), Hq=16) == F.FDEC_ERR_UNSUPPORTED  # G = 2
+    assert call_balanced(kv_struct(head_dim=64, s_outer=4096 * 8 * 64, s_token=8 * 64, s_head=64)) == \
+        F.FDEC_ERR_UNSUPPORTED
+    assert call_balanced(kv_struct(), num_blocks=-1) == F.FDEC_ERR_INVALID_ARG
+    assert call_balanced(kv_struct(), num_blocks=F.MAX_SPLITS + 1) == F.FDEC_ERR_INVALID_ARG
+    assert call_balanced(kv_struct(), out=None) == F.FDEC_ERR_INVALID_ARG
+    need = F.balanced_workspace_size(2, 32, 8, 128, 16)
+    assert call_balanced(kv_struct(), ws_bytes=need - 1) == F.FDEC_ERR_WORKSPACE
+    assert str(need) in last_error()
+    # tiles of all requests must be countable in 31 bits
+    assert call_balanced(kv_struct(capacity=1 << 30, s_outer=(1 << 30) * 1024), B=64) == F.FDEC_ERR_INVALID_ARG
+
+
+def test_balanced_workspace_size(fdec):
+    # meta [B, 2] int32, then m, d and O~ for Hq x (num_blocks + B) slots, each array 256-byte aligned
+    def up(n):
+        return (n + 255) // 256 * 256
+    B, Hq, D, nb = 3, 32, 128, 10
+    slots = Hq * (nb + B)
+    want = up(up(up(B * 8) + slots * 4) + slots * 4) + up(slots * D * 4)
+    assert F.balanced_workspace_size(B, Hq, 8, D, nb) == want
+    with pytest.raises(F.FdecError):
+        F.balanced_workspace_size(B, Hq, 8, D, 257)
