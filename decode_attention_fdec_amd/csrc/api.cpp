@@ -94,15 +94,18 @@ int validate_common(const char *fn, const void *q, int B, int Hq, const fdec_kv 
     return FDEC_OK;
 }
 
-// KV heads (one wave each) per split-KV block: the largest divisor of Hkv up to
-// 8 waves (4 when G = 8 at D = 128, whose waves need the whole register file).
+// KV heads (one wave each) per vector split-KV block: the largest divisor of
+// Hkv up to 8 waves (4 when G = 8 at D = 128, whose waves need the whole
+// register file) that still launches a block per compute unit; with fewer
+// blocks than that even at one head per block, one head per block.
 #ifndef FDEC_HPB_CAP
 #define FDEC_HPB_CAP 8
 #endif
-int heads_per_block(int hkv, int G, int D) {
+constexpr int kTargetBlocks = 256;  // MI355X compute units
+int heads_per_block(int B, int hkv, int G, int D, int S) {
     const int cap = std::min((G >= 8 && D >= 128) ? fdec::kMapMaxWavesBig : fdec::kMapMaxWaves, FDEC_HPB_CAP);
     for (int w = cap; w > 1; --w)
-        if (hkv % w == 0) return w;
+        if (hkv % w == 0 && (int64_t)B * (hkv / w) * S >= kTargetBlocks) return w;
     return 1;
 }
 
@@ -146,7 +149,7 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     p.B = B;
     p.Hq = Hq;
     p.Hkv = kv->num_kv_heads;
-    p.heads_per_block = heads_per_block(kv->num_kv_heads, Hq / kv->num_kv_heads, kv->head_dim);
+    p.heads_per_block = heads_per_block(B, kv->num_kv_heads, Hq / kv->num_kv_heads, kv->head_dim, S);
     p.chunk = (int)fdec_split_chunk(capacity_of(kv), S);
     if (scale == 0.0f) scale = 1.0f / std::sqrt((float)kv->head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;

@@ -11,16 +11,17 @@
 // With B requests and G query heads per KV head, the prefix sees R = B*G query
 // rows per KV head (256 in the 64-request, 4:1 GQA workload): a real dense
 // contraction, so it runs on MFMA (v_mfma_f32_16x16x32_{bf16,f16}). Grid
-// (prefix split, KV head, 256-row chunk); 4 waves, each owning 64 query rows
-// (four 16-row blocks). Per 64-key tile:
+// (prefix split, KV head, 256-row chunk); 8 waves, each owning 32 query rows
+// (two 16-row blocks), two waves per SIMD so one's matrix work hides the
+// other's softmax. Per 64-key tile:
 //   - the block stages K row-major and V transposed ([d][key], key pairs packed)
 //     in LDS, double-buffered, the next tile's global loads in flight meanwhile;
 //   - S^T = K Q^T: A = K (16 keys x 32 d from LDS), B = Q^T (query rows held in
 //     registers), so each lane's result column is one query row and its four
 //     values are four keys of that row;
 //   - online softmax per row in the log2 domain (lazily moved reference as in the
-//     map kernel); P enters the matrix core rounded to the input type, while the
-//     denominator sums the fp32 weights;
+//     map kernel); P enters the matrix core rounded to the input type (hardware
+//     nearest-even conversion), while the denominator sums the fp32 weights;
 //   - O += P V: A = P straight from the S^T registers (the key order inside the
 //     K dimension is permuted identically for A and B), B = V^T from LDS.
 // Layout of v_mfma_f32_16x16x32 (lane l, kq = l / 16): A holds row l % 16,
@@ -50,19 +51,32 @@ template <> struct Mfma<1> {
 };
 
 constexpr int kPfxKeys = 64;            // keys per tile
-constexpr int kPfxRowsPerWave = 64;     // query rows per wave
-constexpr int kPfxRows = 4 * kPfxRowsPerWave;
+constexpr int kPfxWaves = 8;
+constexpr int kPfxRowsPerWave = 32;     // query rows per wave
+constexpr int kRB = kPfxRowsPerWave / 16;
+constexpr int kPfxRows = kPfxWaves * kPfxRowsPerWave;
+constexpr int kPfxThreads = 64 * kPfxWaves;
+
+// Two 16-bit values packed (lo, hi), rounded to nearest even by the hardware.
+template <int DT> __device__ __forceinline__ uint32_t pfx_pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pfx_pack2<0>(float a, float b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+}
+template <> __device__ __forceinline__ uint32_t pfx_pack2<1>(float a, float b) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
+}
 constexpr int kKStride = 128 + 8;       // K tile row stride in elements (padding vs bank conflicts)
 constexpr int kVStride = kPfxKeys + 4;  // V^T tile row stride in elements
 
 template <int DT>
-__global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadeParams p) {
+__global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const CascadeParams p) {
     constexpr int D = 128;
-    using E = Elem<DT>;
     __shared__ __attribute__((aligned(16))) uint16_t sk[2][kPfxKeys * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * kVStride];
     __shared__ int spages[kPrefixPagesPerBlock];
-    __shared__ float srow[4][3][kPfxRowsPerWave];
+    __shared__ float srow[kPfxWaves][3][kPfxRowsPerWave];
 
     const int split = blockIdx.x, g = blockIdx.y, rc = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -77,12 +91,12 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
     // page ids of this split's keys
     const int pg0 = t_begin / p.page_size;
     const int npg = ntiles > 0 ? (t_end - 1) / p.page_size - pg0 + 1 : 0;
-    for (int i = tid; i < npg; i += 256) spages[i] = p.prefix_pages[pg0 + i];
+    for (int i = tid; i < npg; i += kPfxThreads) spages[i] = p.prefix_pages[pg0 + i];
 
-    // query rows of this wave: row = rc*256 + 64w + 16rb + li; B operand per (rb, ks)
-    uint4 qb[4][4];
+    // query rows of this wave: row = rc*256 + 32w + 16rb + li; B operand per (rb, ks)
+    uint4 qb[kRB][4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
         const int row = rc * kPfxRows + w * kPfxRowsPerWave + rb * 16 + li;
         const bool ok = row < R;
         const int b = ok ? row / G : 0, hh = ok ? row - (row / G) * G : 0;
@@ -93,14 +107,14 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
     }
     __syncthreads();
 
-    // Staging: thread t covers rows 2*(t/16) + {0, 1} (+32) of a tile, d piece 8*(t%16).
+    // Staging: thread t covers rows 2*(t/16) + {0, 1} of a tile, d piece 8*(t%16).
     const int srow0 = 2 * (tid >> 4), dpiece = 8 * (tid & 15);
-    uint4 rk[4], rv[4];  // rows srow0, srow0+1, srow0+32, srow0+33
+    uint4 rk[2], rv[2];  // rows srow0, srow0+1
     auto load_tile = [&](int tile) {
         const int t0 = t_begin + tile * kPfxKeys;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = srow0 + (i & 1) + 32 * (i >> 1);
+        for (int i = 0; i < 2; ++i) {
+            const int r = srow0 + i;
             const int t = t0 + r;
             if (t < t_end) {
                 const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
@@ -117,15 +131,14 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = srow0 + (i & 1) + 32 * (i >> 1);
+        for (int i = 0; i < 2; ++i) {
+            const int r = srow0 + i;
             *reinterpret_cast<uint4 *>(&sk[buf][r * kKStride + dpiece]) = rk[i];
         }
         // V^T: dword (key r, key r + 1) for each d of the piece
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint4 a = rv[2 * h], c = rv[2 * h + 1];
-            const int r = srow0 + 32 * h;
+        {
+            const uint4 a = rv[0], c = rv[1];
+            const int r = srow0;
             const uint32_t av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -139,10 +152,10 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
 
     constexpr float kTau = 8.0f;
     constexpr float kFloor = -1.0e30f;
-    float m[4], tmax[4], l[4];
-    f32x4_v o[4][8];
+    float m[kRB], tmax[kRB], l[kRB];
+    f32x4_v o[kRB][8];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
         m[rb] = kFloor;
         tmax[rb] = kNegInf;
         l[rb] = 0.0f;
@@ -163,25 +176,25 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
         const uint16_t *V = sv[buf];
 
         // ---- S^T = K Q^T: s[kb][rb] holds keys 16kb + 4kq + r of row 16rb + li
-        f32x4_v s[4][4];
+        f32x4_v s[4][kRB];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) s[kb][rb] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int rb = 0; rb < kRB; ++rb) s[kb][rb] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const uint4 a = *reinterpret_cast<const uint4 *>(&K[(16 * kb + li) * kKStride + 32 * ks + 8 * kq]);
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) s[kb][rb] = Mfma<DT>::run(a, qb[rb][ks], s[kb][rb]);
+                for (int rb = 0; rb < kRB; ++rb) s[kb][rb] = Mfma<DT>::run(a, qb[rb][ks], s[kb][rb]);
             }
         }
 
         // ---- online softmax per query row
         const int nvalid = t_end - t0;
         bool move = false;
-        float mx[4];
+        float mx[kRB];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
             float x = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
             // move the reference; O rows live in lanes by (kq, r), so the
             // per-row factors go through LDS
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
+            for (int rb = 0; rb < kRB; ++rb) {
                 const float mn = fmaxf(m[rb], mx[rb]);
                 const float alpha = fexp2(m[rb] - mn);
                 m[rb] = mn;
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float alpha = srow[w][0][16 * rb + 4 * kq + r];
@@ -223,9 +236,9 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
         // P rounded to the input type, packed as the A operand of P V (the sum of
         // weights stays in fp32): K-slot 8kq + e is key
         // 32kk + 4kq + e (e < 4) or 32kk + 16 + 4kq + (e - 4) (e >= 4)
-        uint4 pa[4][2];
+        uint4 pa[kRB][2];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
             float ps = 0.0f;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -233,15 +246,14 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
 #pragma unroll
                 for (int hbk = 0; hbk < 2; ++hbk) {
                     const int kb = 2 * kk + hbk;
-                    uint16_t e4[4];
+                    float pv[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float pv = fexp2(s[kb][rb][r] - m[rb]);
-                        ps += pv;  // the denominator keeps fp32 weights
-                        e4[r] = E::from_float(pv);
+                        pv[r] = fexp2(s[kb][rb][r] - m[rb]);
+                        ps += pv[r];  // the denominator keeps fp32 weights
                     }
-                    wv[2 * hbk] = (uint32_t)e4[0] | ((uint32_t)e4[1] << 16);
-                    wv[2 * hbk + 1] = (uint32_t)e4[2] | ((uint32_t)e4[3] << 16);
+                    wv[2 * hbk] = pfx_pack2<DT>(pv[0], pv[1]);
+                    wv[2 * hbk + 1] = pfx_pack2<DT>(pv[2], pv[3]);
                 }
                 pa[rb][kk] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
@@ -258,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
                 const uint2 v1 = *reinterpret_cast<const uint2 *>(vrow + 16);
                 const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
+                for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
             }
         }
 
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
 
     // ---- states against the true maximum: O~ = O 2^(m - T), d = l 2^(m - T)
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
         float lt = l[rb];
         lt += shfl_xor(lt, 16);
         lt += shfl_xor(lt, 32);
@@ -286,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void cascade_prefix_kernel(const CascadePar
     __builtin_amdgcn_wave_barrier();
     const int64_t slot = p.s_offset + split;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int rl = 16 * rb + 4 * kq + r;
@@ -310,9 +322,9 @@ hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t
     const int R = p.B * (p.Hq / p.Hkv);
     dim3 grid(splits, p.Hkv, (R + kPfxRows - 1) / kPfxRows);
     if (p.dtype == 0)
-        hipLaunchKernelGGL(cascade_prefix_kernel<0>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL(cascade_prefix_kernel<0>, grid, dim3(kPfxThreads), 0, st, p);
     else
-        hipLaunchKernelGGL(cascade_prefix_kernel<1>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL(cascade_prefix_kernel<1>, grid, dim3(kPfxThreads), 0, st, p);
     return hipGetLastError();
 }
 

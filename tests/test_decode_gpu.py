@@ -310,3 +310,59 @@ def test_c2_fixed_16_splits_equals_planned_splits():
     op, lp = run(case, num_splits=S_plan)
     assert (o16 - op).abs().max().item() < 1e-4
     assert ((l16 - lp).abs() / l16.abs().clamp(min=1)).max().item() < 1e-6
+
+
+# ---------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("name", ["gqa4_paged", "gqa2_contig", "append_rope"])
+def test_graph_replays_match_eager_bitwise(name, fused):
+    # one step captured as a HIP graph and replayed several times, with eager
+    # work and synchronisations between the replays; every replay must give
+    # the eager result bit for bit (no memset nodes: the fused path's counters
+    # return to zero by themselves)
+    append = None
+    if name == "gqa4_paged":
+        case = paged_case(58, 3, 32, 8, 128, [700, 33, 1500], 16, BF16, extra_pages=3, pad="nan")
+    elif name == "gqa2_contig":
+        case = contiguous_case(59, 2, 16, 8, 128, [999, 250], 1024, F16, pad="nan")
+    else:
+        case = append_case(60, 2, 32, 8, 128, 512, F16, rotary_dim=128, base=10000.0, pad="nan")
+    d = to_dev(case)
+    B, Hq, D = case.q.shape
+    S = 7
+    if case.k_new is not None:
+        append = F.make_append(d["k_new"], d["v_new"], d["rope_cos"], d["rope_sin"], case.rotary_dim)
+    k0, v0 = d["k"].clone(), d["v"].clone()
+    ws = F.Workspace(F.workspace_size(B, Hq, case.Hkv, D, S), DEV)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+
+    def step():
+        F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S,
+                 append=append, fused=fused, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.zero_()
+        lse.zero_()
+        if append is not None:  # the append rewrites the same rows each replay
+            d["k"].copy_(k0)
+            d["v"].copy_(v0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o)
+    if fused:
+        assert torch.count_nonzero(ws.buf[: B * case.Hkv * 4].view(torch.int32)).item() == 0
