@@ -124,7 +124,11 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
                 kd[i] = E::from_float(ks[i]);
                 vd[i] = vsrc[i];
             }
-            __threadfence();  // the row is read back by this wave below
+            // this wave reads the row back below, through the same L2; no
+            // earlier load of this kernel cached it in L1: completing the
+            // stores is enough (an agent-scope fence would also write the
+            // XCD's L2 back to memory)
+            __builtin_amdgcn_s_waitcnt(0);
         }
     } else {
         const uint16_t *qsrc = reinterpret_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hq + hq0) * D;
@@ -149,7 +153,7 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
                     kd[i] = ksrc[i];
                     vd[i] = vsrc[i];
                 }
-                __threadfence();  // the row is read back by this wave below
+                __builtin_amdgcn_s_waitcnt(0);  // as above: the stores complete before the read-back
             }
         }
     }
