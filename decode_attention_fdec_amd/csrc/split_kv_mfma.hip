@@ -112,94 +112,223 @@ constexpr int kMTileBytes = kMT * 256;  // one tile of K (or V) rows of one KV h
 constexpr int kNbuf = FDEC_MFMA_NBUF;   // ring slots per wave: kNbuf - 1 tiles in flight ahead
 static_assert(kNbuf >= 2 && kNbuf <= 8, "ring of 2..8 tiles");
 static_assert(kMapMfmaWaves * kNbuf * 2 * kMTileBytes <= 128 * 1024, "K/V ring fits in LDS");
+constexpr float kTau = 8.0f;            // the softmax reference moves when a score exceeds it by 2^kTau
+constexpr float kFloor = -1.0e30f;      // initial reference (finite: masked scores give p = 0, no NaN)
 
-// One wave's pass over tokens [t_begin, t_end) of request b for KV head g
-// (its four query heads): the state (O~, m, d) of each query head goes to
-// po0 / pm0 / pd0 + i * hs (floats; O~ rows of D). ring / qslot are the
-// wave's LDS: kNbuf ring slots of K and V tiles and 1 KB for Q.
-template <int DT, bool PAGED>
-__device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)[2][kMTileBytes], uint8_t *qslot,
-                                             int b, int g, int lane, int t_begin, int t_end, float *po0, float *pm0,
-                                             float *pd0, int64_t hs) {
-    constexpr int D = 128, G = 4;
-    using E = Elem<DT>;
-    const int hq0 = g * G;
-    const int hme = lane & 3;  // this lane's query head in the S^T layout
-    const int dq = lane >> 4;  // this lane's quarter of D in the S^T products
-    const int ntok = t_end - t_begin;
-    const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
+// LDS address of a shared-memory pointer, for m0.
+__device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)ptr;
+}
 
-    // Global -> LDS staging. Instruction i (0..3) of a tile writes rows
-    // 4i..4i+3: lane l fills slot (l & 15) of row r = 4i + l / 16 with 16-byte
-    // piece (l & 15) ^ swz(r) of that row; piece c of row r therefore sits in
-    // slot c ^ swz(r). K rows use swz = r (an S^T read takes one piece of each
-    // of the 16 rows per quarter wave), V rows swz = 4 (r & 3) (a transpose
-    // read takes 4 pieces of 4 consecutive rows per half wave). Rows past the
-    // end of the split repeat its last row. A tile of a paged cache lies on one
-    // page (page_size and chunk are multiples of 16): one page id per tile,
-    // read with a scalar load a tile before it is staged.
+// Global -> LDS staging of one 16-token tile of one KV head. Instruction i
+// (0..3) writes rows 4i..4i+3: lane l fills slot (l & 15) of row r = 4i + l / 16
+// with 16-byte piece (l & 15) ^ swz(r) of that row; piece c of row r therefore
+// sits in slot c ^ swz(r). K rows use swz = r (an S^T read takes one piece of
+// each of the 16 rows per quarter wave), V rows swz = 4 (r & 3) (a transpose
+// read takes 4 pieces of 4 consecutive rows per half wave). kb / vb address the
+// tile's first row; rows past nrows repeat row nrows - 1.
+__device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint32_t kl, uint32_t vl, int nrows,
+                                           uint32_t stok2, int lane) {
     const int srow = lane >> 4, sslot = lane & 15;
-    typedef const __attribute__((address_space(4))) int32_t *cpage_t;
-    const cpage_t ptab = PAGED ? (cpage_t)(p.page_table + (int64_t)b * p.max_pages) : nullptr;
-    const int64_t stok2 = p.s_token * 2;
-    const int64_t head2 = (int64_t)g * p.s_head * 2;
-    // byte offset of the first token of a tile (uniform)
-    auto tile_offset = [&](int tile) -> int64_t {
-        const int t = t_begin + tile * kMT;
-        if constexpr (PAGED) {
-            const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : (t / p.page_size);
-            const int64_t page = ptab[pidx];
-            return (page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token) * 2 + head2;
-        } else {
-            return ((int64_t)b * p.s_outer + (int64_t)t * p.s_token) * 2 + head2;
-        }
-    };
-    auto stage = [&](int tile, int64_t off) {
-        const int t0 = t_begin + tile * kMT;
-        const int slot = tile % kNbuf;
-        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring[slot][0];
-        const uint32_t vl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring[slot][1];
-        const char *kb = p.k + off, *vb = p.v + off;
 #pragma unroll
-        for (int i = 0; i < kMT / 4; ++i) {
-            const int r = 4 * i + srow;
-            const uint32_t row = (uint32_t)(min(t0 + r, t_end - 1) - t0) * (uint32_t)stok2;
-            dma16(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
-            dma16(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
-        }
-    };
+    for (int i = 0; i < kMT / 4; ++i) {
+        const int r = 4 * i + srow;
+        const uint32_t row = (uint32_t)min(r, nrows - 1) * stok2;
+        dma16(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
+        dma16(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
+    }
+}
 
-    constexpr float kTau = 8.0f;
-    constexpr float kFloor = -1.0e30f;
-    float m_own = kFloor, t_own = kNegInf, l_own = 0.0f;  // per head hme
-    // P enters the P V products as hi + lo, two 16-bit parts whose sum
-    // carries about 16 significant bits, so O is accumulated from P at close
-    // to fp32 accuracy; o[] takes the hi parts, ol[] the lo parts.
-    f32x4_v o[2] = {f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}};
-    f32x4_v ol[2] = {f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}};
+// Byte offset of token t of request b, KV head g (uniform). A tile of a paged
+// cache lies on one page (page_size and tile starts are multiples of 16); the
+// page id comes from a scalar load.
+template <bool PAGED>
+__device__ __forceinline__ int64_t token_offset(const MapParams &p, int b, int g, int t) {
+    if constexpr (PAGED) {
+        typedef const __attribute__((address_space(4))) int32_t *cpage_t;
+        const cpage_t ptab = (cpage_t)(p.page_table + (int64_t)b * p.max_pages);
+        const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : (t / p.page_size);
+        const int64_t page = ptab[pidx];
+        return (page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head) * 2;
+    } else {
+        return ((int64_t)b * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head) * 2;
+    }
+}
 
-    // S^T reads: lane L takes token L & 15, pieces 4 dq .. 4 dq + 3
-    const int rk = lane & 15;
-    // transpose reads: lane L = 16 gq + 4 k + a takes token 4q + k, d = 64h + 16 gq + 4a
-    const int tk = (lane & 15) >> 2, ta = lane & 3, tg = lane >> 4;
+// Q of the four query heads of KV head g of request b (1 KB) to LDS, with the
+// same DMA path, so that every vector load the waits count is a DMA load.
+__device__ __forceinline__ void stage_q(const MapParams &p, int b, int g, uint8_t *qslot, int lane) {
+    dma16(reinterpret_cast<const char *>(p.q) + ((int64_t)b * p.Hq + 4 * g) * 128 * 2, (uint32_t)lane * 16u,
+          lds_addr(qslot));
+}
 
-    // Q of the wave's 4 heads (1 KB) goes to LDS with the same DMA path, so
-    // that every vector load the waits below count is one of these DMA loads.
-    dma16(reinterpret_cast<const char *>(p.q) + ((int64_t)b * p.Hq + hq0) * D * 2, (uint32_t)lane * 16u,
-          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)qslot);
-    // prologue: the first kNbuf - 1 tiles
-    const int npro = min(kNbuf - 1, ntiles);
-    for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
-    int64_t noff = (kNbuf - 1 < ntiles) ? tile_offset(kNbuf - 1) : 0;  // next tile to stage
-    wait_vm8(npro);  // Q has landed
-    // Q^T as the B operand: K-step k of quarter dq = d 32 dq + 4k .. +3 of head hme
-    uint2 qb[8];
+// Q^T as the B operand of S^T: K-step k of quarter dq = d 32 dq + 4k .. +3 of
+// head lane & 3.
+__device__ __forceinline__ void read_q(const uint8_t *qslot, int lane, uint2 qb[8]) {
+    const int hme = lane & 3, dq = lane >> 4;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const uint4 u = *reinterpret_cast<const uint4 *>(qslot + hme * 256 + dq * 64 + 16 * c);
         qb[2 * c] = make_uint2(u.x, u.y);
         qb[2 * c + 1] = make_uint2(u.z, u.w);
     }
+}
+
+// The running softmax of one wave (four query heads; head lane & 3 in the S^T
+// layout): reference m, true maximum t, sum l, and O as hi / lo accumulators
+// (P enters P V as hi + lo, two 16-bit parts whose sum carries about 16
+// significant bits, so O is accumulated from P at close to fp32 accuracy).
+struct MfmaSoftmax {
+    float m, t, l;
+    f32x4_v o[2], ol[2];
+    __device__ __forceinline__ void reset() {
+        m = kFloor;
+        t = kNegInf;
+        l = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            o[h] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+            ol[h] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+};
+
+// One tile: S^T = K Q^T, online softmax, O += P V. nvalid (>= 1) tokens of the
+// tile count; the rest are masked.
+template <int DT>
+__device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 qb[8], int nvalid,
+                                          float scale_log2, int lane, MfmaSoftmax &st) {
+    using E = Elem<DT>;
+    const int dq = lane >> 4;
+    const int rk = lane & 15;  // S^T reads: token L & 15, pieces 4 dq .. 4 dq + 3
+    // transpose reads: lane L = 16 gq + 4 k + a takes token 4q + k, d = 64h + 16 gq + 4a
+    const int tk = (lane & 15) >> 2, ta = lane & 3, tg = lane >> 4;
+
+    // ---- S^T = K Q^T: this lane's quarter of D, 4 pieces of 8 d-values
+    f32x4_v s = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * ((4 * dq + c) ^ rk));
+        s = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[2 * c], s);
+        s1 = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[2 * c + 1], s1);
+    }
+
+    // ---- softmax for head lane & 3, tokens 4 tg .. 4 tg + 3 of this tile
+    // (lanes 0..15 carry the tile; the others hold copies and stay masked)
+    float sv[4], mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float x = sum_quarters(s[r] + s1[r]);
+        const int tok = 4 * ((lane >> 2) & 3) + r;
+        sv[r] = (tok < nvalid && lane < 16) ? x * scale_log2 : kNegInf;
+        mx = fmax_nc(mx, sv[r]);
+    }
+    st.t = fmax_nc(st.t, mx);
+    if (__builtin_amdgcn_ballot_w64(mx > st.m + kTau) != 0) {
+        // move the reference of every head to its running maximum
+        float hm = mx;
+        hm = fmax_nc(hm, shfl_xor(hm, 4));
+        hm = fmax_nc(hm, shfl_xor(hm, 8));
+        hm = fmax_nc(hm, shfl_xor(hm, 16));
+        hm = fmax_nc(hm, shfl_xor(hm, 32));
+        const float mn = fmax_nc(st.m, hm);
+        const float alpha = fexp2(st.m - mn);
+        st.m = mn;
+        st.l *= alpha;
+        f32x4_v al;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = readlane(alpha, i);  // lanes 0..3 carry heads 0..3
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            st.o[h] *= al;
+            st.ol[h] *= al;
+        }
+    }
+    uint32_t ph[2], pl[2];
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {
+        const float p0 = fexp2(sv[r] - st.m), p1 = fexp2(sv[r + 1] - st.m);
+        st.l += p0 + p1;
+        const uint32_t h = pack2<DT>(p0, p1);
+        ph[r / 2] = h;
+        pl[r / 2] = pack2<DT>(p0 - E::lo(h), p1 - E::hi(h));
+    }
+    const uint2 pa = make_uint2(ph[0], ph[1]), pb = make_uint2(pl[0], pl[1]);
+
+    // ---- O += P V over the tile's 4 groups of 4 tokens
+#define FDEC_PV_STEP(Q)                                                                                       \
+    {                                                                                                         \
+        const int row = 4 * (Q) + tk;                                                                         \
+        _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                       \
+            const int piece = 8 * h + 2 * tg + (ta >> 1);                                                     \
+            lds_s16x4 *src = (lds_s16x4 *)(vl + row * 256 + 16 * (piece ^ (4 * (row & 3))) + 8 * (ta & 1));    \
+            const s16x4_v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);                                  \
+            st.o[h] = Mfma4<DT>::template run<4, (Q)>(pa, __builtin_bit_cast(uint2, vt), st.o[h]);            \
+            st.ol[h] = Mfma4<DT>::template run<4, (Q)>(pb, __builtin_bit_cast(uint2, vt), st.ol[h]);          \
+        }                                                                                                     \
+    }
+    FDEC_PV_STEP(0)
+    FDEC_PV_STEP(1)
+    FDEC_PV_STEP(2)
+    FDEC_PV_STEP(3)
+#undef FDEC_PV_STEP
+}
+
+// The wave's state per head against the true maximum T: O~ = 2^(m - T) O,
+// d = 2^(m - T) l, m = T ln 2 (an empty state is (0, -inf, 0)); head i's goes to
+// po0 + i hs D, pm0 + i hs, pd0 + i hs.
+__device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, float *po0, float *pm0, float *pd0,
+                                            int64_t hs) {
+    constexpr int D = 128;
+    float lt = st.l, tt = st.t;
+#pragma unroll
+    for (int x = 4; x <= 32; x <<= 1) {
+        lt += shfl_xor(lt, x);
+        tt = fmax_nc(tt, shfl_xor(tt, x));
+    }
+    const float f_own = (tt == kNegInf) ? 0.0f : fexp2(st.m - tt);
+    f32x4_v fs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fs[i] = readlane(f_own, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float *dst = po0 + i * hs * D;
+        dst[lane] = (st.o[0][i] + st.ol[0][i]) * fs[i];
+        dst[64 + lane] = (st.o[1][i] + st.ol[1][i]) * fs[i];
+    }
+    if (lane < 4) {
+        pm0[lane * hs] = (tt == kNegInf) ? kNegInf : tt * kLn2;
+        pd0[lane * hs] = lt * f_own;
+    }
+}
+
+// One wave's pass over tokens [t_begin, t_end) of request b for KV head g
+// (its four query heads), state to po0 / pm0 / pd0 (+ i hs per head). ring /
+// qslot are the wave's LDS: kNbuf ring slots of K and V tiles and 1 KB of Q.
+template <int DT, bool PAGED>
+__device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)[2][kMTileBytes], uint8_t *qslot,
+                                             int b, int g, int lane, int t_begin, int t_end, float *po0, float *pm0,
+                                             float *pd0, int64_t hs) {
+    const int ntok = t_end - t_begin;
+    const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
+    const uint32_t stok2 = (uint32_t)(p.s_token * 2);
+    auto stage = [&](int tile, int64_t off) {
+        const int slot = tile % kNbuf;
+        stage_tile(p.k + off, p.v + off, lds_addr(ring[slot][0]), lds_addr(ring[slot][1]),
+                   t_end - (t_begin + tile * kMT), stok2, lane);
+    };
+    auto tile_offset = [&](int tile) { return token_offset<PAGED>(p, b, g, t_begin + tile * kMT); };
+
+    MfmaSoftmax st;
+    st.reset();
+    stage_q(p, b, g, qslot, lane);
+    // prologue: the first kNbuf - 1 tiles
+    const int npro = min(kNbuf - 1, ntiles);
+    for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
+    int64_t noff = (kNbuf - 1 < ntiles) ? tile_offset(kNbuf - 1) : 0;  // next tile to stage
+    wait_vm8(npro);  // Q has landed
+    uint2 qb[8];
+    read_q(qslot, lane, qb);
 
     for (int tile = 0; tile < ntiles; ++tile) {
         const int ahead = tile + kNbuf - 1;
@@ -210,101 +339,9 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)
         // this tile's loads have landed once only the later tiles' remain
         wait_vm8(min(kNbuf - 1, ntiles - 1 - tile));
         const int slot = tile % kNbuf;
-        const uint8_t *kl = ring[slot][0];
-        const uint8_t *vl = ring[slot][1];
-
-        // ---- S^T = K Q^T: this lane's quarter of D, 4 pieces of 8 d-values
-        f32x4_v s = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * ((4 * dq + c) ^ rk));
-            s = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[2 * c], s);
-            s1 = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[2 * c + 1], s1);
-        }
-
-        // ---- softmax for head hme, tokens 4 tg .. 4 tg + 3 of this tile
-        // (lanes 0..15 carry the tile; the others hold copies and stay masked)
-        const int nvalid = t_end - (t_begin + tile * kMT);
-        float sv[4], mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float x = sum_quarters(s[r] + s1[r]);
-            const int tok = 4 * ((lane >> 2) & 3) + r;
-            sv[r] = (tok < nvalid && lane < 16) ? x * p.scale_log2 : kNegInf;
-            mx = fmax_nc(mx, sv[r]);
-        }
-        t_own = fmax_nc(t_own, mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m_own + kTau) != 0) {
-            // move the reference of every head to its running maximum
-            float hm = mx;
-            hm = fmax_nc(hm, shfl_xor(hm, 4));
-            hm = fmax_nc(hm, shfl_xor(hm, 8));
-            hm = fmax_nc(hm, shfl_xor(hm, 16));
-            hm = fmax_nc(hm, shfl_xor(hm, 32));
-            const float mn = fmax_nc(m_own, hm);
-            const float alpha = fexp2(m_own - mn);
-            m_own = mn;
-            l_own *= alpha;
-            f32x4_v al;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = readlane(alpha, i);  // lanes 0..3 carry heads 0..3
-            o[0] *= al;
-            o[1] *= al;
-            ol[0] *= al;
-            ol[1] *= al;
-        }
-        uint32_t ph[2], pl[2];
-#pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-            const float p0 = fexp2(sv[r] - m_own), p1 = fexp2(sv[r + 1] - m_own);
-            l_own += p0 + p1;
-            const uint32_t h = pack2<DT>(p0, p1);
-            ph[r / 2] = h;
-            pl[r / 2] = pack2<DT>(p0 - E::lo(h), p1 - E::hi(h));
-        }
-        const uint2 pa = make_uint2(ph[0], ph[1]), pb = make_uint2(pl[0], pl[1]);
-
-        // ---- O += P V over the tile's 4 groups of 4 tokens
-#define FDEC_PV_STEP(Q)                                                                                       \
-    {                                                                                                         \
-        const int row = 4 * (Q) + tk;                                                                         \
-        _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                       \
-            const int piece = 8 * h + 2 * tg + (ta >> 1);                                                     \
-            lds_s16x4 *src = (lds_s16x4 *)(vl + row * 256 + 16 * (piece ^ (4 * (row & 3))) + 8 * (ta & 1));    \
-            const s16x4_v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);                                  \
-            o[h] = Mfma4<DT>::template run<4, (Q)>(pa, __builtin_bit_cast(uint2, vt), o[h]);                  \
-            ol[h] = Mfma4<DT>::template run<4, (Q)>(pb, __builtin_bit_cast(uint2, vt), ol[h]);                \
-        }                                                                                                     \
+        mfma_tile<DT>(ring[slot][0], ring[slot][1], qb, t_end - (t_begin + tile * kMT), p.scale_log2, lane, st);
     }
-        FDEC_PV_STEP(0)
-        FDEC_PV_STEP(1)
-        FDEC_PV_STEP(2)
-        FDEC_PV_STEP(3)
-#undef FDEC_PV_STEP
-    }
-
-    // ---- the wave's state per head against the true maximum T:
-    // O~ = 2^(m - T) O, d = 2^(m - T) l
-    float lt = l_own, tt = t_own;
-#pragma unroll
-    for (int x = 4; x <= 32; x <<= 1) {
-        lt += shfl_xor(lt, x);
-        tt = fmax_nc(tt, shfl_xor(tt, x));
-    }
-    const float f_own = (tt == kNegInf) ? 0.0f : fexp2(m_own - tt);
-    f32x4_v fs;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fs[i] = readlane(f_own, i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float *dst = po0 + i * hs * D;
-        dst[lane] = (o[0][i] + ol[0][i]) * fs[i];
-        dst[64 + lane] = (o[1][i] + ol[1][i]) * fs[i];
-    }
-    if (lane < 4) {
-        pm0[lane * hs] = (tt == kNegInf) ? kNegInf : tt * kLn2;
-        pd0[lane * hs] = lt * f_own;
-    }
+    write_state(st, lane, po0, pm0, pd0, hs);
 }
 
 template <int DT, bool PAGED>
@@ -366,29 +403,37 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 
 // Balanced split: the 16-token tiles of all requests, in request order, are
 // cut into gridDim.x equal ranges, one per block (per group of KV heads). A
-// block walks the requests its range touches and writes one state per request
-// piece, in slot (block + request) of [Hq, nslots] (nslots = gridDim.x + B):
-// the pieces of one request take consecutive slots. The block holding a
+// block streams its range as one sequence of tiles across request boundaries
+// (the DMA ring never drains between requests): at each boundary it writes
+// the finished piece's state to slot (block + request) of [Hq, nslots]
+// (nslots = gridDim.x + B; the pieces of one request take consecutive slots)
+// and resets its softmax. Q of each request is staged by DMA ahead of the
+// request's first tile into one of kNbuf Q slots. The block holding a
 // request's first tile records (first slot, piece count) in seg_meta[2b..].
 // With fewer tiles than blocks, only the first (tiles) blocks take work, so
 // every working block has at least one tile and no slot of a request is left
-// unwritten. Every wave of a block scans seq_lens itself (no block barrier).
+// unwritten. Every wave scans seq_lens itself (no block barrier).
 template <int DT, bool PAGED>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
     constexpr int D = 128, G = 4;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][kNbuf][G * D * 2];
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = blockIdx.z * p.heads_per_block + wv;
     const int hq0 = g * G;
     const int NB = gridDim.x, blk = blockIdx.x;
+    const uint32_t stok2 = (uint32_t)(p.s_token * 2);
 
+    // ---- the block's tile range and its first request
+    const bool one_pass = p.B <= 64;  // lengths stay in registers between the passes
+    const int L0 = lane < p.B ? p.seq_lens[lane] : 0;
     int NT = 0;  // tiles of all requests
     for (int c = 0; c < p.B; c += 64) {
         const int j = c + lane;
-        NT += wave_sum_int(j < p.B ? (p.seq_lens[j] + kMT - 1) / kMT : 0);
+        const int L = one_pass ? L0 : (j < p.B ? p.seq_lens[j] : 0);
+        NT += wave_sum_int((L + kMT - 1) / kMT);
     }
     const int NBe = min(NB, NT);  // working blocks
     // block holding tile x (x < NT), the last working block past the end
@@ -400,10 +445,11 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const int end = working ? (int)((int64_t)(blk + 1) * NT / NBe) : 0;
     const bool meta_writer = blockIdx.z == 0 && wv == 0;
 
-    int carry = 0;  // tiles of the requests before this group of 64
+    int b0 = -1, P0 = 0, T0 = 0;  // first request of the range and its first tile
+    int carry = 0;                // tiles of the requests before this group of 64
     for (int c = 0; c < p.B; c += 64) {
         const int j = c + lane;
-        const int L = j < p.B ? p.seq_lens[j] : 0;
+        const int L = one_pass ? L0 : (j < p.B ? p.seq_lens[j] : 0);
         const int T = (L + kMT - 1) / kMT;
         const int incl = wave_incl_scan(T, lane);
         const int P = carry + incl - T;  // first tile of request j
@@ -414,21 +460,78 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
                 p.seg_meta[2 * j + 1] = T > 0 ? block_of(P + T - 1) - first + 1 : 0;
             }
         }
-        uint64_t mask = __builtin_amdgcn_ballot_w64(working && j < p.B && T > 0 && P < end && P + T > start);
-        while (mask) {
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(working && j < p.B && T > 0 && P <= start && start < P + T);
+        if (b0 < 0 && mask) {
             const int l = __builtin_ctzll(mask);
-            mask &= mask - 1;
-            const int bj = c + l;
-            const int Pj = __builtin_amdgcn_readlane(P, l);
-            const int Lj = __builtin_amdgcn_readlane(L, l);
-            const int Tj = __builtin_amdgcn_readlane(T, l);
-            const int ts = max(start, Pj) - Pj, te = min(end, Pj + Tj) - Pj;
-            const int64_t st0 = (int64_t)hq0 * p.nslots + blk + bj;
-            mfma_segment<DT, PAGED>(p, lds[wv], qlds[wv], bj, g, lane, ts * kMT, min(te * kMT, Lj), p.po + st0 * D,
-                                    p.pm + st0, p.pd + st0, p.nslots);
+            b0 = c + l;
+            P0 = __builtin_amdgcn_readlane(P, l);
+            T0 = __builtin_amdgcn_readlane(T, l);
         }
         carry += __builtin_amdgcn_readlane(incl, 63);
     }
+    if (!working) return;
+    // the scan's loads are done; saying so with a wait the compiler models
+    // keeps it from waiting on them (and so on the DMA loads) further down
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- stream tiles [start, end): a cursor per side walks the requests
+    struct Cursor {
+        int b, P, T, L, seg;  // request, its first tile, tiles, tokens; pieces begun so far
+    };
+    // lengths by scalar loads: a vector load here would make the compiler wait
+    // for every outstanding load, DMA ones included
+    typedef const __attribute__((address_space(4))) int32_t *clen_t;
+    const clen_t slens = (clen_t)p.seq_lens;
+    auto advance = [&](Cursor &c) {  // to the next request with tiles (one exists before tile NT)
+        do {
+            c.P += c.T;
+            c.b += 1;
+            c.L = slens[c.b];
+            c.T = (c.L + kMT - 1) / kMT;
+        } while (c.T == 0);
+        c.seg += 1;
+    };
+    const int Lb0 = slens[b0];
+    Cursor prod{b0, P0, T0, Lb0, 0}, cons{b0, P0, T0, Lb0, 0};
+    uint8_t(*ring)[2][kMTileBytes] = lds[wv];
+    auto produce = [&](int x) {  // stage tile x (and Q when it starts a new piece)
+        if (x >= prod.P + prod.T) {
+            advance(prod);
+            stage_q(p, prod.b, g, qlds[wv][prod.seg % kNbuf], lane);
+        }
+        const int t0 = (x - prod.P) * kMT;
+        const int64_t off = token_offset<PAGED>(p, prod.b, g, t0);
+        const int slot = x % kNbuf;
+        stage_tile(p.k + off, p.v + off, lds_addr(ring[slot][0]), lds_addr(ring[slot][1]), prod.L - t0, stok2,
+                   lane);
+    };
+
+    stage_q(p, b0, g, qlds[wv][0], lane);
+    const int npro = min(kNbuf - 1, end - start);
+    for (int i = 0; i < npro; ++i) produce(start + i);
+
+    MfmaSoftmax st;
+    st.reset();
+    uint2 qb[8];
+    for (int x = start; x < end; ++x) {
+        if (x + kNbuf - 1 < end) produce(x + kNbuf - 1);
+        // tile x has landed once at most the later tiles' loads remain (a Q load
+        // issued after it only makes this wait longer)
+        wait_vm8(min(kNbuf - 1, end - 1 - x));
+        if (x == start) {
+            read_q(qlds[wv][0], lane, qb);
+        } else if (x >= cons.P + cons.T) {
+            const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
+            write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots);
+            st.reset();
+            advance(cons);
+            read_q(qlds[wv][cons.seg % kNbuf], lane, qb);
+        }
+        const int slot = x % kNbuf;
+        mfma_tile<DT>(ring[slot][0], ring[slot][1], qb, cons.L - (x - cons.P) * kMT, p.scale_log2, lane, st);
+    }
+    const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
+    write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots);
 }
 
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
