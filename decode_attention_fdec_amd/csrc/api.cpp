@@ -385,10 +385,35 @@ extern "C" int fdec_merge_states(const float *part_o, const float *part_m, const
                      fn);
 }
 
+// The cascade's suffixes run on the balanced split when the matrix-core map
+// kernel takes the shape (G = 4, head_dim 128): workspace = meta [B, 2], the
+// prefix states [B, Hq, sp] and the suffix pieces [Hq, ss + B].
+bool cascade_balanced_shape(int Hq, int Hkv, int D) { return Hq == 4 * Hkv && D == 128; }
+
+struct CascBalLayout {
+    size_t meta, ppm, ppd, ppo, pm, pd, po, total;
+};
+CascBalLayout casc_bal_layout(int B, int Hq, int D, int sp, int ss) {
+    CascBalLayout w;
+    const size_t pstates = (size_t)B * Hq * sp, sstates = (size_t)Hq * (size_t)(ss + B);
+    w.meta = 0;
+    w.ppm = align_up(w.meta + (size_t)B * 2 * sizeof(int32_t));
+    w.ppd = align_up(w.ppm + pstates * sizeof(float));
+    w.ppo = align_up(w.ppd + pstates * sizeof(float));
+    w.pm = align_up(w.ppo + pstates * D * sizeof(float));
+    w.pd = align_up(w.pm + sstates * sizeof(float));
+    w.po = align_up(w.pd + sstates * sizeof(float));
+    w.total = align_up(w.po + sstates * D * sizeof(float));
+    return w;
+}
+
 extern "C" size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_dim, int splits_prefix,
                                               int splits_suffix) {
-    if (splits_prefix < 1 || splits_suffix < 1) return 0;
-    return fdec_workspace_size(B, Hq, Hkv, head_dim, splits_prefix + splits_suffix);
+    if (splits_prefix < 1 || splits_suffix < 1 || B < 0 || Hq < 1 || Hkv < 1) return 0;
+    size_t n = fdec_workspace_size(B, Hq, Hkv, head_dim, splits_prefix + splits_suffix);
+    if (cascade_balanced_shape(Hq, Hkv, head_dim))
+        n = std::max(n, casc_bal_layout(B, Hq, head_dim, splits_prefix, splits_suffix).total);
+    return n;
 }
 
 extern "C" int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size,
@@ -413,9 +438,20 @@ extern "C" int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int cap
         ++sp;
     }
     int ss = 1;
-    int rc = fdec_plan(B, Hq, Hkv, nullptr, capacity, page_size, cu_count, &ss);
-    if (rc) return rc;
-    ss = std::min(ss, FDEC_MAX_SPLITS - sp);
+    if (Hq == 4 * Hkv) {
+        // balanced suffix (head_dim 128): one block per compute unit over all groups of KV heads
+        int hpb = 1;
+        for (int w = fdec::kMapMfmaWaves; w > 1; --w)
+            if (Hkv % w == 0) {
+                hpb = w;
+                break;
+            }
+        ss = std::max(1, cu_count / (Hkv / hpb));
+    } else {
+        int rc = fdec_plan(B, Hq, Hkv, nullptr, capacity, page_size, cu_count, &ss);
+        if (rc) return rc;
+    }
+    ss = std::max(1, std::min(ss, FDEC_MAX_SPLITS - sp));
     *splits_prefix_out = sp;
     *splits_suffix_out = ss;
     return FDEC_OK;
@@ -456,18 +492,7 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
-    const int S = sp + ss;
-    const WsLayout w = ws_layout(B, Hq, kv->num_kv_heads, kv->head_dim, S);
-    if (!workspace || workspace_bytes < w.total)
-        return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d + %d splits, got %zu", fn,
-                         w.total, sp, ss, workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
-    char *ws = static_cast<char *>(workspace);
-    float *pm = reinterpret_cast<float *>(ws + w.pm);
-    float *pd = reinterpret_cast<float *>(ws + w.pd);
-    float *po = reinterpret_cast<float *>(ws + w.po);
     hipStream_t st = static_cast<hipStream_t>(stream);
-
     float scale = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)kv->head_dim) : softmax_scale;
     fdec::CascadeParams cp;
     std::memset(&cp, 0, sizeof(cp));
@@ -486,12 +511,52 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     cp.Hkv = kv->num_kv_heads;
     cp.chunk = (int)chunk_p;
     cp.scale_log2 = scale * 1.4426950408889634f;
+    cp.dtype = kv->dtype;
+
+    fdec::MapParams pb = map_params(q, B, Hq, kv, suffix_lens, 1, softmax_scale, nullptr);
+    if (pb.mfma && (int64_t)B * (((int64_t)cap + 15) / 16) < (int64_t(1) << 31)) {
+        // suffixes on the balanced split, then one merge of prefix states and suffix pieces
+        const CascBalLayout w = casc_bal_layout(B, Hq, kv->head_dim, sp, ss);
+        if (!workspace || workspace_bytes < w.total)
+            return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d + %d splits, got %zu", fn,
+                             w.total, sp, ss, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace))
+            return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+        char *ws = static_cast<char *>(workspace);
+        cp.pm = reinterpret_cast<float *>(ws + w.ppm);
+        cp.pd = reinterpret_cast<float *>(ws + w.ppd);
+        cp.po = reinterpret_cast<float *>(ws + w.ppo);
+        cp.s_total = sp;
+        cp.s_offset = 0;
+        if ((rc = check_hip(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch")))
+            return rc;
+        pb.seg_meta = reinterpret_cast<int *>(ws + w.meta);
+        pb.pm = reinterpret_cast<float *>(ws + w.pm);
+        pb.pd = reinterpret_cast<float *>(ws + w.pd);
+        pb.po = reinterpret_cast<float *>(ws + w.po);
+        pb.nslots = ss + B;
+        if ((rc = check_hip(fdec::launch_map_mfma_g4_balanced(pb, ss, st), "fdec_cascade_decode: suffix launch")))
+            return rc;
+        return check_hip(fdec::launch_merge_cascade(cp.po, cp.pm, cp.pd, sp, pb.po, pb.pm, pb.pd, pb.seg_meta, B, Hq,
+                                                    pb.nslots, ss, out, lse, st),
+                         "fdec_cascade_decode: merge launch");
+    }
+
+    const int S = sp + ss;
+    const WsLayout w = ws_layout(B, Hq, kv->num_kv_heads, kv->head_dim, S);
+    if (!workspace || workspace_bytes < w.total)
+        return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d + %d splits, got %zu", fn,
+                         w.total, sp, ss, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+    char *ws = static_cast<char *>(workspace);
+    float *pm = reinterpret_cast<float *>(ws + w.pm);
+    float *pd = reinterpret_cast<float *>(ws + w.pd);
+    float *po = reinterpret_cast<float *>(ws + w.po);
     cp.po = po;
     cp.pm = pm;
     cp.pd = pd;
     cp.s_total = S;
     cp.s_offset = 0;
-    cp.dtype = kv->dtype;
     if ((rc = check_hip(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch"))) return rc;
 
     fdec::MapParams p = map_params(q, B, Hq, kv, suffix_lens, ss, softmax_scale, nullptr);

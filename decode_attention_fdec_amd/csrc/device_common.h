@@ -106,16 +106,31 @@ __device__ __forceinline__ float readlane(float x, int lane) {
 // same bits, and so do the merge kernel and the single-kernel path.
 constexpr int kMergeGroup = 32;
 
+// Where the states of one (b, h) live: state s has its O~ row at row(s) (D
+// floats) and its m, d at m(s), d(s).
+template <int D> struct ContigStates {  // S consecutive states
+    const float *po, *pm, *pd;
+    __device__ __forceinline__ const float *row(int s) const { return po + (int64_t)s * D; }
+    __device__ __forceinline__ float m(int s) const { return pm[s]; }
+    __device__ __forceinline__ float d(int s) const { return pd[s]; }
+};
+template <int D> struct TwoRuns {  // n0 consecutive states, then the states of a second run
+    ContigStates<D> a, b;
+    int n0;
+    __device__ __forceinline__ const float *row(int s) const { return s < n0 ? a.row(s) : b.row(s - n0); }
+    __device__ __forceinline__ float m(int s) const { return s < n0 ? a.m(s) : b.m(s - n0); }
+    __device__ __forceinline__ float d(int s) const { return s < n0 ? a.d(s) : b.d(s - n0); }
+};
+
 // M, dsum and the weights a[k] of states lane + 64 k (every lane of the wave).
-template <int D>
-__device__ __forceinline__ void merge_weights(const float *pm, const float *pd, int S, int lane, float &M,
-                                              float &dsum, float a[4]) {
+template <int D, class Src>
+__device__ __forceinline__ void merge_weights(const Src &src, int S, int lane, float &M, float &dsum, float a[4]) {
     float mv[4], dv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int i = lane + 64 * k;
-        mv[k] = i < S ? pm[i] : kNegInf;
-        dv[k] = i < S ? pd[i] : 0.0f;
+        mv[k] = i < S ? src.m(i) : kNegInf;
+        dv[k] = i < S ? src.d(i) : 0.0f;
     }
     M = wave_max(fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
     dsum = 0.0f;
@@ -128,15 +143,15 @@ __device__ __forceinline__ void merge_weights(const float *pm, const float *pd, 
 }
 
 // The rows of group k (zeros past S): this lane's D / 64 elements of each.
-template <int D>
-__device__ __forceinline__ void merge_load_group(const float *po, int S, int k, int lane,
+template <int D, class Src>
+__device__ __forceinline__ void merge_load_group(const Src &src, int S, int k, int lane,
                                                  float x[kMergeGroup][D / 64]) {
     constexpr int NV = D / 64;
 #pragma unroll
     for (int u = 0; u < kMergeGroup; ++u) {
         const int s = k * kMergeGroup + u;
-        const float *row = po + (int64_t)s * D + lane * NV;
         if (s < S) {
+            const float *row = src.row(s) + lane * NV;
             if constexpr (NV == 2) {
                 const float2 t = *reinterpret_cast<const float2 *>(row);
                 x[u][0] = t.x;
@@ -191,23 +206,61 @@ __device__ __forceinline__ void merge_finish(const float acc[D / 64], float M, f
 
 // One wave merges every group in turn; the first group's rows are requested
 // together with m and d, so up to 32 splits merge in one memory round trip.
-template <int D>
-__device__ __forceinline__ void merge_states_wave(const float *po, const float *pm, const float *pd,
-                                                  int S, float *out, float *lse, int lane) {
+template <int D, class Src>
+__device__ __forceinline__ void merge_states_wave(const Src &src, int S, float *out, float *lse, int lane) {
     constexpr int NV = D / 64;
     float x[kMergeGroup][NV];
-    merge_load_group<D>(po, S, 0, lane, x);
+    merge_load_group<D>(src, S, 0, lane, x);
     float M, dsum, a[4];
-    merge_weights<D>(pm, pd, S, lane, M, dsum, a);
+    merge_weights<D>(src, S, lane, M, dsum, a);
     float acc[NV];
     merge_group_sum<D>(x, a, S, 0, acc);
     const int K = (S + kMergeGroup - 1) / kMergeGroup;
     for (int k = 1; k < K; ++k) {
-        merge_load_group<D>(po, S, k, lane, x);
+        merge_load_group<D>(src, S, k, lane, x);
         float g[NV];
         merge_group_sum<D>(x, a, S, k, g);
 #pragma unroll
         for (int e = 0; e < NV; ++e) acc[e] += g[e];
+    }
+    merge_finish<D>(acc, M, dsum, out, lse, lane);
+}
+template <int D>
+__device__ __forceinline__ void merge_states_wave(const float *po, const float *pm, const float *pd, int S,
+                                                  float *out, float *lse, int lane) {
+    merge_states_wave<D>(ContigStates<D>{po, pm, pd}, S, out, lse, lane);
+}
+
+// The waves of a block (nw of them) take the groups of S states side by side,
+// wave w groups w, w + nw, ...; the group sums meet in gs and are added in
+// group order, which gives the bits of merge_states_wave. Every wave of the
+// block calls it (waves without a group only meet the barrier).
+template <int D, class Src>
+__device__ __forceinline__ void merge_states_block(const Src &src, int S, float *out, float *lse, int lane, int w,
+                                                   int nw, float (*gs)[D]) {
+    constexpr int NV = D / 64;
+    const int K = (S + kMergeGroup - 1) / kMergeGroup;
+    float M = kNegInf, dsum = 0.0f, a[4];
+    if (w < K || w == 0) {
+        float x[kMergeGroup][NV];
+        merge_load_group<D>(src, S, w, lane, x);
+        merge_weights<D>(src, S, lane, M, dsum, a);
+        for (int k = w; k < K; k += nw) {
+            if (k != w) merge_load_group<D>(src, S, k, lane, x);
+            float g[NV];
+            merge_group_sum<D>(x, a, S, k, g);
+#pragma unroll
+            for (int e = 0; e < NV; ++e) gs[k][lane * NV + e] = g[e];
+        }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float acc[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) acc[e] = K > 0 ? gs[0][lane * NV + e] : 0.0f;
+    for (int j = 1; j < K; ++j) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) acc[e] += gs[j][lane * NV + e];
     }
     merge_finish<D>(acc, M, dsum, out, lse, lane);
 }

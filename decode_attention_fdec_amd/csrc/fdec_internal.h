@@ -96,6 +96,12 @@ hipError_t launch_merge_segments(const float *po, const float *pm, const float *
                                  int nslots, int max_count, int head_dim, float *out, float *lse,
                                  hipStream_t stream);
 
+// Cascade merge with a balanced suffix: per (b, h) the prefix states
+// [B, Hq, sp] then request b's suffix pieces (as launch_merge_segments).
+hipError_t launch_merge_cascade(const float *ppo, const float *ppm, const float *ppd, int sp, const float *po,
+                                const float *pm, const float *pd, const int *meta, int B, int Hq, int nslots,
+                                int max_count, float *out, float *lse, hipStream_t stream);
+
 // Zero n 32-bit words with a kernel (no memset node, so graph capture stays safe).
 hipError_t launch_zero_words(void *ptr, size_t n_words, hipStream_t stream);
 

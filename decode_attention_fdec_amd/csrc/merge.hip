@@ -27,89 +27,78 @@ template <int D>
 __global__ __launch_bounds__(64 * (256 / kMergeGroup)) void merge_kernel_groups(
     const float *__restrict__ po, const float *__restrict__ pm, const float *__restrict__ pd, int S,
     float *__restrict__ out, float *__restrict__ lse) {
-    constexpr int NV = D / 64;
     __shared__ float gs[256 / kMergeGroup][D];
     const int lane = threadIdx.x & 63;
     const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's group
     const int64_t bh = blockIdx.x;
-    po += bh * S * D;
-    pm += bh * S;
-    pd += bh * S;
-    float x[kMergeGroup][NV];
-    merge_load_group<D>(po, S, k, lane, x);
-    float M, dsum, a[4];
-    merge_weights<D>(pm, pd, S, lane, M, dsum, a);
-    float g[NV];
-    merge_group_sum<D>(x, a, S, k, g);
-#pragma unroll
-    for (int e = 0; e < NV; ++e) gs[k][lane * NV + e] = g[e];
-    __syncthreads();
-    if (k != 0) return;
-    float acc[NV];
-#pragma unroll
-    for (int e = 0; e < NV; ++e) acc[e] = gs[0][lane * NV + e];
-    const int K = blockDim.x >> 6;
-    for (int j = 1; j < K; ++j) {
-#pragma unroll
-        for (int e = 0; e < NV; ++e) acc[e] += gs[j][lane * NV + e];
-    }
-    merge_finish<D>(acc, M, dsum, out + bh * D, lse ? lse + bh : nullptr, lane);
+    const ContigStates<D> src{po + bh * S * D, pm + bh * S, pd + bh * S};
+    merge_states_block<D>(src, S, out + bh * D, lse ? lse + bh : nullptr, lane, k, blockDim.x >> 6, gs);
 }
 
-// Balanced-split merge: one block per (b, h), one wave per group of 32 of the
-// request's states (waves past its count only meet the barrier).
+// Balanced-split merge: one block per (b, h). The piece count is known only on
+// the device, so the block has kSegWaves waves that take the groups in turn.
 template <int D>
 __global__ __launch_bounds__(64 * (256 / kMergeGroup)) void merge_kernel_segments(
     const float *__restrict__ po, const float *__restrict__ pm, const float *__restrict__ pd,
     const int *__restrict__ meta, int Hq, int nslots, float *__restrict__ out, float *__restrict__ lse) {
-    constexpr int NV = D / 64;
     __shared__ float gs[256 / kMergeGroup][D];
     const int lane = threadIdx.x & 63;
     const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bh = blockIdx.x;
     const int b = (int)(bh / Hq), h = (int)(bh % Hq);
-    const int slot0 = meta[2 * b], S = meta[2 * b + 1];
-    const int K = (S + kMergeGroup - 1) / kMergeGroup;
-    const int64_t base = (int64_t)h * nslots + slot0;
-    po += base * D;
-    pm += base;
-    pd += base;
-    float M = kNegInf, dsum = 0.0f, a[4];
-    if (k < K || k == 0) {
-        float x[kMergeGroup][NV];
-        merge_load_group<D>(po, S, k, lane, x);
-        merge_weights<D>(pm, pd, S, lane, M, dsum, a);
-        if (k < K) {
-            float g[NV];
-            merge_group_sum<D>(x, a, S, k, g);
-#pragma unroll
-            for (int e = 0; e < NV; ++e) gs[k][lane * NV + e] = g[e];
-        }
-    }
-    __syncthreads();
-    if (k != 0) return;
-    float acc[NV];
-#pragma unroll
-    for (int e = 0; e < NV; ++e) acc[e] = K > 0 ? gs[0][lane * NV + e] : 0.0f;
-    for (int j = 1; j < K; ++j) {
-#pragma unroll
-        for (int e = 0; e < NV; ++e) acc[e] += gs[j][lane * NV + e];
-    }
-    merge_finish<D>(acc, M, dsum, out + bh * D, lse ? lse + bh : nullptr, lane);
+    const int64_t base = (int64_t)h * nslots + meta[2 * b];
+    const ContigStates<D> src{po + base * D, pm + base, pd + base};
+    merge_states_block<D>(src, meta[2 * b + 1], out + bh * D, lse ? lse + bh : nullptr, lane, k, blockDim.x >> 6,
+                          gs);
 }
+
+// Cascade with a balanced suffix: per (b, h) the sp prefix states [B, Hq, sp]
+// come first, then the request's suffix pieces as in merge_kernel_segments.
+template <int D>
+__global__ __launch_bounds__(64 * (256 / kMergeGroup)) void merge_kernel_cascade(
+    const float *__restrict__ ppo, const float *__restrict__ ppm, const float *__restrict__ ppd, int sp,
+    const float *__restrict__ po, const float *__restrict__ pm, const float *__restrict__ pd,
+    const int *__restrict__ meta, int Hq, int nslots, float *__restrict__ out, float *__restrict__ lse) {
+    __shared__ float gs[256 / kMergeGroup][D];
+    const int lane = threadIdx.x & 63;
+    const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / Hq), h = (int)(bh % Hq);
+    const int64_t base = (int64_t)h * nslots + meta[2 * b];
+    const TwoRuns<D> src{ContigStates<D>{ppo + bh * sp * D, ppm + bh * sp, ppd + bh * sp},
+                         ContigStates<D>{po + base * D, pm + base, pd + base}, sp};
+    merge_states_block<D>(src, sp + meta[2 * b + 1], out + bh * D, lse ? lse + bh : nullptr, lane, k,
+                          blockDim.x >> 6, gs);
+}
+
+// Waves per block of the merges whose state counts only the device knows:
+// enough for the usual one or two groups of 32 in one memory round trip, few
+// enough that idle waves cost little.
+constexpr int kSegWaves = 2;
 
 hipError_t launch_merge_segments(const float *po, const float *pm, const float *pd, const int *meta, int B, int Hq,
                                  int nslots, int max_count, int head_dim, float *out, float *lse,
                                  hipStream_t st) {
     const int K = (max(max_count, 1) + kMergeGroup - 1) / kMergeGroup;
     if (K > 256 / kMergeGroup) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)B * Hq), block(64 * K);
+    const dim3 grid((unsigned)B * Hq), block(64 * min(K, kSegWaves));
     if (head_dim == 128)
         hipLaunchKernelGGL(merge_kernel_segments<128>, grid, block, 0, st, po, pm, pd, meta, Hq, nslots, out, lse);
     else if (head_dim == 64)
         hipLaunchKernelGGL(merge_kernel_segments<64>, grid, block, 0, st, po, pm, pd, meta, Hq, nslots, out, lse);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_cascade(const float *ppo, const float *ppm, const float *ppd, int sp, const float *po,
+                                const float *pm, const float *pd, const int *meta, int B, int Hq, int nslots,
+                                int max_count, float *out, float *lse, hipStream_t st) {
+    const int K = (sp + max(max_count, 1) + kMergeGroup - 1) / kMergeGroup;
+    if (K > 256 / kMergeGroup) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(merge_kernel_cascade<128>, dim3((unsigned)B * Hq), dim3(64 * min(K, kSegWaves)), 0, st, ppo,
+                       ppm, ppd, sp, po,
+                       pm, pd, meta, Hq, nslots, out, lse);
     return hipGetLastError();
 }
 

@@ -238,7 +238,11 @@ size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int nu
  * sequence. kv must be paged, head_dim 128. splits_prefix / splits_suffix >= 1
  * (0 = fdec_cascade_plan's choice); the prefix is cut into chunks of
  * 64 * ceil(ceil(prefix_len / splits_prefix) / 64) tokens, each of at most 1022
- * pages. Workspace: fdec_cascade_workspace_size().
+ * pages. With G = Hq/Hkv = 4 the suffixes run on the balanced split (as
+ * fdec_decode_balanced) and splits_suffix is its block count per group of KV
+ * heads; otherwise splits_suffix splits every suffix (as fdec_decode). At most
+ * FDEC_MAX_SPLITS states merge per request: splits_prefix + splits_suffix
+ * <= FDEC_MAX_SPLITS. Workspace: fdec_cascade_workspace_size().
  */
 int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv,
                         const int32_t *prefix_pages, int prefix_len, const int32_t *suffix_lens,
@@ -248,9 +252,11 @@ int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv,
 /*
  * Split counts for fdec_cascade_decode (host only). The prefix is cut so the
  * matrix-core kernel has about one block per compute unit with at least 256
- * prefix tokens each; the suffix split count comes from fdec_plan over the
- * suffix page table's capacity. prefix_len >= 0; capacity = max_pages_per_seq *
- * page_size of the suffix table.
+ * prefix tokens each. The suffix count is, for G = 4, the balanced split's
+ * block count per group of KV heads (one block per compute unit over all
+ * groups), else fdec_plan's split count over the suffix page table's
+ * capacity. prefix_len >= 0; capacity = max_pages_per_seq * page_size of the
+ * suffix table.
  */
 int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size, int cu_count,
                       int *splits_prefix_out, int *splits_suffix_out);
