@@ -24,7 +24,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # copy, built on the CPU) to check that the pins catch it.
 _LIB_OVERRIDE = os.environ.get("ORACLE_LIB_OVERRIDE")
 
-F16, BF16 = 0, 1
+F16, BF16, FP8 = 0, 1, 2  # FP8: float8 e4m3fn caches (queries stay 16-bit)
 
 
 def build(force: bool = True) -> str:
@@ -48,6 +48,7 @@ class _KV(ctypes.Structure):
         ("s_outer", ctypes.c_int64), ("s_token", ctypes.c_int64), ("s_head", ctypes.c_int64),
         ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int),
         ("prefix_pages", ctypes.c_void_p), ("prefix_len", ctypes.c_int),
+        ("k_descale", ctypes.c_void_p), ("v_descale", ctypes.c_void_p),
     ]
 
 
@@ -74,6 +75,7 @@ def _load():
         lib.oracle_append.argtypes = [ctypes.POINTER(_KV), P, P, P, P, P, P, ctypes.c_int,
                                       ctypes.c_double, P]
         lib.oracle_decode_elems.argtypes = [P, ctypes.c_int, ctypes.c_int64, P]
+        lib.oracle_decode_f8.argtypes = [P, ctypes.c_int64, P]
         lib.oracle_encode_elems.argtypes = [P, ctypes.c_int, ctypes.c_int64, P]
         lib.oracle_now.restype = ctypes.c_double
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -82,19 +84,24 @@ def _load():
 
 
 def _bits(a) -> np.ndarray:
-    """Raw 16-bit patterns of an fp16/bf16 tensor or a uint16 array (C order)."""
+    """Raw bit patterns (C order): uint16 for fp16/bf16, uint8 for float8 e4m3fn."""
     if isinstance(a, np.ndarray):
-        assert a.dtype == np.uint16
+        assert a.dtype in (np.uint16, np.uint8)
         return np.ascontiguousarray(a)
     import torch  # only for unpacking torch tensors handed in by tests
 
+    a = a.detach().cpu().contiguous()
+    if a.dtype == torch.float8_e4m3fn:
+        return np.ascontiguousarray(a.view(torch.uint8).numpy())
     assert a.dtype in (torch.float16, torch.bfloat16)
-    return np.ascontiguousarray(a.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    return np.ascontiguousarray(a.view(torch.int16).numpy().view(np.uint16))
 
 
 def dtype_code(a) -> int:
     import torch
 
+    if a.dtype == torch.float8_e4m3fn:
+        return FP8
     return F16 if a.dtype == torch.float16 else BF16
 
 
@@ -111,10 +118,15 @@ def _ptr(a):
 
 
 def to_f64(bits, dtype: int) -> np.ndarray:
-    """Exact fp16/bf16 -> double conversion by the oracle's own field decoder."""
+    """Exact fp16/bf16/float8 -> double conversion by the oracle's own field decoders."""
     b = _bits(bits)
     out = np.empty(b.shape, dtype=np.float64)
-    _load().oracle_decode_elems(_ptr(b), dtype, b.size, _ptr(out))
+    if dtype == FP8:
+        assert b.dtype == np.uint8
+        _load().oracle_decode_f8(_ptr(b), b.size, _ptr(out))
+    else:
+        assert b.dtype == np.uint16
+        _load().oracle_decode_elems(_ptr(b), dtype, b.size, _ptr(out))
     return out
 
 
@@ -130,7 +142,7 @@ class KV:
     """One KV cache as the oracle reads it (raw bits + geometry)."""
 
     def __init__(self, k, v, dtype: int, Hq: int, B: int, page_size: int = 0,
-                 page_table=None, prefix_pages=None, prefix_len: int = 0):
+                 page_table=None, prefix_pages=None, prefix_len: int = 0, k_descale=None, v_descale=None):
         self.k = _bits(k)
         self.v = _bits(v)
         assert self.k.shape == self.v.shape and self.k.ndim == 4
@@ -144,6 +156,8 @@ class KV:
         self.page_table = _i32(page_table)
         self.prefix_pages = _i32(prefix_pages)
         self.prefix_len = prefix_len
+        self.k_descale = _f64(k_descale, (B, self.Hkv))
+        self.v_descale = _f64(v_descale, (B, self.Hkv))
 
     def _struct(self) -> _KV:
         s = _KV()
@@ -156,13 +170,28 @@ class KV:
         s.max_pages = 0 if self.page_table is None else self.page_table.shape[1]
         s.prefix_pages = _ptr(self.prefix_pages)
         s.prefix_len = self.prefix_len
+        s.k_descale = _ptr(self.k_descale)
+        s.v_descale = _ptr(self.v_descale)
         return s
 
 
+def _f64(a, shape):
+    if a is None:
+        return None
+    if not isinstance(a, np.ndarray):
+        a = a.detach().cpu().double().numpy()
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    assert a.shape == shape
+    return a
+
+
 def _q64(q, dtype):
-    if isinstance(q, np.ndarray) and q.dtype == np.float64:
-        return np.ascontiguousarray(q)
-    return to_f64(q, dtype)
+    """Queries in double: a float64 array as is, a tensor by its own dtype, bits by `dtype`."""
+    if isinstance(q, np.ndarray):
+        if q.dtype == np.float64:
+            return np.ascontiguousarray(q)
+        return to_f64(q, dtype)
+    return to_f64(q, dtype_code(q))
 
 
 def decode(kv: KV, q, lens, scale: float, nthreads: int = 0):

@@ -28,6 +28,9 @@
  *   oracle_append    writes rope(k_new) and v_new at row cache_seqlens[b] and
  *                    returns rope(q); lengths are not advanced
  *                    ([cookbook] §3.2-3.4).
+ *   fp8 cache        K/V stored as float8_e4m3fn with one fp32 descale per
+ *                    (request, KV head) for K and one for V; the element's value
+ *                    is its e4m3 value times that descale ([cookbook] §7.1-7.2).
  *   paging           logical token j of request b lives in page
  *                    page_table[b][j / ps], slot j % ps; entries past the
  *                    request's pages are -1 and are never read ([cookbook] §4.2).
@@ -72,6 +75,24 @@ double oracle_bf16_to_f64(uint16_t b) {
     float f;
     memcpy(&f, &u, 4);
     return (double)f;
+}
+
+/* float8 e4m3fn (OCP): 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits;
+ * no infinities, S.1111.111 is NaN, the largest finite is 448. */
+double oracle_f8_to_f64(uint8_t x) {
+    int s = x >> 7, e = (x >> 3) & 15, m = x & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9); /* subnormal: (m / 8) * 2^(1-7) */
+    else
+        v = ldexp((double)(m + 8), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+void oracle_decode_f8(const uint8_t *src, int64_t n, double *dst) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = oracle_f8_to_f64(src[i]);
 }
 
 /* Round a double once, to nearest with ties to even, onto a binary16. */
@@ -136,8 +157,8 @@ void oracle_encode_elems(const double *src, int dtype, int64_t n, uint16_t *dst)
 
 typedef struct {
     int B, Hq, Hkv, D;
-    int dtype;             /* 0 = fp16, 1 = bf16 */
-    const uint16_t *k, *v; /* raw element bits */
+    int dtype;             /* 0 = fp16, 1 = bf16, 2 = float8 e4m3fn */
+    const void *k, *v;     /* raw element bits (2 bytes, or 1 for float8) */
     int page_size;         /* 0 = contiguous [B, capacity, Hkv, D] (by strides) */
     int capacity;          /* contiguous: rows per request */
     int64_t s_outer, s_token, s_head; /* element strides of (batch-or-page, token, head) */
@@ -145,6 +166,7 @@ typedef struct {
     int max_pages;
     const int32_t *prefix_pages; /* cascade: shared prefix pages, or NULL */
     int prefix_len;              /* cascade: shared prefix tokens */
+    const double *k_descale, *v_descale; /* float8: [B, Hkv] factors, or NULL for 1 */
 } oracle_kv;
 
 /* Element offset of logical token j of request b for KV head g. */
@@ -164,15 +186,21 @@ static int64_t row_offset(const oracle_kv *kv, int b, int j, int g) {
     return outer * kv->s_outer + slot * kv->s_token + (int64_t)g * kv->s_head;
 }
 
-static double elem(const oracle_kv *kv, const uint16_t *base, int64_t off) {
-    return kv->dtype == 0 ? oracle_f16_to_f64(base[off]) : oracle_bf16_to_f64(base[off]);
+/* Value of one K or V element of request b, KV head g (descale applied for float8). */
+static double elem(const oracle_kv *kv, const void *base, const double *descale, int b, int g, int64_t off) {
+    if (kv->dtype == 2) {
+        double f = descale ? descale[(int64_t)b * kv->Hkv + g] : 1.0;
+        return oracle_f8_to_f64(((const uint8_t *)base)[off]) * f;
+    }
+    uint16_t u = ((const uint16_t *)base)[off];
+    return kv->dtype == 0 ? oracle_f16_to_f64(u) : oracle_bf16_to_f64(u);
 }
 
 /* Score of token j for query vector q (already in double) against KV head g. */
 static double score(const oracle_kv *kv, const double *q, int b, int j, int g, double scale) {
     int64_t off = row_offset(kv, b, j, g);
     double s = 0.0;
-    for (int d = 0; d < kv->D; ++d) s += q[d] * elem(kv, kv->k, off + d);
+    for (int d = 0; d < kv->D; ++d) s += q[d] * elem(kv, kv->k, kv->k_descale, b, g, off + d);
     return scale * s;
 }
 
@@ -201,7 +229,7 @@ static void attend_range(const oracle_kv *kv, const double *q, int b, int h, int
         double p = exp(sbuf[j - lo] - m);
         dsum += p;
         int64_t off = row_offset(kv, b, j, g);
-        for (int d = 0; d < D; ++d) o_tilde[d] += p * elem(kv, kv->v, off + d);
+        for (int d = 0; d < D; ++d) o_tilde[d] += p * elem(kv, kv->v, kv->v_descale, b, g, off + d);
     }
     *m_out = m;
     *d_out = dsum;
@@ -354,6 +382,7 @@ void oracle_append(oracle_kv *kv, uint16_t *k_cache, uint16_t *v_cache, const ui
                    const uint16_t *v_new, const double *q, const int32_t *cache_seqlens,
                    int rotary_dim, double base, double *q_out) {
     int B = kv->B, Hq = kv->Hq, Hkv = kv->Hkv, D = kv->D;
+    if (kv->dtype != 0 && kv->dtype != 1) return; /* append is defined for 16-bit caches */
     double *tmp = (double *)malloc(sizeof(double) * (size_t)D);
     for (int b = 0; b < B; ++b) {
         int c = cache_seqlens[b];

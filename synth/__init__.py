@@ -6,7 +6,11 @@ attention arithmetic, and imports neither the HIP library nor the oracle.
 Recipe (the same for every case): a CPU ``torch.Generator`` seeded per case;
 values drawn as float32 N(0, 1) and cast to fp16/bf16 with round-to-nearest-even
 (``Tensor.to``). Draw order: lengths -> page permutation -> q -> K -> V ->
-k_new -> v_new. Rows past a request's length hold zeros, NaN or random values
+k_new -> v_new. Float8 (e4m3fn) caches: q is bf16; K and V are drawn in
+float32 as above, then one descale per (request, KV head) each for K and V is
+drawn uniform in [1/64, 1/16], and the stored value is x / descale clamped to
++-448 and cast with round-to-nearest-even (the dequantised value is stored x
+descale; unused pages use descale 1/32). Rows past a request's length hold zeros, NaN or random values
 (``pad``); paged pools hold exactly the pages the requests use plus
 ``extra_pages`` unused ones (filled like padding), with physical page ids a
 seeded random permutation, and the page table padded with -1.
@@ -19,6 +23,8 @@ The five named workloads follow the shapes of the pages' examples:
       cache_seqlens U{1..2047}, fp16, base 10000, rotary_dim 128
   c5  cascade, 64 requests, Hq=32, Hkv=8, page 64, shared 16384-token prefix,
       suffixes U{256..2048}, bf16
+and float8 versions of c2 and c3 (c2f8, c3f8): the same shapes and seeds with
+float8 e4m3fn K/V and bf16 queries.
 """
 from __future__ import annotations
 
@@ -29,6 +35,7 @@ from typing import Optional
 import torch
 
 F16, BF16 = torch.float16, torch.bfloat16
+FP8 = torch.float8_e4m3fn
 
 
 @dataclass
@@ -56,6 +63,9 @@ class Case:
     # cascade
     prefix_pages: Optional[torch.Tensor] = None  # [n_prefix_pages] int32
     prefix_len: int = 0
+    # float8 caches: per (request, KV head) factors, [B, Hkv] float32
+    k_descale: Optional[torch.Tensor] = None
+    v_descale: Optional[torch.Tensor] = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -73,7 +83,7 @@ class Case:
 
     def kv_bytes(self) -> int:
         """K+V bytes of the attended rows, each KV head read once (prefix counted once)."""
-        e = 2
+        e = 1 if self.dtype == FP8 else 2
         per_tok = 2 * self.Hkv * self.D * e
         suffix = int((self.seq_lens.to(torch.int64) + (1 if self.k_new is not None else 0)).sum())
         return per_tok * (suffix + self.prefix_len)
@@ -87,6 +97,25 @@ def _gen(seed: int) -> torch.Generator:
 
 def _randn(g, shape, dtype):
     return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def _q_dtype(dtype):
+    return BF16 if dtype == FP8 else dtype
+
+
+def _kv_draw_dtype(dtype):
+    return torch.float32 if dtype == FP8 else dtype
+
+
+def _descales(g, B: int, Hkv: int):
+    kd = torch.empty(B, Hkv, dtype=torch.float32).uniform_(1.0 / 64, 1.0 / 16, generator=g)
+    vd = torch.empty(B, Hkv, dtype=torch.float32).uniform_(1.0 / 64, 1.0 / 16, generator=g)
+    return kd, vd
+
+
+def _quantize(x: torch.Tensor, f: torch.Tensor) -> torch.Tensor:
+    """float32 x [.., Hkv, D] divided by f (broadcast), clamped to +-448, cast to e4m3fn."""
+    return (x / f).clamp(-448.0, 448.0).to(FP8)
 
 
 def _fill_pad(t: torch.Tensor, mask: torch.Tensor, pad: str, g) -> None:
@@ -109,13 +138,18 @@ def contiguous_case(seed: int, B: int, Hq: int, Hkv: int, D: int, lens, cap: int
                     dtype=F16, pad: str = "zero", name: str = "contig", num_splits: int = 0) -> Case:
     g = _gen(seed)
     lens = torch.as_tensor(lens, dtype=torch.int32).reshape(B)
-    q = _randn(g, (B, Hq, D), dtype)
-    k = _randn(g, (B, cap, Hkv, D), dtype)
-    v = _randn(g, (B, cap, Hkv, D), dtype)
+    q = _randn(g, (B, Hq, D), _q_dtype(dtype))
+    k = _randn(g, (B, cap, Hkv, D), _kv_draw_dtype(dtype))
+    v = _randn(g, (B, cap, Hkv, D), _kv_draw_dtype(dtype))
     rows = torch.arange(cap)[None, :] >= lens[:, None].to(torch.int64)  # [B, cap]
     _fill_pad(k, rows, pad, g)
     _fill_pad(v, rows, pad, g)
-    return Case(name, dtype, B, Hq, Hkv, D, q, k, v, lens, num_splits=num_splits)
+    kd = vd = None
+    if dtype == FP8:
+        kd, vd = _descales(g, B, Hkv)
+        k = _quantize(k, kd[:, None, :, None])
+        v = _quantize(v, vd[:, None, :, None])
+    return Case(name, dtype, B, Hq, Hkv, D, q, k, v, lens, num_splits=num_splits, k_descale=kd, v_descale=vd)
 
 
 def _page_lists(g, lens, ps, extra_pages):
@@ -146,9 +180,9 @@ def paged_case(seed: int, B: int, Hq: int, Hkv: int, D: int, lens, ps: int, dtyp
     for b, pl in enumerate(lists):
         assert len(pl) <= max_pages
         table[b, :len(pl)] = pl
-    q = _randn(g, (B, Hq, D), dtype)
-    k = _randn(g, (pool, ps, Hkv, D), dtype)
-    v = _randn(g, (pool, ps, Hkv, D), dtype)
+    q = _randn(g, (B, Hq, D), _q_dtype(dtype))
+    k = _randn(g, (pool, ps, Hkv, D), _kv_draw_dtype(dtype))
+    v = _randn(g, (pool, ps, Hkv, D), _kv_draw_dtype(dtype))
     # padding: slots past each request's length in its last page, and unused pages
     mask = torch.zeros(pool, ps, dtype=torch.bool)
     for b, pl in enumerate(lists):
@@ -159,8 +193,18 @@ def paged_case(seed: int, B: int, Hq: int, Hkv: int, D: int, lens, ps: int, dtyp
         mask[p, :] = True
     _fill_pad(k, mask, pad, g)
     _fill_pad(v, mask, pad, g)
+    kd = vd = None
+    if dtype == FP8:
+        kd, vd = _descales(g, B, Hkv)
+        fk = torch.full((pool, Hkv), 1.0 / 32)  # per page: its request's descales
+        fv = torch.full((pool, Hkv), 1.0 / 32)
+        for b, pl in enumerate(lists):
+            fk[pl.long()] = kd[b]
+            fv[pl.long()] = vd[b]
+        k = _quantize(k, fk[:, None, :, None])
+        v = _quantize(v, fv[:, None, :, None])
     return Case(name, dtype, B, Hq, Hkv, D, q, k, v, lens, page_size=ps, page_table=table,
-                num_splits=num_splits)
+                num_splits=num_splits, k_descale=kd, v_descale=vd)
 
 
 def append_case(seed: int, B: int, Hq: int, Hkv: int, D: int, max_seqlen: int, dtype=F16,
@@ -258,6 +302,11 @@ def workload(name: str, pad: str = "zero") -> Case:
         return contiguous_case(1, 1, 32, 32, 128, [4096], 4096, F16, pad, "c1", num_splits=16)
     if name == "c2":
         return contiguous_case(2, 1, 32, 8, 128, [131072], 131072, BF16, pad, "c2")
+    if name == "c2f8":
+        return contiguous_case(2, 1, 32, 8, 128, [131072], 131072, FP8, pad, "c2f8")
+    if name == "c3f8":
+        return paged_case(3, 32, 32, 8, 128, None, 16, FP8, max_pages=512, pad=pad, name="c3f8",
+                          lens_range=(512, 8192))
     if name == "c3":
         return paged_case(3, 32, 32, 8, 128, None, 16, BF16, max_pages=512, pad=pad, name="c3",
                           lens_range=(512, 8192))

@@ -12,13 +12,14 @@ import torch
 
 import oracle
 
-OUT_TOL = {torch.float16: 1e-3, torch.bfloat16: 3e-3}
+OUT_TOL = {torch.float16: 1e-3, torch.bfloat16: 3e-3, torch.float8_e4m3fn: 3e-3}  # float8 caches: bf16 queries
 LSE_RTOL = 1e-4
 
 
 def okv(case, k=None, v=None):
     return oracle.KV(case.k if k is None else k, case.v if v is None else v, oracle.dtype_code(case.k),
-                     case.Hq, case.B, case.page_size, case.page_table, case.prefix_pages, case.prefix_len)
+                     case.Hq, case.B, case.page_size, case.page_table, case.prefix_pages, case.prefix_len,
+                     case.k_descale, case.v_descale)
 
 
 def oracle_decode(case, scale=None, nthreads=0):
@@ -47,7 +48,7 @@ def to_dev(case, device="cuda"):
     """Copy every tensor of a case to the device (returns a dict of device tensors)."""
     d = {}
     for name in ("q", "k", "v", "seq_lens", "page_table", "k_new", "v_new", "rope_cos", "rope_sin",
-                 "prefix_pages"):
+                 "prefix_pages", "k_descale", "v_descale"):
         t = getattr(case, name)
         d[name] = None if t is None else t.to(device).contiguous()
     return d

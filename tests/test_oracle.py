@@ -16,7 +16,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from synth import BF16, F16, append_case, cascade_case, contiguous_case, paged_case
+from synth import BF16, F16, FP8, append_case, cascade_case, contiguous_case, paged_case
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -28,7 +28,7 @@ def _built(oracle_lib):
 
 def okv(case):
     return oracle.KV(case.k, case.v, oracle.dtype_code(case.k), case.Hq, case.B, case.page_size,
-                     case.page_table, case.prefix_pages, case.prefix_len)
+                     case.page_table, case.prefix_pages, case.prefix_len, case.k_descale, case.v_descale)
 
 
 def golden_rows(name):
@@ -61,6 +61,18 @@ def test_bf16_decode_exhaustive():
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(ours), nan)
     assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_f8_decode_exhaustive():
+    # every float8 e4m3fn code against torch's own decoding of the format
+    bits = np.arange(256, dtype=np.uint8)
+    ours = oracle.to_f64(bits, oracle.FP8)
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
 
 
 def _halfway_points(vals):
@@ -429,3 +441,66 @@ def test_golden_split_picture_and_slices():
     (row,) = golden_rows("lpnh_128k_slices.txt")
     n, S, slice_len, B, H, tasks = map(int, row)
     assert n // S == slice_len and B * H * S == tasks
+
+
+# ---------------------------------------------------------------- float8 caches
+
+def _dequant(case, b, L):
+    """K, V of request b as float64 [1, Hkv, L, D], each element times its descale."""
+    k = case.k[b, :L].to(torch.float64) * case.k_descale[b].double()[None, :, None]
+    v = case.v[b, :L].to(torch.float64) * case.v_descale[b].double()[None, :, None]
+    return k.permute(1, 0, 2)[None].contiguous(), v.permute(1, 0, 2)[None].contiguous()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fp8_cache_matches_torch_sdpa_on_dequantised_values(seed):
+    # descales differ per (request, KV head), with B != Hkv so a swapped index shows
+    case = contiguous_case(140 + seed, 3, 8, 2, 16, [1, 9, 16], 16, FP8, pad="nan")
+    scale = 0.3
+    out, lse = oracle.decode(okv(case), case.q, case.seq_lens, scale)
+    for b in range(case.B):
+        L = int(case.seq_lens[b])
+        q = case.q[b].to(torch.float64)[None, :, None, :]
+        k, v = _dequant(case, b, L)
+        ref = F.scaled_dot_product_attention(q, k, v, scale=scale, enable_gqa=True)[0, :, 0, :]
+        np.testing.assert_allclose(out[b], ref.numpy(), rtol=0, atol=1e-12)
+        ones = torch.ones(1, case.Hkv, L + 1, 1, dtype=torch.float64)
+        ones[:, :, L] = 0.0
+        ksink = torch.cat([k, torch.zeros(1, case.Hkv, 1, case.D, dtype=torch.float64)], dim=2)
+        r = F.scaled_dot_product_attention(q, ksink, ones, scale=scale, enable_gqa=True)[0, :, 0, 0].numpy()
+        np.testing.assert_allclose(lse[b], np.log(r / (1.0 - r)), rtol=0, atol=1e-10)
+
+
+def test_fp8_descales_act_as_their_definition():
+    case = contiguous_case(150, 2, 8, 2, 16, [12, 5], 16, FP8, pad="nan")
+    out, lse = oracle.decode(okv(case), case.q, case.seq_lens, 0.25)
+    # V's descale scales the output and leaves the weights alone
+    vd = case.v_descale.clone()
+    case.v_descale = vd * 4.0
+    out4, lse4 = oracle.decode(okv(case), case.q, case.seq_lens, 0.25)
+    np.testing.assert_allclose(out4, out * 4.0, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(lse4, lse)
+    # K's descale 0 flattens the scores: the mean of the dequantised V, lse = ln L
+    case.v_descale = vd
+    case.k_descale = torch.zeros_like(case.k_descale)
+    out0, lse0 = oracle.decode(okv(case), case.q, case.seq_lens, 0.25)
+    for b in range(2):
+        L = int(case.seq_lens[b])
+        mean = (case.v[b, :L].to(torch.float64) * vd[b].double()[None, :, None]).mean(0).numpy()
+        for h in range(8):
+            np.testing.assert_allclose(out0[b, h], mean[h // 4], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse0[b], math.log(L), rtol=0, atol=1e-13)
+
+
+def test_fp8_cache_equals_bf16_cache_holding_the_same_values():
+    # every e4m3 value is a bf16 value: with unit descales the two caches are
+    # the same keys and values, so the oracle gives bitwise equal results
+    case = paged_case(151, 3, 8, 2, 32, [40, 1, 17], 16, FP8, extra_pages=2, pad="nan")
+    case.k_descale = torch.ones_like(case.k_descale)
+    case.v_descale = torch.ones_like(case.v_descale)
+    o8, l8 = oracle.decode(okv(case), case.q, case.seq_lens, 0.2)
+    kb = oracle.KV(case.k.to(BF16), case.v.to(BF16), oracle.BF16, case.Hq, case.B, case.page_size,
+                   case.page_table)
+    ob, lb = oracle.decode(kb, case.q, case.seq_lens, 0.2)
+    np.testing.assert_array_equal(o8, ob)
+    np.testing.assert_array_equal(l8, lb)

@@ -26,7 +26,12 @@ MUTANTS = {
     "rope_pairing": ("double a = x[i], b = x[i + half];", "double a = x[i], b = x[i ^ 1];"),
     "f16_bias": ("ldexp((double)(m + 1024), e - 25)", "ldexp((double)(m + 1024), e - 24)"),
     "f16_truncates": ("double v = rint(a / ulp) * ulp; /* rint", "double v = floor(a / ulp) * ulp; /* rint"),
-    "v_reads_k": ("o_tilde[d] += p * elem(kv, kv->v, off + d);", "o_tilde[d] += p * elem(kv, kv->k, off + d);"),
+    "v_reads_k": ("p * elem(kv, kv->v, kv->v_descale, b, g, off + d);", "p * elem(kv, kv->k, kv->v_descale, b, g, off + d);"),
+    "f8_bias_8": ("ldexp((double)(m + 8), e - 10)", "ldexp((double)(m + 8), e - 11)"),
+    "f8_subnormal_scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "f8_descale_dropped": ("((const uint8_t *)base)[off]) * f;", "((const uint8_t *)base)[off]);"),
+    "f8_v_uses_k_descale": ("p * elem(kv, kv->v, kv->v_descale, b, g, off + d);", "p * elem(kv, kv->v, kv->k_descale, b, g, off + d);"),
+    "f8_descale_index_swapped": ("descale[(int64_t)b * kv->Hkv + g]", "descale[(int64_t)g * kv->B + b]"),
     "last_token_dropped": ("for (int j = lo; j < hi; ++j) {\n        sbuf",
                            "for (int j = lo; j < hi - 1; ++j) {\n        sbuf"),
     "prefix_pages_ignored": ("} else if (kv->prefix_pages && j < kv->prefix_len) {",
