@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfdec.so")
 
 FDEC_OK, FDEC_ERR_INVALID_ARG, FDEC_ERR_UNSUPPORTED, FDEC_ERR_WORKSPACE, FDEC_ERR_HIP = range(5)
-FDEC_F16, FDEC_BF16 = 0, 1
+FDEC_F16, FDEC_BF16, FDEC_FP8_E4M3 = 0, 1, 2
 MAX_SPLITS = 256
 
 
@@ -39,6 +39,7 @@ class FdecKV(ctypes.Structure):
         ("page_size", ctypes.c_int), ("capacity", ctypes.c_int),
         ("s_outer", ctypes.c_int64), ("s_token", ctypes.c_int64), ("s_head", ctypes.c_int64),
         ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int),
+        ("k_descale", ctypes.c_void_p), ("v_descale", ctypes.c_void_p),
     ]
 
 
@@ -113,11 +114,24 @@ def _dtype_code(dt: torch.dtype) -> int:
         return FDEC_F16
     if dt == torch.bfloat16:
         return FDEC_BF16
-    raise FdecError(FDEC_ERR_UNSUPPORTED, f"dtype {dt} not built (float16, bfloat16)")
+    if dt == torch.float8_e4m3fn:
+        return FDEC_FP8_E4M3
+    raise FdecError(FDEC_ERR_UNSUPPORTED, f"dtype {dt} not built (float16, bfloat16, float8_e4m3fn)")
 
 
-def make_kv(k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor] = None) -> FdecKV:
-    """Describe a cache: contiguous [B, cap, Hkv, D] or paged [P, page_size, Hkv, D] (+ page_table)."""
+def _check_q(q: torch.Tensor, k: torch.Tensor) -> None:
+    """q has the cache's dtype (bf16 for a float8 cache) and is contiguous."""
+    want = torch.bfloat16 if k.dtype == torch.float8_e4m3fn else k.dtype
+    if q.dtype != want or not q.is_contiguous():
+        raise FdecError(FDEC_ERR_INVALID_ARG, f"q must be contiguous {want} for a {k.dtype} cache")
+
+
+def make_kv(k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor] = None,
+            k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None) -> FdecKV:
+    """Describe a cache: contiguous [B, cap, Hkv, D] or paged [P, page_size, Hkv, D] (+ page_table).
+
+    Float8 caches take k_descale / v_descale: contiguous [B, Hkv] float32 device tensors (or None = 1).
+    """
     if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype or k.dim() != 4:
         raise FdecError(FDEC_ERR_INVALID_ARG, "k and v must be 4-D with equal shapes, strides and dtypes")
     if k.stride(3) != 1:
@@ -137,6 +151,11 @@ def make_kv(k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor]
         kv.max_pages_per_seq = page_table.shape[1]
         kv.capacity = kv.page_size * kv.max_pages_per_seq
         kv.page_table = page_table.data_ptr()
+    for name, d in (("k_descale", k_descale), ("v_descale", v_descale)):
+        if d is not None:
+            if d.dtype != torch.float32 or not d.is_contiguous():
+                raise FdecError(FDEC_ERR_INVALID_ARG, f"{name} must be a contiguous float32 tensor")
+            setattr(kv, name, d.data_ptr())
     return kv
 
 
@@ -200,13 +219,13 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Te
            page_table: Optional[torch.Tensor] = None, num_splits: int = 0, softmax_scale: float = 0.0,
            append: Optional[FdecAppend] = None, fused: bool = False, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
-           return_lse: bool = True):
+           return_lse: bool = True, k_descale: Optional[torch.Tensor] = None,
+           v_descale: Optional[torch.Tensor] = None):
     """fdec_decode: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32 or None)."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table)
-    if q.dtype != k.dtype or not q.is_contiguous():
-        raise FdecError(FDEC_ERR_INVALID_ARG, "q must be contiguous with the cache dtype")
+    kv = make_kv(k, v, page_table, k_descale, v_descale)
+    _check_q(q, k)
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None and return_lse:
@@ -231,13 +250,13 @@ def balanced_workspace_size(B: int, Hq: int, Hkv: int, D: int, num_blocks: int =
 def decode_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
                     page_table: Optional[torch.Tensor] = None, num_blocks: int = 0, softmax_scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    workspace: Optional[Workspace] = None, return_lse: bool = True):
+                    workspace: Optional[Workspace] = None, return_lse: bool = True,
+                    k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None):
     """fdec_decode_balanced: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32 or None)."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table)
-    if q.dtype != k.dtype or not q.is_contiguous():
-        raise FdecError(FDEC_ERR_INVALID_ARG, "q must be contiguous with the cache dtype")
+    kv = make_kv(k, v, page_table, k_descale, v_descale)
+    _check_q(q, k)
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None and return_lse:
@@ -253,11 +272,13 @@ def decode_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens:
 def decode_partials(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
                     num_splits: int, page_table: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                     append: Optional[FdecAppend] = None, part_o: Optional[torch.Tensor] = None,
-                    part_m: Optional[torch.Tensor] = None, part_d: Optional[torch.Tensor] = None):
+                    part_m: Optional[torch.Tensor] = None, part_d: Optional[torch.Tensor] = None,
+                    k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None):
     """fdec_decode_partials: returns (part_o [B,Hq,S,D], part_m [B,Hq,S], part_d [B,Hq,S]) fp32."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table)
+    kv = make_kv(k, v, page_table, k_descale, v_descale)
+    _check_q(q, k)
     S = num_splits
     if part_o is None:
         part_o = torch.empty(B, Hq, S, D, dtype=torch.float32, device=q.device)

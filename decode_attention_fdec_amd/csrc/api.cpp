@@ -63,8 +63,10 @@ int validate_common(const char *fn, const void *q, int B, int Hq, const fdec_kv 
         return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: GQA group size %d not built (1, 2, 4, 8)", fn, G);
     if (kv->head_dim != 128 && kv->head_dim != 64)
         return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: head_dim %d not built (128, 64)", fn, kv->head_dim);
-    if (kv->dtype != FDEC_F16 && kv->dtype != FDEC_BF16)
-        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: dtype %d not built (fp16 = 0, bf16 = 1)", fn, kv->dtype);
+    if (kv->dtype != FDEC_F16 && kv->dtype != FDEC_BF16 && kv->dtype != FDEC_FP8_E4M3)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: dtype %d not built (fp16 = 0, bf16 = 1, fp8 e4m3 = 2)", fn,
+                         kv->dtype);
+    const int es = kv->dtype == FDEC_FP8_E4M3 ? 1 : 2;  // bytes per element
     if (kv->page_size < 0 || kv->page_size % 16 != 0)
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: page_size %d must be 0 or a multiple of 16", fn,
                          kv->page_size);
@@ -73,10 +75,10 @@ int validate_common(const char *fn, const void *q, int B, int Hq, const fdec_kv 
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: q, kv->k, kv->v and seq_lens must be non-NULL", fn);
     if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: q, k and v must be 16-byte aligned", fn);
-    if (kv->s_outer < 0 || kv->s_token < 0 || kv->s_head < 0 || kv->s_outer % 8 || kv->s_token % 8 ||
-        kv->s_head % 8)
-        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: strides must be non-negative multiples of 8 elements", fn);
-    if ((int64_t)kv->s_token * 2 * 15 > INT32_MAX)
+    if (kv->s_outer < 0 || kv->s_token < 0 || kv->s_head < 0 || (kv->s_outer * es) % 16 ||
+        (kv->s_token * es) % 16 || (kv->s_head * es) % 16)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: strides must be non-negative multiples of 16 bytes", fn);
+    if ((int64_t)kv->s_token * es * 15 > INT32_MAX)
         return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: token stride too large", fn);
     if (kv->page_size == 0) {
         if (kv->capacity < 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: contiguous cache needs capacity >= 1", fn);
@@ -146,6 +148,11 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     p.page_size = kv->page_size;
     p.page_shift = page_shift_of(kv->page_size);
     p.seq_lens = seq_lens;
+    if (kv->dtype == FDEC_FP8_E4M3) {
+        p.kv_fp8 = 1;
+        p.k_descale = kv->k_descale;
+        p.v_descale = kv->v_descale;
+    }
     p.B = B;
     p.Hq = Hq;
     p.Hkv = kv->num_kv_heads;
@@ -153,7 +160,7 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     p.chunk = (int)fdec_split_chunk(capacity_of(kv), S);
     if (scale == 0.0f) scale = 1.0f / std::sqrt((float)kv->head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
-    p.dtype = kv->dtype;
+    p.dtype = kv->dtype == FDEC_FP8_E4M3 ? FDEC_BF16 : kv->dtype;  // the queries' (and MFMA's) type
     p.head_dim = kv->head_dim;
     p.mode = fdec::kPlain;
     if (append) {
@@ -176,6 +183,17 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
             }
     }
     return p;
+}
+
+// Float8 caches run only on the matrix-core map kernel, without append.
+int check_fp8(const char *fn, const fdec_kv *kv, const fdec::MapParams &p, const fdec_append *append) {
+    if (kv->dtype != FDEC_FP8_E4M3) return FDEC_OK;
+    if (append) return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: append into a float8 cache is not built", fn);
+    if (!p.mfma)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED,
+                         "%s: float8 caches need Hq = 4 Hkv, head_dim 128, page_size a multiple of 16 "
+                         "(and the matrix-core map kernel)", fn);
+    return FDEC_OK;
 }
 
 int resolve_splits(const char *fn, int num_splits, int B, int Hq, const fdec_kv *kv, int *S) {
@@ -252,6 +270,7 @@ extern "C" int fdec_decode(const void *q, int B, int Hq, const fdec_kv *kv, cons
 
     char *ws = static_cast<char *>(workspace);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, append);
+    if ((rc = check_fp8(fn, kv, p, append))) return rc;
     p.pm = reinterpret_cast<float *>(ws + w.pm);
     p.pd = reinterpret_cast<float *>(ws + w.pd);
     p.po = reinterpret_cast<float *>(ws + w.po);
@@ -285,6 +304,7 @@ extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv 
     if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_m) & 3u) || (reinterpret_cast<uintptr_t>(part_d) & 3u))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o must be 16-byte aligned", fn);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, num_splits, softmax_scale, append);
+    if ((rc = check_fp8(fn, kv, p, append))) return rc;
     p.po = part_o;
     p.pm = part_m;
     p.pd = part_d;
@@ -465,6 +485,8 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     const char *fn = "fdec_cascade_decode";
     int rc = validate_common(fn, q, B, Hq, kv, suffix_lens, softmax_scale);
     if (rc) return rc;
+    if (kv->dtype == FDEC_FP8_E4M3)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: float8 caches are not built for the cascade path", fn);
     if (kv->page_size == 0) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: the cascade path needs a paged cache", fn);
     if (kv->head_dim != 128)
         return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: head_dim %d not built for the cascade path (128)", fn,

@@ -49,6 +49,9 @@ struct MapParams {
     int dtype;                  // 0 fp16, 1 bf16
     int head_dim;
     int mfma;                   // 1: matrix-core kernel (map_mfma_eligible)
+    // float8 e4m3fn cache (dtype is then the queries' bf16): [B, Hkv] factors or nullptr
+    int kv_fp8;
+    const float *k_descale, *v_descale;
     // balanced split: states [Hq, nslots] and per-request (first slot, count)
     int *seg_meta;
     int nslots;

@@ -2,7 +2,7 @@
 // (gfx950). Same contract as map_kernel in split_kv.hip (the FlashDecoding map
 // stage: per split the local max m_i, the local sum of exponentials d_i and the
 // unnormalised output O~_i -- lpnh.cn explainer §2 stage 1), for G = Hq/Hkv = 4,
-// D = 128, without append.
+// D = 128, without append; K/V in fp16/bf16 or in float8 e4m3fn (bf16 queries).
 //
 // Packing the four query heads of a KV head makes q.K^T a dense contraction for
 // the 16-block v_mfma_f32_4x4x4_16b_{bf16,f16} (M = 4 = G, no padding; lpnh §3
@@ -28,6 +28,12 @@
 //   - O += P V: A = P broadcast from block q (tokens 4q..4q+3), B = V^T from the
 //     transpose read of the row-major V tile; lane L accumulates O[head 0..3]
 //     at d = L and 64 + L.
+// Float8 caches (the pages' FP8 KV cache: e4m3fn values with one fp32 descale
+// per (request, KV head) for K and one for V): tiles arrive at half the bytes;
+// K is converted to bf16 in registers after its LDS read and V into a bf16
+// tile for the transpose read (v_cvt_scalef32_pk_bf16_fp8 at scale 1: every
+// e4m3 value is a bf16 value, so both are exact); K's descale multiplies the
+// score scale and V's the written state.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -90,18 +96,31 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t 
 template <int N> __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
-// wait until at most 8 k DMA loads are outstanding (k uniform, clamped to [0, 7])
-__device__ __forceinline__ void wait_vm8(int k) {
+// wait until at most N k DMA loads are outstanding (k uniform, clamped to [0, 7])
+template <int N> __device__ __forceinline__ void wait_vm_n(int k) {
     switch (k) {
     case 0: wait_vm<0>(); break;
-    case 1: wait_vm<8>(); break;
-    case 2: wait_vm<16>(); break;
-    case 3: wait_vm<24>(); break;
-    case 4: wait_vm<32>(); break;
-    case 5: wait_vm<40>(); break;
-    case 6: wait_vm<48>(); break;
-    default: wait_vm<56>(); break;
+    case 1: wait_vm<N>(); break;
+    case 2: wait_vm<2 * N>(); break;
+    case 3: wait_vm<3 * N>(); break;
+    case 4: wait_vm<4 * N>(); break;
+    case 5: wait_vm<5 * N>(); break;
+    case 6: wait_vm<6 * N>(); break;
+    default: wait_vm<7 * N>(); break;
     }
+}
+
+// KV element formats: KF = 0 for fp16/bf16, KF = 1 for float8 e4m3fn.
+template <int KF> struct KvFmt {
+    static constexpr int kElem = KF ? 1 : 2;  // bytes per element
+    static constexpr int kDma = KF ? 4 : 8;   // DMA instructions per tile (K + V)
+};
+
+// Four e4m3 values (bytes, lowest first) to four bf16 values in two dwords.
+__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w) {
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 constexpr int kMT = 16;                 // tokens per tile
@@ -120,39 +139,74 @@ __device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)ptr;
 }
 
-// Global -> LDS staging of one 16-token tile of one KV head. Instruction i
-// (0..3) writes rows 4i..4i+3: lane l fills slot (l & 15) of row r = 4i + l / 16
-// with 16-byte piece (l & 15) ^ swz(r) of that row; piece c of row r therefore
-// sits in slot c ^ swz(r). K rows use swz = r (an S^T read takes one piece of
-// each of the 16 rows per quarter wave), V rows swz = 4 (r & 3) (a transpose
-// read takes 4 pieces of 4 consecutive rows per half wave). kb / vb address the
-// tile's first row; rows past nrows repeat row nrows - 1.
+// Global -> LDS staging of one 16-token tile of one KV head.
+// 16-bit elements (256-byte rows): instruction i (0..3) writes rows 4i..4i+3:
+// lane l fills slot (l & 15) of row r = 4i + l / 16 with 16-byte piece
+// (l & 15) ^ swz(r) of that row; piece c of row r therefore sits in slot
+// c ^ swz(r). K rows use swz = r (an S^T read takes one piece of each of the 16
+// rows per quarter wave), V rows swz = 4 (r & 3) (a transpose read takes 4
+// pieces of 4 consecutive rows per half wave).
+// float8 (128-byte rows): instruction i (0..1) writes rows 8i..8i+7, lane l
+// slot (l & 7) of row r = 8i + l / 8 with piece (l & 7) ^ ((r >> 1) & 7), for K
+// and V alike (the 16 rows of a quarter-wave read then cover all 64 banks).
+// kb / vb address the tile's first row; rows past nrows repeat row nrows - 1.
+template <int KF>
 __device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint32_t kl, uint32_t vl, int nrows,
-                                           uint32_t stok2, int lane) {
-    const int srow = lane >> 4, sslot = lane & 15;
+                                           uint32_t stok, int lane) {
+    if constexpr (KF == 0) {
+        const int srow = lane >> 4, sslot = lane & 15;
 #pragma unroll
-    for (int i = 0; i < kMT / 4; ++i) {
-        const int r = 4 * i + srow;
-        const uint32_t row = (uint32_t)min(r, nrows - 1) * stok2;
-        dma16(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
-        dma16(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
+        for (int i = 0; i < kMT / 4; ++i) {
+            const int r = 4 * i + srow;
+            const uint32_t row = (uint32_t)min(r, nrows - 1) * stok;
+            dma16(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
+            dma16(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
+        }
+    } else {
+        const int srow = lane >> 3, sslot = lane & 7;
+#pragma unroll
+        for (int i = 0; i < kMT / 8; ++i) {
+            const int r = 8 * i + srow;
+            const uint32_t at = (uint32_t)min(r, nrows - 1) * stok + 16u * (uint32_t)(sslot ^ ((r >> 1) & 7));
+            dma16(kb, at, kl + 1024u * i);
+            dma16(vb, at, vl + 1024u * i);
+        }
     }
 }
 
 // Byte offset of token t of request b, KV head g (uniform). A tile of a paged
 // cache lies on one page (page_size and tile starts are multiples of 16); the
 // page id comes from a scalar load.
-template <bool PAGED>
+template <bool PAGED, int KF>
 __device__ __forceinline__ int64_t token_offset(const MapParams &p, int b, int g, int t) {
+    constexpr int ES = KvFmt<KF>::kElem;
     if constexpr (PAGED) {
         typedef const __attribute__((address_space(4))) int32_t *cpage_t;
         const cpage_t ptab = (cpage_t)(p.page_table + (int64_t)b * p.max_pages);
         const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : (t / p.page_size);
         const int64_t page = ptab[pidx];
-        return (page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head) * 2;
+        return (page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head) * ES;
     } else {
-        return ((int64_t)b * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head) * 2;
+        return ((int64_t)b * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head) * ES;
     }
+}
+
+// The (request b, KV head g) descale of a float8 cache (1 without one), by a
+// scalar load.
+__device__ __forceinline__ float kv_descale(const float *d, const MapParams &p, int b, int g) {
+    if (!d) return 1.0f;
+    typedef const __attribute__((address_space(4))) float *cf_t;
+    return ((cf_t)d)[(int64_t)b * p.Hkv + g];
+}
+
+// LDS addresses of ring slot `slot`: K tile and V tile (16-bit), or the float8
+// K and V tiles in the two halves of the K area (the V area then receives V as
+// bf16 for the transpose read).
+template <int KF>
+__device__ __forceinline__ void slot_dma_addrs(uint8_t (*ring)[2][kMTileBytes], int slot, uint32_t &kl,
+                                               uint32_t &vl) {
+    kl = lds_addr(ring[slot][0]);
+    vl = KF ? kl + kMTileBytes / 2 : lds_addr(ring[slot][1]);
 }
 
 // Q of the four query heads of KV head g of request b (1 KB) to LDS, with the
@@ -194,9 +248,10 @@ struct MfmaSoftmax {
 };
 
 // One tile: S^T = K Q^T, online softmax, O += P V. nvalid (>= 1) tokens of the
-// tile count; the rest are masked.
-template <int DT>
-__device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 qb[8], int nvalid,
+// tile count; the rest are masked. kl: the K tile; vl: the V tile (bf16 target
+// for float8, whose V tile is at kl + kMTileBytes / 2).
+template <int DT, int KF>
+__device__ __forceinline__ void mfma_tile(const uint8_t *kl, uint8_t *vl, const uint2 qb[8], int nvalid,
                                           float scale_log2, int lane, MfmaSoftmax &st) {
     using E = Elem<DT>;
     const int dq = lane >> 4;
@@ -206,11 +261,39 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
 
     // ---- S^T = K Q^T: this lane's quarter of D, 4 pieces of 8 d-values
     f32x4_v s = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (KF == 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * ((4 * dq + c) ^ rk));
-        s = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[2 * c], s);
-        s1 = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[2 * c + 1], s1);
+        for (int c = 0; c < 4; ++c) {
+            const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * ((4 * dq + c) ^ rk));
+            s = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[2 * c], s);
+            s1 = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[2 * c + 1], s1);
+        }
+    } else {
+        // float8 piece 2 dq + e holds d 32 dq + 16 e .. + 15: K-steps 4e .. 4e + 3
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const uint4 k8 = *reinterpret_cast<const uint4 *>(kl + rk * 128 + 16 * ((2 * dq + e) ^ ((rk >> 1) & 7)));
+            s = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.x), qb[4 * e], s);
+            s1 = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.y), qb[4 * e + 1], s1);
+            s = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.z), qb[4 * e + 2], s);
+            s1 = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.w), qb[4 * e + 3], s1);
+        }
+        // V as bf16: lane l converts row l / 4, d 32 (l & 3) .. + 31 (float8
+        // pieces 2 (l & 3) + e), written as bf16 pieces 4 (l & 3) + 2e + {0, 1}
+        // in the 16-bit V layout (slot = piece ^ 4 (row & 3))
+        const uint8_t *v8 = kl + kMTileBytes / 2;
+        const int vr = lane >> 2, vq = lane & 3;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int pc = 2 * vq + e;
+            const uint4 x = *reinterpret_cast<const uint4 *>(v8 + vr * 128 + 16 * (pc ^ ((vr >> 1) & 7)));
+            const uint2 a0 = fp8x4_to_bf16(x.x), a1 = fp8x4_to_bf16(x.y);
+            const uint2 a2 = fp8x4_to_bf16(x.z), a3 = fp8x4_to_bf16(x.w);
+            *reinterpret_cast<uint4 *>(vl + vr * 256 + 16 * ((2 * pc) ^ (4 * (vr & 3)))) =
+                make_uint4(a0.x, a0.y, a1.x, a1.y);
+            *reinterpret_cast<uint4 *>(vl + vr * 256 + 16 * ((2 * pc + 1) ^ (4 * (vr & 3)))) =
+                make_uint4(a2.x, a2.y, a3.x, a3.y);
+        }
     }
 
     // ---- softmax for head lane & 3, tokens 4 tg .. 4 tg + 3 of this tile
@@ -278,7 +361,7 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
 // d = 2^(m - T) l, m = T ln 2 (an empty state is (0, -inf, 0)); head i's goes to
 // po0 + i hs D, pm0 + i hs, pd0 + i hs.
 __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, float *po0, float *pm0, float *pd0,
-                                            int64_t hs) {
+                                            int64_t hs, float vscale = 1.0f) {
     constexpr int D = 128;
     float lt = st.l, tt = st.t;
 #pragma unroll
@@ -289,7 +372,7 @@ __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, flo
     const float f_own = (tt == kNegInf) ? 0.0f : fexp2(st.m - tt);
     f32x4_v fs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fs[i] = readlane(f_own, i);
+    for (int i = 0; i < 4; ++i) fs[i] = readlane(f_own, i) * vscale;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float *dst = po0 + i * hs * D;
@@ -298,26 +381,28 @@ __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, flo
     }
     if (lane < 4) {
         pm0[lane * hs] = (tt == kNegInf) ? kNegInf : tt * kLn2;
-        pd0[lane * hs] = lt * f_own;
+        pd0[lane * hs] = lt * f_own;  // the weights are unscaled: V's descale is on O~ only
     }
 }
 
 // One wave's pass over tokens [t_begin, t_end) of request b for KV head g
 // (its four query heads), state to po0 / pm0 / pd0 (+ i hs per head). ring /
 // qslot are the wave's LDS: kNbuf ring slots of K and V tiles and 1 KB of Q.
-template <int DT, bool PAGED>
+template <int DT, bool PAGED, int KF>
 __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)[2][kMTileBytes], uint8_t *qslot,
                                              int b, int g, int lane, int t_begin, int t_end, float *po0, float *pm0,
                                              float *pd0, int64_t hs) {
     const int ntok = t_end - t_begin;
     const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
-    const uint32_t stok2 = (uint32_t)(p.s_token * 2);
+    const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
     auto stage = [&](int tile, int64_t off) {
-        const int slot = tile % kNbuf;
-        stage_tile(p.k + off, p.v + off, lds_addr(ring[slot][0]), lds_addr(ring[slot][1]),
-                   t_end - (t_begin + tile * kMT), stok2, lane);
+        uint32_t kl, vl;
+        slot_dma_addrs<KF>(ring, tile % kNbuf, kl, vl);
+        stage_tile<KF>(p.k + off, p.v + off, kl, vl, t_end - (t_begin + tile * kMT), stok, lane);
     };
-    auto tile_offset = [&](int tile) { return token_offset<PAGED>(p, b, g, t_begin + tile * kMT); };
+    auto tile_offset = [&](int tile) { return token_offset<PAGED, KF>(p, b, g, t_begin + tile * kMT); };
+    const float kd = KF ? kv_descale(p.k_descale, p, b, g) : 1.0f;
+    const float vd = KF ? kv_descale(p.v_descale, p, b, g) : 1.0f;
 
     MfmaSoftmax st;
     st.reset();
@@ -326,7 +411,7 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)
     const int npro = min(kNbuf - 1, ntiles);
     for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
     int64_t noff = (kNbuf - 1 < ntiles) ? tile_offset(kNbuf - 1) : 0;  // next tile to stage
-    wait_vm8(npro);  // Q has landed
+    wait_vm_n<KvFmt<KF>::kDma>(npro);  // Q has landed
     uint2 qb[8];
     read_q(qslot, lane, qb);
 
@@ -337,14 +422,15 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)
             if (ahead + 1 < ntiles) noff = tile_offset(ahead + 1);
         }
         // this tile's loads have landed once only the later tiles' remain
-        wait_vm8(min(kNbuf - 1, ntiles - 1 - tile));
+        wait_vm_n<KvFmt<KF>::kDma>(min(kNbuf - 1, ntiles - 1 - tile));
         const int slot = tile % kNbuf;
-        mfma_tile<DT>(ring[slot][0], ring[slot][1], qb, t_end - (t_begin + tile * kMT), p.scale_log2, lane, st);
+        mfma_tile<DT, KF>(ring[slot][0], ring[slot][1], qb, t_end - (t_begin + tile * kMT), p.scale_log2 * kd, lane,
+                          st);
     }
-    write_state(st, lane, po0, pm0, pd0, hs);
+    write_state(st, lane, po0, pm0, pd0, hs, vd);
 }
 
-template <int DT, bool PAGED>
+template <int DT, bool PAGED, int KF>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(const MapParams p) {
     constexpr int D = 128, G = 4;
     // [wave][ring slot][K, V][tile bytes]
@@ -361,8 +447,8 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     const int t_begin = split * p.chunk;
     const int t_end = min(t_begin + p.chunk, L);
     const int64_t st0 = ((int64_t)b * p.Hq + hq0) * p.s_total + p.s_offset + split;
-    mfma_segment<DT, PAGED>(p, lds[wv], qlds[wv], b, g, lane, t_begin, t_end, p.po + st0 * D, p.pm + st0,
-                            p.pd + st0, p.s_total);
+    mfma_segment<DT, PAGED, KF>(p, lds[wv], qlds[wv], b, g, lane, t_begin, t_end, p.po + st0 * D, p.pm + st0,
+                                p.pd + st0, p.s_total);
 
     if (p.counters == nullptr) return;
 
@@ -413,7 +499,7 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // With fewer tiles than blocks, only the first (tiles) blocks take work, so
 // every working block has at least one tile and no slot of a request is left
 // unwritten. Every wave scans seq_lens itself (no block barrier).
-template <int DT, bool PAGED>
+template <int DT, bool PAGED, int KF>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
     constexpr int D = 128, G = 4;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
@@ -424,7 +510,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const int g = blockIdx.z * p.heads_per_block + wv;
     const int hq0 = g * G;
     const int NB = gridDim.x, blk = blockIdx.x;
-    const uint32_t stok2 = (uint32_t)(p.s_token * 2);
+    const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
 
     // ---- the block's tile range and its first request
     const bool one_pass = p.B <= 64;  // lengths stay in registers between the passes
@@ -500,10 +586,10 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
             stage_q(p, prod.b, g, qlds[wv][prod.seg % kNbuf], lane);
         }
         const int t0 = (x - prod.P) * kMT;
-        const int64_t off = token_offset<PAGED>(p, prod.b, g, t0);
-        const int slot = x % kNbuf;
-        stage_tile(p.k + off, p.v + off, lds_addr(ring[slot][0]), lds_addr(ring[slot][1]), prod.L - t0, stok2,
-                   lane);
+        const int64_t off = token_offset<PAGED, KF>(p, prod.b, g, t0);
+        uint32_t kl, vl;
+        slot_dma_addrs<KF>(ring, x % kNbuf, kl, vl);
+        stage_tile<KF>(p.k + off, p.v + off, kl, vl, prod.L - t0, stok, lane);
     };
 
     stage_q(p, b0, g, qlds[wv][0], lane);
@@ -513,59 +599,70 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     MfmaSoftmax st;
     st.reset();
     uint2 qb[8];
+    float kd = 1.0f, vd = 1.0f;  // the current request's float8 descales
     for (int x = start; x < end; ++x) {
         if (x + kNbuf - 1 < end) produce(x + kNbuf - 1);
         // tile x has landed once at most the later tiles' loads remain (a Q load
         // issued after it only makes this wait longer)
-        wait_vm8(min(kNbuf - 1, end - 1 - x));
+        wait_vm_n<KvFmt<KF>::kDma>(min(kNbuf - 1, end - 1 - x));
         if (x == start) {
             read_q(qlds[wv][0], lane, qb);
+            if (KF) {
+                kd = kv_descale(p.k_descale, p, cons.b, g);
+                vd = kv_descale(p.v_descale, p, cons.b, g);
+            }
         } else if (x >= cons.P + cons.T) {
             const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
-            write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots);
+            write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
             st.reset();
             advance(cons);
             read_q(qlds[wv][cons.seg % kNbuf], lane, qb);
+            if (KF) {
+                kd = kv_descale(p.k_descale, p, cons.b, g);
+                vd = kv_descale(p.v_descale, p, cons.b, g);
+            }
         }
         const int slot = x % kNbuf;
-        mfma_tile<DT>(ring[slot][0], ring[slot][1], qb, cons.L - (x - cons.P) * kMT, p.scale_log2, lane, st);
+        mfma_tile<DT, KF>(ring[slot][0], ring[slot][1], qb, cons.L - (x - cons.P) * kMT, p.scale_log2 * kd, lane,
+                          st);
     }
     const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
-    write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots);
+    write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
 }
+
+// Instantiations: q / compute type DT (0 fp16, 1 bf16), paged or not, KV
+// format (float8 caches take bf16 queries).
+#define FDEC_MFMA_DISPATCH(KERNEL)                                                                   \
+    if (p.kv_fp8) {                                                                                  \
+        if (p.page_table)                                                                            \
+            hipLaunchKernelGGL((KERNEL<1, true, 1>), grid, block, 0, st, p);                         \
+        else                                                                                         \
+            hipLaunchKernelGGL((KERNEL<1, false, 1>), grid, block, 0, st, p);                        \
+    } else if (p.dtype == 0) {                                                                       \
+        if (p.page_table)                                                                            \
+            hipLaunchKernelGGL((KERNEL<0, true, 0>), grid, block, 0, st, p);                         \
+        else                                                                                         \
+            hipLaunchKernelGGL((KERNEL<0, false, 0>), grid, block, 0, st, p);                        \
+    } else {                                                                                         \
+        if (p.page_table)                                                                            \
+            hipLaunchKernelGGL((KERNEL<1, true, 0>), grid, block, 0, st, p);                         \
+        else                                                                                         \
+            hipLaunchKernelGGL((KERNEL<1, false, 0>), grid, block, 0, st, p);                        \
+    }
 
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
     dim3 grid(nblocks, 1, p.Hkv / p.heads_per_block);
     dim3 block(64 * p.heads_per_block);
-    if (p.dtype == 0) {
-        if (p.page_table)
-            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<0, true>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<0, false>), grid, block, 0, st, p);
-    } else {
-        if (p.page_table)
-            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<1, true>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((map_kernel_mfma_g4_bal<1, false>), grid, block, 0, st, p);
-    }
+    FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal)
     return hipGetLastError();
 }
 
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
     dim3 grid(S, p.B, p.Hkv / p.heads_per_block);
     dim3 block(64 * p.heads_per_block);
-    if (p.dtype == 0) {
-        if (p.page_table)
-            hipLaunchKernelGGL((map_kernel_mfma_g4<0, true>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((map_kernel_mfma_g4<0, false>), grid, block, 0, st, p);
-    } else {
-        if (p.page_table)
-            hipLaunchKernelGGL((map_kernel_mfma_g4<1, true>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((map_kernel_mfma_g4<1, false>), grid, block, 0, st, p);
-    }
+    FDEC_MFMA_DISPATCH(map_kernel_mfma_g4)
     return hipGetLastError();
 }
+#undef FDEC_MFMA_DISPATCH
 
 }  // namespace fdec

@@ -60,7 +60,9 @@ typedef enum {
     FDEC_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } fdec_status;
 
-typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1 } fdec_dtype;
+/* Cache element types. FDEC_FP8_E4M3: float8 e4m3fn (OCP) K/V with bf16
+ * queries and per-(request, KV head) descales ([cookbook] §7.1-7.2 FP8 KV cache). */
+typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
 
 /* Largest num_splits accepted by any call. */
 #define FDEC_MAX_SPLITS 256
@@ -78,13 +80,20 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1 } fdec_dtype;
  *                   slot j % page_size. page_size must be a multiple of 16
  *                   ([vllm-arch] block size rule). capacity must be 0 or
  *                   max_pages_per_seq * page_size.
- * k and v must be 16-byte aligned and every stride a multiple of 8 elements.
- * They are written only by an append (one row per request and KV head).
+ * k and v must be 16-byte aligned and every stride a multiple of 16 bytes (8
+ * 16-bit or 16 float8 elements). They are written only by an append (one row
+ * per request and KV head).
+ * Float8 caches (dtype FDEC_FP8_E4M3): element (b, t, g, d) stands for its
+ * e4m3 value times k_descale[b*Hkv + g] (K) or v_descale[b*Hkv + g] (V); a NULL
+ * descale is 1. Queries are bf16. Built for Hq = 4 Hkv, head_dim 128, page_size
+ * a multiple of 16 (or contiguous), without append, in fdec_decode,
+ * fdec_decode_partials and fdec_decode_balanced; other calls and shapes return
+ * FDEC_ERR_UNSUPPORTED. The partial states then already include V's descale.
  */
 typedef struct fdec_kv {
     void *k;
     void *v;
-    int dtype;        /* fdec_dtype: fp16 or bf16 (q has the same dtype) */
+    int dtype;        /* fdec_dtype: fp16 or bf16 (q has the same dtype), or float8 (q bf16) */
     int num_kv_heads; /* Hkv */
     int head_dim;     /* D: 128 (64 is also built) */
     int page_size;    /* 0 = contiguous */
@@ -92,6 +101,8 @@ typedef struct fdec_kv {
     int64_t s_outer, s_token, s_head; /* element strides */
     const int32_t *page_table;        /* device [B, max_pages_per_seq] int32, -1 = unused */
     int max_pages_per_seq;
+    const float *k_descale;           /* float8 only: device [B, Hkv] fp32, or NULL (1) */
+    const float *v_descale;           /* float8 only: device [B, Hkv] fp32, or NULL (1) */
 } fdec_kv;
 
 /*

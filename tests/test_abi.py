@@ -86,7 +86,7 @@ def test_head_ratio_must_divide(fdec):
 def test_unsupported_shapes_are_reported_as_unsupported(fdec):
     assert call_decode(kv_struct(head_dim=96)) == F.FDEC_ERR_UNSUPPORTED
     assert call_decode(kv_struct(head_dim=256)) == F.FDEC_ERR_UNSUPPORTED
-    assert call_decode(kv_struct(dtype=7)) == F.FDEC_ERR_UNSUPPORTED
+    assert call_decode(kv_struct(dtype=7)) == F.FDEC_ERR_UNSUPPORTED  # not an fdec_dtype
     assert call_decode(kv_struct(num_kv_heads=2), Hq=32) == F.FDEC_ERR_UNSUPPORTED  # G = 16
 
 
@@ -227,3 +227,22 @@ def test_balanced_workspace_size(fdec):
     assert F.balanced_workspace_size(B, Hq, 8, D, nb) == want
     with pytest.raises(F.FdecError):
         F.balanced_workspace_size(B, Hq, 8, D, 257)
+
+
+def test_fp8_validation(fdec):
+    lib = F.load_library()
+    fp8 = dict(dtype=F.FDEC_FP8_E4M3)
+    # strides must be multiples of 16 bytes: 16 float8 elements
+    assert call_decode(kv_struct(s_head=8, **fp8)) == F.FDEC_ERR_INVALID_ARG
+    # float8 runs on the matrix-core kernel only: G = 4, head_dim 128, no append
+    assert call_decode(kv_struct(**fp8), Hq=16) == F.FDEC_ERR_UNSUPPORTED  # G = 2
+    a = F.FdecAppend()
+    a.k_new, a.v_new = FAKE, FAKE
+    assert call_decode(kv_struct(**fp8), append=a) == F.FDEC_ERR_UNSUPPORTED
+    assert "append" in last_error()
+    # no cascade path for float8
+    kvp = kv_struct(page_size=64, page_table=FAKE, max_pages_per_seq=32, capacity=0, **fp8)
+    assert lib.fdec_cascade_decode(FAKE, 2, 32, ctypes.byref(kvp), FAKE, 64, FAKE, 2, 2, 0.0, FAKE, None,
+                                   FAKE, 1 << 30, None) == F.FDEC_ERR_UNSUPPORTED
+    # an unknown element type
+    assert call_decode(kv_struct(dtype=3)) == F.FDEC_ERR_UNSUPPORTED

@@ -1,0 +1,126 @@
+"""Float8 (e4m3fn) KV caches against the fp64 oracle, through the C ABI.
+
+The pages' FP8 KV cache: K and V stored as float8 e4m3fn with one fp32 descale
+per (request, KV head) each, queries in bf16. Each case runs the uniform splits
+(two kernels and the single-kernel merge), the map stage alone and the balanced
+split; padding rows and unused pages hold NaN.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_fdec_amd as F
+import oracle
+from helpers import assert_parity, okv, oracle_decode, to_dev
+from synth import FP8, contiguous_case, paged_case, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(fdec):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build(force=False)
+    torch.cuda.init()
+
+
+CASES = [
+    ("contig_tail", lambda: contiguous_case(91, 4, 16, 4, 128, [1, 15, 17, 1000], 1024, FP8, pad="nan")),
+    ("contig_empty", lambda: contiguous_case(92, 3, 32, 8, 128, [0, 33, 0], 64, FP8, pad="nan")),
+    ("paged16", lambda: paged_case(93, 4, 16, 4, 128, [16, 31, 500, 2], 16, FP8, extra_pages=4, pad="nan")),
+    ("paged32", lambda: paged_case(94, 3, 32, 8, 128, [64, 95, 1500], 32, FP8, extra_pages=3, pad="nan")),
+    ("paged48", lambda: paged_case(95, 3, 8, 2, 128, [48, 49, 480], 48, FP8, extra_pages=2, pad="nan")),
+]
+
+
+def run(case, num_splits=0, fused=False, descales=True):
+    d = to_dev(case)
+    kd, vd = (d["k_descale"], d["v_descale"]) if descales else (None, None)
+    out, lse = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"],
+                        num_splits=num_splits, fused=fused, k_descale=kd, v_descale=vd)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("name,builder", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("num_splits", [1, 5, 32, 0])
+def test_fp8_decode_matches_oracle(name, builder, num_splits):
+    case = builder()
+    ref_out, ref_lse = oracle_decode(case)
+    for fused in (False, True):
+        out, lse = run(case, num_splits, fused)
+        assert_parity(out, lse, ref_out, ref_lse, case.dtype, f"{name} S={num_splits} fused={fused}")
+
+
+@pytest.mark.parametrize("name,builder", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("num_blocks", [1, 3, 64, 0])
+def test_fp8_balanced_matches_oracle(name, builder, num_blocks):
+    case = builder()
+    ref_out, ref_lse = oracle_decode(case)
+    d = to_dev(case)
+    out, lse = F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"],
+                                 num_blocks=num_blocks, k_descale=d["k_descale"], v_descale=d["v_descale"])
+    torch.cuda.synchronize()
+    assert_parity(out, lse, ref_out, ref_lse, case.dtype, f"{name} blocks={num_blocks}")
+
+
+def test_fp8_without_descales_means_unit_descales():
+    case = paged_case(96, 2, 8, 2, 128, [300, 77], 16, FP8, extra_pages=1, pad="nan")
+    out, lse = run(case, 4, descales=False)
+    case.k_descale = torch.ones_like(case.k_descale)
+    case.v_descale = torch.ones_like(case.v_descale)
+    ref_out, ref_lse = oracle_decode(case)
+    assert_parity(out, lse, ref_out, ref_lse, case.dtype, "unit descales")
+
+
+def test_fp8_map_stage_states_match_oracle_states():
+    lens = [1, 33, 300, 1000]
+    case = contiguous_case(97, 4, 16, 4, 128, lens, 1024, FP8, pad="nan")
+    S = 7
+    d = to_dev(case)
+    po, pm, pd = F.decode_partials(d["q"], d["k"], d["v"], d["seq_lens"], S, k_descale=d["k_descale"],
+                                   v_descale=d["v_descale"])
+    torch.cuda.synchronize()
+    chunk = F.split_chunk(case.capacity, S)
+    bounds = np.array([[min(i * chunk, case.capacity) for i in range(S + 1)]] * 4, dtype=np.int32)
+    rpo, rpm, rpd = oracle.partials(okv(case), case.q, case.seq_lens, 1 / math.sqrt(128), bounds)
+    gpo, gpm, gpd = (t.cpu().double().numpy() for t in (po, pm, pd))
+    fin = np.isfinite(rpm)
+    assert np.array_equal(np.isfinite(gpm), fin)
+    assert np.all(gpd[~fin] == 0) and np.all(gpo[~fin] == 0)
+    np.testing.assert_allclose(gpm[fin], rpm[fin], rtol=0, atol=1e-5 * np.abs(rpm[fin]).max() + 1e-5)
+    np.testing.assert_allclose(gpd[fin], rpd[fin], rtol=1e-4)
+    err = np.abs(gpo - rpo)[fin] / rpd[fin][:, None]
+    assert err.max() < 1e-3
+
+
+@pytest.mark.parametrize("name,mode", [("c2f8", "two"), ("c3f8", "bal"), ("c3f8", "two")])
+def test_fp8_full_size_workloads(name, mode):
+    case = workload(name, pad="nan")
+    ref_out, ref_lse = oracle_decode(case)
+    d = to_dev(case)
+    if mode == "bal":
+        out, lse = F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"],
+                                     k_descale=d["k_descale"], v_descale=d["v_descale"])
+    else:
+        B, Hq, _ = case.q.shape
+        S = F.plan(B, Hq, case.Hkv, case.seq_lens.tolist(), case.capacity, case.page_size)
+        out, lse = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S,
+                            k_descale=d["k_descale"], v_descale=d["v_descale"])
+    torch.cuda.synchronize()
+    assert_parity(out, lse, ref_out, ref_lse, case.dtype, f"{name} {mode}")
+
+
+def test_fp8_unsupported_shapes_and_paths_are_reported(monkeypatch):
+    case = contiguous_case(98, 1, 8, 4, 128, [40], 64, FP8, pad="nan")  # G = 2
+    with pytest.raises(F.FdecError) as e:
+        run(case, 2)
+    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
+    case = contiguous_case(99, 1, 8, 2, 128, [40], 64, FP8, pad="nan")  # G = 4 on the vector kernel
+    monkeypatch.setenv("FDEC_MAP_PATH", "vector")
+    with pytest.raises(F.FdecError) as e:
+        run(case, 2)
+    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
