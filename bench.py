@@ -34,6 +34,10 @@ WORKLOAD_TEXT = {
     "c4": "decode with KV append + NeoX rotary: B=4, Hq=32, Hkv=8, D=128, max_seqlen 2048, fp16",
     "c5": "cascade: 64 requests, Hq=32, Hkv=8, D=128, shared 16384-token prefix + U[256,2048] suffix, "
           "page 64, bf16",
+    "c2f8": "long-context GQA decode: B=1, Hq=32, Hkv=8, D=128, 131072 contiguous float8 e4m3fn tokens, "
+            "per-(request, KV head) descales, bf16 queries",
+    "c3f8": "paged batched decode: B=32, Hq=32, Hkv=8, D=128, page 16, lengths U[512,8192], float8 e4m3fn "
+            "KV with per-(request, KV head) descales, bf16 queries",
 }
 KERNEL_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
 
@@ -61,6 +65,9 @@ class Runner:
         self.q = case.q.to(dev)
         self.lens = case.seq_lens.to(dev)
         self.table = None if case.page_table is None else case.page_table.to(dev)
+        # float8 caches: per (request, KV head) descales
+        self.kd = None if case.k_descale is None else case.k_descale.to(dev)
+        self.vd = None if case.v_descale is None else case.v_descale.to(dev)
         kv_footprint = 2 * case.k.numel() * case.k.element_size()
         self.copies = max(1, min(64, math.ceil(min_footprint / kv_footprint)))
         self.k = [case.k.to(dev) for _ in range(self.copies)]
@@ -111,11 +118,12 @@ class Runner:
             return
         if self.mode == "bal":
             self.F.decode_balanced(self.q, self.k[c], self.v[c], self.lens, page_table=self.table,
-                                   num_blocks=self.S, out=self.out, lse=self.lse, workspace=self.ws)
+                                   num_blocks=self.S, out=self.out, lse=self.lse, workspace=self.ws,
+                                   k_descale=self.kd, v_descale=self.vd)
             return
         self.F.decode(self.q, self.k[c], self.v[c], self.lens, page_table=self.table, num_splits=self.S,
                       append=self.append, fused=(self.mode == "fused"), out=self.out, lse=self.lse,
-                      workspace=self.ws)
+                      workspace=self.ws, k_descale=self.kd, v_descale=self.vd)
 
 
 def time_region(runner: Runner, steps: int, warmup: int, copy=None):
@@ -155,6 +163,8 @@ def time_map_kernel(F, runner: Runner, steps: int):
     case = runner.case
     B, Hq, D = case.q.shape
     S = runner.S
+    if S == 0:  # the balanced split has no map-only entry: time the uniform map at the planner's count
+        S = F.plan(B, Hq, case.Hkv, case.seq_lens.tolist(), case.capacity, case.page_size)
     po = torch.empty(B, Hq, S, D, dtype=torch.float32, device=runner.dev)
     pm = torch.empty(B, Hq, S, dtype=torch.float32, device=runner.dev)
     pd = torch.empty(B, Hq, S, dtype=torch.float32, device=runner.dev)
@@ -164,7 +174,8 @@ def time_map_kernel(F, runner: Runner, steps: int):
         if i >= 3:
             ev[i - 3][0].record()
         F.decode_partials(runner.q, runner.k[c], runner.v[c], runner.lens, S, page_table=runner.table,
-                          append=runner.append, part_o=po, part_m=pm, part_d=pd)
+                          append=runner.append, part_o=po, part_m=pm, part_d=pd, k_descale=runner.kd,
+                          v_descale=runner.vd)
         if i >= 3:
             ev[i - 3][1].record()
     torch.cuda.synchronize()
@@ -187,18 +198,22 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> dict:
         out = {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
-                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                out.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
         return out
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
 
-    def pick(d, key):
-        vals = [v for k, vs in d.items() if key in k for v in vs]
+    def pick(d, key):  # median over the dispatches of the kernel
+        vals = [v for k, vs in d.items() if key in k for _, v in vs]
         return sorted(vals)[len(vals) // 2] if vals else None
 
-    fetch_scale = CALIB_BYTES / 1024.0 / pick(f, "read_kernel")
-    write_scale = CALIB_BYTES / 1024.0 / pick(w, "copy_kernel")
+    def last(d, key):  # the calibration probes are the last read / copy dispatches of the run
+        vals = [dv for k, vs in d.items() if key in k for dv in vs]
+        return max(vals)[1] if vals else None
+
+    fetch_scale = CALIB_BYTES / 1024.0 / last(f, "read_kernel")
+    write_scale = CALIB_BYTES / 1024.0 / last(w, "copy_kernel")
     fk, wk = pick(f, "map_kernel"), pick(w, "map_kernel")
     return {"fetch_kib": fk, "write_kib": wk, "fetch_scale": round(fetch_scale, 4),
             "write_scale": round(write_scale, 4),
@@ -229,8 +244,8 @@ def cpu_baseline(case, budget_s: float):
 
     oracle.build(force=False)
     kv = oracle.KV(case.k, case.v, oracle.dtype_code(case.k), case.Hq, case.B, case.page_size, case.page_table,
-                   case.prefix_pages, case.prefix_len)
-    q = oracle.to_f64(case.q, oracle.dtype_code(case.k))
+                   case.prefix_pages, case.prefix_len, case.k_descale, case.v_descale)
+    q = oracle.to_f64(case.q, oracle.dtype_code(case.q))
     scale = 1.0 / math.sqrt(case.D)
     threads = oracle.max_threads()
     reps, t0 = 0, oracle.now()
@@ -271,10 +286,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4,c5", help="other workloads timed for context ('' = none)")
+    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8",
+                    help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -350,6 +366,8 @@ def main() -> int:
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         if name == "c3":
             runs += [("c3", "c3", "bal"), ("c3_uniform_splits", "c3", args.mode)]
+        elif name == "c3f8":
+            runs.append((name, name, "bal"))
         else:
             runs.append((name, name, args.mode))
     for key, name, mode in runs:
@@ -384,7 +402,7 @@ def main() -> int:
         "dtype": "f32",  # arithmetic type: fp32 math on fp16/bf16 KV (kv_dtype in config)
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload],
-                   "kv_dtype": "bf16" if case.dtype == _t.bfloat16 else "fp16", **res},
+                   "kv_dtype": {_t.bfloat16: "bf16", _t.float16: "fp16"}.get(case.dtype, "fp8_e4m3fn"), **res},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "other_workloads": others,

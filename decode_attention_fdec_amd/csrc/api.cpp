@@ -314,7 +314,10 @@ extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv 
 }
 
 // Balanced split: blocks per group of KV heads (0 = one per compute unit over all groups).
-int balanced_blocks(int Hkv, int num_blocks) {
+// Default block count of the balanced split: per_cu blocks per compute unit
+// over all groups of KV heads (16-bit caches: 1; float8 caches: 2, whose
+// tiles take half the LDS and whose blocks then overlap each other's latency).
+int balanced_blocks(int Hkv, int num_blocks, int per_cu) {
     if (num_blocks > 0) return num_blocks;
     int hpb = 1;
     for (int w = fdec::kMapMfmaWaves; w > 1; --w)
@@ -326,7 +329,7 @@ int balanced_blocks(int Hkv, int num_blocks) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
         cu = 256;
-    return std::max(1, std::min(FDEC_MAX_SPLITS, cu / (Hkv / hpb)));
+    return std::max(1, std::min(FDEC_MAX_SPLITS, per_cu * cu / (Hkv / hpb)));
 }
 
 struct BalLayout {
@@ -345,7 +348,8 @@ BalLayout bal_layout(int B, int Hq, int D, int nb) {
 
 extern "C" size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_blocks) {
     if (B < 0 || Hq < 1 || Hkv < 1 || head_dim < 1 || num_blocks < 0 || num_blocks > FDEC_MAX_SPLITS) return 0;
-    return bal_layout(B, Hq, head_dim, balanced_blocks(Hkv, num_blocks)).total;
+    // the default of either cache format fits (the float8 one is the larger)
+    return bal_layout(B, Hq, head_dim, balanced_blocks(Hkv, num_blocks, 2)).total;
 }
 
 extern "C" int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
@@ -367,7 +371,7 @@ extern "C" int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv 
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
-    const int nb = balanced_blocks(kv->num_kv_heads, num_blocks);
+    const int nb = balanced_blocks(kv->num_kv_heads, num_blocks, kv->dtype == FDEC_FP8_E4M3 ? 2 : 1);
     const BalLayout w = bal_layout(B, Hq, kv->head_dim, nb);
     if (!workspace || workspace_bytes < w.total)
         return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d blocks, got %zu", fn, w.total,

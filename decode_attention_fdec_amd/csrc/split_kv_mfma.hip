@@ -30,10 +30,12 @@
 //     at d = L and 64 + L.
 // Float8 caches (the pages' FP8 KV cache: e4m3fn values with one fp32 descale
 // per (request, KV head) for K and one for V): tiles arrive at half the bytes;
-// K is converted to bf16 in registers after its LDS read and V into a bf16
-// tile for the transpose read (v_cvt_scalef32_pk_bf16_fp8 at scale 1: every
-// e4m3 value is a bf16 value, so both are exact); K's descale multiplies the
-// score scale and V's the written state.
+// K is converted to bf16 in registers after its LDS read, V after an 8-bit
+// transpose read (ds_read_b64_tr_b8: in each group of 16 lanes, lane j receives
+// byte j % 8 of the 8-byte chunks addressed by lanes j/8 + 2k, k = 0..7, also
+// verified on the GPU), both by v_cvt_scalef32_pk_bf16_fp8 at scale 1 (every
+// e4m3 value is a bf16 value: exact). K's descale multiplies the score scale
+// and V's the written state.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -42,7 +44,9 @@ namespace fdec {
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_v __attribute__((ext_vector_type(4)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
+typedef int i32x2_v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2_v lds_i32x2;
 
 template <int DT> struct Mfma4;
 template <> struct Mfma4<0> {
@@ -128,9 +132,24 @@ constexpr int kMTileBytes = kMT * 256;  // one tile of K (or V) rows of one KV h
 #ifndef FDEC_MFMA_NBUF
 #define FDEC_MFMA_NBUF 2
 #endif
+#ifndef FDEC_MFMA_NBUF8
+#define FDEC_MFMA_NBUF8 3
+#endif
 constexpr int kNbuf = FDEC_MFMA_NBUF;   // ring slots per wave: kNbuf - 1 tiles in flight ahead
-static_assert(kNbuf >= 2 && kNbuf <= 8, "ring of 2..8 tiles");
-static_assert(kMapMfmaWaves * kNbuf * 2 * kMTileBytes <= 128 * 1024, "K/V ring fits in LDS");
+constexpr int kNbuf8 = FDEC_MFMA_NBUF8; // the same for float8 tiles (half the bytes: a deeper ring)
+static_assert(kNbuf >= 2 && kNbuf <= 8 && kNbuf8 >= 2 && kNbuf8 <= 8, "rings of 2..8 tiles");
+
+// One wave's LDS ring: slots of [K tile | V tile], kNbuf of them for 16-bit
+// tiles, kNbuf8 for float8 tiles (half the size).
+template <int KF> struct Ring {
+    static constexpr int kSlots = KF ? kNbuf8 : kNbuf;
+    static constexpr int kTileBytes = KF ? kMTileBytes / 2 : kMTileBytes;
+    static constexpr int kBytes = kSlots * 2 * kTileBytes;
+    static __device__ __forceinline__ uint8_t *k_tile(uint8_t *w, int slot) { return w + slot * 2 * kTileBytes; }
+    static __device__ __forceinline__ uint8_t *v_tile(uint8_t *w, int slot) { return k_tile(w, slot) + kTileBytes; }
+};
+static_assert(kMapMfmaWaves * Ring<0>::kBytes <= 128 * 1024, "16-bit K/V rings fit in LDS");
+static_assert(kMapMfmaWaves * (Ring<1>::kBytes + kNbuf8 * 1024) <= 128 * 1024, "float8 K/V rings fit in LDS");
 constexpr float kTau = 8.0f;            // the softmax reference moves when a score exceeds it by 2^kTau
 constexpr float kFloor = -1.0e30f;      // initial reference (finite: masked scores give p = 0, no NaN)
 
@@ -147,8 +166,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
 // rows per quarter wave), V rows swz = 4 (r & 3) (a transpose read takes 4
 // pieces of 4 consecutive rows per half wave).
 // float8 (128-byte rows): instruction i (0..1) writes rows 8i..8i+7, lane l
-// slot (l & 7) of row r = 8i + l / 8 with piece (l & 7) ^ ((r >> 1) & 7), for K
-// and V alike (the 16 rows of a quarter-wave read then cover all 64 banks).
+// slot (l & 7) of row r = 8i + l / 8 with piece (l & 7) ^ swz(r): for K
+// swz = (r >> 1) & 7 (the 16 rows of a quarter-wave S^T read cover all 64
+// banks), for V swz = 2 ((r >> 1) & 3) (the 8 rows x 2 pieces of a half-wave
+// transpose read take 16 distinct (row parity, slot) pairs: all 64 banks).
 // kb / vb address the tile's first row; rows past nrows repeat row nrows - 1.
 template <int KF>
 __device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint32_t kl, uint32_t vl, int nrows,
@@ -167,9 +188,9 @@ __device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint3
 #pragma unroll
         for (int i = 0; i < kMT / 8; ++i) {
             const int r = 8 * i + srow;
-            const uint32_t at = (uint32_t)min(r, nrows - 1) * stok + 16u * (uint32_t)(sslot ^ ((r >> 1) & 7));
-            dma16(kb, at, kl + 1024u * i);
-            dma16(vb, at, vl + 1024u * i);
+            const uint32_t row = (uint32_t)min(r, nrows - 1) * stok;
+            dma16(kb, row + 16u * (uint32_t)(sslot ^ ((r >> 1) & 7)), kl + 1024u * i);
+            dma16(vb, row + 16u * (uint32_t)(sslot ^ (2 * ((r >> 1) & 3))), vl + 1024u * i);
         }
     }
 }
@@ -199,14 +220,11 @@ __device__ __forceinline__ float kv_descale(const float *d, const MapParams &p, 
     return ((cf_t)d)[(int64_t)b * p.Hkv + g];
 }
 
-// LDS addresses of ring slot `slot`: K tile and V tile (16-bit), or the float8
-// K and V tiles in the two halves of the K area (the V area then receives V as
-// bf16 for the transpose read).
+// LDS addresses of ring slot `slot`: its K tile and V tile.
 template <int KF>
-__device__ __forceinline__ void slot_dma_addrs(uint8_t (*ring)[2][kMTileBytes], int slot, uint32_t &kl,
-                                               uint32_t &vl) {
-    kl = lds_addr(ring[slot][0]);
-    vl = KF ? kl + kMTileBytes / 2 : lds_addr(ring[slot][1]);
+__device__ __forceinline__ void slot_dma_addrs(uint8_t *wl, int slot, uint32_t &kl, uint32_t &vl) {
+    kl = lds_addr(Ring<KF>::k_tile(wl, slot));
+    vl = lds_addr(Ring<KF>::v_tile(wl, slot));
 }
 
 // Q of the four query heads of KV head g of request b (1 KB) to LDS, with the
@@ -248,10 +266,9 @@ struct MfmaSoftmax {
 };
 
 // One tile: S^T = K Q^T, online softmax, O += P V. nvalid (>= 1) tokens of the
-// tile count; the rest are masked. kl: the K tile; vl: the V tile (bf16 target
-// for float8, whose V tile is at kl + kMTileBytes / 2).
+// tile count; the rest are masked. kl / vl: the K and V tiles in LDS.
 template <int DT, int KF>
-__device__ __forceinline__ void mfma_tile(const uint8_t *kl, uint8_t *vl, const uint2 qb[8], int nvalid,
+__device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 qb[8], int nvalid,
                                           float scale_log2, int lane, MfmaSoftmax &st) {
     using E = Elem<DT>;
     const int dq = lane >> 4;
@@ -278,21 +295,25 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, uint8_t *vl, const 
             s = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.z), qb[4 * e + 2], s);
             s1 = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.w), qb[4 * e + 3], s1);
         }
-        // V as bf16: lane l converts row l / 4, d 32 (l & 3) .. + 31 (float8
-        // pieces 2 (l & 3) + e), written as bf16 pieces 4 (l & 3) + 2e + {0, 1}
-        // in the 16-bit V layout (slot = piece ^ 4 (row & 3))
-        const uint8_t *v8 = kl + kMTileBytes / 2;
-        const int vr = lane >> 2, vq = lane & 3;
+    }
+    // float8 V^T for P V: lane L gets tokens 8c .. 8c + 7 at d = 64h + L from the
+    // 8-bit transpose read whose lane m (of 16) addresses row 8c + m / 2, bytes
+    // 64h + 16 (L / 16) + 8 (m & 1) .. + 7; its first four bytes are the B operand
+    // of token group 2c, the last four that of group 2c + 1
+    uint2 vb[2][2][2];  // [c][h][group within c]
+    if constexpr (KF == 1) {
+        const int m = lane & 15, gq = lane >> 4;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int pc = 2 * vq + e;
-            const uint4 x = *reinterpret_cast<const uint4 *>(v8 + vr * 128 + 16 * (pc ^ ((vr >> 1) & 7)));
-            const uint2 a0 = fp8x4_to_bf16(x.x), a1 = fp8x4_to_bf16(x.y);
-            const uint2 a2 = fp8x4_to_bf16(x.z), a3 = fp8x4_to_bf16(x.w);
-            *reinterpret_cast<uint4 *>(vl + vr * 256 + 16 * ((2 * pc) ^ (4 * (vr & 3)))) =
-                make_uint4(a0.x, a0.y, a1.x, a1.y);
-            *reinterpret_cast<uint4 *>(vl + vr * 256 + 16 * ((2 * pc + 1) ^ (4 * (vr & 3)))) =
-                make_uint4(a2.x, a2.y, a3.x, a3.y);
+        for (int c = 0; c < 2; ++c) {
+            const int r = 8 * c + (m >> 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int piece = 4 * h + gq;
+                lds_i32x2 *src = (lds_i32x2 *)(vl + r * 128 + 16 * (piece ^ (2 * ((r >> 1) & 3))) + 8 * (m & 1));
+                const i32x2_v w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(src);
+                vb[c][h][0] = fp8x4_to_bf16((uint32_t)w[0]);
+                vb[c][h][1] = fp8x4_to_bf16((uint32_t)w[1]);
+            }
         }
     }
 
@@ -343,11 +364,16 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, uint8_t *vl, const 
     {                                                                                                         \
         const int row = 4 * (Q) + tk;                                                                         \
         _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                       \
-            const int piece = 8 * h + 2 * tg + (ta >> 1);                                                     \
-            lds_s16x4 *src = (lds_s16x4 *)(vl + row * 256 + 16 * (piece ^ (4 * (row & 3))) + 8 * (ta & 1));    \
-            const s16x4_v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);                                  \
-            st.o[h] = Mfma4<DT>::template run<4, (Q)>(pa, __builtin_bit_cast(uint2, vt), st.o[h]);            \
-            st.ol[h] = Mfma4<DT>::template run<4, (Q)>(pb, __builtin_bit_cast(uint2, vt), st.ol[h]);          \
+            uint2 vt;                                                                                         \
+            if constexpr (KF == 1) {                                                                          \
+                vt = vb[(Q) >> 1][h][(Q) & 1];                                                                \
+            } else {                                                                                          \
+                const int piece = 8 * h + 2 * tg + (ta >> 1);                                                 \
+                lds_s16x4 *src = (lds_s16x4 *)(vl + row * 256 + 16 * (piece ^ (4 * (row & 3))) + 8 * (ta & 1)); \
+                vt = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));                 \
+            }                                                                                                 \
+            st.o[h] = Mfma4<DT>::template run<4, (Q)>(pa, vt, st.o[h]);                                       \
+            st.ol[h] = Mfma4<DT>::template run<4, (Q)>(pb, vt, st.ol[h]);                                     \
         }                                                                                                     \
     }
     FDEC_PV_STEP(0)
@@ -386,18 +412,19 @@ __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, flo
 }
 
 // One wave's pass over tokens [t_begin, t_end) of request b for KV head g
-// (its four query heads), state to po0 / pm0 / pd0 (+ i hs per head). ring /
-// qslot are the wave's LDS: kNbuf ring slots of K and V tiles and 1 KB of Q.
+// (its four query heads), state to po0 / pm0 / pd0 (+ i hs per head). wl /
+// qslot are the wave's LDS: its ring (Ring<KF>) and 1 KB of Q.
 template <int DT, bool PAGED, int KF>
-__device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)[2][kMTileBytes], uint8_t *qslot,
+__device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, uint8_t *qslot,
                                              int b, int g, int lane, int t_begin, int t_end, float *po0, float *pm0,
                                              float *pd0, int64_t hs) {
     const int ntok = t_end - t_begin;
     const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
     const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
+    constexpr int NS = Ring<KF>::kSlots;
     auto stage = [&](int tile, int64_t off) {
         uint32_t kl, vl;
-        slot_dma_addrs<KF>(ring, tile % kNbuf, kl, vl);
+        slot_dma_addrs<KF>(wl, tile % NS, kl, vl);
         stage_tile<KF>(p.k + off, p.v + off, kl, vl, t_end - (t_begin + tile * kMT), stok, lane);
     };
     auto tile_offset = [&](int tile) { return token_offset<PAGED, KF>(p, b, g, t_begin + tile * kMT); };
@@ -407,25 +434,25 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)
     MfmaSoftmax st;
     st.reset();
     stage_q(p, b, g, qslot, lane);
-    // prologue: the first kNbuf - 1 tiles
-    const int npro = min(kNbuf - 1, ntiles);
+    // prologue: the first NS - 1 tiles
+    const int npro = min(NS - 1, ntiles);
     for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
-    int64_t noff = (kNbuf - 1 < ntiles) ? tile_offset(kNbuf - 1) : 0;  // next tile to stage
+    int64_t noff = (NS - 1 < ntiles) ? tile_offset(NS - 1) : 0;  // next tile to stage
     wait_vm_n<KvFmt<KF>::kDma>(npro);  // Q has landed
     uint2 qb[8];
     read_q(qslot, lane, qb);
 
     for (int tile = 0; tile < ntiles; ++tile) {
-        const int ahead = tile + kNbuf - 1;
+        const int ahead = tile + NS - 1;
         if (ahead < ntiles) {
             stage(ahead, noff);
             if (ahead + 1 < ntiles) noff = tile_offset(ahead + 1);
         }
         // this tile's loads have landed once only the later tiles' remain
-        wait_vm_n<KvFmt<KF>::kDma>(min(kNbuf - 1, ntiles - 1 - tile));
-        const int slot = tile % kNbuf;
-        mfma_tile<DT, KF>(ring[slot][0], ring[slot][1], qb, t_end - (t_begin + tile * kMT), p.scale_log2 * kd, lane,
-                          st);
+        wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, ntiles - 1 - tile));
+        const int slot = tile % NS;
+        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, t_end - (t_begin + tile * kMT),
+                          p.scale_log2 * kd, lane, st);
     }
     write_state(st, lane, po0, pm0, pd0, hs, vd);
 }
@@ -433,8 +460,7 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t (*ring)
 template <int DT, bool PAGED, int KF>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(const MapParams p) {
     constexpr int D = 128, G = 4;
-    // [wave][ring slot][K, V][tile bytes]
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
     __shared__ int sm_flag;
 
@@ -494,7 +520,7 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // the finished piece's state to slot (block + request) of [Hq, nslots]
 // (nslots = gridDim.x + B; the pieces of one request take consecutive slots)
 // and resets its softmax. Q of each request is staged by DMA ahead of the
-// request's first tile into one of kNbuf Q slots. The block holding a
+// request's first tile into one of the ring's Q slots. The block holding a
 // request's first tile records (first slot, piece count) in seg_meta[2b..].
 // With fewer tiles than blocks, only the first (tiles) blocks take work, so
 // every working block has at least one tile and no slot of a request is left
@@ -502,8 +528,10 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 template <int DT, bool PAGED, int KF>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
     constexpr int D = 128, G = 4;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][kNbuf][2][kMTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][kNbuf][G * D * 2];
+    constexpr int NS = Ring<KF>::kSlots;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
+    // Q of the pieces in flight: at most one per ring slot
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][NS][G * D * 2];
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -579,21 +607,21 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     };
     const int Lb0 = slens[b0];
     Cursor prod{b0, P0, T0, Lb0, 0}, cons{b0, P0, T0, Lb0, 0};
-    uint8_t(*ring)[2][kMTileBytes] = lds[wv];
+    uint8_t *wl = lds[wv];
     auto produce = [&](int x) {  // stage tile x (and Q when it starts a new piece)
         if (x >= prod.P + prod.T) {
             advance(prod);
-            stage_q(p, prod.b, g, qlds[wv][prod.seg % kNbuf], lane);
+            stage_q(p, prod.b, g, qlds[wv][prod.seg % NS], lane);
         }
         const int t0 = (x - prod.P) * kMT;
         const int64_t off = token_offset<PAGED, KF>(p, prod.b, g, t0);
         uint32_t kl, vl;
-        slot_dma_addrs<KF>(ring, x % kNbuf, kl, vl);
+        slot_dma_addrs<KF>(wl, x % NS, kl, vl);
         stage_tile<KF>(p.k + off, p.v + off, kl, vl, prod.L - t0, stok, lane);
     };
 
     stage_q(p, b0, g, qlds[wv][0], lane);
-    const int npro = min(kNbuf - 1, end - start);
+    const int npro = min(NS - 1, end - start);
     for (int i = 0; i < npro; ++i) produce(start + i);
 
     MfmaSoftmax st;
@@ -601,10 +629,10 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     uint2 qb[8];
     float kd = 1.0f, vd = 1.0f;  // the current request's float8 descales
     for (int x = start; x < end; ++x) {
-        if (x + kNbuf - 1 < end) produce(x + kNbuf - 1);
+        if (x + NS - 1 < end) produce(x + NS - 1);
         // tile x has landed once at most the later tiles' loads remain (a Q load
         // issued after it only makes this wait longer)
-        wait_vm_n<KvFmt<KF>::kDma>(min(kNbuf - 1, end - 1 - x));
+        wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, end - 1 - x));
         if (x == start) {
             read_q(qlds[wv][0], lane, qb);
             if (KF) {
@@ -616,15 +644,15 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
             write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
             st.reset();
             advance(cons);
-            read_q(qlds[wv][cons.seg % kNbuf], lane, qb);
+            read_q(qlds[wv][cons.seg % NS], lane, qb);
             if (KF) {
                 kd = kv_descale(p.k_descale, p, cons.b, g);
                 vd = kv_descale(p.v_descale, p, cons.b, g);
             }
         }
-        const int slot = x % kNbuf;
-        mfma_tile<DT, KF>(ring[slot][0], ring[slot][1], qb, cons.L - (x - cons.P) * kMT, p.scale_log2 * kd, lane,
-                          st);
+        const int slot = x % NS;
+        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, cons.L - (x - cons.P) * kMT,
+                          p.scale_log2 * kd, lane, st);
     }
     const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
     write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);

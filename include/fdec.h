@@ -224,9 +224,9 @@ int fdec_merge_states(const float *part_o, const float *part_m, const float *par
  * graph whose lengths change between replays.
  *   Supported for G = Hq/Hkv = 4, head_dim 128, page_size a multiple of 16 (or
  *   contiguous), no append: FDEC_ERR_UNSUPPORTED otherwise.
- *   num_blocks  blocks per group of KV heads, 1..256; 0 = one per compute unit
- *               of the current device over all groups (measured best on MI355X:
- *               a second block per unit only adds contention).
+ *   num_blocks  blocks per group of KV heads, 1..256; 0 = per compute unit of
+ *               the current device over all groups, one block for fp16/bf16
+ *               caches and two for float8 caches (measured best on MI355X).
  *   Requires B * ceil(capacity / 16) < 2^31 (FDEC_ERR_INVALID_ARG otherwise).
  *   out / lse as in fdec_decode. workspace >= fdec_balanced_workspace_size()
  *   bytes (no initialisation needed).
@@ -235,7 +235,8 @@ int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv *kv, const 
                          int num_blocks, float softmax_scale, float *out, float *lse, void *workspace,
                          size_t workspace_bytes, void *stream);
 
-/* Workspace bytes for fdec_decode_balanced (num_blocks as there, 0 = default). */
+/* Workspace bytes for fdec_decode_balanced (num_blocks as there; 0 = enough for
+ * the default of every cache dtype). */
 size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_blocks);
 
 /*
