@@ -10,8 +10,8 @@ k_new -> v_new. Float8 (e4m3fn) caches: q is bf16; K and V are drawn in
 float32 as above, then one descale per (request, KV head) each for K and V is
 drawn uniform in [1/64, 1/16], and the stored value is x / descale clamped to
 +-448 and cast with round-to-nearest-even (the dequantised value is stored x
-descale; unused pages use descale 1/32). Rows past a request's length hold zeros, NaN or random values
-(``pad``); paged pools hold exactly the pages the requests use plus
+descale; unused pages use descale 1/32). Rows past a request's length hold
+zeros, NaN or random values (``pad``); paged pools hold exactly the pages the requests use plus
 ``extra_pages`` unused ones (filled like padding), with physical page ids a
 seeded random permutation, and the page table padded with -1.
 
