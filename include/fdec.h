@@ -82,7 +82,13 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  *                   max_pages_per_seq * page_size.
  * k and v must be 16-byte aligned and every stride a multiple of 16 bytes (8
  * 16-bit or 16 float8 elements). They are written only by an append (one row
- * per request and KV head).
+ * per request and KV head). Other layouts are described by their strides
+ * ([vllm-arch] KV cache shapes), e.g. HND pages [pages, Hkv, page, D]:
+ * s_outer = Hkv*page*D, s_token = D, s_head = page*D; one pool
+ * [blocks, 2, page, Hkv, D] holding K and V: k = pool, v = pool + page*Hkv*D,
+ * s_outer = 2*page*Hkv*D, s_token = Hkv*D, s_head = D (HND pool
+ * [blocks, 2, Hkv, page, D] likewise). page_size has no upper bound beyond
+ * capacity < 2^31.
  * Float8 caches (dtype FDEC_FP8_E4M3): element (b, t, g, d) stands for its
  * e4m3 value times k_descale[b*Hkv + g] (K) or v_descale[b*Hkv + g] (V); a NULL
  * descale is 1. Queries are bf16. Built for Hq = 4 Hkv, head_dim 128, page_size
