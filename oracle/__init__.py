@@ -49,6 +49,7 @@ class _KV(ctypes.Structure):
         ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int),
         ("prefix_pages", ctypes.c_void_p), ("prefix_len", ctypes.c_int),
         ("k_descale", ctypes.c_void_p), ("v_descale", ctypes.c_void_p),
+        ("batch_idx", ctypes.c_void_p), ("leftpad", ctypes.c_void_p),
     ]
 
 
@@ -142,7 +143,8 @@ class KV:
     """One KV cache as the oracle reads it (raw bits + geometry)."""
 
     def __init__(self, k, v, dtype: int, Hq: int, B: int, page_size: int = 0,
-                 page_table=None, prefix_pages=None, prefix_len: int = 0, k_descale=None, v_descale=None):
+                 page_table=None, prefix_pages=None, prefix_len: int = 0, k_descale=None, v_descale=None,
+                 batch_idx=None, leftpad=None):
         self.k = _bits(k)
         self.v = _bits(v)
         assert self.k.shape == self.v.shape and self.k.ndim == 4
@@ -158,6 +160,10 @@ class KV:
         self.prefix_len = prefix_len
         self.k_descale = _f64(k_descale, (B, self.Hkv))
         self.v_descale = _f64(v_descale, (B, self.Hkv))
+        self.batch_idx = _i32(batch_idx)  # contiguous caches: cache row of request b
+        self.leftpad = _i32(leftpad)      # first valid row of request b
+        for a in (self.batch_idx, self.leftpad):
+            assert a is None or a.shape == (B,)
 
     def _struct(self) -> _KV:
         s = _KV()
@@ -172,6 +178,8 @@ class KV:
         s.prefix_len = self.prefix_len
         s.k_descale = _ptr(self.k_descale)
         s.v_descale = _ptr(self.v_descale)
+        s.batch_idx = _ptr(self.batch_idx)
+        s.leftpad = _ptr(self.leftpad)
         return s
 
 

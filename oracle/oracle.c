@@ -34,6 +34,10 @@
  *   paging           logical token j of request b lives in page
  *                    page_table[b][j / ps], slot j % ps; entries past the
  *                    request's pages are -1 and are never read ([cookbook] §4.2).
+ *   cache_batch_idx  request b reads (and appends to) row batch_idx[b] of a
+ *                    contiguous cache ([cookbook] §5.2).
+ *   cache_leftpad    request b's valid rows start at leftpad[b]: it attends
+ *                    to rows [leftpad[b], L_b) ([cookbook] §5.3).
  *
  * Readings where the pages are silent (all listed in the design notes):
  *   - empty range: out = 0, lse = -inf; an empty split is (O~=0, m=-inf, d=0)
@@ -43,7 +47,11 @@
  *   - the rotated k row is rounded once (round to nearest even) to the cache
  *     dtype; q stays in double; v is copied unchanged;
  *   - cascade: request b's tokens are the shared prefix (prefix_pages) followed
- *     by its own suffix pages (page_table row b).
+ *     by its own suffix pages (page_table row b);
+ *   - lengths (lens / cache_seqlens) count rows from row 0, left padding
+ *     included; an appended row goes to row cache_seqlens[b] and is rotated at
+ *     its position among the valid rows, cache_seqlens[b] - leftpad[b];
+ *   - float8 descales are indexed by the query's request b.
  */
 #include <math.h>
 #include <stdint.h>
@@ -167,13 +175,17 @@ typedef struct {
     const int32_t *prefix_pages; /* cascade: shared prefix pages, or NULL */
     int prefix_len;              /* cascade: shared prefix tokens */
     const double *k_descale, *v_descale; /* float8: [B, Hkv] factors, or NULL for 1 */
+    const int32_t *batch_idx; /* contiguous: cache row of request b, or NULL for b */
+    const int32_t *leftpad;   /* first valid row of request b, or NULL for 0 */
 } oracle_kv;
+
+static int first_row(const oracle_kv *kv, int b) { return kv->leftpad ? kv->leftpad[b] : 0; }
 
 /* Element offset of logical token j of request b for KV head g. */
 static int64_t row_offset(const oracle_kv *kv, int b, int j, int g) {
     int64_t outer, slot;
     if (kv->page_size == 0) {
-        outer = b;
+        outer = kv->batch_idx ? kv->batch_idx[b] : b;
         slot = j;
     } else if (kv->prefix_pages && j < kv->prefix_len) {
         outer = kv->prefix_pages[j / kv->page_size];
@@ -273,10 +285,11 @@ void oracle_decode(const oracle_kv *kv, const double *q, const int32_t *lens, do
         for (int bh = 0; bh < B * Hq; ++bh) {
             int b = bh / Hq, h = bh % Hq;
             int L = lens[b] + (kv->prefix_pages ? kv->prefix_len : 0);
+            int lo = first_row(kv, b);
             double m, dsum;
             double *o = out + (int64_t)bh * D;
-            attend_range(kv, q + (int64_t)bh * D, b, h, 0, L, scale, sbuf, o, &m, &dsum);
-            if (L == 0) {
+            attend_range(kv, q + (int64_t)bh * D, b, h, lo, L, scale, sbuf, o, &m, &dsum);
+            if (L <= lo) {
                 lse[bh] = -INFINITY;
                 continue;
             }
@@ -289,7 +302,8 @@ void oracle_decode(const oracle_kv *kv, const double *q, const int32_t *lens, do
 
 /*
  * Map stage with explicit split boundaries: bounds is [B, S+1]; split i of
- * request b covers tokens [bounds[b][i], bounds[b][i+1]) (clipped to L_b).
+ * request b covers tokens [bounds[b][i], bounds[b][i+1]) (clipped to
+ * [leftpad[b], L_b)).
  * po [B,Hq,S,D], pm/pd [B,Hq,S].
  */
 void oracle_partials(const oracle_kv *kv, const double *q, const int32_t *lens, double scale,
@@ -310,6 +324,7 @@ void oracle_partials(const oracle_kv *kv, const double *q, const int32_t *lens, 
                 int lo = bounds[(int64_t)b * (S + 1) + i];
                 int hi = bounds[(int64_t)b * (S + 1) + i + 1];
                 if (hi > L) hi = L;
+                if (lo < first_row(kv, b)) lo = first_row(kv, b);
                 if (lo > hi) lo = hi;
                 int64_t si = (int64_t)bh * S + i;
                 attend_range(kv, q + (int64_t)bh * D, b, h, lo, hi, scale, sbuf, po + si * D,
@@ -370,11 +385,11 @@ void oracle_rope_neox(double *x, int D, int rotary_dim, int pos, double base) {
 
 /*
  * KV append with fused rotary, for a contiguous or paged cache. For each
- * request b with c = cache_seqlens[b]:
- *   k row c of every KV head  <- round_once(rope(k_new[b,g], c))   (rotary_dim > 0)
+ * request b with c = cache_seqlens[b] and position p = c - leftpad[b]:
+ *   k row c of every KV head  <- round_once(rope(k_new[b,g], p))   (rotary_dim > 0)
  *                                or k_new[b,g] bit-copied          (rotary_dim == 0)
  *   v row c of every KV head  <- v_new[b,g] bit-copied
- *   q_out[b,h]                <- rope(q[b,h], c) in double (or q unchanged)
+ *   q_out[b,h]                <- rope(q[b,h], p) in double (or q unchanged)
  * k_cache/v_cache are modified in place (the caller passes copies).
  * cache_seqlens is not modified; attention then covers c + 1 tokens.
  */
@@ -386,6 +401,7 @@ void oracle_append(oracle_kv *kv, uint16_t *k_cache, uint16_t *v_cache, const ui
     double *tmp = (double *)malloc(sizeof(double) * (size_t)D);
     for (int b = 0; b < B; ++b) {
         int c = cache_seqlens[b];
+        int pos = c - first_row(kv, b);
         for (int g = 0; g < Hkv; ++g) {
             int64_t off = row_offset(kv, b, c, g);
             const uint16_t *kn = k_new + ((int64_t)b * Hkv + g) * D;
@@ -393,7 +409,7 @@ void oracle_append(oracle_kv *kv, uint16_t *k_cache, uint16_t *v_cache, const ui
             if (rotary_dim > 0) {
                 for (int d = 0; d < D; ++d)
                     tmp[d] = kv->dtype == 0 ? oracle_f16_to_f64(kn[d]) : oracle_bf16_to_f64(kn[d]);
-                oracle_rope_neox(tmp, D, rotary_dim, c, base);
+                oracle_rope_neox(tmp, D, rotary_dim, pos, base);
                 for (int d = 0; d < D; ++d)
                     k_cache[off + d] =
                         kv->dtype == 0 ? oracle_f64_to_f16(tmp[d]) : oracle_f64_to_bf16(tmp[d]);
@@ -406,7 +422,7 @@ void oracle_append(oracle_kv *kv, uint16_t *k_cache, uint16_t *v_cache, const ui
             const double *qi = q + ((int64_t)b * Hq + h) * D;
             double *qo = q_out + ((int64_t)b * Hq + h) * D;
             for (int d = 0; d < D; ++d) qo[d] = qi[d];
-            if (rotary_dim > 0) oracle_rope_neox(qo, D, rotary_dim, c, base);
+            if (rotary_dim > 0) oracle_rope_neox(qo, D, rotary_dim, pos, base);
         }
     }
     free(tmp);

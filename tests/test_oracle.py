@@ -504,3 +504,105 @@ def test_fp8_cache_equals_bf16_cache_holding_the_same_values():
     ob, lb = oracle.decode(kb, case.q, case.seq_lens, 0.2)
     np.testing.assert_array_equal(o8, ob)
     np.testing.assert_array_equal(l8, lb)
+
+
+# ---------------------------------------------------------------- cache_batch_idx and cache_leftpad
+
+def _sdpa_rows(q, k, v, scale):
+    """float64 attention of q [Hq, D] over rows k, v [L, Hkv, D] (torch), and its LSE."""
+    qq = q.to(torch.float64)[None, :, None, :]
+    kk = k.to(torch.float64).permute(1, 0, 2)[None].contiguous()
+    vv = v.to(torch.float64).permute(1, 0, 2)[None].contiguous()
+    out = F.scaled_dot_product_attention(qq, kk, vv, scale=scale, enable_gqa=True)[0, :, 0, :]
+    s = torch.einsum("hd,hld->hl", qq[0, :, 0, :],
+                     kk[0].repeat_interleave(q.shape[0] // k.shape[1], dim=0)) * scale
+    return out.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+def test_cache_batch_idx_reads_the_indexed_rows():
+    # 3 requests over a 5-row cache; rows no request names hold NaN
+    g = torch.Generator().manual_seed(160)
+    Bc, cap, Hkv, D, Hq = 5, 24, 2, 16, 8
+    k = torch.randn(Bc, cap, Hkv, D, generator=g).to(BF16)
+    v = torch.randn(Bc, cap, Hkv, D, generator=g).to(BF16)
+    idx = torch.tensor([4, 0, 2], dtype=torch.int32)
+    lens = torch.tensor([24, 7, 1], dtype=torch.int32)
+    for r in (1, 3):
+        k[r] = float("nan")
+        v[r] = float("nan")
+    q = torch.randn(3, Hq, D, generator=g).to(BF16)
+    kv = oracle.KV(k, v, oracle.BF16, Hq, 3, batch_idx=idx)
+    out, lse = oracle.decode(kv, q, lens, 0.3)
+    for b in range(3):
+        L, r = int(lens[b]), int(idx[b])
+        ro, rl = _sdpa_rows(q[b], k[r, :L], v[r, :L], 0.3)
+        np.testing.assert_allclose(out[b], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_cache_leftpad_attends_to_the_rows_after_the_padding(paged):
+    lens, pads = [40, 9, 17, 30], [0, 5, 17, 29]  # request 2: all rows padding -> empty
+    if paged:
+        case = paged_case(161, 4, 8, 2, 16, lens, 16, BF16, extra_pages=2, pad="nan")
+    else:
+        case = contiguous_case(161, 4, 8, 2, 16, lens, 40, BF16, pad="nan")
+    lp = torch.tensor(pads, dtype=torch.int32)
+    for b, p in enumerate(pads):  # the padding rows hold NaN: reading one poisons the result
+        for j in range(p):
+            if paged:
+                case.k[int(case.page_table[b, j // 16]), j % 16] = float("nan")
+            else:
+                case.k[b, j] = float("nan")
+    kv = oracle.KV(case.k, case.v, oracle.BF16, 8, 4, case.page_size, case.page_table, leftpad=lp)
+    out, lse = oracle.decode(kv, case.q, case.seq_lens, 0.25)
+    for b in range(4):
+        rows = range(pads[b], lens[b])
+        if not len(rows):
+            assert np.all(out[b] == 0) and np.all(lse[b] == -np.inf)
+            continue
+        if paged:
+            kr = torch.stack([case.k[int(case.page_table[b, j // 16]), j % 16] for j in rows])
+            vr = torch.stack([case.v[int(case.page_table[b, j // 16]), j % 16] for j in rows])
+        else:
+            kr, vr = case.k[b, pads[b]:lens[b]], case.v[b, pads[b]:lens[b]]
+        ro, rl = _sdpa_rows(case.q[b], kr, vr, 0.25)
+        np.testing.assert_allclose(out[b], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=0, atol=1e-12)
+    # split states clipped at the padding merge to the same result
+    S = 3
+    bounds = np.array([[p + i * 8 for i in range(S)] + [64] for p in pads], dtype=np.int32)
+    bounds[:, 0] = 0  # a first bound inside the padding is clipped to it
+    po, pm, pd = oracle.partials(kv, case.q, case.seq_lens, 0.25, bounds)
+    mo, ml = oracle.merge(po, pm, pd)
+    np.testing.assert_allclose(mo, out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(ml[np.isfinite(lse)], lse[np.isfinite(lse)], rtol=0, atol=1e-13)
+
+
+def test_append_with_leftpad_and_batch_idx():
+    # the new row goes to row c of cache row batch_idx[b], rotated at its
+    # position among the valid rows, c - leftpad[b]; q is rotated alike
+    case = append_case(162, 3, 8, 2, 128, 64, F16, rotary_dim=128, pad="zero")
+    idx = torch.tensor([2, 0, 1], dtype=torch.int32)
+    c = case.seq_lens
+    lp = torch.minimum(torch.tensor([3, 0, 11], dtype=torch.int32), c)
+    kv = oracle.KV(case.k, case.v, oracle.F16, 8, 3, batch_idx=idx, leftpad=lp)
+    kc, vc, q_rot, after = oracle.append(kv, case.k_new, case.v_new, case.q, c, 128)
+    kn, vn = oracle._bits(case.k_new), oracle._bits(case.v_new)
+    for b in range(3):
+        r, cb, pos = int(idx[b]), int(c[b]), int(c[b]) - int(lp[b])
+        for g in range(2):
+            want = oracle.from_f64(oracle.rope_neox(oracle.to_f64(kn[b, g], 0), pos, 128), 0)
+            assert np.array_equal(kc[r, cb, g], want) and np.array_equal(vc[r, cb, g], vn[b, g])
+        qd = oracle.to_f64(oracle._bits(case.q)[b], 0)
+        for h in range(8):
+            np.testing.assert_array_equal(q_rot[b, h], oracle.rope_neox(qd[h], pos, 128))
+    # attention after the append covers rows [leftpad, c] of the indexed cache row
+    out, lse = oracle.decode(after, q_rot, c + 1, 1 / math.sqrt(128))
+    for b in range(3):
+        r = int(idx[b])
+        kr = torch.from_numpy(oracle.to_f64(kc[r, int(lp[b]):int(c[b]) + 1], 0))
+        vr = torch.from_numpy(oracle.to_f64(vc[r, int(lp[b]):int(c[b]) + 1], 0))
+        ro, rl = _sdpa_rows(torch.from_numpy(q_rot[b]), kr, vr, 1 / math.sqrt(128))
+        np.testing.assert_allclose(out[b], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=0, atol=1e-12)

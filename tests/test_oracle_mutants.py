@@ -37,6 +37,10 @@ MUTANTS = {
     "prefix_pages_ignored": ("} else if (kv->prefix_pages && j < kv->prefix_len) {",
                              "} else if (kv->prefix_pages && j < 0) {"),
     "append_v_not_written": ("for (int d = 0; d < D; ++d) v_cache[off + d] = vn[d];", ""),
+    "batch_idx_ignored": ("outer = kv->batch_idx ? kv->batch_idx[b] : b;", "outer = b;"),
+    "leftpad_ignored": ("int lo = first_row(kv, b);", "int lo = 0;"),
+    "partials_ignore_leftpad": ("if (lo < first_row(kv, b)) lo = first_row(kv, b);", ""),
+    "rope_at_row_not_position": ("int pos = c - first_row(kv, b);", "int pos = c;"),
 }
 
 
