@@ -40,6 +40,7 @@ class FdecKV(ctypes.Structure):
         ("s_outer", ctypes.c_int64), ("s_token", ctypes.c_int64), ("s_head", ctypes.c_int64),
         ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int),
         ("k_descale", ctypes.c_void_p), ("v_descale", ctypes.c_void_p),
+        ("cache_batch_idx", ctypes.c_void_p), ("cache_leftpad", ctypes.c_void_p),
     ]
 
 
@@ -127,10 +128,13 @@ def _check_q(q: torch.Tensor, k: torch.Tensor) -> None:
 
 
 def make_kv(k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor] = None,
-            k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None) -> FdecKV:
-    """Describe a cache: contiguous [B, cap, Hkv, D] or paged [P, page_size, Hkv, D] (+ page_table).
+            k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None,
+            cache_batch_idx: Optional[torch.Tensor] = None,
+            cache_leftpad: Optional[torch.Tensor] = None) -> FdecKV:
+    """Describe a cache: contiguous [rows, cap, Hkv, D] or paged [P, page_size, Hkv, D] (+ page_table).
 
     Float8 caches take k_descale / v_descale: contiguous [B, Hkv] float32 device tensors (or None = 1).
+    cache_batch_idx (contiguous caches) / cache_leftpad: contiguous [B] int32 device tensors or None.
     """
     if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype or k.dim() != 4:
         raise FdecError(FDEC_ERR_INVALID_ARG, "k and v must be 4-D with equal shapes, strides and dtypes")
@@ -155,6 +159,11 @@ def make_kv(k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor]
         if d is not None:
             if d.dtype != torch.float32 or not d.is_contiguous():
                 raise FdecError(FDEC_ERR_INVALID_ARG, f"{name} must be a contiguous float32 tensor")
+            setattr(kv, name, d.data_ptr())
+    for name, d in (("cache_batch_idx", cache_batch_idx), ("cache_leftpad", cache_leftpad)):
+        if d is not None:
+            if d.dtype != torch.int32 or not d.is_contiguous() or d.dim() != 1:
+                raise FdecError(FDEC_ERR_INVALID_ARG, f"{name} must be a contiguous 1-D int32 tensor")
             setattr(kv, name, d.data_ptr())
     return kv
 
@@ -220,11 +229,12 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Te
            append: Optional[FdecAppend] = None, fused: bool = False, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
            return_lse: bool = True, k_descale: Optional[torch.Tensor] = None,
-           v_descale: Optional[torch.Tensor] = None):
+           v_descale: Optional[torch.Tensor] = None, cache_batch_idx: Optional[torch.Tensor] = None,
+           cache_leftpad: Optional[torch.Tensor] = None):
     """fdec_decode: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32 or None)."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table, k_descale, v_descale)
+    kv = make_kv(k, v, page_table, k_descale, v_descale, cache_batch_idx, cache_leftpad)
     _check_q(q, k)
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
@@ -251,11 +261,12 @@ def decode_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens:
                     page_table: Optional[torch.Tensor] = None, num_blocks: int = 0, softmax_scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     workspace: Optional[Workspace] = None, return_lse: bool = True,
-                    k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None):
+                    k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None,
+                    cache_batch_idx: Optional[torch.Tensor] = None, cache_leftpad: Optional[torch.Tensor] = None):
     """fdec_decode_balanced: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32 or None)."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table, k_descale, v_descale)
+    kv = make_kv(k, v, page_table, k_descale, v_descale, cache_batch_idx, cache_leftpad)
     _check_q(q, k)
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
@@ -273,11 +284,12 @@ def decode_partials(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens:
                     num_splits: int, page_table: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                     append: Optional[FdecAppend] = None, part_o: Optional[torch.Tensor] = None,
                     part_m: Optional[torch.Tensor] = None, part_d: Optional[torch.Tensor] = None,
-                    k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None):
+                    k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None,
+                    cache_batch_idx: Optional[torch.Tensor] = None, cache_leftpad: Optional[torch.Tensor] = None):
     """fdec_decode_partials: returns (part_o [B,Hq,S,D], part_m [B,Hq,S], part_d [B,Hq,S]) fp32."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table, k_descale, v_descale)
+    kv = make_kv(k, v, page_table, k_descale, v_descale, cache_batch_idx, cache_leftpad)
     _check_q(q, k)
     S = num_splits
     if part_o is None:
@@ -342,11 +354,11 @@ def cascade_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table
                    prefix_pages: torch.Tensor, prefix_len: int, suffix_lens: torch.Tensor,
                    splits_prefix: int = 0, splits_suffix: int = 0, softmax_scale: float = 0.0,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   workspace: Optional[Workspace] = None):
-    """fdec_cascade_decode: shared prefix + per-request suffix, merged exactly."""
+                   workspace: Optional[Workspace] = None, cache_leftpad: Optional[torch.Tensor] = None):
+    """fdec_cascade_decode: shared prefix + per-request suffix, merged exactly (no left padding)."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table)
+    kv = make_kv(k, v, page_table, cache_leftpad=cache_leftpad)
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None:

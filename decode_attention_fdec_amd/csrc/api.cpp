@@ -83,6 +83,9 @@ int validate_common(const char *fn, const void *q, int B, int Hq, const fdec_kv 
     if (kv->page_size == 0) {
         if (kv->capacity < 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: contiguous cache needs capacity >= 1", fn);
     } else {
+        if (kv->cache_batch_idx)
+            return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: cache_batch_idx is for contiguous caches (a paged cache "
+                             "maps requests through its page table)", fn);
         if (!kv->page_table || kv->max_pages_per_seq < 1)
             return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: paged cache needs page_table and max_pages_per_seq >= 1", fn);
         const int64_t cap = (int64_t)kv->max_pages_per_seq * kv->page_size;
@@ -148,6 +151,8 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     p.page_size = kv->page_size;
     p.page_shift = page_shift_of(kv->page_size);
     p.seq_lens = seq_lens;
+    p.batch_idx = kv->cache_batch_idx;
+    p.leftpad = kv->cache_leftpad;
     if (kv->dtype == FDEC_FP8_E4M3) {
         p.kv_fp8 = 1;
         p.k_descale = kv->k_descale;
@@ -492,6 +497,8 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     if (kv->dtype == FDEC_FP8_E4M3)
         return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: float8 caches are not built for the cascade path", fn);
     if (kv->page_size == 0) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: the cascade path needs a paged cache", fn);
+    if (kv->cache_leftpad)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: cache_leftpad is not supported with a shared prefix", fn);
     if (kv->head_dim != 128)
         return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: head_dim %d not built for the cascade path (128)", fn,
                          kv->head_dim);

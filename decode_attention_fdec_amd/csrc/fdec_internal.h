@@ -55,6 +55,8 @@ struct MapParams {
     // balanced split: states [Hq, nslots] and per-request (first slot, count)
     int *seg_meta;
     int nslots;
+    // [B] int32 or nullptr: cache row of request b (contiguous caches), first valid row
+    const int32_t *batch_idx, *leftpad;
 };
 
 // Whether the matrix-core map kernel can take these parameters (mfma aside).

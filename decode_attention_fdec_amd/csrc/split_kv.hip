@@ -66,7 +66,11 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
 
     const int c_app = p.seq_lens[b];
     const int L = (MODE == kPlain) ? c_app : c_app + 1;
-    const int t_begin = split * p.chunk;
+    const int lp = p.leftpad ? p.leftpad[b] : 0;            // first valid row (left padding)
+    const int64_t crow = p.batch_idx ? p.batch_idx[b] : b;  // contiguous caches: the request's cache row
+    // split boundaries: multiples of 16 rows from the 16-row tile holding the
+    // first valid row (tiles of a paged cache then stay on one page)
+    const int t_begin = (lp & ~15) + split * p.chunk;
     const int t_end = min(t_begin + p.chunk, L);
 
     // Element offset of logical token t (KV head g), page table read for paged caches.
@@ -77,7 +81,7 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
             int64_t page = p.page_table[(int64_t)b * p.max_pages + pidx];
             return page * p.s_outer + (int64_t)slot * p.s_token + (int64_t)g * p.s_head;
         } else {
-            return (int64_t)b * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head;
+            return crow * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head;
         }
     };
 
@@ -97,8 +101,9 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
             for (int i = lane; i < D; i += 64) ks[i] = E::lo((uint32_t)ksrc[i]);
         __builtin_amdgcn_wave_barrier();
         const int half = p.rotary_dim >> 1;
-        const float *cs = p.rope_cos + (int64_t)c_app * half;
-        const float *sn = p.rope_sin + (int64_t)c_app * half;
+        // the new row's position among the valid rows
+        const float *cs = p.rope_cos + (int64_t)(c_app - lp) * half;
+        const float *sn = p.rope_sin + (int64_t)(c_app - lp) * half;
         const int nvec = owner ? G + 1 : G;
         for (int i = lane; i < nvec * half; i += 64) {
             int h = i / half, j = i - h * half;
@@ -177,8 +182,12 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
         for (int e = 0; e < NE; ++e) acc[h][e] = 0.0f;
     }
 
-    const int ntok = t_end - t_begin;
-    const int ntiles = ntok > 0 ? (ntok + TT - 1) / TT : 0;
+    // tokens [t_lo, t_end) in tiles of TT rows from t_first; the first tile's
+    // rows below t_lo are left padding (read as row t_lo, masked)
+    const int t_lo = max(t_begin, lp);
+    const int t_first = t_lo & ~(TT - 1);
+    const int nskip0 = t_lo - t_first;
+    const int ntiles = t_end > t_lo ? (t_end - t_first + TT - 1) / TT : 0;
     const char *kbase = p.k;
     const char *vbase = p.v;
     const uint32_t tok_bytes = (uint32_t)(p.s_token * 2);
@@ -187,18 +196,21 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
         uint4 k[NR][NCH];
         uint4 v[NR][NCH];
     };
-    auto tile_t0 = [&](int i) { return t_begin + i * TT; };
+    auto tile_t0 = [&](int i) { return t_first + i * TT; };
 
     // Per-lane byte offsets of this lane's rows within a tile: loop-invariant,
     // except in the split's last tile, whose rows past t_end clamp to its last
-    // valid row (their scores are masked later).
-    const int last_t0 = t_begin + (ntiles - 1) * TT;
+    // valid row, and a first tile with left padding, whose rows below t_lo
+    // clamp to its first valid row (their scores are masked later).
+    const int last_t0 = t_first + (ntiles - 1) * TT;
     const int nvalid_last = t_end - last_t0;
-    uint32_t off_full[NR], off_last[NR];
+    const int nhi_first = (ntiles == 1 ? nvalid_last : TT) - 1;
+    uint32_t off_full[NR], off_last[NR], off_first[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         off_full[j] = (uint32_t)(8 * j + ra) * tok_bytes + (uint32_t)cb * 16u;
         off_last[j] = (uint32_t)min(8 * j + ra, nvalid_last - 1) * tok_bytes + (uint32_t)cb * 16u;
+        off_first[j] = (uint32_t)min(max(8 * j + ra, nskip0), nhi_first) * tok_bytes + (uint32_t)cb * 16u;
     }
 
     // Issue the loads of the tile starting at token t0.
@@ -207,9 +219,10 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
         const char *kb = kbase + base * 2;
         const char *vb = vbase + base * 2;
         const bool last = (t0 == last_t0);
+        const bool first = (t0 == t_first) && nskip0 > 0;
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            const uint32_t off = last ? off_last[j] : off_full[j];
+            const uint32_t off = first ? off_first[j] : last ? off_last[j] : off_full[j];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 T.k[j][c] = *reinterpret_cast<const uint4 *>(kb + off + c * 128);
@@ -220,6 +233,7 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
 
     auto compute = [&](const Tile &T, int t0) {
         const int nvalid = t_end - t0;
+        const int nskip = (t0 == t_first) ? nskip0 : 0;
         float sc[NR][G];
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
@@ -240,12 +254,12 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
                 sc[j][h] = sum8(s) * p.scale_log2;
             }
         }
-        if (nvalid < TT) {  // only a split's last tile is partial (wave-uniform branch)
+        if (nvalid < TT || nskip > 0) {  // a split's last tile, a padded first tile (wave-uniform branch)
 #pragma unroll
             for (int j = 0; j < NR; ++j)
 #pragma unroll
                 for (int h = 0; h < G; ++h)
-                    if (8 * j + ra >= nvalid) sc[j][h] = kNegInf;
+                    if (8 * j + ra >= nvalid || 8 * j + ra < nskip) sc[j][h] = kNegInf;
         }
         float mx[G];
         bool move = false;

@@ -170,16 +170,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
 // swz = (r >> 1) & 7 (the 16 rows of a quarter-wave S^T read cover all 64
 // banks), for V swz = 2 ((r >> 1) & 3) (the 8 rows x 2 pieces of a half-wave
 // transpose read take 16 distinct (row parity, slot) pairs: all 64 banks).
-// kb / vb address the tile's first row; rows past nrows repeat row nrows - 1.
+// kb / vb address the tile's first row; rows below nskip (left padding) and
+// past nrows (the end) repeat rows nskip and nrows - 1, valid rows whose scores
+// are masked.
 template <int KF>
-__device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint32_t kl, uint32_t vl, int nrows,
-                                           uint32_t stok, int lane) {
+__device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint32_t kl, uint32_t vl, int nskip,
+                                           int nrows, uint32_t stok, int lane) {
     if constexpr (KF == 0) {
         const int srow = lane >> 4, sslot = lane & 15;
 #pragma unroll
         for (int i = 0; i < kMT / 4; ++i) {
             const int r = 4 * i + srow;
-            const uint32_t row = (uint32_t)min(r, nrows - 1) * stok;
+            const uint32_t row = (uint32_t)min(max(r, nskip), nrows - 1) * stok;
             dma16(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
             dma16(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
         }
@@ -188,18 +190,19 @@ __device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint3
 #pragma unroll
         for (int i = 0; i < kMT / 8; ++i) {
             const int r = 8 * i + srow;
-            const uint32_t row = (uint32_t)min(r, nrows - 1) * stok;
+            const uint32_t row = (uint32_t)min(max(r, nskip), nrows - 1) * stok;
             dma16(kb, row + 16u * (uint32_t)(sslot ^ ((r >> 1) & 7)), kl + 1024u * i);
             dma16(vb, row + 16u * (uint32_t)(sslot ^ (2 * ((r >> 1) & 3))), vl + 1024u * i);
         }
     }
 }
 
-// Byte offset of token t of request b, KV head g (uniform). A tile of a paged
-// cache lies on one page (page_size and tile starts are multiples of 16); the
-// page id comes from a scalar load.
+// Byte offset of token t of request b, KV head g (uniform); crow is the
+// request's row of a contiguous cache. A tile of a paged cache lies on one page
+// (page_size and tile starts are multiples of 16); the page id comes from a
+// scalar load.
 template <bool PAGED, int KF>
-__device__ __forceinline__ int64_t token_offset(const MapParams &p, int b, int g, int t) {
+__device__ __forceinline__ int64_t token_offset(const MapParams &p, int b, int64_t crow, int g, int t) {
     constexpr int ES = KvFmt<KF>::kElem;
     if constexpr (PAGED) {
         typedef const __attribute__((address_space(4))) int32_t *cpage_t;
@@ -208,8 +211,19 @@ __device__ __forceinline__ int64_t token_offset(const MapParams &p, int b, int g
         const int64_t page = ptab[pidx];
         return (page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head) * ES;
     } else {
-        return ((int64_t)b * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head) * ES;
+        return (crow * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head) * ES;
     }
+}
+
+// Request b's first valid row (left padding) and its row of a contiguous cache,
+// by scalar loads.
+__device__ __forceinline__ int first_row(const MapParams &p, int b) {
+    typedef const __attribute__((address_space(4))) int32_t *ci_t;
+    return p.leftpad ? ((ci_t)p.leftpad)[b] : 0;
+}
+__device__ __forceinline__ int64_t cache_row(const MapParams &p, int b) {
+    typedef const __attribute__((address_space(4))) int32_t *ci_t;
+    return p.batch_idx ? ((ci_t)p.batch_idx)[b] : b;
 }
 
 // The (request b, KV head g) descale of a float8 cache (1 without one), by a
@@ -265,10 +279,11 @@ struct MfmaSoftmax {
     }
 };
 
-// One tile: S^T = K Q^T, online softmax, O += P V. nvalid (>= 1) tokens of the
-// tile count; the rest are masked. kl / vl: the K and V tiles in LDS.
+// One tile: S^T = K Q^T, online softmax, O += P V. Tokens [nskip, nvalid) of
+// the tile count (nskip < nvalid); the rest are masked. kl / vl: the K and V
+// tiles in LDS.
 template <int DT, int KF>
-__device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 qb[8], int nvalid,
+__device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 qb[8], int nskip, int nvalid,
                                           float scale_log2, int lane, MfmaSoftmax &st) {
     using E = Elem<DT>;
     const int dq = lane >> 4;
@@ -324,7 +339,7 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
     for (int r = 0; r < 4; ++r) {
         const float x = sum_quarters(s[r] + s1[r]);
         const int tok = 4 * ((lane >> 2) & 3) + r;
-        sv[r] = (tok < nvalid && lane < 16) ? x * scale_log2 : kNegInf;
+        sv[r] = (tok >= nskip && tok < nvalid && lane < 16) ? x * scale_log2 : kNegInf;
         mx = fmax_nc(mx, sv[r]);
     }
     st.t = fmax_nc(st.t, mx);
@@ -411,23 +426,27 @@ __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, flo
     }
 }
 
-// One wave's pass over tokens [t_begin, t_end) of request b for KV head g
-// (its four query heads), state to po0 / pm0 / pd0 (+ i hs per head). wl /
-// qslot are the wave's LDS: its ring (Ring<KF>) and 1 KB of Q.
+// One wave's pass over tokens [t_lo, t_end) of request b for KV head g (its
+// four query heads), in 16-token tiles from t_begin (a multiple of 16, <= t_lo:
+// tiles of a paged cache then stay on one page), state to po0 / pm0 / pd0
+// (+ i hs per head). wl / qslot are the wave's LDS: its ring (Ring<KF>) and 1 KB
+// of Q.
 template <int DT, bool PAGED, int KF>
 __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, uint8_t *qslot,
-                                             int b, int g, int lane, int t_begin, int t_end, float *po0, float *pm0,
-                                             float *pd0, int64_t hs) {
-    const int ntok = t_end - t_begin;
-    const int ntiles = ntok > 0 ? (ntok + kMT - 1) / kMT : 0;
+                                             int b, int g, int lane, int t_begin, int t_lo, int t_end, float *po0,
+                                             float *pm0, float *pd0, int64_t hs) {
+    const int ntiles = t_end > t_lo ? (t_end - t_begin + kMT - 1) / kMT : 0;
+    const int nskip0 = t_lo - t_begin;  // left-padding rows of the first tile
     const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
     constexpr int NS = Ring<KF>::kSlots;
     auto stage = [&](int tile, int64_t off) {
         uint32_t kl, vl;
         slot_dma_addrs<KF>(wl, tile % NS, kl, vl);
-        stage_tile<KF>(p.k + off, p.v + off, kl, vl, t_end - (t_begin + tile * kMT), stok, lane);
+        stage_tile<KF>(p.k + off, p.v + off, kl, vl, tile == 0 ? nskip0 : 0, t_end - (t_begin + tile * kMT), stok,
+                       lane);
     };
-    auto tile_offset = [&](int tile) { return token_offset<PAGED, KF>(p, b, g, t_begin + tile * kMT); };
+    const int64_t crow = PAGED ? 0 : cache_row(p, b);
+    auto tile_offset = [&](int tile) { return token_offset<PAGED, KF>(p, b, crow, g, t_begin + tile * kMT); };
     const float kd = KF ? kv_descale(p.k_descale, p, b, g) : 1.0f;
     const float vd = KF ? kv_descale(p.v_descale, p, b, g) : 1.0f;
 
@@ -451,8 +470,8 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, ui
         // this tile's loads have landed once only the later tiles' remain
         wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, ntiles - 1 - tile));
         const int slot = tile % NS;
-        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, t_end - (t_begin + tile * kMT),
-                          p.scale_log2 * kd, lane, st);
+        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, tile == 0 ? nskip0 : 0,
+                          t_end - (t_begin + tile * kMT), p.scale_log2 * kd, lane, st);
     }
     write_state(st, lane, po0, pm0, pd0, hs, vd);
 }
@@ -470,11 +489,13 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     const int g = blockIdx.z * p.heads_per_block + wv;
     const int hq0 = g * G;
     const int L = p.seq_lens[b];
-    const int t_begin = split * p.chunk;
+    // splits start at the 16-row tile holding the first valid row
+    const int lp = first_row(p, b);
+    const int t_begin = (lp & ~(kMT - 1)) + split * p.chunk;
     const int t_end = min(t_begin + p.chunk, L);
     const int64_t st0 = ((int64_t)b * p.Hq + hq0) * p.s_total + p.s_offset + split;
-    mfma_segment<DT, PAGED, KF>(p, lds[wv], qlds[wv], b, g, lane, t_begin, t_end, p.po + st0 * D, p.pm + st0,
-                                p.pd + st0, p.s_total);
+    mfma_segment<DT, PAGED, KF>(p, lds[wv], qlds[wv], b, g, lane, t_begin, max(t_begin, lp), t_end, p.po + st0 * D,
+                                p.pm + st0, p.pd + st0, p.s_total);
 
     if (p.counters == nullptr) return;
 
@@ -541,13 +562,19 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
 
     // ---- the block's tile range and its first request
-    const bool one_pass = p.B <= 64;  // lengths stay in registers between the passes
-    const int L0 = lane < p.B ? p.seq_lens[lane] : 0;
+    const bool one_pass = p.B <= 64;  // valid-row counts stay in registers between the passes
+    // rows [leftpad, seq_len) of request j, counted from the 16-row tile holding
+    // the first (0 when there are none)
+    auto valid_rows = [&](int j) -> int {
+        if (j >= p.B) return 0;
+        const int L = p.seq_lens[j], lp = p.leftpad ? p.leftpad[j] : 0;
+        return L > lp ? L - (lp & ~(kMT - 1)) : 0;
+    };
+    const int E0 = valid_rows(lane);
     int NT = 0;  // tiles of all requests
     for (int c = 0; c < p.B; c += 64) {
-        const int j = c + lane;
-        const int L = one_pass ? L0 : (j < p.B ? p.seq_lens[j] : 0);
-        NT += wave_sum_int((L + kMT - 1) / kMT);
+        const int E = one_pass ? E0 : valid_rows(c + lane);
+        NT += wave_sum_int((E + kMT - 1) / kMT);
     }
     const int NBe = min(NB, NT);  // working blocks
     // block holding tile x (x < NT), the last working block past the end
@@ -563,8 +590,8 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     int carry = 0;                // tiles of the requests before this group of 64
     for (int c = 0; c < p.B; c += 64) {
         const int j = c + lane;
-        const int L = one_pass ? L0 : (j < p.B ? p.seq_lens[j] : 0);
-        const int T = (L + kMT - 1) / kMT;
+        const int E = one_pass ? E0 : valid_rows(j);
+        const int T = (E + kMT - 1) / kMT;
         const int incl = wave_incl_scan(T, lane);
         const int P = carry + incl - T;  // first tile of request j
         if (meta_writer && j < p.B) {
@@ -590,7 +617,8 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
 
     // ---- stream tiles [start, end): a cursor per side walks the requests
     struct Cursor {
-        int b, P, T, L, seg;  // request, its first tile, tiles, tokens; pieces begun so far
+        int b, P, T, L, lp, seg;  // request, its first tile, tiles, end row, first row; pieces begun so far
+        int64_t crow;             // its contiguous-cache row
     };
     // lengths by scalar loads: a vector load here would make the compiler wait
     // for every outstanding load, DMA ones included
@@ -601,23 +629,26 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
             c.P += c.T;
             c.b += 1;
             c.L = slens[c.b];
-            c.T = (c.L + kMT - 1) / kMT;
+            c.lp = first_row(p, c.b);
+            c.T = c.L > c.lp ? (c.L - (c.lp & ~(kMT - 1)) + kMT - 1) / kMT : 0;
         } while (c.T == 0);
+        c.crow = PAGED ? 0 : cache_row(p, c.b);
         c.seg += 1;
     };
-    const int Lb0 = slens[b0];
-    Cursor prod{b0, P0, T0, Lb0, 0}, cons{b0, P0, T0, Lb0, 0};
+    const int Lb0 = slens[b0], lp0 = first_row(p, b0);
+    const int64_t crow0 = PAGED ? 0 : cache_row(p, b0);
+    Cursor prod{b0, P0, T0, Lb0, lp0, 0, crow0}, cons{b0, P0, T0, Lb0, lp0, 0, crow0};
     uint8_t *wl = lds[wv];
     auto produce = [&](int x) {  // stage tile x (and Q when it starts a new piece)
         if (x >= prod.P + prod.T) {
             advance(prod);
             stage_q(p, prod.b, g, qlds[wv][prod.seg % NS], lane);
         }
-        const int t0 = (x - prod.P) * kMT;
-        const int64_t off = token_offset<PAGED, KF>(p, prod.b, g, t0);
+        const int t0 = (prod.lp & ~(kMT - 1)) + (x - prod.P) * kMT;
+        const int64_t off = token_offset<PAGED, KF>(p, prod.b, prod.crow, g, t0);
         uint32_t kl, vl;
         slot_dma_addrs<KF>(wl, x % NS, kl, vl);
-        stage_tile<KF>(p.k + off, p.v + off, kl, vl, prod.L - t0, stok, lane);
+        stage_tile<KF>(p.k + off, p.v + off, kl, vl, max(prod.lp - t0, 0), prod.L - t0, stok, lane);
     };
 
     stage_q(p, b0, g, qlds[wv][0], lane);
@@ -651,8 +682,9 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
             }
         }
         const int slot = x % NS;
-        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, cons.L - (x - cons.P) * kMT,
-                          p.scale_log2 * kd, lane, st);
+        const int t0 = (cons.lp & ~(kMT - 1)) + (x - cons.P) * kMT;
+        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, max(cons.lp - t0, 0),
+                          cons.L - t0, p.scale_log2 * kd, lane, st);
     }
     const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
     write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);

@@ -109,13 +109,28 @@ typedef struct fdec_kv {
     int max_pages_per_seq;
     const float *k_descale;           /* float8 only: device [B, Hkv] fp32, or NULL (1) */
     const float *v_descale;           /* float8 only: device [B, Hkv] fp32, or NULL (1) */
+    /* contiguous caches only: device [B] int32, request b reads (and appends
+     * to) cache row cache_batch_idx[b] ([cookbook] §5.2); NULL = row b. The
+     * cache then has any number of rows >= max(cache_batch_idx) + 1. */
+    const int32_t *cache_batch_idx;
+    /* device [B] int32 or NULL (0): request b's valid rows start at
+     * cache_leftpad[b] ([cookbook] §5.3); it attends to rows
+     * [cache_leftpad[b], L_b) with L_b counted from row 0 (seq_lens[b], +1
+     * with an append), and an appended row is rotated at its position among
+     * the valid rows, seq_lens[b] - cache_leftpad[b]. Requires
+     * 0 <= cache_leftpad[b] <= seq_lens[b] (device data, not checked). Split
+     * boundaries then count from the 16-row tile holding row cache_leftpad[b]
+     * (cache_leftpad[b] rounded down to a multiple of 16), whose rows above the
+     * padding are masked. Not in fdec_cascade_decode. */
+    const int32_t *cache_leftpad;
 } fdec_kv;
 
 /*
  * Optional KV append with fused GPT-NeoX rotary ([cookbook] §3.3-3.4). For each
- * request b with c = seq_lens[b]: k row c of every KV head <- rope(k_new[b,g], c)
- * rounded once (nearest-even) to the cache dtype; v row c <- v_new[b,g] bit copy;
- * the query is rotated by the same position in fp32 before attention. Only q and
+ * request b with c = seq_lens[b]: k row c of every KV head <- rope(k_new[b,g], p)
+ * with p = c - cache_leftpad[b] (p = c without left padding), rounded once
+ * (nearest-even) to the cache dtype; v row c <- v_new[b,g] bit copy; the query
+ * is rotated by the same position in fp32 before attention. Only q and
  * k are rotated, never v. rotary_dim == 0 appends without rotation. Pairs are
  * (i, i + rotary_dim/2) for i < rotary_dim/2; dims >= rotary_dim are untouched.
  */

@@ -66,6 +66,9 @@ class Case:
     # float8 caches: per (request, KV head) factors, [B, Hkv] float32
     k_descale: Optional[torch.Tensor] = None
     v_descale: Optional[torch.Tensor] = None
+    # [B] int32: request b's row of a contiguous cache; its first valid row
+    cache_batch_idx: Optional[torch.Tensor] = None
+    cache_leftpad: Optional[torch.Tensor] = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -79,14 +82,18 @@ class Case:
         L = self.seq_lens.to(torch.int64)
         if self.k_new is not None:
             L = L + 1
+        if self.cache_leftpad is not None:
+            L = L - self.cache_leftpad.to(torch.int64)
         return L + self.prefix_len
 
     def kv_bytes(self) -> int:
         """K+V bytes of the attended rows, each KV head read once (prefix counted once)."""
         e = 1 if self.dtype == FP8 else 2
         per_tok = 2 * self.Hkv * self.D * e
-        suffix = int((self.seq_lens.to(torch.int64) + (1 if self.k_new is not None else 0)).sum())
-        return per_tok * (suffix + self.prefix_len)
+        L = self.seq_lens.to(torch.int64) + (1 if self.k_new is not None else 0)
+        if self.cache_leftpad is not None:
+            L = L - self.cache_leftpad.to(torch.int64)
+        return per_tok * (int(L.sum()) + self.prefix_len)
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -150,6 +157,67 @@ def contiguous_case(seed: int, B: int, Hq: int, Hkv: int, D: int, lens, cap: int
         k = _quantize(k, kd[:, None, :, None])
         v = _quantize(v, vd[:, None, :, None])
     return Case(name, dtype, B, Hq, Hkv, D, q, k, v, lens, num_splits=num_splits, k_descale=kd, v_descale=vd)
+
+
+def indexed_case(seed: int, B: int, Hq: int, Hkv: int, D: int, lens, leftpad, cap: int, dtype=BF16,
+                 cache_rows: Optional[int] = None, pad: str = "nan", name: str = "indexed") -> Case:
+    """Contiguous cache with left padding and, when cache_rows is given, a cache_batch_idx.
+
+    Request b reads rows [leftpad[b], lens[b]) of cache row batch_idx[b] (b without
+    cache_rows); batch_idx is a seeded draw of distinct rows. Every other row of
+    the cache (padding, past the length, rows no request names) is filled by
+    `pad`. Float8 caches: descales per (request, KV head) as in contiguous_case,
+    applied to the request's cache row (1/32 for unnamed rows).
+    """
+    g = _gen(seed)
+    lens = torch.as_tensor(lens, dtype=torch.int32).reshape(B)
+    lp = torch.as_tensor(leftpad, dtype=torch.int32).reshape(B)
+    rows = B if cache_rows is None else cache_rows
+    idx = None
+    if cache_rows is not None:
+        idx = torch.randperm(rows, generator=g)[:B].to(torch.int32)
+    q = _randn(g, (B, Hq, D), _q_dtype(dtype))
+    k = _randn(g, (rows, cap, Hkv, D), _kv_draw_dtype(dtype))
+    v = _randn(g, (rows, cap, Hkv, D), _kv_draw_dtype(dtype))
+    mask = torch.ones(rows, cap, dtype=torch.bool)
+    for b in range(B):
+        r = b if idx is None else int(idx[b])
+        mask[r, int(lp[b]):int(lens[b])] = False
+    _fill_pad(k, mask, pad, g)
+    _fill_pad(v, mask, pad, g)
+    kd = vd = None
+    if dtype == FP8:
+        kd, vd = _descales(g, B, Hkv)
+        fk = torch.full((rows, Hkv), 1.0 / 32)
+        fv = torch.full((rows, Hkv), 1.0 / 32)
+        for b in range(B):
+            r = b if idx is None else int(idx[b])
+            fk[r], fv[r] = kd[b], vd[b]
+        k = _quantize(k, fk[:, None, :, None])
+        v = _quantize(v, fv[:, None, :, None])
+    return Case(name, dtype, B, Hq, Hkv, D, q, k, v, lens, k_descale=kd, v_descale=vd, cache_batch_idx=idx,
+                cache_leftpad=lp)
+
+
+def pad_left(case: Case, leftpad, pad: str = "nan") -> Case:
+    """Mark rows [0, leftpad[b]) of each request as left padding (filled by `pad`) and record leftpad."""
+    lp = torch.as_tensor(leftpad, dtype=torch.int32).reshape(case.B)
+    val = float("nan") if pad == "nan" else 0.0
+    for b in range(case.B):
+        for j in range(int(lp[b])):
+            if case.page_size:
+                p, s = int(case.page_table[b, j // case.page_size]), j % case.page_size
+            else:
+                r = b if case.cache_batch_idx is None else int(case.cache_batch_idx[b])
+                p, s = r, j
+            if case.k.dtype == FP8:
+                case.k[p, s] = torch.full_like(case.k[p, s], val, dtype=torch.float32).to(FP8)
+                case.v[p, s] = torch.full_like(case.v[p, s], val, dtype=torch.float32).to(FP8)
+            else:
+                case.k[p, s] = val
+                case.v[p, s] = val
+    case.cache_leftpad = lp
+    return case
 
 
 def _page_lists(g, lens, ps, extra_pages):

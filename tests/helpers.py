@@ -19,7 +19,7 @@ LSE_RTOL = 1e-4
 def okv(case, k=None, v=None):
     return oracle.KV(case.k if k is None else k, case.v if v is None else v, oracle.dtype_code(case.k),
                      case.Hq, case.B, case.page_size, case.page_table, case.prefix_pages, case.prefix_len,
-                     case.k_descale, case.v_descale)
+                     case.k_descale, case.v_descale, case.cache_batch_idx, case.cache_leftpad)
 
 
 def oracle_decode(case, scale=None, nthreads=0):
@@ -48,7 +48,7 @@ def to_dev(case, device="cuda"):
     """Copy every tensor of a case to the device (returns a dict of device tensors)."""
     d = {}
     for name in ("q", "k", "v", "seq_lens", "page_table", "k_new", "v_new", "rope_cos", "rope_sin",
-                 "prefix_pages", "k_descale", "v_descale"):
+                 "prefix_pages", "k_descale", "v_descale", "cache_batch_idx", "cache_leftpad"):
         t = getattr(case, name)
         d[name] = None if t is None else t.to(device).contiguous()
     return d

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import decode_attention_fdec_amd as F
 
@@ -246,3 +247,29 @@ def test_fp8_validation(fdec):
                                    FAKE, 1 << 30, None) == F.FDEC_ERR_UNSUPPORTED
     # an unknown element type
     assert call_decode(kv_struct(dtype=3)) == F.FDEC_ERR_UNSUPPORTED
+
+
+def test_batch_idx_and_leftpad_validation(fdec):
+    lib = F.load_library()
+    # cache_batch_idx is for contiguous caches only
+    kvp = kv_struct(page_size=16, page_table=FAKE, max_pages_per_seq=64, capacity=0, cache_batch_idx=FAKE)
+    assert call_decode(kvp) == F.FDEC_ERR_INVALID_ARG
+    assert "cache_batch_idx" in last_error()
+    # no left padding with a shared prefix
+    kvc = kv_struct(page_size=64, page_table=FAKE, max_pages_per_seq=32, capacity=0, cache_leftpad=FAKE)
+    assert lib.fdec_cascade_decode(FAKE, 2, 32, ctypes.byref(kvc), FAKE, 64, FAKE, 2, 2, 0.0, FAKE, None,
+                                   FAKE, 1 << 30, None) == F.FDEC_ERR_UNSUPPORTED
+    assert "leftpad" in last_error()
+
+
+def test_binding_checks_index_tensors(fdec):
+    k = torch.zeros(2, 32, 2, 128, dtype=torch.float16)
+    for bad in (torch.zeros(2, dtype=torch.int64), torch.zeros(2, 2, dtype=torch.int32),
+                torch.zeros(4, dtype=torch.int32)[::2]):
+        with pytest.raises(F.FdecError):
+            F.make_kv(k, k, cache_batch_idx=bad)
+        with pytest.raises(F.FdecError):
+            F.make_kv(k, k, cache_leftpad=bad)
+    kv = F.make_kv(k, k, cache_batch_idx=torch.zeros(2, dtype=torch.int32),
+                   cache_leftpad=torch.zeros(2, dtype=torch.int32))
+    assert kv.cache_batch_idx and kv.cache_leftpad
