@@ -67,6 +67,8 @@ def _load():
             lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         lib.oracle_decode.argtypes = [ctypes.POINTER(_KV), P, P, ctypes.c_double, P, P, ctypes.c_int]
+        lib.oracle_decode_multi.argtypes = [ctypes.POINTER(_KV), P, P, ctypes.c_int, ctypes.c_double, P, P,
+                                            ctypes.c_int]
         lib.oracle_partials.argtypes = [ctypes.POINTER(_KV), P, P, ctypes.c_double, ctypes.c_int,
                                         P, P, P, P, ctypes.c_int]
         lib.oracle_merge.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -212,6 +214,23 @@ def decode(kv: KV, q, lens, scale: float, nthreads: int = 0):
     s = kv._struct()
     _load().oracle_decode(ctypes.byref(s), _ptr(q64), _ptr(lens), float(scale), _ptr(out),
                           _ptr(lse), int(nthreads))
+    return out, lse
+
+
+def decode_multi(kv: KV, q, lens, scale: float, nthreads: int = 0):
+    """q_len query tokens per request, causal: q [B, q_len, Hq, D] -> out [B, q_len, Hq, D], lse [B, Hq, q_len]."""
+    if isinstance(q, np.ndarray) and q.dtype == np.float64:
+        q64 = np.ascontiguousarray(q)
+    else:
+        q64 = to_f64(q, dtype_code(q) if not isinstance(q, np.ndarray) else kv.dtype)
+    lens = _i32(lens)
+    B, q_len, Hq, D = q64.shape
+    assert (B, Hq, D) == (kv.B, kv.Hq, kv.D) and lens.shape == (kv.B,)
+    out = np.empty((B, q_len, Hq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, q_len), dtype=np.float64)
+    s = kv._struct()
+    _load().oracle_decode_multi(ctypes.byref(s), _ptr(q64), _ptr(lens), int(q_len), float(scale), _ptr(out),
+                                _ptr(lse), int(nthreads))
     return out, lse
 
 

@@ -38,6 +38,11 @@
  *                    contiguous cache ([cookbook] §5.2).
  *   cache_leftpad    request b's valid rows start at leftpad[b]: it attends
  *                    to rows [leftpad[b], L_b) ([cookbook] §5.3).
+ *   oracle_decode_multi  q_len query tokens per request (speculative decode,
+ *                    [vllm-arch] spec-decode batches; softmax_lse of shape
+ *                    (batch, heads, seqlen_q), [cookbook] §3.5) under the causal
+ *                    mask the calls pass: token i is the request's row
+ *                    L_b - q_len + i and attends to rows [leftpad[b], L_b - q_len + i].
  *
  * Readings where the pages are silent (all listed in the design notes):
  *   - empty range: out = 0, lse = -inf; an empty split is (O~=0, m=-inf, d=0)
@@ -295,6 +300,41 @@ void oracle_decode(const oracle_kv *kv, const double *q, const int32_t *lens, do
             }
             for (int d = 0; d < D; ++d) o[d] /= dsum;
             lse[bh] = m + log(dsum);
+        }
+        free(sbuf);
+    }
+}
+
+/*
+ * Multi-token decode: q is [B, q_len, Hq, D] doubles; query token i of request
+ * b attends to rows [leftpad[b], L_b - q_len + i] (L_b = lens[b], counted from
+ * row 0). out [B, q_len, Hq, D]; lse [B, Hq, q_len]. A token with no rows gives
+ * out = 0, lse = -inf.
+ */
+void oracle_decode_multi(const oracle_kv *kv, const double *q, const int32_t *lens, int q_len,
+                         double scale, double *out, double *lse, int nthreads) {
+    int B = kv->B, Hq = kv->Hq, D = kv->D;
+    int mx = max_len(kv, lens);
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel num_threads(nt)
+    {
+        double *sbuf = (double *)malloc(sizeof(double) * (size_t)(mx > 0 ? mx : 1));
+#pragma omp for schedule(dynamic)
+        for (int bih = 0; bih < B * q_len * Hq; ++bih) {
+            int b = bih / (q_len * Hq), i = (bih / Hq) % q_len, h = bih % Hq;
+            int lo = first_row(kv, b);
+            int hi = lens[b] - q_len + i + 1; /* the token's own row is the last it sees */
+            double m, dsum;
+            double *o = out + (int64_t)bih * D;
+            double *l = lse + ((int64_t)b * Hq + h) * q_len + i;
+            attend_range(kv, q + (int64_t)bih * D, b, h, lo, hi, scale, sbuf, o, &m, &dsum);
+            if (hi <= lo) {
+                *l = -INFINITY;
+                continue;
+            }
+            for (int d = 0; d < D; ++d) o[d] /= dsum;
+            *l = m + log(dsum);
         }
         free(sbuf);
     }

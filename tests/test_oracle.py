@@ -606,3 +606,54 @@ def test_append_with_leftpad_and_batch_idx():
         ro, rl = _sdpa_rows(torch.from_numpy(q_rot[b]), kr, vr, 1 / math.sqrt(128))
         np.testing.assert_allclose(out[b], ro, rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse[b], rl, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- multi-token (speculative) decode
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_multi_token_decode_matches_sdpa_with_causal_mask(paged):
+    # token i of request b is row L_b - q_len + i and sees rows [leftpad, that row];
+    # request 2 is shorter than q_len, so its first token sees nothing
+    q_len, lens, pads = 3, [20, 5, 2], [0, 1, 0]
+    if paged:
+        case = paged_case(170, 3, 8, 2, 16, lens, 16, BF16, extra_pages=2, pad="nan")
+    else:
+        case = contiguous_case(170, 3, 8, 2, 16, lens, 20, BF16, pad="nan")
+    g = torch.Generator().manual_seed(171)
+    q = torch.randn(3, q_len, 8, 16, generator=g).to(BF16)
+    lp = torch.tensor(pads, dtype=torch.int32)
+    kv = oracle.KV(case.k, case.v, oracle.BF16, 8, 3, case.page_size, case.page_table, leftpad=lp)
+    out, lse = oracle.decode_multi(kv, q, case.seq_lens, 0.3)
+    assert out.shape == (3, q_len, 8, 16) and lse.shape == (3, 8, q_len)
+    for b in range(3):
+        L = lens[b]
+        if paged:
+            rows = [(int(case.page_table[b, j // 16]), j % 16) for j in range(L)]
+            kb = torch.stack([case.k[p, s] for p, s in rows]) if L else case.k[:0, 0]
+            vb = torch.stack([case.v[p, s] for p, s in rows]) if L else case.v[:0, 0]
+        else:
+            kb, vb = case.k[b, :L], case.v[b, :L]
+        kk = kb.to(torch.float64).permute(1, 0, 2)[None].contiguous()
+        vv = vb.to(torch.float64).permute(1, 0, 2)[None].contiguous()
+        qq = q[b].to(torch.float64).permute(1, 0, 2)[None].contiguous()  # [1, Hq, q_len, D]
+        j = torch.arange(L)
+        mask = torch.stack([(j >= pads[b]) & (j <= L - q_len + i) for i in range(q_len)])  # [q_len, L]
+        for i in range(q_len):
+            if not bool(mask[i].any()):
+                assert np.all(out[b, i] == 0) and np.all(lse[b, :, i] == -np.inf)
+                continue
+            kk_i = torch.nan_to_num(kk[:, :, mask[i]])  # only the rows token i sees
+            vv_i = vv[:, :, mask[i]]
+            ref = F.scaled_dot_product_attention(qq[:, :, i:i + 1], kk_i, vv_i, scale=0.3, enable_gqa=True)
+            np.testing.assert_allclose(out[b, i], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+            s = torch.einsum("hd,hld->hl", qq[0, :, i], kk_i[0].repeat_interleave(4, dim=0)) * 0.3
+            np.testing.assert_allclose(lse[b, :, i], torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_multi_token_with_one_token_is_single_query_decode():
+    case = paged_case(172, 3, 8, 2, 32, [40, 1, 17], 16, F16, extra_pages=1, pad="nan")
+    kv = okv(case)
+    out1, lse1 = oracle.decode(kv, case.q, case.seq_lens, 0.2)
+    outm, lsem = oracle.decode_multi(kv, case.q[:, None], case.seq_lens, 0.2)
+    np.testing.assert_array_equal(outm[:, 0], out1)
+    np.testing.assert_array_equal(lsem[:, :, 0], lse1)

@@ -41,6 +41,10 @@ MUTANTS = {
     "leftpad_ignored": ("int lo = first_row(kv, b);", "int lo = 0;"),
     "partials_ignore_leftpad": ("if (lo < first_row(kv, b)) lo = first_row(kv, b);", ""),
     "rope_at_row_not_position": ("int pos = c - first_row(kv, b);", "int pos = c;"),
+    "causal_excludes_own_row": ("int hi = lens[b] - q_len + i + 1;", "int hi = lens[b] - q_len + i;"),
+    "tokens_reversed": ("int hi = lens[b] - q_len + i + 1;", "int hi = lens[b] - i;"),
+    "multi_lse_token_major": ("double *l = lse + ((int64_t)b * Hq + h) * q_len + i;",
+                              "double *l = lse + ((int64_t)b * q_len + i) * Hq + h;"),
 }
 
 
