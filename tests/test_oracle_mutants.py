@@ -38,7 +38,9 @@ MUTANTS = {
                              "} else if (kv->prefix_pages && j < 0) {"),
     "append_v_not_written": ("for (int d = 0; d < D; ++d) v_cache[off + d] = vn[d];", ""),
     "batch_idx_ignored": ("outer = kv->batch_idx ? kv->batch_idx[b] : b;", "outer = b;"),
-    "leftpad_ignored": ("int lo = first_row(kv, b);", "int lo = 0;"),
+    "leftpad_ignored": ("int lo = first_row(kv, b);\n            double m, dsum;",
+                        "int lo = 0;\n            double m, dsum;"),
+    "multi_leftpad_ignored": ("int lo = first_row(kv, b);\n            int hi", "int lo = 0;\n            int hi"),
     "partials_ignore_leftpad": ("if (lo < first_row(kv, b)) lo = first_row(kv, b);", ""),
     "rope_at_row_not_position": ("int pos = c - first_row(kv, b);", "int pos = c;"),
     "causal_excludes_own_row": ("int hi = lens[b] - q_len + i + 1;", "int hi = lens[b] - q_len + i;"),
