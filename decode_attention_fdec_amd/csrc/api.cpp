@@ -153,6 +153,8 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     p.seq_lens = seq_lens;
     p.batch_idx = kv->cache_batch_idx;
     p.leftpad = kv->cache_leftpad;
+    p.q_len = 1;
+    p.q_groups = 1;
     if (kv->dtype == FDEC_FP8_E4M3) {
         p.kv_fp8 = 1;
         p.k_descale = kv->k_descale;
@@ -291,6 +293,49 @@ extern "C" int fdec_decode(const void *q, int B, int Hq, const fdec_kv *kv, cons
     if ((rc = check_hip(fdec::launch_map(p, S, st), "fdec_decode: map launch"))) return rc;
     return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st),
                      "fdec_decode: merge launch");
+}
+
+extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const fdec_kv *kv,
+                                 const int32_t *seq_lens, int num_splits, float softmax_scale, float *out,
+                                 float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    fdec_clear_error();
+    const char *fn = "fdec_decode_multi";
+    if (q_len < 1 || q_len > FDEC_MAX_QLEN)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: q_len %d outside [1, %d]", fn, q_len, FDEC_MAX_QLEN);
+    int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
+    if (rc) return rc;
+    int S = 0;
+    if ((rc = resolve_splits(fn, num_splits, B, Hq, kv, &S))) return rc;
+    if (B == 0) return FDEC_OK;
+    if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
+    if ((int64_t)B * q_len * Hq > INT32_MAX)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: B * q_len * Hq overflows int32", fn);
+    const WsLayout w = ws_layout(B * q_len, Hq, kv->num_kv_heads, kv->head_dim, S);
+    if (!workspace || workspace_bytes < w.total)
+        return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d splits, got %zu", fn,
+                         w.total, S, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+    fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, nullptr);
+    if (!p.mfma)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED,
+                         "%s: needs Hq = 4 Hkv, head_dim 128 and page_size a multiple of 16 (matrix-core kernel)", fn);
+    const int ql = fdec::mfma_tokens_per_wave(q_len);
+    p.q_len = q_len;
+    p.q_groups = (q_len + ql - 1) / ql;
+    if ((int64_t)B * p.q_groups > 65535)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: B * ceil(q_len / %d) exceeds the grid", fn, ql);
+    char *ws = static_cast<char *>(workspace);
+    p.pm = reinterpret_cast<float *>(ws + w.pm);
+    p.pd = reinterpret_cast<float *>(ws + w.pd);
+    p.po = reinterpret_cast<float *>(ws + w.po);
+    p.s_total = S;
+    p.s_offset = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = check_hip(fdec::launch_map(p, S, st), "fdec_decode_multi: map launch"))) return rc;
+    return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st, q_len),
+                     "fdec_decode_multi: merge launch");
 }
 
 extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,

@@ -57,6 +57,9 @@ struct MapParams {
     int nslots;
     // [B] int32 or nullptr: cache row of request b (contiguous caches), first valid row
     const int32_t *batch_idx, *leftpad;
+    // query tokens per request (q [B, q_len, Hq, D], causal) and groups of them along
+    // the grid (matrix-core kernel); 1 and 1 for a single query
+    int q_len, q_groups;
 };
 
 // Whether the matrix-core map kernel can take these parameters (mfma aside).
@@ -70,6 +73,7 @@ inline bool map_mfma_eligible(const MapParams &p) {
 // Runs the matrix-core kernel when p.mfma is set (heads_per_block <= 4).
 hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t stream);
 hipError_t launch_map_mfma_g4(const MapParams &p, int num_splits, hipStream_t stream);
+int mfma_tokens_per_wave(int q_len);
 // Balanced split over nblocks blocks per group of KV heads (matrix-core kernel).
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t stream);
 
@@ -94,7 +98,7 @@ hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t
 
 // One wave per (b, h): merges S states into out / lse.
 hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S,
-                        int head_dim, float *out, float *lse, hipStream_t stream);
+                        int head_dim, float *out, float *lse, hipStream_t stream, int q_len = 1);
 // Merge of balanced-split states: request b's states are slots
 // [meta[2b], meta[2b] + meta[2b+1]) of [Hq, nslots]; max_count bounds the counts.
 hipError_t launch_merge_segments(const float *po, const float *pm, const float *pd, const int *meta, int B, int Hq,

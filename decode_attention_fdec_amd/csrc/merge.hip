@@ -10,29 +10,39 @@
 
 namespace fdec {
 
+// LSE slot of state row `row`. Rows are (request, token, head) with Hq heads
+// and q tokens per request; the LSE is [request, head, token] (for q = 1 the
+// row itself).
+__device__ __forceinline__ int64_t lse_slot(int64_t row, int Hq, int q) {
+    if (q <= 1) return row;
+    const int64_t bi = row / Hq, h = row - bi * Hq, b = bi / q, i = bi - b * q;
+    return (b * Hq + h) * q + i;
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float *__restrict__ po,
                                                                   const float *__restrict__ pm,
                                                                   const float *__restrict__ pd, int BH,
                                                                   int S, float *__restrict__ out,
-                                                                  float *__restrict__ lse) {
+                                                                  float *__restrict__ lse, int Hq, int q) {
     const int lane = threadIdx.x & 63;
     const int64_t bh = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
     if (bh >= BH) return;
     merge_states_wave<D>(po + bh * S * D, pm + bh * S, pd + bh * S, S, out + bh * D,
-                         lse ? lse + bh : nullptr, lane);
+                         lse ? lse + lse_slot(bh, Hq, q) : nullptr, lane);
 }
 
 template <int D>
 __global__ __launch_bounds__(64 * (256 / kMergeGroup)) void merge_kernel_groups(
     const float *__restrict__ po, const float *__restrict__ pm, const float *__restrict__ pd, int S,
-    float *__restrict__ out, float *__restrict__ lse) {
+    float *__restrict__ out, float *__restrict__ lse, int Hq, int q) {
     __shared__ float gs[256 / kMergeGroup][D];
     const int lane = threadIdx.x & 63;
     const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's group
     const int64_t bh = blockIdx.x;
     const ContigStates<D> src{po + bh * S * D, pm + bh * S, pd + bh * S};
-    merge_states_block<D>(src, S, out + bh * D, lse ? lse + bh : nullptr, lane, k, blockDim.x >> 6, gs);
+    merge_states_block<D>(src, S, out + bh * D, lse ? lse + lse_slot(bh, Hq, q) : nullptr, lane, k,
+                          blockDim.x >> 6, gs);
 }
 
 // Balanced-split merge: one block per (b, h). The piece count is known only on
@@ -103,24 +113,28 @@ hipError_t launch_merge_cascade(const float *ppo, const float *ppm, const float 
 }
 
 hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S,
-                        int head_dim, float *out, float *lse, hipStream_t st) {
-    const int BH = B * Hq;
+                        int head_dim, float *out, float *lse, hipStream_t st, int q_len) {
+    const int BH = B * q_len * Hq;
     if (S > kMergeGroup) {
         const int K = (S + kMergeGroup - 1) / kMergeGroup;  // <= 8 for S <= 256
         if (K > 256 / kMergeGroup) return hipErrorInvalidValue;
         if (head_dim == 128)
-            hipLaunchKernelGGL(merge_kernel_groups<128>, dim3(BH), dim3(64 * K), 0, st, po, pm, pd, S, out, lse);
+            hipLaunchKernelGGL(merge_kernel_groups<128>, dim3(BH), dim3(64 * K), 0, st, po, pm, pd, S, out, lse, Hq,
+                               q_len);
         else if (head_dim == 64)
-            hipLaunchKernelGGL(merge_kernel_groups<64>, dim3(BH), dim3(64 * K), 0, st, po, pm, pd, S, out, lse);
+            hipLaunchKernelGGL(merge_kernel_groups<64>, dim3(BH), dim3(64 * K), 0, st, po, pm, pd, S, out, lse, Hq,
+                               q_len);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
     }
     dim3 grid((BH + kMergeWaves - 1) / kMergeWaves);
     if (head_dim == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64 * kMergeWaves), 0, st, po, pm, pd, BH, S, out, lse);
+        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64 * kMergeWaves), 0, st, po, pm, pd, BH, S, out, lse, Hq,
+                           q_len);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64 * kMergeWaves), 0, st, po, pm, pd, BH, S, out, lse);
+        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64 * kMergeWaves), 0, st, po, pm, pd, BH, S, out, lse, Hq,
+                           q_len);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -241,10 +241,11 @@ __device__ __forceinline__ void slot_dma_addrs(uint8_t *wl, int slot, uint32_t &
     vl = lds_addr(Ring<KF>::v_tile(wl, slot));
 }
 
-// Q of the four query heads of KV head g of request b (1 KB) to LDS, with the
-// same DMA path, so that every vector load the waits count is a DMA load.
-__device__ __forceinline__ void stage_q(const MapParams &p, int b, int g, uint8_t *qslot, int lane) {
-    dma16(reinterpret_cast<const char *>(p.q) + ((int64_t)b * p.Hq + 4 * g) * 128 * 2, (uint32_t)lane * 16u,
+// Q of the four query heads of KV head g of query row qr (1 KB) to LDS, with
+// the same DMA path, so that every vector load the waits count is a DMA load.
+// qr = b * q_len + token (b for a single query).
+__device__ __forceinline__ void stage_q(const MapParams &p, int qr, int g, uint8_t *qslot, int lane) {
+    dma16(reinterpret_cast<const char *>(p.q) + ((int64_t)qr * p.Hq + 4 * g) * 128 * 2, (uint32_t)lane * 16u,
           lds_addr(qslot));
 }
 
@@ -279,12 +280,15 @@ struct MfmaSoftmax {
     }
 };
 
-// One tile: S^T = K Q^T, online softmax, O += P V. Tokens [nskip, nvalid) of
-// the tile count (nskip < nvalid); the rest are masked. kl / vl: the K and V
-// tiles in LDS.
-template <int DT, int KF>
-__device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 qb[8], int nskip, int nvalid,
-                                          float scale_log2, int lane, MfmaSoftmax &st) {
+// One tile: S^T = K Q^T, online softmax, O += P V, for QL query tokens of the
+// same request (speculative decode; QL = 1 is the single query). Tile tokens
+// [nskip, nvalid[j]) count for query token j (nskip < nvalid[j] for at least
+// the last token); the rest are masked. The K pieces, their float8 conversion
+// and the V^T reads are shared by the QL tokens. kl / vl: the K and V tiles in
+// LDS.
+template <int DT, int KF, int QL>
+__device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 (&qb)[QL][8], int nskip,
+                                          const int (&nvalid)[QL], float scale_log2, int lane, MfmaSoftmax (&st)[QL]) {
     using E = Elem<DT>;
     const int dq = lane >> 4;
     const int rk = lane & 15;  // S^T reads: token L & 15, pieces 4 dq .. 4 dq + 3
@@ -292,23 +296,36 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
     const int tk = (lane & 15) >> 2, ta = lane & 3, tg = lane >> 4;
 
     // ---- S^T = K Q^T: this lane's quarter of D, 4 pieces of 8 d-values
-    f32x4_v s = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_v s[QL], s1[QL];
+#pragma unroll
+    for (int j = 0; j < QL; ++j) {
+        s[j] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+        s1[j] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     if constexpr (KF == 0) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint4 kr = *reinterpret_cast<const uint4 *>(kl + rk * 256 + 16 * ((4 * dq + c) ^ rk));
-            s = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[2 * c], s);
-            s1 = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[2 * c + 1], s1);
+#pragma unroll
+            for (int j = 0; j < QL; ++j) {
+                s[j] = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[j][2 * c], s[j]);
+                s1[j] = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[j][2 * c + 1], s1[j]);
+            }
         }
     } else {
         // float8 piece 2 dq + e holds d 32 dq + 16 e .. + 15: K-steps 4e .. 4e + 3
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const uint4 k8 = *reinterpret_cast<const uint4 *>(kl + rk * 128 + 16 * ((2 * dq + e) ^ ((rk >> 1) & 7)));
-            s = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.x), qb[4 * e], s);
-            s1 = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.y), qb[4 * e + 1], s1);
-            s = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.z), qb[4 * e + 2], s);
-            s1 = Mfma4<DT>::template run<0, 0>(fp8x4_to_bf16(k8.w), qb[4 * e + 3], s1);
+            const uint2 k0 = fp8x4_to_bf16(k8.x), k1 = fp8x4_to_bf16(k8.y);
+            const uint2 k2 = fp8x4_to_bf16(k8.z), k3 = fp8x4_to_bf16(k8.w);
+#pragma unroll
+            for (int j = 0; j < QL; ++j) {
+                s[j] = Mfma4<DT>::template run<0, 0>(k0, qb[j][4 * e], s[j]);
+                s1[j] = Mfma4<DT>::template run<0, 0>(k1, qb[j][4 * e + 1], s1[j]);
+                s[j] = Mfma4<DT>::template run<0, 0>(k2, qb[j][4 * e + 2], s[j]);
+                s1[j] = Mfma4<DT>::template run<0, 0>(k3, qb[j][4 * e + 3], s1[j]);
+            }
         }
     }
     // float8 V^T for P V: lane L gets tokens 8c .. 8c + 7 at d = 64h + L from the
@@ -334,45 +351,51 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
 
     // ---- softmax for head lane & 3, tokens 4 tg .. 4 tg + 3 of this tile
     // (lanes 0..15 carry the tile; the others hold copies and stay masked)
-    float sv[4], mx = kNegInf;
+    uint2 pa[QL], pb[QL];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float x = sum_quarters(s[r] + s1[r]);
-        const int tok = 4 * ((lane >> 2) & 3) + r;
-        sv[r] = (tok >= nskip && tok < nvalid && lane < 16) ? x * scale_log2 : kNegInf;
-        mx = fmax_nc(mx, sv[r]);
-    }
-    st.t = fmax_nc(st.t, mx);
-    if (__builtin_amdgcn_ballot_w64(mx > st.m + kTau) != 0) {
-        // move the reference of every head to its running maximum
-        float hm = mx;
-        hm = fmax_nc(hm, shfl_xor(hm, 4));
-        hm = fmax_nc(hm, shfl_xor(hm, 8));
-        hm = fmax_nc(hm, shfl_xor(hm, 16));
-        hm = fmax_nc(hm, shfl_xor(hm, 32));
-        const float mn = fmax_nc(st.m, hm);
-        const float alpha = fexp2(st.m - mn);
-        st.m = mn;
-        st.l *= alpha;
-        f32x4_v al;
+    for (int j = 0; j < QL; ++j) {
+        float sv[4], mx = kNegInf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = readlane(alpha, i);  // lanes 0..3 carry heads 0..3
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            st.o[h] *= al;
-            st.ol[h] *= al;
+        for (int r = 0; r < 4; ++r) {
+            const float x = sum_quarters(s[j][r] + s1[j][r]);
+            const int tok = 4 * ((lane >> 2) & 3) + r;
+            sv[r] = (tok >= nskip && tok < nvalid[j] && lane < 16) ? x * scale_log2 : kNegInf;
+            mx = fmax_nc(mx, sv[r]);
         }
-    }
-    uint32_t ph[2], pl[2];
+        MfmaSoftmax &t = st[j];
+        t.t = fmax_nc(t.t, mx);
+        if (__builtin_amdgcn_ballot_w64(mx > t.m + kTau) != 0) {
+            // move the reference of every head to its running maximum
+            float hm = mx;
+            hm = fmax_nc(hm, shfl_xor(hm, 4));
+            hm = fmax_nc(hm, shfl_xor(hm, 8));
+            hm = fmax_nc(hm, shfl_xor(hm, 16));
+            hm = fmax_nc(hm, shfl_xor(hm, 32));
+            const float mn = fmax_nc(t.m, hm);
+            const float alpha = fexp2(t.m - mn);
+            t.m = mn;
+            t.l *= alpha;
+            f32x4_v al;
 #pragma unroll
-    for (int r = 0; r < 4; r += 2) {
-        const float p0 = fexp2(sv[r] - st.m), p1 = fexp2(sv[r + 1] - st.m);
-        st.l += p0 + p1;
-        const uint32_t h = pack2<DT>(p0, p1);
-        ph[r / 2] = h;
-        pl[r / 2] = pack2<DT>(p0 - E::lo(h), p1 - E::hi(h));
+            for (int i = 0; i < 4; ++i) al[i] = readlane(alpha, i);  // lanes 0..3 carry heads 0..3
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                t.o[h] *= al;
+                t.ol[h] *= al;
+            }
+        }
+        uint32_t ph[2], pl[2];
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+            const float p0 = fexp2(sv[r] - t.m), p1 = fexp2(sv[r + 1] - t.m);
+            t.l += p0 + p1;
+            const uint32_t h = pack2<DT>(p0, p1);
+            ph[r / 2] = h;
+            pl[r / 2] = pack2<DT>(p0 - E::lo(h), p1 - E::hi(h));
+        }
+        pa[j] = make_uint2(ph[0], ph[1]);
+        pb[j] = make_uint2(pl[0], pl[1]);
     }
-    const uint2 pa = make_uint2(ph[0], ph[1]), pb = make_uint2(pl[0], pl[1]);
 
     // ---- O += P V over the tile's 4 groups of 4 tokens
 #define FDEC_PV_STEP(Q)                                                                                       \
@@ -387,8 +410,10 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
                 lds_s16x4 *src = (lds_s16x4 *)(vl + row * 256 + 16 * (piece ^ (4 * (row & 3))) + 8 * (ta & 1)); \
                 vt = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));                 \
             }                                                                                                 \
-            st.o[h] = Mfma4<DT>::template run<4, (Q)>(pa, vt, st.o[h]);                                       \
-            st.ol[h] = Mfma4<DT>::template run<4, (Q)>(pb, vt, st.ol[h]);                                     \
+            _Pragma("unroll") for (int j = 0; j < QL; ++j) {                                                  \
+                st[j].o[h] = Mfma4<DT>::template run<4, (Q)>(pa[j], vt, st[j].o[h]);                          \
+                st[j].ol[h] = Mfma4<DT>::template run<4, (Q)>(pb[j], vt, st[j].ol[h]);                        \
+            }                                                                                                 \
         }                                                                                                     \
     }
     FDEC_PV_STEP(0)
@@ -428,21 +453,29 @@ __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, flo
 
 // One wave's pass over tokens [t_lo, t_end) of request b for KV head g (its
 // four query heads), in 16-token tiles from t_begin (a multiple of 16, <= t_lo:
-// tiles of a paged cache then stay on one page), state to po0 / pm0 / pd0
-// (+ i hs per head). wl / qslot are the wave's LDS: its ring (Ring<KF>) and 1 KB
-// of Q.
-template <int DT, bool PAGED, int KF>
-__device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, uint8_t *qslot,
-                                             int b, int g, int lane, int t_begin, int t_lo, int t_end, float *po0,
-                                             float *pm0, float *pd0, int64_t hs) {
-    const int ntiles = t_end > t_lo ? (t_end - t_begin + kMT - 1) / kMT : 0;
+// tiles of a paged cache then stay on one page), for nq <= QL query tokens
+// ti0 .. ti0 + nq - 1 of the request: token i sees rows up to
+// L - q_len + i (causal), i.e. its part of the segment ends at
+// min(t_end, L - q_len + i + 1). Token j's state goes to po0[j] / pm0[j] /
+// pd0[j] (+ i hs per head). wl / qslot are the wave's LDS: its ring (Ring<KF>)
+// and QL KB of Q.
+template <int DT, bool PAGED, int KF, int QL>
+__device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, uint8_t *qslot, int b, int g, int lane,
+                                             int t_begin, int t_lo, int t_end, int L, int ti0, int nq,
+                                             float *const (&po0)[QL], float *const (&pm0)[QL],
+                                             float *const (&pd0)[QL], int64_t hs) {
+    int tend[QL];  // each token's end within this segment (t_begin: nothing)
+#pragma unroll
+    for (int j = 0; j < QL; ++j) tend[j] = j < nq ? min(t_end, L - p.q_len + ti0 + j + 1) : t_begin;
+    const int t_stop = min(t_end, L - p.q_len + ti0 + nq);  // past the group's last token's last row
+    const int ntiles = t_stop > t_lo ? (t_stop - t_begin + kMT - 1) / kMT : 0;
     const int nskip0 = t_lo - t_begin;  // left-padding rows of the first tile
     const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
     constexpr int NS = Ring<KF>::kSlots;
     auto stage = [&](int tile, int64_t off) {
         uint32_t kl, vl;
         slot_dma_addrs<KF>(wl, tile % NS, kl, vl);
-        stage_tile<KF>(p.k + off, p.v + off, kl, vl, tile == 0 ? nskip0 : 0, t_end - (t_begin + tile * kMT), stok,
+        stage_tile<KF>(p.k + off, p.v + off, kl, vl, tile == 0 ? nskip0 : 0, t_stop - (t_begin + tile * kMT), stok,
                        lane);
     };
     const int64_t crow = PAGED ? 0 : cache_row(p, b);
@@ -450,16 +483,27 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, ui
     const float kd = KF ? kv_descale(p.k_descale, p, b, g) : 1.0f;
     const float vd = KF ? kv_descale(p.v_descale, p, b, g) : 1.0f;
 
-    MfmaSoftmax st;
-    st.reset();
-    stage_q(p, b, g, qslot, lane);
+    MfmaSoftmax st[QL];
+#pragma unroll
+    for (int j = 0; j < QL; ++j) {
+        st[j].reset();
+        if (j < nq) stage_q(p, b * p.q_len + ti0 + j, g, qslot + 1024 * j, lane);
+    }
     // prologue: the first NS - 1 tiles
     const int npro = min(NS - 1, ntiles);
     for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
     int64_t noff = (NS - 1 < ntiles) ? tile_offset(NS - 1) : 0;  // next tile to stage
     wait_vm_n<KvFmt<KF>::kDma>(npro);  // Q has landed
-    uint2 qb[8];
-    read_q(qslot, lane, qb);
+    uint2 qb[QL][8];
+#pragma unroll
+    for (int j = 0; j < QL; ++j) {
+        if (j < nq) {
+            read_q(qslot + 1024 * j, lane, qb[j]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) qb[j][c] = make_uint2(0u, 0u);
+        }
+    }
 
     for (int tile = 0; tile < ntiles; ++tile) {
         const int ahead = tile + NS - 1;
@@ -470,20 +514,29 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, ui
         // this tile's loads have landed once only the later tiles' remain
         wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, ntiles - 1 - tile));
         const int slot = tile % NS;
-        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, tile == 0 ? nskip0 : 0,
-                          t_end - (t_begin + tile * kMT), p.scale_log2 * kd, lane, st);
+        const int t0 = t_begin + tile * kMT;
+        int nv[QL];
+#pragma unroll
+        for (int j = 0; j < QL; ++j) nv[j] = tend[j] - t0;
+        mfma_tile<DT, KF, QL>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, tile == 0 ? nskip0 : 0, nv,
+                              p.scale_log2 * kd, lane, st);
     }
-    write_state(st, lane, po0, pm0, pd0, hs, vd);
+#pragma unroll
+    for (int j = 0; j < QL; ++j)
+        if (j < nq) write_state(st[j], lane, po0[j], pm0[j], pd0[j], hs, vd);
 }
 
-template <int DT, bool PAGED, int KF>
+template <int DT, bool PAGED, int KF, int QL>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(const MapParams p) {
     constexpr int D = 128, G = 4;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][G * D * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][QL][G * D * 2];
     __shared__ int sm_flag;
 
-    const int split = blockIdx.x, b = blockIdx.y;
+    // grid (split, request x token group, KV-head group); q_groups token groups of QL
+    const int split = blockIdx.x;
+    const int b = blockIdx.y / p.q_groups, tgrp = blockIdx.y - b * p.q_groups;
+    const int ti0 = tgrp * QL, nq = min(QL, p.q_len - ti0);
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = blockIdx.z * p.heads_per_block + wv;
@@ -493,11 +546,20 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     const int lp = first_row(p, b);
     const int t_begin = (lp & ~(kMT - 1)) + split * p.chunk;
     const int t_end = min(t_begin + p.chunk, L);
-    const int64_t st0 = ((int64_t)b * p.Hq + hq0) * p.s_total + p.s_offset + split;
-    mfma_segment<DT, PAGED, KF>(p, lds[wv], qlds[wv], b, g, lane, t_begin, max(t_begin, lp), t_end, p.po + st0 * D,
-                                p.pm + st0, p.pd + st0, p.s_total);
+    float *po0[QL], *pm0[QL], *pd0[QL];
+#pragma unroll
+    for (int j = 0; j < QL; ++j) {
+        // state rows (request, token, head) of [B * q_len * Hq, s_total]
+        const int64_t st0 = (((int64_t)b * p.q_len + ti0 + min(j, nq - 1)) * p.Hq + hq0) * p.s_total + p.s_offset +
+                            split;
+        po0[j] = p.po + st0 * D;
+        pm0[j] = p.pm + st0;
+        pd0[j] = p.pd + st0;
+    }
+    mfma_segment<DT, PAGED, KF, QL>(p, lds[wv], &qlds[wv][0][0], b, g, lane, t_begin, max(t_begin, lp), t_end, L, ti0,
+                                    nq, po0, pm0, pd0, p.s_total);
 
-    if (p.counters == nullptr) return;
+    if (QL > 1 || p.counters == nullptr) return;  // single-kernel merge: single-query decode only
 
     // ---- single-kernel merge (as in map_kernel)
     __syncthreads();
@@ -655,9 +717,9 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const int npro = min(NS - 1, end - start);
     for (int i = 0; i < npro; ++i) produce(start + i);
 
-    MfmaSoftmax st;
-    st.reset();
-    uint2 qb[8];
+    MfmaSoftmax st[1];
+    st[0].reset();
+    uint2 qb[1][8];
     float kd = 1.0f, vd = 1.0f;  // the current request's float8 descales
     for (int x = start; x < end; ++x) {
         if (x + NS - 1 < end) produce(x + NS - 1);
@@ -665,17 +727,17 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
         // issued after it only makes this wait longer)
         wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, end - 1 - x));
         if (x == start) {
-            read_q(qlds[wv][0], lane, qb);
+            read_q(qlds[wv][0], lane, qb[0]);
             if (KF) {
                 kd = kv_descale(p.k_descale, p, cons.b, g);
                 vd = kv_descale(p.v_descale, p, cons.b, g);
             }
         } else if (x >= cons.P + cons.T) {
             const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
-            write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
-            st.reset();
+            write_state(st[0], lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
+            st[0].reset();
             advance(cons);
-            read_q(qlds[wv][cons.seg % NS], lane, qb);
+            read_q(qlds[wv][cons.seg % NS], lane, qb[0]);
             if (KF) {
                 kd = kv_descale(p.k_descale, p, cons.b, g);
                 vd = kv_descale(p.v_descale, p, cons.b, g);
@@ -683,44 +745,57 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
         }
         const int slot = x % NS;
         const int t0 = (cons.lp & ~(kMT - 1)) + (x - cons.P) * kMT;
-        mfma_tile<DT, KF>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, max(cons.lp - t0, 0),
-                          cons.L - t0, p.scale_log2 * kd, lane, st);
+        const int nv[1] = {cons.L - t0};
+        mfma_tile<DT, KF, 1>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, max(cons.lp - t0, 0), nv,
+                             p.scale_log2 * kd, lane, st);
     }
     const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
-    write_state(st, lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
+    write_state(st[0], lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
 }
 
 // Instantiations: q / compute type DT (0 fp16, 1 bf16), paged or not, KV
-// format (float8 caches take bf16 queries).
-#define FDEC_MFMA_DISPATCH(KERNEL)                                                                   \
+// format (float8 caches take bf16 queries); EXTRA: further template arguments.
+#define FDEC_MFMA_DISPATCH(KERNEL, ...)                                                              \
     if (p.kv_fp8) {                                                                                  \
         if (p.page_table)                                                                            \
-            hipLaunchKernelGGL((KERNEL<1, true, 1>), grid, block, 0, st, p);                         \
+            hipLaunchKernelGGL((KERNEL<1, true, 1 __VA_ARGS__>), grid, block, 0, st, p);             \
         else                                                                                         \
-            hipLaunchKernelGGL((KERNEL<1, false, 1>), grid, block, 0, st, p);                        \
+            hipLaunchKernelGGL((KERNEL<1, false, 1 __VA_ARGS__>), grid, block, 0, st, p);            \
     } else if (p.dtype == 0) {                                                                       \
         if (p.page_table)                                                                            \
-            hipLaunchKernelGGL((KERNEL<0, true, 0>), grid, block, 0, st, p);                         \
+            hipLaunchKernelGGL((KERNEL<0, true, 0 __VA_ARGS__>), grid, block, 0, st, p);             \
         else                                                                                         \
-            hipLaunchKernelGGL((KERNEL<0, false, 0>), grid, block, 0, st, p);                        \
+            hipLaunchKernelGGL((KERNEL<0, false, 0 __VA_ARGS__>), grid, block, 0, st, p);            \
     } else {                                                                                         \
         if (p.page_table)                                                                            \
-            hipLaunchKernelGGL((KERNEL<1, true, 0>), grid, block, 0, st, p);                         \
+            hipLaunchKernelGGL((KERNEL<1, true, 0 __VA_ARGS__>), grid, block, 0, st, p);             \
         else                                                                                         \
-            hipLaunchKernelGGL((KERNEL<1, false, 0>), grid, block, 0, st, p);                        \
+            hipLaunchKernelGGL((KERNEL<1, false, 0 __VA_ARGS__>), grid, block, 0, st, p);            \
     }
 
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
     dim3 grid(nblocks, 1, p.Hkv / p.heads_per_block);
     dim3 block(64 * p.heads_per_block);
-    FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal)
+    FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal, )
     return hipGetLastError();
 }
 
+// Query tokens per wave for q_len tokens per request: up to 4 in registers,
+// more in groups of 4 along the grid's y axis.
+int mfma_tokens_per_wave(int q_len) { return q_len <= 1 ? 1 : q_len == 2 ? 2 : 4; }
+
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
-    dim3 grid(S, p.B, p.Hkv / p.heads_per_block);
+    const int ql = mfma_tokens_per_wave(p.q_len);
+    if (p.q_groups != (p.q_len + ql - 1) / ql) return hipErrorInvalidValue;
+    dim3 grid(S, p.B * p.q_groups, p.Hkv / p.heads_per_block);
     dim3 block(64 * p.heads_per_block);
-    FDEC_MFMA_DISPATCH(map_kernel_mfma_g4)
+    if (ql == 1) {
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g4, , 1)
+    } else if (ql == 2) {
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g4, , 2)
+    } else {
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g4, , 4)
+    }
     return hipGetLastError();
 }
 #undef FDEC_MFMA_DISPATCH

@@ -66,6 +66,8 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
 
 /* Largest num_splits accepted by any call. */
 #define FDEC_MAX_SPLITS 256
+/* Largest q_len of fdec_decode_multi. */
+#define FDEC_MAX_QLEN 16
 /* Split chunks are whole multiples of this many tokens. */
 #define FDEC_CHUNK_ALIGN 16
 
@@ -232,6 +234,28 @@ int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv *kv, const 
  */
 int fdec_merge_states(const float *part_o, const float *part_m, const float *part_d, int B, int Hq,
                       int S, int head_dim, float *out, float *lse, void *stream);
+
+/*
+ * Multi-token decode: q_len query tokens per request, e.g. the draft tokens of
+ * speculative decoding ([vllm-arch] spec-decode batches), under the causal mask
+ * the pages' calls pass. Query token i of request b is the request's row
+ * L_b - q_len + i (L_b = seq_lens[b], counted from row 0; the new tokens' K and
+ * V are already in the cache) and attends to rows [cache_leftpad[b],
+ * L_b - q_len + i]; a token with no rows gives out = 0, lse = -inf. The q_len
+ * tokens share each KV tile: the cache is read once per request, as for one
+ * query.
+ *   q    device [B, q_len, Hq, D], the cache's 16-bit dtype (bf16 for float8)
+ *   out  device [B, q_len, Hq, D] fp32; lse device [B, Hq, q_len] fp32 or NULL
+ *        ([cookbook] §3.5 softmax_lse shape (batch, heads, seqlen_q))
+ *   num_splits, softmax_scale as in fdec_decode (splits over the request's rows)
+ *   1 <= q_len <= FDEC_MAX_QLEN. Built for Hq = 4 Hkv, head_dim 128, page_size a
+ *   multiple of 16 or contiguous, all cache dtypes (FDEC_ERR_UNSUPPORTED
+ *   otherwise); no append. workspace >= fdec_workspace_size(B * q_len, Hq, Hkv,
+ *   head_dim, S). q_len = 1 gives fdec_decode's two-kernel result bitwise.
+ */
+int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                      int num_splits, float softmax_scale, float *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /*
  * Decode with a balanced split ([lpnh] §3: the work cut to fill every compute

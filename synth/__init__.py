@@ -199,6 +199,12 @@ def indexed_case(seed: int, B: int, Hq: int, Hkv: int, D: int, lens, leftpad, ca
                 cache_leftpad=lp)
 
 
+def multi_query(seed: int, case: Case, q_len: int) -> torch.Tensor:
+    """Queries of q_len tokens per request, [B, q_len, Hq, D], drawn like a case's q (its own seed)."""
+    g = _gen(seed)
+    return _randn(g, (case.B, q_len, case.Hq, case.D), _q_dtype(case.dtype))
+
+
 def pad_left(case: Case, leftpad, pad: str = "nan") -> Case:
     """Mark rows [0, leftpad[b]) of each request as left padding (filled by `pad`) and record leftpad."""
     lp = torch.as_tensor(leftpad, dtype=torch.int32).reshape(case.B)

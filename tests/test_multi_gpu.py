@@ -1,0 +1,124 @@
+"""Multi-token (speculative) decode on the GPU against the fp64 oracle, through the C ABI.
+
+q_len query tokens per request share each KV tile; token i is the request's
+row L - q_len + i and sees rows [leftpad, L - q_len + i]. Covered: q_len from
+1 to 16 (one wave holds up to 4 tokens, more run as groups of 4), contiguous
+and paged caches, every cache dtype, left padding and a cache row index,
+requests shorter than q_len, the lse layout [B, Hq, q_len], q_len = 1 against
+the single-query decode bitwise, and a full 128k-token request.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_fdec_amd as F
+import oracle
+from helpers import OUT_TOL, LSE_RTOL, okv, to_dev
+from synth import BF16, F16, FP8, contiguous_case, indexed_case, multi_query, pad_left, paged_case, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(fdec):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build(force=False)
+    torch.cuda.init()
+
+
+def check(out, lse, ref_out, ref_lse, dtype, what):
+    o = out.cpu().double().numpy()
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    err = np.abs(o - ref_out).max()
+    assert err <= OUT_TOL[dtype], f"{what}: max-abs out error {err:.3g}"
+    l = lse.cpu().double().numpy()
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(l), fin), f"{what}: lse finiteness differs"
+    assert np.all(l[~fin] == ref_lse[~fin])
+    if fin.any():
+        rel = (np.abs(l[fin] - ref_lse[fin]) / np.maximum(np.abs(ref_lse[fin]), 1.0)).max()
+        assert rel <= LSE_RTOL, f"{what}: lse relative error {rel:.3g}"
+
+
+def run(case, q, S, **extra):
+    d = to_dev(case)
+    out, lse = F.decode_multi(q.to("cuda"), d["k"], d["v"], d["seq_lens"], page_table=d["page_table"],
+                              num_splits=S, k_descale=d["k_descale"], v_descale=d["v_descale"],
+                              cache_batch_idx=d["cache_batch_idx"], cache_leftpad=d["cache_leftpad"], **extra)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+LENS = [700, 3, 1, 64, 65, 2000]  # requests shorter than q_len, tile-edge lengths
+
+
+@pytest.mark.parametrize("q_len", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("kind", ["contig_bf16", "paged_f16", "paged_fp8"])
+@pytest.mark.parametrize("S", [1, 5, 0])
+def test_multi_token_matches_oracle(q_len, kind, S):
+    if kind == "contig_bf16":
+        case = contiguous_case(200 + q_len, 6, 16, 4, 128, LENS, 2048, BF16, pad="nan")
+    elif kind == "paged_f16":
+        case = paged_case(210 + q_len, 6, 16, 4, 128, LENS, 16, F16, extra_pages=3, pad="nan")
+    else:
+        case = paged_case(220 + q_len, 6, 16, 4, 128, LENS, 32, FP8, extra_pages=3, pad="nan")
+    q = multi_query(230 + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    out, lse = run(case, q, S)
+    assert out.shape == (6, q_len, 16, 128) and lse.shape == (6, 16, q_len)
+    check(out, lse, ref_out, ref_lse, case.dtype, f"{kind} q_len={q_len} S={S}")
+
+
+@pytest.mark.parametrize("q_len", [3, 6])
+def test_multi_token_with_leftpad_and_batch_idx(q_len):
+    lens, pads = [300, 40, 19, 1000], [5, 38, 17, 999]  # some tokens see only padding -> empty
+    case = indexed_case(240, 4, 16, 4, 128, lens, pads, 1024, BF16, cache_rows=7)
+    q = multi_query(241, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for S in (1, 4):
+        out, lse = run(case, q, S)
+        check(out, lse, ref_out, ref_lse, BF16, f"indexed q_len={q_len} S={S}")
+    paged = pad_left(paged_case(242, 4, 16, 4, 128, lens, 16, F16, extra_pages=2, pad="nan"), pads)
+    q = multi_query(243, paged, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(paged), q, paged.seq_lens, 1 / math.sqrt(128))
+    out, lse = run(paged, q, 3)
+    check(out, lse, ref_out, ref_lse, F16, f"paged leftpad q_len={q_len}")
+
+
+def test_one_token_equals_single_query_decode_bitwise():
+    case = paged_case(244, 5, 32, 8, 128, [900, 1, 16, 0, 333], 16, BF16, extra_pages=2, pad="nan")
+    d = to_dev(case)
+    for S in (1, 7):
+        o1, l1 = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S)
+        om, lm = F.decode_multi(d["q"][:, None].contiguous(), d["k"], d["v"], d["seq_lens"],
+                                page_table=d["page_table"], num_splits=S)
+        torch.cuda.synchronize()
+        assert torch.equal(om[:, 0], o1) and torch.equal(lm[:, :, 0], l1), f"S={S}"
+
+
+@pytest.mark.parametrize("q_len", [2, 4])
+def test_full_128k_request(q_len):
+    case = workload("c2", pad="nan")
+    q = multi_query(245, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    out, lse = run(case, q, 0)
+    check(out, lse, ref_out, ref_lse, BF16, f"c2 q_len={q_len}")
+
+
+def test_multi_token_shapes_rejected():
+    case = contiguous_case(246, 2, 16, 8, 128, [10, 20], 32, BF16)  # G = 2: no matrix-core kernel
+    q = multi_query(247, case, 2)
+    with pytest.raises(F.FdecError) as e:
+        run(case, q, 1)
+    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
+    case = contiguous_case(248, 2, 16, 4, 128, [10, 20], 32, BF16)
+    for bad in (17, 0):
+        q = torch.zeros(2, max(bad, 1), 16, 128, dtype=BF16)
+        if bad == 0:
+            q = q[:, :0]
+        with pytest.raises(F.FdecError) as e:
+            run(case, q.contiguous(), 1)
+        assert e.value.status == F.FDEC_ERR_INVALID_ARG
