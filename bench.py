@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -103,10 +104,20 @@ class Runner:
             lens_host = (case.seq_lens + (1 if case.k_new is not None else 0)).tolist()
             splits = F.plan(B, Hq, case.Hkv, lens_host, case.capacity, case.page_size)
         self.S = splits
+        self.i = 0
+        if mode.startswith("multi"):
+            # q_len query tokens per request (speculative decode), the case's cache
+            import synth
+
+            self.q_len = int(mode[len("multi"):])
+            self.q = synth.multi_query(300 + self.q_len, case, self.q_len).to(dev)
+            self.out = torch.empty(B, self.q_len, Hq, D, dtype=torch.float32, device=dev)
+            self.lse = torch.empty(B, Hq, self.q_len, dtype=torch.float32, device=dev)
+            self.ws = F.Workspace(F.workspace_size(B * self.q_len, Hq, case.Hkv, D, splits), dev)
+            return
         self.out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
         self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
         self.ws = F.Workspace(F.workspace_size(B, Hq, case.Hkv, D, splits), dev)
-        self.i = 0
 
     def step(self, copy: int | None = None) -> None:
         c = self.i % self.copies if copy is None else copy
@@ -115,6 +126,10 @@ class Runner:
             self.F.cascade_decode(self.q, self.k[c], self.v[c], self.table, self.prefix_pages,
                                   self.case.prefix_len, self.lens, self.S[0], self.S[1], out=self.out,
                                   lse=self.lse, workspace=self.ws)
+            return
+        if self.mode.startswith("multi"):
+            self.F.decode_multi(self.q, self.k[c], self.v[c], self.lens, page_table=self.table, num_splits=self.S,
+                                out=self.out, lse=self.lse, workspace=self.ws, k_descale=self.kd, v_descale=self.vd)
             return
         if self.mode == "bal":
             self.F.decode_balanced(self.q, self.k[c], self.v[c], self.lens, page_table=self.table,
@@ -289,7 +304,7 @@ def main() -> int:
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8",
+    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4",
                     help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -368,6 +383,9 @@ def main() -> int:
             runs += [("c3", "c3", "bal"), ("c3_uniform_splits", "c3", args.mode)]
         elif name == "c3f8":
             runs.append((name, name, "bal"))
+        elif re.fullmatch(r"c\d+q\d+", name):  # e.g. c2q4: workload c2 with 4 query tokens per request
+            base, q = name.split("q")
+            runs.append((name, base, f"multi{q}"))
         else:
             runs.append((name, name, args.mode))
     for key, name, mode in runs:
