@@ -14,8 +14,10 @@
 // (prefix split, KV head, 256-row chunk); 8 waves, each owning 32 query rows
 // (two 16-row blocks), two waves per SIMD so one's matrix work hides the
 // other's softmax. Per 64-key tile:
-//   - the block stages K row-major and V transposed ([d][key], key pairs packed)
-//     in LDS, double-buffered, the next tile's global loads in flight meanwhile;
+//   - K and V go global -> LDS row-major by LDS-DMA (global_load_lds_dwordx4,
+//     no registers), each wave its 8 rows, into a ring of kPfxNS tiles (two in
+//     flight); 16-byte pieces of row r sit in slot piece ^ (r mod 16), so the
+//     K reads below and the transpose reads of V touch distinct banks;
 //   - S^T = K Q^T: A = K (16 keys x 32 d from LDS), B = Q^T (query rows held in
 //     registers), so each lane's result column is one query row and its four
 //     values are four keys of that row;
@@ -23,7 +25,8 @@
 //     map kernel); P enters the matrix core rounded to the input type (hardware
 //     nearest-even conversion), while the denominator sums the fp32 weights;
 //   - O += P V: A = P straight from the S^T registers (the key order inside the
-//     K dimension is permuted identically for A and B), B = V^T from LDS.
+//     K dimension is permuted identically for A and B), B = V^T from two
+//     ds_read_b64_tr_b16 of the row-major V tile (4 keys at one d per lane each).
 // Layout of v_mfma_f32_16x16x32 (lane l, kq = l / 16): A holds row l % 16,
 // k = 8 kq .. 8 kq + 7; B holds column l % 16, k = 8 kq .. 8 kq + 7; D holds rows
 // 4 kq .. 4 kq + 3 of column l % 16.
@@ -67,14 +70,16 @@ template <> __device__ __forceinline__ uint32_t pfx_pack2<1>(float a, float b) {
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
 }
-constexpr int kKStride = 128 + 8;       // K tile row stride in elements (padding vs bank conflicts)
-constexpr int kVStride = kPfxKeys + 4;  // V^T tile row stride in elements
+constexpr int kPfxNS = 3;                  // ring slots (two tiles in flight)
+constexpr int kPfxTileBytes = kPfxKeys * 256;  // 64 rows of 128 16-bit elements
+typedef short pfx_s16x4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) pfx_s16x4_v pfx_lds_s16x4;
 
 template <int DT>
 __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const CascadeParams p) {
     constexpr int D = 128;
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kPfxKeys * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * kVStride];
+    __shared__ __attribute__((aligned(16))) uint8_t kring[kPfxNS][kPfxTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t vring[kPfxNS][kPfxTileBytes];
     __shared__ int spages[kPrefixPagesPerBlock];
     __shared__ float srow[kPfxWaves][3][kPfxRowsPerWave];
 
@@ -105,48 +110,31 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         for (int ks = 0; ks < 4; ++ks)
             qb[rb][ks] = ok ? *reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * kq) : make_uint4(0, 0, 0, 0);
     }
+    // the loads above are done before any DMA is issued: a wait the compiler
+    // models keeps it from waiting on them (and so on the DMA) later
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // Staging: thread t covers rows 2*(t/16) + {0, 1} of a tile, d piece 8*(t%16).
-    const int srow0 = 2 * (tid >> 4), dpiece = 8 * (tid & 15);
-    uint4 rk[2], rv[2];  // rows srow0, srow0+1
-    auto load_tile = [&](int tile) {
+    // DMA of tile `tile` into ring slot tile % kPfxNS: this wave's rows 8w .. 8w + 7
+    // of K and of V, four rows (one page: pages hold multiples of 16 keys) per
+    // instruction; rows past the split's end repeat its last key (masked below)
+    const uint32_t stok = (uint32_t)(p.s_token * 2);
+    auto issue = [&](int tile) {
         const int t0 = t_begin + tile * kPfxKeys;
+        const int nvalid = t_end - t0;
+        const int slot = tile % kPfxNS;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = srow0 + i;
-            const int t = t0 + r;
-            if (t < t_end) {
-                const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
-                const int pl = pidx - pg0, slot = t - pidx * p.page_size;
-                const int64_t off = (int64_t)spages[pl] * p.s_outer + (int64_t)slot * p.s_token +
-                                    (int64_t)g * p.s_head + dpiece;
-                rk[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.k) + off);
-                rv[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.v) + off);
-            } else {
-                rk[i] = make_uint4(0, 0, 0, 0);
-                rv[i] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = srow0 + i;
-            *reinterpret_cast<uint4 *>(&sk[buf][r * kKStride + dpiece]) = rk[i];
-        }
-        // V^T: dword (key r, key r + 1) for each d of the piece
-        {
-            const uint4 a = rv[0], c = rv[1];
-            const int r = srow0;
-            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = __builtin_amdgcn_perm(cv[j], av[j], 0x05040100u);  // (a.lo, c.lo)
-                const uint32_t hi = __builtin_amdgcn_perm(cv[j], av[j], 0x07060302u);  // (a.hi, c.hi)
-                *reinterpret_cast<uint32_t *>(&sv[buf][(dpiece + 2 * j) * kVStride + r]) = lo;
-                *reinterpret_cast<uint32_t *>(&sv[buf][(dpiece + 2 * j + 1) * kVStride + r]) = hi;
-            }
+        for (int gi = 0; gi < 2; ++gi) {
+            const int r0 = 8 * w + 4 * gi;
+            const int rs = min(r0, nvalid - 1);  // the group's first source row
+            const int t = t0 + rs;
+            const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
+            const int64_t eoff = (int64_t)spages[pidx - pg0] * p.s_outer +
+                                 (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head;
+            const int r = r0 + (lane >> 4);
+            const uint32_t voff = (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane & 15) ^ (r & 15));
+            dma16(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kring[slot]) + 256u * r0);
+            dma16(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vring[slot]) + 256u * r0);
         }
     };
 
@@ -163,17 +151,18 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         for (int db = 0; db < 8; ++db) o[rb][db] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-        __syncthreads();
-    }
+    const int npro = min(kPfxNS - 1, ntiles);
+    for (int t = 0; t < npro; ++t) issue(t);
     for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        if (tile + 1 < ntiles) load_tile(tile + 1);  // in flight during this tile's math
+        // this wave's part of the tile has landed once only later tiles' loads
+        // remain; the barrier then covers every wave's part, and every wave is
+        // done with the slot the next DMA overwrites (read two tiles ago)
+        wait_vm_n<4>(min(kPfxNS - 2, ntiles - 1 - tile));
+        __syncthreads();
+        if (tile + kPfxNS - 1 < ntiles) issue(tile + kPfxNS - 1);
         const int t0 = t_begin + tile * kPfxKeys;
-        const uint16_t *K = sk[buf];
-        const uint16_t *V = sv[buf];
+        const uint8_t *K = kring[tile % kPfxNS];
+        const uint8_t *V = vring[tile % kPfxNS];
 
         // ---- S^T = K Q^T: s[kb][rb] holds keys 16kb + 4kq + r of row 16rb + li
         f32x4_v s[4][kRB];
@@ -183,7 +172,8 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
             for (int rb = 0; rb < kRB; ++rb) s[kb][rb] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(&K[(16 * kb + li) * kKStride + 32 * ks + 8 * kq]);
+                const int kr = 16 * kb + li;
+                const uint4 a = *reinterpret_cast<const uint4 *>(K + kr * 256 + 16 * ((4 * ks + kq) ^ (kr & 15)));
 #pragma unroll
                 for (int rb = 0; rb < kRB; ++rb) s[kb][rb] = Mfma<DT>::run(a, qb[rb][ks], s[kb][rb]);
             }
@@ -261,24 +251,26 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         }
 
         // ---- O += P V
+        // B operand of K-slots 8kq .. 8kq + 7 at d = 16db + li: keys 32kk + 4kq + 0..3
+        // and 32kk + 16 + 4kq + 0..3, each set from one transpose read whose lane m
+        // (of 16) addresses key row 32kk (+16) + 4kq + m / 4, d 16db + 4 (m % 4) .. + 3
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const uint16_t *vrow = &V[(16 * db + li) * kVStride + 32 * kk + 4 * kq];
-                const uint2 v0 = *reinterpret_cast<const uint2 *>(vrow);
-                const uint2 v1 = *reinterpret_cast<const uint2 *>(vrow + 16);
+                const int ra = 32 * kk + 4 * kq + (li >> 2), rb2 = ra + 16;
+                const int piece = 2 * db + ((li & 3) >> 1), half = 8 * (li & 1);
+                const pfx_s16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (pfx_lds_s16x4 *)(V + ra * 256 + 16 * (piece ^ (ra & 15)) + half));
+                const pfx_s16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (pfx_lds_s16x4 *)(V + rb2 * 256 + 16 * (piece ^ (rb2 & 15)) + half));
+                const uint2 v0 = __builtin_bit_cast(uint2, x0), v1 = __builtin_bit_cast(uint2, x1);
                 const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
                 for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
             }
         }
 
-        if (tile + 1 < ntiles) {
-            // the other buffer was last read before the previous barrier
-            store_tile(buf ^ 1);
-            __syncthreads();
-        }
     }
 
     // ---- states against the true maximum: O~ = O 2^(m - T), d = l 2^(m - T)

@@ -95,6 +95,42 @@ __device__ __forceinline__ float readlane(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// LDS-DMA load: 64 lanes x 16 bytes from base + voff (per lane) into LDS at
+// lds_addr + 16 * lane. Issued as inline assembly so that the compiler neither
+// waits for it before unrelated LDS reads nor counts it: every wait on these
+// loads is one of the explicit waits below.
+// base and lds_addr are wave-uniform; readfirstlane states that to the compiler.
+__device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t lds_addr) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t ua = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+    const uint32_t ul = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(reinterpret_cast<const char *>(ua)),
+                 "s"(ul) : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+// wait until at most N k DMA loads are outstanding (k uniform, clamped to [0, 7])
+template <int N> __device__ __forceinline__ void wait_vm_n(int k) {
+    switch (k) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<N>(); break;
+    case 2: wait_vm<2 * N>(); break;
+    case 3: wait_vm<3 * N>(); break;
+    case 4: wait_vm<4 * N>(); break;
+    case 5: wait_vm<5 * N>(); break;
+    case 6: wait_vm<6 * N>(); break;
+    default: wait_vm<7 * N>(); break;
+    }
+}
+
+// LDS address of a shared-memory pointer, for m0.
+__device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)ptr;
+}
+
+
 // Merging S <= 256 partial states of one (b, h) (the reduce stage):
 // m = max_i m_i, alpha_i = exp(m_i - m) (0 for an empty state), d = sum alpha_i d_i,
 // out = sum alpha_i O~_i / d, lse = m + ln d. States are in natural-log units.
