@@ -90,6 +90,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_cascade_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.fdec_decode_balanced.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F, P, P, P, Z, P]
     lib.fdec_decode_multi.argtypes = [P, I, I, I, ctypes.POINTER(FdecKV), P, I, F, P, P, P, Z, P]
+    lib.fdec_decode_multi_balanced.argtypes = [P, I, I, I, ctypes.POINTER(FdecKV), P, I, F, P, P, P, Z, P]
     lib.fdec_balanced_workspace_size.restype = Z
     lib.fdec_balanced_workspace_size.argtypes = [I, I, I, I, I]
     if path is None:
@@ -274,6 +275,32 @@ def decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: to
     _check(lib.fdec_decode_multi(q.data_ptr(), B, q_len, Hq, ctypes.byref(kv), seq_lens.data_ptr(), S,
                                  float(softmax_scale), out.data_ptr(), _ptr(lse), workspace.buf.data_ptr(),
                                  workspace.nbytes, _stream(q.device)))
+    return out, lse
+
+
+def decode_multi_balanced(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                          page_table: Optional[torch.Tensor] = None, num_blocks: int = 0, softmax_scale: float = 0.0,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[Workspace] = None, return_lse: bool = True,
+                          k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None,
+                          cache_batch_idx: Optional[torch.Tensor] = None,
+                          cache_leftpad: Optional[torch.Tensor] = None):
+    """fdec_decode_multi_balanced: q [B, q_len, Hq, D] -> (out [B, q_len, Hq, D], lse [B, Hq, q_len] or None)."""
+    lib = load_library()
+    if q.dim() != 4 or not q.is_contiguous():
+        raise FdecError(FDEC_ERR_INVALID_ARG, "q must be a contiguous [B, q_len, Hq, D] tensor")
+    B, q_len, Hq, D = q.shape
+    kv = make_kv(k, v, page_table, k_descale, v_descale, cache_batch_idx, cache_leftpad)
+    _check_q(q, k)
+    if out is None:
+        out = torch.empty(B, q_len, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, q_len, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = Workspace(balanced_workspace_size(B, q_len * Hq, kv.num_kv_heads, D, num_blocks), q.device)
+    _check(lib.fdec_decode_multi_balanced(q.data_ptr(), B, q_len, Hq, ctypes.byref(kv), seq_lens.data_ptr(),
+                                          int(num_blocks), float(softmax_scale), out.data_ptr(), _ptr(lse),
+                                          workspace.buf.data_ptr(), workspace.nbytes, _stream(q.device)))
     return out, lse
 
 

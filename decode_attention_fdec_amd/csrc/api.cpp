@@ -402,11 +402,12 @@ extern "C" size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_
     return bal_layout(B, Hq, head_dim, balanced_blocks(Hkv, num_blocks, 2)).total;
 }
 
-extern "C" int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
-                                    int num_blocks, float softmax_scale, float *out, float *lse, void *workspace,
-                                    size_t workspace_bytes, void *stream) {
-    fdec_clear_error();
-    const char *fn = "fdec_decode_balanced";
+// The balanced split for q_len query tokens per request (1: fdec_decode_balanced).
+int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq, const fdec_kv *kv,
+                         const int32_t *seq_lens, int num_blocks, float softmax_scale, float *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (q_len < 1 || q_len > FDEC_MAX_QLEN)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: q_len %d outside [1, %d]", fn, q_len, FDEC_MAX_QLEN);
     int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
     if (rc) return rc;
     if (num_blocks < 0 || num_blocks > FDEC_MAX_SPLITS)
@@ -421,8 +422,13 @@ extern "C" int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv 
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
-    const int nb = balanced_blocks(kv->num_kv_heads, num_blocks, kv->dtype == FDEC_FP8_E4M3 ? 2 : 1);
-    const BalLayout w = bal_layout(B, Hq, kv->head_dim, nb);
+    const int ql = fdec::mfma_tokens_per_wave(q_len);
+    p.q_len = q_len;
+    p.q_groups = (q_len + ql - 1) / ql;
+    // float8 caches run two blocks per compute unit; with several query tokens the
+    // Q slots take the LDS the second block would need
+    const int nb = balanced_blocks(kv->num_kv_heads, num_blocks, kv->dtype == FDEC_FP8_E4M3 && ql == 1 ? 2 : 1);
+    const BalLayout w = bal_layout(B, q_len * Hq, kv->head_dim, nb);
     if (!workspace || workspace_bytes < w.total)
         return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d blocks, got %zu", fn, w.total,
                          nb, workspace ? workspace_bytes : (size_t)0);
@@ -434,10 +440,26 @@ extern "C" int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv 
     p.po = reinterpret_cast<float *>(ws + w.po);
     p.nslots = nb + B;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = check_hip(fdec::launch_map_mfma_g4_balanced(p, nb, st), "fdec_decode_balanced: map launch"))) return rc;
+    if ((rc = check_hip(fdec::launch_map_mfma_g4_balanced(p, nb, st), "balanced split: map launch"))) return rc;
     return check_hip(fdec::launch_merge_segments(p.po, p.pm, p.pd, p.seg_meta, B, Hq, p.nslots, nb, kv->head_dim, out,
-                                                 lse, st),
-                     "fdec_decode_balanced: merge launch");
+                                                 lse, st, q_len),
+                     "balanced split: merge launch");
+}
+
+extern "C" int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                                    int num_blocks, float softmax_scale, float *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    fdec_clear_error();
+    return decode_balanced_impl("fdec_decode_balanced", q, B, 1, Hq, kv, seq_lens, num_blocks, softmax_scale, out, lse,
+                                workspace, workspace_bytes, stream);
+}
+
+extern "C" int fdec_decode_multi_balanced(const void *q, int B, int q_len, int Hq, const fdec_kv *kv,
+                                          const int32_t *seq_lens, int num_blocks, float softmax_scale, float *out,
+                                          float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    fdec_clear_error();
+    return decode_balanced_impl("fdec_decode_multi_balanced", q, B, q_len, Hq, kv, seq_lens, num_blocks,
+                                softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fdec_merge_states(const float *part_o, const float *part_m, const float *part_d, int B, int Hq,

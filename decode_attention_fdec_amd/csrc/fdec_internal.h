@@ -103,7 +103,7 @@ hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B
 // [meta[2b], meta[2b] + meta[2b+1]) of [Hq, nslots]; max_count bounds the counts.
 hipError_t launch_merge_segments(const float *po, const float *pm, const float *pd, const int *meta, int B, int Hq,
                                  int nslots, int max_count, int head_dim, float *out, float *lse,
-                                 hipStream_t stream);
+                                 hipStream_t stream, int q_len = 1);
 
 // Cascade merge with a balanced suffix: per (b, h) the prefix states
 // [B, Hq, sp] then request b's suffix pieces (as launch_merge_segments).

@@ -45,21 +45,23 @@ __global__ __launch_bounds__(64 * (256 / kMergeGroup)) void merge_kernel_groups(
                           blockDim.x >> 6, gs);
 }
 
-// Balanced-split merge: one block per (b, h). The piece count is known only on
-// the device, so the block has kSegWaves waves that take the groups in turn.
+// Balanced-split merge: one block per (b, token, h) (q tokens per request,
+// rows token * Hq + h of the [q * Hq, nslots] states). The piece count is known
+// only on the device, so the block has kSegWaves waves that take the groups in
+// turn.
 template <int D>
 __global__ __launch_bounds__(64 * (256 / kMergeGroup)) void merge_kernel_segments(
     const float *__restrict__ po, const float *__restrict__ pm, const float *__restrict__ pd,
-    const int *__restrict__ meta, int Hq, int nslots, float *__restrict__ out, float *__restrict__ lse) {
+    const int *__restrict__ meta, int Hq, int q, int nslots, float *__restrict__ out, float *__restrict__ lse) {
     __shared__ float gs[256 / kMergeGroup][D];
     const int lane = threadIdx.x & 63;
     const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bh = blockIdx.x;
-    const int b = (int)(bh / Hq), h = (int)(bh % Hq);
-    const int64_t base = (int64_t)h * nslots + meta[2 * b];
+    const int b = (int)(bh / ((int64_t)q * Hq)), row = (int)(bh - (int64_t)b * q * Hq);
+    const int64_t base = (int64_t)row * nslots + meta[2 * b];
     const ContigStates<D> src{po + base * D, pm + base, pd + base};
-    merge_states_block<D>(src, meta[2 * b + 1], out + bh * D, lse ? lse + bh : nullptr, lane, k, blockDim.x >> 6,
-                          gs);
+    merge_states_block<D>(src, meta[2 * b + 1], out + bh * D, lse ? lse + lse_slot(bh, Hq, q) : nullptr, lane, k,
+                          blockDim.x >> 6, gs);
 }
 
 // Cascade with a balanced suffix: per (b, h) the sp prefix states [B, Hq, sp]
@@ -88,14 +90,16 @@ constexpr int kSegWaves = 2;
 
 hipError_t launch_merge_segments(const float *po, const float *pm, const float *pd, const int *meta, int B, int Hq,
                                  int nslots, int max_count, int head_dim, float *out, float *lse,
-                                 hipStream_t st) {
+                                 hipStream_t st, int q_len) {
     const int K = (max(max_count, 1) + kMergeGroup - 1) / kMergeGroup;
     if (K > 256 / kMergeGroup) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)B * Hq), block(64 * min(K, kSegWaves));
+    const dim3 grid((unsigned)B * q_len * Hq), block(64 * min(K, kSegWaves));
     if (head_dim == 128)
-        hipLaunchKernelGGL(merge_kernel_segments<128>, grid, block, 0, st, po, pm, pd, meta, Hq, nslots, out, lse);
+        hipLaunchKernelGGL(merge_kernel_segments<128>, grid, block, 0, st, po, pm, pd, meta, Hq, q_len, nslots, out,
+                           lse);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(merge_kernel_segments<64>, grid, block, 0, st, po, pm, pd, meta, Hq, nslots, out, lse);
+        hipLaunchKernelGGL(merge_kernel_segments<64>, grid, block, 0, st, po, pm, pd, meta, Hq, q_len, nslots, out,
+                           lse);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -573,13 +573,15 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // With fewer tiles than blocks, only the first (tiles) blocks take work, so
 // every working block has at least one tile and no slot of a request is left
 // unwritten. Every wave scans seq_lens itself (no block barrier).
-template <int DT, bool PAGED, int KF>
+template <int DT, bool PAGED, int KF, int QL>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
     constexpr int D = 128, G = 4;
     constexpr int NS = Ring<KF>::kSlots;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
-    // Q of the pieces in flight: at most one per ring slot
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][NS][G * D * 2];
+    // Q of the pieces in flight (at most one per ring slot), QL query tokens each
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][NS][QL][G * D * 2];
+    // query tokens ti0 .. ti0 + nq - 1 of every request (grid y: groups of QL)
+    const int ti0 = blockIdx.y * QL, nq = min(QL, p.q_len - ti0);
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -611,7 +613,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const bool working = blk < NBe;
     const int start = working ? (int)((int64_t)blk * NT / NBe) : 0;
     const int end = working ? (int)((int64_t)(blk + 1) * NT / NBe) : 0;
-    const bool meta_writer = blockIdx.z == 0 && wv == 0;
+    const bool meta_writer = blockIdx.z == 0 && blockIdx.y == 0 && wv == 0;
 
     int b0 = -1, P0 = 0, T0 = 0;  // first request of the range and its first tile
     int carry = 0;                // tiles of the requests before this group of 64
@@ -666,10 +668,36 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const int64_t crow0 = PAGED ? 0 : cache_row(p, b0);
     Cursor prod{b0, P0, T0, Lb0, lp0, 0, crow0}, cons{b0, P0, T0, Lb0, lp0, 0, crow0};
     uint8_t *wl = lds[wv];
+    // Q of request b's query tokens into ring slot qs
+    auto stage_qs = [&](int b, int qs) {
+#pragma unroll
+        for (int j = 0; j < QL; ++j)
+            if (j < nq) stage_q(p, b * p.q_len + ti0 + j, g, qlds[wv][qs][j], lane);
+    };
+    auto read_qs = [&](int qs, uint2 (&qb)[QL][8]) {
+#pragma unroll
+        for (int j = 0; j < QL; ++j) {
+            if (j < nq) {
+                read_q(qlds[wv][qs][j], lane, qb[j]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) qb[j][c] = make_uint2(0u, 0u);
+            }
+        }
+    };
+    // the states of request b's piece in this block: rows (token, head) of [q_len * Hq, nslots]
+    auto flush = [&](const MfmaSoftmax (&st)[QL], int b, float vd) {
+#pragma unroll
+        for (int j = 0; j < QL; ++j) {
+            if (j >= nq) continue;
+            const int64_t s0 = ((int64_t)(ti0 + j) * p.Hq + hq0) * p.nslots + blk + b;
+            write_state(st[j], lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
+        }
+    };
     auto produce = [&](int x) {  // stage tile x (and Q when it starts a new piece)
         if (x >= prod.P + prod.T) {
             advance(prod);
-            stage_q(p, prod.b, g, qlds[wv][prod.seg % NS], lane);
+            stage_qs(prod.b, prod.seg % NS);
         }
         const int t0 = (prod.lp & ~(kMT - 1)) + (x - prod.P) * kMT;
         const int64_t off = token_offset<PAGED, KF>(p, prod.b, prod.crow, g, t0);
@@ -678,13 +706,14 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
         stage_tile<KF>(p.k + off, p.v + off, kl, vl, max(prod.lp - t0, 0), prod.L - t0, stok, lane);
     };
 
-    stage_q(p, b0, g, qlds[wv][0], lane);
+    stage_qs(b0, 0);
     const int npro = min(NS - 1, end - start);
     for (int i = 0; i < npro; ++i) produce(start + i);
 
-    MfmaSoftmax st[1];
-    st[0].reset();
-    uint2 qb[1][8];
+    MfmaSoftmax st[QL];
+#pragma unroll
+    for (int j = 0; j < QL; ++j) st[j].reset();
+    uint2 qb[QL][8];
     float kd = 1.0f, vd = 1.0f;  // the current request's float8 descales
     for (int x = start; x < end; ++x) {
         if (x + NS - 1 < end) produce(x + NS - 1);
@@ -692,17 +721,17 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
         // issued after it only makes this wait longer)
         wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, end - 1 - x));
         if (x == start) {
-            read_q(qlds[wv][0], lane, qb[0]);
+            read_qs(0, qb);
             if (KF) {
                 kd = kv_descale(p.k_descale, p, cons.b, g);
                 vd = kv_descale(p.v_descale, p, cons.b, g);
             }
         } else if (x >= cons.P + cons.T) {
-            const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
-            write_state(st[0], lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
-            st[0].reset();
+            flush(st, cons.b, vd);
+#pragma unroll
+            for (int j = 0; j < QL; ++j) st[j].reset();
             advance(cons);
-            read_q(qlds[wv][cons.seg % NS], lane, qb[0]);
+            read_qs(cons.seg % NS, qb);
             if (KF) {
                 kd = kv_descale(p.k_descale, p, cons.b, g);
                 vd = kv_descale(p.v_descale, p, cons.b, g);
@@ -710,12 +739,13 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
         }
         const int slot = x % NS;
         const int t0 = (cons.lp & ~(kMT - 1)) + (x - cons.P) * kMT;
-        const int nv[1] = {cons.L - t0};
-        mfma_tile<DT, KF, 1>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, max(cons.lp - t0, 0), nv,
-                             p.scale_log2 * kd, lane, st);
+        int nv[QL];  // token ti0 + j sees rows up to L - q_len + ti0 + j (causal)
+#pragma unroll
+        for (int j = 0; j < QL; ++j) nv[j] = j < nq ? cons.L - p.q_len + ti0 + j + 1 - t0 : 0;
+        mfma_tile<DT, KF, QL>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, max(cons.lp - t0, 0), nv,
+                              p.scale_log2 * kd, lane, st);
     }
-    const int64_t s0 = (int64_t)hq0 * p.nslots + blk + cons.b;
-    write_state(st[0], lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
+    flush(st, cons.b, vd);
 }
 
 // Instantiations: q / compute type DT (0 fp16, 1 bf16), paged or not, KV
@@ -738,16 +768,24 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
             hipLaunchKernelGGL((KERNEL<1, false, 0 __VA_ARGS__>), grid, block, 0, st, p);            \
     }
 
-hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
-    dim3 grid(nblocks, 1, p.Hkv / p.heads_per_block);
-    dim3 block(64 * p.heads_per_block);
-    FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal, )
-    return hipGetLastError();
-}
-
 // Query tokens per wave for q_len tokens per request: up to 4 in registers,
 // more in groups of 4 along the grid's y axis.
 int mfma_tokens_per_wave(int q_len) { return q_len <= 1 ? 1 : q_len == 2 ? 2 : 4; }
+
+hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
+    const int ql = mfma_tokens_per_wave(p.q_len);
+    if (p.q_groups != (p.q_len + ql - 1) / ql) return hipErrorInvalidValue;
+    dim3 grid(nblocks, p.q_groups, p.Hkv / p.heads_per_block);
+    dim3 block(64 * p.heads_per_block);
+    if (ql == 1) {
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal, , 1)
+    } else if (ql == 2) {
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal, , 2)
+    } else {
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal, , 4)
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
     const int ql = mfma_tokens_per_wave(p.q_len);

@@ -281,8 +281,22 @@ int fdec_decode_balanced(const void *q, int B, int Hq, const fdec_kv *kv, const 
                          size_t workspace_bytes, void *stream);
 
 /* Workspace bytes for fdec_decode_balanced (num_blocks as there; 0 = enough for
- * the default of every cache dtype). */
+ * the default of every cache dtype). fdec_decode_multi_balanced takes
+ * fdec_balanced_workspace_size(B, q_len * Hq, Hkv, head_dim, num_blocks). */
 size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_blocks);
+
+/*
+ * fdec_decode_multi on the balanced split: q_len query tokens per request
+ * (q [B, q_len, Hq, D], out [B, q_len, Hq, D], lse [B, Hq, q_len], causal as in
+ * fdec_decode_multi) with the work of all requests cut into num_blocks equal
+ * tile ranges per group of KV heads as in fdec_decode_balanced (0 = one block
+ * per compute unit over all groups). 1 <= q_len <= FDEC_MAX_QLEN; the shapes and
+ * errors of fdec_decode_balanced. q_len = 1 gives fdec_decode_balanced's result
+ * bitwise.
+ */
+int fdec_decode_multi_balanced(const void *q, int B, int q_len, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                               int num_blocks, float softmax_scale, float *out, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /*
  * Cascade decode with a shared prefix ([vllm-arch] cascade attention): all B

@@ -122,3 +122,59 @@ def test_multi_token_shapes_rejected():
         with pytest.raises(F.FdecError) as e:
             run(case, q.contiguous(), 1)
         assert e.value.status == F.FDEC_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- on the balanced split
+
+def run_bal(case, q, nb):
+    d = to_dev(case)
+    out, lse = F.decode_multi_balanced(q.to("cuda"), d["k"], d["v"], d["seq_lens"], page_table=d["page_table"],
+                                       num_blocks=nb, k_descale=d["k_descale"], v_descale=d["v_descale"],
+                                       cache_batch_idx=d["cache_batch_idx"], cache_leftpad=d["cache_leftpad"])
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("q_len", [1, 2, 3, 4, 6, 16])
+@pytest.mark.parametrize("kind", ["contig_bf16", "paged_f16", "paged_fp8"])
+def test_multi_token_balanced_matches_oracle(q_len, kind):
+    if kind == "contig_bf16":
+        case = contiguous_case(250 + q_len, 6, 16, 4, 128, LENS, 2048, BF16, pad="nan")
+    elif kind == "paged_f16":
+        case = paged_case(260 + q_len, 6, 16, 4, 128, LENS, 16, F16, extra_pages=3, pad="nan")
+    else:
+        case = paged_case(270 + q_len, 6, 16, 4, 128, LENS, 32, FP8, extra_pages=3, pad="nan")
+    q = multi_query(280 + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for nb in (1, 3, 0):
+        out, lse = run_bal(case, q, nb)
+        check(out, lse, ref_out, ref_lse, case.dtype, f"balanced {kind} q_len={q_len} nb={nb}")
+
+
+def test_multi_token_balanced_with_leftpad_and_batch_idx():
+    lens, pads = [300, 40, 19, 1000], [5, 38, 17, 999]
+    case = indexed_case(290, 4, 16, 4, 128, lens, pads, 1024, BF16, cache_rows=7)
+    q = multi_query(291, case, 5)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for nb in (2, 0):
+        out, lse = run_bal(case, q, nb)
+        check(out, lse, ref_out, ref_lse, BF16, f"balanced indexed nb={nb}")
+
+
+def test_multi_balanced_one_token_equals_balanced_bitwise():
+    case = paged_case(292, 5, 32, 8, 128, [900, 1, 16, 0, 333], 16, BF16, extra_pages=2, pad="nan")
+    d = to_dev(case)
+    for nb in (3, 0):
+        o1, l1 = F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_blocks=nb)
+        om, lm = F.decode_multi_balanced(d["q"][:, None].contiguous(), d["k"], d["v"], d["seq_lens"],
+                                         page_table=d["page_table"], num_blocks=nb)
+        torch.cuda.synchronize()
+        assert torch.equal(om[:, 0], o1) and torch.equal(lm[:, :, 0], l1), f"nb={nb}"
+
+
+def test_multi_token_balanced_full_paged_batch():
+    case = workload("c3", pad="nan")
+    q = multi_query(293, case, 4)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    out, lse = run_bal(case, q, 0)
+    check(out, lse, ref_out, ref_lse, BF16, "c3 q_len=4 balanced")
