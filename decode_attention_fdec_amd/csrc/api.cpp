@@ -318,9 +318,13 @@ extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const 
                          w.total, S, workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, nullptr);
-    if (!p.mfma)
+    const int G = Hq / kv->num_kv_heads;
+    const bool mt16 = fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
+                      (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
+    if (!p.mfma && !mt16)
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: needs Hq = 4 Hkv, head_dim 128 and page_size a multiple of 16 (matrix-core kernel)", fn);
+                         "%s: needs head_dim 128 and either Hq = 4 Hkv or q_len * Hq / Hkv >= 12 (16-bit caches)",
+                         fn);
     const int ql = fdec::mfma_tokens_per_wave(q_len);
     p.q_len = q_len;
     p.q_groups = (q_len + ql - 1) / ql;
@@ -333,7 +337,9 @@ extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const 
     p.s_total = S;
     p.s_offset = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = check_hip(fdec::launch_map(p, S, st), "fdec_decode_multi: map launch"))) return rc;
+    if ((rc = check_hip(mt16 ? fdec::launch_map_mt16(p, S, st) : fdec::launch_map(p, S, st),
+                        "fdec_decode_multi: map launch")))
+        return rc;
     return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st, q_len),
                      "fdec_decode_multi: merge launch");
 }

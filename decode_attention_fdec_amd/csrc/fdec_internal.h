@@ -74,6 +74,16 @@ inline bool map_mfma_eligible(const MapParams &p) {
 hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t stream);
 hipError_t launch_map_mfma_g4(const MapParams &p, int num_splits, hipStream_t stream);
 int mfma_tokens_per_wave(int q_len);
+// Multi-token map kernel on 16x16x32 matrix cores (16-bit caches, head_dim 128,
+// any G): one wave per (split, request, KV head, 16 or 32 query rows), kMtWaves
+// waves per block.
+constexpr int kMtWaves = 4;
+hipError_t launch_map_mt16(const MapParams &p, int num_splits, hipStream_t stream);
+// Whether fdec_decode_multi takes the 16x16x32 kernel: q_len * G query rows per
+// (request, KV head) fill its row blocks.
+inline bool mt16_eligible(int q_len, int G, int head_dim, bool fp8) {
+    return !fp8 && head_dim == 128 && q_len * G >= 12;
+}
 // Balanced split over nblocks blocks per group of KV heads (matrix-core kernel).
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t stream);
 

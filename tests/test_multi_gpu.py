@@ -178,3 +178,37 @@ def test_multi_token_balanced_full_paged_batch():
     ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
     out, lse = run_bal(case, q, 0)
     check(out, lse, ref_out, ref_lse, BF16, "c3 q_len=4 balanced")
+
+
+# ---------------------------------------------------------------- the 16x16x32 kernel (q_len * G >= 12)
+
+@pytest.mark.parametrize("G,q_len", [(8, 2), (8, 5), (1, 12), (1, 16), (2, 6), (2, 16), (4, 16)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_multi_token_any_group_size(G, q_len, paged):
+    Hkv = 2 if G == 8 else 4
+    lens = [700, 3, 1, 64, 65, 2000]
+    if paged:
+        case = paged_case(300 + G + q_len, 6, G * Hkv, Hkv, 128, lens, 32, F16, extra_pages=3, pad="nan")
+    else:
+        case = contiguous_case(310 + G + q_len, 6, G * Hkv, Hkv, 128, lens, 2048, BF16, pad="nan")
+    q = multi_query(320 + G + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for S in (1, 5, 0):
+        out, lse = run(case, q, S)
+        check(out, lse, ref_out, ref_lse, case.dtype, f"G={G} q_len={q_len} paged={paged} S={S}")
+
+
+@pytest.mark.parametrize("q_len", [3, 4, 8])
+def test_multi_token_both_kernels_agree_with_oracle(q_len, monkeypatch):
+    lens, pads = [300, 40, 19, 1000], [5, 38, 17, 999]
+    case = indexed_case(330 + q_len, 4, 16, 4, 128, lens, pads, 1024, BF16, cache_rows=6)
+    q = multi_query(331 + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    res = {}
+    for path in ("16x16", "4x4"):
+        if path == "4x4":
+            monkeypatch.setenv("FDEC_MULTI_PATH", "4x4")
+        out, lse = run(case, q, 3)
+        check(out, lse, ref_out, ref_lse, BF16, f"{path} q_len={q_len}")
+        res[path] = out
+    assert (res["16x16"] - res["4x4"]).abs().max().item() < 1e-4
