@@ -373,6 +373,14 @@ extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv 
 // Default block count of the balanced split: per_cu blocks per compute unit
 // over all groups of KV heads (16-bit caches: 1; float8 caches: 2, whose
 // tiles take half the LDS and whose blocks then overlap each other's latency).
+int device_cus() {
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+        cu = 256;
+    return cu;
+}
+
 int balanced_blocks(int Hkv, int num_blocks, int per_cu) {
     if (num_blocks > 0) return num_blocks;
     int hpb = 1;
@@ -381,11 +389,7 @@ int balanced_blocks(int Hkv, int num_blocks, int per_cu) {
             hpb = w;
             break;
         }
-    int dev = 0, cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
-        cu = 256;
-    return std::max(1, std::min(FDEC_MAX_SPLITS, per_cu * cu / (Hkv / hpb)));
+    return std::max(1, std::min(FDEC_MAX_SPLITS, per_cu * device_cus() / (Hkv / hpb)));
 }
 
 struct BalLayout {
@@ -421,9 +425,15 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     if ((int64_t)B * (((int64_t)capacity_of(kv) + 15) / 16) >= (int64_t(1) << 31))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: B * ceil(capacity / 16) must stay below 2^31", fn);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, 1, softmax_scale, nullptr);
-    if (!p.mfma)
+    const int G = Hq / kv->num_kv_heads;
+    // several query tokens: the 16x16x32 kernel when its row blocks fill
+    const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
+                      (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
+    if (!p.mfma && !mt16)
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: needs Hq = 4 Hkv, head_dim 128 and page_size a multiple of 16 (matrix-core kernel)", fn);
+                         "%s: needs head_dim 128, page_size a multiple of 16 and Hq = 4 Hkv (q_len * Hq / Hkv >= 12 "
+                         "with several tokens and 16-bit caches)",
+                         fn);
     if (B == 0) return FDEC_OK;
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
@@ -432,8 +442,13 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     p.q_len = q_len;
     p.q_groups = (q_len + ql - 1) / ql;
     // float8 caches run two blocks per compute unit; with several query tokens the
-    // Q slots take the LDS the second block would need
-    const int nb = balanced_blocks(kv->num_kv_heads, num_blocks, kv->dtype == FDEC_FP8_E4M3 && ql == 1 ? 2 : 1);
+    // Q slots take the LDS the second block would need. The 16x16x32 kernel: one
+    // block per compute unit over its blocks along z, within the block count the
+    // workspace size provides for
+    int nb = balanced_blocks(kv->num_kv_heads, num_blocks, kv->dtype == FDEC_FP8_E4M3 && ql == 1 ? 2 : 1);
+    if (mt16 && num_blocks == 0)
+        nb = std::min(balanced_blocks(kv->num_kv_heads, 0, 2),
+                      std::max(1, device_cus() / fdec::mt16_z_blocks(q_len, G, kv->num_kv_heads)));
     const BalLayout w = bal_layout(B, q_len * Hq, kv->head_dim, nb);
     if (!workspace || workspace_bytes < w.total)
         return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d blocks, got %zu", fn, w.total,
@@ -446,7 +461,9 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     p.po = reinterpret_cast<float *>(ws + w.po);
     p.nslots = nb + B;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = check_hip(fdec::launch_map_mfma_g4_balanced(p, nb, st), "balanced split: map launch"))) return rc;
+    if ((rc = check_hip(mt16 ? fdec::launch_map_mt16_balanced(p, nb, st) : fdec::launch_map_mfma_g4_balanced(p, nb, st),
+                        "balanced split: map launch")))
+        return rc;
     return check_hip(fdec::launch_merge_segments(p.po, p.pm, p.pd, p.seg_meta, B, Hq, p.nslots, nb, kv->head_dim, out,
                                                  lse, st, q_len),
                      "balanced split: merge launch");

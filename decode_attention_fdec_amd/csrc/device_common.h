@@ -125,6 +125,21 @@ template <int N> __device__ __forceinline__ void wait_vm_n(int k) {
     }
 }
 
+// Sum and inclusive prefix sum of an int over the wave.
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+    return __builtin_amdgcn_readfirstlane(x);  // the same in every lane
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
 // LDS address of a shared-memory pointer, for m0.
 __device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)ptr;

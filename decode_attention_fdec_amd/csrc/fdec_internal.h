@@ -84,6 +84,15 @@ hipError_t launch_map_mt16(const MapParams &p, int num_splits, hipStream_t strea
 inline bool mt16_eligible(int q_len, int G, int head_dim, bool fp8) {
     return !fp8 && head_dim == 128 && q_len * G >= 12;
 }
+// Blocks along z of the 16x16x32 kernels: kMtWaves waves per block, one per
+// (KV head, chunk of 16 or 32 query rows).
+int mt16_row_blocks(int rows);
+inline int mt16_z_blocks(int q_len, int G, int Hkv) {
+    const int rows = q_len * G, per = 16 * mt16_row_blocks(rows);
+    return (Hkv * ((rows + per - 1) / per) + kMtWaves - 1) / kMtWaves;
+}
+// Balanced split of the 16x16x32 multi-token kernel: grid (nblocks, 1, z blocks).
+hipError_t launch_map_mt16_balanced(const MapParams &p, int nblocks, hipStream_t stream);
 // Balanced split over nblocks blocks per group of KV heads (matrix-core kernel).
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t stream);
 

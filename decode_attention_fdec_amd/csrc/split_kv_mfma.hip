@@ -546,21 +546,6 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     }
 }
 
-// Sum and inclusive prefix sum of an int over the wave.
-__device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-    return __builtin_amdgcn_readfirstlane(x);  // the same in every lane
-}
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
-    return x;
-}
-
 // Balanced split: the 16-token tiles of all requests, in request order, are
 // cut into gridDim.x equal ranges, one per block (per group of KV heads). A
 // block streams its range as one sequence of tiles across request boundaries

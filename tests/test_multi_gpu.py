@@ -212,3 +212,57 @@ def test_multi_token_both_kernels_agree_with_oracle(q_len, monkeypatch):
         check(out, lse, ref_out, ref_lse, BF16, f"{path} q_len={q_len}")
         res[path] = out
     assert (res["16x16"] - res["4x4"]).abs().max().item() < 1e-4
+
+
+@pytest.mark.parametrize("G,q_len", [(8, 2), (1, 12), (2, 16), (4, 16), (4, 3)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_multi_token_balanced_any_group_size(G, q_len, paged):
+    Hkv = 2 if G == 8 else 4
+    lens = [700, 3, 1, 0, 64, 65, 2000]  # an empty request between others
+    if paged:
+        case = paged_case(340 + G + q_len, 7, G * Hkv, Hkv, 128, lens, 32, F16, extra_pages=3, pad="nan")
+    else:
+        case = contiguous_case(350 + G + q_len, 7, G * Hkv, Hkv, 128, lens, 2048, BF16, pad="nan")
+    q = multi_query(360 + G + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for nb in (1, 3, 40, 0):
+        out, lse = run_bal(case, q, nb)
+        check(out, lse, ref_out, ref_lse, case.dtype, f"balanced G={G} q_len={q_len} paged={paged} nb={nb}")
+
+
+def test_multi_token_balanced_many_requests():
+    # more than one wave's worth of requests in the block-range scan, many of them empty
+    rng = np.random.default_rng(370)
+    lens = [int(x) for x in rng.integers(0, 400, size=150)]
+    for i in range(0, 150, 7):
+        lens[i] = 0
+    case = paged_case(371, 150, 16, 4, 128, lens, 16, BF16, extra_pages=4, pad="nan")
+    q = multi_query(372, case, 4)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for nb in (5, 0):
+        out, lse = run_bal(case, q, nb)
+        check(out, lse, ref_out, ref_lse, BF16, f"balanced 150 requests nb={nb}")
+
+
+@pytest.mark.parametrize("q_len", [3, 8])
+def test_multi_token_balanced_both_kernels_agree(q_len, monkeypatch):
+    lens, pads = [300, 40, 19, 1000], [5, 38, 17, 999]
+    case = pad_left(paged_case(380 + q_len, 4, 16, 4, 128, lens, 16, BF16, extra_pages=2, pad="nan"), pads)
+    q = multi_query(381 + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    res = {}
+    for path in ("16x16", "4x4"):
+        if path == "4x4":
+            monkeypatch.setenv("FDEC_MULTI_PATH", "4x4")
+        out, lse = run_bal(case, q, 3)
+        check(out, lse, ref_out, ref_lse, BF16, f"balanced {path} q_len={q_len}")
+        res[path] = out
+    assert (res["16x16"] - res["4x4"]).abs().max().item() < 1e-4
+
+
+def test_multi_token_balanced_shapes_rejected():
+    case = contiguous_case(390, 2, 16, 8, 128, [10, 20], 32, BF16)  # G = 2, q_len 2: 4 rows per KV head
+    q = multi_query(391, case, 2)
+    with pytest.raises(F.FdecError) as e:
+        run_bal(case, q, 1)
+    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
