@@ -116,25 +116,35 @@ __device__ __forceinline__ void mt16_rows(const MapParams &p, int b, int g, int 
 
 // DMA of the 32-key tile at token t0 of request b (contiguous row crow), KV
 // head g, into K / V tiles kt / vt: 8 groups of 4 rows each; tile rows below lo
-// and above hi (outside the valid rows) repeat the nearest valid row.
+// and above hi (outside the valid rows) repeat the nearest valid row. t0 is a
+// multiple of 16 and pages hold a multiple of 16 rows, so each 16-row half of
+// the tile lies in one page: at most two page ids per tile, both read before
+// any address needs them.
 template <bool PAGED>
 __device__ __forceinline__ void mt16_issue(const MapParams &p, int b, int64_t crow, int g, int t0, int lo, int hi,
                                            uint8_t *kt, uint8_t *vt, int lane) {
     const uint32_t stok = (uint32_t)(p.s_token * 2);
+    int64_t half[2];  // element offset of token t0 + 16 h
+    if constexpr (PAGED) {
+        typedef const __attribute__((address_space(4))) int32_t *cpage_t;
+        const cpage_t row = (cpage_t)(p.page_table + (int64_t)b * p.max_pages);
+        const int t1 = t0 + 16;
+        const int i0 = p.page_shift >= 0 ? (t0 >> p.page_shift) : (t0 / p.page_size);
+        // the second half's page exists only when a valid row lies there
+        const int i1 = hi >= 16 ? (p.page_shift >= 0 ? (t1 >> p.page_shift) : (t1 / p.page_size)) : i0;
+        const int64_t pg0 = row[i0], pg1 = row[min(i1, p.max_pages - 1)];
+        half[0] = pg0 * p.s_outer + (int64_t)(t0 - i0 * p.page_size) * p.s_token + (int64_t)g * p.s_head;
+        half[1] = pg1 * p.s_outer + (int64_t)(t1 - i1 * p.page_size) * p.s_token + (int64_t)g * p.s_head;
+    } else {
+        half[0] = crow * p.s_outer + (int64_t)t0 * p.s_token + (int64_t)g * p.s_head;
+        half[1] = half[0] + 16 * p.s_token;
+    }
 #pragma unroll
     for (int gi = 0; gi < kMtKeys / 4; ++gi) {
         const int g0 = 4 * gi;
         const int rs = min(max(g0, lo), hi);  // the group's first source row
-        const int t = t0 + (rs & ~3);         // the 4-row group holding rs: one page
-        int64_t eoff;
-        if constexpr (PAGED) {
-            const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : (t / p.page_size);
-            typedef const __attribute__((address_space(4))) int32_t *cpage_t;
-            const int64_t page = ((cpage_t)(p.page_table + (int64_t)b * p.max_pages))[pidx];
-            eoff = page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head;
-        } else {
-            eoff = crow * p.s_outer + (int64_t)t * p.s_token + (int64_t)g * p.s_head;
-        }
+        const int h = rs >> 4;                // its half of the tile
+        const int64_t eoff = half[h] + (int64_t)((rs & ~3) - 16 * h) * p.s_token;
         const int r = g0 + (lane >> 4);
         const int src = min(max(r, lo), hi) - (rs & ~3);  // 0..3 within the group
         const uint32_t voff = (uint32_t)src * stok + 16u * (uint32_t)((lane & 15) ^ (r & 15));
@@ -439,9 +449,10 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const Ma
         int64_t crow;
     };
     auto load = [&](Cursor &c) {
-        c.L = ((ci_t)p.seq_lens)[c.b];
-        c.lp = p.leftpad ? ((ci_t)p.leftpad)[c.b] : 0;
-        c.crow = p.batch_idx ? ((ci_t)p.batch_idx)[c.b] : c.b;
+        c.b = __builtin_amdgcn_readfirstlane(c.b);
+        c.L = __builtin_amdgcn_readfirstlane(((ci_t)p.seq_lens)[c.b]);
+        c.lp = p.leftpad ? __builtin_amdgcn_readfirstlane(((ci_t)p.leftpad)[c.b]) : 0;
+        c.crow = p.batch_idx ? __builtin_amdgcn_readfirstlane(((ci_t)p.batch_idx)[c.b]) : c.b;
     };
     auto advance = [&](Cursor &c) {  // to the next request with tiles
         do {
@@ -451,6 +462,10 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const Ma
             c.T = c.L > c.lp ? (c.L - (c.lp & ~15) + kMtKeys - 1) / kMtKeys : 0;
         } while (c.T == 0);
     };
+    // uniform by construction; said so, the cursor's loads are scalar
+    b0 = __builtin_amdgcn_readfirstlane(b0);
+    P0 = __builtin_amdgcn_readfirstlane(P0);
+    T0 = __builtin_amdgcn_readfirstlane(T0);
     Cursor prod{b0, P0, T0, 0, 0, 0}, cons{b0, P0, T0, 0, 0, 0};
     load(prod);
     load(cons);
@@ -477,13 +492,17 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const Ma
     st.reset();
     issue(start);
     for (int x = start; x < end; ++x) {
-        if (x + 1 < end) issue(x + 1);
         if (x >= cons.P + cons.T) {
             flush(st, cons.b);
             st.reset();
             advance(cons);
             mt16_rows<RB>(p, cons.b, g, G, R, r0, cons.L, cons.lp, lane, qb, lim);
+            // before the next tile's DMA: this wait (on tile x, needed anyway)
+            // tells the compiler the Q loads are done, so it adds no wait of
+            // its own in the loop, which would also wait on the DMA ahead
+            __builtin_amdgcn_s_waitcnt(0);
         }
+        if (x + 1 < end) issue(x + 1);
         if (x + 1 < end)
             wait_vm<kMtDma>();
         else
