@@ -576,19 +576,31 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
 
     // ---- the block's tile range and its first request
-    const bool one_pass = p.B <= 64;  // valid-row counts stay in registers between the passes
-    // rows [leftpad, seq_len) of request j, counted from the 16-row tile holding
+    // With B <= 64 one scan does it all: lane j holds request j's length, first
+    // row and tile count, the total is the scan's last lane, and the first
+    // request's length and first row come from registers (no second load
+    // before the first DMA).
+    const bool one_pass = p.B <= 64;
+    // rows [leftpad, seq_len) of a request, counted from the 16-row tile holding
     // the first (0 when there are none)
+    auto valid_of = [](int L, int lp) -> int { return L > lp ? L - (lp & ~(kMT - 1)) : 0; };
     auto valid_rows = [&](int j) -> int {
         if (j >= p.B) return 0;
-        const int L = p.seq_lens[j], lp = p.leftpad ? p.leftpad[j] : 0;
-        return L > lp ? L - (lp & ~(kMT - 1)) : 0;
+        return valid_of(p.seq_lens[j], p.leftpad ? p.leftpad[j] : 0);
     };
-    const int E0 = valid_rows(lane);
-    int NT = 0;  // tiles of all requests
-    for (int c = 0; c < p.B; c += 64) {
-        const int E = one_pass ? E0 : valid_rows(c + lane);
-        NT += wave_sum_int((E + kMT - 1) / kMT);
+    int NT = 0;           // tiles of all requests
+    int Lv = 0, lpv = 0;  // one pass: request `lane`'s length and first row
+    int T1 = 0, incl1 = 0;  // one pass: its tiles and their inclusive scan
+    if (one_pass) {
+        if (lane < p.B) {
+            Lv = p.seq_lens[lane];
+            lpv = p.leftpad ? p.leftpad[lane] : 0;
+        }
+        T1 = (valid_of(Lv, lpv) + kMT - 1) / kMT;
+        incl1 = wave_incl_scan(T1, lane);
+        NT = __builtin_amdgcn_readlane(incl1, 63);
+    } else {
+        for (int c = 0; c < p.B; c += 64) NT += wave_sum_int((valid_rows(c + lane) + kMT - 1) / kMT);
     }
     const int NBe = min(NB, NT);  // working blocks
     // block holding tile x (x < NT), the last working block past the end
@@ -599,15 +611,9 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const int start = working ? (int)((int64_t)blk * NT / NBe) : 0;
     const int end = working ? (int)((int64_t)(blk + 1) * NT / NBe) : 0;
     const bool meta_writer = blockIdx.z == 0 && blockIdx.y == 0 && wv == 0;
-
-    int b0 = -1, P0 = 0, T0 = 0;  // first request of the range and its first tile
-    int carry = 0;                // tiles of the requests before this group of 64
-    for (int c = 0; c < p.B; c += 64) {
-        const int j = c + lane;
-        const int E = one_pass ? E0 : valid_rows(j);
-        const int T = (E + kMT - 1) / kMT;
-        const int incl = wave_incl_scan(T, lane);
-        const int P = carry + incl - T;  // first tile of request j
+    // (first slot, piece count) of request j, whose tiles are [P, P + T), when
+    // its first tile lies in this block's range
+    auto write_meta = [&](int j, int P, int T) {
         if (meta_writer && j < p.B) {
             const int first = NT > 0 ? block_of(P) : 0;
             if (first == blk) {
@@ -615,16 +621,50 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
                 p.seg_meta[2 * j + 1] = T > 0 ? block_of(P + T - 1) - first + 1 : 0;
             }
         }
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(working && j < p.B && T > 0 && P <= start && start < P + T);
-        if (b0 < 0 && mask) {
+    };
+
+    int b0 = -1, P0 = 0, T0 = 0;  // first request of the range and its first tile
+    int Lb0 = 0, lp0 = 0;         // its end row and first row
+    if (one_pass) {
+        const int P = incl1 - T1;
+        const uint64_t mask =
+            __builtin_amdgcn_ballot_w64(working && lane < p.B && T1 > 0 && P <= start && start < P + T1);
+        if (mask) {
             const int l = __builtin_ctzll(mask);
-            b0 = c + l;
+            b0 = l;
             P0 = __builtin_amdgcn_readlane(P, l);
-            T0 = __builtin_amdgcn_readlane(T, l);
+            T0 = __builtin_amdgcn_readlane(T1, l);
+            Lb0 = __builtin_amdgcn_readlane(Lv, l);
+            lp0 = __builtin_amdgcn_readlane(lpv, l);
         }
-        carry += __builtin_amdgcn_readlane(incl, 63);
+    } else {
+        int carry = 0;  // tiles of the requests before this group of 64
+        for (int c = 0; c < p.B; c += 64) {
+            const int j = c + lane;
+            const int T = (valid_rows(j) + kMT - 1) / kMT;
+            const int incl = wave_incl_scan(T, lane);
+            const int P = carry + incl - T;  // first tile of request j
+            write_meta(j, P, T);
+            const uint64_t mask =
+                __builtin_amdgcn_ballot_w64(working && j < p.B && T > 0 && P <= start && start < P + T);
+            if (b0 < 0 && mask) {
+                const int l = __builtin_ctzll(mask);
+                b0 = c + l;
+                P0 = __builtin_amdgcn_readlane(P, l);
+                T0 = __builtin_amdgcn_readlane(T, l);
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
+        }
+        if (b0 >= 0) {
+            typedef const __attribute__((address_space(4))) int32_t *clen0_t;
+            Lb0 = ((clen0_t)p.seq_lens)[b0];
+            lp0 = first_row(p, b0);
+        }
     }
-    if (!working) return;
+    if (!working) {
+        if (one_pass) write_meta(lane, incl1 - T1, T1);
+        return;
+    }
     // the scan's loads are done; saying so with a wait the compiler models
     // keeps it from waiting on them (and so on the DMA loads) further down
     __builtin_amdgcn_s_waitcnt(0);
@@ -649,7 +689,6 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
         c.crow = PAGED ? 0 : cache_row(p, c.b);
         c.seg += 1;
     };
-    const int Lb0 = slens[b0], lp0 = first_row(p, b0);
     const int64_t crow0 = PAGED ? 0 : cache_row(p, b0);
     Cursor prod{b0, P0, T0, Lb0, lp0, 0, crow0}, cons{b0, P0, T0, Lb0, lp0, 0, crow0};
     uint8_t *wl = lds[wv];
@@ -731,6 +770,8 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
                               p.scale_log2 * kd, lane, st);
     }
     flush(st, cons.b, vd);
+    // one pass: the request metadata goes out last, off the path to the first DMA
+    if (one_pass) write_meta(lane, incl1 - T1, T1);
 }
 
 // Instantiations: q / compute type DT (0 fp16, 1 bf16), paged or not, KV
