@@ -63,6 +63,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each group of 8
 constexpr int kDppRowRor8 = 0x128;    // rotate right by 8 within 16 (= xor 8)
+constexpr int kDppRowRor4 = 0x124;    // rotate right by 4 within 16
 
 // Sum over each aligned group of 8 lanes; every lane of the group gets the sum.
 __device__ __forceinline__ float sum8(float x) {
@@ -74,13 +75,47 @@ __device__ __forceinline__ float sum8(float x) {
 
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Reductions without the LDS crossbar: DPP within rows of 16 lanes, then the
+// gfx950 row swaps (v_permlane16_swap, v_permlane32_swap) across rows. Each
+// step adds two values that every lane of the pair sees in one or the other
+// order, so every lane of a reduced set ends with the same bits.
+
+// x combined over lanes L, L ^ 16, L ^ 32, L ^ 48.
+template <class Op> __device__ __forceinline__ float across_rows(float x, Op op) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+// x combined over the lanes of L's row with the same L & 3 (rotations by 8,
+// then by 4: the pairs {j, j + 8} first, so every lane of the set gets the
+// same bits).
+template <class Op> __device__ __forceinline__ float within_row_mod4(float x, Op op) {
+    x = op(x, dpp<kDppRowRor8>(x));
+    return op(x, dpp<kDppRowRor4>(x));
+}
+struct AddOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// Over the 16 lanes with the same L & 3 (the four query heads of the
+// matrix-core map kernels' state layout).
+__device__ __forceinline__ float sum_mod4(float x) { return across_rows(within_row_mod4(x, AddOp{}), AddOp{}); }
+__device__ __forceinline__ float max_mod4(float x) { return across_rows(within_row_mod4(x, MaxOp{}), MaxOp{}); }
+
+// Over the whole wave: quad butterfly, then the row and cross-row steps.
 __device__ __forceinline__ float wave_max(float x) {
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor(x, m));
-    return x;
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    return max_mod4(x);
 }
 __device__ __forceinline__ float wave_sum(float x) {
-    for (int m = 32; m >= 1; m >>= 1) x += shfl_xor(x, m);
-    return x;
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    return sum_mod4(x);
 }
 
 // max of two floats that are already canonical (results of arithmetic): one

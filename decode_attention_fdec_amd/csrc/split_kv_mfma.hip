@@ -394,12 +394,7 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
 __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, float *po0, float *pm0, float *pd0,
                                             int64_t hs, float vscale = 1.0f) {
     constexpr int D = 128;
-    float lt = st.l, tt = st.t;
-#pragma unroll
-    for (int x = 4; x <= 32; x <<= 1) {
-        lt += shfl_xor(lt, x);
-        tt = fmax_nc(tt, shfl_xor(tt, x));
-    }
+    const float lt = sum_mod4(st.l), tt = max_mod4(st.t);
     const float f_own = (tt == kNegInf) ? 0.0f : fexp2(st.m - tt);
     f32x4_v fs;
 #pragma unroll
