@@ -2,7 +2,8 @@
 // (gfx950). Same contract as map_kernel in split_kv.hip (the FlashDecoding map
 // stage: per split the local max m_i, the local sum of exponentials d_i and the
 // unnormalised output O~_i -- lpnh.cn explainer §2 stage 1), for G = Hq/Hkv = 4,
-// D = 128, without append; K/V in fp16/bf16 or in float8 e4m3fn (bf16 queries).
+// D = 128; K/V in fp16/bf16 or in float8 e4m3fn (bf16 queries); the in-kernel
+// append with NeoX rotary on fp16/bf16 caches (map_kernel_mfma_g4_app).
 //
 // Packing the four query heads of a KV head makes q.K^T a dense contraction for
 // the 16-block v_mfma_f32_4x4x4_16b_{bf16,f16} (M = 4 = G, no padding; lpnh §3
@@ -251,9 +252,10 @@ struct MfmaSoftmax {
 // the last token); the rest are masked. The K pieces, their float8 conversion
 // and the V^T reads are shared by the QL tokens. kl / vl: the K and V tiles in
 // LDS.
-template <int DT, int KF, int QL>
+template <int DT, int KF, int QL, bool QLO = false>
 __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, const uint2 (&qb)[QL][8], int nskip,
-                                          const int (&nvalid)[QL], float scale_log2, int lane, MfmaSoftmax (&st)[QL]) {
+                                          const int (&nvalid)[QL], float scale_log2, int lane, MfmaSoftmax (&st)[QL],
+                                          const uint2 (*qlo)[8] = nullptr) {
     using E = Elem<DT>;
     const int dq = lane >> 4;
     const int rk = lane & 15;  // S^T reads: token L & 15, pieces 4 dq .. 4 dq + 3
@@ -275,6 +277,10 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
             for (int j = 0; j < QL; ++j) {
                 s[j] = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qb[j][2 * c], s[j]);
                 s1[j] = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qb[j][2 * c + 1], s1[j]);
+                if constexpr (QLO) {  // q = hi + lo: the second 16-bit part of an fp32 query
+                    s[j] = Mfma4<DT>::template run<0, 0>(make_uint2(kr.x, kr.y), qlo[j][2 * c], s[j]);
+                    s1[j] = Mfma4<DT>::template run<0, 0>(make_uint2(kr.z, kr.w), qlo[j][2 * c + 1], s1[j]);
+                }
             }
         }
     } else {
@@ -522,6 +528,145 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     if (QL > 1 || p.counters == nullptr) return;  // single-kernel merge: single-query decode only
 
     // ---- single-kernel merge (as in map_kernel)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (prev == (int)gridDim.x - 1);
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_flag = last;
+    }
+    __syncthreads();
+    if (!sm_flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {
+        const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
+        merge_states_wave<D>(p.po + bh * p.s_total * D, p.pm + bh * p.s_total, p.pd + bh * p.s_total,
+                             p.s_total, p.out + bh * D, p.lse ? p.lse + bh : nullptr, lane);
+    }
+}
+
+// Decode with an in-kernel append (the cookbook's §3.3-3.4: the new token's
+// k / v are written at row cache_seqlens[b] and attended to, with GPT-NeoX
+// rotary of q and k_new at the new token's position when tables are given),
+// uniform splits, single query, fp16 / bf16 caches. Every block rotates q in
+// fp32 (in LDS) and feeds it to S^T = K Q^T as two 16-bit parts, hi + lo (the
+// low part is q - hi rounded again: about 16 significant bits together); the
+// block owning row cache_seqlens[b] rounds the rotated k_new once to the cache
+// type, writes it and v_new into the cache, and waits for those stores before
+// its first DMA, which may read the row back.
+template <int DT, bool PAGED>
+__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(const MapParams p) {
+    constexpr int D = 128, G = 4, KF = 0;
+    constexpr int NS = Ring<KF>::kSlots;
+    using E = Elem<DT>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][2][G * D * 2];  // hi, lo
+    __shared__ float fl[kMapMfmaWaves][(G + 1) * D];                                      // q, then k_new (fp32)
+    __shared__ int sm_flag;
+
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.z * p.heads_per_block + wv;
+    const int hq0 = g * G;
+    const int c_app = p.seq_lens[b];
+    const int L = c_app + 1;
+    const int lp = first_row(p, b);
+    const int t_begin = (lp & ~(kMT - 1)) + split * p.chunk;
+    const int t_end = min(t_begin + p.chunk, L);
+    const bool owner = t_begin <= c_app && c_app < t_begin + p.chunk;
+    const int64_t crow = PAGED ? 0 : cache_row(p, b);
+
+    // ---- q (and k_new in the owner) in fp32, rotated
+    float *qs = fl[wv];
+    float *ks = qs + G * D;
+    const uint16_t *qsrc = reinterpret_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hq + hq0) * D;
+    const uint16_t *ksrc = reinterpret_cast<const uint16_t *>(p.k_new) + ((int64_t)b * p.Hkv + g) * D;
+    for (int i = lane; i < G * D; i += 64) qs[i] = E::lo((uint32_t)qsrc[i]);
+    if (owner)
+        for (int i = lane; i < D; i += 64) ks[i] = E::lo((uint32_t)ksrc[i]);
+    __builtin_amdgcn_wave_barrier();
+    if (p.mode == kAppendRope) {
+        const int half = p.rotary_dim >> 1;
+        // the new row's position among the valid rows
+        const float *cs = p.rope_cos + (int64_t)(c_app - lp) * half;
+        const float *sn = p.rope_sin + (int64_t)(c_app - lp) * half;
+        const int nvec = owner ? G + 1 : G;
+        for (int i = lane; i < nvec * half; i += 64) {
+            const int h = i / half, j = i - h * half;
+            float *x = qs + h * D;
+            const float c = cs[j], sv = sn[j];
+            const float x0 = x[j], x1 = x[j + half];
+            x[j] = x0 * c - x1 * sv;
+            x[j + half] = x0 * sv + x1 * c;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    // q as hi + lo in the layout read_q expects ([head][d], 16-bit)
+    uint16_t *qh = reinterpret_cast<uint16_t *>(qlds[wv][0]);
+    uint16_t *ql = reinterpret_cast<uint16_t *>(qlds[wv][1]);
+    for (int i = lane; i < G * D; i += 64) {
+        const float x = qs[i];
+        const uint16_t h = E::from_float(x);
+        qh[i] = h;
+        ql[i] = E::from_float(x - E::lo((uint32_t)h));
+    }
+    if (owner) {
+        const int64_t off = token_offset<PAGED, KF>(p, b, crow, g, c_app);
+        uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k) + off);
+        uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v) + off);
+        const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)b * p.Hkv + g) * D;
+        for (int i = lane; i < D; i += 64) {
+            kd[i] = E::from_float(ks[i]);  // k_new itself when not rotated: exact
+            vd[i] = vsrc[i];
+        }
+    }
+    // every load and store above is done (the owner's row is in L2 before its
+    // DMA reads it back; no earlier load of this kernel cached the row), and a
+    // wait the compiler models keeps it from waiting on the DMA loads below
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    uint2 qb[1][8], qlo[1][8];
+    read_q(qlds[wv][0], lane, qb[0]);
+    read_q(qlds[wv][1], lane, qlo[0]);
+
+    // ---- stream the split's tiles (as mfma_segment, one query token)
+    const int t_lo = max(t_begin, lp);
+    const int ntiles = t_end > t_lo ? (t_end - t_begin + kMT - 1) / kMT : 0;
+    const int nskip0 = t_lo - t_begin;
+    const uint32_t stok = (uint32_t)(p.s_token * 2);
+    auto tile_offset = [&](int tile) { return token_offset<PAGED, KF>(p, b, crow, g, t_begin + tile * kMT); };
+    auto stage = [&](int tile, int64_t off) {
+        uint32_t kl, vl;
+        slot_dma_addrs<KF>(lds[wv], tile % NS, kl, vl);
+        stage_tile<KF>(p.k + off, p.v + off, kl, vl, tile == 0 ? nskip0 : 0, t_end - (t_begin + tile * kMT), stok,
+                       lane);
+    };
+    MfmaSoftmax st[1];
+    st[0].reset();
+    const int npro = min(NS - 1, ntiles);
+    for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
+    int64_t noff = (NS - 1 < ntiles) ? tile_offset(NS - 1) : 0;
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int ahead = tile + NS - 1;
+        if (ahead < ntiles) {
+            stage(ahead, noff);
+            if (ahead + 1 < ntiles) noff = tile_offset(ahead + 1);
+        }
+        wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, ntiles - 1 - tile));
+        const int slot = tile % NS;
+        const int nv[1] = {t_end - (t_begin + tile * kMT)};
+        mfma_tile<DT, KF, 1, true>(Ring<KF>::k_tile(lds[wv], slot), Ring<KF>::v_tile(lds[wv], slot), qb,
+                                   tile == 0 ? nskip0 : 0, nv, p.scale_log2, lane, st, qlo);
+    }
+    const int64_t st0 = ((int64_t)b * p.Hq + hq0) * p.s_total + p.s_offset + split;
+    write_state(st[0], lane, p.po + st0 * D, p.pm + st0, p.pd + st0, p.s_total);
+
+    if (p.counters == nullptr) return;
+
+    // ---- single-kernel merge (as in map_kernel_mfma_g4)
     __syncthreads();
     if (threadIdx.x == 0) {
         int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
@@ -809,6 +954,22 @@ hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStrea
 }
 
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
+    if (p.mode != kPlain) {  // append (single query, 16-bit caches)
+        if (p.q_len != 1 || p.kv_fp8) return hipErrorInvalidValue;
+        dim3 grid(S, p.B, p.Hkv / p.heads_per_block), block(64 * p.heads_per_block);
+        if (p.dtype == 0) {
+            if (p.page_table)
+                hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, true>), grid, block, 0, st, p);
+            else
+                hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, false>), grid, block, 0, st, p);
+        } else {
+            if (p.page_table)
+                hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, true>), grid, block, 0, st, p);
+            else
+                hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, false>), grid, block, 0, st, p);
+        }
+        return hipGetLastError();
+    }
     const int ql = mfma_tokens_per_wave(p.q_len);
     if (p.q_groups != (p.q_len + ql - 1) / ql) return hipErrorInvalidValue;
     dim3 grid(S, p.B * p.q_groups, p.Hkv / p.heads_per_block);
