@@ -547,9 +547,10 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     }
 }
 
-// Decode with an in-kernel append (the cookbook's §3.3-3.4: the new token's
-// k / v are written at row cache_seqlens[b] and attended to, with GPT-NeoX
-// rotary of q and k_new at the new token's position when tables are given),
+// Decode with an in-kernel append (flash-attn "Inference Cookbook / 推理优化"
+// page §3.3-3.4: the new token's k / v are written at row cache_seqlens[b] and
+// attended to, with GPT-NeoX rotary of q and k_new at the new token's position
+// when tables are given),
 // uniform splits, single query, fp16 / bf16 caches. Every block rotates q in
 // fp32 (in LDS) and feeds it to S^T = K Q^T as two 16-bit parts, hi + lo (the
 // low part is q - hi rounded again: about 16 significant bits together); the
