@@ -619,8 +619,9 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
         uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k) + off);
         uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v) + off);
         const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)b * p.Hkv + g) * D;
+        const bool rotated = p.mode == kAppendRope;
         for (int i = lane; i < D; i += 64) {
-            kd[i] = E::from_float(ks[i]);  // k_new itself when not rotated: exact
+            kd[i] = rotated ? E::from_float(ks[i]) : ksrc[i];  // unrotated: the bits of k_new
             vd[i] = vsrc[i];
         }
     }
