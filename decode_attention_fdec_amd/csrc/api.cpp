@@ -198,7 +198,7 @@ int check_fp8(const char *fn, const fdec_kv *kv, const fdec::MapParams &p, const
     if (append) return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: append into a float8 cache is not built", fn);
     if (!p.mfma)
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: float8 caches need Hq = 4 Hkv, head_dim 128, page_size a multiple of 16 "
+                         "%s: float8 caches need Hq = 4 Hkv or 8 Hkv, head_dim 128, page_size a multiple of 16 "
                          "(and the matrix-core map kernel)", fn);
     return FDEC_OK;
 }
@@ -321,7 +321,7 @@ extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const 
     const int G = Hq / kv->num_kv_heads;
     const bool mt16 = fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
                       (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
-    if (!p.mfma && !mt16)
+    if (!mt16 && !(p.mfma && (G == 4 || q_len == 1)))
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
                          "%s: needs head_dim 128 and either Hq = 4 Hkv or q_len * Hq / Hkv >= 12 (16-bit caches)",
                          fn);
@@ -429,7 +429,7 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     // several query tokens: the 16x16x32 kernel when its row blocks fill
     const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
                       (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
-    if (!p.mfma && !mt16)
+    if (!mt16 && !(p.mfma && G == 4))
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
                          "%s: needs head_dim 128, page_size a multiple of 16 and Hq = 4 Hkv (q_len * Hq / Hkv >= 12 "
                          "with several tokens and 16-bit caches)",
@@ -637,7 +637,8 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     cp.dtype = kv->dtype;
 
     fdec::MapParams pb = map_params(q, B, Hq, kv, suffix_lens, 1, softmax_scale, nullptr);
-    if (pb.mfma && (int64_t)B * (((int64_t)cap + 15) / 16) < (int64_t(1) << 31)) {
+    if (pb.mfma && cascade_balanced_shape(Hq, kv->num_kv_heads, kv->head_dim) &&
+        (int64_t)B * (((int64_t)cap + 15) / 16) < (int64_t(1) << 31)) {
         // suffixes on the balanced split, then one merge of prefix states and suffix pieces
         const CascBalLayout w = casc_bal_layout(B, Hq, kv->head_dim, sp, ss);
         if (!workspace || workspace_bytes < w.total)

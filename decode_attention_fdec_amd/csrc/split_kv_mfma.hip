@@ -418,14 +418,15 @@ __device__ __forceinline__ void write_state(const MfmaSoftmax &st, int lane, flo
 }
 
 // One wave's pass over tokens [t_lo, t_end) of request b for KV head g (its
-// four query heads), in 16-token tiles from t_begin (a multiple of 16, <= t_lo:
+// four query heads; with HG, its eight query heads as QL = 2 groups of four,
+// each group taking the place of a query token with no causal limit), in 16-token tiles from t_begin (a multiple of 16, <= t_lo:
 // tiles of a paged cache then stay on one page), for nq <= QL query tokens
 // ti0 .. ti0 + nq - 1 of the request: token i sees rows up to
 // L - q_len + i (causal), i.e. its part of the segment ends at
 // min(t_end, L - q_len + i + 1). Token j's state goes to po0[j] / pm0[j] /
 // pd0[j] (+ i hs per head). wl / qslot are the wave's LDS: its ring (Ring<KF>)
 // and QL KB of Q.
-template <int DT, bool PAGED, int KF, int QL>
+template <int DT, bool PAGED, int KF, int QL, bool HG = false>
 __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, uint8_t *qslot, int b, int g, int lane,
                                              int t_begin, int t_lo, int t_end, int L, int ti0, int nq,
                                              float *const (&po0)[QL], float *const (&pm0)[QL],
@@ -453,7 +454,12 @@ __device__ __forceinline__ void mfma_segment(const MapParams &p, uint8_t *wl, ui
 #pragma unroll
     for (int j = 0; j < QL; ++j) {
         st[j].reset();
-        if (j < nq) stage_q(p, b * p.q_len + ti0 + j, g, qslot + 1024 * j, lane);
+        if (j < nq) {
+            if constexpr (HG)  // group j of 4 query heads of a G = 8 KV head: heads 8 g + 4 j ..
+                stage_q(p, b, 2 * g + j, qslot + 1024 * j, lane);
+            else
+                stage_q(p, b * p.q_len + ti0 + j, g, qslot + 1024 * j, lane);
+        }
     }
     // prologue: the first NS - 1 tiles
     const int npro = min(NS - 1, ntiles);
@@ -528,6 +534,60 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     if (QL > 1 || p.counters == nullptr) return;  // single-kernel merge: single-query decode only
 
     // ---- single-kernel merge (as in map_kernel)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (prev == (int)gridDim.x - 1);
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_flag = last;
+    }
+    __syncthreads();
+    if (!sm_flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {
+        const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
+        merge_states_wave<D>(p.po + bh * p.s_total * D, p.pm + bh * p.s_total, p.pd + bh * p.s_total,
+                             p.s_total, p.out + bh * D, p.lse ? p.lse + bh : nullptr, lane);
+    }
+}
+
+// GQA groups of eight query heads (single query): one wave per KV head runs
+// its eight heads as two groups of four through the same tiles (the
+// multi-token path of mfma_tile with QL = 2, the groups in place of query
+// tokens, no causal limit), so every staged K/V tile and every K piece read
+// from LDS serves eight query heads.
+template <int DT, bool PAGED, int KF>
+__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g8(const MapParams p) {
+    constexpr int D = 128, G = 8;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][2][4 * D * 2];
+    __shared__ int sm_flag;
+
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.z * p.heads_per_block + wv;
+    const int hq0 = g * G;
+    const int L = p.seq_lens[b];
+    const int lp = first_row(p, b);
+    const int t_begin = (lp & ~(kMT - 1)) + split * p.chunk;
+    const int t_end = min(t_begin + p.chunk, L);
+    float *po0[2], *pm0[2], *pd0[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t st0 = ((int64_t)b * p.Hq + hq0 + 4 * j) * p.s_total + p.s_offset + split;
+        po0[j] = p.po + st0 * D;
+        pm0[j] = p.pm + st0;
+        pd0[j] = p.pd + st0;
+    }
+    mfma_segment<DT, PAGED, KF, 2, true>(p, lds[wv], &qlds[wv][0][0], b, g, lane, t_begin, max(t_begin, lp), t_end,
+                                         L, 0, 2, po0, pm0, pd0, p.s_total);
+
+    if (p.counters == nullptr) return;
+
+    // ---- single-kernel merge (as in map_kernel_mfma_g4)
     __syncthreads();
     if (threadIdx.x == 0) {
         int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
@@ -941,6 +1001,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
 int mfma_tokens_per_wave(int q_len) { return q_len <= 1 ? 1 : q_len == 2 ? 2 : 4; }
 
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
+    if (p.Hq != 4 * p.Hkv) return hipErrorInvalidValue;
     const int ql = mfma_tokens_per_wave(p.q_len);
     if (p.q_groups != (p.q_len + ql - 1) / ql) return hipErrorInvalidValue;
     dim3 grid(nblocks, p.q_groups, p.Hkv / p.heads_per_block);
@@ -956,6 +1017,12 @@ hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStrea
 }
 
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
+    if (p.Hq == 8 * p.Hkv) {  // groups of eight query heads: single query, no append
+        if (p.q_len != 1 || p.mode != kPlain) return hipErrorInvalidValue;
+        dim3 grid(S, p.B, p.Hkv / p.heads_per_block), block(64 * p.heads_per_block);
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g8, )
+        return hipGetLastError();
+    }
     if (p.mode != kPlain) {  // append (single query, 16-bit caches)
         if (p.q_len != 1 || p.kv_fp8) return hipErrorInvalidValue;
         dim3 grid(S, p.B, p.Hkv / p.heads_per_block), block(64 * p.heads_per_block);

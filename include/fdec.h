@@ -93,10 +93,12 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  * capacity < 2^31.
  * Float8 caches (dtype FDEC_FP8_E4M3): element (b, t, g, d) stands for its
  * e4m3 value times k_descale[b*Hkv + g] (K) or v_descale[b*Hkv + g] (V); a NULL
- * descale is 1. Queries are bf16. Built for Hq = 4 Hkv, head_dim 128, page_size
- * a multiple of 16 (or contiguous), without append, in fdec_decode,
- * fdec_decode_partials and fdec_decode_balanced; other calls and shapes return
- * FDEC_ERR_UNSUPPORTED. The partial states then already include V's descale.
+ * descale is 1. Queries are bf16. Built for head_dim 128, page_size a multiple
+ * of 16 (or contiguous), without append: Hq = 4 Hkv in fdec_decode,
+ * fdec_decode_partials, fdec_decode_balanced and fdec_decode_multi, and
+ * Hq = 8 Hkv in fdec_decode and fdec_decode_partials; other calls and shapes
+ * return FDEC_ERR_UNSUPPORTED. The partial states then already include V's
+ * descale.
  */
 typedef struct fdec_kv {
     void *k;
@@ -248,8 +250,9 @@ int fdec_merge_states(const float *part_o, const float *part_m, const float *par
  *   out  device [B, q_len, Hq, D] fp32; lse device [B, Hq, q_len] fp32 or NULL
  *        ([cookbook] §3.5 softmax_lse shape (batch, heads, seqlen_q))
  *   num_splits, softmax_scale as in fdec_decode (splits over the request's rows)
- *   1 <= q_len <= FDEC_MAX_QLEN. Built for Hq = 4 Hkv, head_dim 128, page_size a
- *   multiple of 16 or contiguous, all cache dtypes (FDEC_ERR_UNSUPPORTED
+ *   1 <= q_len <= FDEC_MAX_QLEN. Built for head_dim 128, page_size a multiple
+ *   of 16 or contiguous, and Hq = 4 Hkv (all cache dtypes), q_len * Hq / Hkv >= 12
+ *   (fp16 / bf16 caches) or Hq = 8 Hkv with q_len = 1 (FDEC_ERR_UNSUPPORTED
  *   otherwise); no append. workspace >= fdec_workspace_size(B * q_len, Hq, Hkv,
  *   head_dim, S). q_len = 1 gives fdec_decode's two-kernel result bitwise.
  */

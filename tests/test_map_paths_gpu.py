@@ -1,7 +1,7 @@
 """Both split-KV map kernels against the fp64 oracle, through the C ABI.
 
-GQA groups of four query heads at D = 128 (the common grouped-query shape) run
-on the matrix-core map kernel; FDEC_MAP_PATH=vector forces the vector kernel
+GQA groups of four or eight query heads at D = 128 run on the matrix-core map
+kernels; FDEC_MAP_PATH=vector forces the vector kernel
 for the same inputs. The cases cover every tile position of a ragged tail
 (lengths around multiples of 16 and 32), empty requests, pages of 16, 32 and
 48 tokens, 1, 3 and 4 KV heads per block, both element types, and a head
@@ -49,6 +49,11 @@ CASES = [
                                        pad="nan")),
     ("paged32_bf16", lambda: paged_case(67, 3, 32, 8, 128, [64, 95, 1500], 32, BF16, extra_pages=3, pad="nan")),
     ("paged48_f16", lambda: paged_case(68, 3, 8, 2, 128, [48, 49, 480], 48, F16, extra_pages=2, pad="nan")),
+    # groups of eight query heads (two groups of four per wave on matrix cores)
+    ("g8_contig_bf16", lambda: contiguous_case(69, 3, 64, 8, 128, [1, 33, 3000], 3072, BF16, pad="nan")),
+    ("g8_paged16_f16", lambda: paged_case(70, 4, 16, 2, 128, [0, 16, 17, 1234], 16, F16, extra_pages=3,
+                                          pad="nan")),
+    ("g8_contig_hkv3", lambda: contiguous_case(71, 2, 24, 3, 128, [700, 65], 768, BF16, pad="nan")),
 ]
 
 

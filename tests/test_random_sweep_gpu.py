@@ -50,7 +50,7 @@ def draw(i):
         kinds += ["multi"]
     kind = str(r.choice(kinds))
     dtypes = [F16, BF16]
-    if G == 4 and D == 128 and kind != "append":
+    if D == 128 and kind != "append" and (G == 4 or (G == 8 and kind in ("two", "fused"))):
         dtypes.append(FP8)
     dtype = dtypes[int(r.integers(0, len(dtypes)))]
     ps = int(r.choice([0, 16, 32, 64]))
