@@ -429,10 +429,10 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     // several query tokens: the 16x16x32 kernel when its row blocks fill
     const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
                       (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
-    if (!mt16 && !(p.mfma && G == 4))
+    if (!mt16 && !(p.mfma && (G == 4 || (G == 8 && q_len == 1))))
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: needs head_dim 128, page_size a multiple of 16 and Hq = 4 Hkv (q_len * Hq / Hkv >= 12 "
-                         "with several tokens and 16-bit caches)",
+                         "%s: needs head_dim 128, page_size a multiple of 16 and Hq = 4 Hkv (8 Hkv with one query "
+                         "token; q_len * Hq / Hkv >= 12 with several tokens and 16-bit caches)",
                          fn);
     if (B == 0) return FDEC_OK;
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);

@@ -35,11 +35,12 @@ struct CostModel {
 // G = 4 runs on the matrix-core kernel: blocks of up to 4 KV heads, one block
 // per CU (a second resident block adds no bandwidth), about 42 GB/s per block
 // below saturation and 5.9 TB/s in aggregate (128k-token GQA: 93 us at 256
-// blocks, 107 us at 128). Other shapes run on the vector kernel, modelled per
-// KV head (its blocks stream each head independently).
+// blocks, 107 us at 128). G = 8 runs on its matrix-core kernel with the same
+// blocks (128k tokens: 98 us at 256 blocks). Other shapes run on the vector
+// kernel, modelled per KV head (its blocks stream each head independently).
 CostModel model_for(int Hq, int Hkv) {
     CostModel cm;
-    if (Hq == 4 * Hkv) {
+    if (Hq == 4 * Hkv || Hq == 8 * Hkv) {
         int hpb = 1;
         for (int w = 4; w > 1; --w)
             if (Hkv % w == 0) {

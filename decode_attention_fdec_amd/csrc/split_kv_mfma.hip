@@ -760,20 +760,22 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
 // With fewer tiles than blocks, only the first (tiles) blocks take work, so
 // every working block has at least one tile and no slot of a request is left
 // unwritten. Every wave scans seq_lens itself (no block barrier).
-template <int DT, bool PAGED, int KF, int QL>
+template <int DT, bool PAGED, int KF, int QL, bool HG = false>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
     constexpr int D = 128, G = 4;
     constexpr int NS = Ring<KF>::kSlots;
+    static_assert(!HG || QL == 2, "groups of eight query heads run as two groups of four");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
     // Q of the pieces in flight (at most one per ring slot), QL query tokens each
+    // (with HG: the two groups of four query heads of a G = 8 KV head, one query)
     __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][NS][QL][G * D * 2];
     // query tokens ti0 .. ti0 + nq - 1 of every request (grid y: groups of QL)
-    const int ti0 = blockIdx.y * QL, nq = min(QL, p.q_len - ti0);
+    const int ti0 = HG ? 0 : blockIdx.y * QL, nq = HG ? 2 : min(QL, p.q_len - ti0);
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = blockIdx.z * p.heads_per_block + wv;
-    const int hq0 = g * G;
+    const int hq0 = g * (HG ? 2 * G : G);
     const int NB = gridDim.x, blk = blockIdx.x;
     const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
 
@@ -897,8 +899,13 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     // Q of request b's query tokens into ring slot qs
     auto stage_qs = [&](int b, int qs) {
 #pragma unroll
-        for (int j = 0; j < QL; ++j)
-            if (j < nq) stage_q(p, b * p.q_len + ti0 + j, g, qlds[wv][qs][j], lane);
+        for (int j = 0; j < QL; ++j) {
+            if (j >= nq) continue;
+            if constexpr (HG)
+                stage_q(p, b, 2 * g + j, qlds[wv][qs][j], lane);
+            else
+                stage_q(p, b * p.q_len + ti0 + j, g, qlds[wv][qs][j], lane);
+        }
     };
     auto read_qs = [&](int qs, uint2 (&qb)[QL][8]) {
 #pragma unroll
@@ -916,7 +923,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
 #pragma unroll
         for (int j = 0; j < QL; ++j) {
             if (j >= nq) continue;
-            const int64_t s0 = ((int64_t)(ti0 + j) * p.Hq + hq0) * p.nslots + blk + b;
+            const int64_t s0 = (HG ? (int64_t)(hq0 + 4 * j) : ((int64_t)(ti0 + j) * p.Hq + hq0)) * p.nslots + blk + b;
             write_state(st[j], lane, p.po + s0 * D, p.pm + s0, p.pd + s0, p.nslots, vd);
         }
     };
@@ -967,7 +974,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
         const int t0 = (cons.lp & ~(kMT - 1)) + (x - cons.P) * kMT;
         int nv[QL];  // token ti0 + j sees rows up to L - q_len + ti0 + j (causal)
 #pragma unroll
-        for (int j = 0; j < QL; ++j) nv[j] = j < nq ? cons.L - p.q_len + ti0 + j + 1 - t0 : 0;
+        for (int j = 0; j < QL; ++j) nv[j] = j < nq ? (HG ? cons.L : cons.L - p.q_len + ti0 + j + 1) - t0 : 0;
         mfma_tile<DT, KF, QL>(Ring<KF>::k_tile(wl, slot), Ring<KF>::v_tile(wl, slot), qb, max(cons.lp - t0, 0), nv,
                               p.scale_log2 * kd, lane, st);
     }
@@ -1001,6 +1008,13 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
 int mfma_tokens_per_wave(int q_len) { return q_len <= 1 ? 1 : q_len == 2 ? 2 : 4; }
 
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
+    if (p.Hq == 8 * p.Hkv) {  // two groups of four query heads per wave, single query
+        if (p.q_len != 1 || p.q_groups != 1) return hipErrorInvalidValue;
+        dim3 grid(nblocks, 1, p.Hkv / p.heads_per_block);
+        dim3 block(64 * p.heads_per_block);
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g4_bal, , 2, true)
+        return hipGetLastError();
+    }
     if (p.Hq != 4 * p.Hkv) return hipErrorInvalidValue;
     const int ql = mfma_tokens_per_wave(p.q_len);
     if (p.q_groups != (p.q_len + ql - 1) / ql) return hipErrorInvalidValue;

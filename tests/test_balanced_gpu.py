@@ -11,7 +11,7 @@ import torch
 import decode_attention_fdec_amd as F
 import oracle
 from helpers import assert_parity, oracle_decode, to_dev
-from synth import BF16, F16, contiguous_case, paged_case, workload
+from synth import BF16, F16, FP8, contiguous_case, paged_case, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,7 @@ def _gpu(fdec):
 def run(case, num_blocks):
     d = to_dev(case)
     out, lse = F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"],
-                                 num_blocks=num_blocks)
+                                 num_blocks=num_blocks, k_descale=d["k_descale"], v_descale=d["v_descale"])
     torch.cuda.synchronize()
     return out, lse
 
@@ -40,6 +40,12 @@ CASES = [
     ("many_short_f16", lambda: contiguous_case(84, 70, 4, 1, 128, [(7 * i) % 53 for i in range(70)], 64, F16,
                                                pad="nan")),
     ("all_empty_bf16", lambda: contiguous_case(85, 3, 8, 2, 128, [0, 0, 0], 32, BF16, pad="nan")),
+    # groups of eight query heads per KV head
+    ("g8_paged16_bf16", lambda: paged_case(87, 5, 64, 8, 128, [2500, 0, 33, 1, 900], 16, BF16, extra_pages=3,
+                                           pad="nan")),
+    ("g8_contig_f16", lambda: contiguous_case(88, 3, 16, 2, 128, [1000, 17, 2000], 2048, F16, pad="nan")),
+    ("g8_paged32_fp8", lambda: paged_case(89, 4, 32, 4, 128, [700, 64, 0, 1500], 32, FP8, extra_pages=2,
+                                          pad="nan")),
 ]
 
 

@@ -47,10 +47,10 @@ def draw(i):
     if G == 4 and D == 128:
         kinds += ["balanced", "multi", "multi"]
     elif D == 128 and G * 3 >= 12:
-        kinds += ["multi"]
+        kinds += ["multi", "balanced"]
     kind = str(r.choice(kinds))
     dtypes = [F16, BF16]
-    if D == 128 and kind != "append" and (G == 4 or (G == 8 and kind in ("two", "fused"))):
+    if D == 128 and kind != "append" and (G == 4 or (G == 8 and kind in ("two", "fused", "balanced"))):
         dtypes.append(FP8)
     dtype = dtypes[int(r.integers(0, len(dtypes)))]
     ps = int(r.choice([0, 16, 32, 64]))
