@@ -145,14 +145,21 @@ extern "C" int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, i
     // launch is bandwidth-bound (its bytes take over 20 us at the aggregate
     // rate), candidates start at one block per CU. Short work keeps the model's
     // choice, which splits little.
+    // The vector kernel likewise: a (KV head, split) pair is one wave, and the
+    // measured rate needs about two of them per CU (one request, 8 KV heads,
+    // 128k tokens: 137 us at 19 splits, 97 us at 64; G = 2: 208 against 100;
+    // eight 8k requests at G = 2: 90 us at 3 splits, 53 at 8), so its
+    // candidates start at two pairs per CU.
     const int groups = Hkv / cm.heads_per_block;
     double total_bytes = 0.0;
     for (int b = 0; b < B; ++b) total_bytes += (double)lens[b] * cm.bytes_per_token * Hkv;
-    const bool bw_bound = total_bytes / cm.bw_total > 20.0e-6;
-    const int s_min = (cm.blocks_per_cu == 1 && bw_bound)
-                          ? (int)std::min<int64_t>(max_s, ((int64_t)cu_count + (int64_t)B * groups - 1) /
-                                                                ((int64_t)B * groups))
-                          : 1;
+    // (the vector kernel already from 5 us of reading: 4k tokens x 32 KV heads,
+    // 64 MB, 18.3 us at 16 splits against 23.4 at the fluid model's 5)
+    const bool bw_bound = total_bytes / cm.bw_total > (cm.blocks_per_cu == 1 ? 20.0e-6 : 5.0e-6);
+    const int64_t fill = cm.blocks_per_cu == 1 ? cu_count : 2 * (int64_t)cu_count;
+    const int s_min = bw_bound ? (int)std::max<int64_t>(1, std::min<int64_t>(max_s, (fill + (int64_t)B * groups - 1) /
+                                                                                         ((int64_t)B * groups)))
+                               : 1;
     double best = 1e30;
     std::vector<std::pair<int, double>> est;
     int64_t last_chunk = -1;
