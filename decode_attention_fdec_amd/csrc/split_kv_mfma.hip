@@ -611,15 +611,16 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g8(cons
 // page §3.3-3.4: the new token's k / v are written at row cache_seqlens[b] and
 // attended to, with GPT-NeoX rotary of q and k_new at the new token's position
 // when tables are given),
-// uniform splits, single query, fp16 / bf16 caches. Every block rotates q in
+// uniform splits, single query, fp16 / bf16 caches, G = 4 or 8 (NG = 1 or 2
+// groups of four query heads through the same tiles). Every block rotates q in
 // fp32 (in LDS) and feeds it to S^T = K Q^T as two 16-bit parts, hi + lo (the
 // low part is q - hi rounded again: about 16 significant bits together); the
 // block owning row cache_seqlens[b] rounds the rotated k_new once to the cache
 // type, writes it and v_new into the cache, and waits for those stores before
 // its first DMA, which may read the row back.
-template <int DT, bool PAGED>
+template <int DT, bool PAGED, int NG>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(const MapParams p) {
-    constexpr int D = 128, G = 4, KF = 0;
+    constexpr int D = 128, G = 4 * NG, KF = 0;  // NG groups of four query heads per KV head
     constexpr int NS = Ring<KF>::kSlots;
     using E = Elem<DT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
@@ -690,9 +691,12 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
     // wait the compiler models keeps it from waiting on the DMA loads below
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    uint2 qb[1][8], qlo[1][8];
-    read_q(qlds[wv][0], lane, qb[0]);
-    read_q(qlds[wv][1], lane, qlo[0]);
+    uint2 qb[NG][8], qlo[NG][8];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {  // group j: query heads 4 j .. 4 j + 3 of the KV head
+        read_q(qlds[wv][0] + 1024 * j, lane, qb[j]);
+        read_q(qlds[wv][1] + 1024 * j, lane, qlo[j]);
+    }
 
     // ---- stream the split's tiles (as mfma_segment, one query token)
     const int t_lo = max(t_begin, lp);
@@ -706,8 +710,9 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
         stage_tile<KF>(p.k + off, p.v + off, kl, vl, tile == 0 ? nskip0 : 0, t_end - (t_begin + tile * kMT), stok,
                        lane);
     };
-    MfmaSoftmax st[1];
-    st[0].reset();
+    MfmaSoftmax st[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) st[j].reset();
     const int npro = min(NS - 1, ntiles);
     for (int t = 0; t < npro; ++t) stage(t, tile_offset(t));
     int64_t noff = (NS - 1 < ntiles) ? tile_offset(NS - 1) : 0;
@@ -719,12 +724,17 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
         }
         wait_vm_n<KvFmt<KF>::kDma>(min(NS - 1, ntiles - 1 - tile));
         const int slot = tile % NS;
-        const int nv[1] = {t_end - (t_begin + tile * kMT)};
-        mfma_tile<DT, KF, 1, true>(Ring<KF>::k_tile(lds[wv], slot), Ring<KF>::v_tile(lds[wv], slot), qb,
-                                   tile == 0 ? nskip0 : 0, nv, p.scale_log2, lane, st, qlo);
+        int nv[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) nv[j] = t_end - (t_begin + tile * kMT);
+        mfma_tile<DT, KF, NG, true>(Ring<KF>::k_tile(lds[wv], slot), Ring<KF>::v_tile(lds[wv], slot), qb,
+                                    tile == 0 ? nskip0 : 0, nv, p.scale_log2, lane, st, qlo);
     }
-    const int64_t st0 = ((int64_t)b * p.Hq + hq0) * p.s_total + p.s_offset + split;
-    write_state(st[0], lane, p.po + st0 * D, p.pm + st0, p.pd + st0, p.s_total);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        const int64_t st0 = ((int64_t)b * p.Hq + hq0 + 4 * j) * p.s_total + p.s_offset + split;
+        write_state(st[j], lane, p.po + st0 * D, p.pm + st0, p.pd + st0, p.s_total);
+    }
 
     if (p.counters == nullptr) return;
 
@@ -1031,26 +1041,33 @@ hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStrea
 }
 
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
-    if (p.Hq == 8 * p.Hkv) {  // groups of eight query heads: single query, no append
-        if (p.q_len != 1 || p.mode != kPlain) return hipErrorInvalidValue;
-        dim3 grid(S, p.B, p.Hkv / p.heads_per_block), block(64 * p.heads_per_block);
-        FDEC_MFMA_DISPATCH(map_kernel_mfma_g8, )
-        return hipGetLastError();
-    }
-    if (p.mode != kPlain) {  // append (single query, 16-bit caches)
+    if (p.mode != kPlain) {  // append (single query, 16-bit caches), G = 4 or 8
         if (p.q_len != 1 || p.kv_fp8) return hipErrorInvalidValue;
         dim3 grid(S, p.B, p.Hkv / p.heads_per_block), block(64 * p.heads_per_block);
-        if (p.dtype == 0) {
-            if (p.page_table)
-                hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, true>), grid, block, 0, st, p);
-            else
-                hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, false>), grid, block, 0, st, p);
+#define FDEC_APP(NG)                                                                         \
+    if (p.dtype == 0) {                                                                      \
+        if (p.page_table)                                                                    \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, true, NG>), grid, block, 0, st, p);  \
+        else                                                                                 \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, false, NG>), grid, block, 0, st, p); \
+    } else {                                                                                 \
+        if (p.page_table)                                                                    \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, true, NG>), grid, block, 0, st, p);  \
+        else                                                                                 \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, false, NG>), grid, block, 0, st, p); \
+    }
+        if (p.Hq == 8 * p.Hkv) {
+            FDEC_APP(2)
         } else {
-            if (p.page_table)
-                hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, true>), grid, block, 0, st, p);
-            else
-                hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, false>), grid, block, 0, st, p);
+            FDEC_APP(1)
         }
+#undef FDEC_APP
+        return hipGetLastError();
+    }
+    if (p.Hq == 8 * p.Hkv) {  // groups of eight query heads: single query
+        if (p.q_len != 1) return hipErrorInvalidValue;
+        dim3 grid(S, p.B, p.Hkv / p.heads_per_block), block(64 * p.heads_per_block);
+        FDEC_MFMA_DISPATCH(map_kernel_mfma_g8, )
         return hipGetLastError();
     }
     const int ql = mfma_tokens_per_wave(p.q_len);

@@ -277,6 +277,23 @@ def test_append_writes_rows_and_attends(rd, paged, S):
     assert_parity(out, lse, ref_out2, ref_lse2, case.dtype, f"append rd={rd}")
 
 
+@pytest.mark.parametrize("rd,paged,S,fused", [(128, False, 4, False), (64, True, 3, False), (0, False, 1, True),
+                                              (128, True, 7, True)])
+def test_append_groups_of_eight(rd, paged, S, fused):
+    # eight query heads per KV head: two groups of four through the matrix-core append kernel
+    case = append_case(63, 3, 32, 4, 128, 300, BF16, rotary_dim=rd, pad="nan", page_size=16 if paged else 0,
+                       cache_seqlens=[0, 150, 299])
+    kc, vc, ref_out, ref_lse = _append_oracle(case)
+    k0 = _bits(case.k)
+    out, lse, kg, vg, _ = _append_run(case, S, fused=fused)
+    kg, vg = _bits(kg), _bits(vg)
+    assert np.array_equal(vg, vc)
+    assert np.abs(kg.astype(np.int32) - kc.astype(np.int32)).max() <= 1
+    if rd == 0:
+        assert np.array_equal(kg, kc)
+    assert_parity(out, lse, ref_out, ref_lse, case.dtype, f"append G=8 rd={rd}")
+
+
 def test_append_rotated_rows_mostly_bit_exact():
     case = workload("c4", pad="nan")
     kc, vc, ref_out, ref_lse = _append_oracle(case)
