@@ -81,8 +81,10 @@ constexpr int kMtWaves = 4;
 hipError_t launch_map_mt16(const MapParams &p, int num_splits, hipStream_t stream);
 // Whether fdec_decode_multi takes the 16x16x32 kernel: q_len * G query rows per
 // (request, KV head) fill its row blocks.
+// Below 12 rows it pads its 16-row blocks; G = 4 then keeps the 4x4x4 kernel and
+// G = 8 with one token the G = 8 kernel, every other G takes it at any q_len.
 inline bool mt16_eligible(int q_len, int G, int head_dim, bool fp8) {
-    return !fp8 && head_dim == 128 && q_len * G >= 12;
+    return !fp8 && head_dim == 128 && (q_len * G >= 12 || (G != 4 && G != 8));
 }
 // Blocks along z of the 16x16x32 kernels: kMtWaves waves per block, one per
 // (KV head, chunk of 16 or 32 query rows).

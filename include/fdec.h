@@ -251,8 +251,8 @@ int fdec_merge_states(const float *part_o, const float *part_m, const float *par
  *        ([cookbook] §3.5 softmax_lse shape (batch, heads, seqlen_q))
  *   num_splits, softmax_scale as in fdec_decode (splits over the request's rows)
  *   1 <= q_len <= FDEC_MAX_QLEN. Built for head_dim 128, page_size a multiple
- *   of 16 or contiguous, and Hq = 4 Hkv (all cache dtypes), q_len * Hq / Hkv >= 12
- *   (fp16 / bf16 caches) or Hq = 8 Hkv with q_len = 1 (FDEC_ERR_UNSUPPORTED
+ *   of 16 or contiguous: every Hq / Hkv with fp16 / bf16 caches, and float8
+ *   caches with Hq = 4 Hkv, or Hq = 8 Hkv and q_len = 1 (FDEC_ERR_UNSUPPORTED
  *   otherwise); no append. workspace >= fdec_workspace_size(B * q_len, Hq, Hkv,
  *   head_dim, S). q_len = 1 gives fdec_decode's two-kernel result bitwise.
  */
@@ -270,8 +270,8 @@ int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const fdec_kv *kv
  * fdec_decode's up to rounding. The ranges are computed on the device from
  * seq_lens (no host copy of the lengths), so the call may be captured in a
  * graph whose lengths change between replays.
- *   Supported for G = Hq/Hkv = 4, head_dim 128, page_size a multiple of 16 (or
- *   contiguous), no append: FDEC_ERR_UNSUPPORTED otherwise.
+ *   Supported for G = Hq/Hkv = 4 or 8, head_dim 128, page_size a multiple of 16
+ *   (or contiguous), no append: FDEC_ERR_UNSUPPORTED otherwise.
  *   num_blocks  blocks per group of KV heads, 1..256; 0 = per compute unit of
  *               the current device over all groups, one block for fp16/bf16
  *               caches and two for float8 caches (measured best on MI355X).

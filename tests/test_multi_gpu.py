@@ -108,9 +108,28 @@ def test_full_128k_request(q_len):
     check(out, lse, ref_out, ref_lse, BF16, f"c2 q_len={q_len}")
 
 
+@pytest.mark.parametrize("G,q_len", [(1, 1), (1, 3), (2, 2), (2, 5), (1, 11)])
+def test_multi_token_few_rows_on_the_16x16x32_kernel(G, q_len):
+    # fewer than 12 query rows per KV head pad the 16x16x32 kernel's row block
+    case = paged_case(392 + G * 10 + q_len, 3, 4 * G, 4, 128, [700, 3, 1500], 16, F16, extra_pages=2, pad="nan")
+    q = multi_query(393 + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for S in (1, 6):
+        out, lse = run(case, q, S)
+        check(out, lse, ref_out, ref_lse, F16, f"G={G} q_len={q_len} S={S}")
+    out, lse = run_bal(case, q, 0) if q_len > 1 else (None, None)
+    if out is not None:
+        check(out, lse, ref_out, ref_lse, F16, f"G={G} q_len={q_len} balanced")
+
+
 def test_multi_token_shapes_rejected():
-    case = contiguous_case(246, 2, 16, 8, 128, [10, 20], 32, BF16)  # G = 2: no matrix-core kernel
+    case = contiguous_case(246, 2, 16, 8, 64, [10, 20], 32, BF16)  # head_dim 64: no multi-token kernel
     q = multi_query(247, case, 2)
+    with pytest.raises(F.FdecError) as e:
+        run(case, q, 1)
+    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
+    case = contiguous_case(249, 2, 16, 8, 128, [10, 20], 32, FP8)  # float8 at G = 2
+    q = multi_query(250, case, 2)
     with pytest.raises(F.FdecError) as e:
         run(case, q, 1)
     assert e.value.status == F.FDEC_ERR_UNSUPPORTED
@@ -261,8 +280,8 @@ def test_multi_token_balanced_both_kernels_agree(q_len, monkeypatch):
 
 
 def test_multi_token_balanced_shapes_rejected():
-    case = contiguous_case(390, 2, 16, 8, 128, [10, 20], 32, BF16)  # G = 2, q_len 2: 4 rows per KV head
-    q = multi_query(391, case, 2)
+    case = contiguous_case(390, 2, 16, 8, 128, [10, 20], 32, BF16)  # G = 2, one token: no balanced kernel
+    q = multi_query(391, case, 1)
     with pytest.raises(F.FdecError) as e:
         run_bal(case, q, 1)
     assert e.value.status == F.FDEC_ERR_UNSUPPORTED

@@ -7,7 +7,7 @@ requests whose lengths mix empty, one-token, tile-edge and long requests,
 NaN in every unused row, and a split count from 0 (planned) to 40; then one of
 the entry points that takes that shape: fdec_decode (two kernels or the
 single-kernel merge, with or without an append + NeoX rotary),
-fdec_decode_balanced, fdec_decode_multi (1 to 8 query tokens). The parity bar
+fdec_decode_balanced, fdec_decode_multi (1 to 8 query tokens, any G). The parity bar
 is the one every other parity test uses. The draws are fixed, so a failure
 names a case that can be rerun by its id.
 """
@@ -48,6 +48,8 @@ def draw(i):
         kinds += ["balanced", "multi", "multi"]
     elif D == 128 and G * 3 >= 12:
         kinds += ["multi", "balanced"]
+    elif D == 128:
+        kinds += ["multi"]
     kind = str(r.choice(kinds))
     dtypes = [F16, BF16]
     if D == 128 and kind != "append" and (G == 4 or (G == 8 and kind in ("two", "fused", "balanced"))):
@@ -58,8 +60,6 @@ def draw(i):
     lens = [int(r.choice(special)) if r.random() < 0.35 else int(r.integers(1, cap + 1)) for _ in range(B)]
     S = int(r.choice([0, 1, 2, 5, 13, 40]))
     q_len = int(r.integers(1, 9)) if kind == "multi" else 1
-    if kind == "multi" and G != 4:
-        q_len = max(q_len, (12 + G - 1) // G)
     return dict(i=i, G=G, Hkv=Hkv, Hq=G * Hkv, D=D, B=B, cap=cap, kind=kind, dtype=dtype, ps=ps, lens=lens, S=S,
                 q_len=q_len, rd=int(r.choice([0, D // 2, D])), seed=2000 + i)
 
