@@ -39,6 +39,8 @@ WORKLOAD_TEXT = {
             "per-(request, KV head) descales, bf16 queries",
     "c3f8": "paged batched decode: B=32, Hq=32, Hkv=8, D=128, page 16, lengths U[512,8192], float8 e4m3fn "
             "KV with per-(request, KV head) descales, bf16 queries",
+    "c2g8": "long-context GQA decode with eight query heads per KV head: B=1, Hq=64, Hkv=8, D=128, "
+            "131072 contiguous bf16 tokens",
 }
 KERNEL_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
 
@@ -304,7 +306,7 @@ def main() -> int:
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4",
+    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8",
                     help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

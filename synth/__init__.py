@@ -378,6 +378,8 @@ def workload(name: str, pad: str = "zero") -> Case:
         return contiguous_case(2, 1, 32, 8, 128, [131072], 131072, BF16, pad, "c2")
     if name == "c2f8":
         return contiguous_case(2, 1, 32, 8, 128, [131072], 131072, FP8, pad, "c2f8")
+    if name == "c2g8":  # the long-context request with eight query heads per KV head
+        return contiguous_case(2, 1, 64, 8, 128, [131072], 131072, BF16, pad, "c2g8")
     if name == "c3f8":
         return paged_case(3, 32, 32, 8, 128, None, 16, FP8, max_pages=512, pad=pad, name="c3f8",
                           lens_range=(512, 8192))
