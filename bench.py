@@ -303,7 +303,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8", "c2g8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
     ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8",
