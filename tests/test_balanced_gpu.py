@@ -70,7 +70,7 @@ def test_balanced_repeats_bitwise_and_agrees_with_uniform_splits():
     assert ((l1 - lu).abs() / lu.abs().clamp(min=1)).max().item() < 1e-6
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c2g8"])
 def test_balanced_full_size_workloads(name):
     case = workload(name, pad="nan")
     ref_out, ref_lse = oracle_decode(case)

@@ -309,7 +309,7 @@ def test_append_rotated_rows_mostly_bit_exact():
 
 # ---------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c2g8"])
 def test_full_size_workload_matches_oracle(name):
     case = workload(name, pad="nan")
     ref_out, ref_lse = oracle_decode(case)
