@@ -192,14 +192,11 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     return p;
 }
 
-// Float8 caches run only on the matrix-core map kernel, without append.
-int check_fp8(const char *fn, const fdec_kv *kv, const fdec::MapParams &p, const fdec_append *append) {
+// Float8 caches run on either map kernel (the matrix-core one for G = 4, 8 at
+// head_dim 128, the vector one otherwise), without append.
+int check_fp8(const char *fn, const fdec_kv *kv, const fdec::MapParams &, const fdec_append *append) {
     if (kv->dtype != FDEC_FP8_E4M3) return FDEC_OK;
     if (append) return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: append into a float8 cache is not built", fn);
-    if (!p.mfma)
-        return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: float8 caches need Hq = 4 Hkv or 8 Hkv, head_dim 128, page_size a multiple of 16 "
-                         "(and the matrix-core map kernel)", fn);
     return FDEC_OK;
 }
 

@@ -16,6 +16,23 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Four e4m3 values (bytes, lowest first) to four bf16 values in two dwords
+// (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w) {
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// The (request b, KV head g) descale of a float8 cache (1 without one), by a
+// scalar load; P is the kernels' parameter block (Hkv KV heads).
+template <class P>
+__device__ __forceinline__ float kv_descale(const float *d, const P &p, int b, int g) {
+    if (!d) return 1.0f;
+    typedef const __attribute__((address_space(4))) float *cf_t;
+    return ((cf_t)d)[(int64_t)b * p.Hkv + g];
+}
+
 // Element type operations: 0 = fp16, 1 = bf16. A packed dword holds elements
 // (lo, hi) = (d, d + 1).
 template <int DT> struct Elem;

@@ -21,10 +21,21 @@
 // are in flight while the current one is computed. Each lane row keeps its own
 // (m, d, acc); the eight row states are merged with shuffles and the wave writes
 // its heads' states itself.
+//
+// Float8 e4m3fn caches (plain decode, bf16 queries): a lane loads the same
+// elements as for 16-bit caches, as 8-byte pieces (a row is D bytes), and
+// widens them exactly to packed bf16 before q.k and P.V; K's descale scales
+// the scores and V's the state's O~.
+#include <type_traits>
+
 #include "device_common.h"
 #include "fdec_internal.h"
 
 namespace fdec {
+
+// Kernel-only mode: plain decode over a float8 e4m3fn cache.
+constexpr int kPlainF8 = 3;
+static_assert(kPlainF8 != kPlain && kPlainF8 != kAppend && kPlainF8 != kAppendRope, "distinct modes");
 
 // Register tiles in flight per wave and the waves per SIMD the kernel is
 // compiled for, by GQA group size (D = 128): more tiles hide more latency,
@@ -52,7 +63,12 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     constexpr int TT = 8 * NR;            // tokens per tile
     constexpr bool QF32 = (MODE == kAppendRope);
     constexpr int NBUF = MapConfig<G, D>::nbuf;
+    constexpr bool F8 = (MODE == kPlainF8);
+    constexpr bool APPEND = (MODE == kAppend || MODE == kAppendRope);
+    constexpr int ES = F8 ? 1 : 2;  // bytes per cache element
+    static_assert(!F8 || DT == 1, "float8 caches take bf16 queries");
     using E = Elem<DT>;
+    using Piece = typename std::conditional<F8, uint2, uint4>::type;  // one lane's 8 elements of a row
 
     __shared__ float sm_vec[(MODE == kAppendRope) ? MapConfig<G, D>::max_waves * (G + 1) * D : 1];
     __shared__ int sm_flag;
@@ -65,7 +81,7 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     const int hq0 = g * G;
 
     const int c_app = p.seq_lens[b];
-    const int L = (MODE == kPlain) ? c_app : c_app + 1;
+    const int L = APPEND ? c_app + 1 : c_app;
     const int lp = p.leftpad ? p.leftpad[b] : 0;            // first valid row (left padding)
     const int64_t crow = p.batch_idx ? p.batch_idx[b] : b;  // contiguous caches: the request's cache row
     // split boundaries: multiples of 16 rows from the 16-row tile holding the
@@ -88,7 +104,7 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     // ---------------------------------------------------------------- q (and append)
     uint32_t qp[QF32 ? 1 : G][NQ];
     float qf[QF32 ? G : 1][QF32 ? NE : 1];
-    const bool owner = (MODE != kPlain) && (t_begin <= c_app) && (c_app < t_begin + p.chunk);
+    const bool owner = APPEND && (t_begin <= c_app) && (c_app < t_begin + p.chunk);
     if constexpr (MODE == kAppendRope) {
         // rotate q (and, in the block owning the new row, k_new) in this wave's
         // part of LDS, fp32
@@ -190,11 +206,32 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     const int ntiles = t_end > t_lo ? (t_end - t_first + TT - 1) / TT : 0;
     const char *kbase = p.k;
     const char *vbase = p.v;
-    const uint32_t tok_bytes = (uint32_t)(p.s_token * 2);
+    const uint32_t tok_bytes = (uint32_t)(p.s_token * ES);
+    // float8: scores in log2 units with K's descale, O~ with V's
+    const float score_scale = F8 ? p.scale_log2 * kv_descale(p.k_descale, p, b, g) : p.scale_log2;
+    const float o_scale = F8 ? kv_descale(p.v_descale, p, b, g) : 1.0f;
 
     struct Tile {
-        uint4 k[NR][NCH];
-        uint4 v[NR][NCH];
+        Piece k[NR][NCH];
+        Piece v[NR][NCH];
+    };
+    // the NQ packed 16-bit dwords of one row of a tile (float8: widened to bf16)
+    auto row_words = [](const Piece (&r)[NCH], uint32_t (&w)[NQ]) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if constexpr (F8) {
+                const uint2 a = fp8x4_to_bf16(r[c].x), bb = fp8x4_to_bf16(r[c].y);
+                w[4 * c + 0] = a.x;
+                w[4 * c + 1] = a.y;
+                w[4 * c + 2] = bb.x;
+                w[4 * c + 3] = bb.y;
+            } else {
+                w[4 * c + 0] = r[c].x;
+                w[4 * c + 1] = r[c].y;
+                w[4 * c + 2] = r[c].z;
+                w[4 * c + 3] = r[c].w;
+            }
+        }
     };
     auto tile_t0 = [&](int i) { return t_first + i * TT; };
 
@@ -208,16 +245,16 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     uint32_t off_full[NR], off_last[NR], off_first[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-        off_full[j] = (uint32_t)(8 * j + ra) * tok_bytes + (uint32_t)cb * 16u;
-        off_last[j] = (uint32_t)min(8 * j + ra, nvalid_last - 1) * tok_bytes + (uint32_t)cb * 16u;
-        off_first[j] = (uint32_t)min(max(8 * j + ra, nskip0), nhi_first) * tok_bytes + (uint32_t)cb * 16u;
+        off_full[j] = (uint32_t)(8 * j + ra) * tok_bytes + (uint32_t)cb * 8u * ES;
+        off_last[j] = (uint32_t)min(8 * j + ra, nvalid_last - 1) * tok_bytes + (uint32_t)cb * 8u * ES;
+        off_first[j] = (uint32_t)min(max(8 * j + ra, nskip0), nhi_first) * tok_bytes + (uint32_t)cb * 8u * ES;
     }
 
     // Issue the loads of the tile starting at token t0.
     auto issue = [&](Tile &T, int t0) {
         const int64_t base = row_offset(t0);
-        const char *kb = kbase + base * 2;
-        const char *vb = vbase + base * 2;
+        const char *kb = kbase + base * ES;
+        const char *vb = vbase + base * ES;
         const bool last = (t0 == last_t0);
         const bool first = (t0 == t_first) && nskip0 > 0;
 #pragma unroll
@@ -225,8 +262,8 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
             const uint32_t off = first ? off_first[j] : last ? off_last[j] : off_full[j];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                T.k[j][c] = *reinterpret_cast<const uint4 *>(kb + off + c * 128);
-                T.v[j][c] = *reinterpret_cast<const uint4 *>(vb + off + c * 128);
+                T.k[j][c] = *reinterpret_cast<const Piece *>(kb + off + c * 64 * ES);
+                T.v[j][c] = *reinterpret_cast<const Piece *>(vb + off + c * 64 * ES);
             }
         }
     };
@@ -237,7 +274,8 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
         float sc[NR][G];
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            const uint32_t *kw = reinterpret_cast<const uint32_t *>(&T.k[j][0]);
+            uint32_t kw[NQ];
+            row_words(T.k[j], kw);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float s = 0.0f;
@@ -251,7 +289,7 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
 #pragma unroll
                     for (int i = 0; i < NQ; ++i) s = E::dot2(qp[h][i], kw[i], s);
                 }
-                sc[j][h] = sum8(s) * p.scale_log2;
+                sc[j][h] = sum8(s) * score_scale;
             }
         }
         if (nvalid < TT || nskip > 0) {  // a split's last tile, a padded first tile (wave-uniform branch)
@@ -285,7 +323,8 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
         float vf[NR][NE];
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            const uint32_t *vw = reinterpret_cast<const uint32_t *>(&T.v[j][0]);
+            uint32_t vw[NQ];
+            row_words(T.v[j], vw);
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 vf[j][2 * i] = E::lo(vw[i]);
@@ -358,15 +397,16 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     for (int h = 0; h < G; ++h) {
         const float T = tmax[h];
         const float f = (T == kNegInf) ? 0.0f : fexp2(m[h] - T);
+        const float fo = F8 ? f * o_scale : f;  // O~ carries V's descale
         const int64_t bh = (int64_t)b * p.Hq + hq0 + h;
         if (ra == 0) {
             float *dst = p.po + (bh * p.s_total + slot) * D;
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                float4 lo4 = make_float4(acc[h][8 * c] * f, acc[h][8 * c + 1] * f, acc[h][8 * c + 2] * f,
-                                         acc[h][8 * c + 3] * f);
-                float4 hi4 = make_float4(acc[h][8 * c + 4] * f, acc[h][8 * c + 5] * f, acc[h][8 * c + 6] * f,
-                                         acc[h][8 * c + 7] * f);
+                float4 lo4 = make_float4(acc[h][8 * c] * fo, acc[h][8 * c + 1] * fo, acc[h][8 * c + 2] * fo,
+                                         acc[h][8 * c + 3] * fo);
+                float4 hi4 = make_float4(acc[h][8 * c + 4] * fo, acc[h][8 * c + 5] * fo, acc[h][8 * c + 6] * fo,
+                                         acc[h][8 * c + 7] * fo);
                 *reinterpret_cast<float4 *>(dst + 64 * c + 8 * cb) = lo4;
                 *reinterpret_cast<float4 *>(dst + 64 * c + 8 * cb + 4) = hi4;
             }
@@ -411,6 +451,12 @@ static hipError_t launch_t(const MapParams &p, int S, hipStream_t st) {
 
 template <int DT, int D, int G, bool PAGED>
 static hipError_t launch_mode(const MapParams &p, int S, hipStream_t st) {
+    if (p.kv_fp8) {  // plain decode with bf16 queries only
+        if constexpr (DT == 1) {
+            if (p.mode == kPlain) return launch_t<DT, D, G, PAGED, kPlainF8>(p, S, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (p.mode) {
         case kPlain: return launch_t<DT, D, G, PAGED, kPlain>(p, S, st);
         case kAppend: return launch_t<DT, D, G, PAGED, kAppend>(p, S, st);

@@ -91,13 +91,6 @@ template <int KF> struct KvFmt {
     static constexpr int kDma = KF ? 4 : 8;   // DMA instructions per tile (K + V)
 };
 
-// Four e4m3 values (bytes, lowest first) to four bf16 values in two dwords.
-__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w) {
-    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-}
-
 constexpr int kMT = 16;                 // tokens per tile
 constexpr int kMTileBytes = kMT * 256;  // one tile of K (or V) rows of one KV head
 #ifndef FDEC_MFMA_NBUF
@@ -190,14 +183,6 @@ __device__ __forceinline__ int first_row(const MapParams &p, int b) {
 __device__ __forceinline__ int64_t cache_row(const MapParams &p, int b) {
     typedef const __attribute__((address_space(4))) int32_t *ci_t;
     return p.batch_idx ? ((ci_t)p.batch_idx)[b] : b;
-}
-
-// The (request b, KV head g) descale of a float8 cache (1 without one), by a
-// scalar load.
-__device__ __forceinline__ float kv_descale(const float *d, const MapParams &p, int b, int g) {
-    if (!d) return 1.0f;
-    typedef const __attribute__((address_space(4))) float *cf_t;
-    return ((cf_t)d)[(int64_t)b * p.Hkv + g];
 }
 
 // LDS addresses of ring slot `slot`: its K tile and V tile.

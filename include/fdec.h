@@ -93,12 +93,14 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  * capacity < 2^31.
  * Float8 caches (dtype FDEC_FP8_E4M3): element (b, t, g, d) stands for its
  * e4m3 value times k_descale[b*Hkv + g] (K) or v_descale[b*Hkv + g] (V); a NULL
- * descale is 1. Queries are bf16. Built for head_dim 128, page_size a multiple
- * of 16 (or contiguous), without append: Hq = 4 Hkv in fdec_decode,
- * fdec_decode_partials, fdec_decode_balanced and fdec_decode_multi, and
- * Hq = 8 Hkv in fdec_decode and fdec_decode_partials; other calls and shapes
- * return FDEC_ERR_UNSUPPORTED. The partial states then already include V's
- * descale.
+ * descale is 1. Queries are bf16. Built for page_size a multiple of 16 (or
+ * contiguous), without append: every GQA group size and head_dim in
+ * fdec_decode and fdec_decode_partials (the matrix-core map kernel for
+ * Hq = 4 or 8 Hkv at head_dim 128, the vector kernel otherwise); head_dim 128
+ * with Hq = 4 Hkv in fdec_decode_balanced and fdec_decode_multi, and with
+ * Hq = 8 Hkv in fdec_decode_balanced and in fdec_decode_multi with q_len = 1;
+ * other calls and shapes return FDEC_ERR_UNSUPPORTED. The partial states then
+ * already include V's descale.
  */
 typedef struct fdec_kv {
     void *k;

@@ -235,8 +235,8 @@ def test_fp8_validation(fdec):
     fp8 = dict(dtype=F.FDEC_FP8_E4M3)
     # strides must be multiples of 16 bytes: 16 float8 elements
     assert call_decode(kv_struct(s_head=8, **fp8)) == F.FDEC_ERR_INVALID_ARG
-    # float8 runs on the matrix-core kernel only: G = 4, head_dim 128, no append
-    assert call_decode(kv_struct(**fp8), Hq=16) == F.FDEC_ERR_UNSUPPORTED  # G = 2
+    # float8 runs without append; the balanced split takes it at G = 4 or 8 only
+    assert call_balanced(kv_struct(**fp8), Hq=16) == F.FDEC_ERR_UNSUPPORTED  # G = 2
     a = F.FdecAppend()
     a.k_new, a.v_new = FAKE, FAKE
     assert call_decode(kv_struct(**fp8), append=a) == F.FDEC_ERR_UNSUPPORTED

@@ -3,7 +3,8 @@
 The pages' FP8 KV cache: K and V stored as float8 e4m3fn with one fp32 descale
 per (request, KV head) each, queries in bf16. Each case runs the uniform splits
 (two kernels and the single-kernel merge), the map stage alone and the balanced
-split; padding rows and unused pages hold NaN.
+split, on the matrix-core map kernel (G = 4, 8 at head_dim 128) and on the
+vector one (every other shape); padding rows and unused pages hold NaN.
 """
 import math
 
@@ -114,13 +115,64 @@ def test_fp8_full_size_workloads(name, mode):
     assert_parity(out, lse, ref_out, ref_lse, case.dtype, f"{name} {mode}")
 
 
-def test_fp8_unsupported_shapes_and_paths_are_reported(monkeypatch):
-    case = contiguous_case(98, 1, 8, 4, 128, [40], 64, FP8, pad="nan")  # G = 2
-    with pytest.raises(F.FdecError) as e:
-        run(case, 2)
-    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
-    case = contiguous_case(99, 1, 8, 2, 128, [40], 64, FP8, pad="nan")  # G = 4 on the vector kernel
+# the vector map kernel: group sizes and head dims the matrix-core kernel does
+# not take, and G = 4 / 8 forced onto it
+VECTOR_CASES = [
+    ("g1_contig_d128", lambda: contiguous_case(110, 3, 8, 8, 128, [1, 300, 1000], 1024, FP8, pad="nan")),
+    ("g2_paged16_d128", lambda: paged_case(111, 4, 16, 8, 128, [16, 31, 500, 0], 16, FP8, extra_pages=4,
+                                           pad="nan")),
+    ("g2_paged32_d64", lambda: paged_case(112, 3, 8, 4, 64, [64, 95, 777], 32, FP8, extra_pages=3, pad="nan")),
+    ("g8_contig_d64", lambda: contiguous_case(113, 2, 16, 2, 64, [17, 600], 640, FP8, pad="nan")),
+    ("g1_paged48_d64", lambda: paged_case(114, 2, 4, 4, 64, [48, 481], 48, FP8, extra_pages=2, pad="nan")),
+]
+
+
+@pytest.mark.parametrize("name,builder", VECTOR_CASES, ids=[c[0] for c in VECTOR_CASES])
+@pytest.mark.parametrize("num_splits", [1, 5, 0])
+def test_fp8_vector_kernel_matches_oracle(name, builder, num_splits):
+    case = builder()
+    ref_out, ref_lse = oracle_decode(case)
+    for fused in (False, True):
+        out, lse = run(case, num_splits, fused)
+        assert_parity(out, lse, ref_out, ref_lse, case.dtype, f"{name} S={num_splits} fused={fused}")
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_fp8_matrix_core_shapes_on_the_vector_kernel(G, monkeypatch):
+    case = paged_case(115 + G, 3, 2 * G, 2, 128, [33, 400, 1000], 16, FP8, extra_pages=2, pad="nan")
+    ref_out, ref_lse = oracle_decode(case)
+    mo, ml = run(case, 6)
     monkeypatch.setenv("FDEC_MAP_PATH", "vector")
+    vo, vl = run(case, 6)
+    assert_parity(vo, vl, ref_out, ref_lse, case.dtype, f"G={G} vector kernel")
+    assert (vo - mo).abs().max().item() < 1e-4
+
+
+def test_fp8_vector_kernel_states_match_oracle_states():
+    lens = [1, 33, 300, 1000]
+    case = contiguous_case(119, 4, 8, 4, 128, lens, 1024, FP8, pad="nan")  # G = 2
+    S = 7
+    d = to_dev(case)
+    po, pm, pd = F.decode_partials(d["q"], d["k"], d["v"], d["seq_lens"], S, k_descale=d["k_descale"],
+                                   v_descale=d["v_descale"])
+    torch.cuda.synchronize()
+    chunk = F.split_chunk(case.capacity, S)
+    bounds = np.array([[min(i * chunk, case.capacity) for i in range(S + 1)]] * 4, dtype=np.int32)
+    rpo, rpm, rpd = oracle.partials(okv(case), case.q, case.seq_lens, 1 / math.sqrt(128), bounds)
+    gpo, gpm, gpd = (t.cpu().double().numpy() for t in (po, pm, pd))
+    fin = np.isfinite(rpm)
+    assert np.array_equal(np.isfinite(gpm), fin)
+    assert np.all(gpd[~fin] == 0) and np.all(gpo[~fin] == 0)
+    np.testing.assert_allclose(gpm[fin], rpm[fin], rtol=0, atol=1e-5 * np.abs(rpm[fin]).max() + 1e-5)
+    np.testing.assert_allclose(gpd[fin], rpd[fin], rtol=1e-4)
+    err = np.abs(gpo - rpo)[fin] / rpd[fin][:, None]
+    assert err.max() < 1e-3
+
+
+def test_fp8_unsupported_paths_are_reported():
+    case = contiguous_case(98, 1, 8, 4, 128, [40], 64, FP8, pad="nan")  # G = 2: no balanced split
+    d = to_dev(case)
     with pytest.raises(F.FdecError) as e:
-        run(case, 2)
+        F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], k_descale=d["k_descale"],
+                          v_descale=d["v_descale"])
     assert e.value.status == F.FDEC_ERR_UNSUPPORTED
