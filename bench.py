@@ -41,6 +41,8 @@ WORKLOAD_TEXT = {
             "KV with per-(request, KV head) descales, bf16 queries",
     "c2g8": "long-context GQA decode with eight query heads per KV head: B=1, Hq=64, Hkv=8, D=128, "
             "131072 contiguous bf16 tokens",
+    "c1f8": "unpaged MHA decode: B=1, Hq=Hkv=32, D=128, 4096 contiguous float8 e4m3fn tokens, "
+            "per-(request, KV head) descales, bf16 queries, 16 splits",
 }
 KERNEL_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
 
@@ -303,10 +305,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8", "c2g8"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8", "c2g8", "c1f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8",
+    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8",
                     help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

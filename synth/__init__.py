@@ -374,6 +374,8 @@ def workload(name: str, pad: str = "zero") -> Case:
     """The five named workloads at their full sizes."""
     if name == "c1":
         return contiguous_case(1, 1, 32, 32, 128, [4096], 4096, F16, pad, "c1", num_splits=16)
+    if name == "c1f8":  # c1 with a float8 e4m3fn cache (the vector map kernel)
+        return contiguous_case(1, 1, 32, 32, 128, [4096], 4096, FP8, pad, "c1f8", num_splits=16)
     if name == "c2":
         return contiguous_case(2, 1, 32, 8, 128, [131072], 131072, BF16, pad, "c2")
     if name == "c2f8":
