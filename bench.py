@@ -106,7 +106,7 @@ class Runner:
             splits = case.num_splits
         if splits <= 0:
             lens_host = (case.seq_lens + (1 if case.k_new is not None else 0)).tolist()
-            splits = F.plan(B, Hq, case.Hkv, lens_host, case.capacity, case.page_size)
+            splits = F.plan(B, Hq, case.Hkv, lens_host, case.capacity, case.page_size, kv_dtype=case.dtype)
         self.S = splits
         self.i = 0
         if mode.startswith("multi"):
@@ -183,7 +183,7 @@ def time_map_kernel(F, runner: Runner, steps: int):
     B, Hq, D = case.q.shape
     S = runner.S
     if S == 0:  # the balanced split has no map-only entry: time the uniform map at the planner's count
-        S = F.plan(B, Hq, case.Hkv, case.seq_lens.tolist(), case.capacity, case.page_size)
+        S = F.plan(B, Hq, case.Hkv, case.seq_lens.tolist(), case.capacity, case.page_size, kv_dtype=case.dtype)
     po = torch.empty(B, Hq, S, D, dtype=torch.float32, device=runner.dev)
     pm = torch.empty(B, Hq, S, dtype=torch.float32, device=runner.dev)
     pd = torch.empty(B, Hq, S, dtype=torch.float32, device=runner.dev)

@@ -71,6 +71,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_last_error.restype = ctypes.c_char_p
     lib.fdec_last_error.argtypes = []
     lib.fdec_plan.argtypes = [I, I, I, P, I, I, I, ctypes.POINTER(I)]
+    lib.fdec_plan_kv.argtypes = [I, I, I, P, I, I, I, I, ctypes.POINTER(I)]
     lib.fdec_plan_rules.argtypes = [I, I, I, I, ctypes.POINTER(I)]
     lib.fdec_split_chunk.restype = ctypes.c_int64
     lib.fdec_split_chunk.argtypes = [I, I]
@@ -182,15 +183,20 @@ def make_append(k_new: torch.Tensor, v_new: torch.Tensor, rope_cos: Optional[tor
 
 
 def plan(B: int, Hq: int, Hkv: int, seq_lens_host: Optional[Sequence[int]], capacity: int,
-         page_size: int = 0, cu_count: int = 256) -> int:
+         page_size: int = 0, cu_count: int = 256, kv_dtype=None) -> int:
+    """fdec_plan, or fdec_plan_kv when kv_dtype (a torch dtype or an fdec_dtype code) is given."""
     lib = load_library()
     out = ctypes.c_int(0)
     arr = None
     if seq_lens_host is not None:
         vals = [int(x) for x in seq_lens_host]
         arr = (ctypes.c_int32 * len(vals))(*vals)
-    _check(lib.fdec_plan(B, Hq, Hkv, ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
-                         capacity, page_size, cu_count, ctypes.byref(out)))
+    lens = ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None
+    if kv_dtype is None:
+        _check(lib.fdec_plan(B, Hq, Hkv, lens, capacity, page_size, cu_count, ctypes.byref(out)))
+    else:
+        code = kv_dtype if isinstance(kv_dtype, int) else _dtype_code(kv_dtype)
+        _check(lib.fdec_plan_kv(B, Hq, Hkv, lens, capacity, page_size, code, cu_count, ctypes.byref(out)))
     return out.value
 
 
@@ -242,7 +248,8 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Te
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
-    S = num_splits if num_splits > 0 else plan(B, Hq, kv.num_kv_heads, None, kv.capacity, kv.page_size)
+    S = num_splits if num_splits > 0 else plan(B, Hq, kv.num_kv_heads, None, kv.capacity, kv.page_size,
+                                               kv_dtype=kv.dtype)
     if workspace is None:
         workspace = Workspace(workspace_size(B, Hq, kv.num_kv_heads, D, S), q.device)
     _check(lib.fdec_decode(q.data_ptr(), B, Hq, ctypes.byref(kv), seq_lens.data_ptr(), S,
@@ -269,7 +276,8 @@ def decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: to
         out = torch.empty(B, q_len, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty(B, Hq, q_len, dtype=torch.float32, device=q.device)
-    S = num_splits if num_splits > 0 else plan(B, Hq, kv.num_kv_heads, None, kv.capacity, kv.page_size)
+    S = num_splits if num_splits > 0 else plan(B, Hq, kv.num_kv_heads, None, kv.capacity, kv.page_size,
+                                               kv_dtype=kv.dtype)
     if workspace is None:
         workspace = Workspace(workspace_size(B * q_len, Hq, kv.num_kv_heads, D, S), q.device)
     _check(lib.fdec_decode_multi(q.data_ptr(), B, q_len, Hq, ctypes.byref(kv), seq_lens.data_ptr(), S,

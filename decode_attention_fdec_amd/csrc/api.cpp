@@ -207,7 +207,7 @@ int resolve_splits(const char *fn, int num_splits, int B, int Hq, const fdec_kv 
         *S = num_splits;
         return FDEC_OK;
     }
-    int rc = fdec_plan(B, Hq, kv->num_kv_heads, nullptr, capacity_of(kv), kv->page_size, 256, S);
+    int rc = fdec_plan_kv(B, Hq, kv->num_kv_heads, nullptr, capacity_of(kv), kv->page_size, kv->dtype, 256, S);
     return rc;
 }
 

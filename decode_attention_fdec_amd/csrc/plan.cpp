@@ -30,6 +30,7 @@ struct CostModel {
     double t_empty = 0.1e-6;      // an empty block, s
     double t_merge = 3.0e-6;      // merge kernel launch and latency, s
     double bytes_per_token = 2.0 * 128 * 2;  // K + V row of one KV head (D = 128, 2-byte)
+    int fill_per_cu = 1;          // (KV head, split) pairs per CU a bandwidth-bound launch needs
 };
 
 // G = 4 runs on the matrix-core kernel: blocks of up to 4 KV heads, one block
@@ -38,7 +39,11 @@ struct CostModel {
 // blocks, 107 us at 128). G = 8 runs on its matrix-core kernel with the same
 // blocks (128k tokens: 98 us at 256 blocks). Other shapes run on the vector
 // kernel, modelled per KV head (its blocks stream each head independently).
-CostModel model_for(int Hq, int Hkv) {
+// kv8: a float8 cache. A vector-kernel wave then streams the same tokens per
+// second as over a 16-bit cache, at half the bytes, so more waves are needed to
+// reach the aggregate rate (one 128k-token request, 8 KV heads, G = 1 or 2:
+// 54-55 us at 128 splits against 60-75 at 64).
+CostModel model_for(int Hq, int Hkv, bool kv8) {
     CostModel cm;
     if (Hq == 4 * Hkv || Hq == 8 * Hkv) {
         int hpb = 1;
@@ -52,12 +57,19 @@ CostModel model_for(int Hq, int Hkv) {
         cm.blocks_per_cu = 1;
         cm.heads_per_block = hpb;
         cm.t_block = 2.0e-6;
+        cm.fill_per_cu = 1;
     } else {
         cm.bw_total = 5.4e12;
         cm.bw_block = 35.0e9;
         cm.blocks_per_cu = 2;
         cm.heads_per_block = 1;
         cm.t_block = 3.0e-6;
+        cm.fill_per_cu = 2;
+        if (kv8) {
+            cm.bw_block *= 0.5;
+            cm.bytes_per_token *= 0.5;
+            cm.fill_per_cu = 4;
+        }
     }
     return cm;
 }
@@ -114,8 +126,15 @@ double estimate(const CostModel &cm, int B, int Hq, int Hkv, const std::vector<i
 
 extern "C" int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, int capacity,
                          int page_size, int cu_count, int *num_splits_out) {
+    return fdec_plan_kv(B, Hq, Hkv, seq_lens_host, capacity, page_size, FDEC_BF16, cu_count, num_splits_out);
+}
+
+extern "C" int fdec_plan_kv(int B, int Hq, int Hkv, const int32_t *seq_lens_host, int capacity,
+                            int page_size, int kv_dtype, int cu_count, int *num_splits_out) {
     fdec_clear_error();
     if (!num_splits_out) return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: num_splits_out is NULL");
+    if (kv_dtype != FDEC_F16 && kv_dtype != FDEC_BF16 && kv_dtype != FDEC_FP8_E4M3)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: kv_dtype %d is not an fdec_dtype", kv_dtype);
     if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
         return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: need B >= 0, Hq >= 1, Hkv >= 1, Hq %% Hkv == 0");
     if (capacity < 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_plan: capacity must be >= 1");
@@ -135,7 +154,7 @@ extern "C" int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, i
         *num_splits_out = 1;
         return FDEC_OK;
     }
-    const CostModel cm = model_for(Hq, Hkv);
+    const CostModel cm = model_for(Hq, Hkv, kv_dtype == FDEC_FP8_E4M3);
     // Candidate split counts: every distinct chunk size, up to 64 blocks per slot.
     const int max_s = (int)std::min<int64_t>(FDEC_MAX_SPLITS, (capacity + FDEC_CHUNK_ALIGN - 1) / FDEC_CHUNK_ALIGN);
     const int64_t block_cap = (int64_t)64 * cu_count * cm.blocks_per_cu;
@@ -149,14 +168,15 @@ extern "C" int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, i
     // measured rate needs about two of them per CU (one request, 8 KV heads,
     // 128k tokens: 137 us at 19 splits, 97 us at 64; G = 2: 208 against 100;
     // eight 8k requests at G = 2: 90 us at 3 splits, 53 at 8), so its
-    // candidates start at two pairs per CU.
+    // candidates start at two pairs per CU (four over a float8 cache).
     const int groups = Hkv / cm.heads_per_block;
-    double total_bytes = 0.0;
-    for (int b = 0; b < B; ++b) total_bytes += (double)lens[b] * cm.bytes_per_token * Hkv;
+    // the work in 16-bit bytes: a float8 cache has the same tokens per wave
+    double work_bytes = 0.0;
+    for (int b = 0; b < B; ++b) work_bytes += (double)lens[b] * (2.0 * 128 * 2) * Hkv;
     // (the vector kernel already from 5 us of reading: 4k tokens x 32 KV heads,
     // 64 MB, 18.3 us at 16 splits against 23.4 at the fluid model's 5)
-    const bool bw_bound = total_bytes / cm.bw_total > (cm.blocks_per_cu == 1 ? 20.0e-6 : 5.0e-6);
-    const int64_t fill = cm.blocks_per_cu == 1 ? cu_count : 2 * (int64_t)cu_count;
+    const bool bw_bound = work_bytes / cm.bw_total > (cm.blocks_per_cu == 1 ? 20.0e-6 : 5.0e-6);
+    const int64_t fill = (int64_t)cm.fill_per_cu * cu_count;
     const int s_min = bw_bound ? (int)std::max<int64_t>(1, std::min<int64_t>(max_s, (fill + (int64_t)B * groups - 1) /
                                                                                          ((int64_t)B * groups)))
                                : 1;

@@ -166,6 +166,17 @@ int fdec_plan(int B, int Hq, int Hkv, const int32_t *seq_lens_host, int capacity
               int cu_count, int *num_splits_out);
 
 /*
+ * fdec_plan for a cache of element type kv_dtype (an fdec_dtype). fdec_plan is
+ * this call with a 16-bit cache. A float8 cache on the vector map kernel
+ * (shapes other than Hq = 4 or 8 Hkv) reads half the bytes per token at the
+ * same token rate per wave, so it is planned with more splits; the other
+ * shapes plan as for 16-bit caches. FDEC_ERR_INVALID_ARG for an unknown
+ * kv_dtype, else as fdec_plan. Host only, no HIP calls.
+ */
+int fdec_plan_kv(int B, int Hq, int Hkv, const int32_t *seq_lens_host, int capacity, int page_size,
+                 int kv_dtype, int cu_count, int *num_splits_out);
+
+/*
  * The four-rule split heuristic as the flash-attn cookbook states it
  * ([cookbook] §6.3 with §8.2's block count B*Hkv*num_splits): no split when the
  * blocks already cover 80% of the SMs; otherwise the SM efficiency
@@ -199,7 +210,8 @@ int fdec_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  *   seq_lens   device [B] int32: attended lengths, or (with append) cache_seqlens
  *              before the append. Never modified.
  *   num_splits >= 1 splits per (request, KV head); 0 = planned from capacity alone
- *              with fdec_plan (no device read), as num_splits=0 in [cookbook] §6.2.
+ *              with fdec_plan_kv for kv->dtype (no device read), as num_splits=0
+ *              in [cookbook] §6.2.
  *   softmax_scale 0 => 1/sqrt(D).
  *   append     NULL or an fdec_append (the caches in *kv are then written).
  *   fused      0 = map kernel + merge kernel; 1 = one kernel whose last-arriving

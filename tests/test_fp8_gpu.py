@@ -108,7 +108,7 @@ def test_fp8_full_size_workloads(name, mode):
                                      k_descale=d["k_descale"], v_descale=d["v_descale"])
     else:
         B, Hq, _ = case.q.shape
-        S = F.plan(B, Hq, case.Hkv, case.seq_lens.tolist(), case.capacity, case.page_size)
+        S = F.plan(B, Hq, case.Hkv, case.seq_lens.tolist(), case.capacity, case.page_size, kv_dtype=case.dtype)
         out, lse = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S,
                             k_descale=d["k_descale"], v_descale=d["v_descale"])
     torch.cuda.synchronize()

@@ -71,3 +71,23 @@ def test_plan_rejects_bad_lengths(fdec):
         F.plan(2, 32, 8, [10, 9999], 4096)
     with pytest.raises(F.FdecError):
         F.plan(2, 32, 8, None, 4096, page_size=8)
+
+
+def test_plan_kv_by_cache_type(fdec):
+    shapes = [(1, 8, 8, 131072), (1, 16, 8, 131072), (1, 32, 8, 131072), (1, 64, 8, 131072), (1, 32, 32, 4096),
+              (8, 16, 8, 8192), (32, 8, 8, 4096), (4, 16, 8, 2048), (3, 4, 1, 100)]
+    for B, Hq, Hkv, cap in shapes:
+        S16 = F.plan(B, Hq, Hkv, None, cap)
+        # fdec_plan is fdec_plan_kv with a 16-bit cache
+        assert F.plan(B, Hq, Hkv, None, cap, kv_dtype=F.FDEC_F16) == S16
+        assert F.plan(B, Hq, Hkv, None, cap, kv_dtype=F.FDEC_BF16) == S16
+        S8 = F.plan(B, Hq, Hkv, None, cap, kv_dtype=F.FDEC_FP8_E4M3)
+        assert 1 <= S8 <= F.MAX_SPLITS and F.split_chunk(cap, S8) >= 16
+        if Hq in (4 * Hkv, 8 * Hkv):
+            assert S8 == S16  # the matrix-core kernel plans the same for float8
+        else:
+            assert S8 >= S16  # a float8 wave streams half the bytes: at least as many splits
+    # one 128k-token request on the vector kernel: four (KV head, split) pairs per CU
+    assert 8 * F.plan(1, 16, 8, None, 131072, kv_dtype=F.FDEC_FP8_E4M3) >= 4 * 256
+    with pytest.raises(F.FdecError):
+        F.plan(1, 16, 8, None, 4096, kv_dtype=7)
