@@ -55,6 +55,11 @@ CASES = [
                                        PADS)),
     ("paged48_f16_lp", lambda: pad_left(paged_case(94, 6, 16, 4, 128, LENS, 48, F16, extra_pages=2, pad="nan"),
                                         PADS)),
+    # float8 caches: G = 4 (either map kernel with the path fixture) and G = 2 (the vector kernel)
+    ("contig_fp8_idx", lambda: indexed_case(101, 6, 16, 4, 128, LENS, PADS, 1024, FP8, cache_rows=9)),
+    ("contig_fp8_g2_idx", lambda: indexed_case(102, 6, 16, 8, 128, LENS, PADS, 1024, FP8, cache_rows=7)),
+    ("paged32_fp8_g2_lp", lambda: pad_left(paged_case(103, 6, 8, 4, 64, LENS, 32, FP8, extra_pages=2, pad="nan"),
+                                           PADS)),
 ]
 
 
