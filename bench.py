@@ -43,6 +43,8 @@ WORKLOAD_TEXT = {
             "131072 contiguous bf16 tokens",
     "c1f8": "unpaged MHA decode: B=1, Hq=Hkv=32, D=128, 4096 contiguous float8 e4m3fn tokens, "
             "per-(request, KV head) descales, bf16 queries, 16 splits",
+    "c2g2f8": "long-context GQA decode with two query heads per KV head: B=1, Hq=16, Hkv=8, D=128, "
+              "131072 contiguous float8 e4m3fn tokens, per-(request, KV head) descales, bf16 queries",
 }
 KERNEL_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
 
@@ -245,6 +247,14 @@ def pct(xs, p):
     return xs[min(len(xs) - 1, int(round(p / 100.0 * (len(xs) - 1))))]
 
 
+def map_kernel_name(case) -> str:
+    """The map kernel fdec_decode_partials runs for a case (default kernel paths)."""
+    G = case.q.shape[1] // case.Hkv
+    if case.D == 128 and G in (4, 8) and os.environ.get("FDEC_MAP_PATH") != "vector":
+        return "map_kernel_mfma_g4 (matrix cores)" if G == 4 else "map_kernel_mfma_g8 (matrix cores)"
+    return "map_kernel (vector)"
+
+
 def load_traffic(workload: str):
     """HBM traffic per launch from committed rocprofv3 counter summaries, if current."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
@@ -305,10 +315,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8", "c2g8", "c1f8"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8", "c2g8", "c1f8", "c2g2f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8",
+    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8,c2g2f8",
                     help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -347,7 +358,7 @@ def main() -> int:
     traffic = load_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "map_kernel_mfma_g4 (split-KV map stage on matrix cores, fdec_decode_partials)",
+                "kernel": map_kernel_name(case) + " (split-KV map stage, fdec_decode_partials)",
                 "avg_launch_us": round(kernel_ms * 1e3, 2), "algorithmic_bytes_per_launch": case.kv_bytes(),
                 "kernel_hash": kernel_hash()}
 

@@ -380,6 +380,8 @@ def workload(name: str, pad: str = "zero") -> Case:
         return contiguous_case(2, 1, 32, 8, 128, [131072], 131072, BF16, pad, "c2")
     if name == "c2f8":
         return contiguous_case(2, 1, 32, 8, 128, [131072], 131072, FP8, pad, "c2f8")
+    if name == "c2g2f8":  # the long-context request, two query heads per KV head, float8 cache (vector kernel)
+        return contiguous_case(2, 1, 16, 8, 128, [131072], 131072, FP8, pad, "c2g2f8")
     if name == "c2g8":  # the long-context request with eight query heads per KV head
         return contiguous_case(2, 1, 64, 8, 128, [131072], 131072, BF16, pad, "c2g8")
     if name == "c3f8":

@@ -98,7 +98,8 @@ def test_fp8_map_stage_states_match_oracle_states():
     assert err.max() < 1e-3
 
 
-@pytest.mark.parametrize("name,mode", [("c2f8", "two"), ("c3f8", "bal"), ("c3f8", "two"), ("c1f8", "two")])
+@pytest.mark.parametrize("name,mode", [("c2f8", "two"), ("c3f8", "bal"), ("c3f8", "two"), ("c1f8", "two"),
+                                       ("c2g2f8", "two")])
 def test_fp8_full_size_workloads(name, mode):
     case = workload(name, pad="nan")
     ref_out, ref_lse = oracle_decode(case)
