@@ -91,3 +91,8 @@ def test_plan_kv_by_cache_type(fdec):
     assert 8 * F.plan(1, 16, 8, None, 131072, kv_dtype=F.FDEC_FP8_E4M3) >= 4 * 256
     with pytest.raises(F.FdecError):
         F.plan(1, 16, 8, None, 4096, kv_dtype=7)
+    # the binding takes torch dtypes as well as fdec_dtype codes
+    import torch
+    assert F.plan(1, 16, 8, None, 131072, kv_dtype=torch.float8_e4m3fn) == \
+        F.plan(1, 16, 8, None, 131072, kv_dtype=F.FDEC_FP8_E4M3)
+    assert F.plan(1, 16, 8, None, 131072, kv_dtype=torch.float16) == F.plan(1, 16, 8, None, 131072)
