@@ -13,7 +13,7 @@ import torch
 import decode_attention_fdec_amd as F
 import oracle
 from helpers import LSE_RTOL, OUT_TOL, assert_parity, okv, oracle_decode, to_dev
-from synth import BF16, F16, append_case, contiguous_case, paged_case, workload
+from synth import BF16, F16, FP8, append_case, contiguous_case, paged_case, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -332,7 +332,7 @@ def test_c2_fixed_16_splits_equals_planned_splits():
 # ---------------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("name", ["gqa4_paged", "gqa2_contig", "append_rope"])
+@pytest.mark.parametrize("name", ["gqa4_paged", "gqa2_contig", "append_rope", "fp8_gqa2_paged"])
 def test_graph_replays_match_eager_bitwise(name, fused):
     # one step captured as a HIP graph and replayed several times, with eager
     # work and synchronisations between the replays; every replay must give
@@ -343,6 +343,8 @@ def test_graph_replays_match_eager_bitwise(name, fused):
         case = paged_case(58, 3, 32, 8, 128, [700, 33, 1500], 16, BF16, extra_pages=3, pad="nan")
     elif name == "gqa2_contig":
         case = contiguous_case(59, 2, 16, 8, 128, [999, 250], 1024, F16, pad="nan")
+    elif name == "fp8_gqa2_paged":  # float8 on the vector kernel, unit descales
+        case = paged_case(61, 3, 16, 8, 128, [700, 33, 1500], 16, FP8, extra_pages=3, pad="nan")
     else:
         case = append_case(60, 2, 32, 8, 128, 512, F16, rotary_dim=128, base=10000.0, pad="nan")
     d = to_dev(case)
