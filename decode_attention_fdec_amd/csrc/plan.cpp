@@ -175,8 +175,15 @@ extern "C" int fdec_plan_kv(int B, int Hq, int Hkv, const int32_t *seq_lens_host
     for (int b = 0; b < B; ++b) work_bytes += (double)lens[b] * (2.0 * 128 * 2) * Hkv;
     // (the vector kernel already from 5 us of reading: 4k tokens x 32 KV heads,
     // 64 MB, 18.3 us at 16 splits against 23.4 at the fluid model's 5)
-    const bool bw_bound = work_bytes / cm.bw_total > (cm.blocks_per_cu == 1 ? 20.0e-6 : 5.0e-6);
-    const int64_t fill = (int64_t)cm.fill_per_cu * cu_count;
+    const double work_s = work_bytes / cm.bw_total;
+    const bool bw_bound = work_s > (cm.blocks_per_cu == 1 ? 20.0e-6 : 5.0e-6);
+    // Long vector-kernel launches gain from four pairs per CU over 16-bit caches
+    // too (over 20 us of reading; µs at two → four pairs per CU: one 128k-token
+    // request with 8 KV heads, G = 1: 101.4 → 98.6, G = 2: 103.6 → 100.1; 32 4k
+    // requests, G = 1: 101.1 → 98.0; two 64k requests: 53.1 → 50.7), while
+    // shorter ones do not (4 2k requests, G = 2: 14.8 → 15.2).
+    const int fill_per_cu = (cm.blocks_per_cu != 1 && work_s > 20.0e-6) ? std::max(cm.fill_per_cu, 4) : cm.fill_per_cu;
+    const int64_t fill = (int64_t)fill_per_cu * cu_count;
     const int s_min = bw_bound ? (int)std::max<int64_t>(1, std::min<int64_t>(max_s, (fill + (int64_t)B * groups - 1) /
                                                                                          ((int64_t)B * groups)))
                                : 1;
