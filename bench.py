@@ -46,7 +46,9 @@ WORKLOAD_TEXT = {
     "c2g2f8": "long-context GQA decode with two query heads per KV head: B=1, Hq=16, Hkv=8, D=128, "
               "131072 contiguous float8 e4m3fn tokens, per-(request, KV head) descales, bf16 queries",
 }
-KERNEL_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "device_common.h", "fdec_internal.h", "merge.hip"]
+# every library source: a change to any of them (kernels, launch code, planner) marks stored counters stale
+KERNEL_SOURCES = sorted(f for f in os.listdir(os.path.join(ROOT, "decode_attention_fdec_amd", "csrc"))
+                        if f.endswith((".hip", ".h", ".cpp")))
 
 
 def log(msg: str) -> None:

@@ -19,6 +19,11 @@ thread_local char g_err[512] = "";
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Every layout starts with the fused path's arrival counters [B * Hkv] (zero
+// between calls), so that a workspace shared by every kind of call keeps them
+// intact: the balanced split's (first slot, count) records come after them.
+size_t counter_bytes(int B, int Hkv) { return align_up((size_t)B * Hkv * sizeof(int32_t)); }
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct WsLayout {
@@ -29,7 +34,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int S) {
     WsLayout w;
     const size_t states = (size_t)B * Hq * S;
     w.cnt = 0;
-    w.pm = align_up(w.cnt + (size_t)B * Hkv * sizeof(int32_t));
+    w.pm = counter_bytes(B, Hkv);
     w.pd = align_up(w.pm + states * sizeof(float));
     w.po = align_up(w.pd + states * sizeof(float));
     w.total = align_up(w.po + states * D * sizeof(float));
@@ -316,12 +321,13 @@ extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const 
     if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, nullptr);
     const int G = Hq / kv->num_kv_heads;
-    const bool mt16 = fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
+    // one query token: fdec_decode's own map kernel (vector or matrix-core), so
+    // the result is its two-kernel result bitwise for every shape
+    const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
                       (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
-    if (!mt16 && !(p.mfma && (G == 4 || q_len == 1)))
+    if (q_len > 1 && !mt16 && !(p.mfma && G == 4))
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: needs head_dim 128 and either Hq = 4 Hkv or q_len * Hq / Hkv >= 12 (16-bit caches)",
-                         fn);
+                         "%s: several query tokens need head_dim 128 and either Hq = 4 Hkv or a 16-bit cache", fn);
     const int ql = fdec::mfma_tokens_per_wave(q_len);
     p.q_len = q_len;
     p.q_groups = (q_len + ql - 1) / ql;
@@ -392,10 +398,10 @@ int balanced_blocks(int Hkv, int num_blocks, int per_cu) {
 struct BalLayout {
     size_t meta, pm, pd, po, total;
 };
-BalLayout bal_layout(int B, int Hq, int D, int nb) {
+BalLayout bal_layout(int B, int Hq, int Hkv, int D, int nb) {
     BalLayout w;
     const size_t states = (size_t)Hq * (size_t)(nb + B);
-    w.meta = 0;
+    w.meta = counter_bytes(B, Hkv);
     w.pm = align_up(w.meta + (size_t)B * 2 * sizeof(int32_t));
     w.pd = align_up(w.pm + states * sizeof(float));
     w.po = align_up(w.pd + states * sizeof(float));
@@ -406,7 +412,7 @@ BalLayout bal_layout(int B, int Hq, int D, int nb) {
 extern "C" size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_blocks) {
     if (B < 0 || Hq < 1 || Hkv < 1 || head_dim < 1 || num_blocks < 0 || num_blocks > FDEC_MAX_SPLITS) return 0;
     // the default of either cache format fits (the float8 one is the larger)
-    return bal_layout(B, Hq, head_dim, balanced_blocks(Hkv, num_blocks, 2)).total;
+    return bal_layout(B, Hq, Hkv, head_dim, balanced_blocks(Hkv, num_blocks, 2)).total;
 }
 
 // The balanced split for q_len query tokens per request (1: fdec_decode_balanced).
@@ -446,7 +452,7 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     if (mt16 && num_blocks == 0)
         nb = std::min(balanced_blocks(kv->num_kv_heads, 0, 2),
                       std::max(1, device_cus() / fdec::mt16_z_blocks(q_len, G, kv->num_kv_heads)));
-    const BalLayout w = bal_layout(B, q_len * Hq, kv->head_dim, nb);
+    const BalLayout w = bal_layout(B, q_len * Hq, kv->num_kv_heads, kv->head_dim, nb);
     if (!workspace || workspace_bytes < w.total)
         return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d blocks, got %zu", fn, w.total,
                          nb, workspace ? workspace_bytes : (size_t)0);
@@ -509,10 +515,10 @@ bool cascade_balanced_shape(int Hq, int Hkv, int D) { return Hq == 4 * Hkv && D 
 struct CascBalLayout {
     size_t meta, ppm, ppd, ppo, pm, pd, po, total;
 };
-CascBalLayout casc_bal_layout(int B, int Hq, int D, int sp, int ss) {
+CascBalLayout casc_bal_layout(int B, int Hq, int Hkv, int D, int sp, int ss) {
     CascBalLayout w;
     const size_t pstates = (size_t)B * Hq * sp, sstates = (size_t)Hq * (size_t)(ss + B);
-    w.meta = 0;
+    w.meta = counter_bytes(B, Hkv);
     w.ppm = align_up(w.meta + (size_t)B * 2 * sizeof(int32_t));
     w.ppd = align_up(w.ppm + pstates * sizeof(float));
     w.ppo = align_up(w.ppd + pstates * sizeof(float));
@@ -528,7 +534,7 @@ extern "C" size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_d
     if (splits_prefix < 1 || splits_suffix < 1 || B < 0 || Hq < 1 || Hkv < 1) return 0;
     size_t n = fdec_workspace_size(B, Hq, Hkv, head_dim, splits_prefix + splits_suffix);
     if (cascade_balanced_shape(Hq, Hkv, head_dim))
-        n = std::max(n, casc_bal_layout(B, Hq, head_dim, splits_prefix, splits_suffix).total);
+        n = std::max(n, casc_bal_layout(B, Hq, Hkv, head_dim, splits_prefix, splits_suffix).total);
     return n;
 }
 
@@ -637,7 +643,7 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     if (pb.mfma && cascade_balanced_shape(Hq, kv->num_kv_heads, kv->head_dim) &&
         (int64_t)B * (((int64_t)cap + 15) / 16) < (int64_t(1) << 31)) {
         // suffixes on the balanced split, then one merge of prefix states and suffix pieces
-        const CascBalLayout w = casc_bal_layout(B, Hq, kv->head_dim, sp, ss);
+        const CascBalLayout w = casc_bal_layout(B, Hq, kv->num_kv_heads, kv->head_dim, sp, ss);
         if (!workspace || workspace_bytes < w.total)
             return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d + %d splits, got %zu", fn,
                              w.total, sp, ss, workspace ? workspace_bytes : (size_t)0);

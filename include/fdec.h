@@ -98,8 +98,9 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  * fdec_decode and fdec_decode_partials (the matrix-core map kernel for
  * Hq = 4 or 8 Hkv at head_dim 128, the vector kernel otherwise); head_dim 128
  * with Hq = 4 Hkv in fdec_decode_balanced and fdec_decode_multi, and with
- * Hq = 8 Hkv in fdec_decode_balanced and in fdec_decode_multi with q_len = 1;
- * other calls and shapes return FDEC_ERR_UNSUPPORTED. The partial states then
+ * Hq = 8 Hkv in fdec_decode_balanced; fdec_decode_multi with q_len = 1 takes
+ * every shape fdec_decode does; other calls and shapes return
+ * FDEC_ERR_UNSUPPORTED. The partial states then
  * already include V's descale.
  */
 typedef struct fdec_kv {
@@ -149,7 +150,13 @@ typedef struct fdec_append {
     int rope_max_pos;     /* rows of the tables; seq_lens[b] < rope_max_pos (device data, trusted) */
 } fdec_append;
 
-/* Short text for a status code. Never NULL. */
+/* Short text for a status code. Never NULL. The codes follow the failure
+ * modes the vLLM notes list under "邊界與失敗" (an unsupported head size, cache
+ * type or block size makes the selector fall back to another backend): a shape
+ * this library does not build returns FDEC_ERR_UNSUPPORTED before any launch,
+ * so the caller can route it elsewhere; a workspace that is too small returns
+ * FDEC_ERR_WORKSPACE with the size it needs in fdec_last_error() instead of
+ * allocating (the out-of-memory case of [tbr8] §6.2 problem 1). */
 const char *fdec_status_string(int status);
 
 /* Detail message of the most recent failing call on this thread ("" if none). */
@@ -194,13 +201,29 @@ int fdec_plan_rules(int B, int Hkv, int sm_count, int max_splits, int *num_split
  */
 int64_t fdec_split_chunk(int capacity, int num_splits);
 
-/* Bytes of workspace fdec_decode needs for these sizes (num_splits >= 1). */
+/*
+ * Bytes of workspace fdec_decode needs for these sizes (num_splits >= 1); 0 on
+ * bad arguments. The workspace is one caller-owned contiguous device buffer
+ * that holds the partial states between the map and merge stages, as the
+ * workspace buffer handed to FlashInfer's decode wrapper ([tbr8] §3.1-3.2, and
+ * §6.2 problem 1 on sizing it for large batches and long sequences). Layout:
+ * the fused path's arrival counters [B * Hkv] int32 first, then m, d
+ * [B, Hq, S] and O~ [B, Hq, S, D] fp32, each 256-byte aligned.
+ * With num_splits = 0 in fdec_decode, a C caller sizes the workspace for the
+ * split count the call will use: fdec_plan_kv(B, Hq, Hkv, NULL, capacity,
+ * page_size, kv->dtype, 256, &S), then fdec_workspace_size(B, Hq, Hkv, D, S).
+ */
 size_t fdec_workspace_size(int B, int Hq, int Hkv, int head_dim, int num_splits);
 
 /*
- * Prepare a fresh workspace: zeroes the arrival counters the single-kernel
- * (fused) path uses, with a kernel on `stream`. Needed once per workspace
- * allocation; every completed fdec_decode call leaves the counters at zero.
+ * Prepare a fresh workspace: zeroes it (in particular the arrival counters the
+ * single-kernel (fused) path uses) with a kernel on `stream`. Every call lays
+ * out its data after the first B * Hkv 32-bit words of the workspace (rounded
+ * up to 256 bytes), which are those counters, and a completed fused call
+ * leaves them at zero; so one initialisation serves every later call of any
+ * kind with the same or a smaller B * Hkv. Before a fused call whose B * Hkv
+ * (B * q_len * Hkv for fdec_decode_multi) exceeds that of a call made since the
+ * last initialisation, initialise again. No allocation ([tbr8] §3.1 workspace).
  */
 int fdec_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
@@ -264,11 +287,13 @@ int fdec_merge_states(const float *part_o, const float *part_m, const float *par
  *   out  device [B, q_len, Hq, D] fp32; lse device [B, Hq, q_len] fp32 or NULL
  *        ([cookbook] §3.5 softmax_lse shape (batch, heads, seqlen_q))
  *   num_splits, softmax_scale as in fdec_decode (splits over the request's rows)
- *   1 <= q_len <= FDEC_MAX_QLEN. Built for head_dim 128, page_size a multiple
- *   of 16 or contiguous: every Hq / Hkv with fp16 / bf16 caches, and float8
- *   caches with Hq = 4 Hkv, or Hq = 8 Hkv and q_len = 1 (FDEC_ERR_UNSUPPORTED
+ *   1 <= q_len <= FDEC_MAX_QLEN. q_len = 1 runs fdec_decode's map and merge
+ *   kernels: every shape fdec_decode takes without append, and the result is
+ *   fdec_decode's two-kernel result bitwise. q_len > 1 is built for head_dim
+ *   128, page_size a multiple of 16 or contiguous: every Hq / Hkv with fp16 /
+ *   bf16 caches, and float8 caches with Hq = 4 Hkv (FDEC_ERR_UNSUPPORTED
  *   otherwise); no append. workspace >= fdec_workspace_size(B * q_len, Hq, Hkv,
- *   head_dim, S). q_len = 1 gives fdec_decode's two-kernel result bitwise.
+ *   head_dim, S).
  */
 int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
                       int num_splits, float softmax_scale, float *out, float *lse, void *workspace,

@@ -52,3 +52,33 @@ def to_dev(case, device="cuda"):
         t = getattr(case, name)
         d[name] = None if t is None else t.to(device).contiguous()
     return d
+
+
+def appended_row_mask(case):
+    """Boolean mask over the K cache: the row each append writes ("Inference Cookbook"
+    §3.3: the new token goes to row cache_seqlens[b]), for every KV head and d.
+    Paged caches: slot c % page of page page_table[b, c // page]; contiguous caches:
+    row c of cache row cache_batch_idx[b] (b without one)."""
+    mask = np.zeros(tuple(case.k.shape), dtype=bool)
+    for b in range(case.B):
+        c = int(case.seq_lens[b])
+        if case.page_size:
+            mask[int(case.page_table[b, c // case.page_size]), c % case.page_size] = True
+        else:
+            row = int(case.cache_batch_idx[b]) if case.cache_batch_idx is not None else b
+            mask[row, c] = True
+    return mask
+
+
+def check_append_k(kg, kc, case, what=""):
+    """The K cache after an append (kg: GPU, kc: oracle, both as uint16 bit patterns).
+    Every element outside the appended rows is bitwise equal; an appended (rotated)
+    element may differ from the oracle's single rounding by one unit in the last place
+    (the kernel rotates in fp32, the oracle in double). Returns the number of appended
+    elements that differ by that one ulp."""
+    m = appended_row_mask(case)
+    assert kg.shape == kc.shape == m.shape
+    assert np.array_equal(kg[~m], kc[~m]), f"{what}: a K element outside the appended rows differs"
+    diff = np.abs(kg[m].astype(np.int32) - kc[m].astype(np.int32))
+    assert diff.size == 0 or diff.max() <= 1, f"{what}: an appended K element is off by more than 1 ulp"
+    return int((diff > 0).sum())

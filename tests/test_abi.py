@@ -219,12 +219,13 @@ def test_balanced_validation(fdec):
 
 
 def test_balanced_workspace_size(fdec):
-    # meta [B, 2] int32, then m, d and O~ for Hq x (num_blocks + B) slots, each array 256-byte aligned
+    # the fused path's counters [B, Hkv] int32 (kept clear for it), meta [B, 2] int32, then m, d and O~
+    # for Hq x (num_blocks + B) slots, each array 256-byte aligned
     def up(n):
         return (n + 255) // 256 * 256
     B, Hq, D, nb = 3, 32, 128, 10
     slots = Hq * (nb + B)
-    want = up(up(up(B * 8) + slots * 4) + slots * 4) + up(slots * D * 4)
+    want = up(up(up(up(B * 8 * 4) + B * 8) + slots * 4) + slots * 4) + up(slots * D * 4)
     assert F.balanced_workspace_size(B, Hq, 8, D, nb) == want
     with pytest.raises(F.FdecError):
         F.balanced_workspace_size(B, Hq, 8, D, 257)
@@ -273,3 +274,4 @@ def test_binding_checks_index_tensors(fdec):
     kv = F.make_kv(k, k, cache_batch_idx=torch.zeros(2, dtype=torch.int32),
                    cache_leftpad=torch.zeros(2, dtype=torch.int32))
     assert kv.cache_batch_idx and kv.cache_leftpad
+

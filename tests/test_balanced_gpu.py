@@ -107,3 +107,36 @@ def test_balanced_graph_replay_follows_new_lengths():
         case.seq_lens = torch.tensor(lens, dtype=torch.int32)
         ref_out, ref_lse = oracle_decode(case)
         assert_parity(out.clone(), lse.clone(), ref_out, ref_lse, case.dtype, f"graph replay lens={lens}")
+
+
+@pytest.mark.parametrize("first", ["balanced", "multi_balanced", "cascade"])
+def test_shared_workspace_keeps_fused_counters(first):
+    """A workspace used by a balanced-split call (whose per-request records are
+    device metadata) then serves a fused fdec_decode unchanged: the fused
+    output equals the two-kernel output bitwise, and the arrival counters are
+    back at zero afterwards."""
+    case = paged_case(91, 4, 32, 8, 128, [1500, 3, 700, 64], 16, BF16, extra_pages=2, pad="nan")
+    d = to_dev(case)
+    S = 6
+    size = max(F.workspace_size(case.B, case.Hq, case.Hkv, 128, S),
+               F.balanced_workspace_size(case.B, case.Hq, case.Hkv, 128, 0),
+               F.balanced_workspace_size(case.B, 2 * case.Hq, case.Hkv, 128, 0),
+               F.cascade_workspace_size(case.B, case.Hq, case.Hkv, 128, 4, 4))
+    ws = F.Workspace(size)
+    if first == "balanced":
+        F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], workspace=ws)
+    elif first == "multi_balanced":
+        q2 = torch.cat([d["q"][:, None], d["q"][:, None]], 1).contiguous()
+        F.decode_multi_balanced(q2, d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], workspace=ws)
+    else:
+        F.cascade_decode(d["q"], d["k"], d["v"], d["page_table"], d["page_table"][0], 32, d["seq_lens"],
+                         splits_prefix=4, splits_suffix=4, workspace=ws)
+    o_f, l_f = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S,
+                        fused=True, workspace=ws)
+    o_2, l_2 = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o_f, o_2) and torch.equal(l_f, l_2)
+    counters = ws.buf[: case.B * case.Hkv * 4].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+    ref_out, ref_lse = oracle_decode(case)
+    assert_parity(o_f, l_f, ref_out, ref_lse, case.dtype, f"fused after {first}")

@@ -88,15 +88,19 @@ def test_multi_token_with_leftpad_and_batch_idx(q_len):
     check(out, lse, ref_out, ref_lse, F16, f"paged leftpad q_len={q_len}")
 
 
-def test_one_token_equals_single_query_decode_bitwise():
-    case = paged_case(244, 5, 32, 8, 128, [900, 1, 16, 0, 333], 16, BF16, extra_pages=2, pad="nan")
+@pytest.mark.parametrize("G,D,dt", [(4, 128, BF16), (1, 128, F16), (2, 128, BF16), (8, 128, BF16), (2, 64, F16),
+                                    (1, 128, FP8)])
+def test_one_token_equals_single_query_decode_bitwise(G, D, dt):
+    # one query token runs fdec_decode's own map kernel, whichever it is for the shape
+    case = paged_case(244 + G, 5, 8 * G, 8, D, [900, 1, 16, 0, 333], 16, dt, extra_pages=2, pad="nan")
     d = to_dev(case)
+    kw = dict(k_descale=d["k_descale"], v_descale=d["v_descale"])
     for S in (1, 7):
-        o1, l1 = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S)
+        o1, l1 = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S, **kw)
         om, lm = F.decode_multi(d["q"][:, None].contiguous(), d["k"], d["v"], d["seq_lens"],
-                                page_table=d["page_table"], num_splits=S)
+                                page_table=d["page_table"], num_splits=S, **kw)
         torch.cuda.synchronize()
-        assert torch.equal(om[:, 0], o1) and torch.equal(lm[:, :, 0], l1), f"S={S}"
+        assert torch.equal(om[:, 0], o1) and torch.equal(lm[:, :, 0], l1), f"G={G} D={D} S={S}"
 
 
 @pytest.mark.parametrize("q_len", [2, 4])
