@@ -80,6 +80,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_workspace_init.argtypes = [P, Z, P]
     lib.fdec_decode.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F, ctypes.POINTER(FdecAppend), I,
                                 P, P, P, Z, P]
+    lib.fdec_decode_noalloc.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F, ctypes.POINTER(FdecAppend), I,
+                                        P, P, P]
     lib.fdec_decode_partials.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F,
                                          ctypes.POINTER(FdecAppend), P, P, P, P]
     lib.fdec_merge_states.argtypes = [P, P, P, I, I, I, I, P, P, P]
@@ -256,6 +258,29 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Te
                            float(softmax_scale), ctypes.byref(append) if append is not None else None,
                            int(bool(fused)), out.data_ptr(), _ptr(lse), workspace.buf.data_ptr(),
                            workspace.nbytes, _stream(q.device)))
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                   page_table: Optional[torch.Tensor] = None, num_splits: int = 0, softmax_scale: float = 0.0,
+                   append: Optional[FdecAppend] = None, fused: bool = False, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                   k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None,
+                   cache_batch_idx: Optional[torch.Tensor] = None, cache_leftpad: Optional[torch.Tensor] = None):
+    """fdec_decode_noalloc: fdec_decode on the library's own device scratch (no workspace).
+
+    Allocates nothing when out (and lse, or return_lse=False) are passed in."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    kv = make_kv(k, v, page_table, k_descale, v_descale, cache_batch_idx, cache_leftpad)
+    _check_q(q, k)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    _check(lib.fdec_decode_noalloc(q.data_ptr(), B, Hq, ctypes.byref(kv), seq_lens.data_ptr(), int(num_splits),
+                                   float(softmax_scale), ctypes.byref(append) if append is not None else None,
+                                   int(bool(fused)), out.data_ptr(), _ptr(lse), _stream(q.device)))
     return out, lse
 
 

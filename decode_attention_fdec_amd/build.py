@@ -28,7 +28,8 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-munsafe-fp-atomics"]
 
-HIP_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "multitoken.hip", "merge.hip", "cascade.hip", "probe.hip"]
+HIP_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "multitoken.hip", "merge.hip", "cascade.hip", "probe.hip",
+               "noalloc.hip"]
 CPP_SOURCES = ["api.cpp", "plan.cpp"]
 
 

@@ -256,45 +256,74 @@ extern "C" int fdec_workspace_init(void *workspace, size_t bytes, void *stream) 
                      "fdec_workspace_init");
 }
 
+// Validation of fdec_decode's arguments other than the workspace; resolves the
+// split count (num_splits = 0: planned from the capacity).
+int fdec_decode_validate(const char *fn, const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                         int num_splits, float softmax_scale, const fdec_append *append, int fused, float *out,
+                         float *lse, int *S_out) {
+    int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
+    if (rc) return rc;
+    if ((rc = validate_append(fn, append, kv))) return rc;
+    if (kv->dtype == FDEC_FP8_E4M3 && append)
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: append into a float8 cache is not built", fn);
+    if (fused != 0 && fused != 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: fused must be 0 or 1", fn);
+    if ((rc = resolve_splits(fn, num_splits, B, Hq, kv, S_out))) return rc;
+    if (B == 0) return FDEC_OK;
+    if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
+    return FDEC_OK;
+}
+
+size_t fdec_decode_state_bytes(int B, int Hq, int D, int S) {
+    // the state part of ws_layout, from its 256-byte aligned start
+    return ws_layout(B, Hq, 1, D, S).total - counter_bytes(B, 1);
+}
+
+// fdec_decode's launches once validated: states (m, d, O~ as in ws_layout) from
+// `states`, arrival counters [B * Hkv] at `counters` (all zero; fused only).
+int fdec_decode_launch(const char *fn, const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
+                       int S, float softmax_scale, const fdec_append *append, int fused, float *out, float *lse,
+                       int *counters, char *states, void *stream) {
+    if (B == 0) return FDEC_OK;
+    const WsLayout w = ws_layout(B, Hq, 1, kv->head_dim, S);
+    const size_t base = counter_bytes(B, 1);
+    fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, append);
+    p.pm = reinterpret_cast<float *>(states + (w.pm - base));
+    p.pd = reinterpret_cast<float *>(states + (w.pd - base));
+    p.po = reinterpret_cast<float *>(states + (w.po - base));
+    p.s_total = S;
+    p.s_offset = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fused) {
+        p.counters = counters;
+        p.out = out;
+        p.lse = lse;
+        return check_hip(fdec::launch_map(p, S, st), "fdec_decode: map+merge launch");
+    }
+    int rc = check_hip(fdec::launch_map(p, S, st), "fdec_decode: map launch");
+    if (rc) return rc;
+    (void)fn;
+    return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st),
+                     "fdec_decode: merge launch");
+}
+
 extern "C" int fdec_decode(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
                            int num_splits, float softmax_scale, const fdec_append *append, int fused,
                            float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
     fdec_clear_error();
     const char *fn = "fdec_decode";
-    int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
-    if (rc) return rc;
-    if ((rc = validate_append(fn, append, kv))) return rc;
-    if (fused != 0 && fused != 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: fused must be 0 or 1", fn);
     int S = 0;
-    if ((rc = resolve_splits(fn, num_splits, B, Hq, kv, &S))) return rc;
-    if (B == 0) return FDEC_OK;
-    if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
-    if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
+    int rc = fdec_decode_validate(fn, q, B, Hq, kv, seq_lens, num_splits, softmax_scale, append, fused, out, lse, &S);
+    if (rc || B == 0) return rc;
     const WsLayout w = ws_layout(B, Hq, kv->num_kv_heads, kv->head_dim, S);
     if (!workspace || workspace_bytes < w.total)
         return fdec_fail(FDEC_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d splits, got %zu", fn,
                          w.total, S, workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
-
     char *ws = static_cast<char *>(workspace);
-    fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, append);
-    if ((rc = check_fp8(fn, kv, p, append))) return rc;
-    p.pm = reinterpret_cast<float *>(ws + w.pm);
-    p.pd = reinterpret_cast<float *>(ws + w.pd);
-    p.po = reinterpret_cast<float *>(ws + w.po);
-    p.s_total = S;
-    p.s_offset = 0;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (fused) {
-        p.counters = reinterpret_cast<int *>(ws + w.cnt);
-        p.out = out;
-        p.lse = lse;
-        return check_hip(fdec::launch_map(p, S, st), "fdec_decode: map+merge launch");
-    }
-    if ((rc = check_hip(fdec::launch_map(p, S, st), "fdec_decode: map launch"))) return rc;
-    return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st),
-                     "fdec_decode: merge launch");
+    return fdec_decode_launch(fn, q, B, Hq, kv, seq_lens, S, softmax_scale, append, fused, out, lse,
+                              reinterpret_cast<int *>(ws + w.cnt), ws + w.pm, stream);
 }
 
 extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const fdec_kv *kv,

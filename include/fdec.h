@@ -249,6 +249,27 @@ int fdec_decode(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *
                 float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fdec_decode without a workspace, for callers that cannot allocate device
+ * memory at the call: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, kernels and results as
+ * fdec_decode (bitwise), minus the workspace: the partial states and arrival
+ * counters live in the library's own device array of
+ * FDEC_NOALLOC_SCRATCH_BYTES, one per GPU, held from the first call on that GPU
+ * until the process ends (the first call on a device resolves its address).
+ * Calls needing more than that (the states of B * Hq * S splits,
+ * fdec_workspace_size minus the counters, beyond FDEC_NOALLOC_SCRATCH_BYTES -
+ * 64 KiB, or B * Hkv > 16384) return FDEC_ERR_WORKSPACE before any launch.
+ * Every call on one GPU shares that array and leaves it holding its own
+ * states: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller. With fused = 1 a kernel
+ * first clears the call's counters. Allocates nothing, never synchronises.
+ */
+#define FDEC_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fdec_decode_noalloc(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens, int num_splits,
+                        float softmax_scale, const fdec_append *append, int fused, float *out, float *lse,
+                        void *stream);
+
+/*
  * The map stage alone ([lpnh] §2 stage 1): writes every split's partial state
  * for each (b, h) and split s < num_splits (num_splits >= 1 here):
  *   part_o [B, Hq, num_splits, D] fp32  O~ = sum_j exp(s_j - m) v_j over the split,

@@ -275,3 +275,23 @@ def test_binding_checks_index_tensors(fdec):
                    cache_leftpad=torch.zeros(2, dtype=torch.int32))
     assert kv.cache_batch_idx and kv.cache_leftpad
 
+
+def call_noalloc(kv, B=1, Hq=32, num_splits=4, fused=0, q=FAKE, seq=FAKE, out=FAKE):
+    lib = F.load_library()
+    return lib.fdec_decode_noalloc(q, B, Hq, ctypes.byref(kv), seq, num_splits, 0.0, None, fused, out, None, None)
+
+
+def test_noalloc_validates_like_decode_and_bounds_its_scratch(fdec):
+    # the argument checks of fdec_decode, then the scratch bound, all before any HIP call
+    assert call_noalloc(kv_struct(num_kv_heads=5)) == F.FDEC_ERR_INVALID_ARG
+    assert call_noalloc(kv_struct(head_dim=96)) == F.FDEC_ERR_UNSUPPORTED
+    assert call_noalloc(kv_struct(), q=None) == F.FDEC_ERR_INVALID_ARG
+    assert call_noalloc(kv_struct(), num_splits=-1) == F.FDEC_ERR_INVALID_ARG
+    assert call_noalloc(kv_struct(), fused=2) == F.FDEC_ERR_INVALID_ARG
+    # states of B * Hq * S splits beyond FDEC_NOALLOC_SCRATCH_BYTES - 64 KiB
+    assert call_noalloc(kv_struct(), B=64, Hq=64, num_splits=256) == F.FDEC_ERR_WORKSPACE
+    assert "scratch" in last_error()
+    # more than 16384 (request, KV head) counters
+    assert call_noalloc(kv_struct(num_kv_heads=8, capacity=16), B=4096, Hq=8, num_splits=1) == F.FDEC_ERR_WORKSPACE
+    # B = 0 is a valid empty call
+    assert call_noalloc(kv_struct(), B=0) == F.FDEC_OK
