@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0  # dense bf16 / fp16 matrix peak
 METRIC = "decode attention µs/step + achieved KV-read GB/s (% of 8 TB/s HBM peak)"
 WORKLOAD_TEXT = {
     "c1": "unpaged MHA decode: B=1, Hq=Hkv=32, D=128, 4096 contiguous fp16 tokens, 16 splits",
@@ -179,30 +180,66 @@ def time_per_launch(runner: Runner, steps: int, copy=None):
     return sorted(a.elapsed_time(b) for a, b in ev)  # ms
 
 
-def time_map_kernel(F, runner: Runner, steps: int):
-    """Per-launch durations of the map kernel alone (fdec_decode_partials)."""
+def stage_labels(runner: Runner):
+    """The kernels one step launches, in order."""
+    if runner.cascade:
+        return ["cascade prefix (matrix cores)", "suffix map (balanced split)", "cascade merge"]
+    if runner.mode == "bal":
+        return ["map (balanced split)", "segment merge"]
+    if runner.mode == "fused":
+        return ["map + merge (single kernel)"]
+    return ["map", "merge"]
+
+
+def time_stages(F, runner: Runner, steps: int) -> dict:
+    """Mean duration (us) of each kernel of a step, from the library's stage-timing
+    events (fdec_trace_start / fdec_trace_stop) on the launch stream, over `steps`
+    back-to-back steps."""
     import torch
 
-    case = runner.case
-    B, Hq, D = case.q.shape
-    S = runner.S
-    if S == 0:  # the balanced split has no map-only entry: time the uniform map at the planner's count
-        S = F.plan(B, Hq, case.Hkv, case.seq_lens.tolist(), case.capacity, case.page_size, kv_dtype=case.dtype)
-    po = torch.empty(B, Hq, S, D, dtype=torch.float32, device=runner.dev)
-    pm = torch.empty(B, Hq, S, dtype=torch.float32, device=runner.dev)
-    pd = torch.empty(B, Hq, S, dtype=torch.float32, device=runner.dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(3 + steps):
-        c = i % runner.copies
-        if i >= 3:
-            ev[i - 3][0].record()
-        F.decode_partials(runner.q, runner.k[c], runner.v[c], runner.lens, S, page_table=runner.table,
-                          append=runner.append, part_o=po, part_m=pm, part_d=pd, k_descale=runner.kd,
-                          v_descale=runner.vd)
-        if i >= 3:
-            ev[i - 3][1].record()
+    for _ in range(3):
+        runner.step()
     torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in ev)
+    F.trace_start(8 * steps + 8)
+    for _ in range(steps):
+        runner.step()
+    ms, kinds = F.trace_stop()
+    by = {}
+    for m, k in zip(ms, kinds):
+        if k >= 1:
+            by.setdefault(k, []).append(m * 1e3)
+    labels = stage_labels(runner)
+    return {(labels[k - 1] if k - 1 < len(labels) else f"kernel {k}"): round(sum(v) / len(v), 2)
+            for k, v in sorted(by.items())}
+
+
+def roofline_entry(case, stages: dict, runner: Runner) -> dict:
+    """HBM roofline of the step's dominant kernel(s): algorithmic bytes / mean duration."""
+    out = {}
+    if runner.cascade:
+        pre = case.prefix_len * case.Hkv * 2 * case.D * case.k.element_size()
+        suf = case.kv_bytes() - pre
+        t_pre = stages["cascade prefix (matrix cores)"]
+        t_suf = stages["suffix map (balanced split)"]
+        rows = case.B * case.Hq
+        flops = 4.0 * case.D * rows * case.prefix_len
+        out["prefix"] = {"bound": "hbm", "achieved": round(pre / (t_pre * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(pre / (t_pre * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "avg_launch_us": t_pre, "algorithmic_bytes_per_launch": pre,
+                         "tflops": round(flops / (t_pre * 1e-6) / 1e12, 1), "mfma_peak_tflops": MFMA_BF16_TFLOPS,
+                         "floor_us": round(max(pre / HBM_PEAK_GBS / 1e3, flops / MFMA_BF16_TFLOPS / 1e6), 2),
+                         "frac_of_floor": round(max(pre / HBM_PEAK_GBS / 1e3, flops / MFMA_BF16_TFLOPS / 1e6) / t_pre,
+                                                4)}
+        out["suffix"] = {"bound": "hbm", "achieved": round(suf / (t_suf * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(suf / (t_suf * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "avg_launch_us": t_suf, "algorithmic_bytes_per_launch": suf}
+        return out
+    label = next(iter(stages))
+    t = stages[label]
+    nb = case.kv_bytes()
+    return {"bound": "hbm", "achieved": round(nb / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(nb / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "kernel": label, "avg_launch_us": t,
+            "algorithmic_bytes_per_launch": nb}
 
 
 CALIB_BYTES = 256 << 20
@@ -238,11 +275,89 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> dict:
     fetch_scale = CALIB_BYTES / 1024.0 / last(f, "read_kernel")
     write_scale = CALIB_BYTES / 1024.0 / last(w, "copy_kernel")
     fk, wk = pick(f, "map_kernel"), pick(w, "map_kernel")
-    return {"fetch_kib": fk, "write_kib": wk, "fetch_scale": round(fetch_scale, 4),
-            "write_scale": round(write_scale, 4),
-            "traffic_bytes": int(round((fk * fetch_scale + wk * write_scale) * 1024)),
-            "read_bytes": int(round(fk * fetch_scale * 1024)), "write_bytes": int(round(wk * write_scale * 1024)),
-            "kernel_hash": kernel_hash()}
+    kernels = {}  # every library kernel of the run: median scaled bytes per dispatch
+    for name in sorted(set(f) | set(w)):
+        short = re.sub(r"\(.*", "", name).replace("void ", "").strip()
+        if not short.startswith("fdec::"):
+            continue
+        fr, wr = pick(f, name), pick(w, name)
+        kernels[short] = {"read_bytes": None if fr is None else int(round(fr * fetch_scale * 1024)),
+                          "write_bytes": None if wr is None else int(round(wr * write_scale * 1024))}
+    res = {"fetch_kib": fk, "write_kib": wk, "fetch_scale": round(fetch_scale, 4),
+           "write_scale": round(write_scale, 4), "kernels": kernels, "kernel_hash": kernel_hash()}
+    if fk is not None and wk is not None:
+        res.update({"traffic_bytes": int(round((fk * fetch_scale + wk * write_scale) * 1024)),
+                    "read_bytes": int(round(fk * fetch_scale * 1024)),
+                    "write_bytes": int(round(wk * write_scale * 1024))})
+    return res
+
+
+def probe_ceiling(F, nbytes: int, dev, reps: int = 20) -> dict:
+    """What the memory system delivers at this footprint: the median rate of
+    fdec_probe_read (best-effort streaming read, non-temporal 16-byte loads) and
+    of fdec_probe_stream (the map kernels' LDS-DMA load path, static slices) over
+    nbytes, rotating three buffers so the last-level cache cannot serve repeats."""
+    import torch
+
+    n = max(64 << 20, (nbytes + (256 << 10) - 1) // (256 << 10) * (256 << 10))
+    bufs = [torch.ones(n, dtype=torch.uint8, device=dev) for _ in range(3)]
+    sink = torch.zeros(F.PROBE_BLOCKS + 1, dtype=torch.int32, device=dev)
+    out = {}
+    for key, fn in (("probe_read_GBps", lambda b: F.probe_read(b, sink)),
+                    ("probe_lds_dma_GBps", lambda b: F.probe_stream(b, F.PROBE_STATIC, 1, sink))):
+        for i in range(3):
+            fn(bufs[i])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            fn(bufs[i % 3])
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        out[key] = round(n / (t[len(t) // 2] * 1e-3) / 1e9, 1)
+    out["probe_bytes"] = n
+    del bufs
+    return out
+
+
+SQ_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE",
+               "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
+
+
+def summarize_counters(paths, cu_count: int = 256) -> dict:
+    """Per-kernel medians (over dispatches) of rocprofv3 --pmc csv files, with the
+    derived figures rocprofv3 defines for them:
+      occupancy_pct  = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs / 32
+                       (resident waves as % of 32 per CU; the counter is in quad-cycles),
+      waves_per_cu   = 4 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs,
+      lds_bank_conflicts_per_access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT),
+      lds_bank_conflict_pct_of_time = 100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs;
+    FETCH_SIZE / WRITE_SIZE (KiB) in bytes with the calibration scales when given."""
+    import csv
+
+    per = {}  # kernel -> counter -> dispatch -> value (summed over dimensions)
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "").strip()
+            c = r["Counter_Name"]
+            d = per.setdefault(k, {}).setdefault(c, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for k, cs in per.items():
+        med = {c: sorted(v.values())[len(v) // 2] for c, v in cs.items()}
+        med["dispatches"] = max(len(v) for v in cs.values())
+        g = med.get("GRBM_GUI_ACTIVE")
+        if g and "SQ_WAVE_CYCLES" in med:
+            med["occupancy_pct"] = round(400.0 * med["SQ_WAVE_CYCLES"] / g / cu_count / 32, 2)
+            med["waves_per_cu"] = round(4.0 * med["SQ_WAVE_CYCLES"] / g / cu_count, 3)
+        if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
+            act = med["SQ_LDS_IDX_ACTIVE"] - med["SQ_LDS_BANK_CONFLICT"]
+            med["lds_bank_conflicts_per_access"] = round(med["SQ_LDS_BANK_CONFLICT"] / act, 5) if act > 0 else None
+            if g:
+                med["lds_bank_conflict_pct_of_time"] = round(100.0 * med["SQ_LDS_BANK_CONFLICT"] / g / cu_count, 4)
+        out[k] = med
+    return out
 
 
 def pct(xs, p):
@@ -269,8 +384,22 @@ def load_traffic(workload: str):
     return t.get("traffic_bytes")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s: float):
-    """The fp64 oracle on the same workload, timed on this host's cores."""
+    """The fp64 oracle on the same workload, timed on this host's cores: whole
+    passes over the workload with every host thread (OpenMP over (request, query
+    head)) and with one thread, median of 3 timed runs each. A run repeats passes
+    until it has taken budget_s / 6 seconds (at least one pass)."""
     import oracle
 
     oracle.build(force=False)
@@ -278,18 +407,28 @@ def cpu_baseline(case, budget_s: float):
                    case.prefix_pages, case.prefix_len, case.k_descale, case.v_descale)
     q = oracle.to_f64(case.q, oracle.dtype_code(case.q))
     scale = 1.0 / math.sqrt(case.D)
+
+    def rate(threads):
+        runs = []
+        for _ in range(3):
+            reps, t0 = 0, oracle.now()
+            while True:
+                oracle.decode(kv, q, case.seq_lens, scale, threads)
+                reps += 1
+                if oracle.now() - t0 >= budget_s / 6 or reps >= 1000:
+                    break
+            runs.append(case.kv_bytes() * reps / (oracle.now() - t0) / 1e9)
+        return sorted(runs)[1], [round(r, 4) for r in runs]
+
     threads = oracle.max_threads()
-    reps, t0 = 0, oracle.now()
-    while True:
-        oracle.decode(kv, q, case.seq_lens, scale, threads)
-        reps += 1
-        if oracle.now() - t0 >= budget_s or reps >= 1000:
-            break
-    dt = oracle.now() - t0
-    return {"value": round(case.kv_bytes() * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the full workload ({case.name}), decoded {reps} time(s) by the fp64 oracle in "
-                      f"{dt:.1f} s with {threads} OpenMP threads; rate = KV bytes per pass x passes / time"}
+    all_rate, all_runs = rate(threads)
+    one_rate, one_runs = rate(1)
+    return {"value": round(all_rate, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole passes of the fp64 oracle over the full workload ({case.name}, "
+                      f"{case.kv_bytes()} KV bytes per pass), median of 3 runs of >= {budget_s / 6:.1f} s with "
+                      f"{threads} OpenMP threads; rate = KV bytes per pass x passes / time",
+            "runs_GBps": all_runs, "single_thread_GBps": round(one_rate, 4), "single_thread_runs_GBps": one_runs,
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: int, dev):
@@ -302,12 +441,14 @@ def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: i
     ms = time_region(runner, steps, warmup)
     per = time_per_launch(runner, steps)
     warm = time_region(runner, steps, 2, copy=0)
+    stages = time_stages(F, runner, steps)
     nbytes = case.kv_bytes()
     res = {"us_per_step": round(ms * 1e3, 2), "kv_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "pct_of_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
            "step_us_p10_p50_p90": [round(pct(per, p) * 1e3, 2) for p in (10, 50, 90)],
            "warm_us_per_step": round(warm * 1e3, 2), "num_splits": runner.S, "mode": mode,
-           "kv_copies_rotated": runner.copies}
+           "kv_copies_rotated": runner.copies, "kernel_us": stages,
+           "roofline": roofline_entry(case, stages, runner)}
     log(f"[bench] {name}: {res['us_per_step']} us/step, {res['GBps']} GB/s ({res['pct_of_peak']}% of peak)")
     return case, runner, res, per
 
@@ -318,18 +459,24 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c2f8", "c3f8", "c2g8", "c1f8", "c2g2f8"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "c2f8", "c3f8", "c2g8", "c1f8", "c2g2f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
     ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8,c2g2f8",
                     help="other workloads timed for context ('' = none)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0, help="CPU oracle timing budget (all runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probes (profiler runs)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain read and a plain copy of 256 MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE csv files and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="per-kernel medians of rocprofv3 --pmc csv files (occupancy, LDS bank conflicts) and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return 0
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
         return 0
@@ -352,35 +499,20 @@ def main() -> int:
 
     case, runner, res, per = measure_workload(F, args.workload, args.mode, args.splits, args.steps,
                                               args.warmup, dev)
-    # the dominant kernel: the split-KV map kernel, timed alone (map stage only)
-    # with an event pair around each launch on the stream it runs on
-    map_ms = time_map_kernel(F, runner, args.steps)
-    kernel_ms = sum(map_ms) / len(map_ms)
-    achieved = case.kv_bytes() / (kernel_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": map_kernel_name(case) + " (split-KV map stage, fdec_decode_partials)",
-                "avg_launch_us": round(kernel_ms * 1e3, 2), "algorithmic_bytes_per_launch": case.kv_bytes(),
-                "kernel_hash": kernel_hash()}
+    # the dominant kernel: the split-KV map kernel of the step (the suffix map of a
+    # cascade), timed with the library's stage-timing events on its stream
+    rl = res["roofline"]["suffix"] if runner.cascade else res["roofline"]
+    achieved = rl["achieved"]
+    roofline = dict(rl)
+    roofline.update({"traffic": load_traffic(args.workload),
+                     "kernel": map_kernel_name(case) + f" ({rl.get('kernel', 'suffix map')} stage of the timed step)",
+                     "kernel_hash": kernel_hash()})
 
-    # attainable streaming read at the same footprint (calibration probe)
+    # attainable streaming read at the map kernel's footprint (the probes)
     import torch as _t
 
-    buf = runner.k[0].view(_t.uint8).reshape(-1)
-    F.probe_read(buf)
-    _t.cuda.synchronize()
-    e0, e1 = _t.cuda.Event(enable_timing=True), _t.cuda.Event(enable_timing=True)
-    probe = []
-    for c in range(runner.copies):
-        for kv in (runner.k[c], runner.v[c]):
-            b = kv.view(_t.uint8).reshape(-1)
-            e0.record()
-            F.probe_read(b)
-            e1.record()
-            _t.cuda.synchronize()
-            probe.append(b.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    res["probe_read_GBps"] = round(sorted(probe)[len(probe) // 2], 1)
+    if not args.no_probe:
+        res.update(probe_ceiling(F, case.kv_bytes(), dev))
     if args.calibrate:
         src = _t.empty(CALIB_BYTES, dtype=_t.uint8, device=dev)
         dst = _t.empty(CALIB_BYTES, dtype=_t.uint8, device=dev)
@@ -388,7 +520,9 @@ def main() -> int:
         F.probe_copy(dst, src)
         _t.cuda.synchronize()
         del src, dst
-    res["pct_of_probe"] = round(100 * res["GBps"] / res["probe_read_GBps"], 1)
+    if "probe_read_GBps" in res:
+        res["pct_of_probe"] = round(100 * res["GBps"] / res["probe_read_GBps"], 1)
+        roofline["kernel_pct_of_probe"] = round(100 * achieved / res["probe_read_GBps"], 1)
     del runner
 
     # the paged batch of mixed lengths runs on the balanced split (equal work per

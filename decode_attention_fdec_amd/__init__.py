@@ -88,6 +88,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_cascade_decode.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, P, I, I, F, P, P, P, Z, P]
     lib.fdec_probe_read.argtypes = [P, Z, P, P]
     lib.fdec_probe_copy.argtypes = [P, P, Z, P]
+    lib.fdec_trace_start.argtypes = [I]
+    lib.fdec_trace_stop.argtypes = [P, P, I, ctypes.POINTER(I)]
+    lib.fdec_probe_stream.argtypes = [P, Z, P, I, I, P]
     lib.fdec_cascade_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.fdec_cascade_workspace_size.restype = Z
     lib.fdec_cascade_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -417,6 +420,41 @@ def probe_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.
         sink = torch.empty(PROBE_BLOCKS, dtype=torch.int32, device=src.device)
     _check(load_library().fdec_probe_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
                                           _stream(src.device)))
+    return sink
+
+
+def trace_start(max_events: int = 4096) -> None:
+    """fdec_trace_start: record stage-timing events for this thread's next calls."""
+    _check(load_library().fdec_trace_start(int(max_events)))
+
+
+def trace_stop():
+    """fdec_trace_stop: (intervals_ms, kinds) of the trace; kind k >= 1 marks the end of a call's
+    k-th kernel (the interval is that kernel's time), 0 the start of a call."""
+    lib = load_library()
+    cap = 1 << 20
+    n = ctypes.c_int(0)
+    ms = (ctypes.c_float * 8192)()
+    kinds = (ctypes.c_int * 8192)()
+    _check(lib.fdec_trace_stop(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(kinds, ctypes.c_void_p), 8192,
+                               ctypes.byref(n)))
+    m = max(0, min(n.value - 1, 8192, cap))
+    return [float(ms[i]) for i in range(m)], [int(kinds[i]) for i in range(m)]
+
+
+PROBE_STATIC, PROBE_TICKETS = 0, 1
+
+
+def probe_stream(src: torch.Tensor, mode: int = PROBE_STATIC, per_cu: int = 1,
+                 sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fdec_probe_stream over the bytes of src (LDS-DMA streaming read); returns the sink.
+
+    The sink's last word is the ticket counter: a new sink is zeroed, and each call leaves it zero."""
+    lib = load_library()
+    if sink is None:
+        sink = torch.zeros(PROBE_BLOCKS + 1, dtype=torch.int32, device=src.device)
+    _check(lib.fdec_probe_stream(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), int(mode),
+                                 int(per_cu), _stream(src.device)))
     return sink
 
 

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "../../include/fdec.h"
 #include "fdec_host.h"
@@ -45,6 +46,42 @@ int check_hip(hipError_t e, const char *what) {
     if (e == hipSuccess) return FDEC_OK;
     return fdec_fail(FDEC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// Stage timing (fdec_trace_start / fdec_trace_stop): while on, every call of
+// this thread records an event on its stream before its first kernel (kind 0)
+// and after its k-th kernel (kind k).
+struct Trace {
+    bool on = false;
+    int cap = 0;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> kind;
+};
+thread_local Trace g_trace;
+
+void trace_record(hipStream_t st, int kind) {
+    Trace &t = g_trace;
+    if (!t.on || (int)t.kind.size() >= t.cap) return;
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventRecord(e, st) != hipSuccess) {
+        (void)hipEventDestroy(e);
+        return;
+    }
+    t.ev.push_back(e);
+    t.kind.push_back(kind);
+}
+
+// The launches of one call: records the call's start, then each kernel's end.
+struct Launches {
+    hipStream_t st;
+    int k = 0;
+    explicit Launches(hipStream_t s) : st(s) { trace_record(st, 0); }
+    int done(hipError_t e, const char *what) {
+        const int rc = check_hip(e, what);
+        if (rc == FDEC_OK) trace_record(st, ++k);
+        return rc;
+    }
+};
 
 int page_shift_of(int ps) {
     if (ps <= 0 || (ps & (ps - 1))) return -1;
@@ -295,17 +332,18 @@ int fdec_decode_launch(const char *fn, const void *q, int B, int Hq, const fdec_
     p.s_total = S;
     p.s_offset = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    Launches run(st);
     if (fused) {
         p.counters = counters;
         p.out = out;
         p.lse = lse;
-        return check_hip(fdec::launch_map(p, S, st), "fdec_decode: map+merge launch");
+        return run.done(fdec::launch_map(p, S, st), "fdec_decode: map+merge launch");
     }
-    int rc = check_hip(fdec::launch_map(p, S, st), "fdec_decode: map launch");
+    int rc = run.done(fdec::launch_map(p, S, st), "fdec_decode: map launch");
     if (rc) return rc;
     (void)fn;
-    return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st),
-                     "fdec_decode: merge launch");
+    return run.done(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st),
+                    "fdec_decode: merge launch");
 }
 
 extern "C" int fdec_decode(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
@@ -369,11 +407,12 @@ extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const 
     p.s_total = S;
     p.s_offset = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = check_hip(mt16 ? fdec::launch_map_mt16(p, S, st) : fdec::launch_map(p, S, st),
-                        "fdec_decode_multi: map launch")))
+    Launches run(st);
+    if ((rc = run.done(mt16 ? fdec::launch_map_mt16(p, S, st) : fdec::launch_map(p, S, st),
+                       "fdec_decode_multi: map launch")))
         return rc;
-    return check_hip(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st, q_len),
-                     "fdec_decode_multi: merge launch");
+    return run.done(fdec::launch_merge(p.po, p.pm, p.pd, B, Hq, S, kv->head_dim, out, lse, st, q_len),
+                    "fdec_decode_multi: merge launch");
 }
 
 extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
@@ -398,7 +437,8 @@ extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv 
     p.pd = part_d;
     p.s_total = num_splits;
     p.s_offset = 0;
-    return check_hip(fdec::launch_map(p, num_splits, static_cast<hipStream_t>(stream)), "fdec_decode_partials");
+    Launches run(static_cast<hipStream_t>(stream));
+    return run.done(fdec::launch_map(p, num_splits, static_cast<hipStream_t>(stream)), "fdec_decode_partials");
 }
 
 // Balanced split: blocks per group of KV heads (0 = one per compute unit over all groups).
@@ -493,10 +533,11 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     p.po = reinterpret_cast<float *>(ws + w.po);
     p.nslots = nb + B;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = check_hip(mt16 ? fdec::launch_map_mt16_balanced(p, nb, st) : fdec::launch_map_mfma_g4_balanced(p, nb, st),
-                        "balanced split: map launch")))
+    Launches run(st);
+    if ((rc = run.done(mt16 ? fdec::launch_map_mt16_balanced(p, nb, st) : fdec::launch_map_mfma_g4_balanced(p, nb, st),
+                       "balanced split: map launch")))
         return rc;
-    return check_hip(fdec::launch_merge_segments(p.po, p.pm, p.pd, p.seg_meta, B, Hq, p.nslots, nb, kv->head_dim, out,
+    return run.done(fdec::launch_merge_segments(p.po, p.pm, p.pd, p.seg_meta, B, Hq, p.nslots, nb, kv->head_dim, out,
                                                  lse, st, q_len),
                      "balanced split: merge launch");
 }
@@ -531,9 +572,10 @@ extern "C" int fdec_merge_states(const float *part_o, const float *part_m, const
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o, part_m, part_d and out must be non-NULL", fn);
     if ((reinterpret_cast<uintptr_t>(part_o) & 7u) || (reinterpret_cast<uintptr_t>(out) & 7u))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o and out must be 8-byte aligned", fn);
-    return check_hip(fdec::launch_merge(part_o, part_m, part_d, B, Hq, S, head_dim, out, lse,
-                                        static_cast<hipStream_t>(stream)),
-                     fn);
+    Launches run(static_cast<hipStream_t>(stream));
+    return run.done(fdec::launch_merge(part_o, part_m, part_d, B, Hq, S, head_dim, out, lse,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 // The cascade's suffixes run on the balanced split when the matrix-core map
@@ -684,16 +726,17 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
         cp.po = reinterpret_cast<float *>(ws + w.ppo);
         cp.s_total = sp;
         cp.s_offset = 0;
-        if ((rc = check_hip(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch")))
+        Launches run(st);
+        if ((rc = run.done(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch")))
             return rc;
         pb.seg_meta = reinterpret_cast<int *>(ws + w.meta);
         pb.pm = reinterpret_cast<float *>(ws + w.pm);
         pb.pd = reinterpret_cast<float *>(ws + w.pd);
         pb.po = reinterpret_cast<float *>(ws + w.po);
         pb.nslots = ss + B;
-        if ((rc = check_hip(fdec::launch_map_mfma_g4_balanced(pb, ss, st), "fdec_cascade_decode: suffix launch")))
+        if ((rc = run.done(fdec::launch_map_mfma_g4_balanced(pb, ss, st), "fdec_cascade_decode: suffix launch")))
             return rc;
-        return check_hip(fdec::launch_merge_cascade(cp.po, cp.pm, cp.pd, sp, pb.po, pb.pm, pb.pd, pb.seg_meta, B, Hq,
+        return run.done(fdec::launch_merge_cascade(cp.po, cp.pm, cp.pd, sp, pb.po, pb.pm, pb.pd, pb.seg_meta, B, Hq,
                                                     pb.nslots, ss, out, lse, st),
                          "fdec_cascade_decode: merge launch");
     }
@@ -713,7 +756,8 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     cp.pd = pd;
     cp.s_total = S;
     cp.s_offset = 0;
-    if ((rc = check_hip(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch"))) return rc;
+    Launches run(st);
+    if ((rc = run.done(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch"))) return rc;
 
     fdec::MapParams p = map_params(q, B, Hq, kv, suffix_lens, ss, softmax_scale, nullptr);
     p.po = po;
@@ -721,7 +765,40 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     p.pd = pd;
     p.s_total = S;
     p.s_offset = sp;
-    if ((rc = check_hip(fdec::launch_map(p, ss, st), "fdec_cascade_decode: suffix launch"))) return rc;
-    return check_hip(fdec::launch_merge(po, pm, pd, B, Hq, S, kv->head_dim, out, lse, st),
+    if ((rc = run.done(fdec::launch_map(p, ss, st), "fdec_cascade_decode: suffix launch"))) return rc;
+    return run.done(fdec::launch_merge(po, pm, pd, B, Hq, S, kv->head_dim, out, lse, st),
                      "fdec_cascade_decode: merge launch");
+}
+
+extern "C" int fdec_trace_start(int max_events) {
+    fdec_clear_error();
+    if (max_events < 2 || max_events > (1 << 20))
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "fdec_trace_start: max_events %d outside [2, 2^20]", max_events);
+    Trace &t = g_trace;
+    for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+    t.ev.clear();
+    t.kind.clear();
+    t.cap = max_events;
+    t.on = true;
+    return FDEC_OK;
+}
+
+extern "C" int fdec_trace_stop(float *intervals_ms, int *kinds, int capacity, int *count_out) {
+    fdec_clear_error();
+    Trace &t = g_trace;
+    t.on = false;
+    const int n = (int)t.ev.size();
+    int rc = FDEC_OK;
+    if (n > 0) rc = check_hip(hipEventSynchronize(t.ev.back()), "fdec_trace_stop");
+    for (int i = 1; rc == FDEC_OK && i < n && i - 1 < capacity; ++i) {
+        float ms = 0.0f;
+        rc = check_hip(hipEventElapsedTime(&ms, t.ev[i - 1], t.ev[i]), "fdec_trace_stop");
+        if (intervals_ms) intervals_ms[i - 1] = ms;
+        if (kinds) kinds[i - 1] = t.kind[i];
+    }
+    for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+    t.ev.clear();
+    t.kind.clear();
+    if (count_out) *count_out = n;
+    return rc;
 }

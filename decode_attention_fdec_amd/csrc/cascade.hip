@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
                                  (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head;
             const int r = r0 + (lane >> 4);
             const uint32_t voff = (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane & 15) ^ (r & 15));
-            dma16(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kring[slot]) + 256u * r0);
-            dma16(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vring[slot]) + 256u * r0);
+            dma16_kv(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kring[slot]) + 256u * r0);
+            dma16_kv(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vring[slot]) + 256u * r0);
         }
     };
 

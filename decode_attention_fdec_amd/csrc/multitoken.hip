@@ -148,8 +148,8 @@ __device__ __forceinline__ void mt16_issue(const MapParams &p, int b, int64_t cr
         const int r = g0 + (lane >> 4);
         const int src = min(max(r, lo), hi) - (rs & ~3);  // 0..3 within the group
         const uint32_t voff = (uint32_t)src * stok + 16u * (uint32_t)((lane & 15) ^ (r & 15));
-        dma16(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kt) + 256u * g0);
-        dma16(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vt) + 256u * g0);
+        dma16_kv(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kt) + 256u * g0);
+        dma16_kv(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vt) + 256u * g0);
     }
 }
 

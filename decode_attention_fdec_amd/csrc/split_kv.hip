@@ -262,8 +262,8 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
             const uint32_t off = first ? off_first[j] : last ? off_last[j] : off_full[j];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                T.k[j][c] = *reinterpret_cast<const Piece *>(kb + off + c * 64 * ES);
-                T.v[j][c] = *reinterpret_cast<const Piece *>(vb + off + c * 64 * ES);
+                T.k[j][c] = load_nt<Piece>(kb + off + c * 64 * ES);
+                T.v[j][c] = load_nt<Piece>(vb + off + c * 64 * ES);
             }
         }
     };

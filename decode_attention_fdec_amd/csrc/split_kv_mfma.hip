@@ -141,8 +141,8 @@ __device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint3
         for (int i = 0; i < kMT / 4; ++i) {
             const int r = 4 * i + srow;
             const uint32_t row = (uint32_t)min(max(r, nskip), nrows - 1) * stok;
-            dma16(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
-            dma16(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
+            dma16_kv(kb, row + 16u * (uint32_t)(sslot ^ r), kl + 1024u * i);
+            dma16_kv(vb, row + 16u * (uint32_t)(sslot ^ (4 * (r & 3))), vl + 1024u * i);
         }
     } else {
         const int srow = lane >> 3, sslot = lane & 7;
@@ -150,8 +150,8 @@ __device__ __forceinline__ void stage_tile(const char *kb, const char *vb, uint3
         for (int i = 0; i < kMT / 8; ++i) {
             const int r = 8 * i + srow;
             const uint32_t row = (uint32_t)min(max(r, nskip), nrows - 1) * stok;
-            dma16(kb, row + 16u * (uint32_t)(sslot ^ ((r >> 1) & 7)), kl + 1024u * i);
-            dma16(vb, row + 16u * (uint32_t)(sslot ^ (2 * ((r >> 1) & 3))), vl + 1024u * i);
+            dma16_kv(kb, row + 16u * (uint32_t)(sslot ^ ((r >> 1) & 7)), kl + 1024u * i);
+            dma16_kv(vb, row + 16u * (uint32_t)(sslot ^ (2 * ((r >> 1) & 3))), vl + 1024u * i);
         }
     }
 }

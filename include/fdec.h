@@ -399,6 +399,23 @@ int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int capacity, int 
 size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_dim, int splits_prefix,
                                    int splits_suffix);
 
+/*
+ * Stage timing (tracing). After fdec_trace_start(max_events), every call the
+ * calling thread makes records a HIP event on its stream before its first
+ * kernel and after each kernel it launches, up to max_events events in all
+ * (2..2^20; the events are the library's own). fdec_trace_stop ends the trace,
+ * waits for the last event, and writes for i = 1 .. n-1 the interval between
+ * event i-1 and event i to intervals_ms[i-1] (ms, at most `capacity` of them)
+ * and the kind of event i to kinds[i-1]: k >= 1 for the end of a call's k-th
+ * kernel (so the interval is that kernel's time on the stream, launches queued
+ * back to back), 0 for the start of a call (the interval is the gap since the
+ * previous call's last kernel). *count_out = n, the events recorded. Either
+ * array may be NULL. Tracing adds an event record per kernel; it is for
+ * measurement, off by default. Host-side; no device memory is allocated.
+ */
+int fdec_trace_start(int max_events);
+int fdec_trace_stop(float *intervals_ms, int *kinds, int capacity, int *count_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -295,3 +295,17 @@ def test_noalloc_validates_like_decode_and_bounds_its_scratch(fdec):
     assert call_noalloc(kv_struct(num_kv_heads=8, capacity=16), B=4096, Hq=8, num_splits=1) == F.FDEC_ERR_WORKSPACE
     # B = 0 is a valid empty call
     assert call_noalloc(kv_struct(), B=0) == F.FDEC_OK
+
+
+def test_trace_arguments_and_an_empty_trace(fdec):
+    lib = F.load_library()
+    assert lib.fdec_trace_start(1) == F.FDEC_ERR_INVALID_ARG
+    assert lib.fdec_trace_start(16) == F.FDEC_OK
+    n = ctypes.c_int(-1)
+    assert lib.fdec_trace_stop(None, None, 0, ctypes.byref(n)) == F.FDEC_OK
+    assert n.value == 0
+    # failing calls launch nothing and record nothing
+    assert lib.fdec_trace_start(16) == F.FDEC_OK
+    assert call_decode(kv_struct(num_kv_heads=5)) == F.FDEC_ERR_INVALID_ARG
+    assert lib.fdec_trace_stop(None, None, 0, ctypes.byref(n)) == F.FDEC_OK
+    assert n.value == 0
