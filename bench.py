@@ -325,15 +325,18 @@ SQ_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_LDS"
                "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
 
 
-def summarize_counters(paths, cu_count: int = 256) -> dict:
+def summarize_counters(paths, cu_count: int = 256, xcc_count: int = 8) -> dict:
     """Per-kernel medians (over dispatches) of rocprofv3 --pmc csv files, with the
-    derived figures rocprofv3 defines for them:
-      occupancy_pct  = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs / 32
-                       (resident waves as % of 32 per CU; the counter is in quad-cycles),
-      waves_per_cu   = 4 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs,
-      lds_bank_conflicts_per_access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT),
-      lds_bank_conflict_pct_of_time = 100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs;
-    FETCH_SIZE / WRITE_SIZE (KiB) in bytes with the calibration scales when given."""
+    derived figures rocprofv3 defines for them. The csv holds each counter summed
+    over the GPU's dies; GRBM_GUI_ACTIVE (cycles the GPU is busy) is counted once
+    per die, and rocprofv3's formulas take one die's value (its max), here the
+    sum over xcc_count dies divided by that count:
+      occupancy_pct  = 400 * SQ_WAVE_CYCLES / busy / CUs / 32
+                       (resident waves as % of 32 per CU; SQ_WAVE_CYCLES is in quad-cycles),
+      waves_per_cu   = 4 * SQ_WAVE_CYCLES / busy / CUs,
+      lds_bank_conflicts_per_access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)
+                       (stall cycles per cycle of useful indexed LDS work),
+      lds_bank_conflict_pct_of_time = 100 * SQ_LDS_BANK_CONFLICT / busy / CUs."""
     import csv
 
     per = {}  # kernel -> counter -> dispatch -> value (summed over dimensions)
@@ -348,6 +351,9 @@ def summarize_counters(paths, cu_count: int = 256) -> dict:
         med = {c: sorted(v.values())[len(v) // 2] for c, v in cs.items()}
         med["dispatches"] = max(len(v) for v in cs.values())
         g = med.get("GRBM_GUI_ACTIVE")
+        g = g / xcc_count if g else g
+        if g:
+            med["busy_cycles_per_die"] = round(g)
         if g and "SQ_WAVE_CYCLES" in med:
             med["occupancy_pct"] = round(400.0 * med["SQ_WAVE_CYCLES"] / g / cu_count / 32, 2)
             med["waves_per_cu"] = round(4.0 * med["SQ_WAVE_CYCLES"] / g / cu_count, 3)
@@ -449,6 +455,8 @@ def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: i
            "warm_us_per_step": round(warm * 1e3, 2), "num_splits": runner.S, "mode": mode,
            "kv_copies_rotated": runner.copies, "kernel_us": stages,
            "roofline": roofline_entry(case, stages, runner)}
+    rl = res["roofline"]["suffix"] if runner.cascade else res["roofline"]
+    rl["traffic"] = load_traffic(name)  # HBM bytes of the map kernel from the stored counters, if current
     log(f"[bench] {name}: {res['us_per_step']} us/step, {res['GBps']} GB/s ({res['pct_of_peak']}% of peak)")
     return case, runner, res, per
 
