@@ -73,7 +73,9 @@ inline bool map_mfma_eligible(const MapParams &p) {
 // Runs the matrix-core kernel when p.mfma is set (heads_per_block <= 4).
 hipError_t launch_map(const MapParams &p, int num_splits, hipStream_t stream);
 hipError_t launch_map_mfma_g4(const MapParams &p, int num_splits, hipStream_t stream);
-int mfma_tokens_per_wave(int q_len);
+// Query tokens per wave of the matrix-core map kernels for q_len tokens per
+// request: up to 4 in registers, more in groups of 4 along the grid's y axis.
+inline int mfma_tokens_per_wave(int q_len) { return q_len <= 1 ? 1 : q_len == 2 ? 2 : 4; }
 // Multi-token map kernel on 16x16x32 matrix cores (16-bit caches, head_dim 128,
 // any G): one wave per (split, request, KV head, 16 or 32 query rows), kMtWaves
 // waves per block.
@@ -88,7 +90,7 @@ inline bool mt16_eligible(int q_len, int G, int head_dim, bool fp8) {
 }
 // Blocks along z of the 16x16x32 kernels: kMtWaves waves per block, one per
 // (KV head, chunk of 16 or 32 query rows).
-int mt16_row_blocks(int rows);
+inline int mt16_row_blocks(int rows) { return rows <= 16 ? 1 : 2; }
 inline int mt16_z_blocks(int q_len, int G, int Hkv) {
     const int rows = q_len * G, per = 16 * mt16_row_blocks(rows);
     return (Hkv * ((rows + per - 1) / per) + kMtWaves - 1) / kMtWaves;

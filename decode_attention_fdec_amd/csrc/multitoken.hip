@@ -515,8 +515,6 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const Ma
 }
 
 // Row blocks per wave for q_len * G query rows per (request, KV head).
-int mt16_row_blocks(int rows) { return rows <= 16 ? 1 : 2; }
-
 hipError_t launch_map_mt16(const MapParams &p, int S, hipStream_t st) {
     const int G = p.Hq / p.Hkv, R = p.q_len * G;
     const int rb = mt16_row_blocks(R);

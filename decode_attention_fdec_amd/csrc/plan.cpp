@@ -156,7 +156,8 @@ extern "C" int fdec_plan_kv(int B, int Hq, int Hkv, const int32_t *seq_lens_host
     }
     const CostModel cm = model_for(Hq, Hkv, kv_dtype == FDEC_FP8_E4M3);
     // Candidate split counts: every distinct chunk size, up to 64 blocks per slot.
-    const int max_s = (int)std::min<int64_t>(FDEC_MAX_SPLITS, (capacity + FDEC_CHUNK_ALIGN - 1) / FDEC_CHUNK_ALIGN);
+    const int max_s =
+        (int)std::min<int64_t>(FDEC_MAX_SPLITS, ((int64_t)capacity + FDEC_CHUNK_ALIGN - 1) / FDEC_CHUNK_ALIGN);
     const int64_t block_cap = (int64_t)64 * cu_count * cm.blocks_per_cu;
     // The matrix-core kernel reaches its aggregate rate only with a block on
     // every CU (measured: 128 or 192 blocks of a 256-CU part stream at ~5.0

@@ -998,10 +998,6 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
             hipLaunchKernelGGL((KERNEL<1, false, 0 __VA_ARGS__>), grid, block, 0, st, p);            \
     }
 
-// Query tokens per wave for q_len tokens per request: up to 4 in registers,
-// more in groups of 4 along the grid's y axis.
-int mfma_tokens_per_wave(int q_len) { return q_len <= 1 ? 1 : q_len == 2 ? 2 : 4; }
-
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStream_t st) {
     if (p.Hq == 8 * p.Hkv) {  // two groups of four query heads per wave, single query
         if (p.q_len != 1 || p.q_groups != 1) return hipErrorInvalidValue;

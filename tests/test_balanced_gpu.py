@@ -140,3 +140,25 @@ def test_shared_workspace_keeps_fused_counters(first):
     assert int(counters.abs().sum()) == 0
     ref_out, ref_lse = oracle_decode(case)
     assert_parity(o_f, l_f, ref_out, ref_lse, case.dtype, f"fused after {first}")
+
+
+@pytest.mark.parametrize("lens,nb", [([3000, 1, 0, 17, 700], 64), ([0] * 3 + [5000], 7),
+                                     ([(13 * i) % 400 for i in range(70)], 256), ([1600], 1),
+                                     ([100] * 9, 3)])
+def test_device_records_follow_the_partition_rule(lens, nb):
+    """The (first slot, piece count) records the kernel writes per request equal the
+    partition rule that tests/test_balanced_partition.py checks on the CPU, so that
+    check pins the device code."""
+    from test_balanced_partition import partition
+
+    B = len(lens)
+    case = contiguous_case(93, B, 16, 4, 128, lens, max(max(lens), 1), BF16, pad="nan")
+    d = to_dev(case)
+    ws = F.Workspace(F.balanced_workspace_size(B, case.Hq, case.Hkv, 128, nb))
+    ws.buf.fill_(0x7f)  # records the kernel does not write would show up
+    F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], num_blocks=nb, workspace=ws)
+    torch.cuda.synchronize()
+    off = (B * case.Hkv * 4 + 255) // 256 * 256  # after the fused path's counters
+    got = ws.buf[off: off + 8 * B].view(torch.int32).cpu().view(B, 2).tolist()
+    meta, _ = partition(lens, nb)
+    assert [tuple(x) for x in got] == [meta[j] for j in range(B)]
