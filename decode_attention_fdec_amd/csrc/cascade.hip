@@ -117,7 +117,10 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
 
     // DMA of tile `tile` into ring slot tile % kPfxNS: this wave's rows 8w .. 8w + 7
     // of K and of V, four rows (one page: pages hold multiples of 16 keys) per
-    // instruction; rows past the split's end repeat its last key (masked below)
+    // instruction; rows past the split's end repeat its last key (masked below).
+    // Default cache policy: unlike the split-KV kernels' streaming reads, the
+    // non-temporal one measured slower here (the prefix block's loads are fewer and
+    // its time goes to the matrix cores and the state writes, not to the stream)
     const uint32_t stok = (uint32_t)(p.s_token * 2);
     auto issue = [&](int tile) {
         const int t0 = t_begin + tile * kPfxKeys;
@@ -133,8 +136,8 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
                                  (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head;
             const int r = r0 + (lane >> 4);
             const uint32_t voff = (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane & 15) ^ (r & 15));
-            dma16_kv(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kring[slot]) + 256u * r0);
-            dma16_kv(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vring[slot]) + 256u * r0);
+            dma16(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kring[slot]) + 256u * r0);
+            dma16(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vring[slot]) + 256u * r0);
         }
     };
 

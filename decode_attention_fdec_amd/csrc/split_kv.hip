@@ -426,7 +426,7 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     __syncthreads();  // every wave's state stores are complete
     if (threadIdx.x == 0) {
         int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
-        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         const int last = (prev == (int)gridDim.x - 1);
         if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm_flag = last;

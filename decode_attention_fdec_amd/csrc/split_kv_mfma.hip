@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4(cons
     __syncthreads();
     if (threadIdx.x == 0) {
         int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
-        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         const int last = (prev == (int)gridDim.x - 1);
         if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm_flag = last;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g8(cons
     __syncthreads();
     if (threadIdx.x == 0) {
         int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
-        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         const int last = (prev == (int)gridDim.x - 1);
         if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm_flag = last;
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
     __syncthreads();
     if (threadIdx.x == 0) {
         int *cnt = p.counters + (int64_t)b * gridDim.z + blockIdx.z;
-        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         const int last = (prev == (int)gridDim.x - 1);
         if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm_flag = last;
