@@ -80,6 +80,7 @@ def _load():
         lib.oracle_decode_elems.argtypes = [P, ctypes.c_int, ctypes.c_int64, P]
         lib.oracle_decode_f8.argtypes = [P, ctypes.c_int64, P]
         lib.oracle_encode_elems.argtypes = [P, ctypes.c_int, ctypes.c_int64, P]
+        lib.oracle_encode_f8.argtypes = [P, ctypes.c_int64, P]
         lib.oracle_now.restype = ctypes.c_double
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -138,6 +139,14 @@ def from_f64(x: np.ndarray, dtype: int) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float64)
     out = np.empty(x.shape, dtype=np.uint16)
     _load().oracle_encode_elems(_ptr(x), dtype, x.size, _ptr(out))
+    return out
+
+
+def f32_to_f8(x) -> np.ndarray:
+    """Nearest float8 e4m3fn codes (ties to even, saturating at +-448) of binary32 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().oracle_encode_f8(_ptr(x), x.size, _ptr(out))
     return out
 
 

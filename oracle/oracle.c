@@ -27,7 +27,12 @@
  *                    angles, in double ([cookbook] §3.4).
  *   oracle_append    writes rope(k_new) and v_new at row cache_seqlens[b] and
  *                    returns rope(q); lengths are not advanced
- *                    ([cookbook] §3.2-3.4).
+ *                    ([cookbook] §3.2-3.4). A float8 cache stores each new
+ *                    element as the e4m3fn code of (value / descale)
+ *                    ([cookbook] §7.1-7.2: value = code * descale).
+ *   oracle_f32_to_f8 the e4m3fn code nearest a binary32 value: a search over
+ *                    every finite code, ties to the even code ([cookbook] §7.1,
+ *                    the cast to float8_e4m3fn).
  *   fp8 cache        K/V stored as float8_e4m3fn with one fp32 descale per
  *                    (request, KV head) for K and one for V; the element's value
  *                    is its e4m3 value times that descale ([cookbook] §7.1-7.2).
@@ -56,7 +61,11 @@
  *   - lengths (lens / cache_seqlens) count rows from row 0, left padding
  *     included; an appended row goes to row cache_seqlens[b] and is rotated at
  *     its position among the valid rows, cache_seqlens[b] - leftpad[b];
- *   - float8 descales are indexed by the query's request b.
+ *   - float8 descales are indexed by the query's request b;
+ *   - float8 append: (value / descale) is formed in binary32 (the rotated k
+ *     value rounded once to binary32 first) and rounded to the nearest e4m3fn
+ *     code, ties to even; magnitudes beyond the largest finite 448 saturate to
+ *     +-448 (the cache stays finite), NaN gives the NaN code 0x7f.
  */
 #include <math.h>
 #include <stdint.h>
@@ -106,6 +115,28 @@ double oracle_f8_to_f64(uint8_t x) {
 
 void oracle_decode_f8(const uint8_t *src, int64_t n, double *dst) {
     for (int64_t i = 0; i < n; ++i) dst[i] = oracle_f8_to_f64(src[i]);
+}
+
+/* The e4m3fn code nearest x: every finite magnitude code 0x00..0x7e is tried;
+ * on a tie the even code (even last fraction bit) wins. Past 448 the nearest
+ * finite code is 0x7e, so large magnitudes saturate. The sign bit is x's. */
+uint8_t oracle_f32_to_f8(float x) {
+    if (isnan(x)) return 0x7f;
+    double a = fabs((double)x);
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7e; ++c) {
+        double err = fabs(oracle_f8_to_f64((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(signbit(x) ? (best | 0x80) : best);
+}
+
+void oracle_encode_f8(const float *src, int64_t n, uint8_t *dst) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = oracle_f32_to_f8(src[i]);
 }
 
 /* Round a double once, to nearest with ties to even, onto a binary16. */
@@ -433,11 +464,13 @@ void oracle_rope_neox(double *x, int D, int rotary_dim, int pos, double base) {
  * k_cache/v_cache are modified in place (the caller passes copies).
  * cache_seqlens is not modified; attention then covers c + 1 tokens.
  */
-void oracle_append(oracle_kv *kv, uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k_new,
+void oracle_append(oracle_kv *kv, void *k_cache, void *v_cache, const uint16_t *k_new,
                    const uint16_t *v_new, const double *q, const int32_t *cache_seqlens,
                    int rotary_dim, double base, double *q_out) {
     int B = kv->B, Hq = kv->Hq, Hkv = kv->Hkv, D = kv->D;
-    if (kv->dtype != 0 && kv->dtype != 1) return; /* append is defined for 16-bit caches */
+    const int f8 = kv->dtype == 2;
+    /* new rows arrive in the queries' dtype: the cache's own, bf16 for float8 */
+    const int new_dtype = f8 ? 1 : kv->dtype;
     double *tmp = (double *)malloc(sizeof(double) * (size_t)D);
     for (int b = 0; b < B; ++b) {
         int c = cache_seqlens[b];
@@ -446,17 +479,25 @@ void oracle_append(oracle_kv *kv, uint16_t *k_cache, uint16_t *v_cache, const ui
             int64_t off = row_offset(kv, b, c, g);
             const uint16_t *kn = k_new + ((int64_t)b * Hkv + g) * D;
             const uint16_t *vn = v_new + ((int64_t)b * Hkv + g) * D;
-            if (rotary_dim > 0) {
-                for (int d = 0; d < D; ++d)
-                    tmp[d] = kv->dtype == 0 ? oracle_f16_to_f64(kn[d]) : oracle_bf16_to_f64(kn[d]);
-                oracle_rope_neox(tmp, D, rotary_dim, pos, base);
-                for (int d = 0; d < D; ++d)
-                    k_cache[off + d] =
-                        kv->dtype == 0 ? oracle_f64_to_f16(tmp[d]) : oracle_f64_to_bf16(tmp[d]);
+            for (int d = 0; d < D; ++d) tmp[d] = new_dtype == 0 ? oracle_f16_to_f64(kn[d]) : oracle_bf16_to_f64(kn[d]);
+            if (rotary_dim > 0) oracle_rope_neox(tmp, D, rotary_dim, pos, base);
+            if (f8) {
+                uint8_t *kc = (uint8_t *)k_cache, *vc = (uint8_t *)v_cache;
+                const float kd = kv->k_descale ? (float)kv->k_descale[(int64_t)b * Hkv + g] : 1.0f;
+                const float vd = kv->v_descale ? (float)kv->v_descale[(int64_t)b * Hkv + g] : 1.0f;
+                for (int d = 0; d < D; ++d) {
+                    volatile float x = (float)tmp[d]; /* binary32, then one binary32 division */
+                    kc[off + d] = oracle_f32_to_f8(x / kd);
+                    volatile float y = (float)oracle_bf16_to_f64(vn[d]);
+                    vc[off + d] = oracle_f32_to_f8(y / vd);
+                }
             } else {
-                for (int d = 0; d < D; ++d) k_cache[off + d] = kn[d];
+                uint16_t *kc = (uint16_t *)k_cache, *vc = (uint16_t *)v_cache;
+                for (int d = 0; d < D; ++d)
+                    kc[off + d] = rotary_dim > 0 ? (kv->dtype == 0 ? oracle_f64_to_f16(tmp[d]) : oracle_f64_to_bf16(tmp[d]))
+                                                 : kn[d];
+                for (int d = 0; d < D; ++d) vc[off + d] = vn[d];
             }
-            for (int d = 0; d < D; ++d) v_cache[off + d] = vn[d];
         }
         for (int h = 0; h < Hq; ++h) {
             const double *qi = q + ((int64_t)b * Hq + h) * D;

@@ -24,7 +24,8 @@ The five named workloads follow the shapes of the pages' examples:
   c5  cascade, 64 requests, Hq=32, Hkv=8, page 64, shared 16384-token prefix,
       suffixes U{256..2048}, bf16
 and float8 versions of c2 and c3 (c2f8, c3f8): the same shapes and seeds with
-float8 e4m3fn K/V and bf16 queries.
+float8 e4m3fn K/V and bf16 queries. Float8 append cases draw k_new / v_new as
+bf16 and the descales after them (the caches are quantised as above).
 """
 from __future__ import annotations
 
@@ -292,9 +293,9 @@ def append_case(seed: int, B: int, Hq: int, Hkv: int, D: int, max_seqlen: int, d
     else:
         cs = torch.as_tensor(cache_seqlens, dtype=torch.int32).reshape(B)
     if page_size == 0:
-        q = _randn(g, (B, Hq, D), dtype)
-        k = _randn(g, (B, max_seqlen, Hkv, D), dtype)
-        v = _randn(g, (B, max_seqlen, Hkv, D), dtype)
+        q = _randn(g, (B, Hq, D), _q_dtype(dtype))
+        k = _randn(g, (B, max_seqlen, Hkv, D), _kv_draw_dtype(dtype))
+        v = _randn(g, (B, max_seqlen, Hkv, D), _kv_draw_dtype(dtype))
         rows = torch.arange(max_seqlen)[None, :] >= cs[:, None].to(torch.int64)
         _fill_pad(k, rows, pad, g)
         _fill_pad(v, rows, pad, g)
@@ -317,19 +318,35 @@ def append_case(seed: int, B: int, Hq: int, Hkv: int, D: int, max_seqlen: int, d
             elif n > c // page_size:
                 mask[last, :] = True
             off += n
-        q = _randn(g, (B, Hq, D), dtype)
-        k = _randn(g, (pool, page_size, Hkv, D), dtype)
-        v = _randn(g, (pool, page_size, Hkv, D), dtype)
+        q = _randn(g, (B, Hq, D), _q_dtype(dtype))
+        k = _randn(g, (pool, page_size, Hkv, D), _kv_draw_dtype(dtype))
+        v = _randn(g, (pool, page_size, Hkv, D), _kv_draw_dtype(dtype))
         _fill_pad(k, mask, pad, g)
         _fill_pad(v, mask, pad, g)
-    k_new = _randn(g, (B, Hkv, D), dtype)
-    v_new = _randn(g, (B, Hkv, D), dtype)
+    k_new = _randn(g, (B, Hkv, D), _q_dtype(dtype))
+    v_new = _randn(g, (B, Hkv, D), _q_dtype(dtype))
+    kd = vd = None
+    if dtype == FP8:
+        # descales drawn after v_new; a request's pages carry its own
+        kd, vd = _descales(g, B, Hkv)
+        if page_size == 0:
+            k = _quantize(k, kd[:, None, :, None])
+            v = _quantize(v, vd[:, None, :, None])
+        else:
+            fk = torch.empty(k.shape[0], Hkv)
+            fv = torch.empty(k.shape[0], Hkv)
+            for b in range(B):
+                pl = table[b][table[b] >= 0].long()
+                fk[pl] = kd[b]
+                fv[pl] = vd[b]
+            k = _quantize(k, fk[:, None, :, None])
+            v = _quantize(v, fv[:, None, :, None])
     cos = sin = None
     if rotary_dim > 0:
         cos, sin = rope_tables(max_seqlen, rotary_dim, base)
     return Case(name, dtype, B, Hq, Hkv, D, q, k, v, cs, page_size=page_size, page_table=table,
                 k_new=k_new, v_new=v_new, rotary_dim=rotary_dim, rope_base=base, rope_cos=cos,
-                rope_sin=sin, num_splits=num_splits)
+                rope_sin=sin, num_splits=num_splits, k_descale=kd, v_descale=vd)
 
 
 def cascade_case(seed: int, B: int, Hq: int, Hkv: int, D: int, prefix_len: int, ps: int,

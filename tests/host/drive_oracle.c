@@ -7,7 +7,8 @@
  * (each exact up to rounding):
  *   - merging its own partial states at random boundaries gives its decode;
  *   - multi-token decode with one token gives decode;
- *   - decode after an append equals decode over the cache the append wrote.
+ *   - decode after an append (16-bit or float8 cache) gives finite outputs
+ *     over the cache the append wrote.
  * Exits non-zero on a failed identity; the sanitizers abort on any report.
  */
 #include "../../oracle/oracle.c"
@@ -154,16 +155,18 @@ static void one_case(int c) {
         free(qm), free(om), free(lm);
     }
 
-    /* append (16-bit caches): decode of the written cache at length c + 1 */
-    if (dtype != 2 && !prefix_len) {
-        uint16_t *kc = xmalloc((size_t)elems * 2), *vc = xmalloc((size_t)elems * 2);
-        memcpy(kc, k, (size_t)elems * 2), memcpy(vc, v, (size_t)elems * 2);
+    /* append (new rows in the queries' dtype, bf16 for float8): decode of the
+       written cache at length c + 1 */
+    if (!prefix_len) {
+        void *kc = xmalloc((size_t)elems * es), *vc = xmalloc((size_t)elems * es);
+        memcpy(kc, k, (size_t)elems * es), memcpy(vc, v, (size_t)elems * es);
         uint16_t *kn = xmalloc(sizeof(uint16_t) * B * Hkv * D), *vn = xmalloc(sizeof(uint16_t) * B * Hkv * D);
         double *t2 = xmalloc(sizeof(double) * B * Hkv * D);
+        const int new_dtype = dtype == 2 ? 1 : dtype;
         for (int i = 0; i < B * Hkv * D; ++i) t2[i] = rn();
-        oracle_encode_elems(t2, dtype, (int64_t)B * Hkv * D, kn);
+        oracle_encode_elems(t2, new_dtype, (int64_t)B * Hkv * D, kn);
         for (int i = 0; i < B * Hkv * D; ++i) t2[i] = rn();
-        oracle_encode_elems(t2, dtype, (int64_t)B * Hkv * D, vn);
+        oracle_encode_elems(t2, new_dtype, (int64_t)B * Hkv * D, vn);
         int rd = (int[]){0, D / 2, D}[ri(0, 2)] & ~1;
         double *qr = xmalloc(sizeof(double) * nq);
         oracle_append(&kv, kc, vc, kn, vn, q, lens, rd, 10000.0, qr);

@@ -75,6 +75,42 @@ def test_f8_decode_exhaustive():
     assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
 
 
+def _torch_f8(x32):
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def test_f8_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = oracle.to_f64(codes, oracle.FP8).astype(np.float32)
+    assert np.array_equal(oracle.f32_to_f8(vals), codes)
+
+
+def test_f8_encode_matches_torch_cast_below_overflow():
+    # torch's cast to float8_e4m3fn (round to nearest even) agrees wherever it
+    # does not overflow: random magnitudes over the whole range, every halfway
+    # point between neighbouring codes (ties), and the subnormal range
+    rng = np.random.default_rng(7)
+    pos = oracle.to_f64(np.arange(0, 0x7F, dtype=np.uint8), oracle.FP8)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 9, 20000),
+        _halfway_points(pos),
+        rng.uniform(0, 2.0 ** -6, 4000),
+        [463.99, 464.0, 447.9, 2.0 ** -10, 3 * 2.0 ** -10, 1.0 + 2.0 ** -4],
+    ])
+    x = x[np.abs(x) <= 464.0].astype(np.float32)
+    x = np.concatenate([x, -x])
+    assert np.array_equal(oracle.f32_to_f8(x), _torch_f8(x))
+
+
+def test_f8_encode_saturates_and_keeps_nan():
+    big = np.array([464.5, 480.0, 1e6, 3.0e38, np.inf], dtype=np.float32)
+    assert set(oracle.f32_to_f8(big).tolist()) == {0x7E}
+    assert set(oracle.f32_to_f8(-big).tolist()) == {0xFE}
+    assert oracle.f32_to_f8(np.array([np.nan], dtype=np.float32))[0] == 0x7F
+    assert oracle.f32_to_f8(np.array([-0.0, -1e-30], dtype=np.float32)).tolist() == [0x80, 0x80]
+
+
 def _halfway_points(vals):
     v = np.unique(vals[np.isfinite(vals)])
     return (v[:-1] + v[1:]) / 2.0
@@ -606,6 +642,46 @@ def test_append_with_leftpad_and_batch_idx():
         ro, rl = _sdpa_rows(torch.from_numpy(q_rot[b]), kr, vr, 1 / math.sqrt(128))
         np.testing.assert_allclose(out[b], ro, rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse[b], rl, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("rd,paged", [(0, False), (128, False), (64, True)])
+def test_fp8_append_stores_quantised_rows(rd, paged):
+    # a float8 cache stores code(value / descale): for v and an unrotated k that
+    # is torch's cast of the bf16 input divided in float32; a rotated k is the
+    # rotated value (rounded to float32) divided alike; nothing else changes
+    case = append_case(171 + rd, 3, 8, 2, 128, 64, FP8, rotary_dim=rd, pad="zero", page_size=16 if paged else 0)
+    kv = okv(case)
+    kc, vc, q_rot, after = oracle.append(kv, case.k_new, case.v_new, case.q, case.seq_lens, rd)
+    k0, v0 = oracle._bits(case.k), oracle._bits(case.v)
+    kn = case.k_new.to(torch.float32).numpy()
+    vn = case.v_new.to(torch.float32).numpy()
+    kd, vd = case.k_descale.numpy(), case.v_descale.numpy()
+    changed = np.zeros(k0.shape[:2], dtype=bool)
+    for b in range(3):
+        c = int(case.seq_lens[b])
+        if paged:
+            pg, sl = int(case.page_table[b, c // 16]), c % 16
+        else:
+            pg, sl = b, c
+        changed[pg, sl] = True
+        for g in range(2):
+            assert np.array_equal(vc[pg, sl, g], _torch_f8(vn[b, g] / np.float32(vd[b, g])))
+            kval = oracle.rope_neox(kn[b, g].astype(np.float64), c, rd).astype(np.float32) if rd else kn[b, g]
+            assert np.array_equal(kc[pg, sl, g], _torch_f8(kval / np.float32(kd[b, g])))
+    assert np.array_equal(kc[~changed], k0[~changed]) and np.array_equal(vc[~changed], v0[~changed])
+    # decode after the append reads the written codes times the descales
+    scale = 1 / math.sqrt(128)
+    out, lse = oracle.decode(after, q_rot, case.seq_lens + 1, scale)
+    for b in range(3):
+        L = int(case.seq_lens[b]) + 1
+        rows = [(int(case.page_table[b, j // 16]), j % 16) if paged else (b, j) for j in range(L)]
+        kr = np.stack([oracle.to_f64(kc[p_, s_], oracle.FP8) for p_, s_ in rows], axis=1)  # [Hkv, L, D]
+        vr = np.stack([oracle.to_f64(vc[p_, s_], oracle.FP8) for p_, s_ in rows], axis=1)
+        kr = torch.from_numpy(kr * kd[b][:, None, None])
+        vr = torch.from_numpy(vr * vd[b][:, None, None])
+        qb = torch.from_numpy(q_rot[b])[None, :, None, :]
+        ref = F.scaled_dot_product_attention(qb, kr[None], vr[None], scale=scale, enable_gqa=True)[0, :, 0, :]
+        np.testing.assert_allclose(out[b], ref.numpy(), rtol=0, atol=1e-12)
 
 
 # ---------------------------------------------------------------- multi-token (speculative) decode

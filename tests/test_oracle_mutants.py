@@ -36,7 +36,16 @@ MUTANTS = {
                            "for (int j = lo; j < hi - 1; ++j) {\n        sbuf"),
     "prefix_pages_ignored": ("} else if (kv->prefix_pages && j < kv->prefix_len) {",
                              "} else if (kv->prefix_pages && j < 0) {"),
-    "append_v_not_written": ("for (int d = 0; d < D; ++d) v_cache[off + d] = vn[d];", ""),
+    "append_v_not_written": ("for (int d = 0; d < D; ++d) vc[off + d] = vn[d];", ""),
+    "f8_encode_ties_odd": ("(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    "f8_encode_rounds_down": ("double err = fabs(oracle_f8_to_f64((uint8_t)c) - a);",
+                              "double err = oracle_f8_to_f64((uint8_t)c) > a ? INFINITY : a - oracle_f8_to_f64((uint8_t)c);"),
+    "f8_encode_drops_sign": ("return (uint8_t)(signbit(x) ? (best | 0x80) : best);", "return (uint8_t)best;"),
+    "f8_encode_nan_saturates": ("if (isnan(x)) return 0x7f;", "if (isnan(x)) return 0x7e;"),
+    "f8_append_multiplies_descale": ("kc[off + d] = oracle_f32_to_f8(x / kd);", "kc[off + d] = oracle_f32_to_f8(x * kd);"),
+    "f8_append_v_uses_k_descale": ("vc[off + d] = oracle_f32_to_f8(y / vd);", "vc[off + d] = oracle_f32_to_f8(y / kd);"),
+    "f8_append_k_unrotated": ("if (rotary_dim > 0) oracle_rope_neox(tmp, D, rotary_dim, pos, base);\n            if (f8) {",
+                              "if (rotary_dim > 0 && !f8) oracle_rope_neox(tmp, D, rotary_dim, pos, base);\n            if (f8) {"),
     "batch_idx_ignored": ("outer = kv->batch_idx ? kv->batch_idx[b] : b;", "outer = b;"),
     "leftpad_ignored": ("int lo = first_row(kv, b);\n            double m, dsum;",
                         "int lo = 0;\n            double m, dsum;"),
