@@ -234,14 +234,6 @@ fdec::MapParams map_params(const void *q, int B, int Hq, const fdec_kv *kv, cons
     return p;
 }
 
-// Float8 caches run on either map kernel (the matrix-core one for G = 4, 8 at
-// head_dim 128, the vector one otherwise), without append.
-int check_fp8(const char *fn, const fdec_kv *kv, const fdec::MapParams &, const fdec_append *append) {
-    if (kv->dtype != FDEC_FP8_E4M3) return FDEC_OK;
-    if (append) return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: append into a float8 cache is not built", fn);
-    return FDEC_OK;
-}
-
 int resolve_splits(const char *fn, int num_splits, int B, int Hq, const fdec_kv *kv, int *S) {
     if (num_splits < 0 || num_splits > FDEC_MAX_SPLITS)
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: num_splits %d outside [0, %d]", fn, num_splits, FDEC_MAX_SPLITS);
@@ -301,8 +293,6 @@ int fdec_decode_validate(const char *fn, const void *q, int B, int Hq, const fde
     int rc = validate_common(fn, q, B, Hq, kv, seq_lens, softmax_scale);
     if (rc) return rc;
     if ((rc = validate_append(fn, append, kv))) return rc;
-    if (kv->dtype == FDEC_FP8_E4M3 && append)
-        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: append into a float8 cache is not built", fn);
     if (fused != 0 && fused != 1) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: fused must be 0 or 1", fn);
     if ((rc = resolve_splits(fn, num_splits, B, Hq, kv, S_out))) return rc;
     if (B == 0) return FDEC_OK;
@@ -431,7 +421,6 @@ extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv 
     if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_m) & 3u) || (reinterpret_cast<uintptr_t>(part_d) & 3u))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: part_o must be 16-byte aligned", fn);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, num_splits, softmax_scale, append);
-    if ((rc = check_fp8(fn, kv, p, append))) return rc;
     p.po = part_o;
     p.pm = part_m;
     p.pd = part_d;

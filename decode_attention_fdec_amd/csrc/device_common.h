@@ -24,6 +24,29 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w) {
     return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
+// The e4m3fn code (OCP float8: sign, 4 exponent bits with bias 7, 3 fraction
+// bits) of a binary32 value, rounded to nearest with ties to even. Magnitudes
+// of 448 (the largest finite code) and above saturate to +-448, NaN gives the
+// NaN code 0x7f. Below 2^-6 the codes are the multiples of 2^-9 (a rounded to
+// an integer count of them; 8 of them is the smallest normal code 0x08).
+// Above, the top three fraction bits are kept and rounded on the rest; a
+// carry out of the fraction moves into the exponent field by the addition.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = __builtin_fabsf(x);
+    if (!(a == a)) return 0x7fu;
+    if (a >= 448.0f) return sign | 0x7eu;
+    if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+    const uint32_t ua = u & 0x7fffffffu;
+    const uint32_t e = (ua >> 23) - 120u;  // binary32 exponent field - 127 + 7
+    const uint32_t frac = ua & 0x7fffffu;
+    const uint32_t rest = frac & 0xfffffu;
+    uint32_t r = frac >> 20;
+    r += (rest > 0x80000u || (rest == 0x80000u && (r & 1u))) ? 1u : 0u;
+    return sign | ((e << 3) + r);
+}
+
 // The (request b, KV head g) descale of a float8 cache (1 without one), by a
 // scalar load; P is the kernels' parameter block (Hkv KV heads).
 template <class P>

@@ -33,9 +33,11 @@
 
 namespace fdec {
 
-// Kernel-only mode: plain decode over a float8 e4m3fn cache.
-constexpr int kPlainF8 = 3;
-static_assert(kPlainF8 != kPlain && kPlainF8 != kAppend && kPlainF8 != kAppendRope, "distinct modes");
+// Kernel-only modes over a float8 e4m3fn cache: plain decode, and the two
+// append modes (the new row stored as codes of value / descale).
+constexpr int kPlainF8 = 3, kAppendF8 = 4, kAppendRopeF8 = 5;
+static_assert(kPlainF8 != kPlain && kPlainF8 != kAppend && kPlainF8 != kAppendRope && kAppendF8 > kAppendRope,
+              "distinct modes");
 
 // Register tiles in flight per wave and the waves per SIMD the kernel is
 // compiled for, by GQA group size (D = 128): more tiles hide more latency,
@@ -61,16 +63,16 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
     constexpr int NQ = NCH * 4;           // packed dwords per lane per row
     constexpr int NR = (G >= 8) ? 1 : 2;  // 8-row groups per tile
     constexpr int TT = 8 * NR;            // tokens per tile
-    constexpr bool QF32 = (MODE == kAppendRope);
+    constexpr bool QF32 = (MODE == kAppendRope || MODE == kAppendRopeF8);  // rotary: q in fp32
     constexpr int NBUF = MapConfig<G, D>::nbuf;
-    constexpr bool F8 = (MODE == kPlainF8);
-    constexpr bool APPEND = (MODE == kAppend || MODE == kAppendRope);
+    constexpr bool F8 = (MODE == kPlainF8 || MODE == kAppendF8 || MODE == kAppendRopeF8);
+    constexpr bool APPEND = (MODE == kAppend || MODE == kAppendRope || MODE == kAppendF8 || MODE == kAppendRopeF8);
     constexpr int ES = F8 ? 1 : 2;  // bytes per cache element
     static_assert(!F8 || DT == 1, "float8 caches take bf16 queries");
     using E = Elem<DT>;
     using Piece = typename std::conditional<F8, uint2, uint4>::type;  // one lane's 8 elements of a row
 
-    __shared__ float sm_vec[(MODE == kAppendRope) ? MapConfig<G, D>::max_waves * (G + 1) * D : 1];
+    __shared__ float sm_vec[QF32 ? MapConfig<G, D>::max_waves * (G + 1) * D : 1];
     __shared__ int sm_flag;
 
     const int split = blockIdx.x, b = blockIdx.y;
@@ -101,11 +103,25 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
         }
     };
 
+    // Float8 append: the new row's codes, value / descale rounded to e4m3fn
+    // (the k value from kf in fp32 when rotated, else from the bf16 ksrc).
+    auto store_row_f8 = [&](int64_t off, const float *kf, const uint16_t *ksrc, const uint16_t *vsrc, int ln) {
+        uint8_t *kd = reinterpret_cast<uint8_t *>(const_cast<char *>(p.k)) + off;
+        uint8_t *vd = reinterpret_cast<uint8_t *>(const_cast<char *>(p.v)) + off;
+        const float kds = kv_descale(p.k_descale, p, b, g), vds = kv_descale(p.v_descale, p, b, g);
+        for (int i = ln; i < D; i += 64) {
+            const float kx = kf ? kf[i] : Elem<1>::lo((uint32_t)ksrc[i]);
+            kd[i] = (uint8_t)f32_to_e4m3(__fdiv_rn(kx, kds));
+            vd[i] = (uint8_t)f32_to_e4m3(__fdiv_rn(Elem<1>::lo((uint32_t)vsrc[i]), vds));
+        }
+    };
+    (void)store_row_f8;
+
     // ---------------------------------------------------------------- q (and append)
     uint32_t qp[QF32 ? 1 : G][NQ];
     float qf[QF32 ? G : 1][QF32 ? NE : 1];
     const bool owner = APPEND && (t_begin <= c_app) && (c_app < t_begin + p.chunk);
-    if constexpr (MODE == kAppendRope) {
+    if constexpr (QF32) {
         // rotate q (and, in the block owning the new row, k_new) in this wave's
         // part of LDS, fp32
         float *qs = sm_vec + wv * (G + 1) * D;
@@ -138,12 +154,16 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
                 for (int e = 0; e < 8; ++e) qf[h][c * 8 + e] = qs[h * D + 64 * c + 8 * cb + e];
         if (owner) {
             const int64_t off = row_offset(c_app);
-            uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k)) + off;
-            uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v)) + off;
             const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)b * p.Hkv + g) * D;
-            for (int i = lane; i < D; i += 64) {
-                kd[i] = E::from_float(ks[i]);
-                vd[i] = vsrc[i];
+            if constexpr (F8) {
+                store_row_f8(off, ks, nullptr, vsrc, lane);
+            } else {
+                uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k)) + off;
+                uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v)) + off;
+                for (int i = lane; i < D; i += 64) {
+                    kd[i] = E::from_float(ks[i]);
+                    vd[i] = vsrc[i];
+                }
             }
             // this wave reads the row back below, through the same L2; no
             // earlier load of this kernel cached it in L1: completing the
@@ -163,16 +183,20 @@ __global__ __launch_bounds__((64 * MapConfig<G, D>::max_waves), (MapConfig<G, D>
                 qp[h][4 * c + 2] = u.z;
                 qp[h][4 * c + 3] = u.w;
             }
-        if constexpr (MODE == kAppend) {
+        if constexpr (APPEND) {
             if (owner) {
                 const int64_t off = row_offset(c_app);
-                uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k)) + off;
-                uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v)) + off;
                 const uint16_t *ksrc = reinterpret_cast<const uint16_t *>(p.k_new) + ((int64_t)b * p.Hkv + g) * D;
                 const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)b * p.Hkv + g) * D;
-                for (int i = lane; i < D; i += 64) {
-                    kd[i] = ksrc[i];
-                    vd[i] = vsrc[i];
+                if constexpr (F8) {
+                    store_row_f8(off, nullptr, ksrc, vsrc, lane);
+                } else {
+                    uint16_t *kd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.k)) + off;
+                    uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v)) + off;
+                    for (int i = lane; i < D; i += 64) {
+                        kd[i] = ksrc[i];
+                        vd[i] = vsrc[i];
+                    }
                 }
                 __builtin_amdgcn_s_waitcnt(0);  // as above: the stores complete before the read-back
             }
@@ -451,9 +475,13 @@ static hipError_t launch_t(const MapParams &p, int S, hipStream_t st) {
 
 template <int DT, int D, int G, bool PAGED>
 static hipError_t launch_mode(const MapParams &p, int S, hipStream_t st) {
-    if (p.kv_fp8) {  // plain decode with bf16 queries only
+    if (p.kv_fp8) {  // bf16 queries only
         if constexpr (DT == 1) {
-            if (p.mode == kPlain) return launch_t<DT, D, G, PAGED, kPlainF8>(p, S, st);
+            switch (p.mode) {
+                case kPlain: return launch_t<DT, D, G, PAGED, kPlainF8>(p, S, st);
+                case kAppend: return launch_t<DT, D, G, PAGED, kAppendF8>(p, S, st);
+                default: return launch_t<DT, D, G, PAGED, kAppendRopeF8>(p, S, st);
+            }
         }
         return hipErrorInvalidValue;
     }

@@ -94,9 +94,10 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  * Float8 caches (dtype FDEC_FP8_E4M3): element (b, t, g, d) stands for its
  * e4m3 value times k_descale[b*Hkv + g] (K) or v_descale[b*Hkv + g] (V); a NULL
  * descale is 1. Queries are bf16. Built for page_size a multiple of 16 (or
- * contiguous), without append: every GQA group size and head_dim in
- * fdec_decode and fdec_decode_partials (the matrix-core map kernel for
- * Hq = 4 or 8 Hkv at head_dim 128, the vector kernel otherwise); head_dim 128
+ * contiguous): every GQA group size and head_dim in fdec_decode and
+ * fdec_decode_partials (the matrix-core map kernel for Hq = 4 or 8 Hkv at
+ * head_dim 128 without append, the vector kernel otherwise, and for every
+ * append); head_dim 128
  * with Hq = 4 Hkv in fdec_decode_balanced and fdec_decode_multi, and with
  * Hq = 8 Hkv in fdec_decode_balanced; fdec_decode_multi with q_len = 1 takes
  * every shape fdec_decode does; other calls and shapes return
@@ -140,9 +141,14 @@ typedef struct fdec_kv {
  * is rotated by the same position in fp32 before attention. Only q and
  * k are rotated, never v. rotary_dim == 0 appends without rotation. Pairs are
  * (i, i + rotary_dim/2) for i < rotary_dim/2; dims >= rotary_dim are untouched.
+ * Float8 caches ([cookbook] §7.2 FP8 KV cache): k_new and v_new are bf16 (the
+ * queries' dtype) and each element of the new rows is stored as the e4m3fn
+ * code of (value / descale), the k value rotated in fp32 first; the division
+ * is fp32, the code the nearest one (ties to even), magnitudes from 448 up
+ * saturate to +-448 and NaN stays NaN. Attention then reads the stored codes.
  */
 typedef struct fdec_append {
-    const void *k_new;    /* device [B, Hkv, D], cache dtype, contiguous */
+    const void *k_new;    /* device [B, Hkv, D], the queries' dtype, contiguous */
     const void *v_new;    /* device [B, Hkv, D] */
     const float *rope_cos; /* device [rope_max_pos, rotary_dim/2] fp32, or NULL if rotary_dim == 0 */
     const float *rope_sin;

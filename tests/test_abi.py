@@ -236,12 +236,14 @@ def test_fp8_validation(fdec):
     fp8 = dict(dtype=F.FDEC_FP8_E4M3)
     # strides must be multiples of 16 bytes: 16 float8 elements
     assert call_decode(kv_struct(s_head=8, **fp8)) == F.FDEC_ERR_INVALID_ARG
-    # float8 runs without append; the balanced split takes it at G = 4 or 8 only
+    # the balanced split takes float8 at G = 4 or 8 only
     assert call_balanced(kv_struct(**fp8), Hq=16) == F.FDEC_ERR_UNSUPPORTED  # G = 2
+    # an append into a float8 cache is checked like any other
     a = F.FdecAppend()
     a.k_new, a.v_new = FAKE, FAKE
-    assert call_decode(kv_struct(**fp8), append=a) == F.FDEC_ERR_UNSUPPORTED
-    assert "append" in last_error()
+    a.rotary_dim = 3
+    assert call_decode(kv_struct(**fp8), append=a) == F.FDEC_ERR_INVALID_ARG
+    assert "rotary_dim" in last_error()
     # no cascade path for float8
     kvp = kv_struct(page_size=64, page_table=FAKE, max_pages_per_seq=32, capacity=0, **fp8)
     assert lib.fdec_cascade_decode(FAKE, 2, 32, ctypes.byref(kvp), FAKE, 64, FAKE, 2, 2, 0.0, FAKE, None,
