@@ -24,7 +24,9 @@ The five named workloads follow the shapes of the pages' examples:
   c5  cascade, 64 requests, Hq=32, Hkv=8, page 64, shared 16384-token prefix,
       suffixes U{256..2048}, bf16
 and float8 versions of c2 and c3 (c2f8, c3f8): the same shapes and seeds with
-float8 e4m3fn K/V and bf16 queries. Float8 append cases draw k_new / v_new as
+float8 e4m3fn K/V and bf16 queries (also c1f8, c2g2f8 and the cascade c5f8, whose
+shared prefix pages are stored at descale 1/32 and read with each request's
+descales). Float8 append cases draw k_new / v_new as
 bf16 and the descales after them (the caches are quantised as above).
 """
 from __future__ import annotations
@@ -378,13 +380,26 @@ def cascade_case(seed: int, B: int, Hq: int, Hkv: int, D: int, prefix_len: int, 
         off += n
     for p in perm[off:].tolist():
         mask[p, :] = True
-    q = _randn(g, (B, Hq, D), dtype)
-    k = _randn(g, (pool, ps, Hkv, D), dtype)
-    v = _randn(g, (pool, ps, Hkv, D), dtype)
+    q = _randn(g, (B, Hq, D), _q_dtype(dtype))
+    k = _randn(g, (pool, ps, Hkv, D), _kv_draw_dtype(dtype))
+    v = _randn(g, (pool, ps, Hkv, D), _kv_draw_dtype(dtype))
     _fill_pad(k, mask, pad, g)
     _fill_pad(v, mask, pad, g)
+    kd = vd = None
+    if dtype == FP8:
+        # a request's own pages carry its descales; the shared prefix pages (and
+        # unused ones) are stored at 1/32 and read with each request's descale
+        kd, vd = _descales(g, B, Hkv)
+        fk = torch.full((pool, Hkv), 1.0 / 32)
+        fv = torch.full((pool, Hkv), 1.0 / 32)
+        for b in range(B):
+            pl = table[b][table[b] >= 0].long()
+            fk[pl] = kd[b]
+            fv[pl] = vd[b]
+        k = _quantize(k, fk[:, None, :, None])
+        v = _quantize(v, fv[:, None, :, None])
     return Case(name, dtype, B, Hq, Hkv, D, q, k, v, sl, page_size=ps, page_table=table,
-                prefix_pages=prefix_pages, prefix_len=prefix_len)
+                prefix_pages=prefix_pages, prefix_len=prefix_len, k_descale=kd, v_descale=vd)
 
 
 def workload(name: str, pad: str = "zero") -> Case:
@@ -413,6 +428,9 @@ def workload(name: str, pad: str = "zero") -> Case:
     if name == "c5":
         return cascade_case(5, 64, 32, 8, 128, 16384, 64, suffix_range=(256, 2048), dtype=BF16,
                             pad=pad, name="c5")
+    if name == "c5f8":  # c5 with a float8 e4m3fn page pool
+        return cascade_case(5, 64, 32, 8, 128, 16384, 64, suffix_range=(256, 2048), dtype=FP8,
+                            pad=pad, name="c5f8")
     raise KeyError(name)
 
 

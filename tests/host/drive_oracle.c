@@ -71,7 +71,7 @@ static void one_case(int c) {
     } else {
         maxp = (cap + ps - 1) / ps;
         cap = maxp * ps;
-        if (dtype != 2 && ri(0, 2) == 0) prefix_len = ri(1, 100);
+        if (ri(0, 2) == 0) prefix_len = ri(1, 100);
         int prefix_pages = (prefix_len + ps - 1) / ps;
         npages = B * maxp + prefix_pages + ri(0, 3);
         kv.s_token = (int64_t)Hkv * D, kv.s_head = D, kv.s_outer = (int64_t)ps * Hkv * D;

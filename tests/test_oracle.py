@@ -381,6 +381,23 @@ def test_cascade_equals_attention_over_prefix_then_suffix():
     assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
 
 
+def test_fp8_cascade_matches_sdpa_over_dequantised_prefix_then_suffix():
+    # a float8 pool: request b attends to the shared prefix, then its own pages,
+    # every element read as its e4m3 value times request b's descales
+    case = cascade_case(24, 3, 8, 2, 32, prefix_len=50, ps=16, suffix_lens=[0, 5, 40], dtype=FP8,
+                        pad="nan", extra_pages=2)
+    got = oracle.decode(okv(case), case.q, case.seq_lens, 0.2)
+    for b in range(3):
+        toks = [(int(case.prefix_pages[j // 16]), j % 16) for j in range(50)]
+        toks += [(int(case.page_table[b, j // 16]), j % 16) for j in range(int(case.seq_lens[b]))]
+        kd, vd = case.k_descale[b].double(), case.v_descale[b].double()
+        kr = torch.stack([case.k[p_, s_].double() * kd[:, None] for p_, s_ in toks])  # [L, Hkv, D]
+        vr = torch.stack([case.v[p_, s_].double() * vd[:, None] for p_, s_ in toks])
+        ro, rl = _sdpa_rows(case.q[b], kr, vr, 0.2)
+        np.testing.assert_allclose(got[0][b], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(got[1][b], rl, rtol=0, atol=1e-12)
+
+
 def test_cascade_with_ragged_prefix_matches_gathered_rows():
     case = cascade_case(22, 2, 4, 2, 16, prefix_len=37, ps=16, suffix_lens=[3, 19], dtype=F16,
                         pad="nan")
