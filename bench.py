@@ -46,6 +46,8 @@ WORKLOAD_TEXT = {
             "per-(request, KV head) descales, bf16 queries, 16 splits",
     "c2g2f8": "long-context GQA decode with two query heads per KV head: B=1, Hq=16, Hkv=8, D=128, "
               "131072 contiguous float8 e4m3fn tokens, per-(request, KV head) descales, bf16 queries",
+    "c5f8": "cascade: 64 requests, Hq=32, Hkv=8, D=128, shared 16384-token prefix + U[256,2048] suffix, "
+            "page 64, float8 e4m3fn pool with per-(request, KV head) descales, bf16 queries",
 }
 # every library source: a change to any of them (kernels, launch code, planner) marks stored counters stale
 KERNEL_SOURCES = sorted(f for f in os.listdir(os.path.join(ROOT, "decode_attention_fdec_amd", "csrc"))
@@ -134,7 +136,7 @@ class Runner:
         if self.cascade:
             self.F.cascade_decode(self.q, self.k[c], self.v[c], self.table, self.prefix_pages,
                                   self.case.prefix_len, self.lens, self.S[0], self.S[1], out=self.out,
-                                  lse=self.lse, workspace=self.ws)
+                                  lse=self.lse, workspace=self.ws, k_descale=self.kd, v_descale=self.vd)
             return
         if self.mode.startswith("multi"):
             self.F.decode_multi(self.q, self.k[c], self.v[c], self.lens, page_table=self.table, num_splits=self.S,
@@ -467,10 +469,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5", "c2f8", "c3f8", "c2g8", "c1f8", "c2g2f8"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "c2f8", "c3f8", "c2g8", "c1f8", "c2g2f8", "c5f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8,c2g2f8",
+    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8,c2g2f8,c5f8",
                     help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=24.0, help="CPU oracle timing budget (all runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

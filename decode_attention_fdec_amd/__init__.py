@@ -479,11 +479,13 @@ def cascade_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table
                    prefix_pages: torch.Tensor, prefix_len: int, suffix_lens: torch.Tensor,
                    splits_prefix: int = 0, splits_suffix: int = 0, softmax_scale: float = 0.0,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   workspace: Optional[Workspace] = None, cache_leftpad: Optional[torch.Tensor] = None):
+                   workspace: Optional[Workspace] = None, cache_leftpad: Optional[torch.Tensor] = None,
+                   k_descale: Optional[torch.Tensor] = None, v_descale: Optional[torch.Tensor] = None):
     """fdec_cascade_decode: shared prefix + per-request suffix, merged exactly (no left padding)."""
     lib = load_library()
     B, Hq, D = q.shape
-    kv = make_kv(k, v, page_table, cache_leftpad=cache_leftpad)
+    kv = make_kv(k, v, page_table, k_descale, v_descale, cache_leftpad=cache_leftpad)
+    _check_q(q, k)
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None:

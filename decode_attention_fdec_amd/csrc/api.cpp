@@ -647,8 +647,6 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     const char *fn = "fdec_cascade_decode";
     int rc = validate_common(fn, q, B, Hq, kv, suffix_lens, softmax_scale);
     if (rc) return rc;
-    if (kv->dtype == FDEC_FP8_E4M3)
-        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: float8 caches are not built for the cascade path", fn);
     if (kv->page_size == 0) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: the cascade path needs a paged cache", fn);
     if (kv->cache_leftpad)
         return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: cache_leftpad is not supported with a shared prefix", fn);
@@ -697,7 +695,10 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     cp.Hkv = kv->num_kv_heads;
     cp.chunk = (int)chunk_p;
     cp.scale_log2 = scale * 1.4426950408889634f;
-    cp.dtype = kv->dtype;
+    cp.kv_fp8 = kv->dtype == FDEC_FP8_E4M3;
+    cp.dtype = cp.kv_fp8 ? FDEC_BF16 : kv->dtype;  // the queries' type
+    cp.k_descale = cp.kv_fp8 ? kv->k_descale : nullptr;
+    cp.v_descale = cp.kv_fp8 ? kv->v_descale : nullptr;
 
     fdec::MapParams pb = map_params(q, B, Hq, kv, suffix_lens, 1, softmax_scale, nullptr);
     if (pb.mfma && cascade_balanced_shape(Hq, kv->num_kv_heads, kv->head_dim) &&

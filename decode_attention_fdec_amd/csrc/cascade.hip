@@ -27,6 +27,11 @@
 //   - O += P V: A = P straight from the S^T registers (the key order inside the
 //     K dimension is permuted identically for A and B), B = V^T from two
 //     ds_read_b64_tr_b16 of the row-major V tile (4 keys at one d per lane each).
+// Float8 pools (the pages' FP8 KV cache, e4m3fn with per-(request, KV head)
+// descales): rows of 128 bytes, one DMA instruction per wave for its 8 rows of
+// K and one for V; K pieces and V (by the 8-bit transpose read) widen to bf16
+// in registers (exact), the K descale of each query row's request scales its
+// scores and the V descale its state.
 // Layout of v_mfma_f32_16x16x32 (lane l, kq = l / 16): A holds row l % 16,
 // k = 8 kq .. 8 kq + 7; B holds column l % 16, k = 8 kq .. 8 kq + 7; D holds rows
 // 4 kq .. 4 kq + 3 of column l % 16.
@@ -71,15 +76,26 @@ template <> __device__ __forceinline__ uint32_t pfx_pack2<1>(float a, float b) {
     return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
 }
 constexpr int kPfxNS = 3;                  // ring slots (two tiles in flight)
-constexpr int kPfxTileBytes = kPfxKeys * 256;  // 64 rows of 128 16-bit elements
 typedef short pfx_s16x4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) pfx_s16x4_v pfx_lds_s16x4;
+typedef int pfx_i32x2_v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) pfx_i32x2_v pfx_lds_i32x2;
 
-template <int DT>
+// Float8 tiles: the 16-byte slot of piece p in row r is p ^ pfx_swz8(r). A K read
+// (16 rows 16kb .. 16kb + 15, one piece) and a V transpose read (rows 4kq + 0..3
+// and 16 + 4kq + 0..3 of a 32-row half, one piece) then take distinct
+// (row parity, slot) pairs in each group of 16 lanes: distinct banks.
+__device__ __forceinline__ int pfx_swz8(int r) { return ((r >> 1) & 7) ^ ((r >> 2) & 4); }
+
+template <int DT, int KF>
 __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const CascadeParams p) {
     constexpr int D = 128;
-    __shared__ __attribute__((aligned(16))) uint8_t kring[kPfxNS][kPfxTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t vring[kPfxNS][kPfxTileBytes];
+    constexpr int ES = KF ? 1 : 2;                 // bytes per element
+    constexpr int RB = D * ES;                     // bytes per K / V row in LDS
+    constexpr int kDma = KF ? 2 : 4;               // DMA instructions per wave and tile
+    static_assert(!KF || DT == 1, "float8 pools take bf16 queries");
+    __shared__ __attribute__((aligned(16))) uint8_t kring[kPfxNS][kPfxKeys * RB];
+    __shared__ __attribute__((aligned(16))) uint8_t vring[kPfxNS][kPfxKeys * RB];
     __shared__ int spages[kPrefixPagesPerBlock];
     __shared__ float srow[kPfxWaves][3][kPfxRowsPerWave];
 
@@ -115,29 +131,44 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // per-lane factors of the query rows 16rb + li: float8 descales of the row's request
+    float ksc[kRB], vsc[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+        const int row = rc * kPfxRows + w * kPfxRowsPerWave + rb * 16 + li;
+        const int64_t i = (int64_t)(row < R ? row / G : 0) * p.Hkv + g;
+        ksc[rb] = p.scale_log2 * (KF && p.k_descale ? p.k_descale[i] : 1.0f);
+        vsc[rb] = KF && p.v_descale ? p.v_descale[i] : 1.0f;
+    }
+
     // DMA of tile `tile` into ring slot tile % kPfxNS: this wave's rows 8w .. 8w + 7
-    // of K and of V, four rows (one page: pages hold multiples of 16 keys) per
-    // instruction; rows past the split's end repeat its last key (masked below).
+    // of K and of V, four rows (16-bit) or all eight (float8) per instruction
+    // (one page: pages hold multiples of 16 keys); rows past the split's end
+    // repeat its last key (masked below).
     // Default cache policy: unlike the split-KV kernels' streaming reads, the
     // non-temporal one measured slower here (the prefix block's loads are fewer and
     // its time goes to the matrix cores and the state writes, not to the stream)
-    const uint32_t stok = (uint32_t)(p.s_token * 2);
+    const uint32_t stok = (uint32_t)(p.s_token * ES);
     auto issue = [&](int tile) {
         const int t0 = t_begin + tile * kPfxKeys;
         const int nvalid = t_end - t0;
         const int slot = tile % kPfxNS;
+        constexpr int kPieces = RB / 16;           // 16-byte pieces per row
+        constexpr int kRowsPerDma = 64 / kPieces;  // rows one instruction moves
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int r0 = 8 * w + 4 * gi;
+        for (int gi = 0; gi < 8 / kRowsPerDma; ++gi) {
+            const int r0 = 8 * w + kRowsPerDma * gi;
             const int rs = min(r0, nvalid - 1);  // the group's first source row
             const int t = t0 + rs;
             const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
             const int64_t eoff = (int64_t)spages[pidx - pg0] * p.s_outer +
                                  (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head;
-            const int r = r0 + (lane >> 4);
-            const uint32_t voff = (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane & 15) ^ (r & 15));
-            dma16(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kring[slot]) + 256u * r0);
-            dma16(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vring[slot]) + 256u * r0);
+            const int r = r0 + lane / kPieces;
+            const int sw = KF ? pfx_swz8(r) : (r & 15);
+            const uint32_t voff =
+                (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane % kPieces) ^ sw);
+            dma16(reinterpret_cast<const char *>(p.k) + eoff * ES, voff, lds_addr(kring[slot]) + (uint32_t)RB * r0);
+            dma16(reinterpret_cast<const char *>(p.v) + eoff * ES, voff, lds_addr(vring[slot]) + (uint32_t)RB * r0);
         }
     };
 
@@ -160,7 +191,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         // this wave's part of the tile has landed once only later tiles' loads
         // remain; the barrier then covers every wave's part, and every wave is
         // done with the slot the next DMA overwrites (read two tiles ago)
-        wait_vm_n<4>(min(kPfxNS - 2, ntiles - 1 - tile));
+        wait_vm_n<kDma>(min(kPfxNS - 2, ntiles - 1 - tile));
         __syncthreads();
         if (tile + kPfxNS - 1 < ntiles) issue(tile + kPfxNS - 1);
         const int t0 = t_begin + tile * kPfxKeys;
@@ -176,7 +207,15 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int kr = 16 * kb + li;
-                const uint4 a = *reinterpret_cast<const uint4 *>(K + kr * 256 + 16 * ((4 * ks + kq) ^ (kr & 15)));
+                uint4 a;
+                if constexpr (KF == 1) {  // d = 32ks + 8kq .. + 7: half kq & 1 of piece 2ks + kq / 2
+                    const uint2 k8 = *reinterpret_cast<const uint2 *>(
+                        K + kr * 128 + 16 * ((2 * ks + (kq >> 1)) ^ pfx_swz8(kr)) + 8 * (kq & 1));
+                    const uint2 lo = fp8x4_to_bf16(k8.x), hi = fp8x4_to_bf16(k8.y);
+                    a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                } else {
+                    a = *reinterpret_cast<const uint4 *>(K + kr * 256 + 16 * ((4 * ks + kq) ^ (kr & 15)));
+                }
 #pragma unroll
                 for (int rb = 0; rb < kRB; ++rb) s[kb][rb] = Mfma<DT>::run(a, qb[rb][ks], s[kb][rb]);
             }
@@ -193,7 +232,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = s[kb][rb][r] * p.scale_log2;
+                    float v = s[kb][rb][r] * ksc[rb];
                     if (16 * kb + 4 * kq + r >= nvalid) v = kNegInf;
                     s[kb][rb][r] = v;
                     x = fmaxf(x, v);
@@ -256,21 +295,38 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         // ---- O += P V
         // B operand of K-slots 8kq .. 8kq + 7 at d = 16db + li: keys 32kk + 4kq + 0..3
         // and 32kk + 16 + 4kq + 0..3, each set from one transpose read whose lane m
-        // (of 16) addresses key row 32kk (+16) + 4kq + m / 4, d 16db + 4 (m % 4) .. + 3
+        // (of 16) addresses key row 32kk (+16) + 4kq + m / 4, d 16db + 4 (m % 4) .. + 3.
+        // Float8: one 8-bit transpose read (in each group of 16 lanes, lane j gets
+        // byte j % 8 of the 8-byte chunks of lanes j / 8 + 2k, k = 0..7) whose lane m
+        // addresses the k = m / 2-th of those 8 keys, bytes 16db + 8 (m & 1) .. + 7
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+            if constexpr (KF == 1) {
+                const int k8 = li >> 1;
+                const int rv = 32 * kk + (k8 < 4 ? 4 * kq + k8 : 16 + 4 * kq + (k8 - 4));
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const int ra = 32 * kk + 4 * kq + (li >> 2), rb2 = ra + 16;
-                const int piece = 2 * db + ((li & 3) >> 1), half = 8 * (li & 1);
-                const pfx_s16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (pfx_lds_s16x4 *)(V + ra * 256 + 16 * (piece ^ (ra & 15)) + half));
-                const pfx_s16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (pfx_lds_s16x4 *)(V + rb2 * 256 + 16 * (piece ^ (rb2 & 15)) + half));
-                const uint2 v0 = __builtin_bit_cast(uint2, x0), v1 = __builtin_bit_cast(uint2, x1);
-                const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
+                for (int db = 0; db < 8; ++db) {
+                    const pfx_i32x2_v x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (pfx_lds_i32x2 *)(V + rv * 128 + 16 * (db ^ pfx_swz8(rv)) + 8 * (li & 1)));
+                    const uint2 v0 = fp8x4_to_bf16((uint32_t)x[0]), v1 = fp8x4_to_bf16((uint32_t)x[1]);
+                    const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-                for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
+                    for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
+                }
+            } else {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const int ra = 32 * kk + 4 * kq + (li >> 2), rb2 = ra + 16;
+                    const int piece = 2 * db + ((li & 3) >> 1), half = 8 * (li & 1);
+                    const pfx_s16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (pfx_lds_s16x4 *)(V + ra * 256 + 16 * (piece ^ (ra & 15)) + half));
+                    const pfx_s16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (pfx_lds_s16x4 *)(V + rb2 * 256 + 16 * (piece ^ (rb2 & 15)) + half));
+                    const uint2 v0 = __builtin_bit_cast(uint2, x0), v1 = __builtin_bit_cast(uint2, x1);
+                    const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+                    for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
+                }
             }
         }
 
@@ -285,7 +341,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         const float T = tmax[rb];
         const float f = (T == kNegInf) ? 0.0f : fexp2(m[rb] - T);
         if (kq == 0) {
-            srow[w][0][16 * rb + li] = f;
+            srow[w][0][16 * rb + li] = f * vsc[rb];  // V's descale (1 for 16-bit pools)
             srow[w][1][16 * rb + li] = lt * f;
             srow[w][2][16 * rb + li] = (T == kNegInf) ? kNegInf : T * kLn2;
         }
@@ -316,10 +372,14 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
 hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t st) {
     const int R = p.B * (p.Hq / p.Hkv);
     dim3 grid(splits, p.Hkv, (R + kPfxRows - 1) / kPfxRows);
-    if (p.dtype == 0)
-        hipLaunchKernelGGL(cascade_prefix_kernel<0>, grid, dim3(kPfxThreads), 0, st, p);
-    else
-        hipLaunchKernelGGL(cascade_prefix_kernel<1>, grid, dim3(kPfxThreads), 0, st, p);
+    if (p.kv_fp8) {
+        if (p.dtype != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((cascade_prefix_kernel<1, 1>), grid, dim3(kPfxThreads), 0, st, p);
+    } else if (p.dtype == 0) {
+        hipLaunchKernelGGL((cascade_prefix_kernel<0, 0>), grid, dim3(kPfxThreads), 0, st, p);
+    } else {
+        hipLaunchKernelGGL((cascade_prefix_kernel<1, 0>), grid, dim3(kPfxThreads), 0, st, p);
+    }
     return hipGetLastError();
 }
 

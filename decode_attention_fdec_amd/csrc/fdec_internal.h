@@ -114,7 +114,10 @@ struct CascadeParams {
     float scale_log2;
     float *po, *pm, *pd;            // states, slots [s_offset, s_offset + splits)
     int s_total, s_offset;
-    int dtype;
+    int dtype;                      // the queries' (and matrix cores') type: 0 fp16, 1 bf16
+    // float8 e4m3fn pool (queries bf16): [B, Hkv] descales of the querying request, or nullptr (1)
+    int kv_fp8;
+    const float *k_descale, *v_descale;
 };
 // Grid: (splits, Hkv, ceil(B * Hq / Hkv / 256)).
 hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t stream);

@@ -244,10 +244,12 @@ def test_fp8_validation(fdec):
     a.rotary_dim = 3
     assert call_decode(kv_struct(**fp8), append=a) == F.FDEC_ERR_INVALID_ARG
     assert "rotary_dim" in last_error()
-    # no cascade path for float8
-    kvp = kv_struct(page_size=64, page_table=FAKE, max_pages_per_seq=32, capacity=0, **fp8)
+    # the cascade takes float8 pools under the same checks as 16-bit ones
+    kvp = kv_struct(page_size=64, page_table=FAKE, max_pages_per_seq=32, capacity=0, head_dim=64, s_outer=64 * 8 * 64,
+                    s_token=8 * 64, s_head=64, **fp8)
     assert lib.fdec_cascade_decode(FAKE, 2, 32, ctypes.byref(kvp), FAKE, 64, FAKE, 2, 2, 0.0, FAKE, None,
                                    FAKE, 1 << 30, None) == F.FDEC_ERR_UNSUPPORTED
+    assert "head_dim" in last_error()
     # an unknown element type
     assert call_decode(kv_struct(dtype=3)) == F.FDEC_ERR_UNSUPPORTED
 

@@ -9,7 +9,7 @@ import torch
 import decode_attention_fdec_amd as F
 import oracle
 from helpers import assert_parity, oracle_decode, to_dev
-from synth import BF16, F16, cascade_case, workload
+from synth import BF16, F16, FP8, cascade_case, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,8 @@ def _gpu(fdec):
 def run_cascade(case, sp=0, ss=0, scale=0.0):
     d = to_dev(case)
     out, lse = F.cascade_decode(d["q"], d["k"], d["v"], d["page_table"], d["prefix_pages"], case.prefix_len,
-                                d["seq_lens"], sp, ss, softmax_scale=scale)
+                                d["seq_lens"], sp, ss, softmax_scale=scale, k_descale=d["k_descale"],
+                                v_descale=d["v_descale"])
     torch.cuda.synchronize()
     return out, lse
 
@@ -42,7 +43,67 @@ CASES = [
                                            dtype=BF16, pad="nan")),
     ("empty_prefix", lambda: cascade_case(76, 3, 8, 2, 128, prefix_len=0, ps=16, suffix_lens=[10, 0, 70],
                                           dtype=BF16, pad="nan")),
+    # float8 pools (the pages' FP8 KV cache): the prefix kernel's float8 tiles,
+    # the suffix on the balanced split (G = 4) or the uniform map kernels
+    ("fp8_ragged_g4", lambda: cascade_case(78, 3, 16, 4, 128, prefix_len=100, ps=16, suffix_lens=[0, 5, 40],
+                                           dtype=FP8, pad="nan", extra_pages=2)),
+    ("fp8_g1_ps64", lambda: cascade_case(79, 2, 8, 8, 128, prefix_len=700, ps=64, suffix_lens=[100, 300],
+                                         dtype=FP8, pad="nan")),
+    ("fp8_g8_ps32", lambda: cascade_case(80, 5, 16, 2, 128, prefix_len=512, ps=32, suffix_lens=[31, 32, 33, 0, 5],
+                                         dtype=FP8, pad="nan")),
+    ("fp8_rows_over_256", lambda: cascade_case(81, 70, 8, 2, 128, prefix_len=333, ps=16, suffix_range=(0, 40),
+                                               dtype=FP8, pad="nan")),
+    ("fp8_g2", lambda: cascade_case(82, 4, 8, 4, 128, prefix_len=129, ps=48, suffix_lens=[1, 2, 100, 47],
+                                    dtype=FP8, pad="nan")),
 ]
+
+
+def _request_rows(case, t, b):
+    """Rows [L, Hkv, D] (float64, dequantised) request b attends to: prefix, then suffix."""
+    ps = case.page_size
+    pre = t[case.prefix_pages.long()].reshape(-1, case.Hkv, case.D)[:case.prefix_len]
+    n = int(case.seq_lens[b])
+    suf = t[case.page_table[b, :(n + ps - 1) // ps].long()].reshape(-1, case.Hkv, case.D)[:n]
+    return torch.cat([pre, suf]).double()
+
+
+def p_rounding_bound(case):
+    """Per output element, the most that rounding P to bf16 for the P V matrix-core
+    operand (relative error at most 2^-9 per weight) can move it:
+    2^-9 sum_j p_j |v_jd| / sum_j p_j, with the exact weights p_j (float64, from the
+    dequantised rows). Test-side arithmetic for the tolerance only."""
+    G = case.Hq // case.Hkv
+    scale = 1.0 / math.sqrt(case.D)
+    out = np.zeros((case.B, case.Hq, case.D))
+    for b in range(case.B):
+        k, v = _request_rows(case, case.k, b), _request_rows(case, case.v, b)
+        if k.shape[0] == 0:
+            continue
+        if case.k_descale is not None:
+            k = k * case.k_descale[b].double()[None, :, None]
+            v = v * case.v_descale[b].double()[None, :, None]
+        q = case.q[b].double().view(case.Hkv, G, case.D)
+        s = torch.einsum("gid,lgd->gil", q, k) * scale
+        p = torch.exp(s - s.amax(dim=-1, keepdim=True))
+        wv = torch.einsum("gil,lgd->gid", p, v.abs()) / p.sum(-1, keepdim=True)
+        out[b] = (2.0 ** -9 * wv).reshape(case.Hq, case.D).numpy()
+    return out
+
+
+def assert_cascade_parity(case, out, lse, ref_out, ref_lse, what):
+    """16-bit pools: the usual tolerance. Float8 pools: the shared prefix pages hold
+    codes of value * 32 read at descales up to 1/16, so values reach twice N(0, 1) and
+    one key can hold much of a softmax; each output element is held to twice its
+    P-rounding bound (plus fp32 noise), the LSE to the usual tolerance."""
+    if case.dtype != FP8:
+        assert_parity(out, lse, ref_out, ref_lse, case.dtype, what)
+        return
+    err = np.abs(out.cpu().double().numpy() - ref_out)
+    assert np.isfinite(err).all(), f"{what}: non-finite output"
+    tol = 2.0 * p_rounding_bound(case) + 2e-5
+    r = err / tol
+    assert r.max() <= 1.0, f"{what}: error {err.max():.3g}, {r.max():.3g} x its bound at {np.unravel_index(r.argmax(), r.shape)}"
+    assert_parity(out * 0, lse, ref_out * 0, ref_lse, case.dtype, what)  # the LSE
 
 
 @pytest.mark.parametrize("name,builder", CASES, ids=[c[0] for c in CASES])
@@ -51,7 +112,7 @@ def test_cascade_matches_oracle(name, builder, sp, ss):
     case = builder()
     ref_out, ref_lse = oracle_decode(case)
     out, lse = run_cascade(case, sp, ss)
-    assert_parity(out, lse, ref_out, ref_lse, case.dtype, f"{name} sp={sp} ss={ss}")
+    assert_cascade_parity(case, out, lse, ref_out, ref_lse, f"{name} sp={sp} ss={ss}")
 
 
 def test_cascade_equals_plain_decode_over_concatenated_pages():
@@ -76,3 +137,49 @@ def test_cascade_full_workload():
     ref_out, ref_lse = oracle_decode(case)
     out, lse = run_cascade(case)
     assert_parity(out, lse, ref_out, ref_lse, case.dtype, "c5")
+
+
+def test_fp8_cascade_full_workload():
+    case = workload("c5f8", pad="nan")
+    ref_out, ref_lse = oracle_decode(case)
+    out, lse = run_cascade(case)
+    assert_cascade_parity(case, out, lse, ref_out, ref_lse, "c5f8")
+
+
+@pytest.mark.parametrize("sp,ss", [(1, 1), (3, 2)])
+@pytest.mark.parametrize("suffix", [True, False])
+def test_fp8_cascade_is_bitwise_the_bf16_cascade_on_the_same_values(sp, ss, suffix):
+    # descales 1/32 (a power of two): code / 32 is exact in bf16, the score scale and
+    # the state scale change by a power of two only, so the matrix cores see the same
+    # operands and the float8 pool gives the bf16 pool's bits
+    case = cascade_case(81, 70, 8, 2, 128, prefix_len=333, ps=16, suffix_range=(0, 40),
+                        suffix_lens=None if suffix else [0] * 70, dtype=FP8, pad="zero")
+    case.k_descale = torch.full((70, 2), 1.0 / 32)
+    case.v_descale = case.k_descale.clone()
+    o8, l8 = run_cascade(case, sp, ss)
+    bf = cascade_case(81, 70, 8, 2, 128, prefix_len=333, ps=16, suffix_range=(0, 40),
+                      suffix_lens=None if suffix else [0] * 70, dtype=FP8, pad="zero")
+    bf.k = (case.k.to(torch.float32) / 32).to(BF16)
+    bf.v = (case.v.to(torch.float32) / 32).to(BF16)
+    assert torch.equal(bf.k.to(torch.float32) * 32, case.k.to(torch.float32))
+    bf.k_descale = bf.v_descale = None
+    bf.dtype = BF16
+    ob, lb = run_cascade(bf, sp, ss)
+    assert torch.equal(o8, ob) and torch.equal(l8, lb)
+
+
+def test_fp8_cascade_equals_fp8_decode_over_concatenated_pages():
+    case = cascade_case(83, 4, 32, 8, 128, prefix_len=256, ps=16, suffix_lens=[5, 100, 16, 0], dtype=FP8,
+                        pad="nan")
+    out_c, lse_c = run_cascade(case, 2, 2)
+    n_pre = case.prefix_pages.numel()
+    table = torch.full((4, n_pre + case.page_table.shape[1]), -1, dtype=torch.int32)
+    for b in range(4):
+        table[b, :n_pre] = case.prefix_pages
+        table[b, n_pre:] = case.page_table[b]
+    d = to_dev(case)
+    out_p, lse_p = F.decode(d["q"], d["k"], d["v"], (case.seq_lens + 256).to("cuda"), page_table=table.cuda(),
+                            num_splits=4, k_descale=d["k_descale"], v_descale=d["v_descale"])
+    torch.cuda.synchronize()
+    assert (out_c - out_p).abs().max().item() < 3e-3
+    assert ((lse_c - lse_p).abs() / lse_p.abs().clamp(min=1)).max().item() < 1e-4
