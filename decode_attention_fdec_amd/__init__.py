@@ -41,6 +41,7 @@ class FdecKV(ctypes.Structure):
         ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int),
         ("k_descale", ctypes.c_void_p), ("v_descale", ctypes.c_void_p),
         ("cache_batch_idx", ctypes.c_void_p), ("cache_leftpad", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int),
     ]
 
 
@@ -99,6 +100,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_decode_multi_balanced.argtypes = [P, I, I, I, ctypes.POINTER(FdecKV), P, I, F, P, P, P, Z, P]
     lib.fdec_balanced_workspace_size.restype = Z
     lib.fdec_balanced_workspace_size.argtypes = [I, I, I, I, I]
+    lib.fdec_check_inputs.argtypes = [I, ctypes.POINTER(FdecKV), P, ctypes.POINTER(FdecAppend), P, I,
+                                      ctypes.POINTER(I), ctypes.POINTER(I), P]
+    lib.fdec_set_debug.restype = None
+    lib.fdec_set_debug.argtypes = [I]
+    lib.fdec_debug_enabled.argtypes = []
     if path is None:
         _lib = lib
     return lib
@@ -153,6 +159,7 @@ def make_kv(k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor]
     kv.dtype = _dtype_code(k.dtype)
     kv.num_kv_heads, kv.head_dim = k.shape[2], k.shape[3]
     kv.s_outer, kv.s_token, kv.s_head = k.stride(0), k.stride(1), k.stride(2)
+    kv.num_blocks = k.shape[0]  # pages of a pool / rows of a contiguous cache
     if page_table is None:
         kv.page_size, kv.capacity = 0, k.shape[1]
         kv.page_table, kv.max_pages_per_seq = None, 0
@@ -440,6 +447,32 @@ def trace_stop():
                                ctypes.byref(n)))
     m = max(0, min(n.value - 1, 8192, cap))
     return [float(ms[i]) for i in range(m)], [int(kinds[i]) for i in range(m)]
+
+
+CHECK_LENGTH, CHECK_PAGE, CHECK_LEFTPAD, CHECK_BATCH_IDX, CHECK_ROPE_POS, CHECK_PREFIX_PAGE = 1, 2, 4, 8, 16, 32
+
+
+def check_inputs(k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor, page_table: Optional[torch.Tensor] = None,
+                 append: Optional[FdecAppend] = None, prefix_pages: Optional[torch.Tensor] = None,
+                 prefix_len: int = 0, cache_batch_idx: Optional[torch.Tensor] = None,
+                 cache_leftpad: Optional[torch.Tensor] = None):
+    """fdec_check_inputs: (flags, first flagged request) of the device data a call would trust."""
+    kv = make_kv(k, v, page_table, cache_batch_idx=cache_batch_idx, cache_leftpad=cache_leftpad)
+    flags, first = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load_library().fdec_check_inputs(seq_lens.shape[0], ctypes.byref(kv), seq_lens.data_ptr(),
+                                            ctypes.byref(append) if append is not None else None,
+                                            _ptr(prefix_pages), prefix_len, ctypes.byref(flags),
+                                            ctypes.byref(first), _stream(k.device)))
+    return flags.value, first.value
+
+
+def set_debug(on: bool) -> None:
+    """fdec_set_debug: every decode call checks its device data first (and refuses bad data)."""
+    load_library().fdec_set_debug(int(bool(on)))
+
+
+def debug_enabled() -> bool:
+    return bool(load_library().fdec_debug_enabled())
 
 
 PROBE_STATIC, PROBE_TICKETS = 0, 1

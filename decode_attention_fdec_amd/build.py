@@ -29,7 +29,7 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-t
              "-munsafe-fp-atomics"]
 
 HIP_SOURCES = ["split_kv.hip", "split_kv_mfma.hip", "multitoken.hip", "merge.hip", "cascade.hip", "probe.hip",
-               "noalloc.hip"]
+               "noalloc.hip", "check.hip"]
 CPP_SOURCES = ["api.cpp", "plan.cpp"]
 
 

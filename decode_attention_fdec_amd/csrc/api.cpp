@@ -313,6 +313,7 @@ int fdec_decode_launch(const char *fn, const void *q, int B, int Hq, const fdec_
                        int S, float softmax_scale, const fdec_append *append, int fused, float *out, float *lse,
                        int *counters, char *states, void *stream) {
     if (B == 0) return FDEC_OK;
+    if (int rc = fdec_debug_gate(fn, B, kv, seq_lens, append, nullptr, 0, stream)) return rc;
     const WsLayout w = ws_layout(B, Hq, 1, kv->head_dim, S);
     const size_t base = counter_bytes(B, 1);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, S, softmax_scale, append);
@@ -396,6 +397,7 @@ extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const 
     p.po = reinterpret_cast<float *>(ws + w.po);
     p.s_total = S;
     p.s_offset = 0;
+    if ((rc = fdec_debug_gate(fn, B, kv, seq_lens, nullptr, nullptr, 0, stream))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     Launches run(st);
     if ((rc = run.done(mt16 ? fdec::launch_map_mt16(p, S, st) : fdec::launch_map(p, S, st),
@@ -426,6 +428,7 @@ extern "C" int fdec_decode_partials(const void *q, int B, int Hq, const fdec_kv 
     p.pd = part_d;
     p.s_total = num_splits;
     p.s_offset = 0;
+    if ((rc = fdec_debug_gate(fn, B, kv, seq_lens, append, nullptr, 0, stream))) return rc;
     Launches run(static_cast<hipStream_t>(stream));
     return run.done(fdec::launch_map(p, num_splits, static_cast<hipStream_t>(stream)), "fdec_decode_partials");
 }
@@ -521,6 +524,7 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     p.pd = reinterpret_cast<float *>(ws + w.pd);
     p.po = reinterpret_cast<float *>(ws + w.po);
     p.nslots = nb + B;
+    if ((rc = fdec_debug_gate(fn, B, kv, seq_lens, nullptr, nullptr, 0, stream))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     Launches run(st);
     if ((rc = run.done(mt16 ? fdec::launch_map_mt16_balanced(p, nb, st) : fdec::launch_map_mfma_g4_balanced(p, nb, st),
@@ -676,6 +680,7 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out must be 8-byte and lse 4-byte aligned", fn);
+    if ((rc = fdec_debug_gate(fn, B, kv, suffix_lens, nullptr, prefix_pages, prefix_len, stream))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     float scale = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)kv->head_dim) : softmax_scale;
     fdec::CascadeParams cp;

@@ -27,3 +27,9 @@ size_t fdec_decode_state_bytes(int B, int Hq, int D, int S);
 int fdec_decode_launch(const char *fn, const void *q, int B, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
                        int S, float softmax_scale, const fdec_append *append, int fused, float *out, float *lse,
                        int *counters, char *states, void *stream);
+
+// The debug mode (FDEC_DEBUG in the environment, or fdec_set_debug): checks the
+// call's device data with fdec_check_inputs and returns FDEC_ERR_INVALID_ARG,
+// before any launch, when some of it is out of range; FDEC_OK when the mode is off.
+int fdec_debug_gate(const char *fn, int B, const fdec_kv *kv, const int32_t *seq_lens, const fdec_append *append,
+                    const int32_t *prefix_pages, int prefix_len, void *stream);

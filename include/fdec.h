@@ -31,7 +31,9 @@
  *     with fdec_last_error() on the calling thread.
  *   - Device data is trusted: page ids, lengths and positions out of range are
  *     undefined behaviour (the kernels never read page-table entries past
- *     ceil(L_b / page_size), so -1 padding is safe).
+ *     ceil(L_b / page_size), so -1 padding is safe). The debug mode
+ *     (fdec_set_debug, or FDEC_DEBUG=1 in the environment) checks them first in
+ *     every decode call, which then waits for that check on its stream.
  *   - Lengths are never modified. With an append, the new token goes to row
  *     seq_lens[b] and attention covers seq_lens[b] + 1 tokens; the caller bumps
  *     the lengths afterwards ([cookbook] §3.2).
@@ -131,6 +133,10 @@ typedef struct fdec_kv {
      * (cache_leftpad[b] rounded down to a multiple of 16), whose rows above the
      * padding are masked. Not in fdec_cascade_decode. */
     const int32_t *cache_leftpad;
+    /* pages in a paged pool, or rows (the outer index) of a contiguous cache; 0 =
+     * not given. Read only by fdec_check_inputs and the debug mode, to bound
+     * page ids and cache_batch_idx. */
+    int num_blocks;
 } fdec_kv;
 
 /*
@@ -421,6 +427,45 @@ size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_dim, int spl
  */
 int fdec_trace_start(int max_events);
 int fdec_trace_stop(float *intervals_ms, int *kinds, int capacity, int *count_out);
+
+/*
+ * Device-data check ([vllm-arch] the backend's failure modes; [cookbook] §4.2 page
+ * tables padded with -1 past a request's pages). Reads, on `stream`, what a
+ * decode call with these arguments would trust: seq_lens[b] (plus one row with an
+ * append) within [0, capacity]; page-table entries covering those rows (never
+ * past max_pages_per_seq) in [0, num_blocks); cache_batch_idx[b] in
+ * [0, num_blocks) (contiguous caches); 0 <= cache_leftpad[b] <= seq_lens[b];
+ * with a rotary append, the position seq_lens[b] - cache_leftpad[b] below
+ * rope_max_pos; the ceil(prefix_len / page_size) prefix_pages in [0, num_blocks).
+ * Upper bounds on ids apply only when kv->num_blocks > 0. Writes the OR of the
+ * FDEC_CHECK_* flags of what is out of range to *flags_out (0: nothing) and the
+ * smallest request flagged (B for the prefix, -1 for none) to *first_out (may be
+ * NULL). Waits for the check (hipStreamSynchronize): not for graph capture. The
+ * check uses one device word per GPU, guarded by a host lock. FDEC_ERR_INVALID_ARG
+ * for NULL or malformed arguments, FDEC_ERR_HIP if a HIP call fails.
+ */
+enum {
+    FDEC_CHECK_LENGTH = 1,       /* seq_lens[b] < 0, or its rows past the capacity */
+    FDEC_CHECK_PAGE = 2,         /* a page id the request's rows cover is < 0 or >= num_blocks */
+    FDEC_CHECK_LEFTPAD = 4,      /* cache_leftpad[b] < 0 or > seq_lens[b] */
+    FDEC_CHECK_BATCH_IDX = 8,    /* cache_batch_idx[b] < 0 or >= num_blocks */
+    FDEC_CHECK_ROPE_POS = 16,    /* the appended row's rotary position outside the tables */
+    FDEC_CHECK_PREFIX_PAGE = 32  /* a shared-prefix page id < 0 or >= num_blocks */
+};
+int fdec_check_inputs(int B, const fdec_kv *kv, const int32_t *seq_lens, const fdec_append *append,
+                      const int32_t *prefix_pages, int prefix_len, int *flags_out, int *first_out, void *stream);
+
+/*
+ * The debug mode: with it on, fdec_decode, fdec_decode_noalloc,
+ * fdec_decode_partials, fdec_decode_balanced, fdec_decode_multi,
+ * fdec_decode_multi_balanced and fdec_cascade_decode run fdec_check_inputs on
+ * their own arguments before any launch and return FDEC_ERR_INVALID_ARG (message
+ * in fdec_last_error()) without launching when a flag is set. Off by default;
+ * FDEC_DEBUG set to anything but "0" in the environment turns it on at the
+ * first call; fdec_set_debug overrides it (process-wide).
+ */
+void fdec_set_debug(int on);
+int fdec_debug_enabled(void);
 
 #ifdef __cplusplus
 }

@@ -151,8 +151,7 @@ def one_case(rng, i):
                 app.rope_sin = buf(4096 * app.rotary_dim // 2 * 4, "sin")
         rc = lib.fdec_decode(qb, B, Hq, ctypes.byref(kv), lens, S, 0.0, ctypes.byref(app) if app else None,
                              int(kind == "fused"), out, lse, ws, n, None)
-        ok = (OK,) if not (app and dtype == 2) else (UNSUPPORTED,)
-        check(rc, ok, what)
+        check(rc, (OK,), what)
         if B > 0 and rc == OK:  # one byte less of workspace is refused
             check(lib.fdec_decode(qb, B, Hq, ctypes.byref(kv), lens, S, 0.0, ctypes.byref(app) if app else None,
                                   int(kind == "fused"), out, lse, ws, n - 1, None), (WORKSPACE,), what + " (short)")
@@ -202,7 +201,7 @@ def one_case(rng, i):
         rc = lib.fdec_cascade_decode(qb, B, Hq, ctypes.byref(kv), pages, prefix_len, lens, sp, ss, 0.0, out, lse, ws,
                                      n, None)
         check(rc, (OK, UNSUPPORTED, INVALID), what + f" prefix={prefix_len} sp={sp} ss={ss}")
-        if D == 128 and dtype != 2 and not kv.cache_leftpad and rc != OK:
+        if D == 128 and not kv.cache_leftpad and rc != OK:
             msg = lib.fdec_last_error().decode()
             if "too many pages" not in msg and "too many splits" not in msg:
                 raise SystemExit(f"{what}: cascade refused: {msg}")

@@ -13,6 +13,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "../../decode_attention_fdec_amd/csrc/fdec_host.h"
 #include "../../decode_attention_fdec_amd/csrc/fdec_internal.h"
 
 namespace {
@@ -215,6 +216,11 @@ hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t
     note("cascade_prefix");
     const char *w = "launch_cascade_prefix";
     inside(w, p.q, (size_t)p.B * p.Hq * 128 * 2);
+    if (p.kv_fp8) {  // float8 pools: bf16 queries, descales [B, Hkv] when given
+        if (p.dtype != 1) fail(w, "float8 pool without bf16 queries");
+        if (p.k_descale) inside(w, p.k_descale, (size_t)p.B * p.Hkv * 4);
+        if (p.v_descale) inside(w, p.v_descale, (size_t)p.B * p.Hkv * 4);
+    }
     if (p.prefix_len > 0) inside(w, p.prefix_pages, (size_t)((p.prefix_len + p.page_size - 1) / p.page_size) * 4);
     if (p.s_offset < 0 || p.s_offset + splits > p.s_total) fail(w, "prefix slots past s_total");
     if ((int64_t)splits * p.chunk < p.prefix_len) fail(w, "prefix splits do not cover the prefix");
@@ -281,3 +287,9 @@ hipError_t launch_zero_words(void *p, size_t n, hipStream_t) {
 }
 
 }  // namespace fdec
+
+// The debug mode's device-data check runs on the GPU (check.hip): off here.
+int fdec_debug_gate(const char *, int, const fdec_kv *, const int32_t *, const fdec_append *, const int32_t *, int,
+                    void *) {
+    return 0;
+}

@@ -313,3 +313,28 @@ def test_trace_arguments_and_an_empty_trace(fdec):
     assert call_decode(kv_struct(num_kv_heads=5)) == F.FDEC_ERR_INVALID_ARG
     assert lib.fdec_trace_stop(None, None, 0, ctypes.byref(n)) == F.FDEC_OK
     assert n.value == 0
+
+
+def test_check_inputs_validation_and_debug_switch(fdec):
+    lib = F.load_library()
+    flags, first = ctypes.c_int(0), ctypes.c_int(0)
+    kv = kv_struct()
+    # malformed arguments are refused before any HIP call
+    assert lib.fdec_check_inputs(1, ctypes.byref(kv), FAKE, None, None, 0, None, None, None) == F.FDEC_ERR_INVALID_ARG
+    assert lib.fdec_check_inputs(-1, ctypes.byref(kv), FAKE, None, None, 0, ctypes.byref(flags), None,
+                                 None) == F.FDEC_ERR_INVALID_ARG
+    assert lib.fdec_check_inputs(1, ctypes.byref(kv), None, None, None, 0, ctypes.byref(flags), None,
+                                 None) == F.FDEC_ERR_INVALID_ARG
+    # a prefix needs a paged pool
+    assert lib.fdec_check_inputs(1, ctypes.byref(kv), FAKE, None, FAKE, 16, ctypes.byref(flags), ctypes.byref(first),
+                                 None) == F.FDEC_ERR_INVALID_ARG
+    assert "prefix" in last_error()
+    assert lib.fdec_check_inputs(1, ctypes.byref(kv_struct(num_blocks=-2)), FAKE, None, None, 0,
+                                 ctypes.byref(flags), None, None) == F.FDEC_ERR_INVALID_ARG
+    # the debug switch is process-wide and needs no GPU
+    was = lib.fdec_debug_enabled()
+    lib.fdec_set_debug(1)
+    assert lib.fdec_debug_enabled() == 1
+    lib.fdec_set_debug(0)
+    assert lib.fdec_debug_enabled() == 0
+    lib.fdec_set_debug(was)
