@@ -94,7 +94,8 @@ class Runner:
         self.cascade = case.prefix_pages is not None
         if self.cascade:
             self.prefix_pages = case.prefix_pages.to(dev)
-            sp, ss = F.cascade_plan(B, Hq, case.Hkv, case.prefix_len, case.capacity, case.page_size)
+            sp, ss = F.cascade_plan(B, Hq, case.Hkv, case.prefix_len, case.capacity, case.page_size,
+                                    kv_dtype=case.dtype)
             self.S = (sp, ss)
             self.out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
             self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)

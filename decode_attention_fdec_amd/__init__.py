@@ -93,6 +93,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fdec_trace_stop.argtypes = [P, P, I, ctypes.POINTER(I)]
     lib.fdec_probe_stream.argtypes = [P, Z, P, I, I, P]
     lib.fdec_cascade_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.fdec_cascade_plan_kv.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.fdec_cascade_workspace_size.restype = Z
     lib.fdec_cascade_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.fdec_decode_balanced.argtypes = [P, I, I, ctypes.POINTER(FdecKV), P, I, F, P, P, P, Z, P]
@@ -500,11 +501,18 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
 
 
 def cascade_plan(B: int, Hq: int, Hkv: int, prefix_len: int, capacity: int, page_size: int,
-                 cu_count: int = 256):
-    """fdec_cascade_plan: (splits_prefix, splits_suffix)."""
+                 cu_count: int = 256, kv_dtype=None):
+    """fdec_cascade_plan, or fdec_cascade_plan_kv when kv_dtype (a torch dtype or an fdec_dtype
+    code) is given: (splits_prefix, splits_suffix)."""
     sp, ss = ctypes.c_int(0), ctypes.c_int(0)
-    _check(load_library().fdec_cascade_plan(B, Hq, Hkv, prefix_len, capacity, page_size, cu_count,
-                                            ctypes.byref(sp), ctypes.byref(ss)))
+    lib = load_library()
+    if kv_dtype is None:
+        _check(lib.fdec_cascade_plan(B, Hq, Hkv, prefix_len, capacity, page_size, cu_count, ctypes.byref(sp),
+                                     ctypes.byref(ss)))
+    else:
+        code = kv_dtype if isinstance(kv_dtype, int) else _dtype_code(kv_dtype)
+        _check(lib.fdec_cascade_plan_kv(B, Hq, Hkv, prefix_len, capacity, page_size, code, cu_count,
+                                        ctypes.byref(sp), ctypes.byref(ss)))
     return sp.value, ss.value
 
 
@@ -524,7 +532,7 @@ def cascade_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table
     if lse is None:
         lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
     if splits_prefix <= 0 or splits_suffix <= 0:
-        sp, ss = cascade_plan(B, Hq, kv.num_kv_heads, prefix_len, kv.capacity, kv.page_size)
+        sp, ss = cascade_plan(B, Hq, kv.num_kv_heads, prefix_len, kv.capacity, kv.page_size, kv_dtype=k.dtype)
         splits_prefix = splits_prefix if splits_prefix > 0 else sp
         splits_suffix = splits_suffix if splits_suffix > 0 else ss
     if workspace is None:

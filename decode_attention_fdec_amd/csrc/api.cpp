@@ -604,10 +604,18 @@ extern "C" size_t fdec_cascade_workspace_size(int B, int Hq, int Hkv, int head_d
 
 extern "C" int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size,
                                  int cu_count, int *splits_prefix_out, int *splits_suffix_out) {
+    return fdec_cascade_plan_kv(B, Hq, Hkv, prefix_len, capacity, page_size, FDEC_BF16, cu_count, splits_prefix_out,
+                                splits_suffix_out);
+}
+
+extern "C" int fdec_cascade_plan_kv(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size,
+                                    int kv_dtype, int cu_count, int *splits_prefix_out, int *splits_suffix_out) {
     fdec_clear_error();
     const char *fn = "fdec_cascade_plan";
     if (!splits_prefix_out || !splits_suffix_out)
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: output pointers must be non-NULL", fn);
+    if (kv_dtype != FDEC_F16 && kv_dtype != FDEC_BF16 && kv_dtype != FDEC_FP8_E4M3)
+        return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: kv_dtype %d is not an fdec_dtype", fn, kv_dtype);
     if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || prefix_len < 0 || capacity < 1 || page_size < 16 ||
         page_size % 16)
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: bad sizes", fn);
@@ -632,9 +640,11 @@ extern "C" int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int cap
                 hpb = w;
                 break;
             }
-        ss = std::max(1, cu_count / (Hkv / hpb));
+        // float8 pools: two blocks per compute unit (half the bytes per tile, so more
+        // tiles in flight per compute unit), as far as the merge's 256 states allow
+        ss = std::max(1, cu_count / (Hkv / hpb)) * (kv_dtype == FDEC_FP8_E4M3 ? 2 : 1);
     } else {
-        int rc = fdec_plan(B, Hq, Hkv, nullptr, capacity, page_size, cu_count, &ss);
+        int rc = fdec_plan_kv(B, Hq, Hkv, nullptr, capacity, page_size, kv_dtype, cu_count, &ss);
         if (rc) return rc;
     }
     ss = std::max(1, std::min(ss, FDEC_MAX_SPLITS - sp));
@@ -666,7 +676,8 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
     int sp = splits_prefix, ss = splits_suffix;
     if (sp == 0 || ss == 0) {
         int psp = 1, pss = 1;
-        if ((rc = fdec_cascade_plan(B, Hq, kv->num_kv_heads, prefix_len, cap, kv->page_size, 256, &psp, &pss)))
+        if ((rc = fdec_cascade_plan_kv(B, Hq, kv->num_kv_heads, prefix_len, cap, kv->page_size, kv->dtype, 256, &psp,
+                                       &pss)))
             return rc;
         if (sp == 0) sp = psp;
         if (ss == 0) ss = pss;

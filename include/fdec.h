@@ -402,8 +402,15 @@ int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv,
  * block count per group of KV heads (one block per compute unit over all
  * groups), else fdec_plan's split count over the suffix page table's
  * capacity. prefix_len >= 0; capacity = max_pages_per_seq * page_size of the
- * suffix table.
+ * suffix table. fdec_cascade_plan_kv plans for a pool of element type kv_dtype
+ * (an fdec_dtype; fdec_cascade_plan is it with a 16-bit pool): a float8 pool
+ * with G = 4 takes two suffix blocks per compute unit (measured on MI355X: the
+ * 64-request shared-prefix workload's suffix 43.6 -> 32.7 us) within
+ * splits_prefix + splits_suffix <= FDEC_MAX_SPLITS, and fdec_plan_kv's count
+ * otherwise.
  */
+int fdec_cascade_plan_kv(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size, int kv_dtype,
+                         int cu_count, int *splits_prefix_out, int *splits_suffix_out);
 int fdec_cascade_plan(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size, int cu_count,
                       int *splits_prefix_out, int *splits_suffix_out);
 

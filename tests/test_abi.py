@@ -188,6 +188,24 @@ def test_cascade_validation(fdec):
                                    small, None) == F.FDEC_ERR_WORKSPACE
 
 
+def test_cascade_plan_for_float8_pools(fdec):
+    import torch
+
+    # G = 4: the balanced suffix takes two blocks per compute unit for float8 pools,
+    # within the 256 states a merge holds; 16-bit pools and other G as before
+    assert F.cascade_plan(64, 32, 8, 16384, 2048, 64, kv_dtype=torch.bfloat16) == F.cascade_plan(64, 32, 8, 16384,
+                                                                                                  2048, 64)
+    sp, ss = F.cascade_plan(64, 32, 8, 16384, 2048, 64, kv_dtype=torch.float8_e4m3fn)
+    sp16, ss16 = F.cascade_plan(64, 32, 8, 16384, 2048, 64)
+    assert sp == sp16 and ss == min(2 * ss16, F.MAX_SPLITS - sp)
+    assert F.cascade_plan(4, 8, 4, 500, 512, 16, kv_dtype=torch.float8_e4m3fn)[1] == \
+        F.plan(4, 8, 4, None, 512, 16, kv_dtype=torch.float8_e4m3fn)
+    lib = F.load_library()
+    a, b = ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.fdec_cascade_plan_kv(4, 8, 4, 500, 512, 16, 9, 256, ctypes.byref(a), ctypes.byref(b)) == \
+        F.FDEC_ERR_INVALID_ARG
+
+
 def test_cascade_plan(fdec):
     sp, ss = F.cascade_plan(64, 32, 8, 16384, 2048, 64)
     assert 8 * sp >= 256 and 1 <= ss and sp + ss <= F.MAX_SPLITS
