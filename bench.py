@@ -8,7 +8,12 @@ or the single fused kernel; with append or cascade workloads those parts
 too). Inputs are resident in HBM before timing starts. To keep the 256 MB
 last-level cache (MALL) from serving repeated reads, steps rotate through
 enough copies of the KV cache to cover >= 1 GiB; the single-copy ("warm")
-figure is reported separately.
+figure is reported separately. The K timed steps are captured as one HIP graph
+and replayed between two events (the median of three replays) (how a serving loop launches decode
+steps: a graph launch costs ~5 µs once, its kernels then dispatch back to back);
+the same K steps launched eagerly are timed too (`eager_us_per_step`, the median
+of three regions), and
+`--launch eager` makes those the headline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -167,6 +172,39 @@ def time_region(runner: Runner, steps: int, warmup: int, copy=None):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps  # ms
+
+
+def time_region_graph(runner: Runner, steps: int, warmup: int):
+    """Whole-region time of `steps` steps captured as one HIP graph (on a side stream)
+    and replayed between events on the launch stream: one untimed replay, then the
+    median of three timed ones.
+    The steps rotate KV copies as eager steps do, so the graph holds `steps`
+    distinct steps."""
+    import torch
+
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(steps):
+                runner.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / steps)
+    return sorted(times)[1]  # ms, the median of three replays
 
 
 def time_per_launch(runner: Runner, steps: int, copy=None):
@@ -440,14 +478,20 @@ def cpu_baseline(case, budget_s: float):
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
-def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: int, dev):
+def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: int, dev, launch: str = "graph"):
     import synth
 
     t0 = time.time()
     case = synth.workload(name)
     runner = Runner(F, case, mode, splits, 1 << 30, dev)
     log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s, copies={runner.copies}, S={runner.S}")
-    ms = time_region(runner, steps, warmup)
+    eager = sorted([time_region(runner, steps, warmup)] + [time_region(runner, steps, 0) for _ in range(2)])[1]
+    ms, how = eager, "eager"
+    if launch == "graph":
+        try:
+            ms, how = time_region_graph(runner, steps, 2), "hip_graph"
+        except Exception as e:  # keep the eager figure if this runtime cannot capture
+            how = f"eager (graph capture failed: {type(e).__name__})"
     per = time_per_launch(runner, steps)
     warm = time_region(runner, steps, 2, copy=0)
     stages = time_stages(F, runner, steps)
@@ -455,6 +499,7 @@ def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: i
     res = {"us_per_step": round(ms * 1e3, 2), "kv_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "pct_of_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
            "step_us_p10_p50_p90": [round(pct(per, p) * 1e3, 2) for p in (10, 50, 90)],
+           "launch": how, "eager_us_per_step": round(eager * 1e3, 2),
            "warm_us_per_step": round(warm * 1e3, 2), "num_splits": runner.S, "mode": mode,
            "kv_copies_rotated": runner.copies, "kernel_us": stages,
            "roofline": roofline_entry(case, stages, runner)}
@@ -472,6 +517,8 @@ def main() -> int:
     ap.add_argument("--workload", default="c2",
                     choices=["c1", "c2", "c3", "c4", "c5", "c2f8", "c3f8", "c2g8", "c1f8", "c2g2f8", "c5f8"])
     ap.add_argument("--mode", default="two", choices=["fused", "two", "bal"])
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="time the K steps as one captured HIP graph replay (default) or as eager launches")
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
     ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8,c2g2f8,c5f8",
                     help="other workloads timed for context ('' = none)")
@@ -509,7 +556,7 @@ def main() -> int:
     dev = torch.device("cuda:0")
 
     case, runner, res, per = measure_workload(F, args.workload, args.mode, args.splits, args.steps,
-                                              args.warmup, dev)
+                                              args.warmup, dev, args.launch)
     # the dominant kernel: the split-KV map kernel of the step (the suffix map of a
     # cascade), timed with the library's stage-timing events on its stream
     rl = res["roofline"]["suffix"] if runner.cascade else res["roofline"]
@@ -552,7 +599,7 @@ def main() -> int:
             runs.append((name, name, args.mode))
     for key, name, mode in runs:
         try:
-            _, r2, res2, _ = measure_workload(F, name, mode, 0, args.steps, args.warmup, dev)
+            _, r2, res2, _ = measure_workload(F, name, mode, 0, args.steps, args.warmup, dev, args.launch)
             others[key] = res2
             del r2
         except F.FdecError as e:  # a workload whose path is not built yet
