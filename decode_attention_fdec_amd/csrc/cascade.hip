@@ -75,11 +75,17 @@ template <> __device__ __forceinline__ uint32_t pfx_pack2<1>(float a, float b) {
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
 }
-constexpr int kPfxNS = 3;                  // ring slots (two tiles in flight)
+constexpr int kPfxNS = 3;                  // ring slots (two tiles in flight; four measured no faster)
 typedef short pfx_s16x4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) pfx_s16x4_v pfx_lds_s16x4;
 typedef int pfx_i32x2_v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) pfx_i32x2_v pfx_lds_i32x2;
+typedef __attribute__((address_space(3))) const uint8_t pfx_lds_u8;
+typedef unsigned int pfx_u32x2_v __attribute__((ext_vector_type(2)));
+typedef unsigned int pfx_u32x4_v __attribute__((ext_vector_type(4)));
+// An LDS pointer from an LDS byte address (reads through it are ds_* instructions
+// on that address, with constant offsets folded into the instruction).
+__device__ __forceinline__ pfx_lds_u8 *pfx_lds(uint32_t a) { return (pfx_lds_u8 *)(size_t)a; }
 
 // Float8 tiles: the 16-byte slot of piece p in row r is p ^ pfx_swz8(r). A K read
 // (16 rows 16kb .. 16kb + 15, one piece) and a V transpose read (rows 4kq + 0..3
@@ -141,6 +147,34 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         vsc[rb] = KF && p.v_descale ? p.v_descale[i] : 1.0f;
     }
 
+    // Lane-constant parts of the LDS read addresses: the piece swizzles depend only
+    // on the lane, the ring slot and the key block enter as uniform offsets.
+    //  K (A of S^T): row 16kb + li, the 8 (16-bit: 16 bytes) or 8 float8 (8 bytes)
+    //  elements at d = 32ks + 8kq. 16-bit: piece 4ks + kq in slot (4ks + kq) ^ li;
+    //  float8: half kq & 1 of piece 2ks + kq / 2 in slot piece ^ pfx_swz8(16kb + li)
+    //  = piece ^ (li / 2) ^ 4 (kb & 1), i.e. koff[ks] ^ 64 for odd kb.
+    //  V (B of P V): 16-bit, row 32kk + ra0 (+16), ra0 = 4kq + li / 4 < 16, piece
+    //  2db + p0 in slot (2db + p0) ^ ra0 = 2 (db ^ ra0 / 2) + (p0 ^ (ra0 & 1));
+    //  float8, row 32kk + rv0, rv0 the (li / 2)-th of the lane group's 8 keys,
+    //  piece db in slot db ^ pfx_swz8(rv0) (32kk leaves the swizzle unchanged).
+    uint32_t koff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        koff[ks] = KF ? (uint32_t)(li * 128 + 16 * ((2 * ks + (kq >> 1)) ^ (li >> 1)) + 8 * (kq & 1))
+                      : (uint32_t)(li * 256 + 16 * ((4 * ks + kq) ^ li));
+    uint32_t vlane, vsw;
+    if constexpr (KF == 1) {
+        const int k8 = li >> 1;
+        const int rv0 = k8 < 4 ? 4 * kq + k8 : 16 + 4 * kq + (k8 - 4);
+        vlane = (uint32_t)(rv0 * 128 + 8 * (li & 1));
+        vsw = (uint32_t)pfx_swz8(rv0);
+    } else {
+        const int ra0 = 4 * kq + (li >> 2);
+        const int p0 = (li & 3) >> 1;
+        vlane = (uint32_t)(ra0 * 256 + 16 * (p0 ^ (ra0 & 1)) + 8 * (li & 1));
+        vsw = (uint32_t)(ra0 >> 1);
+    }
+
     // DMA of tile `tile` into ring slot tile % kPfxNS: this wave's rows 8w .. 8w + 7
     // of K and of V, four rows (16-bit) or all eight (float8) per instruction
     // (one page: pages hold multiples of 16 keys); rows past the split's end
@@ -195,8 +229,11 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         __syncthreads();
         if (tile + kPfxNS - 1 < ntiles) issue(tile + kPfxNS - 1);
         const int t0 = t_begin + tile * kPfxKeys;
-        const uint8_t *K = kring[tile % kPfxNS];
-        const uint8_t *V = vring[tile % kPfxNS];
+        // the slot's LDS bases as scalars (one value per wave), so each read adds
+        // only its lane-constant offset
+        const uint32_t slot_off = (uint32_t)(tile % kPfxNS) * (uint32_t)(kPfxKeys * RB);
+        pfx_lds_u8 *K = pfx_lds(__builtin_amdgcn_readfirstlane(lds_addr(kring[0]) + slot_off));
+        pfx_lds_u8 *V = pfx_lds(__builtin_amdgcn_readfirstlane(lds_addr(vring[0]) + slot_off));
 
         // ---- S^T = K Q^T: s[kb][rb] holds keys 16kb + 4kq + r of row 16rb + li
         f32x4_v s[4][kRB];
@@ -206,44 +243,56 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
             for (int rb = 0; rb < kRB; ++rb) s[kb][rb] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int kr = 16 * kb + li;
                 uint4 a;
-                if constexpr (KF == 1) {  // d = 32ks + 8kq .. + 7: half kq & 1 of piece 2ks + kq / 2
-                    const uint2 k8 = *reinterpret_cast<const uint2 *>(
-                        K + kr * 128 + 16 * ((2 * ks + (kq >> 1)) ^ pfx_swz8(kr)) + 8 * (kq & 1));
+                if constexpr (KF == 1) {
+                    const pfx_u32x2_v k8 = *(const __attribute__((address_space(3))) pfx_u32x2_v *)(
+                        K + 2048 * kb + (koff[ks] ^ (64u * (uint32_t)(kb & 1))));
                     const uint2 lo = fp8x4_to_bf16(k8.x), hi = fp8x4_to_bf16(k8.y);
                     a = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 } else {
-                    a = *reinterpret_cast<const uint4 *>(K + kr * 256 + 16 * ((4 * ks + kq) ^ (kr & 15)));
+                    const pfx_u32x4_v k16 =
+                        *(const __attribute__((address_space(3))) pfx_u32x4_v *)(K + 4096 * kb + koff[ks]);
+                    a = make_uint4(k16.x, k16.y, k16.z, k16.w);
                 }
 #pragma unroll
                 for (int rb = 0; rb < kRB; ++rb) s[kb][rb] = Mfma<DT>::run(a, qb[rb][ks], s[kb][rb]);
             }
         }
 
-        // ---- online softmax per query row
+        // ---- online softmax per query row (only a split's last tile can hold keys
+        // past its end)
         const int nvalid = t_end - t0;
         bool move = false;
         float mx[kRB];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[kb][rb][r] *= ksc[rb];
+        if (__builtin_expect(nvalid < kPfxKeys, 0)) {
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * kb + 4 * kq + r >= nvalid) s[kb][rb][r] = kNegInf;
+        }
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
             float x = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = s[kb][rb][r] * ksc[rb];
-                    if (16 * kb + 4 * kq + r >= nvalid) v = kNegInf;
-                    s[kb][rb][r] = v;
-                    x = fmaxf(x, v);
-                }
+                for (int r = 0; r < 4; ++r) x = fmaxf(x, s[kb][rb][r]);
             x = fmaxf(x, shfl_xor(x, 16));
             x = fmaxf(x, shfl_xor(x, 32));
             mx[rb] = x;
             tmax[rb] = fmaxf(tmax[rb], x);
             move |= x > m[rb] + kTau;
         }
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
             // move the reference; O rows live in lanes by (kq, r), so the
             // per-row factors go through LDS
 #pragma unroll
@@ -302,12 +351,10 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             if constexpr (KF == 1) {
-                const int k8 = li >> 1;
-                const int rv = 32 * kk + (k8 < 4 ? 4 * kq + k8 : 16 + 4 * kq + (k8 - 4));
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
                     const pfx_i32x2_v x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (pfx_lds_i32x2 *)(V + rv * 128 + 16 * (db ^ pfx_swz8(rv)) + 8 * (li & 1)));
+                        (pfx_lds_i32x2 *)(V + 4096 * kk + vlane + 16u * ((uint32_t)db ^ vsw)));
                     const uint2 v0 = fp8x4_to_bf16((uint32_t)x[0]), v1 = fp8x4_to_bf16((uint32_t)x[1]);
                     const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
@@ -316,12 +363,9 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
             } else {
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
-                    const int ra = 32 * kk + 4 * kq + (li >> 2), rb2 = ra + 16;
-                    const int piece = 2 * db + ((li & 3) >> 1), half = 8 * (li & 1);
-                    const pfx_s16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (pfx_lds_s16x4 *)(V + ra * 256 + 16 * (piece ^ (ra & 15)) + half));
-                    const pfx_s16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (pfx_lds_s16x4 *)(V + rb2 * 256 + 16 * (piece ^ (rb2 & 15)) + half));
+                    pfx_lds_u8 *va = V + 8192 * kk + vlane + 32u * ((uint32_t)db ^ vsw);
+                    const pfx_s16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pfx_lds_s16x4 *)va);
+                    const pfx_s16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pfx_lds_s16x4 *)(va + 4096));
                     const uint2 v0 = __builtin_bit_cast(uint2, x0), v1 = __builtin_bit_cast(uint2, x1);
                     const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
