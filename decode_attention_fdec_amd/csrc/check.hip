@@ -72,11 +72,14 @@ __global__ void check_inputs_kernel(const CheckParams c, int *w) {
         }
         if (c.batch_idx && bad_block(c.batch_idx[b], c.num_blocks)) f |= FDEC_CHECK_BATCH_IDX;
         if (c.page_table) {
-            // only the entries the request's rows cover, and never past its table row
+            // only the entries the kernels read: from the page holding the 16-row
+            // tile of the first valid row (left padding below it is never read) to
+            // the page of the last row, and never past the request's table row
             const int64_t need = rows > 0 ? (rows + c.page_size - 1) / c.page_size : 0;
             const int n = (int)(need < c.max_pages ? need : c.max_pages);
+            const int j0 = (lp > 0 && lp <= L) ? (lp & ~15) / c.page_size : 0;
             const int32_t *row = c.page_table + (int64_t)b * c.max_pages;
-            for (int j = 0; j < n; ++j)
+            for (int j = j0; j < n; ++j)
                 if (bad_block(row[j], c.num_blocks)) f |= FDEC_CHECK_PAGE;
         }
         if (c.rope_max_pos > 0 && L >= 0 && (L - lp < 0 || L - lp >= c.rope_max_pos)) f |= FDEC_CHECK_ROPE_POS;

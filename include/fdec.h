@@ -444,7 +444,9 @@ int fdec_trace_stop(float *intervals_ms, int *kinds, int capacity, int *count_ou
  * [0, num_blocks) (contiguous caches); 0 <= cache_leftpad[b] <= seq_lens[b];
  * with a rotary append, the position seq_lens[b] - cache_leftpad[b] below
  * rope_max_pos; the ceil(prefix_len / page_size) prefix_pages in [0, num_blocks).
- * Upper bounds on ids apply only when kv->num_blocks > 0. Writes the OR of the
+ * Page entries below the one holding the 16-row tile of cache_leftpad[b] are
+ * not read (the kernels never read them). Upper bounds on ids apply only when
+ * kv->num_blocks > 0. Writes the OR of the
  * FDEC_CHECK_* flags of what is out of range to *flags_out (0: nothing) and the
  * smallest request flagged (B for the prefix, -1 for none) to *first_out (may be
  * NULL). Waits for the check (hipStreamSynchronize): not for graph capture. The

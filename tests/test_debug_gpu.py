@@ -80,6 +80,19 @@ def test_lengths_leftpad_rows_and_positions_are_flagged():
     assert F.check_inputs(da["k"], da["v"], da["seq_lens"], append=short) == (F.CHECK_ROPE_POS, 0)
 
 
+def test_pages_below_the_left_padding_are_not_read():
+    # request 2 (length 500, 32 pages) with 100 rows of left padding: its first tile
+    # starts at row 96, on page 6; pages 0..5 are never read and may hold -1
+    case = _paged()
+    d = to_dev(case)
+    table = d["page_table"].clone()
+    table[2, :6] = -1
+    lp = torch.tensor([0, 0, 100, 0], dtype=torch.int32, device="cuda")
+    assert F.check_inputs(d["k"], d["v"], d["seq_lens"], page_table=table, cache_leftpad=lp) == (0, -1)
+    table[2, 6] = -1  # the page holding row 96 is read
+    assert F.check_inputs(d["k"], d["v"], d["seq_lens"], page_table=table, cache_leftpad=lp) == (F.CHECK_PAGE, 2)
+
+
 def test_prefix_pages_are_flagged():
     case = cascade_case(205, 3, 16, 4, 128, prefix_len=100, ps=16, suffix_lens=[0, 5, 40], dtype=BF16,
                         pad="nan")
