@@ -286,8 +286,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x = fmaxf(x, s[kb][rb][r]);
-            x = fmaxf(x, shfl_xor(x, 16));
-            x = fmaxf(x, shfl_xor(x, 32));
+            x = across_rows(x, MaxOp{});  // lanes L, L ^ 16, L ^ 32, L ^ 48: the row's 64 keys
             mx[rb] = x;
             tmax[rb] = fmaxf(tmax[rb], x);
             move |= x > m[rb] + kTau;
@@ -380,8 +379,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
         float lt = l[rb];
-        lt += shfl_xor(lt, 16);
-        lt += shfl_xor(lt, 32);
+        lt = across_rows(lt, AddOp{});
         const float T = tmax[rb];
         const float f = (T == kNegInf) ? 0.0f : fexp2(m[rb] - T);
         if (kq == 0) {
