@@ -532,9 +532,12 @@ def cascade_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table
     if lse is None:
         lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
     if splits_prefix <= 0 or splits_suffix <= 0:
+        # as fdec_cascade_decode plans: a planned count fits beside a count the caller gave
         sp, ss = cascade_plan(B, Hq, kv.num_kv_heads, prefix_len, kv.capacity, kv.page_size, kv_dtype=k.dtype)
-        splits_prefix = splits_prefix if splits_prefix > 0 else sp
-        splits_suffix = splits_suffix if splits_suffix > 0 else ss
+        if splits_prefix <= 0:
+            splits_prefix = max(1, min(sp, MAX_SPLITS - splits_suffix)) if splits_suffix > 0 else sp
+        if splits_suffix <= 0:
+            splits_suffix = max(1, min(ss, MAX_SPLITS - splits_prefix))
     if workspace is None:
         workspace = Workspace(cascade_workspace_size(B, Hq, kv.num_kv_heads, D, splits_prefix, splits_suffix),
                               q.device)

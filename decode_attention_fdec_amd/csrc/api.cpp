@@ -679,8 +679,9 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
         if ((rc = fdec_cascade_plan_kv(B, Hq, kv->num_kv_heads, prefix_len, cap, kv->page_size, kv->dtype, 256, &psp,
                                        &pss)))
             return rc;
-        if (sp == 0) sp = psp;
-        if (ss == 0) ss = pss;
+        // a planned count fits beside a count the caller gave
+        if (sp == 0) sp = ss ? std::max(1, std::min(psp, FDEC_MAX_SPLITS - ss)) : psp;
+        if (ss == 0) ss = std::max(1, std::min(pss, FDEC_MAX_SPLITS - sp));
         if (sp + ss > FDEC_MAX_SPLITS) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: too many splits", fn);
     }
     const int64_t chunk_p = cascade_chunk(prefix_len, sp);

@@ -382,7 +382,8 @@ int fdec_decode_multi_balanced(const void *q, int B, int q_len, int Hq, const fd
  * head), the suffixes by the split-KV kernel, and one merge combines both:
  * the result equals fdec_decode over the concatenated [prefix; suffix]
  * sequence. kv must be paged, head_dim 128. splits_prefix / splits_suffix >= 1
- * (0 = fdec_cascade_plan's choice); the prefix is cut into chunks of
+ * (0 = fdec_cascade_plan_kv's choice for the pool's type, a planned count
+ * reduced to fit beside a count the caller gave); the prefix is cut into chunks of
  * 64 * ceil(ceil(prefix_len / splits_prefix) / 64) tokens, each of at most 1022
  * pages. With G = Hq/Hkv = 4 the suffixes run on the balanced split (as
  * fdec_decode_balanced) and splits_suffix is its block count per group of KV

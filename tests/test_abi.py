@@ -356,3 +356,18 @@ def test_check_inputs_validation_and_debug_switch(fdec):
     lib.fdec_set_debug(0)
     assert lib.fdec_debug_enabled() == 0
     lib.fdec_set_debug(was)
+
+
+def test_cascade_plans_one_count_beside_the_other(fdec):
+    # a planned suffix count fits beside an explicit prefix count (and the other
+    # way round): the planner alone would give 1 + 255 here
+    lib = F.load_library()
+    kvp = kv_struct(page_size=16, page_table=FAKE, max_pages_per_seq=4, capacity=0, num_kv_heads=4)
+    sp, ss = F.cascade_plan(40, 16, 4, 15, 64, 16)
+    assert sp + ss == F.MAX_SPLITS
+    n = lib.fdec_cascade_workspace_size(40, 16, 4, 128, 3, ss)
+    # explicit 3 + planned: accepted up to the workspace check (too small on purpose)
+    assert lib.fdec_cascade_decode(FAKE, 40, 16, ctypes.byref(kvp), FAKE, 15, FAKE, 3, 0, 0.0, FAKE, None, FAKE, 16,
+                                   None) == F.FDEC_ERR_WORKSPACE
+    assert "splits" in last_error() and str(F.MAX_SPLITS - 3) in last_error()
+    assert n > 0

@@ -14,7 +14,7 @@ import torch
 
 import decode_attention_fdec_amd as F
 import oracle
-from helpers import OUT_TOL, appended_row_mask, assert_parity, okv, oracle_decode, to_dev
+from helpers import assert_parity, check_fp8_append, okv, oracle_decode, to_dev
 from synth import FP8, append_case, contiguous_case, paged_case, workload
 
 pytestmark = pytest.mark.gpu
@@ -183,75 +183,30 @@ def test_fp8_unsupported_paths_are_reported():
 # ("Inference Cookbook / 推理优化" §3.3-3.4 append and rotary, §7.2 FP8 KV cache:
 # the new row is stored as codes of value / descale, then attended to)
 
-def _f8_order(c):
-    """Position of e4m3fn codes on the number line (the two zeros coincide)."""
-    c = c.astype(np.int32)
-    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
-
-
-def _fp8_append(case, S, fused=False):
-    d = to_dev(case)
-    a = F.make_append(d["k_new"], d["v_new"], d["rope_cos"], d["rope_sin"], case.rotary_dim)
-    out, lse = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=S,
-                        append=a, fused=fused, k_descale=d["k_descale"], v_descale=d["v_descale"],
-                        cache_batch_idx=d["cache_batch_idx"], cache_leftpad=d["cache_leftpad"])
-    torch.cuda.synchronize()
-    kg = d["k"].cpu().view(torch.uint8).numpy()
-    vg = d["v"].cpu().view(torch.uint8).numpy()
-    return out, lse, kg, vg
-
-
-def _check_fp8_append(case, S, fused, what):
-    kc, vc, q_rot, after = oracle.append(okv(case), case.k_new, case.v_new, case.q, case.seq_lens,
-                                         case.rotary_dim, case.rope_base)
-    ref_out, ref_lse = oracle.decode(after, q_rot, case.seq_lens + 1, 1 / math.sqrt(case.D))
-    out, lse, kg, vg = _fp8_append(case, S, fused)
-    # v, the k rows not written and the k dims not rotated are bitwise the oracle's
-    assert np.array_equal(vg, vc), f"{what}: v cache differs"
-    m = appended_row_mask(case)
-    assert np.array_equal(kg[~m], kc[~m]), f"{what}: a k element outside the appended rows differs"
-    rd = case.rotary_dim
-    kg_r, kc_r = kg[m].reshape(-1, case.D), kc[m].reshape(-1, case.D)
-    assert np.array_equal(kg_r[:, rd:], kc_r[:, rd:]), f"{what}: an unrotated appended k element differs"
-    # a rotated element: the kernel rotates in fp32, the oracle in double; the
-    # code may then sit one step away when the value lies at a rounding midpoint
-    step = np.abs(_f8_order(kg_r[:, :rd]) - _f8_order(kc_r[:, :rd]))
-    assert step.size == 0 or step.max() <= 1, f"{what}: a rotated k code is off by more than one step"
-    n_off = int((step > 0).sum())
-    assert n_off <= max(2, step.size // 1000), f"{what}: {n_off} rotated codes off by one step"
-    if n_off == 0:
-        assert_parity(out, lse, ref_out, ref_lse, case.dtype, what)
-    else:  # outputs of the (request, KV head) groups whose row differs move by that step only
-        assert torch.isfinite(out).all()
-        err = np.abs(out.cpu().double().numpy() - ref_out).max()
-        assert err <= 0.05, f"{what}: output error {err:.3g} with {n_off} codes one step off"
-    return n_off
-
-
 @pytest.mark.parametrize("G,rd,paged,S,fused", [
     (1, 128, False, 4, False), (2, 0, True, 3, True), (4, 128, True, 7, False), (4, 64, False, 1, True),
     (8, 128, False, 5, False), (8, 0, True, 2, True), (2, 128, False, 32, False)])
 def test_fp8_append_matches_oracle(G, rd, paged, S, fused):
     case = append_case(181 + G + rd, 3, 2 * G, 2, 128, 300, FP8, rotary_dim=rd, pad="nan",
                        page_size=16 if paged else 0, cache_seqlens=[0, 150, 299])
-    _check_fp8_append(case, S, fused, f"fp8 append G={G} rd={rd} paged={paged} S={S}")
+    check_fp8_append(case, S, fused, f"fp8 append G={G} rd={rd} paged={paged} S={S}")
 
 
 def test_fp8_append_head_dim_64():
     case = append_case(188, 3, 8, 2, 64, 300, FP8, rotary_dim=64, pad="nan", cache_seqlens=[5, 150, 298])
-    _check_fp8_append(case, 3, False, "fp8 append D=64")
+    check_fp8_append(case, 3, False, "fp8 append D=64")
 
 
 def test_fp8_append_with_batch_idx_and_leftpad():
     case = append_case(189, 3, 8, 2, 128, 256, FP8, rotary_dim=128, pad="zero", cache_seqlens=[40, 0, 255])
     case.cache_batch_idx = torch.tensor([2, 0, 1], dtype=torch.int32)
     case.cache_leftpad = torch.tensor([7, 0, 100], dtype=torch.int32)
-    _check_fp8_append(case, 4, False, "fp8 append batch_idx + leftpad")
+    check_fp8_append(case, 4, False, "fp8 append batch_idx + leftpad")
 
 
 def test_fp8_append_at_the_append_workload_size():
     # the append + rotary workload's shapes (4 requests, 32 query heads, 8 KV
     # heads, 2048 rows, rotary 128) with a float8 cache
     case = append_case(4, 4, 32, 8, 128, 2048, FP8, rotary_dim=128, pad="nan")
-    n_off = _check_fp8_append(case, 0, False, "fp8 append workload")
+    n_off = check_fp8_append(case, 0, False, "fp8 append workload")
     assert n_off <= 2
