@@ -7,8 +7,9 @@ requests whose lengths mix empty, one-token, tile-edge and long requests,
 NaN in every unused row, and a split count from 0 (planned) to 40; then one of
 the entry points that takes that shape: fdec_decode (two kernels or the
 single-kernel merge, with or without an append + NeoX rotary),
-fdec_decode_balanced, fdec_decode_multi (1 to 8 query tokens, any G). The parity bar
-is the one every other parity test uses. The draws are fixed, so a failure
+fdec_decode_balanced, fdec_decode_multi (1 to 8 query tokens, any G). Each case
+first runs the device-data check on its inputs, which must flag nothing. The
+parity bar is the one every other parity test uses. The draws are fixed, so a failure
 names a case that can be rerun by its id.
 """
 import math
@@ -104,11 +105,15 @@ def test_random_case_matches_oracle(i):
     what = case_id(i)
     d = to_dev(case)
     kw = dict(k_descale=d["k_descale"], v_descale=d["v_descale"])
+    a = None
+    if c["kind"] == "append":
+        a = F.make_append(d["k_new"], d["v_new"], d["rope_cos"], d["rope_sin"], case.rotary_dim)
+    flags = F.check_inputs(d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], append=a)
+    assert flags == (0, -1), f"{what}: the device-data check flagged valid inputs {flags}"
     if c["kind"] == "append":
         kc, vc, q_rot, after = oracle.append(okv(case), case.k_new, case.v_new, case.q, case.seq_lens,
                                              case.rotary_dim, case.rope_base)
         ref_out, ref_lse = oracle.decode(after, q_rot, case.seq_lens + 1, 1 / math.sqrt(case.D))
-        a = F.make_append(d["k_new"], d["v_new"], d["rope_cos"], d["rope_sin"], case.rotary_dim)
         out, lse = F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"], num_splits=c["S"],
                             append=a)
         torch.cuda.synchronize()
