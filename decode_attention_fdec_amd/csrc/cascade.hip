@@ -16,17 +16,23 @@
 // other's softmax. Per 64-key tile:
 //   - K and V go global -> LDS row-major by LDS-DMA (global_load_lds_dwordx4,
 //     no registers), each wave its 8 rows, into a ring of kPfxNS tiles (two in
-//     flight); 16-byte pieces of row r sit in slot piece ^ (r mod 16), so the
+//     flight; the first goes out beside the query loads, so the block's start
+//     waits for one memory round trip, not two); 16-byte pieces of row r sit in slot piece ^ (r mod 16), so the
 //     K reads below and the transpose reads of V touch distinct banks;
 //   - S^T = K Q^T: A = K (16 keys x 32 d from LDS), B = Q^T (query rows held in
 //     registers), so each lane's result column is one query row and its four
 //     values are four keys of that row;
 //   - online softmax per row in the log2 domain (lazily moved reference as in the
-//     map kernel); P enters the matrix core rounded to the input type (hardware
+//     map kernel; the scale enters with the reference in one FMA per score, and
+//     the row maximum is taken over raw scores, then scaled: rounding is
+//     monotone); P enters the matrix core rounded to the input type (hardware
 //     nearest-even conversion), while the denominator sums the fp32 weights;
-//   - O += P V: A = P straight from the S^T registers (the key order inside the
-//     K dimension is permuted identically for A and B), B = V^T from two
-//     ds_read_b64_tr_b16 of the row-major V tile (4 keys at one d per lane each).
+//   - O^T += V^T P^T: A = V^T from two ds_read_b64_tr_b16 of the row-major V
+//     tile (4 keys at one d per lane each), B = P^T straight from the S^T
+//     registers (the key order inside the K dimension is permuted identically
+//     for A and B). Each lane's result column is then its own query row, so a
+//     moved reference rescales O in the lane, and the states leave as 16-byte
+//     stores of four consecutive d.
 // Float8 pools (the pages' FP8 KV cache, e4m3fn with per-(request, KV head)
 // descales): rows of 128 bytes, one DMA instruction per wave for its 8 rows of
 // K and one for V; K pieces and V (by the 8-bit transpose read) widen to bf16
@@ -103,7 +109,6 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
     __shared__ __attribute__((aligned(16))) uint8_t kring[kPfxNS][kPfxKeys * RB];
     __shared__ __attribute__((aligned(16))) uint8_t vring[kPfxNS][kPfxKeys * RB];
     __shared__ int spages[kPrefixPagesPerBlock];
-    __shared__ float srow[kPfxWaves][3][kPfxRowsPerWave];
 
     const int split = blockIdx.x, g = blockIdx.y, rc = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -115,10 +120,8 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
     const int t_end = min(t_begin + p.chunk, p.prefix_len);
     const int ntiles = t_end > t_begin ? (t_end - t_begin + kPfxKeys - 1) / kPfxKeys : 0;
 
-    // page ids of this split's keys
-    const int pg0 = t_begin / p.page_size;
+    const int pg0 = t_begin / p.page_size;  // first page of this split's keys
     const int npg = ntiles > 0 ? (t_end - 1) / p.page_size - pg0 + 1 : 0;
-    for (int i = tid; i < npg; i += kPfxThreads) spages[i] = p.prefix_pages[pg0 + i];
 
     // query rows of this wave: row = rc*256 + 32w + 16rb + li; B operand per (rb, ks)
     uint4 qb[kRB][4];
@@ -132,10 +135,6 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         for (int ks = 0; ks < 4; ++ks)
             qb[rb][ks] = ok ? *reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * kq) : make_uint4(0, 0, 0, 0);
     }
-    // the loads above are done before any DMA is issued: a wait the compiler
-    // models keeps it from waiting on them (and so on the DMA) later
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     // per-lane factors of the query rows 16rb + li: float8 descales of the row's request
     float ksc[kRB], vsc[kRB];
@@ -182,25 +181,58 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
     // Default cache policy: unlike the split-KV kernels' streaming reads, the
     // non-temporal one measured slower here (the prefix block's loads are fewer and
     // its time goes to the matrix cores and the state writes, not to the stream)
+    // Page ids come from the LDS copy of the split's page list, or (the first
+    // tiles, issued before that copy exists) from registers loaded up front.
     const uint32_t stok = (uint32_t)(p.s_token * ES);
-    auto issue = [&](int tile) {
+    constexpr int kPieces = RB / 16;           // 16-byte pieces per row
+    constexpr int kRowsPerDma = 64 / kPieces;  // rows one instruction moves
+    constexpr int kGroups = 8 / kRowsPerDma;   // instructions per wave for K (and for V)
+    uint32_t voff_full[kGroups];               // lane offsets of a full tile
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+        const int r = 8 * w + kRowsPerDma * gi + lane / kPieces;
+        const int sw = KF ? pfx_swz8(r) : (r & 15);
+        voff_full[gi] = (uint32_t)(lane / kPieces) * stok + 16u * (uint32_t)((lane % kPieces) ^ sw);
+    }
+    // the first source row of group gi of a tile (rows past the split's end
+    // repeat its last key) and the page index holding it
+    auto src_row = [&](int tile, int gi, int &t, int &pidx) {
+        const int t0 = t_begin + tile * kPfxKeys;
+        t = t0 + min(8 * w + kRowsPerDma * gi, t_end - t0 - 1);
+        pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
+    };
+    // page ids of the first tiles, read before any tile load is issued (wave-
+    // uniform scalar loads: nothing the kernel writes has happened yet)
+    int ppage[kPfxNS - 1][kGroups] = {};
+    if (ntiles > 0) {
+#pragma unroll
+        for (int tt = 0; tt < kPfxNS - 1; ++tt)
+#pragma unroll
+            for (int gi = 0; gi < kGroups; ++gi) {
+                int t, pidx;
+                src_row(min(tt, ntiles - 1), gi, t, pidx);
+                ppage[tt][gi] = p.prefix_pages[__builtin_amdgcn_readfirstlane(pidx)];
+            }
+    }
+    auto issue = [&](int tile, const int *pro) {
         const int t0 = t_begin + tile * kPfxKeys;
         const int nvalid = t_end - t0;
         const int slot = tile % kPfxNS;
-        constexpr int kPieces = RB / 16;           // 16-byte pieces per row
-        constexpr int kRowsPerDma = 64 / kPieces;  // rows one instruction moves
 #pragma unroll
-        for (int gi = 0; gi < 8 / kRowsPerDma; ++gi) {
+        for (int gi = 0; gi < kGroups; ++gi) {
             const int r0 = 8 * w + kRowsPerDma * gi;
             const int rs = min(r0, nvalid - 1);  // the group's first source row
-            const int t = t0 + rs;
-            const int pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
-            const int64_t eoff = (int64_t)spages[pidx - pg0] * p.s_outer +
-                                 (int64_t)(t - pidx * p.page_size) * p.s_token + (int64_t)g * p.s_head;
-            const int r = r0 + lane / kPieces;
-            const int sw = KF ? pfx_swz8(r) : (r & 15);
-            const uint32_t voff =
-                (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane % kPieces) ^ sw);
+            int t, pidx;
+            src_row(tile, gi, t, pidx);
+            const int page = pro ? pro[gi] : spages[pidx - pg0];
+            const int64_t eoff = (int64_t)page * p.s_outer + (int64_t)(t - pidx * p.page_size) * p.s_token +
+                                 (int64_t)g * p.s_head;
+            uint32_t voff = voff_full[gi];
+            if (__builtin_expect(nvalid < kPfxKeys, 0)) {
+                const int r = r0 + lane / kPieces;
+                const int sw = KF ? pfx_swz8(r) : (r & 15);
+                voff = (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane % kPieces) ^ sw);
+            }
             dma16(reinterpret_cast<const char *>(p.k) + eoff * ES, voff, lds_addr(kring[slot]) + (uint32_t)RB * r0);
             dma16(reinterpret_cast<const char *>(p.v) + eoff * ES, voff, lds_addr(vring[slot]) + (uint32_t)RB * r0);
         }
@@ -219,15 +251,25 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         for (int db = 0; db < 8; ++db) o[rb][db] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
+    // The first tile's loads go out at once, so that their latency overlaps the
+    // query loads above and the page-list copy below. One wait (modelled by the
+    // compiler, so no later wait of its own counts the tile loads) covers those;
+    // the second tile then streams in while the first is computed, and the first
+    // iteration's barrier publishes the page list.
     const int npro = min(kPfxNS - 1, ntiles);
-    for (int t = 0; t < npro; ++t) issue(t);
+    if (npro > 0) issue(0, ppage[0]);
+    for (int i = tid; i < npg; i += kPfxThreads) spages[i] = p.prefix_pages[pg0 + i];
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int t = 1; t < kPfxNS - 1; ++t)
+        if (t < npro) issue(t, ppage[t]);
     for (int tile = 0; tile < ntiles; ++tile) {
         // this wave's part of the tile has landed once only later tiles' loads
         // remain; the barrier then covers every wave's part, and every wave is
         // done with the slot the next DMA overwrites (read two tiles ago)
         wait_vm_n<kDma>(min(kPfxNS - 2, ntiles - 1 - tile));
         __syncthreads();
-        if (tile + kPfxNS - 1 < ntiles) issue(tile + kPfxNS - 1);
+        if (tile + kPfxNS - 1 < ntiles) issue(tile + kPfxNS - 1, nullptr);
         const int t0 = t_begin + tile * kPfxKeys;
         // the slot's LDS bases as scalars (one value per wave), so each read adds
         // only its lane-constant offset
@@ -264,12 +306,6 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         const int nvalid = t_end - t0;
         bool move = false;
         float mx[kRB];
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s[kb][rb][r] *= ksc[rb];
         if (__builtin_expect(nvalid < kPfxKeys, 0)) {
 #pragma unroll
             for (int rb = 0; rb < kRB; ++rb)
@@ -287,34 +323,27 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x = fmaxf(x, s[kb][rb][r]);
             x = across_rows(x, MaxOp{});  // lanes L, L ^ 16, L ^ 32, L ^ 48: the row's 64 keys
+            x *= ksc[rb];  // the largest scaled score (rounding is monotone, the factor positive)
             mx[rb] = x;
             tmax[rb] = fmaxf(tmax[rb], x);
             move |= x > m[rb] + kTau;
         }
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
-            // move the reference; O rows live in lanes by (kq, r), so the
-            // per-row factors go through LDS
+            // move the reference; a lane's O^T values belong to its own row
 #pragma unroll
             for (int rb = 0; rb < kRB; ++rb) {
                 const float mn = fmaxf(m[rb], mx[rb]);
                 const float alpha = fexp2(m[rb] - mn);
                 m[rb] = mn;
                 l[rb] *= alpha;
-                if (kq == 0) srow[w][0][16 * rb + li] = alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[rb][db][r] *= alpha;
             }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float alpha = srow[w][0][16 * rb + 4 * kq + r];
-#pragma unroll
-                    for (int db = 0; db < 8; ++db) o[rb][db][r] *= alpha;
-                }
-            __builtin_amdgcn_wave_barrier();
         }
-        // P rounded to the input type, packed as the A operand of P V (the sum of
-        // weights stays in fp32): K-slot 8kq + e is key
+        // P rounded to the input type, packed as the B operand of V^T P^T (the sum
+        // of weights stays in fp32): K-slot 8kq + e is key
         // 32kk + 4kq + e (e < 4) or 32kk + 16 + 4kq + (e - 4) (e >= 4)
         uint4 pa[kRB][2];
 #pragma unroll
@@ -329,7 +358,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
                     float pv[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        pv[r] = fexp2(s[kb][rb][r] - m[rb]);
+                        pv[r] = fexp2(fmaf(s[kb][rb][r], ksc[rb], -m[rb]));
                         ps += pv[r];  // the denominator keeps fp32 weights
                     }
                     wv[2 * hbk] = pfx_pack2<DT>(pv[0], pv[1]);
@@ -340,8 +369,8 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
             l[rb] += ps;
         }
 
-        // ---- O += P V
-        // B operand of K-slots 8kq .. 8kq + 7 at d = 16db + li: keys 32kk + 4kq + 0..3
+        // ---- O^T += V^T P^T
+        // A operand of K-slots 8kq .. 8kq + 7 at d = 16db + li: keys 32kk + 4kq + 0..3
         // and 32kk + 16 + 4kq + 0..3, each set from one transpose read whose lane m
         // (of 16) addresses key row 32kk (+16) + 4kq + m / 4, d 16db + 4 (m % 4) .. + 3.
         // Float8: one 8-bit transpose read (in each group of 16 lanes, lane j gets
@@ -357,7 +386,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
                     const uint2 v0 = fp8x4_to_bf16((uint32_t)x[0]), v1 = fp8x4_to_bf16((uint32_t)x[1]);
                     const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-                    for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
+                    for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(bop, pa[rb][kk], o[rb][db]);
                 }
             } else {
 #pragma unroll
@@ -368,45 +397,34 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
                     const uint2 v0 = __builtin_bit_cast(uint2, x0), v1 = __builtin_bit_cast(uint2, x1);
                     const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-                    for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(pa[rb][kk], bop, o[rb][db]);
+                    for (int rb = 0; rb < kRB; ++rb) o[rb][db] = Mfma<DT>::run(bop, pa[rb][kk], o[rb][db]);
                 }
             }
         }
 
     }
 
-    // ---- states against the true maximum: O~ = O 2^(m - T), d = l 2^(m - T)
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-        float lt = l[rb];
-        lt = across_rows(lt, AddOp{});
-        const float T = tmax[rb];
-        const float f = (T == kNegInf) ? 0.0f : fexp2(m[rb] - T);
-        if (kq == 0) {
-            srow[w][0][16 * rb + li] = f * vsc[rb];  // V's descale (1 for 16-bit pools)
-            srow[w][1][16 * rb + li] = lt * f;
-            srow[w][2][16 * rb + li] = (T == kNegInf) ? kNegInf : T * kLn2;
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
+    // ---- states against the true maximum: O~ = O 2^(m - T), d = l 2^(m - T).
+    // Lane (kq, li) holds d = 16db + 4kq .. + 3 of row 16rb + li: one 16-byte
+    // store per (rb, db).
     const int64_t slot = p.s_offset + split;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
+        const float lt = across_rows(l[rb], AddOp{});
+        const float T = tmax[rb];
+        const float f = (T == kNegInf) ? 0.0f : fexp2(m[rb] - T);
+        const int row = rc * kPfxRows + w * kPfxRowsPerWave + 16 * rb + li;
+        if (row >= R) continue;
+        const int b = row / G, hh = row - b * G;
+        const int64_t bh = (int64_t)b * p.Hq + g * G + hh;
+        const float fo = f * vsc[rb];  // V's descale (1 for 16-bit pools)
+        float4 *dst = reinterpret_cast<float4 *>(p.po + (bh * p.s_total + slot) * D + 4 * kq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rl = 16 * rb + 4 * kq + r;
-            const int row = rc * kPfxRows + w * kPfxRowsPerWave + rl;
-            if (row >= R) continue;
-            const int b = row / G, hh = row - b * G;
-            const int64_t bh = (int64_t)b * p.Hq + g * G + hh;
-            const float f = srow[w][0][rl];
-            float *dst = p.po + (bh * p.s_total + slot) * D;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) dst[16 * db + li] = o[rb][db][r] * f;
-            if (li == 0) {
-                p.pd[bh * p.s_total + slot] = srow[w][1][rl];
-                p.pm[bh * p.s_total + slot] = srow[w][2][rl];
-            }
+        for (int db = 0; db < 8; ++db)
+            dst[4 * db] = make_float4(o[rb][db][0] * fo, o[rb][db][1] * fo, o[rb][db][2] * fo, o[rb][db][3] * fo);
+        if (kq == 0) {
+            p.pd[bh * p.s_total + slot] = lt * f;
+            p.pm[bh * p.s_total + slot] = (T == kNegInf) ? kNegInf : T * kLn2;
         }
     }
 }
