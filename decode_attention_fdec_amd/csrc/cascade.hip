@@ -65,11 +65,15 @@ template <> struct Mfma<1> {
 };
 
 constexpr int kPfxKeys = 64;            // keys per tile
-constexpr int kPfxWaves = 8;
+#ifndef FDEC_PFX_WAVES
+#define FDEC_PFX_WAVES 8
+#endif
+constexpr int kPfxWaves = FDEC_PFX_WAVES;
 constexpr int kPfxRowsPerWave = 32;     // query rows per wave
 constexpr int kRB = kPfxRowsPerWave / 16;
 constexpr int kPfxRows = kPfxWaves * kPfxRowsPerWave;
 constexpr int kPfxThreads = 64 * kPfxWaves;
+constexpr int kPfxDmaRows = kPfxKeys / kPfxWaves;  // rows of each tile one wave loads
 
 // Two 16-bit values packed (lo, hi), rounded to nearest even by the hardware.
 template <int DT> __device__ __forceinline__ uint32_t pfx_pack2(float a, float b);
@@ -81,7 +85,10 @@ template <> __device__ __forceinline__ uint32_t pfx_pack2<1>(float a, float b) {
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
 }
-constexpr int kPfxNS = 3;                  // ring slots (two tiles in flight; four measured no faster)
+#ifndef FDEC_PFX_NS
+#define FDEC_PFX_NS 3
+#endif
+constexpr int kPfxNS = FDEC_PFX_NS;  // ring slots (two tiles in flight; four measured no faster)
 typedef short pfx_s16x4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) pfx_s16x4_v pfx_lds_s16x4;
 typedef int pfx_i32x2_v __attribute__((ext_vector_type(2)));
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
     constexpr int D = 128;
     constexpr int ES = KF ? 1 : 2;                 // bytes per element
     constexpr int RB = D * ES;                     // bytes per K / V row in LDS
-    constexpr int kDma = KF ? 2 : 4;               // DMA instructions per wave and tile
+    constexpr int kDma = 2 * kPfxDmaRows * RB / 1024;  // DMA instructions per wave and tile
     static_assert(!KF || DT == 1, "float8 pools take bf16 queries");
     __shared__ __attribute__((aligned(16))) uint8_t kring[kPfxNS][kPfxKeys * RB];
     __shared__ __attribute__((aligned(16))) uint8_t vring[kPfxNS][kPfxKeys * RB];
@@ -174,8 +181,9 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         vsw = (uint32_t)(ra0 >> 1);
     }
 
-    // DMA of tile `tile` into ring slot tile % kPfxNS: this wave's rows 8w .. 8w + 7
-    // of K and of V, four rows (16-bit) or all eight (float8) per instruction
+    // DMA of tile `tile` into ring slot tile % kPfxNS: this wave's kPfxDmaRows rows
+    // (8w .. 8w + 7 with eight waves) of K and of V, four rows (16-bit) or eight
+    // (float8) per instruction
     // (one page: pages hold multiples of 16 keys); rows past the split's end
     // repeat its last key (masked below).
     // Default cache policy: unlike the split-KV kernels' streaming reads, the
@@ -186,11 +194,12 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
     const uint32_t stok = (uint32_t)(p.s_token * ES);
     constexpr int kPieces = RB / 16;           // 16-byte pieces per row
     constexpr int kRowsPerDma = 64 / kPieces;  // rows one instruction moves
-    constexpr int kGroups = 8 / kRowsPerDma;   // instructions per wave for K (and for V)
+    constexpr int kGroups = kPfxDmaRows / kRowsPerDma;  // instructions per wave for K (and for V)
+    static_assert(2 * kGroups == kDma, "one K and one V instruction per row group");
     uint32_t voff_full[kGroups];               // lane offsets of a full tile
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
-        const int r = 8 * w + kRowsPerDma * gi + lane / kPieces;
+        const int r = kPfxDmaRows * w + kRowsPerDma * gi + lane / kPieces;
         const int sw = KF ? pfx_swz8(r) : (r & 15);
         voff_full[gi] = (uint32_t)(lane / kPieces) * stok + 16u * (uint32_t)((lane % kPieces) ^ sw);
     }
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
     // repeat its last key) and the page index holding it
     auto src_row = [&](int tile, int gi, int &t, int &pidx) {
         const int t0 = t_begin + tile * kPfxKeys;
-        t = t0 + min(8 * w + kRowsPerDma * gi, t_end - t0 - 1);
+        t = t0 + min(kPfxDmaRows * w + kRowsPerDma * gi, t_end - t0 - 1);
         pidx = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
     };
     // page ids of the first tiles, read before any tile load is issued (wave-
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(kPfxThreads, 1) void cascade_prefix_kernel(const Ca
         const int slot = tile % kPfxNS;
 #pragma unroll
         for (int gi = 0; gi < kGroups; ++gi) {
-            const int r0 = 8 * w + kRowsPerDma * gi;
+            const int r0 = kPfxDmaRows * w + kRowsPerDma * gi;
             const int rs = min(r0, nvalid - 1);  // the group's first source row
             int t, pidx;
             src_row(tile, gi, t, pidx);
