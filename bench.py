@@ -542,7 +542,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the decode path has no multi-GPU mode in this build", file=sys.stderr)
+              "the decode path runs on one GPU and has no multi-GPU mode", file=sys.stderr)
         return 2
 
     import torch
