@@ -221,9 +221,15 @@ def time_per_launch(runner: Runner, steps: int, copy=None):
     return sorted(a.elapsed_time(b) for a, b in ev)  # ms
 
 
-def stage_labels(runner: Runner):
-    """The kernels one step launches, in order."""
+CASCADE_SINGLE = "cascade prefix + suffix (single kernel)"
+
+
+def stage_labels(runner: Runner, nkernels: int = 0):
+    """The kernels one step launches, in order (a cascade step launches two when
+    its prefix and suffix blocks share one grid, three otherwise)."""
     if runner.cascade:
+        if nkernels == 2:
+            return [CASCADE_SINGLE, "cascade merge"]
         return ["cascade prefix (matrix cores)", "suffix map (balanced split)", "cascade merge"]
     if runner.mode == "bal":
         return ["map (balanced split)", "segment merge"]
@@ -249,7 +255,7 @@ def time_stages(F, runner: Runner, steps: int) -> dict:
     for m, k in zip(ms, kinds):
         if k >= 1:
             by.setdefault(k, []).append(m * 1e3)
-    labels = stage_labels(runner)
+    labels = stage_labels(runner, len(by))
     return {(labels[k - 1] if k - 1 < len(labels) else f"kernel {k}"): round(sum(v) / len(v), 2)
             for k, v in sorted(by.items())}
 
@@ -257,6 +263,19 @@ def time_stages(F, runner: Runner, steps: int) -> dict:
 def roofline_entry(case, stages: dict, runner: Runner) -> dict:
     """HBM roofline of the step's dominant kernel(s): algorithmic bytes / mean duration."""
     out = {}
+    if runner.cascade and CASCADE_SINGLE in stages:
+        # prefix and suffix blocks in one kernel: its bytes are every attended K/V
+        # byte (the prefix once), its flops the prefix's; floor = max of the two
+        nb = case.kv_bytes()
+        t = stages[CASCADE_SINGLE]
+        flops = 4.0 * case.D * case.B * case.Hq * case.prefix_len
+        floor = max(nb / HBM_PEAK_GBS / 1e3, flops / MFMA_BF16_TFLOPS / 1e6)
+        out["prefix_suffix"] = {"bound": "hbm", "achieved": round(nb / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(nb / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "kernel": CASCADE_SINGLE, "avg_launch_us": t, "algorithmic_bytes_per_launch": nb,
+                                "prefix_tflops": round(flops / (t * 1e-6) / 1e12, 1), "floor_us": round(floor, 2),
+                                "frac_of_floor": round(floor / t, 4)}
+        return out
     if runner.cascade:
         pre = case.prefix_len * case.Hkv * 2 * case.D * case.k.element_size()
         suf = case.kv_bytes() - pre
@@ -503,7 +522,7 @@ def measure_workload(F, name: str, mode: str, splits: int, steps: int, warmup: i
            "warm_us_per_step": round(warm * 1e3, 2), "num_splits": runner.S, "mode": mode,
            "kv_copies_rotated": runner.copies, "kernel_us": stages,
            "roofline": roofline_entry(case, stages, runner)}
-    rl = res["roofline"]["suffix"] if runner.cascade else res["roofline"]
+    rl = res["roofline"] if not runner.cascade else res["roofline"].get("prefix_suffix", res["roofline"].get("suffix"))
     rl["traffic"] = load_traffic(name)  # HBM bytes of the map kernel from the stored counters, if current
     log(f"[bench] {name}: {res['us_per_step']} us/step, {res['GBps']} GB/s ({res['pct_of_peak']}% of peak)")
     return case, runner, res, per
@@ -559,12 +578,12 @@ def main() -> int:
                                               args.warmup, dev, args.launch)
     # the dominant kernel: the split-KV map kernel of the step (the suffix map of a
     # cascade), timed with the library's stage-timing events on its stream
-    rl = res["roofline"]["suffix"] if runner.cascade else res["roofline"]
+    rl = res["roofline"] if not runner.cascade else res["roofline"].get("prefix_suffix", res["roofline"].get("suffix"))
     achieved = rl["achieved"]
     roofline = dict(rl)
-    roofline.update({"traffic": load_traffic(args.workload),
-                     "kernel": map_kernel_name(case) + f" ({rl.get('kernel', 'suffix map')} stage of the timed step)",
-                     "kernel_hash": kernel_hash()})
+    kname = ("cascade_fused_kernel (prefix and suffix blocks)" if rl.get("kernel") == CASCADE_SINGLE
+             else map_kernel_name(case) + f" ({rl.get('kernel', 'suffix map')} stage of the timed step)")
+    roofline.update({"traffic": load_traffic(args.workload), "kernel": kname, "kernel_hash": kernel_hash()})
 
     # attainable streaming read at the map kernel's footprint (the probes)
     import torch as _t

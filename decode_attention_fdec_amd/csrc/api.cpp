@@ -575,6 +575,12 @@ extern "C" int fdec_merge_states(const float *part_o, const float *part_m, const
 // kernel takes the shape (G = 4, head_dim 128): workspace = meta [B, 2], the
 // prefix states [B, Hq, sp] and the suffix pieces [Hq, ss + B].
 bool cascade_balanced_shape(int Hq, int Hkv, int D) { return Hq == 4 * Hkv && D == 128; }
+// The single-launch cascade needs suffix blocks of four KV heads (Hkv a multiple
+// of 4); FDEC_CASCADE_PATH=two keeps the prefix and suffix kernels apart.
+bool cascade_single_launch(const fdec::MapParams &pb) {
+    const char *path = std::getenv("FDEC_CASCADE_PATH");
+    return pb.heads_per_block == fdec::kMapMfmaWaves && !(path && std::strcmp(path, "two") == 0);
+}
 
 struct CascBalLayout {
     size_t meta, ppm, ppd, ppo, pm, pd, po, total;
@@ -620,9 +626,23 @@ extern "C" int fdec_cascade_plan_kv(int B, int Hq, int Hkv, int prefix_len, int 
         page_size % 16)
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: bad sizes", fn);
     if (cu_count <= 0) cu_count = 256;
+    // the single-launch cascade (G = 4, Hkv a multiple of 4) runs 128-row prefix
+    // blocks beside one suffix block per compute unit; otherwise the prefix
+    // kernel's 256-row blocks take the whole GPU first
+    const char *path = std::getenv("FDEC_CASCADE_PATH");
+    const bool single = Hq == 4 * Hkv && Hkv % fdec::kMapMfmaWaves == 0 && !(path && std::strcmp(path, "two") == 0);
     const int rows = B * (Hq / Hkv);
-    const int row_chunks = rows > 0 ? (rows + 255) / 256 : 1;
+    const int chunk_rows = single ? fdec::kMapMfmaWaves * 32 : 256;
+    const int row_chunks = rows > 0 ? (rows + chunk_rows - 1) / chunk_rows : 1;
     int sp = (cu_count + Hkv * row_chunks - 1) / (Hkv * row_chunks);
+    if (single) {
+        // at most one prefix block per compute unit (more start only when others
+        // end); with 16-bit pools three quarters of the units measured faster
+        // (the shared-prefix workload: 70 us at 192 prefix blocks against 76 at
+        // 256), with float8 pools all of them (61 against 68)
+        const int target = kv_dtype == FDEC_FP8_E4M3 ? cu_count : (3 * cu_count) / 4;
+        sp = std::max(1, target / (Hkv * row_chunks));
+    }
     sp = std::min(sp, std::max(1, prefix_len / 256));
     sp = std::max(1, std::min(sp, FDEC_MAX_SPLITS / 2));
     // each prefix block stages at most kPrefixPagesPerBlock - 2 page ids
@@ -640,9 +660,10 @@ extern "C" int fdec_cascade_plan_kv(int B, int Hq, int Hkv, int prefix_len, int 
                 hpb = w;
                 break;
             }
-        // float8 pools: two blocks per compute unit (half the bytes per tile, so more
-        // tiles in flight per compute unit), as far as the merge's 256 states allow
-        ss = std::max(1, cu_count / (Hkv / hpb)) * (kv_dtype == FDEC_FP8_E4M3 ? 2 : 1);
+        // float8 pools on the separate suffix kernel: two blocks per compute unit
+        // (half the bytes per tile, so more tiles in flight per compute unit), as far
+        // as the merge's 256 states allow; the single launch keeps one per unit
+        ss = std::max(1, cu_count / (Hkv / hpb)) * (kv_dtype == FDEC_FP8_E4M3 && !single ? 2 : 1);
     } else {
         int rc = fdec_plan_kv(B, Hq, Hkv, nullptr, capacity, page_size, kv_dtype, cu_count, &ss);
         if (rc) return rc;
@@ -733,16 +754,23 @@ extern "C" int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *
         cp.po = reinterpret_cast<float *>(ws + w.ppo);
         cp.s_total = sp;
         cp.s_offset = 0;
-        Launches run(st);
-        if ((rc = run.done(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch")))
-            return rc;
         pb.seg_meta = reinterpret_cast<int *>(ws + w.meta);
         pb.pm = reinterpret_cast<float *>(ws + w.pm);
         pb.pd = reinterpret_cast<float *>(ws + w.pd);
         pb.po = reinterpret_cast<float *>(ws + w.po);
         pb.nslots = ss + B;
-        if ((rc = run.done(fdec::launch_map_mfma_g4_balanced(pb, ss, st), "fdec_cascade_decode: suffix launch")))
-            return rc;
+        Launches run(st);
+        if (cascade_single_launch(pb)) {
+            // prefix and suffix blocks share the compute units (one launch)
+            if ((rc = run.done(fdec::launch_cascade_fused(cp, pb, sp, ss, st),
+                               "fdec_cascade_decode: prefix and suffix launch")))
+                return rc;
+        } else {
+            if ((rc = run.done(fdec::launch_cascade_prefix(cp, sp, st), "fdec_cascade_decode: prefix launch")))
+                return rc;
+            if ((rc = run.done(fdec::launch_map_mfma_g4_balanced(pb, ss, st), "fdec_cascade_decode: suffix launch")))
+                return rc;
+        }
         return run.done(fdec::launch_merge_cascade(cp.po, cp.pm, cp.pd, sp, pb.po, pb.pm, pb.pd, pb.seg_meta, B, Hq,
                                                     pb.nslots, ss, out, lse, st),
                          "fdec_cascade_decode: merge launch");

@@ -121,6 +121,11 @@ struct CascadeParams {
 };
 // Grid: (splits, Hkv, ceil(B * Hq / Hkv / 256)).
 hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t stream);
+// Shared prefix and balanced suffixes (G = 4, four KV heads per suffix block) in
+// one launch: sp prefix splits of 128-row chunks and ss suffix blocks per group of
+// four KV heads; cascade_fused_blocks gives the two block counts (0 on overflow).
+int cascade_fused_blocks(const CascadeParams &cp, int sp, int ss, int *nprefix, int *nsuffix);
+hipError_t launch_cascade_fused(const CascadeParams &cp, const MapParams &pb, int sp, int ss, hipStream_t stream);
 
 // One wave per (b, h): merges S states into out / lse.
 hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S,

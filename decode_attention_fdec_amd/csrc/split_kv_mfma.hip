@@ -37,6 +37,7 @@
 // verified on the GPU), both by v_cvt_scalef32_pk_bf16_fp8 at scale 1 (every
 // e4m3 value is a bf16 value: exact). K's descale multiplies the score scale
 // and V's the written state.
+#include "cascade_prefix.h"
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -755,23 +756,31 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
 // With fewer tiles than blocks, only the first (tiles) blocks take work, so
 // every working block has at least one tile and no slot of a request is left
 // unwritten. Every wave scans seq_lens itself (no block barrier).
+// The LDS of one balanced-split block: each wave's K/V ring, and the Q of the
+// pieces in flight (at most one per ring slot), QL query tokens each (with HG:
+// the two groups of four query heads of a G = 8 KV head, one query).
+template <int KF, int QL> struct BalLds {
+    __attribute__((aligned(16))) uint8_t ring[kMapMfmaWaves][Ring<KF>::kBytes];
+    __attribute__((aligned(16))) uint8_t q[kMapMfmaWaves][Ring<KF>::kSlots][QL][4 * 128 * 2];
+};
+
+// Block blk of NB of the balanced split, grid row by (groups of QL query
+// tokens) and group bz of KV heads.
 template <int DT, bool PAGED, int KF, int QL, bool HG = false>
-__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
+__device__ __forceinline__ void map_g4_bal_body(const MapParams &p, int blk, int NB, int by, int bz,
+                                                BalLds<KF, QL> &sm) {
     constexpr int D = 128, G = 4;
     constexpr int NS = Ring<KF>::kSlots;
     static_assert(!HG || QL == 2, "groups of eight query heads run as two groups of four");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
-    // Q of the pieces in flight (at most one per ring slot), QL query tokens each
-    // (with HG: the two groups of four query heads of a G = 8 KV head, one query)
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kMapMfmaWaves][NS][QL][G * D * 2];
+    auto &lds = sm.ring;
+    auto &qlds = sm.q;
     // query tokens ti0 .. ti0 + nq - 1 of every request (grid y: groups of QL)
-    const int ti0 = HG ? 0 : blockIdx.y * QL, nq = HG ? 2 : min(QL, p.q_len - ti0);
+    const int ti0 = HG ? 0 : by * QL, nq = HG ? 2 : min(QL, p.q_len - ti0);
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = blockIdx.z * p.heads_per_block + wv;
+    const int g = bz * p.heads_per_block + wv;
     const int hq0 = g * (HG ? 2 * G : G);
-    const int NB = gridDim.x, blk = blockIdx.x;
     const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
 
     // ---- the block's tile range and its first request
@@ -809,7 +818,7 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     const bool working = blk < NBe;
     const int start = working ? (int)((int64_t)blk * NT / NBe) : 0;
     const int end = working ? (int)((int64_t)(blk + 1) * NT / NBe) : 0;
-    const bool meta_writer = blockIdx.z == 0 && blockIdx.y == 0 && wv == 0;
+    const bool meta_writer = bz == 0 && by == 0 && wv == 0;
     // (first slot, piece count) of request j, whose tiles are [P, P + T), when
     // its first tile lies in this block's range
     auto write_meta = [&](int j, int P, int T) {
@@ -978,6 +987,12 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(
     if (one_pass) write_meta(lane, incl1 - T1, T1);
 }
 
+template <int DT, bool PAGED, int KF, int QL, bool HG = false>
+__global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_bal(const MapParams p) {
+    __shared__ BalLds<KF, QL> sm;
+    map_g4_bal_body<DT, PAGED, KF, QL, HG>(p, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, sm);
+}
+
 // Instantiations: q / compute type DT (0 fp16, 1 bf16), paged or not, KV
 // format (float8 caches take bf16 queries); EXTRA: further template arguments.
 #define FDEC_MFMA_DISPATCH(KERNEL, ...)                                                              \
@@ -1065,5 +1080,93 @@ hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
     return hipGetLastError();
 }
 #undef FDEC_MFMA_DISPATCH
+
+// ---- Single-launch cascade (shared prefix + balanced suffixes, G = 4).
+// The prefix blocks are compute-bound (matrix cores and the softmax, HBM mostly
+// idle) and the balanced suffix blocks stream; run one after the other, each
+// leaves the other's resource idle. Here one grid holds both: prefix blocks of
+// four waves (128 query rows) take the suffix blocks' shape, so a
+// block of each fits on one compute unit (LDS and VGPRs), and the roles are
+// dealt so that every compute unit gets one of each. Blocks go to the eight XCDs
+// in turn (block b to XCD b % 8) and, within an XCD, one per compute unit before
+// any gets a second: within each run of 256 blocks, the XCDs of one parity take
+// one role, and the next run swaps the parities. Pairs beyond whole runs
+// alternate, and the count left over goes to whichever role has more blocks.
+// The roles change only where blocks run, not what they compute: a prefix block
+// is the prefix kernel's work on its row chunk, a suffix block the balanced
+// kernel's block `blk` of `ss`, both with the same arithmetic.
+__device__ __forceinline__ void cascade_role(int b, int NPf, int NSf, bool &prefix, int &v) {
+    const int npair = min(NPf, NSf);
+    const int runs = (2 * npair) / 256;  // whole runs of 256 blocks, 128 of each role
+    if (b < 256 * runs) {
+        const int run = b >> 8, x = b & 7, j = (b & 255) >> 3;
+        prefix = ((x + run) & 1) == 0;
+        v = run * 128 + j * 4 + (x >> 1);
+        return;
+    }
+    const int b_alt = 256 * runs + 2 * (npair - 128 * runs);
+    if (b < b_alt) {
+        const int k = b - 256 * runs;
+        prefix = (k & 1) == 0;
+        v = 128 * runs + (k >> 1);
+        return;
+    }
+    prefix = NPf > NSf;
+    v = npair + (b - b_alt);
+}
+
+// Prefix ring slots: two for 16-bit pools (the union is then the suffix's 72 KB),
+// three for float8 pools (half-size tiles: 52 KB, inside the suffix's 60 KB).
+template <int KF> struct CascadeFusedSlots {
+    static constexpr int kValue = KF ? 3 : 2;
+};
+template <int KF> union CascadeFusedLds {
+    PfxLds<KF, CascadeFusedSlots<KF>::kValue> pf;
+    BalLds<KF, 1> sf;
+};
+
+template <int DT, int KF>
+__global__ __launch_bounds__(64 * kMapMfmaWaves, 2) void cascade_fused_kernel(const CascadeParams cp,
+                                                                                const MapParams pb, int NPf,
+                                                                                int NSf, int sp, int ss) {
+    __shared__ CascadeFusedLds<KF> sm;
+    bool prefix;
+    int v;
+    cascade_role((int)blockIdx.x, NPf, NSf, prefix, v);
+    if (prefix)
+        cascade_prefix_body<DT, KF, kMapMfmaWaves, CascadeFusedSlots<KF>::kValue>(cp, v % sp, (v / sp) % cp.Hkv,
+                                                                               v / (sp * cp.Hkv), sm.pf);
+    else
+        map_g4_bal_body<DT, true, KF, 1, false>(pb, v % ss, ss, 0, v / ss, sm.sf);
+}
+
+int cascade_fused_blocks(const CascadeParams &cp, int sp, int ss, int *nprefix, int *nsuffix) {
+    constexpr int kRows = kMapMfmaWaves * kPfxRowsPerWave;
+    const int R = cp.B * (cp.Hq / cp.Hkv);
+    const int64_t np = (int64_t)sp * cp.Hkv * ((R + kRows - 1) / kRows);
+    const int64_t ns = (int64_t)ss * (cp.Hkv / kMapMfmaWaves);
+    if (np + ns > INT32_MAX) return 0;
+    *nprefix = (int)np;
+    *nsuffix = (int)ns;
+    return 1;
+}
+
+hipError_t launch_cascade_fused(const CascadeParams &cp, const MapParams &pb, int sp, int ss, hipStream_t st) {
+    if (pb.heads_per_block != kMapMfmaWaves || cp.Hq != 4 * cp.Hkv || pb.Hq != cp.Hq || pb.Hkv != cp.Hkv ||
+        pb.q_len != 1 || pb.q_groups != 1 || !pb.page_table || pb.kv_fp8 != cp.kv_fp8 || sp < 1 || ss < 1)
+        return hipErrorInvalidValue;
+    int np = 0, ns = 0;
+    if (!cascade_fused_blocks(cp, sp, ss, &np, &ns)) return hipErrorInvalidValue;
+    const dim3 grid(np + ns), block(64 * kMapMfmaWaves);
+    if (cp.kv_fp8) {
+        if (cp.dtype != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((cascade_fused_kernel<1, 1>), grid, block, 0, st, cp, pb, np, ns, sp, ss);
+    } else if (cp.dtype == 0) {
+        hipLaunchKernelGGL((cascade_fused_kernel<0, 0>), grid, block, 0, st, cp, pb, np, ns, sp, ss);
+    } else {
+        hipLaunchKernelGGL((cascade_fused_kernel<1, 0>), grid, block, 0, st, cp, pb, np, ns, sp, ss);
+    }
+    return hipGetLastError();
+}
 
 }  // namespace fdec

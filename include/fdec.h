@@ -387,7 +387,12 @@ int fdec_decode_multi_balanced(const void *q, int B, int q_len, int Hq, const fd
  * 64 * ceil(ceil(prefix_len / splits_prefix) / 64) tokens, each of at most 1022
  * pages. With G = Hq/Hkv = 4 the suffixes run on the balanced split (as
  * fdec_decode_balanced) and splits_suffix is its block count per group of KV
- * heads; otherwise splits_suffix splits every suffix (as fdec_decode). At most
+ * heads; otherwise splits_suffix splits every suffix (as fdec_decode). With
+ * G = 4 and Hkv a multiple of 4, the prefix blocks (128 query rows each) and
+ * the suffix blocks share one launch, so that the matrix-core prefix work and
+ * the streaming suffix work run side by side on every compute unit (two
+ * launches, prefix then suffix, when FDEC_CASCADE_PATH=two is set in the
+ * environment); the states and the merge are the same either way. At most
  * FDEC_MAX_SPLITS states merge per request: splits_prefix + splits_suffix
  * <= FDEC_MAX_SPLITS. Workspace: fdec_cascade_workspace_size().
  */
@@ -397,18 +402,20 @@ int fdec_cascade_decode(const void *q, int B, int Hq, const fdec_kv *kv,
                         float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Split counts for fdec_cascade_decode (host only). The prefix is cut so the
- * matrix-core kernel has about one block per compute unit with at least 256
- * prefix tokens each. The suffix count is, for G = 4, the balanced split's
- * block count per group of KV heads (one block per compute unit over all
- * groups), else fdec_plan's split count over the suffix page table's
- * capacity. prefix_len >= 0; capacity = max_pages_per_seq * page_size of the
- * suffix table. fdec_cascade_plan_kv plans for a pool of element type kv_dtype
- * (an fdec_dtype; fdec_cascade_plan is it with a 16-bit pool): a float8 pool
- * with G = 4 takes two suffix blocks per compute unit (measured on MI355X: the
- * 64-request shared-prefix workload's suffix 43.6 -> 32.7 us) within
- * splits_prefix + splits_suffix <= FDEC_MAX_SPLITS, and fdec_plan_kv's count
- * otherwise.
+ * Split counts for fdec_cascade_decode (host only), with at least 256 prefix
+ * tokens per prefix split. When prefix and suffix share one launch (G = 4, Hkv
+ * a multiple of 4), each role gets at most one block per compute unit: prefix
+ * blocks of 128 query rows on three quarters of the units for 16-bit pools and
+ * on all of them for float8 pools (measured on MI355X, the 64-request
+ * shared-prefix workload: 70 against 76 us, and 61 against 68 us), and one
+ * balanced-split suffix block per unit. Otherwise the prefix kernel (256 query
+ * rows per block) gets about one block per compute unit, and the suffix count
+ * is, for G = 4, the balanced split's block count per group of KV heads (one
+ * block per compute unit; two for float8 pools) and else fdec_plan's split count
+ * over the suffix page table's capacity. prefix_len >= 0; capacity =
+ * max_pages_per_seq * page_size of the suffix table. fdec_cascade_plan_kv plans
+ * for a pool of element type kv_dtype (an fdec_dtype; fdec_cascade_plan is it
+ * with a 16-bit pool), within splits_prefix + splits_suffix <= FDEC_MAX_SPLITS.
  */
 int fdec_cascade_plan_kv(int B, int Hq, int Hkv, int prefix_len, int capacity, int page_size, int kv_dtype,
                          int cu_count, int *splits_prefix_out, int *splits_suffix_out);

@@ -212,9 +212,7 @@ hipError_t launch_map_mt16_balanced(const MapParams &p, int nb, hipStream_t) {
     balanced_states("launch_map_mt16_balanced", p, nb);
     return hipSuccess;
 }
-hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t) {
-    note("cascade_prefix");
-    const char *w = "launch_cascade_prefix";
+void prefix_checks(const char *w, const CascadeParams &p, int splits) {
     inside(w, p.q, (size_t)p.B * p.Hq * 128 * 2);
     if (p.kv_fp8) {  // float8 pools: bf16 queries, descales [B, Hkv] when given
         if (p.dtype != 1) fail(w, "float8 pool without bf16 queries");
@@ -230,6 +228,22 @@ hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t
     inside(w, p.po, slots * 128 * 4);
     Range r[3] = {{p.pm, slots * 4, "m"}, {p.pd, slots * 4, "d"}, {p.po, slots * 128 * 4, "O~"}};
     disjoint(w, r, 3);
+}
+hipError_t launch_cascade_prefix(const CascadeParams &p, int splits, hipStream_t) {
+    note("cascade_prefix");
+    prefix_checks("launch_cascade_prefix", p, splits);
+    return hipSuccess;
+}
+hipError_t launch_cascade_fused(const CascadeParams &cp, const MapParams &pb, int sp, int ss, hipStream_t) {
+    note("cascade_fused");
+    const char *w = "launch_cascade_fused";
+    if (pb.heads_per_block != 4 || cp.Hq != 4 * cp.Hkv || pb.Hq != cp.Hq || pb.Hkv != cp.Hkv)
+        fail(w, "needs G = 4 and four KV heads per suffix block");
+    if (!pb.page_table || pb.q_len != 1 || pb.kv_fp8 != cp.kv_fp8) fail(w, "suffix parameters disagree");
+    if (ss < 1 || ss > 256) fail(w, "suffix block count outside [1, 256]");
+    prefix_checks(w, cp, sp);
+    map_inputs(w, pb);
+    balanced_states(w, pb, ss);
     return hipSuccess;
 }
 hipError_t launch_merge(const float *po, const float *pm, const float *pd, int B, int Hq, int S, int D, float *out,

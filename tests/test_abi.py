@@ -188,16 +188,29 @@ def test_cascade_validation(fdec):
                                    small, None) == F.FDEC_ERR_WORKSPACE
 
 
-def test_cascade_plan_for_float8_pools(fdec):
+def test_cascade_plan_for_float8_pools(fdec, monkeypatch):
     import torch
 
-    # G = 4: the balanced suffix takes two blocks per compute unit for float8 pools,
-    # within the 256 states a merge holds; 16-bit pools and other G as before
+    # G = 4 with Hkv a multiple of 4: prefix and suffix share one launch, with at
+    # most one block of each per compute unit: 128-row prefix chunks on three
+    # quarters of the 256 units for 16-bit pools (12 splits x 8 KV heads x 2
+    # chunks), on all of them for float8 pools (16 splits), and one suffix block
+    # per unit
+    monkeypatch.delenv("FDEC_CASCADE_PATH", raising=False)
     assert F.cascade_plan(64, 32, 8, 16384, 2048, 64, kv_dtype=torch.bfloat16) == F.cascade_plan(64, 32, 8, 16384,
                                                                                                   2048, 64)
-    sp, ss = F.cascade_plan(64, 32, 8, 16384, 2048, 64, kv_dtype=torch.float8_e4m3fn)
-    sp16, ss16 = F.cascade_plan(64, 32, 8, 16384, 2048, 64)
-    assert sp == sp16 and ss == min(2 * ss16, F.MAX_SPLITS - sp)
+    assert F.cascade_plan(64, 32, 8, 16384, 2048, 64) == (12, 128)
+    assert F.cascade_plan(64, 32, 8, 16384, 2048, 64, kv_dtype=torch.float8_e4m3fn) == (16, 128)
+    # separate prefix and suffix kernels (forced, or two KV heads per suffix block):
+    # 256-row prefix chunks, and float8 pools take two suffix blocks per compute
+    # unit within the 256 states a merge holds
+    for Hq, Hkv, env in ((32, 8, "two"), (8, 2, None)):
+        if env:
+            monkeypatch.setenv("FDEC_CASCADE_PATH", env)
+        sp, ss = F.cascade_plan(64, Hq, Hkv, 16384, 2048, 64, kv_dtype=torch.float8_e4m3fn)
+        sp16, ss16 = F.cascade_plan(64, Hq, Hkv, 16384, 2048, 64)
+        assert sp == sp16 and ss == min(2 * ss16, F.MAX_SPLITS - sp)
+        monkeypatch.delenv("FDEC_CASCADE_PATH", raising=False)
     assert F.cascade_plan(4, 8, 4, 500, 512, 16, kv_dtype=torch.float8_e4m3fn)[1] == \
         F.plan(4, 8, 4, None, 512, 16, kv_dtype=torch.float8_e4m3fn)
     lib = F.load_library()
@@ -208,7 +221,7 @@ def test_cascade_plan_for_float8_pools(fdec):
 
 def test_cascade_plan(fdec):
     sp, ss = F.cascade_plan(64, 32, 8, 16384, 2048, 64)
-    assert 8 * sp >= 256 and 1 <= ss and sp + ss <= F.MAX_SPLITS
+    assert 8 * sp * 2 <= 256 and 1 <= ss and sp + ss <= F.MAX_SPLITS  # at most one prefix block per unit
     sp, ss = F.cascade_plan(2, 8, 2, 100, 256, 16)
     assert sp == 1  # fewer than 256 prefix tokens: one split
     sp, ss = F.cascade_plan(1, 8, 8, 0, 64, 16)
