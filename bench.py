@@ -306,7 +306,8 @@ CALIB_BYTES = 256 << 20
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str) -> dict:
-    """HBM traffic of the map kernel from rocprofv3 counter csv files.
+    """HBM traffic of the step's dominant kernel (the map kernel, or the
+    single-launch cascade kernel) from rocprofv3 counter csv files.
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
     counter reads for the calibration probes: a plain read (FETCH) and a plain
@@ -334,7 +335,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> dict:
 
     fetch_scale = CALIB_BYTES / 1024.0 / last(f, "read_kernel")
     write_scale = CALIB_BYTES / 1024.0 / last(w, "copy_kernel")
-    fk, wk = pick(f, "map_kernel"), pick(w, "map_kernel")
+    dom = "map_kernel" if any("map_kernel" in k for k in f) else "cascade_fused_kernel"
+    fk, wk = pick(f, dom), pick(w, dom)
     kernels = {}  # every library kernel of the run: median scaled bytes per dispatch
     for name in sorted(set(f) | set(w)):
         short = re.sub(r"\(.*", "", name).replace("void ", "").strip()

@@ -135,3 +135,34 @@ def test_fp8_cascade_equals_fp8_decode_over_concatenated_pages():
     torch.cuda.synchronize()
     assert (out_c - out_p).abs().max().item() < 3e-3
     assert ((lse_c - lse_p).abs() / lse_p.abs().clamp(min=1)).max().item() < 1e-4
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16, FP8])
+@pytest.mark.parametrize("B,Hkv,sp,ss", [(5, 4, 3, 7), (70, 8, 0, 0), (33, 8, 2, 130)])
+def test_single_launch_is_bitwise_the_two_launches(monkeypatch, dtype, B, Hkv, sp, ss):
+    """With G = 4 and Hkv a multiple of 4 the prefix and suffix blocks share one
+    launch; each query row's prefix state is computed the same way in a 4-wave
+    block as in the 8-wave prefix kernel, and the suffix blocks are the balanced
+    kernel's, so at the same split counts the outputs are bit for bit those of
+    the two launches (FDEC_CASCADE_PATH=two). Row counts that are not multiples
+    of 128 (20, 132) leave partly empty prefix blocks; 130 suffix blocks per
+    group of KV heads exceed one per compute unit."""
+    case = cascade_case(400 + B, B, 4 * Hkv, Hkv, 128, 900, 64, suffix_range=(0, 300), dtype=dtype, pad="nan",
+                        extra_pages=2)
+    d = to_dev(case)
+    if sp == 0:
+        sp, ss = F.cascade_plan(B, 4 * Hkv, Hkv, case.prefix_len, case.capacity, 64, kv_dtype=dtype)
+
+    def run():
+        out, lse = F.cascade_decode(d["q"], d["k"], d["v"], d["page_table"], d["prefix_pages"], case.prefix_len,
+                                    d["seq_lens"], sp, ss, k_descale=d["k_descale"], v_descale=d["v_descale"])
+        torch.cuda.synchronize()
+        return out, lse
+
+    monkeypatch.delenv("FDEC_CASCADE_PATH", raising=False)
+    o1, l1 = run()
+    monkeypatch.setenv("FDEC_CASCADE_PATH", "two")
+    o2, l2 = run()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), f"B={B} Hkv={Hkv} sp={sp} ss={ss}"
+    ref_out, ref_lse = oracle_decode(case)
+    assert_cascade_parity(case, o1, l1, ref_out, ref_lse, f"single launch B={B} Hkv={Hkv}")
