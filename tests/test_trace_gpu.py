@@ -43,13 +43,20 @@ def test_trace_marks_each_kernel_and_changes_nothing():
     del bal
 
 
-def test_trace_cascade_has_three_kernels():
+def test_trace_cascade_kernels(monkeypatch):
+    # G = 4, Hkv = 8: prefix and suffix blocks in one launch, then the merge; with
+    # FDEC_CASCADE_PATH=two the prefix kernel, the suffix kernel and the merge
     case = cascade_case(502, 8, 32, 8, 128, 1024, 64, suffix_lens=[300, 64, 1000, 5, 700, 256, 128, 900])
     d = to_dev(case)
-    F.trace_start(16)
-    F.cascade_decode(d["q"], d["k"], d["v"], d["page_table"], d["prefix_pages"], case.prefix_len, d["seq_lens"])
-    ms, kinds = F.trace_stop()
-    assert kinds == [1, 2, 3] and all(m > 0 for m in ms)
+    for env, want in ((None, [1, 2]), ("two", [1, 2, 3])):
+        if env:
+            monkeypatch.setenv("FDEC_CASCADE_PATH", env)
+        else:
+            monkeypatch.delenv("FDEC_CASCADE_PATH", raising=False)
+        F.trace_start(16)
+        F.cascade_decode(d["q"], d["k"], d["v"], d["page_table"], d["prefix_pages"], case.prefix_len, d["seq_lens"])
+        ms, kinds = F.trace_stop()
+        assert kinds == want and all(m > 0 for m in ms), f"path {env}: {kinds}"
 
 
 def test_trace_capacity_bounds_the_events():
