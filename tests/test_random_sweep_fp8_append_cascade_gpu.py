@@ -13,7 +13,9 @@ bf16, float8), pages of 16, 32, 48, 64 or 128 tokens, a shared prefix of 0 to
 per KV head) with suffixes of 0 to 500 tokens, NaN in every unused slot, and the
 prefix / suffix split counts (0 = planned). The bar is the cascade bar of the
 fixed tests (`assert_cascade_parity`: float8 pools within twice the P-rounding
-bound). The draws are fixed, so a failure names a case that can be rerun by its id.
+bound); where prefix and suffix share one launch (G = 4, Hkv 4 or 8) the result is
+also compared bit for bit with the two launches. The draws are fixed, so a failure
+names a case that can be rerun by its id.
 """
 import numpy as np
 import pytest
@@ -26,7 +28,7 @@ from synth import BF16, F16, FP8, append_case, cascade_case
 
 pytestmark = pytest.mark.gpu
 
-NAPPEND, NCASCADE = 48, 64
+NAPPEND, NCASCADE = 48, 128
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -85,13 +87,29 @@ def test_random_fp8_append_matches_oracle(i):
 
 
 @pytest.mark.parametrize("i", range(NCASCADE), ids=[cascade_id(i) for i in range(NCASCADE)])
-def test_random_cascade_matches_oracle(i):
+def test_random_cascade_matches_oracle(i, monkeypatch):
     c = draw_cascade(i)
     case = cascade_case(c["seed"], c["B"], c["G"] * c["Hkv"], c["Hkv"], 128, c["prefix"], c["ps"], suffix_lens=c["sl"],
                         dtype=c["dtype"], pad="nan", extra_pages=2)
     d = to_dev(case)
     ref_out, ref_lse = oracle_decode(case)
-    out, lse = F.cascade_decode(d["q"], d["k"], d["v"], d["page_table"], d["prefix_pages"], case.prefix_len,
-                                d["seq_lens"], c["sp"], c["ss"], k_descale=d["k_descale"], v_descale=d["v_descale"])
-    torch.cuda.synchronize()
+    monkeypatch.delenv("FDEC_CASCADE_PATH", raising=False)
+    sp, ss = c["sp"], c["ss"]
+    if sp == 0 or ss == 0:  # as the library plans (the planned counts depend on the launch path)
+        psp, pss = F.cascade_plan(c["B"], c["G"] * c["Hkv"], c["Hkv"], case.prefix_len, case.capacity, c["ps"],
+                                  kv_dtype=c["dtype"])
+        sp = sp or (max(1, min(psp, F.MAX_SPLITS - ss)) if ss else psp)
+        ss = ss or max(1, min(pss, F.MAX_SPLITS - sp))
+
+    def run():
+        out, lse = F.cascade_decode(d["q"], d["k"], d["v"], d["page_table"], d["prefix_pages"], case.prefix_len,
+                                    d["seq_lens"], sp, ss, k_descale=d["k_descale"], v_descale=d["v_descale"])
+        torch.cuda.synchronize()
+        return out, lse
+
+    out, lse = run()
     assert_cascade_parity(case, out, lse, ref_out, ref_lse, cascade_id(i))
+    if c["G"] == 4 and c["Hkv"] % 4 == 0:  # the single launch: bitwise the two launches at the same counts
+        monkeypatch.setenv("FDEC_CASCADE_PATH", "two")
+        o2, l2 = run()
+        assert torch.equal(out, o2) and torch.equal(lse, l2), f"{cascade_id(i)}: single launch differs from two"
