@@ -166,3 +166,19 @@ def test_single_launch_is_bitwise_the_two_launches(monkeypatch, dtype, B, Hkv, s
     assert torch.equal(o1, o2) and torch.equal(l1, l2), f"B={B} Hkv={Hkv} sp={sp} ss={ss}"
     ref_out, ref_lse = oracle_decode(case)
     assert_cascade_parity(case, o1, l1, ref_out, ref_lse, f"single launch B={B} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("dtype", [BF16, FP8])
+def test_cascade_many_requests(dtype):
+    """300 requests of G = 4 (1200 query rows per KV head, ten 128-row prefix
+    chunks): the planned single launch then has fewer prefix splits than row
+    chunks need for one block per compute unit, and more blocks of one role than
+    the other."""
+    case = cascade_case(431, 300, 32, 8, 128, 2048, 64, suffix_range=(0, 64), dtype=dtype, pad="nan",
+                        extra_pages=2)
+    # 192 (16-bit) or 256 (float8) prefix blocks at most, over 8 KV heads x 10 chunks
+    sp, ss = F.cascade_plan(300, 32, 8, case.prefix_len, case.capacity, 64, kv_dtype=dtype)
+    assert (sp, ss) == ((2 if dtype == BF16 else 3), 128)
+    ref_out, ref_lse = oracle_decode(case)
+    out, lse = run_cascade(case)
+    assert_cascade_parity(case, out, lse, ref_out, ref_lse, f"300 requests {dtype}")
