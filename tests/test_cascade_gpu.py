@@ -182,3 +182,19 @@ def test_cascade_many_requests(dtype):
     ref_out, ref_lse = oracle_decode(case)
     out, lse = run_cascade(case)
     assert_cascade_parity(case, out, lse, ref_out, ref_lse, f"300 requests {dtype}")
+
+
+@pytest.mark.parametrize("name", ["c5", "c5f8"])
+@pytest.mark.parametrize("sp,ss", [(32, 64), (24, 200), (1, 1)])
+def test_single_launch_role_counts_bitwise(monkeypatch, name, sp, ss):
+    """The full shared-prefix workloads with prefix and suffix block counts far
+    apart (512 prefix blocks against 128 suffix blocks: whole runs of paired
+    roles, then prefix blocks alone; 384 against 400; 16 against 2): the single
+    launch equals the two launches bit for bit."""
+    case = workload(name, pad="nan")
+    monkeypatch.delenv("FDEC_CASCADE_PATH", raising=False)
+    o1, l1 = run_cascade(case, sp, ss)
+    monkeypatch.setenv("FDEC_CASCADE_PATH", "two")
+    o2, l2 = run_cascade(case, sp, ss)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), f"{name} sp={sp} ss={ss}"
+    assert torch.isfinite(o1).all()
