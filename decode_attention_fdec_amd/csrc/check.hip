@@ -184,6 +184,11 @@ extern "C" int fdec_check_inputs(int B, const fdec_kv *kv, const int32_t *seq_le
 int fdec_debug_gate(const char *fn, int B, const fdec_kv *kv, const int32_t *seq_lens, const fdec_append *append,
                     const int32_t *prefix_pages, int prefix_len, void *stream) {
     if (!fdec::debug_on()) return FDEC_OK;
+    // the check waits for its result on the host, which a stream under graph
+    // capture cannot do: captured calls go unchecked
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+        return FDEC_OK;
     int flags = 0, first = -1;
     int rc = fdec_check_inputs(B, kv, seq_lens, append, prefix_pages, prefix_len, &flags, &first, stream);
     if (rc) return rc;

@@ -477,9 +477,11 @@ int fdec_check_inputs(int B, const fdec_kv *kv, const int32_t *seq_lens, const f
  * fdec_decode_partials, fdec_decode_balanced, fdec_decode_multi,
  * fdec_decode_multi_balanced and fdec_cascade_decode run fdec_check_inputs on
  * their own arguments before any launch and return FDEC_ERR_INVALID_ARG (message
- * in fdec_last_error()) without launching when a flag is set. Off by default;
- * FDEC_DEBUG set to anything but "0" in the environment turns it on at the
- * first call; fdec_set_debug overrides it (process-wide).
+ * in fdec_last_error()) without launching when a flag is set. The check waits
+ * for its result, which a stream under graph capture cannot: calls made while
+ * their stream is capturing launch unchecked. Off by default; FDEC_DEBUG set to
+ * anything but "0" in the environment turns it on at the first call;
+ * fdec_set_debug overrides it (process-wide).
  */
 void fdec_set_debug(int on);
 int fdec_debug_enabled(void);

@@ -140,3 +140,43 @@ def test_debug_mode_refuses_bad_data_and_keeps_the_bits():
     finally:
         F.set_debug(False)
     assert not F.debug_enabled()
+
+
+def test_debug_mode_under_graph_capture():
+    """The check waits for its result on the host, so a call made while its stream
+    is capturing launches unchecked: the captured graph replays the eager result
+    bit for bit, and the same call made eagerly is still checked."""
+    case = _paged()
+    d = to_dev(case)
+    ws = F.Workspace(F.workspace_size(case.B, case.Hq, case.Hkv, case.D, 5), torch.device("cuda"))
+    out = torch.empty(case.B, case.Hq, case.D, dtype=torch.float32, device="cuda")
+    lse = torch.empty(case.B, case.Hq, dtype=torch.float32, device="cuda")
+
+    def step(table):
+        F.decode(d["q"], d["k"], d["v"], d["seq_lens"], page_table=table, num_splits=5, out=out, lse=lse,
+                 workspace=ws)
+
+    step(d["page_table"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    F.set_debug(True)
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                step(d["page_table"])
+        torch.cuda.synchronize()
+        for _ in range(3):
+            out.zero_()
+            lse.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+        table = d["page_table"].clone()
+        table[2, 7] = case.k.shape[0] + 3
+        with pytest.raises(F.FdecError):
+            step(table)
+    finally:
+        F.set_debug(False)
