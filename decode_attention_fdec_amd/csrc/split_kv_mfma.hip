@@ -1133,6 +1133,12 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 2) void cascade_fused_kernel(co
     bool prefix;
     int v;
     cascade_role((int)blockIdx.x, NPf, NSf, prefix, v);
+    // Float8 pools: a suffix block's waves win issue over the prefix block's waves
+    // on a shared SIMD, so their tile loads go out without waiting behind the
+    // prefix's conversions and products (a wave's priority only orders issue;
+    // no wave waits on another block). 16-bit pools keep equal priority, which
+    // measured no slower.
+    if (KF && !prefix) __builtin_amdgcn_s_setprio(3);
     if (prefix)
         cascade_prefix_body<DT, KF, kMapMfmaWaves, CascadeFusedSlots<KF>::kValue>(cp, v % sp, (v / sp) % cp.Hkv,
                                                                                v / (sp * cp.Hkv), sm.pf);
