@@ -541,7 +541,7 @@ def main() -> int:
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="time the K steps as one captured HIP graph replay (default) or as eager launches")
     ap.add_argument("--splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2g8,c1f8,c2g2f8,c5f8",
+    ap.add_argument("--also", default="c1,c3,c4,c5,c2f8,c3f8,c2q2,c2q4,c2f8q4,c2g8,c1f8,c2g2f8,c5f8",
                     help="other workloads timed for context ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=24.0, help="CPU oracle timing budget (all runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -613,8 +613,8 @@ def main() -> int:
             runs += [("c3", "c3", "bal"), ("c3_uniform_splits", "c3", args.mode)]
         elif name == "c3f8":
             runs.append((name, name, "bal"))
-        elif re.fullmatch(r"c\d+q\d+", name):  # e.g. c2q4: workload c2 with 4 query tokens per request
-            base, q = name.split("q")
+        elif re.fullmatch(r"c\d+\w*?q\d+", name):  # e.g. c2q4 / c2f8q4: c2 / c2f8 with 4 query tokens
+            base, q = name.rsplit("q", 1)
             runs.append((name, base, f"multi{q}"))
         else:
             runs.append((name, name, args.mode))

@@ -381,11 +381,11 @@ extern "C" int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const 
     const int G = Hq / kv->num_kv_heads;
     // one query token: fdec_decode's own map kernel (vector or matrix-core), so
     // the result is its two-kernel result bitwise for every shape
-    const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
+    const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim) &&
                       (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
     if (q_len > 1 && !mt16 && !(p.mfma && G == 4))
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: several query tokens need head_dim 128 and either Hq = 4 Hkv or a 16-bit cache", fn);
+                         "%s: several query tokens need head_dim 128 and page_size a multiple of 16", fn);
     const int ql = fdec::mfma_tokens_per_wave(q_len);
     p.q_len = q_len;
     p.q_groups = (q_len + ql - 1) / ql;
@@ -491,12 +491,12 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, 1, softmax_scale, nullptr);
     const int G = Hq / kv->num_kv_heads;
     // several query tokens: the 16x16x32 kernel when its row blocks fill
-    const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim, kv->dtype == FDEC_FP8_E4M3) &&
+    const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim) &&
                       (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
     if (!mt16 && !(p.mfma && (G == 4 || (G == 8 && q_len == 1))))
         return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: needs head_dim 128, page_size a multiple of 16 and Hq = 4 Hkv (8 Hkv with one query "
-                         "token; q_len * Hq / Hkv >= 12 with several tokens and 16-bit caches)",
+                         "%s: needs head_dim 128, page_size a multiple of 16 and, with one query token, "
+                         "Hq = 4 or 8 Hkv",
                          fn);
     if (B == 0) return FDEC_OK;
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);

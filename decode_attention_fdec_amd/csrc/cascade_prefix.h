@@ -49,12 +49,6 @@ typedef unsigned int pfx_u32x4_v __attribute__((ext_vector_type(4)));
 // on that address, with constant offsets folded into the instruction).
 __device__ __forceinline__ pfx_lds_u8 *pfx_lds(uint32_t a) { return (pfx_lds_u8 *)(size_t)a; }
 
-// Float8 tiles: the 16-byte slot of piece p in row r is p ^ pfx_swz8(r). A K read
-// (16 rows 16kb .. 16kb + 15, one piece) and a V transpose read (rows 4kq + 0..3
-// and 16 + 4kq + 0..3 of a 32-row half, one piece) then take distinct
-// (row parity, slot) pairs in each group of 16 lanes: distinct banks.
-__device__ __forceinline__ int pfx_swz8(int r) { return ((r >> 1) & 7) ^ ((r >> 2) & 4); }
-
 // The LDS of one prefix block: rings of NSL K tiles and NSL V tiles, and the
 // split's page ids.
 template <int KF, int NSL> struct PfxLds {
@@ -123,12 +117,12 @@ __device__ __forceinline__ void cascade_prefix_body(const CascadeParams &p, int 
     // on the lane, the ring slot and the key block enter as uniform offsets.
     //  K (A of S^T): row 16kb + li, the 8 (16-bit: 16 bytes) or 8 float8 (8 bytes)
     //  elements at d = 32ks + 8kq. 16-bit: piece 4ks + kq in slot (4ks + kq) ^ li;
-    //  float8: half kq & 1 of piece 2ks + kq / 2 in slot piece ^ pfx_swz8(16kb + li)
+    //  float8: half kq & 1 of piece 2ks + kq / 2 in slot piece ^ fp8_row_swz(16kb + li)
     //  = piece ^ (li / 2) ^ 4 (kb & 1), i.e. koff[ks] ^ 64 for odd kb.
     //  V (B of P V): 16-bit, row 32kk + ra0 (+16), ra0 = 4kq + li / 4 < 16, piece
     //  2db + p0 in slot (2db + p0) ^ ra0 = 2 (db ^ ra0 / 2) + (p0 ^ (ra0 & 1));
     //  float8, row 32kk + rv0, rv0 the (li / 2)-th of the lane group's 8 keys,
-    //  piece db in slot db ^ pfx_swz8(rv0) (32kk leaves the swizzle unchanged).
+    //  piece db in slot db ^ fp8_row_swz(rv0) (32kk leaves the swizzle unchanged).
     uint32_t koff[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -139,7 +133,7 @@ __device__ __forceinline__ void cascade_prefix_body(const CascadeParams &p, int 
         const int k8 = li >> 1;
         const int rv0 = k8 < 4 ? 4 * kq + k8 : 16 + 4 * kq + (k8 - 4);
         vlane = (uint32_t)(rv0 * 128 + 8 * (li & 1));
-        vsw = (uint32_t)pfx_swz8(rv0);
+        vsw = (uint32_t)fp8_row_swz(rv0);
     } else {
         const int ra0 = 4 * kq + (li >> 2);
         const int p0 = (li & 3) >> 1;
@@ -166,7 +160,7 @@ __device__ __forceinline__ void cascade_prefix_body(const CascadeParams &p, int 
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
         const int r = kPfxDmaRows * w + kRowsPerDma * gi + lane / kPieces;
-        const int sw = KF ? pfx_swz8(r) : (r & 15);
+        const int sw = KF ? fp8_row_swz(r) : (r & 15);
         voff_full[gi] = (uint32_t)(lane / kPieces) * stok + 16u * (uint32_t)((lane % kPieces) ^ sw);
     }
     // the first source row of group gi of a tile (rows past the split's end
@@ -205,7 +199,7 @@ __device__ __forceinline__ void cascade_prefix_body(const CascadeParams &p, int 
             uint32_t voff = voff_full[gi];
             if (__builtin_expect(nvalid < kPfxKeys, 0)) {
                 const int r = r0 + lane / kPieces;
-                const int sw = KF ? pfx_swz8(r) : (r & 15);
+                const int sw = KF ? fp8_row_swz(r) : (r & 15);
                 voff = (uint32_t)(min(r, nvalid - 1) - rs) * stok + 16u * (uint32_t)((lane % kPieces) ^ sw);
             }
             dma16(reinterpret_cast<const char *>(p.k) + eoff * ES, voff, lds_addr(kring[slot]) + (uint32_t)RB * r0);

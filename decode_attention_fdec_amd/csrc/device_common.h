@@ -24,6 +24,13 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w) {
     return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
+// Float8 tiles of 128-byte rows on the 16x16x32 matrix cores: the 16-byte slot
+// of piece p in row r is p ^ fp8_row_swz(r). A K read (16 rows 16kb .. 16kb + 15,
+// one piece) and a V transpose read (rows 4kq + 0..3 and 16 + 4kq + 0..3 of a
+// 32-row half, one piece) then take distinct (row parity, slot) pairs in each
+// group of 16 lanes: distinct banks.
+__device__ __forceinline__ int fp8_row_swz(int r) { return ((r >> 1) & 7) ^ ((r >> 2) & 4); }
+
 // The e4m3fn code (OCP float8: sign, 4 exponent bits with bias 7, 3 fraction
 // bits) of a binary32 value, rounded to nearest with ties to even. Magnitudes
 // of 448 (the largest finite code) and above saturate to +-448, NaN gives the

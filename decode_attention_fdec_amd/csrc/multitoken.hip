@@ -13,7 +13,11 @@
 // holds kMtWaves such waves, each with a private LDS ring. Per 32-key tile:
 //   - K and V rows go global -> LDS by LDS-DMA (no registers), 4 rows per
 //     instruction (a page holds a multiple of 16 rows, so 4 rows lie on one
-//     page), 16-byte pieces of row r in slot piece ^ (r mod 16);
+//     page), 16-byte pieces of row r in slot piece ^ (r mod 16); float8 caches
+//     (the pages' FP8 KV cache, bf16 queries): 128-byte rows, 8 per instruction,
+//     piece slots swizzled by fp8_row_swz, widened to bf16 in registers after
+//     each LDS read (K: an 8-byte read; V: an 8-bit transpose read), the
+//     request's descales applied to the scores and to the output;
 //   - S^T = K Q^T: A = 16 keys x 32 d of K from LDS, B = Q^T held in registers,
 //     so lane l's result column is query row l % 16 and its four values four
 //     keys of that row: each lane applies its row's causal limit;
@@ -37,6 +41,8 @@ typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+typedef int i32x2_v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_v lds_i32x2;
 
 template <int DT> struct Mfma16;
 template <> struct Mfma16<0> {
@@ -64,9 +70,12 @@ template <> __device__ __forceinline__ uint32_t mt_pack2<1>(float a, float b) {
 }
 
 constexpr int kMtKeys = 32;                  // keys per tile
-constexpr int kMtTileBytes = kMtKeys * 256;  // 32 rows of 128 16-bit elements
+constexpr int kMtTileBytes = kMtKeys * 256;  // 32 rows of 128 16-bit elements (float8: the first half)
 constexpr int kMtNS = 2;                     // ring slots per wave (one tile in flight ahead)
-constexpr int kMtDma = 2 * kMtKeys / 4;      // DMA instructions per tile (K and V, 4 rows each)
+// DMA instructions per tile: K and V, 4 rows (16-bit) or 8 rows (float8) each
+template <int KF> struct MtDma {
+    static constexpr int kValue = 2 * kMtKeys / (KF ? 8 : 4);
+};
 constexpr float kMtTau = 8.0f;
 constexpr float kMtFloor = -1.0e30f;
 
@@ -115,15 +124,18 @@ __device__ __forceinline__ void mt16_rows(const MapParams &p, int b, int g, int 
 }
 
 // DMA of the 32-key tile at token t0 of request b (contiguous row crow), KV
-// head g, into K / V tiles kt / vt: 8 groups of 4 rows each; tile rows below lo
-// and above hi (outside the valid rows) repeat the nearest valid row. t0 is a
-// multiple of 16 and pages hold a multiple of 16 rows, so each 16-row half of
-// the tile lies in one page: at most two page ids per tile, both read before
-// any address needs them.
-template <bool PAGED>
+// head g, into K / V tiles kt / vt: 8 groups of 4 rows (16-bit) or 4 groups of 8
+// rows (float8); tile rows below lo and above hi (outside the valid rows) repeat
+// the nearest valid row. t0 is a multiple of 16 and pages hold a multiple of 16
+// rows, so each 16-row half of the tile lies in one page: at most two page ids
+// per tile, both read before any address needs them.
+template <bool PAGED, int KF>
 __device__ __forceinline__ void mt16_issue(const MapParams &p, int b, int64_t crow, int g, int t0, int lo, int hi,
                                            uint8_t *kt, uint8_t *vt, int lane) {
-    const uint32_t stok = (uint32_t)(p.s_token * 2);
+    constexpr int ES = KF ? 1 : 2;   // bytes per element
+    constexpr int RW = KF ? 8 : 4;   // rows per instruction (1 KB)
+    constexpr int LPR = 64 / RW;     // lanes per row (16-byte pieces)
+    const uint32_t stok = (uint32_t)(p.s_token * ES);
     int64_t half[2];  // element offset of token t0 + 16 h
     if constexpr (PAGED) {
         typedef const __attribute__((address_space(4))) int32_t *cpage_t;
@@ -140,22 +152,26 @@ __device__ __forceinline__ void mt16_issue(const MapParams &p, int b, int64_t cr
         half[1] = half[0] + 16 * p.s_token;
     }
 #pragma unroll
-    for (int gi = 0; gi < kMtKeys / 4; ++gi) {
-        const int g0 = 4 * gi;
+    for (int gi = 0; gi < kMtKeys / RW; ++gi) {
+        const int g0 = RW * gi;
         const int rs = min(max(g0, lo), hi);  // the group's first source row
         const int h = rs >> 4;                // its half of the tile
-        const int64_t eoff = half[h] + (int64_t)((rs & ~3) - 16 * h) * p.s_token;
-        const int r = g0 + (lane >> 4);
-        const int src = min(max(r, lo), hi) - (rs & ~3);  // 0..3 within the group
-        const uint32_t voff = (uint32_t)src * stok + 16u * (uint32_t)((lane & 15) ^ (r & 15));
-        dma16_kv(reinterpret_cast<const char *>(p.k) + eoff * 2, voff, lds_addr(kt) + 256u * g0);
-        dma16_kv(reinterpret_cast<const char *>(p.v) + eoff * 2, voff, lds_addr(vt) + 256u * g0);
+        const int base = rs & ~(RW - 1);      // the RW-aligned block holding every source row
+        const int64_t eoff = half[h] + (int64_t)(base - 16 * h) * p.s_token;
+        const int r = g0 + lane / LPR;
+        const int src = min(max(r, lo), hi) - base;  // 0 .. RW - 1
+        const int sw = KF ? fp8_row_swz(r) : (r & 15);
+        const uint32_t voff = (uint32_t)src * stok + 16u * (uint32_t)((lane % LPR) ^ sw);
+        dma16_kv(reinterpret_cast<const char *>(p.k) + eoff * ES, voff, lds_addr(kt) + (uint32_t)(128 * ES * g0));
+        dma16_kv(reinterpret_cast<const char *>(p.v) + eoff * ES, voff, lds_addr(vt) + (uint32_t)(128 * ES * g0));
     }
 }
 
 // One 32-key tile at token t0: S^T = K Q^T, online softmax per query row (keys
-// [t_lo, lim[rb]) count), O += P V. srow: the wave's LDS row factors.
-template <int DT, int RB>
+// [t_lo, lim[rb]) count), O += P V. srow: the wave's LDS row factors. Float8
+// tiles (KF = 1, bf16 queries) are widened to bf16 as they are read; scale_log2
+// then carries the K descale.
+template <int DT, int RB, int KF>
 __device__ __forceinline__ void mt16_tile(const uint8_t *K, const uint8_t *V, const uint4 (&qb)[RB][4], int t0,
                                           int t_lo, const int (&lim)[RB], float scale_log2, int lane,
                                           Mt16State<RB> &st, float (*srow)[16 * RB]) {
@@ -169,7 +185,16 @@ __device__ __forceinline__ void mt16_tile(const uint8_t *K, const uint8_t *V, co
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kr = 16 * kb + li;
-            const uint4 a = *reinterpret_cast<const uint4 *>(K + kr * 256 + 16 * ((4 * ks + kq) ^ (kr & 15)));
+            uint4 a;
+            if constexpr (KF == 1) {
+                // elements d = 32ks + 8kq .. + 7: half kq & 1 of piece 2ks + kq / 2
+                const uint2 k8 = *reinterpret_cast<const uint2 *>(
+                    K + kr * 128 + 16 * ((2 * ks + (kq >> 1)) ^ fp8_row_swz(kr)) + 8 * (kq & 1));
+                const uint2 lo = fp8x4_to_bf16(k8.x), hi = fp8x4_to_bf16(k8.y);
+                a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+                a = *reinterpret_cast<const uint4 *>(K + kr * 256 + 16 * ((4 * ks + kq) ^ (kr & 15)));
+            }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[kb][rb] = Mfma16<DT>::run(a, qb[rb][ks], s[kb][rb]);
         }
@@ -251,31 +276,52 @@ __device__ __forceinline__ void mt16_tile(const uint8_t *K, const uint8_t *V, co
 
     // ---- O += P V: B operand of K-slots 8kq .. 8kq + 7 at d = 16db + li from two
     // transpose reads whose lane m (of 16) addresses key row 4kq + m / 4 (+ 16),
-    // d 16db + 4 (m % 4) .. + 3
+    // d 16db + 4 (m % 4) .. + 3. Float8: one 8-bit transpose read (in each group
+    // of 16 lanes, lane j gets byte j % 8 of the 8-byte pieces of lanes j / 8 + 2k,
+    // k = 0..7) whose lane m addresses the (m / 2)-th of the same 8 keys, bytes
+    // 16db + 8 (m & 1) .. + 7.
+    if constexpr (KF == 1) {
+        const int k8 = li >> 1;
+        const int rv0 = k8 < 4 ? 4 * kq + k8 : 16 + 4 * kq + (k8 - 4);
+        const uint8_t *vrow = V + rv0 * 128 + 8 * (li & 1);
+        const int vsw = fp8_row_swz(rv0);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        const int ra = 4 * kq + (li >> 2), rb2 = ra + 16;
-        const int piece = 2 * db + ((li & 3) >> 1), half = 8 * (li & 1);
-        const s16x4_v x0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(V + ra * 256 + 16 * (piece ^ (ra & 15)) + half));
-        const s16x4_v x1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(V + rb2 * 256 + 16 * (piece ^ (rb2 & 15)) + half));
-        const uint2 v0 = __builtin_bit_cast(uint2, x0), v1 = __builtin_bit_cast(uint2, x1);
-        const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        for (int db = 0; db < 8; ++db) {
+            const i32x2_v x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(vrow + 16 * (db ^ vsw)));
+            const uint2 v0 = fp8x4_to_bf16((uint32_t)x[0]), v1 = fp8x4_to_bf16((uint32_t)x[1]);
+            const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            st.o[rb][db] = Mfma16<DT>::run(pah[rb], bop, st.o[rb][db]);
-            st.ol[rb][db] = Mfma16<DT>::run(pal[rb], bop, st.ol[rb][db]);
+            for (int rb = 0; rb < RB; ++rb) {
+                st.o[rb][db] = Mfma16<DT>::run(pah[rb], bop, st.o[rb][db]);
+                st.ol[rb][db] = Mfma16<DT>::run(pal[rb], bop, st.ol[rb][db]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int ra = 4 * kq + (li >> 2), rb2 = ra + 16;
+            const int piece = 2 * db + ((li & 3) >> 1), half = 8 * (li & 1);
+            const s16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(V + ra * 256 + 16 * (piece ^ (ra & 15)) + half));
+            const s16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(V + rb2 * 256 + 16 * (piece ^ (rb2 & 15)) + half));
+            const uint2 v0 = __builtin_bit_cast(uint2, x0), v1 = __builtin_bit_cast(uint2, x1);
+            const uint4 bop = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                st.o[rb][db] = Mfma16<DT>::run(pah[rb], bop, st.o[rb][db]);
+                st.ol[rb][db] = Mfma16<DT>::run(pal[rb], bop, st.ol[rb][db]);
+            }
         }
     }
 }
 
-// The rows' states against their true maximum T: O~ = O 2^(m - T), d = l 2^(m - T),
-// m = T ln 2 (empty: (0, -inf, 0)). Query row rr = r0 + local row (rows < R)
+// The rows' states against their true maximum T: O~ = O 2^(m - T) vdesc,
+// d = l 2^(m - T), m = T ln 2 (empty: (0, -inf, 0)). Query row rr = r0 + local row (rows < R)
 // goes to state index slot(i, head) of po / pm / pd.
 template <int RB, class SlotOf>
 __device__ __forceinline__ void mt16_write(const MapParams &p, const Mt16State<RB> &st, float (*srow)[16 * RB],
-                                           int r0, int R, int G, int lane, SlotOf slot) {
+                                           int r0, int R, int G, int lane, float vdesc, SlotOf slot) {
     constexpr int D = 128;
     const int kq = lane >> 4, li = lane & 15;
 #pragma unroll
@@ -301,7 +347,7 @@ __device__ __forceinline__ void mt16_write(const MapParams &p, const Mt16State<R
             if (rr >= R) continue;
             const int i = rr / G, hh = rr - i * G;
             const int64_t sidx = slot(i, hh);
-            const float f = srow[0][rl];
+            const float f = srow[0][rl] * vdesc;  // V's descale (1 for 16-bit caches)
             float *dst = p.po + sidx * D;
 #pragma unroll
             for (int db = 0; db < 8; ++db) dst[16 * db + li] = (st.o[rb][db][r] + st.ol[rb][db][r]) * f;
@@ -314,8 +360,9 @@ __device__ __forceinline__ void mt16_write(const MapParams &p, const Mt16State<R
     __builtin_amdgcn_wave_barrier();  // srow is reused by the next piece
 }
 
-template <int DT, bool PAGED, int RB>
+template <int DT, bool PAGED, int RB, int KF>
 __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16(const MapParams p) {
+    static_assert(!KF || DT == 1, "float8 caches take bf16 queries");
     constexpr int ROWS = 16 * RB;  // query rows of a wave
     __shared__ __attribute__((aligned(16))) uint8_t ring[kMtWaves][kMtNS][2][kMtTileBytes];
     __shared__ float srow[kMtWaves][3][ROWS];
@@ -346,6 +393,9 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16(const MapPar
     mt16_rows<RB>(p, b, g, G, R, r0, L, t_lo, lane, qb, lim);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) lim[rb] = min(lim[rb], t_end);
+    // float8 caches: the request's descales for this KV head (scalar loads)
+    const float kd = KF ? kv_descale(p.k_descale, p, b, g) : 1.0f;
+    const float vd = KF ? kv_descale(p.v_descale, p, b, g) : 1.0f;
     // the loads above are done before any DMA is issued: a wait the compiler
     // models keeps it from waiting on them (and so on the DMA) later
     __builtin_amdgcn_s_waitcnt(0);
@@ -354,8 +404,8 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16(const MapPar
     auto issue = [&](int tile) {
         const int t0 = t_begin + tile * kMtKeys;
         const int slot = tile % kMtNS;
-        mt16_issue<PAGED>(p, b, crow, g, t0, tile == 0 ? nskip0 : 0, t_stop - t0 - 1, ring[w][slot][0],
-                          ring[w][slot][1], lane);
+        mt16_issue<PAGED, KF>(p, b, crow, g, t0, tile == 0 ? nskip0 : 0, t_stop - t0 - 1, ring[w][slot][0],
+                              ring[w][slot][1], lane);
     };
     Mt16State<RB> st;
     st.reset();
@@ -364,14 +414,14 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16(const MapPar
         if (tile + 1 < ntiles) issue(tile + 1);
         // this tile's loads have landed once only the next tile's remain
         if (tile + 1 < ntiles)
-            wait_vm<kMtDma>();
+            wait_vm<MtDma<KF>::kValue>();
         else
             wait_vm<0>();
-        mt16_tile<DT, RB>(ring[w][tile % kMtNS][0], ring[w][tile % kMtNS][1], qb, t_begin + tile * kMtKeys, t_lo,
-                          lim, p.scale_log2, lane, st, srow[w]);
+        mt16_tile<DT, RB, KF>(ring[w][tile % kMtNS][0], ring[w][tile % kMtNS][1], qb, t_begin + tile * kMtKeys,
+                              t_lo, lim, p.scale_log2 * kd, lane, st, srow[w]);
     }
     // state rows (request, token, head) of [B * q_len * Hq, s_total]
-    mt16_write<RB>(p, st, srow[w], r0, R, G, lane, [&](int i, int hh) -> int64_t {
+    mt16_write<RB>(p, st, srow[w], r0, R, G, lane, vd, [&](int i, int hh) -> int64_t {
         return (((int64_t)b * p.q_len + i) * p.Hq + g * G + hh) * p.s_total + p.s_offset + split;
     });
 }
@@ -382,8 +432,9 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16(const MapPar
 // slot (block + request) of rows (token, head) of [q_len * Hq, nslots], and the
 // block holding a request's first tile records (first slot, piece count) in
 // seg_meta. Q of each request is loaded into registers when its piece starts.
-template <int DT, bool PAGED, int RB>
+template <int DT, bool PAGED, int RB, int KF>
 __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const MapParams p) {
+    static_assert(!KF || DT == 1, "float8 caches take bf16 queries");
     constexpr int ROWS = 16 * RB;
     __shared__ __attribute__((aligned(16))) uint8_t ring[kMtWaves][kMtNS][2][kMtTileBytes];
     __shared__ float srow[kMtWaves][3][ROWS];
@@ -474,12 +525,15 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const Ma
         const int k = x - prod.P;
         const int t0 = (prod.lp & ~15) + k * kMtKeys;
         const int lo = k == 0 ? prod.lp - (prod.lp & ~15) : 0;
-        mt16_issue<PAGED>(p, prod.b, prod.crow, g, t0, lo, prod.L - t0 - 1, ring[w][x % kMtNS][0],
-                          ring[w][x % kMtNS][1], lane);
+        mt16_issue<PAGED, KF>(p, prod.b, prod.crow, g, t0, lo, prod.L - t0 - 1, ring[w][x % kMtNS][0],
+                              ring[w][x % kMtNS][1], lane);
     };
+    // float8 caches: the current request's descales for this KV head
+    float kd = KF ? kv_descale(p.k_descale, p, cons.b, g) : 1.0f;
+    float vd = KF ? kv_descale(p.v_descale, p, cons.b, g) : 1.0f;
     // the states of request b's piece: slot blk + b of rows (token, head)
     auto flush = [&](const Mt16State<RB> &st, int b) {
-        mt16_write<RB>(p, st, srow[w], r0, R, G, lane, [&](int i, int hh) -> int64_t {
+        mt16_write<RB>(p, st, srow[w], r0, R, G, lane, vd, [&](int i, int hh) -> int64_t {
             return ((int64_t)i * p.Hq + g * G + hh) * p.nslots + blk + b;
         });
     };
@@ -497,6 +551,10 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const Ma
             st.reset();
             advance(cons);
             mt16_rows<RB>(p, cons.b, g, G, R, r0, cons.L, cons.lp, lane, qb, lim);
+            if constexpr (KF == 1) {
+                kd = kv_descale(p.k_descale, p, cons.b, g);
+                vd = kv_descale(p.v_descale, p, cons.b, g);
+            }
             // before the next tile's DMA: this wait (on tile x, needed anyway)
             // tells the compiler the Q loads are done, so it adds no wait of
             // its own in the loop, which would also wait on the DMA ahead
@@ -504,12 +562,12 @@ __global__ __launch_bounds__(64 * kMtWaves, 1) void map_kernel_mt16_bal(const Ma
         }
         if (x + 1 < end) issue(x + 1);
         if (x + 1 < end)
-            wait_vm<kMtDma>();
+            wait_vm<MtDma<KF>::kValue>();
         else
             wait_vm<0>();
         const int t0 = (cons.lp & ~15) + (x - cons.P) * kMtKeys;
-        mt16_tile<DT, RB>(ring[w][x % kMtNS][0], ring[w][x % kMtNS][1], qb, t0, cons.lp, lim, p.scale_log2, lane, st,
-                          srow[w]);
+        mt16_tile<DT, RB, KF>(ring[w][x % kMtNS][0], ring[w][x % kMtNS][1], qb, t0, cons.lp, lim,
+                              p.scale_log2 * kd, lane, st, srow[w]);
     }
     flush(st, cons.b);
 }
@@ -521,9 +579,16 @@ hipError_t launch_map_mt16(const MapParams &p, int S, hipStream_t st) {
     const int nchunk = (R + 16 * rb - 1) / (16 * rb);
     const int units = p.Hkv * nchunk;
     dim3 grid(S, p.B, (units + kMtWaves - 1) / kMtWaves), block(64 * kMtWaves);
-    if (p.head_dim != 128 || p.kv_fp8 || p.mode != kPlain) return hipErrorInvalidValue;
-#define FDEC_MT16(DT, PG, RBV) hipLaunchKernelGGL((map_kernel_mt16<DT, PG, RBV>), grid, block, 0, st, p)
-    if (rb == 1) {
+    if (p.head_dim != 128 || p.mode != kPlain || (p.kv_fp8 && p.dtype != 1)) return hipErrorInvalidValue;
+#define FDEC_MT16(DT, PG, RBV) hipLaunchKernelGGL((map_kernel_mt16<DT, PG, RBV, 0>), grid, block, 0, st, p)
+#define FDEC_MT16F8(PG, RBV) hipLaunchKernelGGL((map_kernel_mt16<1, PG, RBV, 1>), grid, block, 0, st, p)
+    if (p.kv_fp8) {
+        if (rb == 1) {
+            if (p.page_table) FDEC_MT16F8(true, 1); else FDEC_MT16F8(false, 1);
+        } else {
+            if (p.page_table) FDEC_MT16F8(true, 2); else FDEC_MT16F8(false, 2);
+        }
+    } else if (rb == 1) {
         if (p.dtype == 0) {
             if (p.page_table) FDEC_MT16(0, true, 1); else FDEC_MT16(0, false, 1);
         } else {
@@ -537,6 +602,7 @@ hipError_t launch_map_mt16(const MapParams &p, int S, hipStream_t st) {
         }
     }
 #undef FDEC_MT16
+#undef FDEC_MT16F8
     return hipGetLastError();
 }
 
@@ -546,9 +612,16 @@ hipError_t launch_map_mt16_balanced(const MapParams &p, int nblocks, hipStream_t
     const int nchunk = (R + 16 * rb - 1) / (16 * rb);
     const int units = p.Hkv * nchunk;
     dim3 grid(nblocks, 1, (units + kMtWaves - 1) / kMtWaves), block(64 * kMtWaves);
-    if (p.head_dim != 128 || p.kv_fp8 || p.mode != kPlain) return hipErrorInvalidValue;
-#define FDEC_MT16B(DT, PG, RBV) hipLaunchKernelGGL((map_kernel_mt16_bal<DT, PG, RBV>), grid, block, 0, st, p)
-    if (rb == 1) {
+    if (p.head_dim != 128 || p.mode != kPlain || (p.kv_fp8 && p.dtype != 1)) return hipErrorInvalidValue;
+#define FDEC_MT16B(DT, PG, RBV) hipLaunchKernelGGL((map_kernel_mt16_bal<DT, PG, RBV, 0>), grid, block, 0, st, p)
+#define FDEC_MT16BF8(PG, RBV) hipLaunchKernelGGL((map_kernel_mt16_bal<1, PG, RBV, 1>), grid, block, 0, st, p)
+    if (p.kv_fp8) {
+        if (rb == 1) {
+            if (p.page_table) FDEC_MT16BF8(true, 1); else FDEC_MT16BF8(false, 1);
+        } else {
+            if (p.page_table) FDEC_MT16BF8(true, 2); else FDEC_MT16BF8(false, 2);
+        }
+    } else if (rb == 1) {
         if (p.dtype == 0) {
             if (p.page_table) FDEC_MT16B(0, true, 1); else FDEC_MT16B(0, false, 1);
         } else {
@@ -562,6 +635,7 @@ hipError_t launch_map_mt16_balanced(const MapParams &p, int nblocks, hipStream_t
         }
     }
 #undef FDEC_MT16B
+#undef FDEC_MT16BF8
     return hipGetLastError();
 }
 

@@ -99,11 +99,11 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  * contiguous): every GQA group size and head_dim in fdec_decode and
  * fdec_decode_partials (the matrix-core map kernel for Hq = 4 or 8 Hkv at
  * head_dim 128 without append, the vector kernel otherwise, and for every
- * append); head_dim 128
- * with Hq = 4 Hkv in fdec_decode_balanced and fdec_decode_multi, and with
- * Hq = 8 Hkv in fdec_decode_balanced; fdec_decode_multi with q_len = 1 takes
- * every shape fdec_decode does; other calls and shapes return
- * FDEC_ERR_UNSUPPORTED. The partial states then
+ * append); head_dim 128 with Hq = 4 or 8 Hkv in fdec_decode_balanced;
+ * fdec_decode_multi and fdec_decode_multi_balanced with q_len > 1 at head_dim
+ * 128 for every Hq / Hkv (the 16x16x32 matrix-core kernel widens float8 tiles to
+ * bf16 as it reads them); fdec_decode_multi with q_len = 1 takes every shape
+ * fdec_decode does; other calls and shapes return FDEC_ERR_UNSUPPORTED. The partial states then
  * already include V's descale.
  */
 typedef struct fdec_kv {
@@ -323,9 +323,10 @@ int fdec_merge_states(const float *part_o, const float *part_m, const float *par
  *   1 <= q_len <= FDEC_MAX_QLEN. q_len = 1 runs fdec_decode's map and merge
  *   kernels: every shape fdec_decode takes without append, and the result is
  *   fdec_decode's two-kernel result bitwise. q_len > 1 is built for head_dim
- *   128, page_size a multiple of 16 or contiguous: every Hq / Hkv with fp16 /
- *   bf16 caches, and float8 caches with Hq = 4 Hkv (FDEC_ERR_UNSUPPORTED
- *   otherwise); no append. workspace >= fdec_workspace_size(B * q_len, Hq, Hkv,
+ *   128, page_size a multiple of 16 or contiguous, every Hq / Hkv and every
+ *   cache dtype (FDEC_ERR_UNSUPPORTED otherwise): the 16x16x32 matrix-core
+ *   kernel over 16-row blocks of the q_len * Hq / Hkv query rows of a (request,
+ *   KV head); no append. workspace >= fdec_workspace_size(B * q_len, Hq, Hkv,
  *   head_dim, S).
  */
 int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
@@ -365,9 +366,9 @@ size_t fdec_balanced_workspace_size(int B, int Hq, int Hkv, int head_dim, int nu
  * (q [B, q_len, Hq, D], out [B, q_len, Hq, D], lse [B, Hq, q_len], causal as in
  * fdec_decode_multi) with the work of all requests cut into num_blocks equal
  * tile ranges per group of KV heads as in fdec_decode_balanced (0 = one block
- * per compute unit over all groups). 1 <= q_len <= FDEC_MAX_QLEN; the shapes and
- * errors of fdec_decode_balanced. q_len = 1 gives fdec_decode_balanced's result
- * bitwise.
+ * per compute unit over all groups). 1 <= q_len <= FDEC_MAX_QLEN. q_len = 1: the
+ * shapes and errors of fdec_decode_balanced, and its result bitwise; q_len > 1:
+ * the shapes of fdec_decode_multi.
  */
 int fdec_decode_multi_balanced(const void *q, int B, int q_len, int Hq, const fdec_kv *kv, const int32_t *seq_lens,
                                int num_blocks, float softmax_scale, float *out, float *lse, void *workspace,

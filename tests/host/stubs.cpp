@@ -196,7 +196,7 @@ hipError_t launch_map_mt16(const MapParams &p, int S, hipStream_t) {
     note("map_mt16");
     map_inputs("launch_map_mt16", p);
     uniform_states("launch_map_mt16", p, S);
-    if (p.head_dim != 128 || p.kv_fp8) return hipErrorInvalidValue;
+    if (p.head_dim != 128 || (p.kv_fp8 && p.dtype != 1)) return hipErrorInvalidValue;
     return hipSuccess;
 }
 hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nb, hipStream_t) {
@@ -210,6 +210,7 @@ hipError_t launch_map_mt16_balanced(const MapParams &p, int nb, hipStream_t) {
     note("map_mt16_balanced");
     map_inputs("launch_map_mt16_balanced", p);
     balanced_states("launch_map_mt16_balanced", p, nb);
+    if (p.head_dim != 128 || (p.kv_fp8 && p.dtype != 1)) return hipErrorInvalidValue;
     return hipSuccess;
 }
 void prefix_checks(const char *w, const CascadeParams &p, int splits) {

@@ -132,11 +132,6 @@ def test_multi_token_shapes_rejected():
     with pytest.raises(F.FdecError) as e:
         run(case, q, 1)
     assert e.value.status == F.FDEC_ERR_UNSUPPORTED
-    case = contiguous_case(249, 2, 16, 8, 128, [10, 20], 32, FP8)  # float8 at G = 2
-    q = multi_query(250, case, 2)
-    with pytest.raises(F.FdecError) as e:
-        run(case, q, 1)
-    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
     case = contiguous_case(248, 2, 16, 4, 128, [10, 20], 32, BF16)
     for bad in (17, 0):
         q = torch.zeros(2, max(bad, 1), 16, 128, dtype=BF16)
@@ -289,3 +284,53 @@ def test_multi_token_balanced_shapes_rejected():
     with pytest.raises(F.FdecError) as e:
         run_bal(case, q, 1)
     assert e.value.status == F.FDEC_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- float8 caches on the 16x16x32 kernel
+# ("Inference Cookbook / 推理优化" §7.2, FP8 KV cache: e4m3 codes times a descale per
+# (request, KV head), bf16 queries). The 16x16x32 kernel widens the float8 tiles to
+# bf16 after each LDS read; G = 1, 2 and 8 (and G = 4 from 12 query rows) run it.
+
+@pytest.mark.parametrize("G,q_len", [(1, 2), (1, 13), (2, 3), (2, 8), (4, 3), (4, 16), (8, 2), (8, 5)])
+@pytest.mark.parametrize("kind", ["contig", "paged"])
+def test_fp8_multi_token_on_the_16x16x32_kernel(G, q_len, kind):
+    if kind == "contig":
+        case = contiguous_case(600 + 10 * G + q_len, 6, 4 * G, 4, 128, LENS, 2048, FP8, pad="nan")
+    else:
+        case = paged_case(700 + 10 * G + q_len, 6, 4 * G, 4, 128, LENS, 32, FP8, extra_pages=3, pad="nan")
+    q = multi_query(800 + 10 * G + q_len, case, q_len)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for S in (1, 5, 0):
+        out, lse = run(case, q, S)
+        check(out, lse, ref_out, ref_lse, FP8, f"float8 {kind} G={G} q_len={q_len} S={S}")
+    for nb in (1, 3, 0):
+        out, lse = run_bal(case, q, nb)
+        check(out, lse, ref_out, ref_lse, FP8, f"float8 balanced {kind} G={G} q_len={q_len} nb={nb}")
+
+
+def test_fp8_multi_token_with_leftpad_and_batch_idx():
+    lens, pads = [300, 40, 19, 1000], [5, 38, 17, 999]  # some tokens see only padding -> empty
+    case = indexed_case(640, 4, 8, 4, 128, lens, pads, 1024, FP8, cache_rows=7)  # G = 2
+    q = multi_query(641, case, 5)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for S in (1, 4):
+        out, lse = run(case, q, S)
+        check(out, lse, ref_out, ref_lse, FP8, f"float8 indexed S={S}")
+    for nb in (2, 0):
+        out, lse = run_bal(case, q, nb)
+        check(out, lse, ref_out, ref_lse, FP8, f"float8 balanced indexed nb={nb}")
+
+
+def test_fp8_multi_token_both_g4_kernels_match_the_oracle(monkeypatch):
+    # G = 4 with 16 query rows: the 16x16x32 kernel, and the 4x4x4 kernel when forced
+    case = paged_case(660, 5, 16, 4, 128, [900, 3, 64, 1500, 0], 16, FP8, extra_pages=2, pad="nan")
+    q = multi_query(661, case, 4)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for path in ("16x16", "4x4"):
+        if path == "4x4":
+            monkeypatch.setenv("FDEC_MULTI_PATH", "4x4")
+        for S in (3, 0):
+            out, lse = run(case, q, S)
+            check(out, lse, ref_out, ref_lse, FP8, f"float8 G=4 {path} S={S}")
+        out, lse = run_bal(case, q, 4)
+        check(out, lse, ref_out, ref_lse, FP8, f"float8 G=4 balanced {path}")

@@ -53,10 +53,9 @@ def draw(i):
         kinds += ["multi"]
     kind = str(r.choice(kinds))
     dtypes = [F16, BF16]
-    # float8: uniform splits for every shape; the balanced split at G = 4 or 8,
-    # multi-token decode at G = 4 (head_dim 128)
-    if kind in ("two", "fused") or (D == 128 and ((G == 4 and kind in ("balanced", "multi")) or
-                                                  (G == 8 and kind == "balanced"))):
+    # float8: uniform splits for every shape; the balanced split (G = 4 or 8) and
+    # multi-token decode (every G) at head_dim 128
+    if kind in ("two", "fused") or (D == 128 and kind in ("balanced", "multi")):
         dtypes.append(FP8)
     dtype = dtypes[int(r.integers(0, len(dtypes)))]
     ps = int(r.choice([0, 16, 32, 64]))
