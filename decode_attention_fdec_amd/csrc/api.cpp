@@ -490,14 +490,12 @@ int decode_balanced_impl(const char *fn, const void *q, int B, int q_len, int Hq
         return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: B * ceil(capacity / 16) must stay below 2^31", fn);
     fdec::MapParams p = map_params(q, B, Hq, kv, seq_lens, 1, softmax_scale, nullptr);
     const int G = Hq / kv->num_kv_heads;
-    // several query tokens: the 16x16x32 kernel when its row blocks fill
-    const bool mt16 = q_len > 1 && fdec::mt16_eligible(q_len, G, kv->head_dim) &&
+    // the 16x16x32 kernel: several query tokens, and one query token at G = 1, 2
+    // (its 16-row block padded; G = 4 and 8 keep their own single-query kernels)
+    const bool mt16 = (q_len > 1 || (G != 4 && G != 8)) && fdec::mt16_eligible(q_len, G, kv->head_dim) &&
                       (kv->page_size == 0 || kv->page_size % 16 == 0) && std::getenv("FDEC_MULTI_PATH") == nullptr;
     if (!mt16 && !(p.mfma && (G == 4 || (G == 8 && q_len == 1))))
-        return fdec_fail(FDEC_ERR_UNSUPPORTED,
-                         "%s: needs head_dim 128, page_size a multiple of 16 and, with one query token, "
-                         "Hq = 4 or 8 Hkv",
-                         fn);
+        return fdec_fail(FDEC_ERR_UNSUPPORTED, "%s: needs head_dim 128 and page_size a multiple of 16", fn);
     if (B == 0) return FDEC_OK;
     if (!out) return fdec_fail(FDEC_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if ((reinterpret_cast<uintptr_t>(out) & 7u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))

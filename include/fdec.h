@@ -99,9 +99,8 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  * contiguous): every GQA group size and head_dim in fdec_decode and
  * fdec_decode_partials (the matrix-core map kernel for Hq = 4 or 8 Hkv at
  * head_dim 128 without append, the vector kernel otherwise, and for every
- * append); head_dim 128 with Hq = 4 or 8 Hkv in fdec_decode_balanced;
- * fdec_decode_multi and fdec_decode_multi_balanced with q_len > 1 at head_dim
- * 128 for every Hq / Hkv (the 16x16x32 matrix-core kernel widens float8 tiles to
+ * append); head_dim 128 for every Hq / Hkv in fdec_decode_balanced, and in
+ * fdec_decode_multi and fdec_decode_multi_balanced with q_len > 1 (the 16x16x32 matrix-core kernel widens float8 tiles to
  * bf16 as it reads them); fdec_decode_multi with q_len = 1 takes every shape
  * fdec_decode does; other calls and shapes return FDEC_ERR_UNSUPPORTED. The partial states then
  * already include V's descale.
@@ -343,8 +342,10 @@ int fdec_decode_multi(const void *q, int B, int q_len, int Hq, const fdec_kv *kv
  * fdec_decode's up to rounding. The ranges are computed on the device from
  * seq_lens (no host copy of the lengths), so the call may be captured in a
  * graph whose lengths change between replays.
- *   Supported for G = Hq/Hkv = 4 or 8, head_dim 128, page_size a multiple of 16
- *   (or contiguous), no append: FDEC_ERR_UNSUPPORTED otherwise.
+ *   Supported for every G = Hq/Hkv (G = 4 and 8 on their single-query
+ *   matrix-core kernels, G = 1 and 2 on the 16x16x32 kernel with its 16-row
+ *   block padded), head_dim 128, page_size a multiple of 16 (or contiguous), no
+ *   append: FDEC_ERR_UNSUPPORTED otherwise.
  *   num_blocks  blocks per group of KV heads, 1..256; 0 = per compute unit of
  *               the current device over all groups, one block for fp16/bf16
  *               caches and two for float8 caches (measured best on MI355X).

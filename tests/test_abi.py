@@ -235,8 +235,7 @@ def call_balanced(kv, B=2, Hq=32, num_blocks=16, ws_bytes=1 << 30, out=FAKE, ws=
 
 
 def test_balanced_validation(fdec):
-    # only the matrix-core shapes: G = 4, D = 128, pages of 16k tokens
-    assert call_balanced(kv_struct(), Hq=16) == F.FDEC_ERR_UNSUPPORTED  # G = 2
+    # only the matrix-core kernels' head_dim 128
     assert call_balanced(kv_struct(head_dim=64, s_outer=4096 * 8 * 64, s_token=8 * 64, s_head=64)) == \
         F.FDEC_ERR_UNSUPPORTED
     assert call_balanced(kv_struct(), num_blocks=-1) == F.FDEC_ERR_INVALID_ARG
@@ -267,8 +266,9 @@ def test_fp8_validation(fdec):
     fp8 = dict(dtype=F.FDEC_FP8_E4M3)
     # strides must be multiples of 16 bytes: 16 float8 elements
     assert call_decode(kv_struct(s_head=8, **fp8)) == F.FDEC_ERR_INVALID_ARG
-    # the balanced split takes float8 at G = 4 or 8 only
-    assert call_balanced(kv_struct(**fp8), Hq=16) == F.FDEC_ERR_UNSUPPORTED  # G = 2
+    # the balanced split takes float8 at head_dim 128 only
+    assert call_balanced(kv_struct(head_dim=64, s_outer=4096 * 8 * 64, s_token=8 * 64, s_head=64, **fp8)) == \
+        F.FDEC_ERR_UNSUPPORTED
     # an append into a float8 cache is checked like any other
     a = F.FdecAppend()
     a.k_new, a.v_new = FAKE, FAKE

@@ -170,13 +170,19 @@ def test_fp8_vector_kernel_states_match_oracle_states():
     assert err.max() < 1e-3
 
 
-def test_fp8_unsupported_paths_are_reported():
-    case = contiguous_case(98, 1, 8, 4, 128, [40], 64, FP8, pad="nan")  # G = 2: no balanced split
-    d = to_dev(case)
-    with pytest.raises(F.FdecError) as e:
-        F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], k_descale=d["k_descale"],
-                          v_descale=d["v_descale"])
-    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
+def test_fp8_balanced_split_at_g1_g2():
+    """One query token at G = 1 and 2 on the balanced split: the 16x16x32 kernel
+    (float8 tiles), its 16-row block padded, against the oracle."""
+    for G in (1, 2):
+        case = paged_case(98 + G, 7, 8 * G, 8, 128, [40, 0, 3000, 1, 777, 64, 65], 16, FP8, extra_pages=2,
+                          pad="nan")
+        d = to_dev(case)
+        ref_out, ref_lse = oracle_decode(case)
+        for nb in (1, 5, 0):
+            out, lse = F.decode_balanced(d["q"], d["k"], d["v"], d["seq_lens"], page_table=d["page_table"],
+                                         num_blocks=nb, k_descale=d["k_descale"], v_descale=d["v_descale"])
+            torch.cuda.synchronize()
+            assert_parity(out, lse, ref_out, ref_lse, FP8, f"float8 balanced G={G} nb={nb}")
 
 
 # ---------------------------------------------------------------- append into a float8 cache

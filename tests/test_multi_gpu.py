@@ -278,12 +278,21 @@ def test_multi_token_balanced_both_kernels_agree(q_len, monkeypatch):
     assert (res["16x16"] - res["4x4"]).abs().max().item() < 1e-4
 
 
-def test_multi_token_balanced_shapes_rejected():
-    case = contiguous_case(390, 2, 16, 8, 128, [10, 20], 32, BF16)  # G = 2, one token: no balanced kernel
-    q = multi_query(391, case, 1)
-    with pytest.raises(F.FdecError) as e:
-        run_bal(case, q, 1)
-    assert e.value.status == F.FDEC_ERR_UNSUPPORTED
+@pytest.mark.parametrize("G,dt", [(1, F16), (2, BF16), (1, BF16)])
+def test_one_token_balanced_at_g1_g2(G, dt):
+    # one query token at G = 1, 2 on the balanced split: the 16x16x32 kernel with its
+    # 16-row block padded; fdec_decode_multi_balanced with q_len = 1 is the same call
+    case = paged_case(390 + G, 7, 8 * G, 8, 128, [40, 0, 3000, 1, 777, 64, 65], 16, dt, extra_pages=2, pad="nan")
+    d = to_dev(case)
+    q = multi_query(391 + G, case, 1)
+    ref_out, ref_lse = oracle.decode_multi(okv(case), q, case.seq_lens, 1 / math.sqrt(128))
+    for nb in (1, 5, 0):
+        om, lm = run_bal(case, q, nb)
+        check(om, lm, ref_out, ref_lse, dt, f"one-token balanced G={G} nb={nb}")
+        o1, l1 = F.decode_balanced(q[:, 0].contiguous().to("cuda"), d["k"], d["v"], d["seq_lens"],
+                                   page_table=d["page_table"], num_blocks=nb)
+        torch.cuda.synchronize()
+        assert torch.equal(om[:, 0], o1) and torch.equal(lm[:, :, 0], l1), f"G={G} nb={nb}"
 
 
 # ---------------------------------------------------------------- float8 caches on the 16x16x32 kernel

@@ -47,14 +47,12 @@ def draw(i):
     kinds = ["two", "fused", "append"]
     if G == 4 and D == 128:
         kinds += ["balanced", "multi", "multi"]
-    elif D == 128 and G * 3 >= 12:
-        kinds += ["multi", "balanced"]
     elif D == 128:
-        kinds += ["multi"]
+        kinds += ["multi", "balanced"]
     kind = str(r.choice(kinds))
     dtypes = [F16, BF16]
-    # float8: uniform splits for every shape; the balanced split (G = 4 or 8) and
-    # multi-token decode (every G) at head_dim 128
+    # float8: uniform splits for every shape; the balanced split and multi-token
+    # decode (every G) at head_dim 128
     if kind in ("two", "fused") or (D == 128 and kind in ("balanced", "multi")):
         dtypes.append(FP8)
     dtype = dtypes[int(r.integers(0, len(dtypes)))]
