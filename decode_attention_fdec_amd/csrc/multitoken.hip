@@ -6,8 +6,10 @@
 // b is its row L_b - q_len + i and sees rows [leftpad, L_b - q_len + i]. The
 // q_len * G query rows of one (request, KV head) -- G query heads per KV head --
 // form the row blocks of v_mfma_f32_16x16x32_{bf16,f16}, so the contraction is
-// dense for any G once q_len * G reaches 16 (the 4x4x4 kernel in
-// split_kv_mfma.hip covers short q_len).
+// dense for any G once q_len * G reaches 16; below that the row blocks are
+// padded. It takes every call with two or more query tokens, and the balanced
+// split's single-query calls at G = 1, 2 (the 4x4x4 kernel's multi-token tiles
+// in split_kv_mfma.hip remain as the path FDEC_MULTI_PATH forces).
 //
 // One wave per (split, request, KV head, chunk of 32 query rows); a block
 // holds kMtWaves such waves, each with a private LDS ring. Per 32-key tile:
