@@ -64,7 +64,7 @@ struct MapParams {
 
 // Whether the matrix-core map kernel can take these parameters (mfma aside).
 inline bool map_mfma_eligible(const MapParams &p) {
-    return (p.Hq == 4 * p.Hkv || p.Hq == 8 * p.Hkv) && p.head_dim == 128 && (p.mode == kPlain || !p.kv_fp8) &&
+    return (p.Hq == 4 * p.Hkv || p.Hq == 8 * p.Hkv) && p.head_dim == 128 &&
            (p.page_table == nullptr || p.page_size % 16 == 0) && p.s_token > 0 &&
            p.s_token < (int64_t(1) << 26);  // 16 rows of a tile as 32-bit byte offsets
 }

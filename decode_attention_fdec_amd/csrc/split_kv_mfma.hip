@@ -282,6 +282,12 @@ __device__ __forceinline__ void mfma_tile(const uint8_t *kl, const uint8_t *vl, 
                 s1[j] = Mfma4<DT>::template run<0, 0>(k1, qb[j][4 * e + 1], s1[j]);
                 s[j] = Mfma4<DT>::template run<0, 0>(k2, qb[j][4 * e + 2], s[j]);
                 s1[j] = Mfma4<DT>::template run<0, 0>(k3, qb[j][4 * e + 3], s1[j]);
+                if constexpr (QLO) {
+                    s[j] = Mfma4<DT>::template run<0, 0>(k0, qlo[j][4 * e], s[j]);
+                    s1[j] = Mfma4<DT>::template run<0, 0>(k1, qlo[j][4 * e + 1], s1[j]);
+                    s[j] = Mfma4<DT>::template run<0, 0>(k2, qlo[j][4 * e + 2], s[j]);
+                    s1[j] = Mfma4<DT>::template run<0, 0>(k3, qlo[j][4 * e + 3], s1[j]);
+                }
             }
         }
     }
@@ -604,9 +610,10 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g8(cons
 // block owning row cache_seqlens[b] rounds the rotated k_new once to the cache
 // type, writes it and v_new into the cache, and waits for those stores before
 // its first DMA, which may read the row back.
-template <int DT, bool PAGED, int NG>
+template <int DT, bool PAGED, int NG, int KF>
 __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(const MapParams p) {
-    constexpr int D = 128, G = 4 * NG, KF = 0;  // NG groups of four query heads per KV head
+    constexpr int D = 128, G = 4 * NG;  // NG groups of four query heads per KV head
+    static_assert(!KF || DT == 1, "float8 caches take bf16 queries and new rows");
     constexpr int NS = Ring<KF>::kSlots;
     using E = Elem<DT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMapMfmaWaves][Ring<KF>::kBytes];
@@ -667,9 +674,22 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
         uint16_t *vd = reinterpret_cast<uint16_t *>(const_cast<char *>(p.v) + off);
         const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(p.v_new) + ((int64_t)b * p.Hkv + g) * D;
         const bool rotated = p.mode == kAppendRope;
-        for (int i = lane; i < D; i += 64) {
-            kd[i] = rotated ? E::from_float(ks[i]) : ksrc[i];  // unrotated: the bits of k_new
-            vd[i] = vsrc[i];
+        if constexpr (KF == 1) {
+            // float8: the codes of value / descale (the k value rotated in fp32, or
+            // k_new's bf16 value), as the vector kernel stores them
+            uint8_t *k8 = reinterpret_cast<uint8_t *>(const_cast<char *>(p.k)) + off;
+            uint8_t *v8 = reinterpret_cast<uint8_t *>(const_cast<char *>(p.v)) + off;
+            const float kds = kv_descale(p.k_descale, p, b, g), vds = kv_descale(p.v_descale, p, b, g);
+            for (int i = lane; i < D; i += 64) {
+                const float kx = rotated ? ks[i] : E::lo((uint32_t)ksrc[i]);
+                k8[i] = (uint8_t)f32_to_e4m3(__fdiv_rn(kx, kds));
+                v8[i] = (uint8_t)f32_to_e4m3(__fdiv_rn(E::lo((uint32_t)vsrc[i]), vds));
+            }
+        } else {
+            for (int i = lane; i < D; i += 64) {
+                kd[i] = rotated ? E::from_float(ks[i]) : ksrc[i];  // unrotated: the bits of k_new
+                vd[i] = vsrc[i];
+            }
         }
     }
     // every load and store above is done (the owner's row is in L2 before its
@@ -688,7 +708,10 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
     const int t_lo = max(t_begin, lp);
     const int ntiles = t_end > t_lo ? (t_end - t_begin + kMT - 1) / kMT : 0;
     const int nskip0 = t_lo - t_begin;
-    const uint32_t stok = (uint32_t)(p.s_token * 2);
+    const uint32_t stok = (uint32_t)(p.s_token * KvFmt<KF>::kElem);
+    // float8 caches: the request's descales for this KV head
+    const float kd8 = KF ? kv_descale(p.k_descale, p, b, g) : 1.0f;
+    const float vd8 = KF ? kv_descale(p.v_descale, p, b, g) : 1.0f;
     auto tile_offset = [&](int tile) { return token_offset<PAGED, KF>(p, b, crow, g, t_begin + tile * kMT); };
     auto stage = [&](int tile, int64_t off) {
         uint32_t kl, vl;
@@ -714,12 +737,12 @@ __global__ __launch_bounds__(64 * kMapMfmaWaves, 1) void map_kernel_mfma_g4_app(
 #pragma unroll
         for (int j = 0; j < NG; ++j) nv[j] = t_end - (t_begin + tile * kMT);
         mfma_tile<DT, KF, NG, true>(Ring<KF>::k_tile(lds[wv], slot), Ring<KF>::v_tile(lds[wv], slot), qb,
-                                    tile == 0 ? nskip0 : 0, nv, p.scale_log2, lane, st, qlo);
+                                    tile == 0 ? nskip0 : 0, nv, p.scale_log2 * kd8, lane, st, qlo);
     }
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
         const int64_t st0 = ((int64_t)b * p.Hq + hq0 + 4 * j) * p.s_total + p.s_offset + split;
-        write_state(st[j], lane, p.po + st0 * D, p.pm + st0, p.pd + st0, p.s_total);
+        write_state(st[j], lane, p.po + st0 * D, p.pm + st0, p.pd + st0, p.s_total, vd8);
     }
 
     if (p.counters == nullptr) return;
@@ -1037,20 +1060,25 @@ hipError_t launch_map_mfma_g4_balanced(const MapParams &p, int nblocks, hipStrea
 }
 
 hipError_t launch_map_mfma_g4(const MapParams &p, int S, hipStream_t st) {
-    if (p.mode != kPlain) {  // append (single query, 16-bit caches), G = 4 or 8
-        if (p.q_len != 1 || p.kv_fp8) return hipErrorInvalidValue;
+    if (p.mode != kPlain) {  // append (single query), G = 4 or 8
+        if (p.q_len != 1 || (p.kv_fp8 && p.dtype != 1)) return hipErrorInvalidValue;
         dim3 grid(S, p.B, p.Hkv / p.heads_per_block), block(64 * p.heads_per_block);
-#define FDEC_APP(NG)                                                                         \
-    if (p.dtype == 0) {                                                                      \
-        if (p.page_table)                                                                    \
-            hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, true, NG>), grid, block, 0, st, p);  \
-        else                                                                                 \
-            hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, false, NG>), grid, block, 0, st, p); \
-    } else {                                                                                 \
-        if (p.page_table)                                                                    \
-            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, true, NG>), grid, block, 0, st, p);  \
-        else                                                                                 \
-            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, false, NG>), grid, block, 0, st, p); \
+#define FDEC_APP(NG)                                                                            \
+    if (p.kv_fp8) {                                                                             \
+        if (p.page_table)                                                                       \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, true, NG, 1>), grid, block, 0, st, p);  \
+        else                                                                                    \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, false, NG, 1>), grid, block, 0, st, p); \
+    } else if (p.dtype == 0) {                                                                  \
+        if (p.page_table)                                                                       \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, true, NG, 0>), grid, block, 0, st, p);  \
+        else                                                                                    \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<0, false, NG, 0>), grid, block, 0, st, p); \
+    } else {                                                                                    \
+        if (p.page_table)                                                                       \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, true, NG, 0>), grid, block, 0, st, p);  \
+        else                                                                                    \
+            hipLaunchKernelGGL((map_kernel_mfma_g4_app<1, false, NG, 0>), grid, block, 0, st, p); \
     }
         if (p.Hq == 8 * p.Hkv) {
             FDEC_APP(2)

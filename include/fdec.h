@@ -98,8 +98,7 @@ typedef enum { FDEC_F16 = 0, FDEC_BF16 = 1, FDEC_FP8_E4M3 = 2 } fdec_dtype;
  * descale is 1. Queries are bf16. Built for page_size a multiple of 16 (or
  * contiguous): every GQA group size and head_dim in fdec_decode and
  * fdec_decode_partials (the matrix-core map kernel for Hq = 4 or 8 Hkv at
- * head_dim 128 without append, the vector kernel otherwise, and for every
- * append); head_dim 128 for every Hq / Hkv in fdec_decode_balanced, and in
+ * head_dim 128, with or without append, the vector kernel otherwise); head_dim 128 for every Hq / Hkv in fdec_decode_balanced, and in
  * fdec_decode_multi and fdec_decode_multi_balanced with q_len > 1 (the 16x16x32 matrix-core kernel widens float8 tiles to
  * bf16 as it reads them); fdec_decode_multi with q_len = 1 takes every shape
  * fdec_decode does; other calls and shapes return FDEC_ERR_UNSUPPORTED. The partial states then
